@@ -1,0 +1,18 @@
+"""One context-parallel rank's causal attention share on MI355X (gfx950).
+
+The computation runs in the HIP library libcpattn.so (built in-tree by
+``context_causal_attention_attn_amd.build``); this package is its Python
+binding. Importing the binding does not load the library; the first call
+does, and raises ImportError if the library has not been built.
+"""
+from .api import (  # noqa: F401
+    cp_attn_share_positions,
+    cp_attn_validate,
+    cp_attn_share_pairs,
+    cp_attn_workspace_bytes,
+    cp_attn_plan_stats_fwd,
+    cp_attn_fwd,
+    cp_attn_bwd,
+    make_desc,
+)
+from .shares import Share, cut_share  # noqa: F401

@@ -1,0 +1,169 @@
+"""Python binding of the C ABI (include/cp_attn.h), same names.
+
+Argument marshalling only: shapes and strides are read from the tensors, the
+descriptor is filled in, outputs are allocated with torch on the inputs'
+device, and the call is enqueued on torch's current stream. Every step of the
+attention itself runs in the HIP kernels of libcpattn.so.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import CpAttnDesc, CpAttnPlanStats, check
+
+_DT = {torch.bfloat16: _lib.DTYPE_BF16, torch.float32: _lib.DTYPE_FP32}
+
+
+def cp_attn_share_positions(layout: str, s_global: int, cp_size: int, cp_rank: int):
+    """Global start positions of a rank's query chunks and the chunk length."""
+    lib = _lib.load()
+    pos = (ctypes.c_int64 * 2)()
+    n = ctypes.c_int32()
+    length = ctypes.c_int64()
+    check(lib.cp_attn_share_positions(_lib.LAYOUTS[layout], s_global, cp_size, cp_rank,
+                                      pos, ctypes.byref(n), ctypes.byref(length)),
+          "cp_attn_share_positions")
+    return [pos[i] for i in range(n.value)], length.value
+
+
+class _Desc:
+    """A filled cp_attn_desc plus the host arrays it points to."""
+
+    def __init__(self, *, dtype, batch, hq, hkv, head_dim, sq_local, skv, q_chunk_pos,
+                 kv_chunk_pos, layout, causal, softmax_scale, q_strides, kv_strides, o_strides):
+        self.qpos = (ctypes.c_int64 * max(1, len(q_chunk_pos)))(*q_chunk_pos)
+        self.kvpos = (ctypes.c_int64 * max(1, len(kv_chunk_pos)))(*kv_chunk_pos)
+        d = CpAttnDesc()
+        d.abi_version = _lib.ABI_VERSION
+        d.dtype = dtype
+        d.batch, d.hq, d.hkv, d.head_dim = batch, hq, hkv, head_dim
+        d.sq_local, d.skv = sq_local, skv
+        d.n_q_chunks = len(q_chunk_pos)
+        d.q_chunk_pos = ctypes.cast(self.qpos, ctypes.POINTER(ctypes.c_int64))
+        d.n_kv_chunks = len(kv_chunk_pos)
+        d.kv_chunk_pos = ctypes.cast(self.kvpos, ctypes.POINTER(ctypes.c_int64))
+        d.layout = _lib.LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+        d.causal = int(bool(causal))
+        d.softmax_scale = float(softmax_scale)
+        for i in range(3):
+            d.q_strides[i], d.kv_strides[i], d.o_strides[i] = q_strides[i], kv_strides[i], o_strides[i]
+        self.desc = d
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def _check_inputs(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, rows, head_dim]")
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape and strides")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError("q and k/v disagree on batch or head_dim")
+    for t in (q, k, v):
+        if t.stride(3) != 1:
+            raise ValueError("the head_dim axis must be contiguous")
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def make_desc(q, k, v, o_strides, q_chunk_pos: Sequence[int], kv_chunk_pos: Sequence[int],
+              layout, causal: bool, softmax_scale: Optional[float]) -> _Desc:
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+    return _Desc(dtype=_DT.get(q.dtype, -1), batch=B, hq=Hq, hkv=Hkv, head_dim=D, sq_local=Sq, skv=Skv,
+                 q_chunk_pos=list(q_chunk_pos), kv_chunk_pos=list(kv_chunk_pos), layout=layout,
+                 causal=causal, softmax_scale=scale, q_strides=q.stride()[:3],
+                 kv_strides=k.stride()[:3], o_strides=tuple(o_strides)[:3])
+
+
+def _stream_handle(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def cp_attn_validate(q, k, v, q_chunk_pos, *, layout="contiguous", kv_chunk_pos=(0,), causal=True,
+                     softmax_scale=None) -> None:
+    d = make_desc(q, k, v, q.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale)
+    check(_lib.load().cp_attn_validate(d.ref()), "cp_attn_validate")
+
+
+def cp_attn_share_pairs(d: _Desc) -> int:
+    out = ctypes.c_int64()
+    check(_lib.load().cp_attn_share_pairs(d.ref(), ctypes.byref(out)), "cp_attn_share_pairs")
+    return out.value
+
+
+def cp_attn_workspace_bytes(d: _Desc, backward: bool) -> int:
+    out = ctypes.c_size_t()
+    check(_lib.load().cp_attn_workspace_bytes(d.ref(), int(bool(backward)), ctypes.byref(out)),
+          "cp_attn_workspace_bytes")
+    return out.value
+
+
+def cp_attn_plan_stats_fwd(d: _Desc) -> dict:
+    st = CpAttnPlanStats()
+    check(_lib.load().cp_attn_plan_stats_fwd(d.ref(), ctypes.byref(st)), "cp_attn_plan_stats_fwd")
+    return {name: getattr(st, name) for name, _ in CpAttnPlanStats._fields_}
+
+
+def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: Sequence[int], *,
+                layout="contiguous", kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
+                softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None):
+    """Forward of one share: returns (out [B, Hq, Sq, D] in q's dtype, lse [B, Hq, Sq] float32).
+
+    q is the local query shard (rows in chunk order), k/v the gathered K/V.
+    q_chunk_pos gives each chunk's global start position (see
+    cp_attn_share_positions); kv_chunk_pos the global position of key row 0.
+    """
+    lib = _lib.load()
+    _check_inputs(q, k, v)
+    B, Hq, Sq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or out.stride(3) != 1 or out.device != q.device:
+        raise ValueError("out must match q's shape, dtype and device, with a contiguous head_dim")
+    if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
+    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale)
+    check(lib.cp_attn_fwd(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), None, 0, _stream_handle(q)), "cp_attn_fwd")
+    return out, lse
+
+
+def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="contiguous",
+                kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
+                softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward of one share: returns (dq in q's dtype, dk, dv float32 partials over the gathered K/V)."""
+    lib = _lib.load()
+    _check_inputs(q, k, v)
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if dout.shape != q.shape or out.shape != q.shape or dout.dtype != q.dtype or out.dtype != q.dtype:
+        raise ValueError("out and dout must match q's shape and dtype")
+    if dout.stride() != out.stride() or out.stride(3) != 1:
+        out, dout = out.contiguous(), dout.contiguous()
+    if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
+    dq = torch.empty_strided(out.shape, out.stride(), dtype=q.dtype, device=q.device)
+    dk = torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=q.device)
+    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale)
+    need = cp_attn_workspace_bytes(d, True)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    check(lib.cp_attn_bwd(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream_handle(q)), "cp_attn_bwd")
+    return dq, dk, dv

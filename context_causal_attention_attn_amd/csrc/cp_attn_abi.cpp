@@ -1,0 +1,268 @@
+// C ABI of the CP attention share: descriptor validation, share geometry,
+// workspace sizing, the forward tile schedule, and dispatch to the kernels.
+//
+// Fail-fast policy ("新流程 CP 多通信模式迁移设计方案" §13.2 and
+// "HyperModels 新 Trainer Context Parallel 接入设计方案" §4.4): every check runs
+// on the host before any device work is enqueued, and a failed check returns
+// a negative status with no buffer touched. Nothing falls back to a slower or
+// different computation.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "cp_attn.h"
+#include "plan.h"
+
+namespace cpattn {
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int32_t elem_bytes(int32_t dtype) { return dtype == CP_ATTN_BF16 ? 2 : 4; }
+
+int32_t make_share(const cp_attn_desc *d, Share *s) {
+  s->n_q_chunks = d->n_q_chunks;
+  s->chunk_len = d->sq_local / d->n_q_chunks;
+  for (int c = 0; c < d->n_q_chunks; ++c) {
+    s->chunk_pos[c] = d->q_chunk_pos[c];
+    s->order[c] = c;
+  }
+  // Latest global position first: under the causal mask those rows see the
+  // most keys, so their work items are dispatched first (longest first).
+  std::stable_sort(s->order, s->order + d->n_q_chunks,
+                   [&](int a, int b) { return s->chunk_pos[a] > s->chunk_pos[b]; });
+  s->kv_pos0 = d->kv_chunk_pos[0];
+  return CP_ATTN_OK;
+}
+
+static int32_t validate(const cp_attn_desc *d) {
+  if (!d) return CP_ATTN_ERR_NULL_PTR;
+  if (d->abi_version != CP_ATTN_ABI_VERSION) return CP_ATTN_ERR_ABI;
+  if (d->dtype != CP_ATTN_BF16 && d->dtype != CP_ATTN_FP32) return CP_ATTN_ERR_UNSUPPORTED;
+  if (d->batch < 1 || d->hq < 1 || d->hkv < 1 || d->hq % d->hkv != 0) return CP_ATTN_ERR_BAD_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return CP_ATTN_ERR_UNSUPPORTED;
+  if (d->sq_local < 0 || d->skv < 0) return CP_ATTN_ERR_BAD_SHAPE;
+  if (d->sq_local > INT32_MAX || d->skv > INT32_MAX) return CP_ATTN_ERR_UNSUPPORTED;
+  if (d->layout != CP_ATTN_LAYOUT_CONTIGUOUS && d->layout != CP_ATTN_LAYOUT_HEAD_TAIL)
+    return CP_ATTN_ERR_BAD_LAYOUT;
+  if (d->n_q_chunks < 1 || d->n_q_chunks > CP_ATTN_MAX_Q_CHUNKS) return CP_ATTN_ERR_BAD_LAYOUT;
+  if (d->layout == CP_ATTN_LAYOUT_CONTIGUOUS && d->n_q_chunks != 1) return CP_ATTN_ERR_BAD_LAYOUT;
+  if (d->layout == CP_ATTN_LAYOUT_HEAD_TAIL && d->n_q_chunks != 2) return CP_ATTN_ERR_BAD_LAYOUT;
+  if (!d->q_chunk_pos || !d->kv_chunk_pos) return CP_ATTN_ERR_NULL_PTR;
+  if (d->n_kv_chunks < 1) return CP_ATTN_ERR_BAD_LAYOUT;
+  if (d->n_kv_chunks != 1) return CP_ATTN_ERR_UNSUPPORTED;
+  if (d->sq_local % d->n_q_chunks != 0 || d->skv % d->n_kv_chunks != 0) return CP_ATTN_ERR_BAD_SHAPE;
+  if (d->causal != 0 && d->causal != 1) return CP_ATTN_ERR_BAD_SHAPE;
+  if (!isfinite(d->softmax_scale) || !(d->softmax_scale > 0.0f)) return CP_ATTN_ERR_BAD_SHAPE;
+  // Positions: non-negative, far from overflow, and the query chunks disjoint.
+  const int64_t L = d->sq_local / d->n_q_chunks;
+  const int64_t lim = (int64_t)1 << 60;
+  for (int c = 0; c < d->n_q_chunks; ++c) {
+    const int64_t p = d->q_chunk_pos[c];
+    if (p < 0 || p > lim) return CP_ATTN_ERR_BAD_POSITIONS;
+    for (int e = 0; e < c; ++e) {
+      const int64_t o = d->q_chunk_pos[e];
+      if (L > 0 && p < o + L && o < p + L) return CP_ATTN_ERR_BAD_POSITIONS;
+    }
+  }
+  for (int c = 0; c < d->n_kv_chunks; ++c)
+    if (d->kv_chunk_pos[c] < 0 || d->kv_chunk_pos[c] > lim) return CP_ATTN_ERR_BAD_POSITIONS;
+  // Strides: non-negative, and every row start 16-byte aligned given an
+  // aligned base pointer (the kernels move 16-byte vectors along the dim).
+  const int64_t vec = 16 / elem_bytes(d->dtype);
+  const int64_t *all[3] = {d->q_strides, d->kv_strides, d->o_strides};
+  for (auto st : all)
+    for (int i = 0; i < 3; ++i) {
+      if (st[i] < 0) return CP_ATTN_ERR_BAD_SHAPE;
+      if (st[i] % vec != 0) return CP_ATTN_ERR_ALIGNMENT;
+    }
+  return CP_ATTN_OK;
+}
+
+void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
+  memset(p, 0, sizeof(*p));
+  p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
+  p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
+  p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
+  p->kv_pos0 = s.kv_pos0;
+  p->hq = d->hq;
+  p->hkv = d->hkv;
+  p->group = d->hq / d->hkv;
+  p->heads_per_item = fwd_heads_per_item(p->group);
+  p->n_head_packs = d->batch * (d->hq / p->heads_per_item);
+  p->sq = (int32_t)d->sq_local;
+  p->skv = (int32_t)d->skv;
+  p->chunk_len = (int32_t)s.chunk_len;
+  p->n_q_chunks = s.n_q_chunks;
+  const int rows = fwd_block_rows(p->group);
+  p->tiles_per_chunk = (int32_t)((s.chunk_len + rows - 1) / rows);
+  p->causal = d->causal;
+  p->scale = d->softmax_scale;
+  p->scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  for (int i = 0; i < s.n_q_chunks; ++i) {
+    p->chunk_idx[i] = s.order[i];
+    p->chunk_pos[i] = s.chunk_pos[s.order[i]];
+  }
+}
+
+int64_t fwd_grid_size(const FwdParams &p) {
+  return (int64_t)p.n_head_packs * p.n_q_chunks * p.tiles_per_chunk;
+}
+
+}  // namespace cpattn
+
+using namespace cpattn;
+
+extern "C" {
+
+int32_t cp_attn_abi_version(void) { return CP_ATTN_ABI_VERSION; }
+
+const char *cp_attn_error_string(int32_t status) {
+  switch (status) {
+    case CP_ATTN_OK: return "ok";
+    case CP_ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
+    case CP_ATTN_ERR_BAD_SHAPE: return "inconsistent sizes or strides (hq % hkv, chunk lengths, negative strides, non-finite or non-positive scale, causal flag)";
+    case CP_ATTN_ERR_BAD_LAYOUT: return "layout does not match the chunk table (contiguous: 1 Q chunk, head_tail: 2)";
+    case CP_ATTN_ERR_BAD_POSITIONS: return "chunk positions negative, too large, or overlapping";
+    case CP_ATTN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, size or KV chunk table";
+    case CP_ATTN_ERR_WORKSPACE: return "workspace missing or smaller than cp_attn_workspace_bytes()";
+    case CP_ATTN_ERR_HIP: return "HIP launch or runtime error";
+    case CP_ATTN_ERR_ABI: return "descriptor abi_version does not match the library";
+    case CP_ATTN_ERR_ALIGNMENT: return "device pointer or stride not 16-byte aligned";
+    case CP_ATTN_ERR_DIVISIBILITY: return "sequence length not divisible by cp_size (contiguous) or 2*cp_size (head_tail)";
+    default: return "unknown status";
+  }
+}
+
+int32_t cp_attn_share_positions(int32_t layout, int64_t s_global, int32_t cp_size,
+                                int32_t cp_rank, int64_t *q_chunk_pos,
+                                int32_t *n_q_chunks, int64_t *chunk_len) {
+  if (!q_chunk_pos || !n_q_chunks || !chunk_len) return CP_ATTN_ERR_NULL_PTR;
+  if (cp_size < 1 || cp_rank < 0 || cp_rank >= cp_size || s_global < 0) return CP_ATTN_ERR_BAD_SHAPE;
+  if (layout == CP_ATTN_LAYOUT_CONTIGUOUS) {
+    if (s_global % cp_size != 0) return CP_ATTN_ERR_DIVISIBILITY;
+    const int64_t n = s_global / cp_size;
+    q_chunk_pos[0] = (int64_t)cp_rank * n;
+    *n_q_chunks = 1;
+    *chunk_len = n;
+    return CP_ATTN_OK;
+  }
+  if (layout == CP_ATTN_LAYOUT_HEAD_TAIL) {
+    if (s_global % (2 * (int64_t)cp_size) != 0) return CP_ATTN_ERR_DIVISIBILITY;
+    const int64_t n = s_global / (2 * (int64_t)cp_size);
+    q_chunk_pos[0] = (int64_t)cp_rank * n;
+    q_chunk_pos[1] = (int64_t)(2 * cp_size - 1 - cp_rank) * n;
+    *n_q_chunks = 2;
+    *chunk_len = n;
+    return CP_ATTN_OK;
+  }
+  return CP_ATTN_ERR_BAD_LAYOUT;
+}
+
+int32_t cp_attn_validate(const cp_attn_desc *desc) { return validate(desc); }
+
+int32_t cp_attn_share_pairs(const cp_attn_desc *d, int64_t *pairs) {
+  int32_t st = validate(d);
+  if (st) return st;
+  if (!pairs) return CP_ATTN_ERR_NULL_PTR;
+  const int64_t L = d->sq_local / d->n_q_chunks;
+  const int64_t kv0 = d->kv_chunk_pos[0], skv = d->skv;
+  int64_t total = 0;
+  for (int c = 0; c < d->n_q_chunks; ++c) {
+    if (!d->causal) { total += L * skv; continue; }
+    // Row at position p sees keys kv0..min(p, kv0+skv-1): clamp(p-kv0+1, 0, skv).
+    const int64_t p0 = d->q_chunk_pos[c], p1 = p0 + L - 1;
+    // Rows with p < kv0 see nothing; rows with p >= kv0+skv-1 see all skv.
+    const int64_t a = std::max(p0, kv0), b = std::min(p1, kv0 + skv - 1);
+    if (a <= b) {
+      const int64_t n = b - a + 1, f = a - kv0 + 1;  // counts f, f+1, ..., f+n-1
+      total += n * f + n * (n - 1) / 2;
+    }
+    const int64_t full_from = std::max(p0, kv0 + skv - 1 + 1);
+    if (full_from <= p1) total += (p1 - full_from + 1) * skv;
+  }
+  *pairs = total;
+  return CP_ATTN_OK;
+}
+
+int32_t cp_attn_workspace_bytes(const cp_attn_desc *d, int32_t backward, size_t *bytes) {
+  int32_t st = validate(d);
+  if (st) return st;
+  if (!bytes) return CP_ATTN_ERR_NULL_PTR;
+  if (!backward) { *bytes = 0; return CP_ATTN_OK; }
+  // Backward: Delta [B, Hq, Sq] fp32, then the fp32 dQ accumulator [B, Hq, Sq, D].
+  const size_t rows = (size_t)d->batch * d->hq * (size_t)d->sq_local;
+  const size_t delta = (rows * 4 + 255) & ~(size_t)255;
+  *bytes = delta + rows * (size_t)d->head_dim * 4;
+  return CP_ATTN_OK;
+}
+
+int32_t cp_attn_plan_stats_fwd(const cp_attn_desc *d, cp_attn_plan_stats *out) {
+  int32_t st = validate(d);
+  if (st) return st;
+  if (!out) return CP_ATTN_ERR_NULL_PTR;
+  Share s;
+  make_share(d, &s);
+  FwdParams p;
+  fill_fwd_params(d, s, &p);
+  const int rows = fwd_block_rows(p.group);
+  const int bn = kFwdBlockKV;
+  int64_t visits = 0, masked = 0;
+  for (int c = 0; c < p.n_q_chunks; ++c)
+    for (int t = 0; t < p.tiles_per_chunk; ++t) {
+      const int64_t r0 = (int64_t)t * rows;
+      const int64_t nrow = std::min<int64_t>(rows, p.chunk_len - r0);
+      const int64_t qlo = p.chunk_pos[c] + r0, qhi = qlo + nrow - 1;
+      int64_t nvis = p.skv;
+      if (p.causal) nvis = std::min<int64_t>(p.skv, std::max<int64_t>(0, qhi - p.kv_pos0 + 1));
+      const int64_t nt = (nvis + bn - 1) / bn;
+      visits += nt;
+      for (int64_t kt = 0; kt < nt; ++kt) {
+        const int64_t klast = kt * bn + bn - 1;
+        if (klast >= p.skv || (p.causal && p.kv_pos0 + klast > qlo)) ++masked;
+      }
+    }
+  out->work_items = fwd_grid_size(p);
+  out->kv_tile_visits = visits * p.n_head_packs;
+  out->masked_tile_visits = masked * p.n_head_packs;
+  out->block_q_rows = rows;
+  out->block_kv_rows = bn;
+  out->heads_per_item = p.heads_per_item;
+  return CP_ATTN_OK;
+}
+
+int32_t cp_attn_fwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
+                    void *out, float *lse, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int32_t st = validate(d);
+  if (st) return st;
+  if (d->sq_local == 0) return CP_ATTN_OK;
+  if (!q || !out || !lse) return CP_ATTN_ERR_NULL_PTR;
+  if (d->skv > 0 && (!k || !v)) return CP_ATTN_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(out) || (d->skv > 0 && (!aligned16(k) || !aligned16(v))))
+    return CP_ATTN_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return CP_ATTN_ERR_ALIGNMENT;
+  Share s;
+  make_share(d, &s);
+  FwdParams p;
+  fill_fwd_params(d, s, &p);
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  const int e = (d->dtype == CP_ATTN_BF16) ? launch_fwd_bf16(p, d->head_dim, stream)
+                                           : launch_fwd_fp32(p, d->head_dim, stream);
+  return e == 0 ? CP_ATTN_OK : CP_ATTN_ERR_HIP;
+}
+
+}  // extern "C"
+
+extern "C" int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
+                               const void *out, const float *lse, const void *dout, void *dq,
+                               float *dk, float *dv, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  (void)q; (void)k; (void)v; (void)out; (void)lse; (void)dout; (void)dq; (void)dk; (void)dv;
+  (void)workspace; (void)workspace_bytes; (void)stream;
+  int32_t st = validate(d);
+  if (st) return st;
+  return CP_ATTN_ERR_UNSUPPORTED;
+}

@@ -1,0 +1,77 @@
+// Internal host/device contract of the share kernels: the validated share
+// geometry, the forward tile schedule and the kernel parameter blocks.
+//
+// The schedule follows the causal structure of a CP share
+// ("新流程 CP 多通信模式迁移设计方案" §8: every query row carries its own global
+// position; "HyperModels 新 Trainer Context Parallel 接入设计方案" §4.4: each
+// Head-Tail segment keeps its own global interval). A work item is one tile of
+// query rows of one chunk, for a pack of query heads that share one KV head;
+// it visits only the KV tiles its rows can see.
+#pragma once
+
+#include <stdint.h>
+
+#include "cp_attn.h"
+
+namespace cpattn {
+
+constexpr int kMaxQChunks = CP_ATTN_MAX_Q_CHUNKS;
+
+// ---------------------------------------------------------------------------
+// Forward, bf16 MFMA kernel
+// ---------------------------------------------------------------------------
+// Keys per KV tile staged in LDS, and query rows per wavefront.
+constexpr int kFwdBlockKV = 64;
+constexpr int kWaveRows = 32;
+constexpr int kFwdWaves = 4;
+
+struct FwdParams {
+  const void *q;
+  const void *k;
+  const void *v;
+  void *out;
+  float *lse;
+  int64_t q_sb, q_sh, q_ss;     // element strides of q (batch, head, row)
+  int64_t kv_sb, kv_sh, kv_ss;  // of k and v
+  int64_t o_sb, o_sh, o_ss;     // of out
+  int64_t kv_pos0;              // global position of key row 0
+  int32_t hq, hkv, group;       // group = hq / hkv
+  int32_t heads_per_item;       // query heads of one KV group packed in a work item
+  int32_t n_head_packs;         // batch * hq / heads_per_item
+  int32_t sq, skv;
+  int32_t chunk_len;            // rows per query chunk
+  int32_t n_q_chunks;
+  int32_t tiles_per_chunk;      // ceil(chunk_len / block rows)
+  int32_t causal;
+  float scale;                  // softmax_scale
+  float scale_log2;             // softmax_scale * log2(e)
+  // Query chunks in scheduling order (latest global position first, so the
+  // longest causal rows start first); chunk_idx maps back to local order.
+  int64_t chunk_pos[kMaxQChunks];
+  int32_t chunk_idx[kMaxQChunks];
+};
+
+// Geometry derived from a validated descriptor.
+struct Share {
+  int32_t n_q_chunks;
+  int64_t chunk_len;
+  int64_t chunk_pos[kMaxQChunks];   // local chunk order
+  int32_t order[kMaxQChunks];       // chunk indices, latest position first
+  int64_t kv_pos0;
+};
+
+int32_t make_share(const cp_attn_desc *d, Share *s);
+
+// Heads packed per forward work item for a GQA group of size g (a divisor of
+// g, at most kFwdWaves) and the query rows per item (per head).
+inline int fwd_heads_per_item(int g) { return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1; }
+inline int fwd_block_rows(int g) { return kWaveRows * (kFwdWaves / fwd_heads_per_item(g)); }
+
+void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p);
+int64_t fwd_grid_size(const FwdParams &p);
+
+// Launchers (defined with their kernels); return a hipError_t as int.
+int launch_fwd_bf16(const FwdParams &p, int head_dim, void *stream);
+int launch_fwd_fp32(const FwdParams &p, int head_dim, void *stream);
+
+}  // namespace cpattn

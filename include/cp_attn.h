@@ -1,0 +1,200 @@
+/*
+ * cp_attn.h -- C ABI of one context-parallel (CP) rank's causal attention share
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * A "share" is the attention a single CP rank computes: its local query rows
+ * against the gathered (global) keys and values, masked causally by GLOBAL
+ * token position. Sources, by page title and section:
+ *
+ *  [CP-migration] "新流程 CP 多通信模式迁移设计方案" (hyper-parallel issue 7):
+ *      §6.1 AllGather / Pure Colossal (local Q, all-gathered K/V, output stays
+ *      local; backward: dQ local, dK/dV reduce-scattered with sum),
+ *      §6.2 Pure Ulysses and §6.3 Hybrid (head-sliced shares),
+ *      §8 Causal mask (the per-strategy global Q offsets; a flash backend
+ *      should take the offsets natively instead of a materialised mask),
+ *      §9.2 GQA/MQA, §9.3 Layout (BNSD by default).
+ *  [Trainer-CP] "HyperModels 新 Trainer Context Parallel 接入设计方案":
+ *      §0 (Head-Tail load balance), §4.2 (padding / divisibility policy),
+ *      §4.3 (the three synchronous strategies), §4.4 (Head-Tail: two Q
+ *      segments, each with its own global interval; fail fast, no fallback).
+ *  [FLA-CP] "flash-linear-attention 上下文并行CP 从 CP2TP、Ring CP 到 True CP
+ *      的设计取舍与源码实现" §3.2 (contiguous vs zigzag layout, [front; back]
+ *      local order) and §3.3 (divisibility errors).
+ *
+ * Every call validates its descriptor on the host first and returns a negative
+ * status without touching any buffer when something is wrong; there is no
+ * silent fallback to a slower path. All functions are thread-safe and
+ * reentrant; the library keeps no state between calls and never allocates,
+ * frees or retains device memory: the caller owns every buffer, including the
+ * workspace.
+ *
+ * Device work is enqueued on the caller's stream (a hipStream_t passed as
+ * `void *`; NULL means the default stream) and the call returns without
+ * synchronising. The caller keeps every buffer alive until the stream has
+ * passed the work. Kernel faults surface at the caller's next synchronisation.
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CP_ATTN_ABI_VERSION 1
+#define CP_ATTN_MAX_Q_CHUNKS 16
+
+/* Local row order of the query shard. */
+typedef enum {
+  /* One chunk of consecutive global positions: the all-gather (Colossal)
+   * share at offset cp_rank*S/cp, the Ulysses share (offset 0, whole
+   * sequence) and the Hybrid share (offset co_rank*S/C). [CP-migration] §8. */
+  CP_ATTN_LAYOUT_CONTIGUOUS = 0,
+  /* Head-Tail (zigzag): exactly two equal chunks, front = chunk r, back =
+   * chunk 2*cp-1-r of 2*cp chunks. [Trainer-CP] §4.4, [FLA-CP] §3.2. */
+  CP_ATTN_LAYOUT_HEAD_TAIL = 1
+} cp_attn_layout;
+
+/* Element type of q, k, v, out, dout and dq. lse, the backward workspace and
+ * dk/dv are always float32. */
+typedef enum { CP_ATTN_BF16 = 0, CP_ATTN_FP32 = 1 } cp_attn_dtype;
+
+/* Status codes. 0 is success; every error is negative. */
+typedef enum {
+  CP_ATTN_OK = 0,
+  CP_ATTN_ERR_NULL_PTR = -1,      /* a required pointer is NULL */
+  CP_ATTN_ERR_BAD_SHAPE = -2,     /* sizes/strides inconsistent (hq % hkv, chunk lengths, ...) */
+  CP_ATTN_ERR_BAD_LAYOUT = -3,    /* layout vs chunk count, or unknown layout */
+  CP_ATTN_ERR_BAD_POSITIONS = -4, /* negative or overlapping chunk positions */
+  CP_ATTN_ERR_UNSUPPORTED = -5,   /* head_dim / dtype / chunk table this build does not implement */
+  CP_ATTN_ERR_WORKSPACE = -6,     /* workspace NULL or smaller than cp_attn_workspace_bytes() */
+  CP_ATTN_ERR_HIP = -7,           /* a HIP launch or query failed */
+  CP_ATTN_ERR_ABI = -8,           /* desc->abi_version != CP_ATTN_ABI_VERSION */
+  CP_ATTN_ERR_ALIGNMENT = -9,     /* a device pointer or stride breaks the 16-byte vector alignment */
+  CP_ATTN_ERR_DIVISIBILITY = -10  /* cp_attn_share_positions: S not divisible by cp (or 2*cp) */
+} cp_attn_status;
+
+/*
+ * Descriptor of one share. Tensors are indexed [batch][head][row][dim] with
+ * the dim index contiguous (stride 1) and the other three strides given in
+ * ELEMENTS, so BNSD tensors, head slices and row slices of a larger tensor can
+ * be passed without copies ([CP-migration] §9.3).
+ *
+ *   q           [batch, hq,  sq_local, head_dim]  q_strides
+ *   k, v        [batch, hkv, skv,      head_dim]  kv_strides (shared by k and v)
+ *   out, dout,
+ *   dq          [batch, hq,  sq_local, head_dim]  o_strides (shared by the three)
+ *   lse         [batch, hq,  sq_local]            contiguous float32
+ *   dk, dv      [batch, hkv, skv, head_dim]       contiguous float32
+ *
+ * Query row i lies in chunk c = i / L (L = sq_local / n_q_chunks) and has
+ * global position q_chunk_pos[c] + i % L. Key row j lies in KV chunk
+ * c = j / Lkv (Lkv = skv / n_kv_chunks) and has global position
+ * kv_chunk_pos[c] + j % Lkv. With causal != 0, key j is visible to query i iff
+ * pos(j) <= pos(i) (the diagonal included); with causal == 0 every key is
+ * visible. Query head h reads KV head h / (hq / hkv) (contiguous GQA groups,
+ * [CP-migration] §9.2).
+ *
+ * The LSE is the natural log of the sum of exp(softmax_scale * q.k) over the
+ * visible keys; a row with no visible key gets out = 0 and lse = -inf.
+ */
+typedef struct cp_attn_desc {
+  int32_t abi_version;         /* must be CP_ATTN_ABI_VERSION */
+  int32_t dtype;               /* cp_attn_dtype */
+  int32_t batch, hq, hkv;      /* hq % hkv == 0 */
+  int32_t head_dim;            /* bf16: 64 or 128; fp32: 64 or 128 */
+  int64_t sq_local;            /* local query rows (all chunks) */
+  int64_t skv;                 /* gathered key/value rows */
+  int32_t n_q_chunks;          /* 1..CP_ATTN_MAX_Q_CHUNKS, equal lengths */
+  const int64_t *q_chunk_pos;  /* host array [n_q_chunks]: global position of each chunk's row 0 */
+  int32_t n_kv_chunks;         /* this build: 1 (keys in natural order from kv_chunk_pos[0]) */
+  const int64_t *kv_chunk_pos; /* host array [n_kv_chunks] */
+  int32_t layout;              /* cp_attn_layout: contiguous needs 1 Q chunk, head_tail needs 2 */
+  int32_t causal;              /* 1: global-position causal mask, 0: no mask */
+  float softmax_scale;         /* scale applied to q.k, finite and > 0 (1/sqrt(head_dim) is SDPA's default) */
+  int64_t q_strides[3];        /* batch, head, row strides of q (elements) */
+  int64_t kv_strides[3];       /* batch, head, row strides of k and v (elements) */
+  int64_t o_strides[3];        /* batch, head, row strides of out, dout and dq (elements) */
+} cp_attn_desc;
+
+/* ABI version of the loaded library (CP_ATTN_ABI_VERSION of its build). */
+int32_t cp_attn_abi_version(void);
+
+/* Human-readable text of a status code; never NULL, static storage. */
+const char *cp_attn_error_string(int32_t status);
+
+/*
+ * Global chunk positions of CP rank `cp_rank` of `cp_size` over a sequence of
+ * `s_global` tokens ([CP-migration] §8 offset table; [FLA-CP] §3.2):
+ *   contiguous: one chunk at cp_rank * s_global / cp_size of length s_global / cp_size;
+ *   head_tail : two chunks of length L = s_global / (2 cp_size) at
+ *               cp_rank * L (front) and (2 cp_size - 1 - cp_rank) * L (back).
+ * Outputs: q_chunk_pos[0..n-1] (the caller provides room for 2), *n_q_chunks,
+ * *chunk_len. Returns CP_ATTN_ERR_DIVISIBILITY when s_global is not a multiple
+ * of cp_size (contiguous) or 2*cp_size (head_tail) ([Trainer-CP] §4.2,
+ * [FLA-CP] §3.3), CP_ATTN_ERR_BAD_SHAPE for cp_size < 1 or a rank out of range.
+ * Host only; no GPU needed.
+ */
+int32_t cp_attn_share_positions(int32_t layout, int64_t s_global, int32_t cp_size,
+                                int32_t cp_rank, int64_t *q_chunk_pos,
+                                int32_t *n_q_chunks, int64_t *chunk_len);
+
+/* Validate a descriptor (host only; no GPU needed). Checks everything that
+ * does not need device pointers. */
+int32_t cp_attn_validate(const cp_attn_desc *desc);
+
+/* Number of visible (query, key) pairs per (batch, query head) of the share:
+ * the causal work that FLOP counts are based on. Host only. */
+int32_t cp_attn_share_pairs(const cp_attn_desc *desc, int64_t *pairs);
+
+/* Bytes of device workspace cp_attn_fwd (backward == 0) or cp_attn_bwd
+ * (backward != 0) needs for this descriptor; may be 0. Host only. */
+int32_t cp_attn_workspace_bytes(const cp_attn_desc *desc, int32_t backward, size_t *bytes);
+
+/* Work-list statistics of the forward tile scheduler (host only), for tests
+ * and reports: number of work items (one workgroup each), the KV tiles they
+ * visit in total, and the tile shape. */
+typedef struct cp_attn_plan_stats {
+  int64_t work_items;
+  int64_t kv_tile_visits;      /* summed over work items */
+  int64_t masked_tile_visits;  /* visits that need an element-wise mask */
+  int32_t block_q_rows;        /* query rows per work item (per head) */
+  int32_t block_kv_rows;       /* keys per KV tile */
+  int32_t heads_per_item;      /* query heads of one GQA group packed in a work item */
+} cp_attn_plan_stats;
+int32_t cp_attn_plan_stats_fwd(const cp_attn_desc *desc, cp_attn_plan_stats *stats);
+
+/*
+ * Forward of the share: out = softmax(scale * q k^T, masked) v and the LSE.
+ * q, k, v: device pointers of `dtype`; out: device, `dtype`, o_strides;
+ * lse: device float32 [batch, hq, sq_local] contiguous.
+ * Needs no workspace (workspace may be NULL when cp_attn_workspace_bytes
+ * reports 0). Deterministic: the same inputs give bitwise the same outputs.
+ */
+int32_t cp_attn_fwd(const cp_attn_desc *desc, const void *q, const void *k, const void *v,
+                    void *out, float *lse, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * Backward of the share for the loss sum(dout * out):
+ *   dq [batch, hq, sq_local, head_dim] of `dtype` (o_strides);
+ *   dk, dv [batch, hkv, skv, head_dim] float32 contiguous: this share's
+ *   PARTIAL gradients over the gathered K/V, to be summed across ranks by a
+ *   reduce-scatter ([CP-migration] §6.1 backward). Key rows no query of the
+ *   share can see are written as zeros.
+ * out and lse are the forward's outputs for the same inputs. The workspace
+ * (cp_attn_workspace_bytes with backward != 0) is caller-owned device memory;
+ * its contents on entry do not matter.
+ */
+int32_t cp_attn_bwd(const cp_attn_desc *desc, const void *q, const void *k, const void *v,
+                    const void *out, const float *lse, const void *dout,
+                    void *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

@@ -1,0 +1,51 @@
+"""Shared helpers of the GPU parity tests: cut shares on both sides of the
+parity check, each side with its own code (the oracle's share builders on the
+CPU side, the package's cut_share on the HIP side), from one seeded global
+problem."""
+import math
+
+import numpy as np
+import torch
+
+import oracle.cp_share as oc
+from context_causal_attention_attn_amd import cut_share
+from synthetic import global_problem
+
+
+def oracle_share(kind, S, Hq, Hkv, cp, rank, U=2):
+    if kind == "contiguous":
+        return oc.contiguous_share(S, Hq, Hkv, cp, rank)
+    if kind == "head_tail":
+        return oc.head_tail_share(S, Hq, Hkv, cp, rank)
+    if kind == "ulysses":
+        return oc.ulysses_share(S, Hq, Hkv, cp, rank)
+    if kind == "hybrid":
+        return oc.hybrid_share(S, Hq, Hkv, cp, U, rank)
+    raise ValueError(kind)
+
+
+def to_f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def oracle_rows(prob, sh, scale, rows=None, heads=None, causal=True):
+    """Oracle out/lse of a share, optionally only for some local rows/heads.
+    Returns arrays indexed [b, local_head, local_row]."""
+    q = prob.q[:, sh["q_heads"]]
+    q_pos = sh["q_pos"]
+    qsel = q[:, :, torch.from_numpy(q_pos)]
+    k = prob.k[:, sh["kv_heads"]]
+    v = prob.v[:, sh["kv_heads"]]
+    hq_loc = len(sh["q_heads"])
+    G = hq_loc // len(sh["kv_heads"])
+    heads = list(range(hq_loc)) if heads is None else list(heads)
+    rows = np.arange(len(q_pos)) if rows is None else np.asarray(rows)
+    outs, lses = [], []
+    for h in heads:
+        hk = h // G
+        o, l = oc.attention_rows(to_f64(qsel[:, h:h + 1, torch.from_numpy(rows)]),
+                                 to_f64(k[:, hk:hk + 1]), to_f64(v[:, hk:hk + 1]),
+                                 q_pos[rows], sh["kv_pos"], scale, causal)
+        outs.append(o[:, 0])
+        lses.append(l[:, 0])
+    return np.stack(outs, 1), np.stack(lses, 1)

@@ -27,3 +27,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionstart(session):
+    """Build the HIP library once if nothing is built yet (a built library is
+    used as is; rebuilding after a source change is the caller's job)."""
+    from context_causal_attention_attn_amd import build as b
+    if not os.path.exists(b.LIB_PATH):
+        b.build()

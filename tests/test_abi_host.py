@@ -1,0 +1,173 @@
+"""Host-side checks of the C ABI (CPU only; no kernel is launched).
+
+The library must load and export every function include/cp_attn.h declares;
+descriptor validation must reject each malformed input with its documented
+status; the host-side share geometry, pair counts and the forward tile
+schedule are checked against the oracle's geometry and the page-derived
+golden tables.
+"""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.cp_share as oc
+from context_causal_attention_attn_amd import _lib
+from context_causal_attention_attn_amd.api import _Desc, cp_attn_plan_stats_fwd, cp_attn_share_pairs
+from context_causal_attention_attn_amd.api import cp_attn_share_positions, cp_attn_workspace_bytes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cp_attn.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(cp_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), f"libcpattn.so does not export {n}"
+        assert n in _lib.SIGNATURES, f"binding has no signature for {n}"
+    assert set(_lib.SIGNATURES) == set(names)
+    assert lib.cp_attn_abi_version() == _lib.ABI_VERSION
+    for st in list(_lib.STATUS) + [-99]:
+        assert lib.cp_attn_error_string(st)
+
+
+def test_share_positions_golden():
+    geo = json.load(open(os.path.join(GOLDEN, "share_geometry.json")))
+    for c in geo["cases"]:
+        pos, n = cp_attn_share_positions(c["layout"], c["S"], c["cp"], c["rank"])
+        assert pos == c["chunk_pos"] and n == c["chunk_len"]
+    for c in geo["errors"]:
+        with pytest.raises(_lib.CpAttnError) as e:
+            cp_attn_share_positions(c["layout"], c["S"], c["cp"], c["rank"])
+        assert e.value.status in (-10, -2)
+
+
+def desc(**kw):
+    base = dict(dtype=0, batch=1, hq=8, hkv=2, head_dim=128, sq_local=500, skv=2000,
+                q_chunk_pos=[500], kv_chunk_pos=[0], layout="contiguous", causal=True,
+                softmax_scale=0.088, q_strides=(8 * 2000 * 128, 2000 * 128, 128),
+                kv_strides=(2 * 2000 * 128, 2000 * 128, 128), o_strides=(8 * 500 * 128, 500 * 128, 128))
+    base.update(kw)
+    return _Desc(**base)
+
+
+def status(d):
+    return _lib.load().cp_attn_validate(d.ref())
+
+
+def test_validate_accepts_good_descriptors():
+    assert status(desc()) == 0
+    assert status(desc(layout="head_tail", q_chunk_pos=[250, 1750], sq_local=500)) == 0
+    assert status(desc(dtype=1, head_dim=64, q_strides=(0, 0, 64), kv_strides=(0, 0, 64), o_strides=(0, 0, 64))) == 0
+    assert status(desc(sq_local=0)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=6, hkv=4), -2),                                  # hq % hkv
+    (dict(batch=0), -2),
+    (dict(head_dim=96), -5),                                  # unsupported head_dim
+    (dict(dtype=7), -5),
+    (dict(layout="head_tail"), -3),                           # head_tail needs 2 chunks
+    (dict(q_chunk_pos=[0, 250], sq_local=500), -3),           # contiguous needs 1 chunk
+    (dict(layout=5), -3),
+    (dict(layout="head_tail", q_chunk_pos=[0, 100], sq_local=500), -4),   # overlapping chunks
+    (dict(q_chunk_pos=[-1]), -4),
+    (dict(layout="head_tail", q_chunk_pos=[0, 300], sq_local=501), -2),   # unequal chunks
+    (dict(kv_chunk_pos=[0, 1000]), -5),                       # KV chunk tables: not in this build
+    (dict(softmax_scale=float("nan")), -2),
+    (dict(softmax_scale=0.0), -2),
+    (dict(q_strides=(8 * 2000 * 128, 2000 * 128, 132)), -9),   # row stride breaks 16-byte alignment
+    (dict(kv_strides=(-1, 2000 * 128, 128)), -2),
+    (dict(sq_local=2 ** 31), -5),
+])
+def test_validate_rejects(kw, code):
+    assert status(desc(**kw)) == code
+
+
+def test_validate_abi_version_causal_flag_and_null():
+    d = desc()
+    d.desc.abi_version = 2
+    assert status(d) == -8
+    d = desc()
+    d.desc.causal = 2
+    assert status(d) == -2
+    assert _lib.load().cp_attn_validate(None) == -1
+
+
+CONFIGS = [
+    ("contiguous", 256, 4, 1, 2, 2),
+    ("contiguous", 32768, 8, 7, 32, 8),
+    ("head_tail", 32768, 8, 0, 32, 8),
+    ("head_tail", 32768, 8, 5, 32, 8),
+    ("head_tail", 2000, 4, 2, 8, 2),
+    ("ulysses", 32768, 8, 0, 32, 8),
+    ("hybrid", 32768, 8, 4, 32, 8),
+]
+
+
+def _share(kind, S, cp, r, Hq, Hkv):
+    if kind == "contiguous":
+        return oc.contiguous_share(S, Hq, Hkv, cp, r)
+    if kind == "head_tail":
+        return oc.head_tail_share(S, Hq, Hkv, cp, r)
+    if kind == "ulysses":
+        return oc.ulysses_share(S, Hq, Hkv, cp, r)
+    return oc.hybrid_share(S, Hq, Hkv, cp, 2, r)
+
+
+def _desc_for(sh, S, Hq, Hkv, D=128, causal=True):
+    hq, hkv = len(sh["q_heads"]), len(sh["kv_heads"])
+    n = sh["chunk_len"]
+    layout = "head_tail" if len(sh["q_chunk_pos"]) == 2 else "contiguous"
+    sq = n * len(sh["q_chunk_pos"])
+    return desc(hq=hq, hkv=hkv, head_dim=D, sq_local=sq, skv=S, q_chunk_pos=sh["q_chunk_pos"],
+                layout=layout, causal=causal, q_strides=(0, 0, D), kv_strides=(0, 0, D), o_strides=(0, 0, D))
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_share_pairs_match_oracle(cfg):
+    kind, S, cp, r, Hq, Hkv = cfg
+    sh = _share(kind, S, cp, r, Hq, Hkv)
+    for causal in (True, False):
+        d = _desc_for(sh, S, Hq, Hkv, causal=causal)
+        assert cp_attn_share_pairs(d) == oc.share_pairs(sh["q_pos"], sh["kv_pos"], causal)
+
+
+def test_share_pairs_with_kv_offset_and_masked_rows():
+    # Keys start after some queries: those rows see nothing; later rows see all keys.
+    d = desc(sq_local=100, skv=50, q_chunk_pos=[10], kv_chunk_pos=[40])
+    exp = oc.share_pairs(np.arange(10, 110), np.arange(40, 90), True)
+    assert cp_attn_share_pairs(d) == exp
+
+
+def test_head_tail_tile_schedule_is_balanced():
+    """Every Head-Tail rank visits the same number of KV tiles, and the visits
+    cover every visible pair (at most one partly masked tile per row tile)."""
+    visits = set()
+    for r in range(8):
+        sh = oc.head_tail_share(32768, 32, 8, 8, r)
+        st = cp_attn_plan_stats_fwd(_desc_for(sh, 32768, 32, 8))
+        visits.add(st["kv_tile_visits"])
+        rows_per_item = st["block_q_rows"] * st["heads_per_item"]
+        area = st["kv_tile_visits"] * rows_per_item * st["block_kv_rows"]
+        pairs = oc.share_pairs(sh["q_pos"], sh["kv_pos"]) * 32
+        assert pairs <= area
+        assert area - pairs <= st["work_items"] * rows_per_item * st["block_kv_rows"]
+    assert len(visits) == 1
+
+
+def test_workspace_bytes():
+    d = desc()
+    assert cp_attn_workspace_bytes(d, False) == 0
+    rows = 1 * 8 * 500
+    assert cp_attn_workspace_bytes(d, True) == ((rows * 4 + 255) // 256) * 256 + rows * 128 * 4

@@ -1,0 +1,225 @@
+"""GPU parity of the forward share kernels against the fp64 oracle.
+
+Both sides cut their share from the same seeded global problem with their own
+code. Gates (bf16 inputs, fp32 accumulation): out max-abs <= 2e-2 and LSE
+max-abs <= 1e-3; fp32 inputs: out and LSE <= 1e-4. Mid-size cases compare every
+element and span several tiles with ragged tails; the 32K shares compare
+sampled rows (the oracle computes them one by one) plus closed forms that hold
+at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from context_causal_attention_attn_amd import cp_attn_fwd, cut_share
+from synthetic import global_problem, workload
+from tests._share_cases import oracle_rows, oracle_share, to_f64
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL_BF16, LSE_TOL_BF16 = 2e-2, 1e-3
+TOL_FP32 = 1e-4
+
+
+def run_gpu_share(prob, kind, cp, rank, U=2, causal=True, scale=None):
+    dev = torch.device("cuda")
+    q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
+    sh = cut_share(kind, q, k, v, cp, rank, ulysses=U)
+    D = q.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, causal=causal,
+                           softmax_scale=scale)
+    torch.cuda.synchronize()
+    return sh, out, lse, scale
+
+
+def check_close(out, lse, ref_out, ref_lse, out_tol, lse_tol, what):
+    o = to_f64(out)
+    l = to_f64(lse)
+    assert o.shape == ref_out.shape and l.shape == ref_lse.shape, what
+    both_inf = np.isneginf(l) & np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(l), np.isneginf(ref_lse)), f"{what}: -inf LSE rows differ"
+    err_o = np.max(np.abs(o - ref_out)) if o.size else 0.0
+    err_l = np.max(np.abs(np.where(both_inf, 0.0, l - ref_lse))) if l.size else 0.0
+    rel = np.linalg.norm(o - ref_out) / max(np.linalg.norm(ref_out), 1e-30)
+    print(f"{what}: out max-abs {err_o:.3e} rel-L2 {rel:.3e}  lse max-abs {err_l:.3e}", flush=True)
+    assert err_o <= out_tol, f"{what}: out max-abs {err_o}"
+    assert err_l <= lse_tol, f"{what}: lse max-abs {err_l}"
+    assert rel <= 1e-2, f"{what}: out relative L2 {rel}"
+
+
+# ---------------------------------------------------------------------------
+# Tiny fp32 share (whole output compared)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind,cp,rank", [("contiguous", 4, 1), ("contiguous", 4, 3),
+                                          ("head_tail", 4, 0), ("head_tail", 4, 2)])
+def test_tiny_fp32_share(kind, cp, rank):
+    spec, prob = workload("tiny_fp32_contiguous_cp4_r1")
+    S = spec["seq"]
+    sh, out, lse, scale = run_gpu_share(prob, kind, cp, rank)
+    osh = oracle_share(kind, S, spec["hq"], spec["hkv"], cp, rank)
+    ref_o, ref_l = oracle_rows(prob, osh, scale)
+    check_close(out, lse, ref_o, ref_l, TOL_FP32, TOL_FP32, f"fp32 {kind} cp{cp} r{rank}")
+
+
+# ---------------------------------------------------------------------------
+# Mid-size bf16 shares (whole output compared; several tiles, ragged tails)
+# ---------------------------------------------------------------------------
+MID = [
+    # kind, S, Hq, Hkv, D, cp, U, causal
+    ("contiguous", 2000, 8, 2, 128, 4, 2, True),
+    ("head_tail", 2000, 8, 2, 128, 4, 2, True),
+    ("ulysses", 1000, 8, 2, 128, 2, 2, True),
+    ("hybrid", 2000, 8, 2, 128, 4, 2, True),
+    ("head_tail", 1200, 4, 4, 128, 3, 2, True),     # MHA: 4 row blocks per work item
+    ("contiguous", 999, 8, 1, 128, 3, 2, True),     # G = 8: two work items per KV group
+    ("head_tail", 1000, 6, 3, 64, 2, 2, True),      # G = 2, D = 64
+    ("contiguous", 1000, 4, 2, 64, 4, 2, False),    # non-causal
+    ("head_tail", 1000, 8, 2, 128, 2, 2, False),
+]
+
+
+@pytest.mark.parametrize("case", MID, ids=[f"{c[0]}-S{c[1]}-{c[2]}x{c[3]}-D{c[4]}-cp{c[5]}-{'c' if c[7] else 'nc'}" for c in MID])
+def test_bf16_mid_shares_all_ranks(case):
+    kind, S, Hq, Hkv, D, cp, U, causal = case
+    prob = global_problem(1, Hq, Hkv, S, D, dtype="bf16", seed=1)
+    ranks = range(cp)
+    for r in ranks:
+        sh, out, lse, scale = run_gpu_share(prob, kind, cp, r, U=U, causal=causal)
+        osh = oracle_share(kind, S, Hq, Hkv, cp, r, U)
+        ref_o, ref_l = oracle_rows(prob, osh, scale, causal=causal)
+        check_close(out, lse, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, f"{case} r{r}")
+
+
+def test_bf16_batch2_and_strided_views():
+    """B = 2 and a query shard that is a strided row slice of the global tensor."""
+    prob = global_problem(2, 8, 2, 1536, 128, dtype="bf16", seed=4)
+    sh, out, lse, scale = run_gpu_share(prob, "contiguous", 3, 2)
+    assert not sh.q.is_contiguous()
+    osh = oracle_share("contiguous", 1536, 8, 2, 3, 2)
+    ref_o, ref_l = oracle_rows(prob, osh, scale)
+    check_close(out, lse, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, "B=2 strided")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+def test_empty_share_and_single_row_chunks():
+    dev = torch.device("cuda")
+    q = torch.zeros(1, 4, 0, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.randn(1, 2, 64, 128, device=dev).to(torch.bfloat16)
+    out, lse = cp_attn_fwd(q, k, k, [0])
+    assert out.shape == (1, 4, 0, 128) and lse.shape == (1, 4, 0)
+    prob = global_problem(1, 4, 2, 8, 128, dtype="bf16", seed=2)
+    for r in range(4):   # head_tail with 8 tokens over cp=4: one row per chunk
+        sh, out, lse, scale = run_gpu_share(prob, "head_tail", 4, r)
+        osh = oracle_share("head_tail", 8, 4, 2, 4, r)
+        ref_o, ref_l = oracle_rows(prob, osh, scale)
+        check_close(out, lse, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, f"S=8 head_tail r{r}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_keys_after_queries_give_empty_rows(dtype):
+    """K/V starting at global position 300: query rows before it see no key
+    (out = 0, LSE = -inf); the rest see a growing prefix."""
+    import oracle.cp_share as oc
+    prob = global_problem(1, 4, 2, 512, 64, dtype=dtype, seed=3)
+    dev = torch.device("cuda")
+    q = prob.q[:, :, :400].to(dev)
+    k = prob.k[:, :, :200].to(dev)
+    v = prob.v[:, :, :200].to(dev)
+    out, lse = cp_attn_fwd(q, k, v, [100], kv_chunk_pos=[300], softmax_scale=0.125)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oc.attention_rows(to_f64(prob.q[:, :, :400]), to_f64(prob.k[:, :, :200]),
+                                     to_f64(prob.v[:, :, :200]), np.arange(100, 500),
+                                     np.arange(300, 500), 0.125, True)
+    tol = (OUT_TOL_BF16, LSE_TOL_BF16) if dtype == "bf16" else (TOL_FP32, TOL_FP32)
+    check_close(out, lse, ref_o, ref_l, *tol, f"kv offset {dtype}")
+    assert torch.all(out[:, :, :200] == 0)
+    # No keys at all.
+    out, lse = cp_attn_fwd(q, k[:, :, :0], v[:, :, :0], [0])
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_invalid_inputs_raise_before_launch():
+    dev = torch.device("cuda")
+    q = torch.zeros(1, 4, 64, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, 3, 64, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        cp_attn_fwd(q, k, k, [0])                                  # hq % hkv
+    k = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        cp_attn_fwd(q, k, k, [0, 16], layout="head_tail")          # chunks overlap
+    with pytest.raises(ValueError):
+        cp_attn_fwd(q, k, k.float(), [0])                          # dtype mismatch
+
+
+# ---------------------------------------------------------------------------
+# 32K shares: sampled rows against the oracle, closed forms, determinism
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def big_problem():
+    spec, prob = workload("colossal_cp8_r7_s32k_gqa32x8_d128")
+    return spec, prob
+
+
+def sample_rows(n_local, chunks, rng, per=24):
+    """Sampled local rows: chunk edges, tile edges and random rows."""
+    rows = set()
+    L = n_local // chunks
+    for c in range(chunks):
+        base = c * L
+        for r in (0, 1, 31, 32, 63, 64, 127, 128, L - 1, L - 2):
+            if 0 <= r < L:
+                rows.add(base + r)
+        rows.update((base + rng.integers(0, L, per)).tolist())
+    return np.array(sorted(rows))
+
+
+FULL = [("contiguous", 8, 7), ("head_tail", 8, 0), ("head_tail", 8, 3), ("head_tail", 8, 7),
+        ("ulysses", 8, 0), ("hybrid", 8, 4)]
+
+
+@pytest.mark.parametrize("kind,cp,rank", FULL)
+def test_full_size_share_sampled_rows(big_problem, kind, cp, rank):
+    spec, prob = big_problem
+    S, Hq, Hkv = spec["seq"], spec["hq"], spec["hkv"]
+    sh, out, lse, scale = run_gpu_share(prob, kind, cp, rank)
+    osh = oracle_share(kind, S, Hq, Hkv, cp, rank, 2)
+    rng = np.random.default_rng(rank)
+    rows = sample_rows(out.shape[2], len(osh["q_chunk_pos"]), rng)
+    hq_loc = out.shape[1]
+    heads = sorted({0, 1, hq_loc // 2, hq_loc - 1})
+    ref_o, ref_l = oracle_rows(prob, osh, scale, rows=rows, heads=heads)
+    r_t = torch.from_numpy(rows).to(out.device)
+    got_o = out[:, heads][:, :, r_t]
+    got_l = lse[:, heads][:, :, r_t]
+    check_close(got_o, got_l, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, f"32K {kind} r{rank}")
+    # Deterministic: a second launch gives the same bits.
+    out2, lse2 = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("kind,cp,rank", [("contiguous", 8, 7), ("head_tail", 8, 2)])
+def test_full_size_closed_form_uniform(big_problem, kind, cp, rank):
+    """q = 0 gives uniform weights over the visible prefix: out = prefix mean
+    of v and LSE = ln(pos + 1), checked on every row of the 32K share."""
+    spec, prob = big_problem
+    dev = torch.device("cuda")
+    zq = torch.zeros_like(prob.q[:, :8])
+    sh = cut_share(kind, zq.to(dev), prob.k[:, :2].to(dev), prob.v[:, :2].to(dev), cp, rank)
+    out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout)
+    torch.cuda.synchronize()
+    vcs = torch.cumsum(prob.v[:, :2].double(), dim=2)
+    pos = torch.cat([torch.arange(a, b) for a, b in sh.rows])
+    mean = vcs[:, :, pos] / (pos.double() + 1)[None, None, :, None]
+    exp_o = mean.repeat_interleave(4, dim=1)
+    exp_l = torch.log(pos.double() + 1).expand(1, 8, -1)
+    err_o = (out.double().cpu() - exp_o).abs().max().item()
+    err_l = (lse.double().cpu() - exp_l).abs().max().item()
+    print(f"closed form {kind} r{rank}: out {err_o:.3e} lse {err_l:.3e}")
+    assert err_o <= OUT_TOL_BF16 and err_l <= LSE_TOL_BF16
