@@ -160,7 +160,7 @@ def main():
 
     lib = _lib.load()
     spec, prob = workload(args.workload, seed=0)
-    with_bwd = False
+    with_bwd = True
     if with_bwd and prob.dout is None:
         from synthetic import global_problem
         prob = global_problem(spec["batch"], spec["hq"], spec["hkv"], spec["seq"], spec["head_dim"],
@@ -174,7 +174,7 @@ def main():
     fwd_tflops = res["f_fwd"] / (fwd_avg * 1e-3) / 1e12
     bwd_tflops = res["f_bwd"] / (bwd_avg * 1e-3) / 1e12 if bwd_avg else None
     if bwd_avg > fwd_avg:
-        dom, achieved = "cp_attn_bwd kernels", bwd_tflops
+        dom, achieved = "cp_attn_bwd (bwd_main_kernel<128> + pre/convert)", bwd_tflops
     else:
         dom, achieved = "fwd_bf16_kernel<128,1>", fwd_tflops
     line = {
@@ -207,15 +207,23 @@ def main():
     if args.detail:
         detail = {}
         for name, sp in WORKLOADS.items():
-            if sp["dtype"] != "bf16" or sp.get("backward"):
+            if sp["dtype"] != "bf16":
                 continue
+            bw = bool(sp.get("backward"))
             _, pr = workload(name, seed=0)
             for r in sp["ranks"]:
-                rr = time_share(sp, pr, r, max(5, args.steps // 2), 2, False)
+                rr = time_share(sp, pr, r, max(5, args.steps // 2), 2, bw)
                 avg = sum(rr["fwd_ms"]) / len(rr["fwd_ms"])
                 tf = rr["f_fwd"] / (avg * 1e-3) / 1e12
-                detail[f"{name}/r{r}"] = {"fwd_ms": round(avg, 4), "fwd_tflops": round(tf, 2),
-                                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+                ent = {"fwd_ms": round(avg, 4), "fwd_tflops": round(tf, 2),
+                       "fwd_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+                if bw:
+                    bavg = sum(rr["bwd_ms"]) / len(rr["bwd_ms"])
+                    btf = rr["f_bwd"] / (bavg * 1e-3) / 1e12
+                    ent.update({"bwd_ms": round(bavg, 4), "bwd_tflops": round(btf, 2),
+                                "bwd_frac": round(btf / PEAK_BF16_TFLOPS, 4)})
+                detail[f"{name}/r{r}"] = ent
+            del pr
         line["detail"] = detail
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(spec, prob)

@@ -105,6 +105,26 @@ void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   }
 }
 
+void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
+  memset(p, 0, sizeof(*p));
+  p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
+  p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
+  p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
+  p->kv_pos0 = s.kv_pos0;
+  p->batch = d->batch;
+  p->hq = d->hq;
+  p->hkv = d->hkv;
+  p->group = d->hq / d->hkv;
+  p->sq = (int32_t)d->sq_local;
+  p->skv = (int32_t)d->skv;
+  p->chunk_len = (int32_t)s.chunk_len;
+  p->n_q_chunks = s.n_q_chunks;
+  p->causal = d->causal;
+  p->scale = d->softmax_scale;
+  p->scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  for (int i = 0; i < s.n_q_chunks; ++i) p->chunk_pos[i] = s.chunk_pos[i];
+}
+
 int64_t fwd_grid_size(const FwdParams &p) {
   return (int64_t)p.n_head_packs * p.n_q_chunks * p.tiles_per_chunk;
 }
@@ -254,15 +274,34 @@ int32_t cp_attn_fwd(const cp_attn_desc *d, const void *q, const void *k, const v
   return e == 0 ? CP_ATTN_OK : CP_ATTN_ERR_HIP;
 }
 
-}  // extern "C"
-
-extern "C" int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
-                               const void *out, const float *lse, const void *dout, void *dq,
-                               float *dk, float *dv, void *workspace, size_t workspace_bytes,
-                               void *stream) {
-  (void)q; (void)k; (void)v; (void)out; (void)lse; (void)dout; (void)dq; (void)dk; (void)dv;
-  (void)workspace; (void)workspace_bytes; (void)stream;
+int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
+                    const void *out, const float *lse, const void *dout, void *dq, float *dk,
+                    float *dv, void *workspace, size_t workspace_bytes, void *stream) {
   int32_t st = validate(d);
   if (st) return st;
-  return CP_ATTN_ERR_UNSUPPORTED;
+  size_t need = 0;
+  cp_attn_workspace_bytes(d, 1, &need);
+  if (d->sq_local > 0 && (!q || !out || !lse || !dout || !dq)) return CP_ATTN_ERR_NULL_PTR;
+  if (d->skv > 0 && (!k || !v || !dk || !dv)) return CP_ATTN_ERR_NULL_PTR;
+  if (d->sq_local == 0 && d->skv == 0) return CP_ATTN_OK;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CP_ATTN_ERR_WORKSPACE;
+  const void *ptrs16[] = {q, out, dout, dq, k, v, dk, dv, workspace};
+  for (const void *ptr : ptrs16)
+    if (ptr && !aligned16(ptr)) return CP_ATTN_ERR_ALIGNMENT;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return CP_ATTN_ERR_ALIGNMENT;
+  Share s;
+  make_share(d, &s);
+  BwdParams p;
+  fill_bwd_params(d, s, &p);
+  p.q = q; p.k = k; p.v = v; p.out = out; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  const size_t rows = (size_t)d->batch * d->hq * (size_t)d->sq_local;
+  const size_t delta_bytes = (rows * 4 + 255) & ~(size_t)255;
+  p.delta = static_cast<float *>(workspace);
+  p.dq_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + delta_bytes);
+  const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream)
+                                           : launch_bwd_fp32(p, d->head_dim, stream);
+  return e == 0 ? CP_ATTN_OK : CP_ATTN_ERR_HIP;
 }
+
+}  // extern "C"

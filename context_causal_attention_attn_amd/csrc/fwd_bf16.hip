@@ -28,51 +28,15 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "gfx950_common.h"
 #include "plan.h"
 
 namespace cpattn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
 constexpr int BN = kFwdBlockKV;
 constexpr int NT = kFwdWaves * 64;
-constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
-
-// LDS tile of `rows` x D bf16, row-major, with the 16-byte chunks of each row
-// XOR-swizzled so that the A-operand reads (16 consecutive rows, same chunk)
-// and the transpose reads (4 rows x 64 contiguous bytes per half-wavefront)
-// spread over all banks.
-template <int D>
-struct Tile {
-  static constexpr int NC = D / 8;
-  __device__ static __forceinline__ int swz(int row) {
-    return ((row & 3) * (NC / 4) + ((row >> 2) & (NC / 4 - 1))) & (NC - 1);
-  }
-  __device__ static __forceinline__ int chunk_off(int row, int c) {
-    return row * D + ((c ^ swz(row)) << 3);
-  }
-  __device__ static __forceinline__ int elem_off(int row, int d) {
-    return chunk_off(row, d >> 3) + (d & 7);
-  }
-};
-
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int D, int RB>
 __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
@@ -179,10 +143,6 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   float l_part = 0.0f;      // this lane's partial row sum (its half of the keys)
   const float c = p.scale_log2;
 
-  // Lane-constant pieces of the transpose-read addresses of V^T.
-  const int tr_key = 4 * half + ((lane & 15) >> 2);             // + 16*kstep (+8)
-  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);     // + 32*db
-
   if (ntiles > 0) {
     gload(0);
     swrite(0);
@@ -206,7 +166,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + T::chunk_off(kb * 32 + col, 2 * s + half));
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
         }
       }
       const bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
@@ -252,17 +212,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-          const int d = 32 * db + tr_d;
-          const int r0 = 16 * k2 + tr_key;
-          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4 *)(vs + T::elem_off(r0, d)));
-          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4 *)(vs + T::elem_off(r0 + 8, d)));
-          const i16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[k2],
-                                                            oacc[db], 0, 0, 0);
-        }
+        for (int k2 = 0; k2 < 4; ++k2)
+          oacc[db] = mfma32(tr_operand<D>(vs, 16 * k2, 32 * db, lane), pf[k2], oacc[db]);
     }
     if (kt + 1 < ntiles) swrite(st ^ 1);
     __syncthreads();

@@ -1,0 +1,75 @@
+// Vector types, LDS tile addressing and wavefront helpers shared by the
+// gfx950 share kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace cpattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Row-major LDS tile of bf16 rows of W elements whose 16-byte chunks are
+// XOR-swizzled by row: 16 consecutive rows reading the same chunk (MFMA
+// A/B operand reads) and 4 rows x 64 contiguous bytes (transpose reads) both
+// spread over the banks.
+template <int W>
+struct Tile {
+  static constexpr int NC = W / 8;
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (NC >= 16) {
+      return ((row & 3) * (NC / 4) + ((row >> 2) & (NC / 4 - 1))) & (NC - 1);
+    } else if constexpr (NC == 8) {
+      return ((row & 3) * 2 + ((row >> 2) & 1)) & 7;
+    } else {
+      return (row >> 1) & (NC - 1);
+    }
+  }
+  __device__ static __forceinline__ int chunk_off(int row, int c) {
+    return row * W + ((c ^ swz(row)) << 3);
+  }
+  __device__ static __forceinline__ int elem_off(int row, int col) {
+    return chunk_off(row, col >> 3) + (col & 7);
+  }
+};
+
+// Two transpose reads (ds_read_b64_tr_b16) forming one 8 x bf16 MFMA operand
+// whose contraction index runs down `rows` of a row-major tile: lane l of the
+// wavefront gets column (col0 + 16*((l>>4)&1) + (l&15)) at the 8 rows
+// {r0 + 4*(l>>5) + e, r0 + 8 + 4*(l>>5) + e : e = 0..3}, matching the
+// row order of a 32x32 MFMA accumulator's register blocks.
+template <int W>
+__device__ __forceinline__ bf16x8 tr_operand(const __bf16 *tile, int r0, int col0, int lane) {
+  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + Tile<W>::elem_off(row, col)));
+  const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + Tile<W>::elem_off(row + 8, col)));
+  const i16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, a);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace cpattn

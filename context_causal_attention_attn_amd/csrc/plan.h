@@ -67,11 +67,48 @@ int32_t make_share(const cp_attn_desc *d, Share *s);
 inline int fwd_heads_per_item(int g) { return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1; }
 inline int fwd_block_rows(int g) { return kWaveRows * (kFwdWaves / fwd_heads_per_item(g)); }
 
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+// A backward work item is one tile of kBwdBlockKV keys of one KV head: it
+// keeps that tile's dK/dV in registers and visits every query tile (of every
+// head of the GQA group, of every chunk) that can see one of its keys.
+constexpr int kBwdBlockKV = 128;
+constexpr int kBwdBlockQ = 32;
+
+struct BwdParams {
+  const void *q;
+  const void *k;
+  const void *v;
+  const void *out;
+  const void *dout;
+  const float *lse;
+  float *delta;                 // workspace [B, Hq, Sq]
+  float *dq_acc;                // workspace [B, Hq, Sq, D] fp32
+  void *dq;
+  float *dk;                    // [B, Hkv, Skv, D]
+  float *dv;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t kv_sb, kv_sh, kv_ss;
+  int64_t o_sb, o_sh, o_ss;     // out, dout and dq
+  int64_t kv_pos0;
+  int32_t batch, hq, hkv, group;
+  int32_t sq, skv;
+  int32_t chunk_len, n_q_chunks;
+  int32_t causal;
+  float scale;
+  float scale_log2;
+  int64_t chunk_pos[kMaxQChunks];   // local chunk order
+};
+
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p);
+void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p);
 int64_t fwd_grid_size(const FwdParams &p);
 
 // Launchers (defined with their kernels); return a hipError_t as int.
 int launch_fwd_bf16(const FwdParams &p, int head_dim, void *stream);
 int launch_fwd_fp32(const FwdParams &p, int head_dim, void *stream);
+int launch_bwd_bf16(const BwdParams &p, int head_dim, void *stream);
+int launch_bwd_fp32(const BwdParams &p, int head_dim, void *stream);
 
 }  // namespace cpattn

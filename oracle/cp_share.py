@@ -176,7 +176,7 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
 # ----------------------------------------------------------------------------
 def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
                        causal: bool = True, kv_index: Optional[np.ndarray] = None,
-                       row_block: int = 1024):
+                       row_block: int = 1024, want_dq: bool = True):
     """Gradients of ``sum(dout * out)`` for one share.
 
     Returns (dq [B, Hq, Sq, D], dk, dv) in float64, where dk/dv are this share's
@@ -196,6 +196,9 @@ def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
         dQ_i  = scale * sum_j dS_ij k_j
         dK_j  = scale * sum_i dS_ij q_i
     ``out`` and ``LSE`` are recomputed here in float64 with ``attention_rows``.
+    Rows of dQ are independent of each other, so dQ of a subset of rows is
+    obtained by passing only those rows; dK/dV need every row and are computed
+    only for the keys in ``kv_index``. ``want_dq=False`` skips dQ (zeros).
     """
     q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
     q_pos = np.asarray(q_pos, dtype=np.int64)
@@ -207,26 +210,33 @@ def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
     dq = np.zeros_like(q)
     dk = np.zeros((B, Hkv, sel.size, D))
     dv = np.zeros((B, Hkv, sel.size, D))
+
+    def grads(qb, dob, delta, lse_b, has, pos_b, kk, vv, kpos):
+        """P and dS of a block of rows against the keys kk/vv at positions kpos."""
+        vis = visible(pos_b, kpos, causal) & has[:, None]
+        s = scale * (qb @ kk.T)
+        lse_safe = np.where(has, lse_b, 0.0)
+        p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
+        dp = dob @ vv.T
+        return p, p * (dp - delta[:, None])
+
     for b in range(B):
         for h in range(Hq):
             hk = kv_head_of(h, Hq, Hkv)
             for r0 in range(0, Sq, row_block):
                 r1 = min(Sq, r0 + row_block)
-                rows_lse = lse[b, h, r0:r1]
-                has = np.isfinite(rows_lse)
-                lse_safe = np.where(has, rows_lse, 0.0)
+                lse_b = lse[b, h, r0:r1]
+                has = np.isfinite(lse_b)
                 delta = np.sum(dout[b, h, r0:r1] * out[b, h, r0:r1], axis=1)
-                # dQ needs every visible key of the row.
-                vis = visible(q_pos[r0:r1], kv_pos, causal) & has[:, None]
-                s = scale * (q[b, h, r0:r1] @ k[b, hk].T)
-                p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
-                dp = dout[b, h, r0:r1] @ v[b, hk].T
-                ds = p * (dp - delta[:, None])
-                dq[b, h, r0:r1] = scale * (ds @ k[b, hk])
-                # dK/dV only for the requested key rows.
-                ds_sel, p_sel = ds[:, sel], p[:, sel]
-                dv[b, hk] += p_sel.T @ dout[b, h, r0:r1]
-                dk[b, hk] += scale * (ds_sel.T @ q[b, h, r0:r1])
+                qb, dob = q[b, h, r0:r1], dout[b, h, r0:r1]
+                if want_dq:
+                    _, ds = grads(qb, dob, delta, lse_b, has, q_pos[r0:r1], k[b, hk], v[b, hk], kv_pos)
+                    dq[b, h, r0:r1] = scale * (ds @ k[b, hk])
+                if sel.size:
+                    p_sel, ds_sel = grads(qb, dob, delta, lse_b, has, q_pos[r0:r1],
+                                          k[b, hk][sel], v[b, hk][sel], kv_pos[sel])
+                    dv[b, hk] += p_sel.T @ dob
+                    dk[b, hk] += scale * (ds_sel.T @ qb)
     return dq, dk, dv
 
 

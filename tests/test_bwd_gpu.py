@@ -1,0 +1,168 @@
+"""GPU parity of the backward share kernels against the fp64 oracle.
+
+The GPU backward consumes the GPU forward's own out and LSE (as a training step
+would); the oracle recomputes everything in float64 from the same seeded
+inputs. Gate: relative L2 error <= 1e-2 for dQ, dK and dV each (fp32 inputs:
+1e-4). Mid-size shares compare whole tensors; the 32K Head-Tail backward
+(B = 2, ranks 0 and 7) compares sampled dQ rows and the dK/dV rows of sampled
+keys of one KV head, plus the exact zeros of keys no local query can see.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.cp_share as oc
+from context_causal_attention_attn_amd import cp_attn_bwd, cp_attn_fwd, cut_share
+from synthetic import global_problem, workload
+from tests._share_cases import oracle_share, to_f64
+
+pytestmark = pytest.mark.gpu
+
+REL_BF16 = 1e-2
+REL_FP32 = 1e-4
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def gpu_share_grads(prob, kind, cp, rank, U=2, causal=True):
+    dev = torch.device("cuda")
+    q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
+    sh = cut_share(kind, q, k, v, cp, rank, ulysses=U)
+    scale = 1.0 / math.sqrt(q.shape[-1])
+    out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, causal=causal,
+                           softmax_scale=scale)
+    dout = sh.take_rows(prob.dout.to(dev))
+    dq, dk, dv = cp_attn_bwd(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, layout=sh.layout,
+                             causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return sh, dq, dk, dv, scale
+
+
+def oracle_share_grads(prob, osh, scale, causal=True):
+    qh, kh = osh["q_heads"], osh["kv_heads"]
+    rows = torch.from_numpy(osh["q_pos"])
+    q = to_f64(prob.q[:, qh][:, :, rows])
+    do = to_f64(prob.dout[:, qh][:, :, rows])
+    k, v = to_f64(prob.k[:, kh]), to_f64(prob.v[:, kh])
+    return oc.attention_rows_bwd(q, k, v, do, osh["q_pos"], osh["kv_pos"], scale, causal)
+
+
+def check_grads(got, ref, tol, what):
+    errs = {n: rel_l2(to_f64(g), r) for n, g, r in zip(("dq", "dk", "dv"), got, ref)}
+    print(f"{what}: " + "  ".join(f"{n} rel-L2 {e:.3e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= tol, f"{what}: {n} relative L2 {e}"
+
+
+@pytest.mark.parametrize("kind,cp,rank", [("contiguous", 4, 1), ("contiguous", 4, 3), ("head_tail", 4, 0),
+                                          ("head_tail", 4, 3)])
+def test_tiny_fp32_backward(kind, cp, rank):
+    spec, _ = workload("tiny_fp32_contiguous_cp4_r1")
+    prob = global_problem(1, spec["hq"], spec["hkv"], spec["seq"], spec["head_dim"], "fp32", 0, with_dout=True)
+    sh, dq, dk, dv, scale = gpu_share_grads(prob, kind, cp, rank)
+    osh = oracle_share(kind, spec["seq"], spec["hq"], spec["hkv"], cp, rank)
+    check_grads((dq, dk, dv), oracle_share_grads(prob, osh, scale), REL_FP32, f"fp32 {kind} r{rank}")
+
+
+MID = [
+    # kind, S, Hq, Hkv, D, cp, U, causal
+    ("contiguous", 2000, 8, 2, 128, 4, 2, True),
+    ("head_tail", 2000, 8, 2, 128, 4, 2, True),
+    ("ulysses", 1000, 8, 2, 128, 2, 2, True),
+    ("hybrid", 2000, 8, 2, 128, 4, 2, True),
+    ("head_tail", 1200, 4, 4, 128, 3, 2, True),
+    ("contiguous", 999, 8, 1, 128, 3, 2, True),
+    ("head_tail", 1000, 6, 3, 64, 2, 2, True),
+    ("contiguous", 1000, 4, 2, 64, 4, 2, False),
+    ("head_tail", 1000, 8, 2, 128, 2, 2, False),
+]
+
+
+@pytest.mark.parametrize("case", MID, ids=[f"{c[0]}-S{c[1]}-{c[2]}x{c[3]}-D{c[4]}-cp{c[5]}-{'c' if c[7] else 'nc'}" for c in MID])
+def test_bf16_mid_backward_all_ranks(case):
+    kind, S, Hq, Hkv, D, cp, U, causal = case
+    prob = global_problem(1, Hq, Hkv, S, D, dtype="bf16", seed=5, with_dout=True)
+    dk_sum = None
+    for r in range(cp):
+        sh, dq, dk, dv, scale = gpu_share_grads(prob, kind, cp, r, U=U, causal=causal)
+        osh = oracle_share(kind, S, Hq, Hkv, cp, r, U)
+        ref = oracle_share_grads(prob, osh, scale, causal)
+        check_grads((dq, dk, dv), ref, REL_BF16, f"{case} r{r}")
+        if kind in ("contiguous", "head_tail") and causal:
+            # Keys after every local query: partial dK/dV rows are exact zeros.
+            last = int(osh["q_pos"].max())
+            assert torch.all(dk[:, :, last + 1:] == 0) and torch.all(dv[:, :, last + 1:] == 0)
+            dk_sum = dk.double().cpu() if dk_sum is None else dk_sum + dk.double().cpu()
+    if dk_sum is not None:
+        # reduce-scatter(sum) semantics: the rank partials add up to the full dK.
+        full = oc.contiguous_share(S, Hq, Hkv, 1, 0)
+        ref_full = oracle_share_grads(prob, full, 1.0 / math.sqrt(D), causal)
+        assert rel_l2(dk_sum.numpy(), ref_full[1]) <= REL_BF16
+
+
+def test_backward_edge_cases():
+    """Keys after some queries (rows with no visible key get dQ = 0) and a
+    head_tail share of single-row chunks."""
+    prob = global_problem(1, 4, 2, 512, 64, dtype="bf16", seed=6, with_dout=True)
+    dev = torch.device("cuda")
+    q, k, v = prob.q[:, :, :400].to(dev), prob.k[:, :, :200].to(dev), prob.v[:, :, :200].to(dev)
+    do = prob.dout[:, :, :400].to(dev)
+    out, lse = cp_attn_fwd(q, k, v, [100], kv_chunk_pos=[300], softmax_scale=0.125)
+    dq, dk, dv = cp_attn_bwd(q, k, v, out, lse, do, [100], kv_chunk_pos=[300], softmax_scale=0.125)
+    torch.cuda.synchronize()
+    ref = oc.attention_rows_bwd(to_f64(prob.q[:, :, :400]), to_f64(prob.k[:, :, :200]),
+                                to_f64(prob.v[:, :, :200]), to_f64(prob.dout[:, :, :400]),
+                                np.arange(100, 500), np.arange(300, 500), 0.125, True)
+    check_grads((dq, dk, dv), ref, REL_BF16, "kv offset")
+    assert torch.all(dq[:, :, :200] == 0)
+    prob = global_problem(1, 4, 2, 8, 128, dtype="bf16", seed=2, with_dout=True)
+    for r in range(4):
+        sh, dq, dk, dv, scale = gpu_share_grads(prob, "head_tail", 4, r)
+        osh = oracle_share("head_tail", 8, 4, 2, 4, r)
+        check_grads((dq, dk, dv), oracle_share_grads(prob, osh, scale), REL_BF16, f"S=8 r{r}")
+
+
+@pytest.fixture(scope="module")
+def htbwd_problem():
+    return workload("head_tail_bwd_b2_cp8_s32k_gqa32x8_d128")
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_full_size_head_tail_backward_sampled(htbwd_problem, rank):
+    spec, prob = htbwd_problem
+    S, Hq, Hkv, D = spec["seq"], spec["hq"], spec["hkv"], spec["head_dim"]
+    sh, dq, dk, dv, scale = gpu_share_grads(prob, "head_tail", spec["cp"], rank)
+    osh = oracle_share("head_tail", S, Hq, Hkv, spec["cp"], rank)
+    rng = np.random.default_rng(rank)
+    b, hk = 1, 5
+    heads = list(range(hk * 4, hk * 4 + 4))
+    # dQ on sampled rows (every head of the group): exact row by row.
+    rows = np.unique(np.concatenate([[0, 31, 32, 2047, 2048, 4095], rng.integers(0, 4096, 40)]))
+    pos = osh["q_pos"][rows]
+    qd = to_f64(prob.q[b:b + 1, heads][:, :, torch.from_numpy(pos)])
+    dod = to_f64(prob.dout[b:b + 1, heads][:, :, torch.from_numpy(pos)])
+    kd, vd = to_f64(prob.k[b:b + 1, hk:hk + 1]), to_f64(prob.v[b:b + 1, hk:hk + 1])
+    ref_dq, _, _ = oc.attention_rows_bwd(qd, kd, vd, dod, pos, osh["kv_pos"], scale, True,
+                                         kv_index=np.array([], dtype=np.int64))
+    got_dq = to_f64(dq[b:b + 1, heads][:, :, torch.from_numpy(rows).cuda()])
+    e_dq = rel_l2(got_dq, ref_dq)
+    # dK/dV of sampled keys: needs every local row of the group's heads.
+    keys = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 2048], rng.integers(0, S, 40)]))
+    qa = to_f64(prob.q[b:b + 1, heads][:, :, torch.from_numpy(osh["q_pos"])])
+    doa = to_f64(prob.dout[b:b + 1, heads][:, :, torch.from_numpy(osh["q_pos"])])
+    _, ref_dk, ref_dv = oc.attention_rows_bwd(qa, kd, vd, doa, osh["q_pos"], osh["kv_pos"], scale, True,
+                                              kv_index=keys, want_dq=False)
+    kt = torch.from_numpy(keys).cuda()
+    e_dk = rel_l2(to_f64(dk[b:b + 1, hk:hk + 1][:, :, kt]), ref_dk)
+    e_dv = rel_l2(to_f64(dv[b:b + 1, hk:hk + 1][:, :, kt]), ref_dv)
+    print(f"32K head_tail bwd r{rank}: dq {e_dq:.3e} dk {e_dk:.3e} dv {e_dv:.3e}", flush=True)
+    assert e_dq <= REL_BF16 and e_dk <= REL_BF16 and e_dv <= REL_BF16
+    last = int(osh["q_pos"].max())
+    assert torch.all(dk[:, :, last + 1:] == 0) and torch.all(dv[:, :, last + 1:] == 0)
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()

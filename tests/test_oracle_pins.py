@@ -371,6 +371,15 @@ def test_kv_index_subset_of_dk_dv():
     _, dk2, dv2 = oc.attention_rows_bwd(q, k, v, do, pos, pos, 0.5, kv_index=sel)
     np.testing.assert_allclose(dk2, dk[:, :, sel], atol=1e-14)
     np.testing.assert_allclose(dv2, dv[:, :, sel], atol=1e-14)
+    dq3, dk3, _ = oc.attention_rows_bwd(q, k, v, do, pos, pos, 0.5, kv_index=sel, want_dq=False)
+    assert np.all(dq3 == 0)
+    np.testing.assert_allclose(dk3, dk[:, :, sel], atol=1e-14)
+    # dQ of a subset of rows, computed from those rows alone.
+    dq_all, _, _ = oc.attention_rows_bwd(q, k, v, do, pos, pos, 0.5)
+    rows = np.array([3, 11, 19])
+    dq4, _, _ = oc.attention_rows_bwd(q[:, :, rows], k, v, do[:, :, rows], pos[rows], pos, 0.5,
+                                      kv_index=np.array([], dtype=np.int64))
+    np.testing.assert_allclose(dq4, dq_all[:, :, rows], atol=1e-14)
 
 
 # ----------------------------------------------------------------------------
