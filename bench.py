@@ -65,7 +65,7 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd):
     f_bwd = 10.0 * D * B * Hq * pairs
     out = torch.empty(sh.q.shape, dtype=sh.q.dtype, device=dev)
     lse = torch.empty(sh.q.shape[:3], dtype=torch.float32, device=dev)
-    dout = sh.take_rows(prob.dout.to(dev)) if (with_bwd and prob.dout is not None) else None
+    dout = sh.take_rows(prob.dout.to(dev)).contiguous() if (with_bwd and prob.dout is not None) else None
 
     def fwd():
         api.cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,

@@ -9,7 +9,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libcpattn.so")
+# CPATTN_LIB may point at another build of the same library (e.g. one compiled
+# with different tuning flags); by default the in-tree build is used.
+LIB_PATH = os.environ.get("CPATTN_LIB") or os.path.join(HERE, "libcpattn.so")
 
 ABI_VERSION = 1
 MAX_Q_CHUNKS = 16

@@ -52,23 +52,28 @@ def _compile(hipcc: str, src: str, extra):
     return obj
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile and link the library; returns its path. Always recompiles."""
+def build(verbose: bool = False, extra_flags=(), out_path: str = None, build_dir: str = None) -> str:
+    """Compile and link the library; returns its path. Always recompiles.
+    ``extra_flags``/``out_path``/``build_dir`` build a variant elsewhere."""
     hipcc = _hipcc()
+    global BUILD_DIR
+    lib_path = out_path or LIB_PATH
+    if build_dir:
+        BUILD_DIR = build_dir
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")), 16)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(hipcc, s, list(extra_flags)), srcs))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources", file=sys.stderr)
-    return LIB_PATH
+        print(f"built {lib_path} from {len(srcs)} sources", file=sys.stderr)
+    return lib_path
 
 
 if __name__ == "__main__":

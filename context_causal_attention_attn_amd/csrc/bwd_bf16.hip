@@ -9,20 +9,22 @@
 //     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - Delta),  Delta = rowsum(dO o O),
 //     dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three launches:
-//  1. bwd_pre: Delta for every local row, and the fp32 dQ accumulator zeroed;
-//  2. bwd_main: one workgroup (4 wavefronts) per 128-key tile of one KV head.
-//     Each wavefront owns 32 keys and keeps their K and V rows (MFMA B
-//     operands) and their dK^T/dV^T accumulators in registers, while the
-//     workgroup streams 32-row query tiles -- of every head of the GQA group
-//     and every chunk of the share -- that can see one of its keys. Per tile:
-//     S = Q K^T and dP = dO V^T (lane = key column), P and dS in registers,
-//     dV^T += dO^T P and dK^T += Q^T dS with dO^T/Q^T read by LDS transpose
-//     reads; dS^T goes once through LDS so that dQ^T = K^T dS^T (K^T resident
-//     per wavefront) sums over the 128 keys, and is added to the fp32 dQ
-//     accumulator with atomics. Query tiles wholly before the key tile are
-//     never visited; tiles crossing the diagonal are masked element-wise.
-//  3. bwd_dq_convert: dQ = scale * accumulator, rounded to bf16.
+// Three launches, no atomics:
+//  1. bwd_pre: Delta for every local row.
+//  2. bwd_dkdv (key-stationary): one workgroup of 4 wavefronts per 128-key
+//     tile of one KV head. Each wavefront owns 32 keys, keeps their K and V
+//     rows (MFMA B operands) and their dK^T/dV^T accumulators in registers,
+//     and streams the 32-row query tiles -- of every head of the GQA group and
+//     every chunk -- that can see one of its keys: S = Q K^T and dP = dO V^T
+//     with the key as the lane's column, P and dS in registers, then
+//     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read by LDS
+//     transpose reads. Query tiles wholly before the keys are never visited.
+//  3. bwd_dq (query-stationary, scheduled like the forward): the transposed
+//     tiles S^T = K Q^T and dP^T = V dO^T put the query in the lane, so P^T and
+//     dS^T come from the saved LSE and Delta with per-lane scalars and feed
+//     dQ^T += K^T dS^T straight from registers (K^T by transpose reads).
+// Recomputing S and dP in the second kernel costs two extra contractions per
+// visible tile but removes every cross-workgroup reduction of dQ.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -32,17 +34,18 @@
 namespace cpattn {
 namespace {
 
-constexpr int BK = kBwdBlockKV;   // keys per workgroup
-constexpr int BQ = kBwdBlockQ;    // query rows per step
+constexpr int BK = kBwdBlockKV;   // keys per key-stationary workgroup
+constexpr int BQ = kBwdBlockQ;    // query rows per step of that workgroup
+constexpr int BN = kDqBlockKV;    // keys per tile of the query-stationary kernel
 constexpr int NT = 256;
 
 // ---------------------------------------------------------------------------
-// 1. Delta = rowsum(dO o O) and dQ accumulator = 0. 16 lanes per row.
+// 1. Delta = rowsum(dO o O), 16 lanes per row.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
-  constexpr int LPR = 16;                  // lanes per row
-  constexpr int EPL = D / LPR;             // elements per lane (8 or 4)
+  constexpr int LPR = 16;
+  constexpr int EPL = D / LPR;
   const int64_t rows = (int64_t)p.batch * p.hq * p.sq;
   const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
   const int part = threadIdx.x % LPR;
@@ -56,9 +59,6 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
     const __bf16 *g = static_cast<const __bf16 *>(p.dout) + off;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
-    float *dqa = p.dq_acc + row * D + part * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; e += 4) *reinterpret_cast<f32x4 *>(dqa + e) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
@@ -66,120 +66,70 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = scale * accumulator -> bf16
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256) bwd_dq_convert_kernel(const BwdParams p) {
-  constexpr int VPR = D / 4;  // float4 vectors per row
-  const int64_t n = (int64_t)p.batch * p.hq * p.sq * VPR;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int64_t row = i / VPR;
-  const int c = (int)(i % VPR);
-  const int64_t bh = row / p.sq;
-  const int r = (int)(row % p.sq);
-  const int b = (int)(bh / p.hq), h = (int)(bh % p.hq);
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p.dq_acc + row * D + 4 * c);
-  bf16x4 o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = (__bf16)(a[e] * p.scale);
-  *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(p.dq) + b * p.o_sb + h * p.o_sh +
-                              (int64_t)r * p.o_ss + 4 * c) = o;
-}
-
-// ---------------------------------------------------------------------------
-// 2. main backward
+// 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------
 struct StepGeom {
   int chunk, tile, head_in_group;
 };
 
-template <int D>
-__global__ void __launch_bounds__(NT, 1) bwd_main_kernel(const BwdParams p) {
-  constexpr int NC = D / 8;
-  constexpr int KSTEPS = D / 16;          // MFMA k-steps over head_dim
-  constexpr int DB = D / 32;              // 32-wide blocks of head_dim
-  constexpr int WPD = 4 / DB;             // wavefronts sharing one dQ d-block (1 or 2)
-  constexpr int QK_KEYS = BK / WPD;       // keys each wavefront sums for dQ
-  constexpr int QK_STEPS = QK_KEYS / 16;
-  constexpr int Q_LOADS = BQ * NC / NT;   // 16-byte chunks per thread per Q (or dO) tile
-  constexpr int K_LOADS = BK * NC / NT;
-  static_assert(Q_LOADS >= 1 && K_LOADS >= 1, "tile sizes");
-  using TQ = Tile<D>;
-  using TS = Tile<BQ>;
+// One workgroup of 8 wavefronts per 128-key tile of one KV head, in two
+// roles sharing the tile's 4 x 32 keys:
+//  * score wavefronts (0..3) keep their keys' K and V rows in registers and,
+//    for query tile t, compute S = Q K^T and dP = dO V^T, then P and dS, and
+//    hand both (bf16, in MFMA-operand layout) to LDS;
+//  * accumulate wavefronts (4..7) keep their keys' dK^T/dV^T in registers and,
+//    one step behind, add dO^T P and Q^T dS of query tile t-1 (dO^T and Q^T by
+//    transpose reads of the staged tiles).
+// Query tiles go through a 3-stage LDS ring (being loaded / scored /
+// accumulated), P and dS through a 2-stage exchange; one barrier per step.
+constexpr int kDkdvWaves = 8;
+constexpr int kDkdvThreads = kDkdvWaves * 64;
 
-  // LDS: [0, BK*D) holds the K tile during set-up, then the two stages of the
-  // Q and dO tiles; dS^T [BK keys][BQ queries] follows; then LSE and Delta.
-  __shared__ __attribute__((aligned(16))) __bf16 lds[BK * D + BK * BQ];
-  __shared__ float lse_s[2][BQ];
-  __shared__ float dl_s[2][BQ];
-  __bf16 *const k_s = lds;
-  __bf16 *const ds_s = lds + BK * D;
-  auto q_s = [&](int st) { return lds + st * (2 * BQ * D); };
-  auto do_s = [&](int st) { return lds + st * (2 * BQ * D) + BQ * D; };
-  static_assert(4 * BQ * D <= BK * D, "Q/dO stages must fit in the K set-up region");
+template <int D>
+__global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int NT2 = kDkdvThreads;
+  constexpr int NC = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int Q_CHUNKS = BQ * NC;           // 16-byte chunks per Q (and dO) tile
+  constexpr int Q_LOADS = (Q_CHUNKS + NT2 - 1) / NT2;
+  constexpr int QSTAGES = 3;
+  using TQ = Tile<D>;
+
+  __shared__ __attribute__((aligned(16))) __bf16 q_s[QSTAGES][BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 do_s[QSTAGES][BQ * D];
+  __shared__ __attribute__((aligned(16))) float lse_s[QSTAGES][BQ];
+  __shared__ __attribute__((aligned(16))) float dl_s[QSTAGES][BQ];
+  // P and dS exchange: [stage][key wavefront][P/dS][k-step][lane] x 8 bf16
+  __shared__ __attribute__((aligned(16))) bf16x8 xs[2][4][2][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool scorer = wave < 4;
+  const int kw = wave & 3;                 // which 32 keys of the tile
   const int half = lane >> 5;
   const int col = lane & 31;
 
   const int groups = p.batch * p.hkv;
   const int g = blockIdx.x % groups;
-  const int kt = blockIdx.x / groups;
+  const int kt = blockIdx.x / groups;      // ascending: earliest keys (most work) first
   const int b = g / p.hkv;
   const int hk = g % p.hkv;
   const int key0 = kt * BK;
-  const int wkey0 = key0 + 32 * wave;     // first key of this wavefront's S/dP columns
+  const int wkey0 = key0 + 32 * kw;
   const int my_key = wkey0 + col;
   const bool key_ok = my_key < p.skv;
   const int64_t kv_lo = p.kv_pos0 + key0;
 
-  const __bf16 *kg = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hk * p.kv_sh;
-  const __bf16 *vg = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hk * p.kv_sh;
-
-  // ---- set-up: K/V rows of this lane's key (B operands of S and dP) ------
-  bf16x8 kf[KSTEPS], vf[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    if (key_ok) {
-      kf[s] = *reinterpret_cast<const bf16x8 *>(kg + (int64_t)my_key * p.kv_ss + 16 * s + 8 * half);
-      vf[s] = *reinterpret_cast<const bf16x8 *>(vg + (int64_t)my_key * p.kv_ss + 16 * s + 8 * half);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kf[s][e] = (__bf16)0.0f;
-        vf[s][e] = (__bf16)0.0f;
-      }
-    }
-  }
-  // K tile into LDS, then K^T operands of dQ^T = K^T dS^T for this wavefront.
-#pragma unroll
-  for (int i = 0; i < K_LOADS; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / NC, c = idx % NC;
-    const int key = key0 + row;
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (key < p.skv) val = *reinterpret_cast<const u32x4 *>(kg + (int64_t)key * p.kv_ss + 8 * c);
-    *reinterpret_cast<u32x4 *>(k_s + TQ::chunk_off(row, c)) = val;
-  }
-  __syncthreads();
-  const int dq_dblk = wave % DB;          // d-block of dQ this wavefront produces
-  const int dq_key0 = (wave / DB) * QK_KEYS;  // its keys within the tile
-  bf16x8 ktf[QK_STEPS];
-#pragma unroll
-  for (int s = 0; s < QK_STEPS; ++s) ktf[s] = tr_operand<D>(k_s, dq_key0 + 16 * s, 32 * dq_dblk, lane);
-  __syncthreads();  // the K region is reused for the Q/dO stages below
-
-  // ---- the query tiles this key tile meets --------------------------------
+  // Query tiles this key tile meets, chunk by chunk.
   const int nq_tiles = (p.chunk_len + BQ - 1) / BQ;
   int first_tile[kMaxQChunks];
   int total = 0;
   for (int c = 0; c < p.n_q_chunks; ++c) {
     int t0 = 0;
     if (p.causal) {
-      const int64_t rel = kv_lo - p.chunk_pos[c];   // rows before it cannot see the tile
+      const int64_t rel = kv_lo - p.chunk_pos[c];
       t0 = rel <= 0 ? 0 : (int)min<int64_t>(nq_tiles, rel / BQ);
     }
     first_tile[c] = t0;
@@ -200,33 +150,33 @@ __global__ void __launch_bounds__(NT, 1) bwd_main_kernel(const BwdParams p) {
     return sg;
   };
 
-  // ---- staging of Q, dO, LSE, Delta -----------------------------------------
   u32x4 qreg[Q_LOADS], oreg[Q_LOADS];
-  float aux = 0.0f;   // LSE (threads 0..31) or Delta (threads 32..63)
+  float aux = 0.0f;   // LSE*log2(e) (threads 0..31) or Delta (threads 32..63)
   auto gload = [&](int it) {
     const StepGeom sg = decode(it);
     const int head = hk * p.group + sg.head_in_group;
     const int row0 = sg.tile * BQ;
+    const int last = p.chunk_len - 1;   // rows past the chunk end read its last row
     const __bf16 *qg = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh;
     const __bf16 *og = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh;
 #pragma unroll
     for (int i = 0; i < Q_LOADS; ++i) {
-      const int idx = tid + NT * i;
-      const int r = idx / NC, c = idx % NC;
-      const bool ok = row0 + r < p.chunk_len;
-      const int64_t lr = (int64_t)sg.chunk * p.chunk_len + row0 + r;
-      qreg[i] = ok ? *reinterpret_cast<const u32x4 *>(qg + lr * p.q_ss + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-      oreg[i] = ok ? *reinterpret_cast<const u32x4 *>(og + lr * p.o_ss + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      const int idx = tid + NT2 * i;
+      if (Q_CHUNKS % NT2 == 0 || idx < Q_CHUNKS) {
+        const int r = idx / NC, c = idx % NC;
+        const int64_t lr = (int64_t)sg.chunk * p.chunk_len + min(row0 + r, last);
+        qreg[i] = *reinterpret_cast<const u32x4 *>(qg + lr * p.q_ss + 8 * c);
+        oreg[i] = *reinterpret_cast<const u32x4 *>(og + lr * p.o_ss + 8 * c);
+      }
     }
     if (tid < 2 * BQ) {
       const int r = tid % BQ;
       const bool ok = row0 + r < p.chunk_len;
-      const int64_t idx = ((int64_t)b * p.hq + head) * p.sq + (int64_t)sg.chunk * p.chunk_len + row0 + r;
+      const int64_t idx = ((int64_t)b * p.hq + head) * p.sq + (int64_t)sg.chunk * p.chunk_len + min(row0 + r, last);
       if (tid < BQ) {
-        // exp2 argument offset: LSE * log2(e); +inf for rows with no visible
-        // key or past the chunk end, which makes every P of the row 0.
-        const float l = ok ? p.lse[idx] : -INFINITY;
-        aux = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        // +inf for rows with no visible key or past the chunk end: P = 0.
+        const float l = p.lse[idx];
+        aux = (!ok || l == -INFINITY) ? INFINITY : l * kLog2e;
       } else {
         aux = ok ? p.delta[idx] : 0.0f;
       }
@@ -235,14 +185,100 @@ __global__ void __launch_bounds__(NT, 1) bwd_main_kernel(const BwdParams p) {
   auto swrite = [&](int st) {
 #pragma unroll
     for (int i = 0; i < Q_LOADS; ++i) {
-      const int idx = tid + NT * i;
-      const int r = idx / NC, c = idx % NC;
-      *reinterpret_cast<u32x4 *>(q_s(st) + TQ::chunk_off(r, c)) = qreg[i];
-      *reinterpret_cast<u32x4 *>(do_s(st) + TQ::chunk_off(r, c)) = oreg[i];
+      const int idx = tid + NT2 * i;
+      if (Q_CHUNKS % NT2 == 0 || idx < Q_CHUNKS) {
+        const int r = idx / NC, c = idx % NC;
+        *reinterpret_cast<u32x4 *>(q_s[st] + TQ::chunk_off(r, c)) = qreg[i];
+        *reinterpret_cast<u32x4 *>(do_s[st] + TQ::chunk_off(r, c)) = oreg[i];
+      }
     }
     if (tid < BQ) lse_s[st][tid] = aux;
     else if (tid < 2 * BQ) dl_s[st][tid - BQ] = aux;
   };
+
+  const float c2 = p.scale_log2;
+  const bool wave_keys_ok = wkey0 + 31 < p.skv;
+
+  if (total > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+
+  // Step it: scorers handle query tile it (it < total), accumulators tile
+  // it-1 (it >= 1); tile it+1 is loaded meanwhile. The two roles run separate
+  // loops (so their register sets do not add up) with the same barriers.
+  if (scorer) {
+    // K and V rows of this lane's key (B operands of S and dP).
+    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    {
+      const __bf16 *kg = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hk * p.kv_sh;
+      const __bf16 *vg = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hk * p.kv_sh;
+      const int64_t ro = (int64_t)min(my_key, p.skv - 1) * p.kv_ss + 8 * half;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        kf[s] = *reinterpret_cast<const bf16x8 *>(kg + ro + 16 * s);
+        vf[s] = *reinterpret_cast<const bf16x8 *>(vg + ro + 16 * s);
+      }
+      wait_vmem_all();
+    }
+    for (int it = 0; it <= total; ++it) {
+      const int st = it % QSTAGES;
+      if (it + 1 < total) gload(it + 1);
+      if (it < total) {
+        const StepGeom sg = decode(it);
+        const __bf16 *qs = q_s[st];
+        const __bf16 *os = do_s[st];
+        const int64_t qpos0 = p.chunk_pos[sg.chunk] + sg.tile * BQ;
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[i] = 0.0f;
+          pacc[i] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const int qo = TQ::chunk_off(col, 2 * s + half);
+          sacc = mfma32(*reinterpret_cast<const bf16x8 *>(qs + qo), kf[s], sacc);
+          pacc = mfma32(*reinterpret_cast<const bf16x8 *>(os + qo), vf[s], pacc);
+        }
+        // Register i holds query row 8*(i/4) + 4*half + i%4 of the tile; the
+        // lane's key is visible to rows >= its first visible row.
+        const bool need_mask = !wave_keys_ok || (p.causal && p.kv_pos0 + wkey0 + 31 > qpos0);
+        int t = -BQ;
+        if (need_mask) {
+          int rel = -1;
+          if (p.causal) {
+            const int64_t r = p.kv_pos0 + my_key - qpos0;
+            rel = (int)(r < -1 ? -1 : (r > BQ ? BQ : r));
+          }
+          t = key_ok ? rel - 4 * half : BQ;
+        }
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[st][8 * gq + 4 * half]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl_s[st][8 * gq + 4 * half]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * gq + e;
+            float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -l4[e]));
+            if (need_mask) pv = (8 * gq + e < t) ? 0.0f : pv;
+            pf[i >> 3][i & 7] = (__bf16)pv;
+            dsf[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - d4[e]));
+          }
+        }
+        const int xst = it & 1;
+        xs[xst][kw][0][0][lane] = pf[0];
+        xs[xst][kw][0][1][lane] = pf[1];
+        xs[xst][kw][1][0][lane] = dsf[0];
+        xs[xst][kw][1][1][lane] = dsf[1];
+      }
+      if (it + 1 < total) swrite((it + 1) % QSTAGES);
+      __syncthreads();
+    }
+    return;
+  }
 
   f32x16 dv[DB], dk[DB];
 #pragma unroll
@@ -252,89 +288,28 @@ __global__ void __launch_bounds__(NT, 1) bwd_main_kernel(const BwdParams p) {
       dv[db][i] = 0.0f;
       dk[db][i] = 0.0f;
     }
-  const float c2 = p.scale_log2;
-
-  if (total > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < total; ++it) {
-    const int st = it & 1;
-    const StepGeom sg = decode(it);
+  for (int it = 0; it <= total; ++it) {
     if (it + 1 < total) gload(it + 1);
-    const __bf16 *qs = q_s(st);
-    const __bf16 *os = do_s(st);
-    const int64_t qpos0 = p.chunk_pos[sg.chunk] + sg.tile * BQ;  // global position of the tile's row 0
-
-    // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys.
-    f32x16 sacc, pacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sacc[i] = 0.0f;
-      pacc[i] = 0.0f;
-    }
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(qs + TQ::chunk_off(col, 2 * s + half));
-      const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(os + TQ::chunk_off(col, 2 * s + half));
-      sacc = mfma32(qa, kf[s], sacc);
-      pacc = mfma32(oa, vf[s], pacc);
-    }
-    // P and dS; register i holds query row 8*(i/4) + 4*half + i%4 of the tile.
-    const bool need_mask = !key_ok || (p.causal && p.kv_pos0 + wkey0 + 31 > qpos0) ||
-                           (sg.tile * BQ + BQ > p.chunk_len);
-    bf16x8 pf[2], dsf[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qr = 8 * (i >> 2) + 4 * half + (i & 3);
-      float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -lse_s[st][qr]));
-      if (need_mask) {
-        const bool hide = !key_ok || (p.causal && p.kv_pos0 + my_key > qpos0 + qr);
-        if (hide) pv = 0.0f;
-      }
-      const float dsv = pv * (pacc[i] - dl_s[st][qr]);
-      pf[i >> 3][i & 7] = (__bf16)pv;
-      dsf[i >> 3][i & 7] = (__bf16)dsv;
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (d rows x this wavefront's keys).
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
+    if (it >= 1) {
+      const int pst = (it + QSTAGES - 1) % QSTAGES;
+      const int xst = (it - 1) & 1;
+      const __bf16 *qs = q_s[pst];
+      const __bf16 *os = do_s[pst];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        dv[db] = mfma32(tr_operand<D>(os, 16 * k2, 32 * db, lane), pf[k2], dv[db]);
-        dk[db] = mfma32(tr_operand<D>(qs, 16 * k2, 32 * db, lane), dsf[k2], dk[db]);
+        const bf16x8 pk = xs[xst][kw][0][k2][lane];
+        const bf16x8 dk2 = xs[xst][kw][1][k2][lane];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = mfma32(tr_operand<D>(os, 16 * k2, 32 * db, lane), pk, dv[db]);
+          dk[db] = mfma32(tr_operand<D>(qs, 16 * k2, 32 * db, lane), dk2, dk[db]);
+        }
       }
-    // dS^T -> LDS: row = key in tile, 4 consecutive queries per 8-byte store.
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      bf16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = dsf[gq >> 1][4 * (gq & 1) + e];
-      *reinterpret_cast<bf16x4 *>(ds_s + TS::elem_off(32 * wave + col, 8 * gq + 4 * half)) = w;
     }
-    __syncthreads();
-    // dQ^T (32 d x 32 queries) = K^T dS^T over this wavefront's keys.
-    f32x16 qacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) qacc[i] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < QK_STEPS; ++s)
-      qacc = mfma32(ktf[s], tr_operand<BQ>(ds_s, dq_key0 + 16 * s, 0, lane), qacc);
-    // Accumulate: lane = query column, registers = d rows.
-    if (sg.tile * BQ + col < p.chunk_len) {
-      const int head = hk * p.group + sg.head_in_group;
-      const int64_t lr = (int64_t)sg.chunk * p.chunk_len + sg.tile * BQ + col;
-      float *dst = p.dq_acc + (((int64_t)b * p.hq + head) * p.sq + lr) * D + 32 * dq_dblk + 4 * half;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) atomicAdd(dst + 8 * (i >> 2) + (i & 3), qacc[i]);
-    }
-    if (it + 1 < total) swrite(st ^ 1);
+    if (it + 1 < total) swrite((it + 1) % QSTAGES);
     __syncthreads();
   }
 
-  // ---- dK, dV of this wavefront's keys (zeros where no query sees them) ----
   if (!key_ok) return;
   float *dvp = p.dv + (((int64_t)b * p.hkv + hk) * p.skv + my_key) * D;
   float *dkp = p.dk + (((int64_t)b * p.hkv + hk) * p.skv + my_key) * D;
@@ -354,6 +329,183 @@ __global__ void __launch_bounds__(NT, 1) bwd_main_kernel(const BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 3. dQ (query-stationary; work items and K/V staging as in the forward)
+// ---------------------------------------------------------------------------
+template <int D, int RB>
+__global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
+  constexpr int HPW = kFwdWaves / RB;
+  constexpr int BM = kWaveRows * RB;
+  constexpr int NC = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int LOADS = BN * NC / NT;
+  using T = Tile<D>;
+
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BN * D];  // [stage][K,V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  const int bid = blockIdx.x;
+  const int pack = bid % p.n_head_packs;
+  const int rank = bid / p.n_head_packs;
+  const int ci = rank / p.tiles_per_chunk;
+  const int tile = p.tiles_per_chunk - 1 - (rank % p.tiles_per_chunk);
+  const int chunk = p.lpt_chunk_idx[ci];
+  const int64_t chunk_pos = p.lpt_chunk_pos[ci];
+  const int packs_per_batch = p.hq / HPW;
+  const int b = pack / packs_per_batch;
+  const int head0 = (pack % packs_per_batch) * HPW;
+  const int hkv = head0 / p.group;
+  const int item_row0 = tile * BM;
+  const int item_rows = min(BM, p.chunk_len - item_row0);
+  const int64_t item_qhi = chunk_pos + item_row0 + item_rows - 1;
+
+  const int head = head0 + wave / RB;
+  const int wrow0 = (wave % RB) * kWaveRows;
+  const int wrows = max(0, min(kWaveRows, item_rows - wrow0));
+  const int64_t wave_qlo = chunk_pos + item_row0 + wrow0;
+  const int64_t wave_qhi = wave_qlo + max(wrows, 1) - 1;
+  const bool qvalid = col < wrows;
+  const int64_t qpos = wave_qlo + min(col, max(wrows - 1, 0));
+  const int local_row = chunk * p.chunk_len + item_row0 + wrow0 + col;
+
+  int nvis = p.skv;
+  if (p.causal) {
+    const int64_t n = item_qhi - p.kv_pos0 + 1;
+    nvis = (int)(n < 0 ? 0 : (n > p.skv ? p.skv : n));
+  }
+  const int ntiles = (nvis + BN - 1) / BN;
+
+  // Q and dO rows of this lane's query: B operands of S^T and dP^T. Lanes past
+  // the item's last row read its first row and get LSE = +inf (P = 0).
+  bf16x8 qf[KSTEPS], gf[KSTEPS];
+  float lse2 = INFINITY, delta = 0.0f;
+  {
+    const int load_row = qvalid ? local_row : chunk * p.chunk_len + item_row0;
+    const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh +
+                       (int64_t)load_row * p.q_ss + 8 * half;
+    const __bf16 *gp = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh +
+                       (int64_t)load_row * p.o_ss + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
+      gf[s] = *reinterpret_cast<const bf16x8 *>(gp + 16 * s);
+    }
+    if (qvalid) {
+      const int64_t row = ((int64_t)b * p.hq + head) * p.sq + local_row;
+      const float l = p.lse[row];
+      lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      delta = p.delta[row];
+    }
+    wait_vmem_all();
+  }
+
+  const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
+  const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
+  u32x4 kreg[LOADS], vreg[LOADS];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int idx = tid + NT * i;
+      const int row = idx / NC, c = idx % NC;
+      const int key = min(kt * BN + row, p.skv - 1);   // rows past the end: always masked
+      const int64_t o = (int64_t)key * p.kv_ss + c * 8;
+      kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
+      vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
+    }
+  };
+  auto swrite = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int idx = tid + NT * i;
+      const int row = idx / NC, c = idx % NC;
+      *reinterpret_cast<u32x4 *>(&smem[stage][0][T::chunk_off(row, c)]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][1][T::chunk_off(row, c)]) = vreg[i];
+    }
+  };
+
+  f32x16 qacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qacc[db][i] = 0.0f;
+  const float c2 = p.scale_log2;
+
+  if (ntiles > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < ntiles) gload(kt + 1);
+    const int64_t tile_plo = p.kv_pos0 + (int64_t)kt * BN;
+    const bool active = wrows > 0 && (!p.causal || tile_plo <= wave_qhi);
+    if (active) {
+      const __bf16 *ks = smem[st][0];
+      const __bf16 *vs = smem[st][1];
+      const bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
+      int t = BN;   // key kb*32 + 8*(i/4) + 4*half + i%4 visible iff (that - 4*half) <= t
+      if (need_mask) {
+        int lim = p.skv - 1 - kt * BN;
+        if (p.causal) {
+          const int64_t rel = qpos - tile_plo;
+          lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
+        }
+        t = lim - 4 * half;
+      }
+      // One 32-key block at a time keeps only one S^T/dP^T pair live.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[i] = 0.0f;
+          pacc[i] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const int off = T::chunk_off(kb * 32 + col, 2 * s + half);
+          sacc = mfma32(*reinterpret_cast<const bf16x8 *>(ks + off), qf[s], sacc);
+          pacc = mfma32(*reinterpret_cast<const bf16x8 *>(vs + off), gf[s], pacc);
+        }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -lse2));
+          if (need_mask) pv = (kb * 32 + 8 * (i >> 2) + (i & 3) > t) ? 0.0f : pv;
+          dsf[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - delta));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2)
+            qacc[db] = mfma32(tr_operand<D>(ks, 32 * kb + 16 * k2, 32 * db, lane), dsf[k2], qacc[db]);
+      }
+    }
+    if (kt + 1 < ntiles) swrite(st ^ 1);
+    __syncthreads();
+  }
+
+  if (!qvalid) return;
+  __bf16 *dst = static_cast<__bf16 *>(p.dq) + b * p.o_sb + head * p.o_sh + (int64_t)local_row * p.o_ss;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(qacc[db][4 * gq + e] * p.scale);
+      *reinterpret_cast<bf16x4 *>(dst + 32 * db + 8 * gq + 4 * half) = o4;
+    }
+}
+
 template <int D>
 int launch_d(const BwdParams &p, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -364,11 +516,17 @@ int launch_d(const BwdParams &p, void *stream) {
   }
   const int64_t kv_tiles = (p.skv + BK - 1) / BK;
   if (kv_tiles > 0) {
-    hipLaunchKernelGGL(bwd_main_kernel<D>, dim3(kv_tiles * p.batch * p.hkv), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(kv_tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
   }
-  if (rows > 0) {
-    const int64_t blocks = (rows * (D / 4) + 255) / 256;
-    hipLaunchKernelGGL(bwd_dq_convert_kernel<D>, dim3(blocks), dim3(256), 0, s, p);
+  const int64_t items = (int64_t)p.n_head_packs * p.n_q_chunks * p.tiles_per_chunk;
+  if (rows > 0 && items > 0) {
+    const int rb = kFwdWaves / p.heads_per_item;
+    switch (rb) {
+      case 1: hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), dim3(items), dim3(NT), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3(items), dim3(NT), 0, s, p); break;
+      case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3(items), dim3(NT), 0, s, p); break;
+      default: return (int)hipErrorInvalidValue;
+    }
   }
   return (int)hipGetLastError();
 }

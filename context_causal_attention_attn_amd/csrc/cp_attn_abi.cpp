@@ -123,6 +123,15 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
   p->scale = d->softmax_scale;
   p->scale_log2 = d->softmax_scale * 1.4426950408889634f;
   for (int i = 0; i < s.n_q_chunks; ++i) p->chunk_pos[i] = s.chunk_pos[i];
+  FwdParams f;
+  fill_fwd_params(d, s, &f);
+  p->heads_per_item = f.heads_per_item;
+  p->n_head_packs = f.n_head_packs;
+  p->tiles_per_chunk = f.tiles_per_chunk;
+  for (int i = 0; i < s.n_q_chunks; ++i) {
+    p->lpt_chunk_pos[i] = f.chunk_pos[i];
+    p->lpt_chunk_idx[i] = f.chunk_idx[i];
+  }
 }
 
 int64_t fwd_grid_size(const FwdParams &p) {
@@ -210,10 +219,9 @@ int32_t cp_attn_workspace_bytes(const cp_attn_desc *d, int32_t backward, size_t 
   if (st) return st;
   if (!bytes) return CP_ATTN_ERR_NULL_PTR;
   if (!backward) { *bytes = 0; return CP_ATTN_OK; }
-  // Backward: Delta [B, Hq, Sq] fp32, then the fp32 dQ accumulator [B, Hq, Sq, D].
+  // Backward: Delta = rowsum(dO o O), [B, Hq, Sq] fp32.
   const size_t rows = (size_t)d->batch * d->hq * (size_t)d->sq_local;
-  const size_t delta = (rows * 4 + 255) & ~(size_t)255;
-  *bytes = delta + rows * (size_t)d->head_dim * 4;
+  *bytes = (rows * 4 + 255) & ~(size_t)255;
   return CP_ATTN_OK;
 }
 
@@ -295,10 +303,7 @@ int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const v
   fill_bwd_params(d, s, &p);
   p.q = q; p.k = k; p.v = v; p.out = out; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;
-  const size_t rows = (size_t)d->batch * d->hq * (size_t)d->sq_local;
-  const size_t delta_bytes = (rows * 4 + 255) & ~(size_t)255;
   p.delta = static_cast<float *>(workspace);
-  p.dq_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + delta_bytes);
   const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream)
                                            : launch_bwd_fp32(p, d->head_dim, stream);
   return e == 0 ? CP_ATTN_OK : CP_ATTN_ERR_HIP;

@@ -8,8 +8,8 @@
 //
 // How (one workgroup = 4 wavefronts = one work item):
 //  * a work item is a tile of query rows of one chunk for a pack of query
-//    heads that read the same KV head (GQA); K/V tiles of 64 keys are staged
-//    through LDS once per workgroup and read by every head of the pack;
+//    heads that read the same KV head (GQA); K/V tiles of 32 keys pass through
+//    a 3-stage LDS ring once per workgroup and are read by every head;
 //  * each wavefront owns 32 query rows of one head and computes the transposed
 //    score tile S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16, so
 //    that a lane holds one query column: the row max and sum of the online
@@ -19,14 +19,18 @@
 //    of O^T += V^T P^T without any shuffle: the contraction index (keys) is
 //    permuted identically in both operands, and V^T is read from the
 //    row-major V tile with the gfx950 LDS transpose read ds_read_b64_tr_b16;
-//  * KV tiles wholly after a wavefront's last query are skipped; only tiles
-//    crossing the causal diagonal (or the ragged end of K/V) are masked
-//    element-wise; the running max is only moved (and O rescaled) when a new
-//    score exceeds it by more than 2^8, which keeps exp2 arguments <= 8;
-//  * K/V tiles are double-buffered: the global loads of tile t+1 are in flight
-//    while tile t is computed.
+//  * software pipeline: while the vector ALU exponentiates tile j, the matrix
+//    cores already compute S^T of tile j+1 (the two are interleaved
+//    instruction by instruction), and the global loads of tile j+2 are in
+//    flight;
+//  * KV tiles wholly after the work item's last query are never visited; only
+//    tiles crossing the causal diagonal (or the ragged end of K/V) are masked;
+//    the running max is only moved (and O rescaled) when a new score exceeds
+//    it by more than 2^8, which keeps every exp2 argument <= 8.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "gfx950_common.h"
 #include "plan.h"
@@ -34,9 +38,15 @@
 namespace cpattn {
 namespace {
 
-constexpr int BN = kFwdBlockKV;
+constexpr int BN = kFwdBlockKV;          // keys per tile (32)
 constexpr int NT = kFwdWaves * 64;
-constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int STAGES = 3;
+constexpr float kRescaleSlack = 8.0f;    // log2 units
+
+// sched_group_barrier masks
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedDsRead = 0x100;
 
 template <int D, int RB>
 __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
@@ -45,10 +55,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr int NC = D / 8;
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int TILE = BN * D;
   constexpr int LOADS = BN * NC / NT;
+  static_assert(BN == 32 && LOADS >= 1, "tile shape");
   using T = Tile<D>;
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BN * D];  // [stage][K,V]
+  __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES][2][TILE];  // [stage][K,V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -75,11 +87,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const int head = head0 + wave / RB;
   const int wrow0 = (wave % RB) * kWaveRows;
   const int wrows = max(0, min(kWaveRows, item_rows - wrow0));
-  const int64_t wave_qlo = chunk_pos + item_row0 + wrow0;
-  const int64_t wave_qhi = wave_qlo + max(wrows, 1) - 1;
+  const int64_t wave_qlo = chunk_pos + item_row0 + min(wrow0, item_rows - 1);
   const bool qvalid = col < wrows;
-  const int64_t qpos = wave_qlo + min(col, max(wrows - 1, 0));
-  const int local_row = chunk * p.chunk_len + item_row0 + wrow0 + col;
+  // Lanes past the last row of the item act as its last row (never stored).
+  const int qrow = min(wrow0 + col, item_rows - 1);
+  const int64_t qpos = chunk_pos + item_row0 + qrow;
+  const int local_row = chunk * p.chunk_len + item_row0 + qrow;
 
   int nvis = p.skv;
   if (p.causal) {
@@ -94,43 +107,54 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh +
                        (int64_t)local_row * p.q_ss + 8 * half;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      if (qvalid) {
-        qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)0.0f;
-      }
-    }
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
+    wait_vmem_all();
   }
 
-  // ---- K/V staging --------------------------------------------------------
+  // ---- per-lane addressing, computed once ----------------------------------
+  int koff[KSTEPS];                        // K-fragment reads: row col, chunk 2s+half
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = T::chunk_off(col, 2 * s + half);
+  int troff[2][DB];                        // V^T transpose reads (k-step 1 adds 16 rows)
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      troff[u][db] = T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
+                                 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  int woff[LOADS];                         // staging writes
+  int64_t goff[LOADS];                     // global offset of the chunk within a tile
+  int grow[LOADS], gcol[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int idx = tid + NT * i;
+    const int row = idx / NC, c = idx % NC;
+    woff[i] = T::chunk_off(row, c);
+    goff[i] = (int64_t)row * p.kv_ss + c * 8;
+    grow[i] = row;
+    gcol[i] = c * 8;
+  }
   const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
+  const int64_t tile_stride = (int64_t)BN * p.kv_ss;
+
   u32x4 kreg[LOADS], vreg[LOADS];
   auto gload = [&](int kt) {
+    // Rows past the end of K/V are read from the last row (always masked).
+    const bool full = kt * BN + BN <= p.skv;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int idx = tid + NT * i;
-      const int row = idx / NC, c = idx % NC;
-      const int key = kt * BN + row;
-      if (key < p.skv) {
-        const int64_t o = (int64_t)key * p.kv_ss + c * 8;
-        kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int64_t o = full ? (int64_t)kt * tile_stride + goff[i]
+                             : (int64_t)min(kt * BN + grow[i], p.skv - 1) * p.kv_ss + gcol[i];
+      kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
+      vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
     }
   };
   auto swrite = [&](int stage) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int idx = tid + NT * i;
-      const int row = idx / NC, c = idx % NC;
-      *reinterpret_cast<u32x4 *>(&smem[stage][0][T::chunk_off(row, c)]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&smem[stage][1][T::chunk_off(row, c)]) = vreg[i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][0][woff[i]]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][1][woff[i]]) = vreg[i];
     }
   };
 
@@ -143,101 +167,129 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   float l_part = 0.0f;      // this lane's partial row sum (its half of the keys)
   const float c = p.scale_log2;
 
+  // ---- prologue: tiles 0 and 1 staged, S^T of tile 0 ----------------------
+  f32x16 sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
   if (ntiles > 0) {
     gload(0);
     swrite(0);
+    if (ntiles > 1) {
+      gload(1);
+      swrite(1);
+    }
   }
   __syncthreads();
+  if (ntiles > 0) {
+    const __bf16 *ks = smem[0][0];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      sacc = mfma32(*reinterpret_cast<const bf16x8 *>(ks + koff[s]), qf[s], sacc);
+  }
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
+  // One step of the pipeline on tile kt held in stage ST (kt % 3 == ST).
+  auto step = [&](auto st_tag, int kt) {
+    constexpr int ST = decltype(st_tag)::value;
+    constexpr int NEXT = (ST + 1) % STAGES;
+    constexpr int FREE = (ST + 2) % STAGES;
+    if (kt + 2 < ntiles) gload(kt + 2);
     const int64_t tile_plo = p.kv_pos0 + (int64_t)kt * BN;
-    const bool active = wrows > 0 && (!p.causal || tile_plo <= wave_qhi);
-    if (active) {
-      const __bf16 *ks = smem[st][0];
-      const __bf16 *vs = smem[st][1];
-      // S^T tile [64 keys x 32 queries] as two 32x32 accumulators.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + T::chunk_off(kb * 32 + col, 2 * s + half));
-          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
-        }
+
+    // Mask (diagonal or ragged tiles only): key 8*(i/4) + 4*half + i%4 of the
+    // tile is visible iff it is <= lim.
+    const bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
+    if (need_mask) {
+      int lim = p.skv - 1 - kt * BN;
+      if (p.causal) {
+        const int64_t rel = qpos - tile_plo;
+        lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
       }
-      const bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
-      if (need_mask) {
+      const int t = lim - 4 * half;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3) > t) ? -INFINITY : sacc[i];
+    }
+    // Online softmax bookkeeping for tile kt.
+    float mx = fmaxf(sacc[0], sacc[1]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt * BN + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool hide = key >= p.skv || (p.causal && p.kv_pos0 + key > qpos);
-            if (hide) sacc[kb][i] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = pair_max(mx) * c;
-      const bool upd = mx > m_run + kRescaleSlack;
-      if (__any(upd)) {
-        const float m_new = upd ? mx : m_run;
-        const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        m_run = m_new;
-      }
-      const float mneg = (m_run == -INFINITY) ? 0.0f : -m_run;
-      // P^T = exp2(c*s - m) as bf16 B operands, one per 16-key step.
-      bf16x8 pf[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, mneg));
-          l_part += pv;
-          pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
-        }
-      // O^T += V^T P^T.
+    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[i], sacc[i + 1]));
+    mx = pair_max(mx) * c;
+    const bool upd = mx > m_run + kRescaleSlack;
+    if (__any(upd)) {
+      const float m_new = upd ? mx : m_run;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2)
-          oacc[db] = mfma32(tr_operand<D>(vs, 16 * k2, 32 * db, lane), pf[k2], oacc[db]);
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_run = m_new;
     }
-    if (kt + 1 < ntiles) swrite(st ^ 1);
+    const float mneg = (m_run == -INFINITY) ? 0.0f : -m_run;
+
+    // S^T of tile kt+1 on the matrix cores, interleaved with exp2 of tile kt.
+    // (After the last tile this reads a stale stage; the result is unused.)
+    f32x16 snext;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) snext[i] = 0.0f;
+    const __bf16 *ksn = smem[NEXT][0];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      snext = mfma32(*reinterpret_cast<const bf16x8 *>(ksn + koff[s]), qf[s], snext);
+    // The row sum uses the unrounded fp32 probabilities (summing the bf16
+    // values instead costs up to ~2^-9 relative error in short rows).
+    bf16x8 pf[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, mneg));
+      l_part += pv;
+      pf[i >> 3][i & 7] = (__bf16)pv;
+    }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+    }
+
+    // O^T += V^T P^T for tile kt.
+    const __bf16 *vs = smem[ST][1];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vs + troff[0][db] + 16 * D * k2));
+        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vs + troff[1][db] + 16 * D * k2));
+        const i16x8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pf[k2], oacc[db]);
+      }
+    if (kt + 2 < ntiles) swrite(FREE);
     __syncthreads();
+    sacc = snext;
+  };
+
+  for (int kt = 0; kt < ntiles; kt += STAGES) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < ntiles) step(std::integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 < ntiles) step(std::integral_constant<int, 2>{}, kt + 2);
   }
 
   // ---- epilogue -------------------------------------------------------------
-  if (wrows == 0) return;
+  if (!qvalid) return;
   const float l = pair_sum(l_part);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  if (qvalid) {
-    __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + head * p.o_sh + (int64_t)local_row * p.o_ss;
+  __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + head * p.o_sh + (int64_t)local_row * p.o_ss;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 o4;
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g + 4 * half) = o4;
-      }
-    if (half == 0) {
-      const float lse = l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
-      p.lse[((int64_t)b * p.hq + head) * p.sq + local_row] = lse;
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][4 * g + e] * inv);
+      *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g + 4 * half) = o4;
     }
+  if (half == 0) {
+    const float lse = l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+    p.lse[((int64_t)b * p.hq + head) * p.sq + local_row] = lse;
   }
 }
 

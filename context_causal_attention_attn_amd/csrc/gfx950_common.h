@@ -68,6 +68,13 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wait until every outstanding vector-memory load of this wavefront has
+// returned (s_waitcnt vmcnt(0); expcnt/lgkmcnt left unconstrained). Used once
+// after the loads of register-resident operands, so that the compiler's
+// wait-count bookkeeping does not carry them into the main loop, where it
+// would otherwise wait on the in-flight prefetch of later tiles.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

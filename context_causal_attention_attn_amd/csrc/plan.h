@@ -21,7 +21,7 @@ constexpr int kMaxQChunks = CP_ATTN_MAX_Q_CHUNKS;
 // Forward, bf16 MFMA kernel
 // ---------------------------------------------------------------------------
 // Keys per KV tile staged in LDS, and query rows per wavefront.
-constexpr int kFwdBlockKV = 64;
+constexpr int kFwdBlockKV = 32;
 constexpr int kWaveRows = 32;
 constexpr int kFwdWaves = 4;
 
@@ -70,11 +70,15 @@ inline int fwd_block_rows(int g) { return kWaveRows * (kFwdWaves / fwd_heads_per
 // ---------------------------------------------------------------------------
 // Backward
 // ---------------------------------------------------------------------------
-// A backward work item is one tile of kBwdBlockKV keys of one KV head: it
-// keeps that tile's dK/dV in registers and visits every query tile (of every
-// head of the GQA group, of every chunk) that can see one of its keys.
+// The backward runs two main kernels. The key-stationary one owns a tile of
+// kBwdBlockKV keys of one KV head, keeps that tile's dK/dV in registers and
+// visits every query tile (of every head of the GQA group, of every chunk)
+// that can see one of its keys. The query-stationary one owns a query tile
+// (scheduled exactly like the forward) and accumulates its dQ over the keys
+// it can see.
 constexpr int kBwdBlockKV = 128;
 constexpr int kBwdBlockQ = 32;
+constexpr int kDqBlockKV = 64;    // keys per tile of the query-stationary dQ kernel
 
 struct BwdParams {
   const void *q;
@@ -84,7 +88,6 @@ struct BwdParams {
   const void *dout;
   const float *lse;
   float *delta;                 // workspace [B, Hq, Sq]
-  float *dq_acc;                // workspace [B, Hq, Sq, D] fp32
   void *dq;
   float *dk;                    // [B, Hkv, Skv, D]
   float *dv;
@@ -99,6 +102,10 @@ struct BwdParams {
   float scale;
   float scale_log2;
   int64_t chunk_pos[kMaxQChunks];   // local chunk order
+  // Schedule of the query-stationary dQ kernel (same as the forward's).
+  int32_t heads_per_item, n_head_packs, tiles_per_chunk;
+  int64_t lpt_chunk_pos[kMaxQChunks];
+  int32_t lpt_chunk_idx[kMaxQChunks];
 };
 
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p);

@@ -170,4 +170,4 @@ def test_workspace_bytes():
     d = desc()
     assert cp_attn_workspace_bytes(d, False) == 0
     rows = 1 * 8 * 500
-    assert cp_attn_workspace_bytes(d, True) == ((rows * 4 + 255) // 256) * 256 + rows * 128 * 4
+    assert cp_attn_workspace_bytes(d, True) == ((rows * 4 + 255) // 256) * 256
