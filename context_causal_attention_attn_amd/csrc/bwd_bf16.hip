@@ -39,6 +39,10 @@ constexpr int BQ = kBwdBlockQ;    // query rows per step of that workgroup
 constexpr int BN = kDqBlockKV;    // keys per tile of the query-stationary kernel
 constexpr int NT = 256;
 
+// sched_group_barrier masks
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 // ---------------------------------------------------------------------------
 // 1. Delta = rowsum(dO o O), 16 lanes per row.
 // ---------------------------------------------------------------------------
@@ -105,7 +109,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool scorer = wave < 4;
   const int kw = wave & 3;                 // which 32 keys of the tile
   const int half = lane >> 5;
@@ -150,58 +154,69 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     return sg;
   };
 
-  u32x4 qreg[Q_LOADS], oreg[Q_LOADS];
-  float aux = 0.0f;   // LSE*log2(e) (threads 0..31) or Delta (threads 32..63)
-  auto gload = [&](int it) {
+  // Staging of query tiles: loaded into registers at the start of a step and
+  // written to the LDS ring at its end, one step ahead of use.
+  int woff[Q_LOADS], grow[Q_LOADS], gcol[Q_LOADS];
+#pragma unroll
+  for (int i = 0; i < Q_LOADS; ++i) {
+    const int idx = min(tid + NT2 * i, Q_CHUNKS - 1);
+    grow[i] = idx / NC;
+    gcol[i] = 8 * (idx % NC);
+    woff[i] = TQ::chunk_off(grow[i], idx % NC);
+  }
+  struct Staged {
+    u32x4 q[Q_LOADS], o[Q_LOADS];
+    float aux;   // raw LSE (threads 0..31) or Delta (threads 32..63) of one row
+    int ok;      // that row lies inside the chunk
+  };
+  Staged reg0;
+  // Wave-uniform copies of the two row-statistics pointers: selecting between
+  // them per lane must not turn into a per-lane load of the pointer itself.
+  const float *const lse_ptr = p.lse;
+  const float *const delta_ptr = p.delta;
+  // Loads only: anything computed from the loaded values waits until swrite,
+  // so the loads stay in flight during the step's compute.
+  auto gload = [&](int it, Staged &r) {
     const StepGeom sg = decode(it);
     const int head = hk * p.group + sg.head_in_group;
     const int row0 = sg.tile * BQ;
     const int last = p.chunk_len - 1;   // rows past the chunk end read its last row
+    const int64_t rbase = (int64_t)sg.chunk * p.chunk_len;
     const __bf16 *qg = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh;
     const __bf16 *og = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh;
 #pragma unroll
     for (int i = 0; i < Q_LOADS; ++i) {
-      const int idx = tid + NT2 * i;
-      if (Q_CHUNKS % NT2 == 0 || idx < Q_CHUNKS) {
-        const int r = idx / NC, c = idx % NC;
-        const int64_t lr = (int64_t)sg.chunk * p.chunk_len + min(row0 + r, last);
-        qreg[i] = *reinterpret_cast<const u32x4 *>(qg + lr * p.q_ss + 8 * c);
-        oreg[i] = *reinterpret_cast<const u32x4 *>(og + lr * p.o_ss + 8 * c);
-      }
+      const int64_t lr = rbase + min(row0 + grow[i], last);
+      r.q[i] = *reinterpret_cast<const u32x4 *>(qg + lr * p.q_ss + gcol[i]);
+      r.o[i] = *reinterpret_cast<const u32x4 *>(og + lr * p.o_ss + gcol[i]);
     }
     if (tid < 2 * BQ) {
-      const int r = tid % BQ;
-      const bool ok = row0 + r < p.chunk_len;
-      const int64_t idx = ((int64_t)b * p.hq + head) * p.sq + (int64_t)sg.chunk * p.chunk_len + min(row0 + r, last);
-      if (tid < BQ) {
-        // +inf for rows with no visible key or past the chunk end: P = 0.
-        const float l = p.lse[idx];
-        aux = (!ok || l == -INFINITY) ? INFINITY : l * kLog2e;
-      } else {
-        aux = ok ? p.delta[idx] : 0.0f;
-      }
+      const int rr = tid % BQ;
+      r.ok = row0 + rr < p.chunk_len;
+      const int64_t idx = ((int64_t)b * p.hq + head) * p.sq + rbase + min(row0 + rr, last);
+      r.aux = (tid < BQ ? lse_ptr : delta_ptr)[idx];
     }
   };
-  auto swrite = [&](int st) {
+  auto swrite = [&](int st, const Staged &r) {
 #pragma unroll
     for (int i = 0; i < Q_LOADS; ++i) {
-      const int idx = tid + NT2 * i;
-      if (Q_CHUNKS % NT2 == 0 || idx < Q_CHUNKS) {
-        const int r = idx / NC, c = idx % NC;
-        *reinterpret_cast<u32x4 *>(q_s[st] + TQ::chunk_off(r, c)) = qreg[i];
-        *reinterpret_cast<u32x4 *>(do_s[st] + TQ::chunk_off(r, c)) = oreg[i];
+      if (Q_CHUNKS % NT2 == 0 || tid + NT2 * i < Q_CHUNKS) {
+        *reinterpret_cast<u32x4 *>(q_s[st] + woff[i]) = r.q[i];
+        *reinterpret_cast<u32x4 *>(do_s[st] + woff[i]) = r.o[i];
       }
     }
-    if (tid < BQ) lse_s[st][tid] = aux;
-    else if (tid < 2 * BQ) dl_s[st][tid - BQ] = aux;
+    // LSE is stored as LSE*log2(e), +inf for rows with no visible key or past
+    // the chunk end (P = 0); Delta is 0 past the chunk end.
+    if (tid < BQ) lse_s[st][tid] = (!r.ok || r.aux == -INFINITY) ? INFINITY : r.aux * kLog2e;
+    else if (tid < 2 * BQ) dl_s[st][tid - BQ] = r.ok ? r.aux : 0.0f;
   };
 
   const float c2 = p.scale_log2;
   const bool wave_keys_ok = wkey0 + 31 < p.skv;
 
   if (total > 0) {
-    gload(0);
-    swrite(0);
+    gload(0, reg0);
+    swrite(0, reg0);
   }
   __syncthreads();
 
@@ -209,8 +224,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   // it-1 (it >= 1); tile it+1 is loaded meanwhile. The two roles run separate
   // loops (so their register sets do not add up) with the same barriers.
   if (scorer) {
-    // K and V rows of this lane's key (B operands of S and dP).
-    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    bf16x8 kf[KSTEPS], vf[KSTEPS];   // K and V rows of this lane's key
+    int qoff[KSTEPS];                // A-operand reads of the Q and dO rows
     {
       const __bf16 *kg = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hk * p.kv_sh;
       const __bf16 *vg = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hk * p.kv_sh;
@@ -219,13 +234,14 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
       for (int s = 0; s < KSTEPS; ++s) {
         kf[s] = *reinterpret_cast<const bf16x8 *>(kg + ro + 16 * s);
         vf[s] = *reinterpret_cast<const bf16x8 *>(vg + ro + 16 * s);
+        qoff[s] = TQ::chunk_off(col, 2 * s + half);
       }
       wait_vmem_all();
     }
     for (int it = 0; it <= total; ++it) {
-      const int st = it % QSTAGES;
-      if (it + 1 < total) gload(it + 1);
+      if (it + 1 < total) gload(it + 1, reg0);
       if (it < total) {
+        const int st = it % QSTAGES;
         const StepGeom sg = decode(it);
         const __bf16 *qs = q_s[st];
         const __bf16 *os = do_s[st];
@@ -236,12 +252,25 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
           sacc[i] = 0.0f;
           pacc[i] = 0.0f;
         }
+        bf16x8 qa[KSTEPS], oa[KSTEPS];
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const int qo = TQ::chunk_off(col, 2 * s + half);
-          sacc = mfma32(*reinterpret_cast<const bf16x8 *>(qs + qo), kf[s], sacc);
-          pacc = mfma32(*reinterpret_cast<const bf16x8 *>(os + qo), vf[s], pacc);
+          qa[s] = *reinterpret_cast<const bf16x8 *>(qs + qoff[s]);
+          oa[s] = *reinterpret_cast<const bf16x8 *>(os + qoff[s]);
         }
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          sacc = mfma32(qa[s], kf[s], sacc);
+          pacc = mfma32(oa[s], vf[s], pacc);
+        }
+        // Half the operand reads up front, the rest two MFMAs ahead of use.
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KSTEPS, 0);
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, KSTEPS, 0);
         // Register i holds query row 8*(i/4) + 4*half + i%4 of the tile; the
         // lane's key is visible to rows >= its first visible row.
         const bool need_mask = !wave_keys_ok || (p.causal && p.kv_pos0 + wkey0 + 31 > qpos0);
@@ -274,12 +303,14 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
         xs[xst][kw][1][0][lane] = dsf[0];
         xs[xst][kw][1][1][lane] = dsf[1];
       }
-      if (it + 1 < total) swrite((it + 1) % QSTAGES);
+      if (it + 1 < total) swrite((it + 1) % QSTAGES, reg0);
       __syncthreads();
     }
     return;
   }
 
+  TrOffsets<D> tro;   // Q^T and dO^T transpose reads (same tile layout)
+  tro.init(lane);
   f32x16 dv[DB], dk[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -289,24 +320,42 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
       dk[db][i] = 0.0f;
     }
   for (int it = 0; it <= total; ++it) {
-    if (it + 1 < total) gload(it + 1);
+    if (it + 1 < total) gload(it + 1, reg0);
     if (it >= 1) {
       const int pst = (it + QSTAGES - 1) % QSTAGES;
       const int xst = (it - 1) & 1;
       const __bf16 *qs = q_s[pst];
       const __bf16 *os = do_s[pst];
+      // LDS operands of the first half of the step are read up front; those
+      // of the second half while the first half's matrix operations run.
+      bf16x8 ao[2][DB], aq[2][DB], pk[2], dsk[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8 pk = xs[xst][kw][0][k2][lane];
-        const bf16x8 dk2 = xs[xst][kw][1][k2][lane];
+        pk[k2] = xs[xst][kw][0][k2][lane];
+        dsk[k2] = xs[xst][kw][1][k2][lane];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32(tr_operand<D>(os, 16 * k2, 32 * db, lane), pk, dv[db]);
-          dk[db] = mfma32(tr_operand<D>(qs, 16 * k2, 32 * db, lane), dk2, dk[db]);
+          ao[k2][db] = tro.read(os, 16 * k2, db);
+          aq[k2][db] = tro.read(qs, 16 * k2, db);
         }
       }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = mfma32(ao[k2][db], pk[k2], dv[db]);
+          dk[db] = mfma32(aq[k2][db], dsk[k2], dk[db]);
+        }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 + 4 * DB, 0);
+#pragma unroll
+      for (int j = 0; j < 2 * DB; ++j) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * DB, 0);
     }
-    if (it + 1 < total) swrite((it + 1) % QSTAGES);
+    if (it + 1 < total) swrite((it + 1) % QSTAGES, reg0);
     __syncthreads();
   }
 
@@ -346,7 +395,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -407,25 +456,48 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 
   const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
+  // Per-lane addressing, computed once.
+  int koff[KSTEPS];                     // A-operand reads of K and V rows
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = T::chunk_off(col, 2 * s + half);
+  TrOffsets<D> tro;                     // K^T transpose reads
+  tro.init(lane);
+  // Staging: thread tid moves chunk (tid % NC) of rows tid / NC + i * RSTEP.
+  // Row steps of RSTEP (a multiple of 16) keep the swizzle, so every load's
+  // LDS and global offsets are the first one's plus a constant.
+  constexpr int RSTEP = NT / NC;
+  static_assert(RSTEP % 16 == 0, "row step must preserve the swizzle");
+  const int srow = tid / NC, scol = 8 * (tid % NC);
+  const int woff0 = T::chunk_off(srow, tid % NC);
+  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
+  const int64_t tile_stride = (int64_t)BN * p.kv_ss;
+  const int64_t rstep_bytes = (int64_t)RSTEP * p.kv_ss * 2;
   u32x4 kreg[LOADS], vreg[LOADS];
   auto gload = [&](int kt) {
+    if (kt * BN + BN <= p.skv) {
+      // Full tile: scalar tile base plus a 32-bit per-lane byte offset.
+      const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride);
+      const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int idx = tid + NT * i;
-      const int row = idx / NC, c = idx % NC;
-      const int key = min(kt * BN + row, p.skv - 1);   // rows past the end: always masked
-      const int64_t o = (int64_t)key * p.kv_ss + c * 8;
-      kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
-      vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
+      for (int i = 0; i < LOADS; ++i) {
+        kreg[i] = *reinterpret_cast<const u32x4 *>(kt_base + i * rstep_bytes + goff0);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(vt_base + i * rstep_bytes + goff0);
+      }
+    } else {
+      // Ragged last tile: rows past the end read the last row (always masked).
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int64_t o = (int64_t)min(kt * BN + srow + i * RSTEP, p.skv - 1) * p.kv_ss + scol;
+        kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
+      }
     }
   };
   auto swrite = [&](int stage) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int idx = tid + NT * i;
-      const int row = idx / NC, c = idx % NC;
-      *reinterpret_cast<u32x4 *>(&smem[stage][0][T::chunk_off(row, c)]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&smem[stage][1][T::chunk_off(row, c)]) = vreg[i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][0][woff0 + i * RSTEP * D]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][1][woff0 + i * RSTEP * D]) = vreg[i];
     }
   };
 
@@ -471,7 +543,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
         }
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const int off = T::chunk_off(kb * 32 + col, 2 * s + half);
+          const int off = koff[s] + kb * 32 * D;
           sacc = mfma32(*reinterpret_cast<const bf16x8 *>(ks + off), qf[s], sacc);
           pacc = mfma32(*reinterpret_cast<const bf16x8 *>(vs + off), gf[s], pacc);
         }
@@ -486,7 +558,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2)
-            qacc[db] = mfma32(tr_operand<D>(ks, 32 * kb + 16 * k2, 32 * db, lane), dsf[k2], qacc[db]);
+            qacc[db] = mfma32(tro.read(ks, 32 * kb + 16 * k2, db), dsf[k2], qacc[db]);
       }
     }
     if (kt + 1 < ntiles) swrite(st ^ 1);

@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -122,39 +122,44 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     for (int db = 0; db < DB; ++db)
       troff[u][db] = T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
                                  32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-  int woff[LOADS];                         // staging writes
-  int64_t goff[LOADS];                     // global offset of the chunk within a tile
-  int grow[LOADS], gcol[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int idx = tid + NT * i;
-    const int row = idx / NC, c = idx % NC;
-    woff[i] = T::chunk_off(row, c);
-    goff[i] = (int64_t)row * p.kv_ss + c * 8;
-    grow[i] = row;
-    gcol[i] = c * 8;
-  }
   const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
+  // Staging: thread tid moves chunk (tid % NC) of rows tid / NC + i * RSTEP.
+  // Row steps of RSTEP (a multiple of 16) keep the swizzle, so every load's
+  // LDS and global offsets are the first one's plus a constant.
+  constexpr int RSTEP = NT / NC;
+  static_assert(RSTEP % 16 == 0, "row step must preserve the swizzle");
+  const int srow = tid / NC, scol = 8 * (tid % NC);
+  const int woff0 = T::chunk_off(srow, tid % NC);
+  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
   const int64_t tile_stride = (int64_t)BN * p.kv_ss;
-
+  const int64_t rstep_bytes = (int64_t)RSTEP * p.kv_ss * 2;
   u32x4 kreg[LOADS], vreg[LOADS];
   auto gload = [&](int kt) {
-    // Rows past the end of K/V are read from the last row (always masked).
-    const bool full = kt * BN + BN <= p.skv;
+    if (kt * BN + BN <= p.skv) {
+      // Full tile: scalar tile base plus a 32-bit per-lane byte offset.
+      const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride);
+      const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int64_t o = full ? (int64_t)kt * tile_stride + goff[i]
-                             : (int64_t)min(kt * BN + grow[i], p.skv - 1) * p.kv_ss + gcol[i];
-      kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
-      vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
+      for (int i = 0; i < LOADS; ++i) {
+        kreg[i] = *reinterpret_cast<const u32x4 *>(kt_base + i * rstep_bytes + goff0);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(vt_base + i * rstep_bytes + goff0);
+      }
+    } else {
+      // Ragged last tile: rows past the end read the last row (always masked).
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int64_t o = (int64_t)min(kt * BN + srow + i * RSTEP, p.skv - 1) * p.kv_ss + scol;
+        kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
+      }
     }
   };
   auto swrite = [&](int stage) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      *reinterpret_cast<u32x4 *>(&smem[stage][0][woff[i]]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&smem[stage][1][woff[i]]) = vreg[i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][0][woff0 + i * RSTEP * D]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][1][woff0 + i * RSTEP * D]) = vreg[i];
     }
   };
 
@@ -209,9 +214,10 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3) > t) ? -INFINITY : sacc[i];
     }
     // Online softmax bookkeeping for tile kt.
-    float mx = fmaxf(sacc[0], sacc[1]);
+    float mx = sacc[0];
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[i], sacc[i + 1]));
+    for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), sacc[i + 1]);   // v_max3 chain
+    mx = fmaxf(mx, sacc[15]);
     mx = pair_max(mx) * c;
     const bool upd = mx > m_run + kRescaleSlack;
     if (__any(upd)) {

@@ -58,6 +58,30 @@ __device__ __forceinline__ bf16x8 tr_operand(const __bf16 *tile, int r0, int col
   return __builtin_bit_cast(bf16x8, a);
 }
 
+// Per-lane offsets of the two transpose reads of tr_operand for every 32-wide
+// column block, computed once. A block of rows starting at a multiple of 16
+// only adds a constant (the swizzle depends on the row modulo 16).
+template <int W>
+struct TrOffsets {
+  static constexpr int NB = W / 32;
+  int off[2][NB];
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+        off[u][cb] = Tile<W>::elem_off(8 * u + 4 * (lane >> 5) + ((lane & 15) >> 2),
+                                        32 * cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  }
+  // Operand of rows [r16, r16+16) (r16 a multiple of 16), column block cb.
+  __device__ __forceinline__ bf16x8 read(const __bf16 *tile, int r16, int cb) const {
+    const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + off[0][cb] + r16 * W));
+    const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + off[1][cb] + r16 * W));
+    const i16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, a);
+  }
+};
+
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
