@@ -2,7 +2,7 @@
 """Benchmark of one CP rank's causal attention share on one MI355X.
 
 A step is one pass of the share's hot path over one synthetic batch: the
-forward (out + LSE) and, where built, the backward (dQ and partial dK/dV) of
+forward (out + LSE) and the backward (Delta pass, dK/dV kernel, dQ kernel) of
 the Colossal (all-gather) share of rank 7 of cp=8 at S = 32768: B = 1, 32 query
 heads over 8 KV heads (GQA), head_dim 128, bf16 inputs with fp32 accumulation,
 query rows 28672..32767 against all 32768 keys. Inputs are iid N(0, 1) rounded
@@ -12,8 +12,14 @@ FLOPs are causal-effective: only visible (query, key) pairs count, 4*D per pair
 for the forward and 10*D per pair for the backward (its five contractions,
 including the recomputed Q K^T). Peak: 2.5 PFLOP/s dense bf16 MFMA.
 
+Each kernel's time is the average, over the timed steps, of HIP events the
+library records on the launch stream around it (cp_attn_bwd_timed); the
+roofline object describes the kernel with the largest average. Its "traffic"
+comes from the rocprofv3 counter summaries in profiles/ when one matches the
+kernel's current source text, else null.
+
 Prints ONE JSON line. `--detail` adds every other share of the workload list
-(forward only) to that line under "detail".
+to that line under "detail".
 """
 from __future__ import annotations
 
@@ -29,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
 WORKLOAD = "colossal_cp8_r7_s32k_gqa32x8_d128"
 
 
@@ -39,13 +46,51 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--detail", action="store_true", help="also time every other share (forward)")
+    ap.add_argument("--detail", action="store_true", help="also time every other share")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
 def share_for(spec, rank):
     kind = spec["kind"]
     return kind, spec["cp"], rank, spec.get("ulysses", 2)
+
+
+KERNEL_SOURCES = {   # files whose text determines each kernel's machine code
+    "fwd": ["fwd_bf16.hip", "gfx950_common.h", "plan.h"],
+    "pre": ["bwd_bf16.hip", "gfx950_common.h", "plan.h"],
+    "dkdv": ["bwd_bf16.hip", "gfx950_common.h", "plan.h"],
+    "dq": ["bwd_bf16.hip", "gfx950_common.h", "plan.h"],
+}
+KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128, 1>", "pre": "bwd_pre_kernel<128>",
+                "dkdv": "bwd_dkdv_kernel<128>", "dq": "bwd_dq_kernel<128, 1>"}
+
+
+def sources_sha256(part):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[part]:
+        with open(os.path.join(ROOT, "context_causal_attention_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_record(part):
+    """HBM bytes per launch of a kernel from the rocprofv3 counter summaries in
+    profiles/ (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy of known
+    size), or None when no summary matches the kernel's current source text."""
+    import glob
+    import re
+    want = sources_sha256(part)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            m = re.match(r"traffic-record kernel=(\S+) sources_sha256=([0-9a-f]+) "
+                         r"fetch_bytes=(\d+) write_bytes=(\d+)", line.strip())
+            if m and m.group(1) == KERNEL_NAMES[part].replace(" ", "") and m.group(2) == want:
+                return {"fetch_bytes": int(m.group(3)), "write_bytes": int(m.group(4)),
+                        "source": os.path.relpath(path, ROOT)}
+    return None
 
 
 def time_share(spec, prob, rank, steps, warmup, with_bwd):
@@ -60,48 +105,82 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd):
     scale = 1.0 / math.sqrt(D)
     d = api.make_desc(sh.q, sh.k, sh.v, sh.q.stride(), sh.q_chunk_pos, [0], sh.layout, True, scale)
     pairs = api.cp_attn_share_pairs(d)
-    B, Hq = sh.q.shape[0], sh.q.shape[1]
-    f_fwd = 4.0 * D * B * Hq * pairs
-    f_bwd = 10.0 * D * B * Hq * pairs
+    B, Hq, Sq = sh.q.shape[0], sh.q.shape[1], sh.q.shape[2]
+    Hkv, Skv = sh.k.shape[1], sh.k.shape[2]
     out = torch.empty(sh.q.shape, dtype=sh.q.dtype, device=dev)
     lse = torch.empty(sh.q.shape[:3], dtype=torch.float32, device=dev)
     dout = sh.take_rows(prob.dout.to(dev)).contiguous() if (with_bwd and prob.dout is not None) else None
+    if dout is not None:
+        grads = (torch.empty_like(out), torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=dev),
+                 torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=dev))
+        ws = torch.empty(max(1, api.cp_attn_workspace_bytes(d, True)), dtype=torch.uint8, device=dev)
 
     def fwd():
         api.cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,
                         out=out, lse=lse)
 
-    def bwd():
-        return api.cp_attn_bwd(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, layout=sh.layout,
-                               softmax_scale=scale)
+    def bwd(events):
+        api.cp_attn_bwd_timed(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, events,
+                              layout=sh.layout, softmax_scale=scale, workspace=ws, grads=grads)
+
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
     for _ in range(warmup):
+        ev = new_events()
         fwd()
         if dout is not None:
-            bwd()
+            bwd(ev[1:])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [new_events() for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
+        ev = evs[i]
+        ev[0].record(stream)
         fwd()
-        ev[i][1].record(stream)
+        ev[1].record(stream)
         if dout is not None:
-            bwd()
-        ev[i][2].record(stream)
+            bwd(ev[1:])   # records ev[1] again (same point: nothing runs in between) .. ev[4]
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    bwd_ms = [b.elapsed_time(c) for _, b, c in ev] if dout is not None else []
-    return dict(pairs=pairs, f_fwd=f_fwd, f_bwd=f_bwd if dout is not None else 0.0, total_ms=total_ms,
-                wall_s=wall, fwd_ms=fwd_ms, bwd_ms=bwd_ms, hq=Hq, batch=B, sq=sh.q.shape[2])
+
+    def avg(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in evs) / steps
+
+    ms = {"fwd": avg(0, 1)}
+    if dout is not None:
+        ms.update(pre=avg(1, 2), dkdv=avg(2, 3), dq=avg(3, 4), bwd=avg(1, 4))
+    fl = {"fwd": 4.0 * D * B * Hq * pairs, "bwd": 10.0 * D * B * Hq * pairs,
+          # contractions each kernel performs on visible pairs: dK/dV recomputes
+          # S and dP and forms dV, dK (4 x 2D); dQ recomputes S and dP and forms dQ (3 x 2D)
+          "dkdv": 8.0 * D * B * Hq * pairs, "dq": 6.0 * D * B * Hq * pairs}
+    el = 2 if sh.q.dtype == torch.bfloat16 else 4
+    io = {"pre": 2 * B * Hq * Sq * D * el + 4 * B * Hq * Sq,   # read out, dout; write Delta
+          "fwd": (B * Hq * Sq * D * el * 2 + 2 * B * Hkv * Skv * D * el + 4 * B * Hq * Sq),
+          "dkdv": (2 * B * Hq * Sq * D * el + 2 * B * Hkv * Skv * D * el + 8 * B * Hq * Sq
+                   + 2 * B * Hkv * Skv * D * 4),
+          "dq": (3 * B * Hq * Sq * D * el + 2 * B * Hkv * Skv * D * el + 8 * B * Hq * Sq)}
+    return dict(pairs=pairs, flops=fl, bytes=io, ms=ms, total_ms=total_ms, wall_s=wall,
+                hq=Hq, batch=B, sq=Sq, has_bwd=dout is not None)
+
+
+def copy_calibration(mib):
+    """One plain device-to-device copy of `mib` MiB, for scaling the HBM byte
+    counters of a rocprofv3 --pmc pass over this process."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(spec, prob):
@@ -147,8 +226,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported: every share "
-              "runs on one GPU with the gathered K/V as an input, and no collective is part of this "
-              "build.", file=sys.stderr)
+              "runs on one GPU with the gathered K/V as an input, and this library runs no collective."
+              , file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -166,17 +245,36 @@ def main():
         prob = global_problem(spec["batch"], spec["hq"], spec["hkv"], spec["seq"], spec["head_dim"],
                               spec["dtype"], 0, with_dout=True)
     res = time_share(spec, prob, spec["ranks"][0], args.steps, args.warmup, with_bwd)
+    ms, fl, io = res["ms"], res["flops"], res["bytes"]
     ms_per_step = res["total_ms"] / args.steps
-    flops_step = res["f_fwd"] + res["f_bwd"]
+    flops_step = fl["fwd"] + (fl["bwd"] if res["has_bwd"] else 0.0)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
-    fwd_avg = sum(res["fwd_ms"]) / len(res["fwd_ms"])
-    bwd_avg = sum(res["bwd_ms"]) / len(res["bwd_ms"]) if res["bwd_ms"] else 0.0
-    fwd_tflops = res["f_fwd"] / (fwd_avg * 1e-3) / 1e12
-    bwd_tflops = res["f_bwd"] / (bwd_avg * 1e-3) / 1e12 if bwd_avg else None
-    if bwd_avg > fwd_avg:
-        dom, achieved = "cp_attn_bwd (bwd_main_kernel<128> + pre/convert)", bwd_tflops
-    else:
-        dom, achieved = "fwd_bf16_kernel<128,1>", fwd_tflops
+
+    def tf(f, t):
+        return f / (t * 1e-3) / 1e12
+
+    kernels = {}
+    for part in ("fwd", "pre", "dkdv", "dq"):
+        if part not in ms:
+            continue
+        ent = {"kernel": KERNEL_NAMES[part], "ms": round(ms[part], 4)}
+        if part == "pre":
+            gbs = io[part] / (ms[part] * 1e-3) / 1e9
+            ent.update(bound="hbm", achieved=round(gbs, 1), unit="GB/s", peak=PEAK_HBM_GBS,
+                       frac=round(gbs / PEAK_HBM_GBS, 4))
+        else:
+            a = tf(fl[part], ms[part])
+            ent.update(bound="mfma", achieved=round(a, 2), unit="TFLOP/s", peak=PEAK_BF16_TFLOPS,
+                       frac=round(a / PEAK_BF16_TFLOPS, 4))
+        ent["algorithmic_bytes"] = io[part]
+        kernels[part] = ent
+    dom = max(kernels, key=lambda p: ms[p])
+    tr = traffic_record(dom)
+    roof = dict(kernels[dom])
+    roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if tr else None
+    if tr:
+        roof["traffic_detail"] = tr
+    roof["flops_per_launch"] = fl.get(dom)
     line = {
         "metric": "causal-effective TFLOP/s per CP-rank share (fwd, bwd) and % of bf16 MFMA peak",
         "value": round(value, 2),
@@ -194,14 +292,14 @@ def main():
                    "rank": spec["ranks"][0], "batch": spec["batch"], "hq": spec["hq"], "hkv": spec["hkv"],
                    "head_dim": spec["head_dim"], "seq_global": spec["seq"], "sq_local": res["sq"],
                    "causal_pairs_per_head": res["pairs"],
-                   "passes": "fwd+bwd" if with_bwd else "fwd (backward not built yet)"},
-        "fwd": {"ms": round(fwd_avg, 4), "tflops": round(fwd_tflops, 2),
-                "frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
-        "bwd": ({"ms": round(bwd_avg, 4), "tflops": round(bwd_tflops, 2),
-                 "frac_of_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4)} if bwd_avg else None),
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                   "passes": "fwd+bwd" if res["has_bwd"] else "fwd"},
+        "fwd": {"ms": round(ms["fwd"], 4), "tflops": round(tf(fl["fwd"], ms["fwd"]), 2),
+                "frac_of_peak": round(tf(fl["fwd"], ms["fwd"]) / PEAK_BF16_TFLOPS, 4)},
+        "bwd": ({"ms": round(ms["bwd"], 4), "tflops": round(tf(fl["bwd"], ms["bwd"]), 2),
+                 "frac_of_peak": round(tf(fl["bwd"], ms["bwd"]) / PEAK_BF16_TFLOPS, 4)}
+                if res["has_bwd"] else None),
+        "roofline": roof,
+        "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
     }
     if args.detail:
@@ -213,18 +311,19 @@ def main():
             _, pr = workload(name, seed=0)
             for r in sp["ranks"]:
                 rr = time_share(sp, pr, r, max(5, args.steps // 2), 2, bw)
-                avg = sum(rr["fwd_ms"]) / len(rr["fwd_ms"])
-                tf = rr["f_fwd"] / (avg * 1e-3) / 1e12
-                ent = {"fwd_ms": round(avg, 4), "fwd_tflops": round(tf, 2),
-                       "fwd_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-                if bw:
-                    bavg = sum(rr["bwd_ms"]) / len(rr["bwd_ms"])
-                    btf = rr["f_bwd"] / (bavg * 1e-3) / 1e12
-                    ent.update({"bwd_ms": round(bavg, 4), "bwd_tflops": round(btf, 2),
-                                "bwd_frac": round(btf / PEAK_BF16_TFLOPS, 4)})
+                t = rr["ms"]
+                ent = {"fwd_ms": round(t["fwd"], 4), "fwd_tflops": round(tf(rr["flops"]["fwd"], t["fwd"]), 2),
+                       "fwd_frac": round(tf(rr["flops"]["fwd"], t["fwd"]) / PEAK_BF16_TFLOPS, 4)}
+                if rr["has_bwd"]:
+                    btf = tf(rr["flops"]["bwd"], t["bwd"])
+                    ent.update({"bwd_ms": round(t["bwd"], 4), "bwd_tflops": round(btf, 2),
+                                "bwd_frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                                "dkdv_ms": round(t["dkdv"], 4), "dq_ms": round(t["dq"], 4)})
                 detail[f"{name}/r{r}"] = ent
             del pr
         line["detail"] = detail
+    if args.copy_calib_mib:
+        copy_calibration(args.copy_calib_mib)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(spec, prob)
     print(json.dumps(line), flush=True)

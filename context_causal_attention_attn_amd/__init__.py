@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     cp_attn_plan_stats_fwd,
     cp_attn_fwd,
     cp_attn_bwd,
+    cp_attn_bwd_timed,
     make_desc,
 )
 from .shares import Share, cut_share  # noqa: F401

@@ -68,6 +68,11 @@ SIGNATURES = {
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "cp_attn_bwd_timed": (_i32, [ctypes.POINTER(CpAttnDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_void_p), _i32]),
 }
 
 _lib = None

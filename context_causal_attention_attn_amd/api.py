@@ -143,8 +143,37 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
 
 def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="contiguous",
                 kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
-                softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
-    """Backward of one share: returns (dq in q's dtype, dk, dv float32 partials over the gathered K/V)."""
+                softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                grads: Optional[tuple] = None):
+    """Backward of one share: returns (dq in q's dtype, dk, dv float32 partials over the gathered K/V).
+
+    grads, if given, is a (dq, dk, dv) triple of preallocated outputs: dq with
+    out's strides, dk/dv contiguous float32 [B, Hkv, Skv, D].
+    """
+    return _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal,
+                softmax_scale, workspace, grads, None)
+
+
+def cp_attn_bwd_timed(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], events, *,
+                      layout="contiguous", kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
+                      softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                      grads: Optional[tuple] = None):
+    """cp_attn_bwd with four torch.cuda.Event (enable_timing=True) recorded by the
+    library on the current stream around its phases (for bf16: Delta pass,
+    dK/dV kernel, dQ kernel), so events[i].elapsed_time(events[i+1]) is phase i+1."""
+    if len(events) != 4:
+        raise ValueError("cp_attn_bwd_timed needs exactly four events")
+    stream = torch.cuda.current_stream(q.device)
+    for e in events:
+        if not e.cuda_event:   # torch creates the HIP event on first record
+            e.record(stream)
+    handles = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    return _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal,
+                softmax_scale, workspace, grads, handles)
+
+
+def _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal, softmax_scale,
+         workspace, grads, events):
     lib = _lib.load()
     _check_inputs(q, k, v)
     B, Hq, Sq, D = q.shape
@@ -155,15 +184,26 @@ def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="
         out, dout = out.contiguous(), dout.contiguous()
     if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
-    dq = torch.empty_strided(out.shape, out.stride(), dtype=q.dtype, device=q.device)
-    dk = torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=q.device)
-    dv = torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=q.device)
+    if grads is None:
+        dq = torch.empty_strided(out.shape, out.stride(), dtype=q.dtype, device=q.device)
+        dk = torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=q.device)
+        dv = torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv = grads
+        if dq.shape != q.shape or dq.dtype != q.dtype or dq.stride() != out.stride():
+            raise ValueError("dq must match q's shape and dtype, with out's strides")
+        for t in (dk, dv):
+            if t.shape != (B, Hkv, Skv, D) or t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError("dk and dv must be contiguous float32 [B, Hkv, Skv, D] tensors")
     d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale)
     need = cp_attn_workspace_bytes(d, True)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    check(lib.cp_attn_bwd(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                          _stream_handle(q)), "cp_attn_bwd")
+    args = (d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(q))
+    if events is None:
+        check(lib.cp_attn_bwd(*args), "cp_attn_bwd")
+    else:
+        check(lib.cp_attn_bwd_timed(*args, events, 4), "cp_attn_bwd_timed")
     return dq, dk, dv

@@ -579,17 +579,23 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 }
 
 template <int D>
-int launch_d(const BwdParams &p, void *stream) {
+int launch_d(const BwdParams &p, void *stream, void *const *events) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) {
+    return events ? (int)hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : 0;
+  };
+  if (int e = mark(0)) return e;
   const int64_t rows = (int64_t)p.batch * p.hq * p.sq;
   if (rows > 0) {
     const int64_t blocks = (rows * 16 + 255) / 256;
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(blocks), dim3(256), 0, s, p);
   }
+  if (int e = mark(1)) return e;
   const int64_t kv_tiles = (p.skv + BK - 1) / BK;
   if (kv_tiles > 0) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(kv_tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
   }
+  if (int e = mark(2)) return e;
   const int64_t items = (int64_t)p.n_head_packs * p.n_q_chunks * p.tiles_per_chunk;
   if (rows > 0 && items > 0) {
     const int rb = kFwdWaves / p.heads_per_item;
@@ -600,14 +606,15 @@ int launch_d(const BwdParams &p, void *stream) {
       default: return (int)hipErrorInvalidValue;
     }
   }
+  if (int e = mark(3)) return e;
   return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_bwd_bf16(const BwdParams &p, int head_dim, void *stream) {
-  if (head_dim == 128) return launch_d<128>(p, stream);
-  if (head_dim == 64) return launch_d<64>(p, stream);
+int launch_bwd_bf16(const BwdParams &p, int head_dim, void *stream, void *const *events) {
+  if (head_dim == 128) return launch_d<128>(p, stream, events);
+  if (head_dim == 64) return launch_d<64>(p, stream, events);
   return (int)hipErrorInvalidValue;
 }
 

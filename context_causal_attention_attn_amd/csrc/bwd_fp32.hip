@@ -106,24 +106,31 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
 }
 
 template <int D>
-int launch_d(const BwdParams &p, void *stream) {
+int launch_d(const BwdParams &p, void *stream, void *const *events) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) {
+    return events ? (int)hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : 0;
+  };
+  if (int e = mark(0)) return e;
   if (p.sq > 0) {
     dim3 g1((p.sq + 63) / 64, p.hq, p.batch);
     hipLaunchKernelGGL(bwd_fp32_delta_dq_kernel<D>, g1, dim3(64), 0, s, p);
   }
+  if (int e = mark(1)) return e;
   if (p.skv > 0) {
     dim3 g2((p.skv + 63) / 64, p.hkv, p.batch);
     hipLaunchKernelGGL(bwd_fp32_dkv_kernel<D>, g2, dim3(64), 0, s, p);
   }
+  if (int e = mark(2)) return e;
+  if (int e = mark(3)) return e;
   return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_bwd_fp32(const BwdParams &p, int head_dim, void *stream) {
-  if (head_dim == 128) return launch_d<128>(p, stream);
-  if (head_dim == 64) return launch_d<64>(p, stream);
+int launch_bwd_fp32(const BwdParams &p, int head_dim, void *stream, void *const *events) {
+  if (head_dim == 128) return launch_d<128>(p, stream, events);
+  if (head_dim == 64) return launch_d<64>(p, stream, events);
   return (int)hipErrorInvalidValue;
 }
 

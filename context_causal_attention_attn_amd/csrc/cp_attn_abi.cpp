@@ -282,16 +282,22 @@ int32_t cp_attn_fwd(const cp_attn_desc *d, const void *q, const void *k, const v
   return e == 0 ? CP_ATTN_OK : CP_ATTN_ERR_HIP;
 }
 
-int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
-                    const void *out, const float *lse, const void *dout, void *dq, float *dk,
-                    float *dv, void *workspace, size_t workspace_bytes, void *stream) {
+int32_t cp_attn_bwd_timed(const cp_attn_desc *d, const void *q, const void *k, const void *v,
+                          const void *out, const float *lse, const void *dout, void *dq, float *dk,
+                          float *dv, void *workspace, size_t workspace_bytes, void *stream,
+                          void *const *events, int32_t n_events) {
   int32_t st = validate(d);
   if (st) return st;
+  if (!(n_events == 0 && events == nullptr) && n_events != 4) return CP_ATTN_ERR_BAD_SHAPE;
+  if (n_events == 4) {
+    if (!events) return CP_ATTN_ERR_NULL_PTR;
+    for (int i = 0; i < 4; ++i)
+      if (!events[i]) return CP_ATTN_ERR_NULL_PTR;
+  }
   size_t need = 0;
   cp_attn_workspace_bytes(d, 1, &need);
   if (d->sq_local > 0 && (!q || !out || !lse || !dout || !dq)) return CP_ATTN_ERR_NULL_PTR;
   if (d->skv > 0 && (!k || !v || !dk || !dv)) return CP_ATTN_ERR_NULL_PTR;
-  if (d->sq_local == 0 && d->skv == 0) return CP_ATTN_OK;
   if (need > 0 && (!workspace || workspace_bytes < need)) return CP_ATTN_ERR_WORKSPACE;
   const void *ptrs16[] = {q, out, dout, dq, k, v, dk, dv, workspace};
   for (const void *ptr : ptrs16)
@@ -304,9 +310,17 @@ int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const v
   p.q = q; p.k = k; p.v = v; p.out = out; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.delta = static_cast<float *>(workspace);
-  const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream)
-                                           : launch_bwd_fp32(p, d->head_dim, stream);
+  void *const *ev = n_events == 4 ? events : nullptr;
+  const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream, ev)
+                                           : launch_bwd_fp32(p, d->head_dim, stream, ev);
   return e == 0 ? CP_ATTN_OK : CP_ATTN_ERR_HIP;
+}
+
+int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
+                    const void *out, const float *lse, const void *dout, void *dq, float *dk,
+                    float *dv, void *workspace, size_t workspace_bytes, void *stream) {
+  return cp_attn_bwd_timed(d, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                           stream, nullptr, 0);
 }
 
 }  // extern "C"

@@ -115,7 +115,8 @@ int64_t fwd_grid_size(const FwdParams &p);
 // Launchers (defined with their kernels); return a hipError_t as int.
 int launch_fwd_bf16(const FwdParams &p, int head_dim, void *stream);
 int launch_fwd_fp32(const FwdParams &p, int head_dim, void *stream);
-int launch_bwd_bf16(const BwdParams &p, int head_dim, void *stream);
-int launch_bwd_fp32(const BwdParams &p, int head_dim, void *stream);
+// `events` is NULL or four hipEvent_t recorded at the phase boundaries.
+int launch_bwd_bf16(const BwdParams &p, int head_dim, void *stream, void *const *events);
+int launch_bwd_fp32(const BwdParams &p, int head_dim, void *stream, void *const *events);
 
 }  // namespace cpattn

@@ -68,7 +68,7 @@ typedef enum {
   CP_ATTN_ERR_BAD_SHAPE = -2,     /* sizes/strides inconsistent (hq % hkv, chunk lengths, ...) */
   CP_ATTN_ERR_BAD_LAYOUT = -3,    /* layout vs chunk count, or unknown layout */
   CP_ATTN_ERR_BAD_POSITIONS = -4, /* negative or overlapping chunk positions */
-  CP_ATTN_ERR_UNSUPPORTED = -5,   /* head_dim / dtype / chunk table this build does not implement */
+  CP_ATTN_ERR_UNSUPPORTED = -5,   /* head_dim / dtype / chunk table the library does not implement */
   CP_ATTN_ERR_WORKSPACE = -6,     /* workspace NULL or smaller than cp_attn_workspace_bytes() */
   CP_ATTN_ERR_HIP = -7,           /* a HIP launch or query failed */
   CP_ATTN_ERR_ABI = -8,           /* desc->abi_version != CP_ATTN_ABI_VERSION */
@@ -109,7 +109,7 @@ typedef struct cp_attn_desc {
   int64_t skv;                 /* gathered key/value rows */
   int32_t n_q_chunks;          /* 1..CP_ATTN_MAX_Q_CHUNKS, equal lengths */
   const int64_t *q_chunk_pos;  /* host array [n_q_chunks]: global position of each chunk's row 0 */
-  int32_t n_kv_chunks;         /* this build: 1 (keys in natural order from kv_chunk_pos[0]) */
+  int32_t n_kv_chunks;         /* must be 1 (keys in natural order from kv_chunk_pos[0]) */
   const int64_t *kv_chunk_pos; /* host array [n_kv_chunks] */
   int32_t layout;              /* cp_attn_layout: contiguous needs 1 Q chunk, head_tail needs 2 */
   int32_t causal;              /* 1: global-position causal mask, 0: no mask */
@@ -192,6 +192,24 @@ int32_t cp_attn_bwd(const cp_attn_desc *desc, const void *q, const void *k, cons
                     const void *out, const float *lse, const void *dout,
                     void *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * cp_attn_bwd with its phases bracketed by caller-owned HIP events, for
+ * per-kernel timing on the caller's stream. `events` holds n_events
+ * hipEvent_t handles (n_events must be 4, or events NULL and n_events 0,
+ * which makes this call identical to cp_attn_bwd). They are recorded on
+ * `stream` before phase 1 and after phases 1, 2 and 3:
+ *   bf16: 1 = Delta pre-pass, 2 = dK/dV kernel, 3 = dQ kernel;
+ *   fp32: 1 = Delta + dQ kernel, 2 = dK/dV kernel, 3 = nothing.
+ * A phase with no work still records its events. Results are bitwise those
+ * of cp_attn_bwd. Errors as cp_attn_bwd; CP_ATTN_ERR_NULL_PTR when
+ * n_events is 4 and an event is NULL, CP_ATTN_ERR_BAD_SHAPE for any other
+ * n_events. Events are not recorded when validation fails.
+ */
+int32_t cp_attn_bwd_timed(const cp_attn_desc *desc, const void *q, const void *k, const void *v,
+                          const void *out, const float *lse, const void *dout,
+                          void *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
+                          void *stream, void *const *events, int32_t n_events);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,7 @@ status; the host-side share geometry, pair counts and the forward tile
 schedule are checked against the oracle's geometry and the page-derived
 golden tables.
 """
+import ctypes
 import json
 import os
 import re
@@ -83,7 +84,7 @@ def test_validate_accepts_good_descriptors():
     (dict(layout="head_tail", q_chunk_pos=[0, 100], sq_local=500), -4),   # overlapping chunks
     (dict(q_chunk_pos=[-1]), -4),
     (dict(layout="head_tail", q_chunk_pos=[0, 300], sq_local=501), -2),   # unequal chunks
-    (dict(kv_chunk_pos=[0, 1000]), -5),                       # KV chunk tables: not in this build
+    (dict(kv_chunk_pos=[0, 1000]), -5),                       # KV chunk tables: not implemented
     (dict(softmax_scale=float("nan")), -2),
     (dict(softmax_scale=0.0), -2),
     (dict(q_strides=(8 * 2000 * 128, 2000 * 128, 132)), -9),   # row stride breaks 16-byte alignment
@@ -171,3 +172,18 @@ def test_workspace_bytes():
     assert cp_attn_workspace_bytes(d, False) == 0
     rows = 1 * 8 * 500
     assert cp_attn_workspace_bytes(d, True) == ((rows * 4 + 255) // 256) * 256
+
+
+def test_bwd_timed_rejects_bad_event_arrays_before_any_device_work():
+    # Host-side checks only: every call below returns before touching a device.
+    lib = _lib.load()
+    d = desc()
+    fake = [256 * (i + 1) for i in range(10)]
+    ev4 = (ctypes.c_void_p * 4)(256, 512, 768, 1024)
+    ev_null = (ctypes.c_void_p * 4)(256, None, 768, 1024)
+    args = (d.ref(), *fake[:6], *fake[6:9], fake[9], 1 << 30, None)
+    assert lib.cp_attn_bwd_timed(*args, ev4, 3) == -2
+    assert lib.cp_attn_bwd_timed(*args, None, 4) == -1
+    assert lib.cp_attn_bwd_timed(*args, ev_null, 4) == -1
+    bad = desc(batch=0)
+    assert lib.cp_attn_bwd_timed(bad.ref(), *args[1:], ev4, 4) == -2

@@ -166,3 +166,25 @@ def test_full_size_head_tail_backward_sampled(htbwd_problem, rank):
     last = int(osh["q_pos"].max())
     assert torch.all(dk[:, :, last + 1:] == 0) and torch.all(dv[:, :, last + 1:] == 0)
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_timed_backward_matches_untimed(dtype):
+    # cp_attn_bwd_timed runs the same kernels with events between them: the
+    # gradients must be bitwise those of cp_attn_bwd, and every phase's time
+    # non-negative (the dK/dV phase strictly positive).
+    from context_causal_attention_attn_amd import cp_attn_bwd_timed
+    S, Hq, Hkv, D = (1200, 8, 2, 128) if dtype == "bf16" else (240, 2, 2, 64)
+    prob = global_problem(1, Hq, Hkv, S, D, dtype, 3, with_dout=True)
+    sh, dq, dk, dv, scale = gpu_share_grads(prob, "head_tail", 3, 1)
+    dev = torch.device("cuda")
+    out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale)
+    dout = sh.take_rows(prob.dout.to(dev))
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    g = cp_attn_bwd_timed(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, events, layout=sh.layout,
+                          softmax_scale=scale)
+    torch.cuda.synchronize()
+    for a, b, n in zip((dq, dk, dv), g, ("dq", "dk", "dv")):
+        assert torch.equal(a, b), n
+    times = [events[i].elapsed_time(events[i + 1]) for i in range(3)]
+    assert min(times) >= 0.0 and times[1] > 0.0, times
