@@ -11,14 +11,18 @@
 //
 // Three launches, no atomics:
 //  1. bwd_pre: Delta for every local row.
-//  2. bwd_dkdv (key-stationary): one workgroup of 4 wavefronts per 128-key
-//     tile of one KV head. Each wavefront owns 32 keys, keeps their K and V
-//     rows (MFMA B operands) and their dK^T/dV^T accumulators in registers,
-//     and streams the 32-row query tiles -- of every head of the GQA group and
-//     every chunk -- that can see one of its keys: S = Q K^T and dP = dO V^T
-//     with the key as the lane's column, P and dS in registers, then
-//     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read by LDS
-//     transpose reads. Query tiles wholly before the keys are never visited.
+//  2. bwd_dkdv (key-stationary): one workgroup of 8 wavefronts per 128-key
+//     tile of one KV head; it streams the 32-row query tiles -- of every
+//     head of the GQA group and every chunk -- that can see one of its keys.
+//     Four "scorer" wavefronts own 32 keys each and keep their K and V rows
+//     (MFMA B operands) in registers: S = Q K^T and dP = dO V^T with the key
+//     as the lane's column, then P and dS (bf16) are written to LDS. Four
+//     "accumulator" wavefronts own the dK^T/dV^T accumulators of the same
+//     keys and, one query tile behind, run dV^T += dO^T P and dK^T += Q^T dS
+//     with dO^T and Q^T from LDS transpose reads. Splitting the roles keeps
+//     each wavefront's registers within budget and lets the two halves'
+//     matrix work overlap. Query tiles wholly before the keys are never
+//     visited.
 //  3. bwd_dq (query-stationary, scheduled like the forward): the transposed
 //     tiles S^T = K Q^T and dP^T = V dO^T put the query in the lane, so P^T and
 //     dS^T come from the saved LSE and Delta with per-lane scalars and feed
