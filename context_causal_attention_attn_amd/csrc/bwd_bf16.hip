@@ -41,7 +41,7 @@ namespace {
 constexpr int BK = kBwdBlockKV;   // keys per key-stationary workgroup
 constexpr int BQ = kBwdBlockQ;    // query rows per step of that workgroup
 constexpr int BN = kDqBlockKV;    // keys per tile of the query-stationary kernel
-constexpr int NT = 256;
+constexpr int NT = kFwdWaves * 64;
 
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008;
@@ -76,10 +76,6 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------
-struct StepGeom {
-  int chunk, tile, head_in_group;
-};
-
 // One workgroup of 8 wavefronts per 128-key tile of one KV head, in two
 // roles sharing the tile's 4 x 32 keys:
 //  * score wavefronts (0..3) keep their keys' K and V rows in registers and,
@@ -130,36 +126,39 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   const bool key_ok = my_key < p.skv;
   const int64_t kv_lo = p.kv_pos0 + key0;
 
-  // Query tiles this key tile meets, chunk by chunk.
+  // Query tiles this key tile meets: per chunk, tiles first_tile(c) ..
+  // nq_tiles-1, each for every head of the GQA group. A cursor walks them in
+  // that order (chunk, tile, head), one step per tile of one head.
   const int nq_tiles = (p.chunk_len + BQ - 1) / BQ;
-  int first_tile[kMaxQChunks];
-  int total = 0;
-  for (int c = 0; c < p.n_q_chunks; ++c) {
-    int t0 = 0;
-    if (p.causal) {
-      const int64_t rel = kv_lo - p.chunk_pos[c];
-      t0 = rel <= 0 ? 0 : (int)min<int64_t>(nq_tiles, rel / BQ);
-    }
-    first_tile[c] = t0;
-    total += (nq_tiles - t0) * p.group;
-  }
-  auto decode = [&](int it) {
-    StepGeom sg{0, 0, 0};
-    for (int c = 0; c < p.n_q_chunks; ++c) {
-      const int n = (nq_tiles - first_tile[c]) * p.group;
-      if (it < n) {
-        sg.chunk = c;
-        sg.tile = first_tile[c] + it / p.group;
-        sg.head_in_group = it % p.group;
-        return sg;
-      }
-      it -= n;
-    }
-    return sg;
+  auto first_tile = [&](int c) {
+    if (!p.causal) return 0;
+    const int64_t rel = kv_lo - p.chunk_pos[c];
+    return rel <= 0 ? 0 : (int)min<int64_t>(nq_tiles, rel / BQ);
   };
+  int total = 0;
+  for (int c = 0; c < p.n_q_chunks; ++c) total += (nq_tiles - first_tile(c)) * p.group;
+  struct Cursor {
+    int c, t, h;
+  };
+  auto skip_empty = [&](Cursor &u) {
+    while (u.c < p.n_q_chunks && u.t >= nq_tiles) {
+      ++u.c;
+      u.t = u.c < p.n_q_chunks ? first_tile(u.c) : 0;
+    }
+  };
+  auto advance = [&](Cursor &u) {
+    if (++u.h == p.group) {
+      u.h = 0;
+      ++u.t;
+      skip_empty(u);
+    }
+  };
+  Cursor c0{0, first_tile(0), 0};
+  skip_empty(c0);
 
-  // Staging of query tiles: loaded into registers at the start of a step and
-  // written to the LDS ring at its end, one step ahead of use.
+  // Staging of query tiles (Q, dO and the rows' LSE and Delta): loaded into
+  // registers two steps ahead and written to the LDS ring one step ahead of
+  // use, through two register sets.
   int woff[Q_LOADS], grow[Q_LOADS], gcol[Q_LOADS];
 #pragma unroll
   for (int i = 0; i < Q_LOADS; ++i) {
@@ -173,19 +172,19 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     float aux;   // raw LSE (threads 0..31) or Delta (threads 32..63) of one row
     int ok;      // that row lies inside the chunk
   };
-  Staged reg0;
   // Wave-uniform copies of the two row-statistics pointers: selecting between
   // them per lane must not turn into a per-lane load of the pointer itself.
   const float *const lse_ptr = p.lse;
   const float *const delta_ptr = p.delta;
+  const int rr = tid % BQ;
   // Loads only: anything computed from the loaded values waits until swrite,
-  // so the loads stay in flight during the step's compute.
-  auto gload = [&](int it, Staged &r) {
-    const StepGeom sg = decode(it);
-    const int head = hk * p.group + sg.head_in_group;
-    const int row0 = sg.tile * BQ;
+  // so the loads stay in flight. Every thread loads (the statistics too), so
+  // that all paths carry the same number of loads.
+  auto gload = [&](const Cursor &u, Staged &r) {
+    const int head = hk * p.group + u.h;
+    const int row0 = u.t * BQ;
     const int last = p.chunk_len - 1;   // rows past the chunk end read its last row
-    const int64_t rbase = (int64_t)sg.chunk * p.chunk_len;
+    const int64_t rbase = (int64_t)u.c * p.chunk_len;
     const __bf16 *qg = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh;
     const __bf16 *og = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh;
 #pragma unroll
@@ -194,12 +193,9 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
       r.q[i] = *reinterpret_cast<const u32x4 *>(qg + lr * p.q_ss + gcol[i]);
       r.o[i] = *reinterpret_cast<const u32x4 *>(og + lr * p.o_ss + gcol[i]);
     }
-    if (tid < 2 * BQ) {
-      const int rr = tid % BQ;
-      r.ok = row0 + rr < p.chunk_len;
-      const int64_t idx = ((int64_t)b * p.hq + head) * p.sq + rbase + min(row0 + rr, last);
-      r.aux = (tid < BQ ? lse_ptr : delta_ptr)[idx];
-    }
+    r.ok = row0 + rr < p.chunk_len;
+    const int64_t idx = ((int64_t)b * p.hq + head) * p.sq + rbase + min(row0 + rr, last);
+    r.aux = (tid < BQ ? lse_ptr : delta_ptr)[idx];
   };
   auto swrite = [&](int st, const Staged &r) {
 #pragma unroll
@@ -214,19 +210,39 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     if (tid < BQ) lse_s[st][tid] = (!r.ok || r.aux == -INFINITY) ? INFINITY : r.aux * kLog2e;
     else if (tid < 2 * BQ) dl_s[st][tid - BQ] = r.ok ? r.aux : 0.0f;
   };
-
+  // Load cursor: the step whose tile the next gload fetches. Past the last
+  // step it stays on the last one (the loads are then repeated, unused).
+  Cursor cl = c0;
+  auto next_load = [&](int step_to_load) {
+    if (step_to_load < total) advance(cl);
+  };
+  Staged sa, sb;   // register sets: step s is loaded into (s % 2 ? sb : sa)
   const float c2 = p.scale_log2;
   const bool wave_keys_ok = wkey0 + 31 < p.skv;
 
+  // Prologue: step 0 staged, step 1 in registers.
   if (total > 0) {
-    gload(0, reg0);
-    swrite(0, reg0);
+    gload(cl, sa);
+    swrite(0, sa);
+    next_load(1);
+    gload(cl, sb);
   }
   __syncthreads();
 
   // Step it: scorers handle query tile it (it < total), accumulators tile
-  // it-1 (it >= 1); tile it+1 is loaded meanwhile. The two roles run separate
-  // loops (so their register sets do not add up) with the same barriers.
+  // it-1 (it >= 1); tile it+2 is loaded and tile it+1 written to the ring
+  // meanwhile. The two roles run separate loops (so their register sets do
+  // not add up) with the same barriers. Each loop is unrolled by two so that
+  // the register sets alternate at compile time.
+  // (Only called when total > 0, so the load cursor is always valid.)
+  auto staging_begin = [&](int it, Staged &ld) {
+    next_load(it + 2);
+    gload(cl, ld);
+  };
+  auto staging_end = [&](int it, const Staged &wr) {
+    if (it + 1 < total) swrite((it + 1) % QSTAGES, wr);
+    __syncthreads();
+  };
   if (scorer) {
     bf16x8 kf[KSTEPS], vf[KSTEPS];   // K and V rows of this lane's key
     int qoff[KSTEPS];                // A-operand reads of the Q and dO rows
@@ -242,14 +258,14 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
       }
       wait_vmem_all();
     }
-    for (int it = 0; it <= total; ++it) {
-      if (it + 1 < total) gload(it + 1, reg0);
+    Cursor cs = c0;   // the step being scored
+    auto score = [&](int it, Staged &ld, const Staged &wr) {
+      staging_begin(it, ld);
       if (it < total) {
         const int st = it % QSTAGES;
-        const StepGeom sg = decode(it);
         const __bf16 *qs = q_s[st];
         const __bf16 *os = do_s[st];
-        const int64_t qpos0 = p.chunk_pos[sg.chunk] + sg.tile * BQ;
+        const int64_t qpos0 = p.chunk_pos[cs.c] + cs.t * BQ;
         f32x16 sacc, pacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -306,9 +322,15 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
         xs[xst][kw][0][1][lane] = pf[1];
         xs[xst][kw][1][0][lane] = dsf[0];
         xs[xst][kw][1][1][lane] = dsf[1];
+        advance(cs);
       }
-      if (it + 1 < total) swrite((it + 1) % QSTAGES, reg0);
-      __syncthreads();
+      staging_end(it, wr);
+    };
+    if (total > 0) {
+      for (int it = 0; it <= total; it += 2) {
+        score(it, sa, sb);
+        if (it + 1 <= total) score(it + 1, sb, sa);
+      }
     }
     return;
   }
@@ -323,8 +345,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
       dv[db][i] = 0.0f;
       dk[db][i] = 0.0f;
     }
-  for (int it = 0; it <= total; ++it) {
-    if (it + 1 < total) gload(it + 1, reg0);
+  auto accumulate = [&](int it, Staged &ld, const Staged &wr) {
+    staging_begin(it, ld);
     if (it >= 1) {
       const int pst = (it + QSTAGES - 1) % QSTAGES;
       const int xst = (it - 1) & 1;
@@ -359,8 +381,13 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * DB, 0);
     }
-    if (it + 1 < total) swrite((it + 1) % QSTAGES, reg0);
-    __syncthreads();
+    staging_end(it, wr);
+  };
+  if (total > 0) {
+    for (int it = 0; it <= total; it += 2) {
+      accumulate(it, sa, sb);
+      if (it + 1 <= total) accumulate(it + 1, sb, sa);
+    }
   }
 
   if (!key_ok) return;
@@ -604,9 +631,9 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
   if (rows > 0 && items > 0) {
     const int rb = kFwdWaves / p.heads_per_item;
     switch (rb) {
-      case 1: hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), dim3(items), dim3(NT), 0, s, p); break;
       case 2: hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3(items), dim3(NT), 0, s, p); break;
       case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3(items), dim3(NT), 0, s, p); break;
+      case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, 8>), dim3(items), dim3(NT), 0, s, p); break;
       default: return (int)hipErrorInvalidValue;
     }
   }

@@ -56,8 +56,9 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = BN * D;
-  constexpr int LOADS = BN * NC / NT;
-  static_assert(BN == 32 && LOADS >= 1, "tile shape");
+  constexpr int CHUNKS = BN * NC;      // 16-byte chunks per K (or V) tile
+  constexpr int LOADS = (CHUNKS + NT - 1) / NT;
+  static_assert(BN == 32 && (CHUNKS % NT == 0 || LOADS == 1), "tile shape");
   using T = Tile<D>;
 
   __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES][2][TILE];  // [stage][K,V]
@@ -134,34 +135,45 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
   const int64_t tile_stride = (int64_t)BN * p.kv_ss;
   const int64_t rstep_bytes = (int64_t)RSTEP * p.kv_ss * 2;
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int kt) {
+  // Two register sets: tile t is loaded into set t % 2 two steps before it is
+  // written to the LDS ring, which gives each load two steps of latency cover.
+  u32x4 kreg[2][LOADS], vreg[2][LOADS];
+  // With fewer chunks than threads (D = 64) only the first CHUNKS threads stage.
+  const bool stager = (CHUNKS % NT == 0) || tid < CHUNKS;
+  auto gload = [&](int kt, auto set_tag) {
+    constexpr int SET = decltype(set_tag)::value;
+    if (!stager) return;
     if (kt * BN + BN <= p.skv) {
       // Full tile: scalar tile base plus a 32-bit per-lane byte offset.
       const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride);
       const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        kreg[i] = *reinterpret_cast<const u32x4 *>(kt_base + i * rstep_bytes + goff0);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(vt_base + i * rstep_bytes + goff0);
+        kreg[SET][i] = *reinterpret_cast<const u32x4 *>(kt_base + i * rstep_bytes + goff0);
+        vreg[SET][i] = *reinterpret_cast<const u32x4 *>(vt_base + i * rstep_bytes + goff0);
       }
     } else {
       // Ragged last tile: rows past the end read the last row (always masked).
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int64_t o = (int64_t)min(kt * BN + srow + i * RSTEP, p.skv - 1) * p.kv_ss + scol;
-        kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
+        kreg[SET][i] = *reinterpret_cast<const u32x4 *>(kbase + o);
+        vreg[SET][i] = *reinterpret_cast<const u32x4 *>(vbase + o);
       }
     }
   };
-  auto swrite = [&](int stage) {
+  auto swrite = [&](int stage, auto set_tag) {
+    constexpr int SET = decltype(set_tag)::value;
+    if (!stager) return;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      *reinterpret_cast<u32x4 *>(&smem[stage][0][woff0 + i * RSTEP * D]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&smem[stage][1][woff0 + i * RSTEP * D]) = vreg[i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][0][woff0 + i * RSTEP * D]) = kreg[SET][i];
+      *reinterpret_cast<u32x4 *>(&smem[stage][1][woff0 + i * RSTEP * D]) = vreg[SET][i];
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -177,12 +189,13 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
   if (ntiles > 0) {
-    gload(0);
-    swrite(0);
+    gload(0, I0{});
+    swrite(0, I0{});
     if (ntiles > 1) {
-      gload(1);
-      swrite(1);
+      gload(1, I1{});
+      swrite(1, I1{});
     }
+    gload(min(2, ntiles - 1), I0{});
   }
   __syncthreads();
   if (ntiles > 0) {
@@ -192,12 +205,18 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       sacc = mfma32(*reinterpret_cast<const bf16x8 *>(ks + koff[s]), qf[s], sacc);
   }
 
-  // One step of the pipeline on tile kt held in stage ST (kt % 3 == ST).
-  auto step = [&](auto st_tag, int kt) {
+  // One step of the pipeline on tile kt held in stage ST (kt % 3 == ST);
+  // PAR = kt % 2 selects the register set of tile kt + 2 (written to the ring
+  // at the end of this step); tile kt + 3 is loaded into the other set.
+  auto step = [&](auto st_tag, auto par_tag, int kt) {
     constexpr int ST = decltype(st_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
     constexpr int NEXT = (ST + 1) % STAGES;
     constexpr int FREE = (ST + 2) % STAGES;
-    if (kt + 2 < ntiles) gload(kt + 2);
+    // Unconditional (past the end it re-reads the last tile): every path then
+    // has the same number of loads in flight, so the wait before the ring
+    // write below covers only the older set.
+    gload(min(kt + 3, ntiles - 1), std::integral_constant<int, 1 - PAR>{});
     const int64_t tile_plo = p.kv_pos0 + (int64_t)kt * BN;
 
     // Mask (diagonal or ragged tiles only): key 8*(i/4) + 4*half + i%4 of the
@@ -268,15 +287,18 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
         const i16x8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pf[k2], oacc[db]);
       }
-    if (kt + 2 < ntiles) swrite(FREE);
+    if (kt + 2 < ntiles) swrite(FREE, par_tag);
     __syncthreads();
     sacc = snext;
   };
 
-  for (int kt = 0; kt < ntiles; kt += STAGES) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < ntiles) step(std::integral_constant<int, 1>{}, kt + 1);
-    if (kt + 2 < ntiles) step(std::integral_constant<int, 2>{}, kt + 2);
+  for (int kt = 0; kt < ntiles; kt += 2 * STAGES) {
+    step(I0{}, I0{}, kt);
+    if (kt + 1 < ntiles) step(I1{}, I1{}, kt + 1);
+    if (kt + 2 < ntiles) step(I2{}, I0{}, kt + 2);
+    if (kt + 3 < ntiles) step(I0{}, I1{}, kt + 3);
+    if (kt + 4 < ntiles) step(I1{}, I0{}, kt + 4);
+    if (kt + 5 < ntiles) step(I2{}, I1{}, kt + 5);
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -306,9 +328,9 @@ int launch_d(const FwdParams &p, void *stream) {
   const int rb = kFwdWaves / p.heads_per_item;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (rb) {
-    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<D, 1>), dim3(grid), dim3(NT), 0, s, p); break;
     case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2>), dim3(grid), dim3(NT), 0, s, p); break;
     case 4: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), dim3(grid), dim3(NT), 0, s, p); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -23,7 +23,7 @@ constexpr int kMaxQChunks = CP_ATTN_MAX_Q_CHUNKS;
 // Keys per KV tile staged in LDS, and query rows per wavefront.
 constexpr int kFwdBlockKV = 32;
 constexpr int kWaveRows = 32;
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;
 
 struct FwdParams {
   const void *q;
