@@ -14,15 +14,10 @@
 //  2. bwd_dkdv (key-stationary): one workgroup of 8 wavefronts per 128-key
 //     tile of one KV head; it streams the 32-row query tiles -- of every
 //     head of the GQA group and every chunk -- that can see one of its keys.
-//     Four "scorer" wavefronts own 32 keys each and keep their K and V rows
-//     (MFMA B operands) in registers: S = Q K^T and dP = dO V^T with the key
-//     as the lane's column, then P and dS (bf16) are written to LDS. Four
-//     "accumulator" wavefronts own the dK^T/dV^T accumulators of the same
-//     keys and, one query tile behind, run dV^T += dO^T P and dK^T += Q^T dS
-//     with dO^T and Q^T from LDS transpose reads. Splitting the roles keeps
-//     each wavefront's registers within budget and lets the two halves'
-//     matrix work overlap. Query tiles wholly before the keys are never
-//     visited.
+//     Wavefronts w and w+4 own the same 32 keys: the first keeps K rows and
+//     dV^T (S = Q K^T, P, dV^T += dO^T P), the second, one tile behind, V
+//     rows and dK^T (dP = dO V^T, dS = P o (dP - Delta) with P from LDS,
+//     dK^T += Q^T dS). Query tiles wholly before the keys are never visited.
 //  3. bwd_dq (query-stationary, scheduled like the forward): the transposed
 //     tiles S^T = K Q^T and dP^T = V dO^T put the query in the lane, so P^T and
 //     dS^T come from the saved LSE and Delta with per-lane scalars and feed
@@ -76,16 +71,21 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------
-// One workgroup of 8 wavefronts per 128-key tile of one KV head, in two
-// roles sharing the tile's 4 x 32 keys:
-//  * score wavefronts (0..3) keep their keys' K and V rows in registers and,
-//    for query tile t, compute S = Q K^T and dP = dO V^T, then P and dS, and
-//    hand both (bf16, in MFMA-operand layout) to LDS;
-//  * accumulate wavefronts (4..7) keep their keys' dK^T/dV^T in registers and,
-//    one step behind, add dO^T P and Q^T dS of query tile t-1 (dO^T and Q^T by
-//    transpose reads of the staged tiles).
-// Query tiles go through a 3-stage LDS ring (being loaded / scored /
-// accumulated), P and dS through a 2-stage exchange; one barrier per step.
+// One workgroup of 8 wavefronts per 128-key tile of one KV head; wavefronts
+// w and w+4 (which share a SIMD) own the same 32 keys, in two roles:
+//  * P wavefronts (0..3) keep their keys' K rows and dV^T accumulators in
+//    registers; for query tile t they compute S = Q K^T, P = exp(S - LSE)
+//    (masked), add dV^T += dO^T P and hand P (bf16, in MFMA-operand layout)
+//    to LDS;
+//  * dS wavefronts (4..7) keep V rows and dK^T accumulators; one step behind,
+//    they compute dP = dO V^T, dS = P o (dP - Delta) with P from LDS, and add
+//    dK^T += Q^T dS.
+// Each role thus has the same matrix work per step (two products of 8
+// MFMAs) and half of the element-wise work, so the two wavefronts of a SIMD
+// keep its matrix core busy in turn. dO^T and Q^T come from transpose reads
+// of the staged tiles. Query tiles go through a 3-stage LDS ring (being
+// loaded / used by P wavefronts / used by dS wavefronts), P through a 2-stage
+// exchange; one barrier per step.
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * 64;
 
@@ -104,13 +104,13 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   __shared__ __attribute__((aligned(16))) __bf16 do_s[QSTAGES][BQ * D];
   __shared__ __attribute__((aligned(16))) float lse_s[QSTAGES][BQ];
   __shared__ __attribute__((aligned(16))) float dl_s[QSTAGES][BQ];
-  // P and dS exchange: [stage][key wavefront][P/dS][k-step][lane] x 8 bf16
-  __shared__ __attribute__((aligned(16))) bf16x8 xs[2][4][2][2][64];
+  // P exchange: [stage][key wavefront][k-step][lane] x 8 bf16
+  __shared__ __attribute__((aligned(16))) bf16x8 xs[2][4][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool scorer = wave < 4;
+  const bool prole = wave < 4;             // P role (else dS role)
   const int kw = wave & 3;                 // which 32 keys of the tile
   const int half = lane >> 5;
   const int col = lane & 31;
@@ -229,11 +229,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   }
   __syncthreads();
 
-  // Step it: scorers handle query tile it (it < total), accumulators tile
-  // it-1 (it >= 1); tile it+2 is loaded and tile it+1 written to the ring
-  // meanwhile. The two roles run separate loops (so their register sets do
-  // not add up) with the same barriers. Each loop is unrolled by two so that
-  // the register sets alternate at compile time.
+  // Step it: P wavefronts handle query tile it (it < total), dS wavefronts
+  // tile it-1 (it >= 1); tile it+2 is loaded and tile it+1 written to the
+  // ring meanwhile. The two roles run separate loops (so their register sets
+  // do not add up) with the same barriers. Each loop is unrolled by two so
+  // that the register sets alternate at compile time.
   // (Only called when total > 0, so the load cursor is always valid.)
   auto staging_begin = [&](int it, Staged &ld) {
     next_load(it + 2);
@@ -243,56 +243,58 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     if (it + 1 < total) swrite((it + 1) % QSTAGES, wr);
     __syncthreads();
   };
-  if (scorer) {
-    bf16x8 kf[KSTEPS], vf[KSTEPS];   // K and V rows of this lane's key
-    int qoff[KSTEPS];                // A-operand reads of the Q and dO rows
-    {
-      const __bf16 *kg = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hk * p.kv_sh;
-      const __bf16 *vg = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hk * p.kv_sh;
-      const int64_t ro = (int64_t)min(my_key, p.skv - 1) * p.kv_ss + 8 * half;
+  TrOffsets<D> tro;   // Q^T and dO^T transpose reads (same tile layout)
+  tro.init(lane);
+  int qoff[KSTEPS];   // A-operand reads of Q (P role) or dO (dS role) rows
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        kf[s] = *reinterpret_cast<const bf16x8 *>(kg + ro + 16 * s);
-        vf[s] = *reinterpret_cast<const bf16x8 *>(vg + ro + 16 * s);
-        qoff[s] = TQ::chunk_off(col, 2 * s + half);
-      }
-      wait_vmem_all();
-    }
-    Cursor cs = c0;   // the step being scored
-    auto score = [&](int it, Staged &ld, const Staged &wr) {
+  for (int s = 0; s < KSTEPS; ++s) qoff[s] = TQ::chunk_off(col, 2 * s + half);
+  // This lane's key row of K (P role) or V (dS role): the B operand.
+  bf16x8 kvf[KSTEPS];
+  {
+    const __bf16 *src = static_cast<const __bf16 *>(prole ? p.k : p.v) + b * p.kv_sb + hk * p.kv_sh;
+    const int64_t ro = (int64_t)min(my_key, p.skv - 1) * p.kv_ss + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) kvf[s] = *reinterpret_cast<const bf16x8 *>(src + ro + 16 * s);
+    wait_vmem_all();
+  }
+  f32x16 acc[DB];     // dV^T (P role) or dK^T (dS role) of the 32 keys
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+
+  if (prole) {
+    Cursor cs = c0;   // the step being processed
+    auto step_p = [&](int it, Staged &ld, const Staged &wr) {
       staging_begin(it, ld);
       if (it < total) {
         const int st = it % QSTAGES;
         const __bf16 *qs = q_s[st];
         const __bf16 *os = do_s[st];
         const int64_t qpos0 = p.chunk_pos[cs.c] + cs.t * BQ;
-        f32x16 sacc, pacc;
+        // S = Q K^T: register i holds query row 8*(i/4) + 4*half + i%4.
+        f32x16 sacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] = 0.0f;
-          pacc[i] = 0.0f;
-        }
-        bf16x8 qa[KSTEPS], oa[KSTEPS];
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
+        bf16x8 qa[KSTEPS];
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          qa[s] = *reinterpret_cast<const bf16x8 *>(qs + qoff[s]);
-          oa[s] = *reinterpret_cast<const bf16x8 *>(os + qoff[s]);
-        }
+        for (int s = 0; s < KSTEPS; ++s) qa[s] = *reinterpret_cast<const bf16x8 *>(qs + qoff[s]);
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          sacc = mfma32(qa[s], kf[s], sacc);
-          pacc = mfma32(oa[s], vf[s], pacc);
-        }
-        // Half the operand reads up front, the rest two MFMAs ahead of use.
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KSTEPS, 0);
+        for (int s = 0; s < KSTEPS; ++s) sacc = mfma32(qa[s], kvf[s], sacc);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KSTEPS / 2, 0);
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) {
+        for (int j = 0; j < KSTEPS / 2; ++j) {
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, KSTEPS, 0);
-        // Register i holds query row 8*(i/4) + 4*half + i%4 of the tile; the
-        // lane's key is visible to rows >= its first visible row.
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, KSTEPS / 2, 0);
+        // dO^T operands of dV^T += dO^T P, read while S completes.
+        bf16x8 ao[2][DB];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) ao[k2][db] = tro.read(os, 16 * k2, db);
+        // The lane's key is visible to rows >= its first visible row.
         const bool need_mask = !wave_keys_ok || (p.causal && p.kv_pos0 + wkey0 + 31 > qpos0);
         int t = -BQ;
         if (need_mask) {
@@ -303,109 +305,105 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
           }
           t = key_ok ? rel - 4 * half : BQ;
         }
-        bf16x8 pf[2], dsf[2];
+        bf16x8 pf[2];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[st][8 * gq + 4 * half]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl_s[st][8 * gq + 4 * half]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * gq + e;
             float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -l4[e]));
             if (need_mask) pv = (8 * gq + e < t) ? 0.0f : pv;
             pf[i >> 3][i & 7] = (__bf16)pv;
-            dsf[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - d4[e]));
           }
         }
         const int xst = it & 1;
-        xs[xst][kw][0][0][lane] = pf[0];
-        xs[xst][kw][0][1][lane] = pf[1];
-        xs[xst][kw][1][0][lane] = dsf[0];
-        xs[xst][kw][1][1][lane] = dsf[1];
+        xs[xst][kw][0][lane] = pf[0];
+        xs[xst][kw][1][lane] = pf[1];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = mfma32(ao[k2][db], pf[k2], acc[db]);
         advance(cs);
       }
       staging_end(it, wr);
     };
     if (total > 0) {
       for (int it = 0; it <= total; it += 2) {
-        score(it, sa, sb);
-        if (it + 1 <= total) score(it + 1, sb, sa);
+        step_p(it, sa, sb);
+        if (it + 1 <= total) step_p(it + 1, sb, sa);
       }
     }
-    return;
-  }
-
-  TrOffsets<D> tro;   // Q^T and dO^T transpose reads (same tile layout)
-  tro.init(lane);
-  f32x16 dv[DB], dk[DB];
+  } else {
+    auto step_ds = [&](int it, Staged &ld, const Staged &wr) {
+      staging_begin(it, ld);
+      if (it >= 1) {
+        const int st = (it + QSTAGES - 1) % QSTAGES;
+        const int xst = (it - 1) & 1;
+        const __bf16 *qs = q_s[st];
+        const __bf16 *os = do_s[st];
+        // dP = dO V^T (same layout as S).
+        f32x16 pacc;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+        for (int i = 0; i < 16; ++i) pacc[i] = 0.0f;
+        bf16x8 oa[KSTEPS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dv[db][i] = 0.0f;
-      dk[db][i] = 0.0f;
-    }
-  auto accumulate = [&](int it, Staged &ld, const Staged &wr) {
-    staging_begin(it, ld);
-    if (it >= 1) {
-      const int pst = (it + QSTAGES - 1) % QSTAGES;
-      const int xst = (it - 1) & 1;
-      const __bf16 *qs = q_s[pst];
-      const __bf16 *os = do_s[pst];
-      // LDS operands of the first half of the step are read up front; those
-      // of the second half while the first half's matrix operations run.
-      bf16x8 ao[2][DB], aq[2][DB], pk[2], dsk[2];
+        for (int s = 0; s < KSTEPS; ++s) oa[s] = *reinterpret_cast<const bf16x8 *>(os + qoff[s]);
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        pk[k2] = xs[xst][kw][0][k2][lane];
-        dsk[k2] = xs[xst][kw][1][k2][lane];
+        for (int s = 0; s < KSTEPS; ++s) pacc = mfma32(oa[s], kvf[s], pacc);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KSTEPS / 2, 0);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          ao[k2][db] = tro.read(os, 16 * k2, db);
-          aq[k2][db] = tro.read(qs, 16 * k2, db);
+        for (int j = 0; j < KSTEPS / 2; ++j) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
-      }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, KSTEPS / 2, 0);
+        // Q^T operands of dK^T += Q^T dS and P, read while dP completes.
+        bf16x8 aq[2][DB], pk[2];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+        for (int k2 = 0; k2 < 2; ++k2) {
+          pk[k2] = xs[xst][kw][k2][lane];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32(ao[k2][db], pk[k2], dv[db]);
-          dk[db] = mfma32(aq[k2][db], dsk[k2], dk[db]);
+          for (int db = 0; db < DB; ++db) aq[k2][db] = tro.read(qs, 16 * k2, db);
         }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 + 4 * DB, 0);
+        bf16x8 dsf[2];
 #pragma unroll
-      for (int j = 0; j < 2 * DB; ++j) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl_s[st][8 * gq + 4 * half]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * gq + e;
+            const float pv = (float)pk[i >> 3][i & 7];
+            dsf[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - d4[e]));
+          }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = mfma32(aq[k2][db], dsf[k2], acc[db]);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * DB, 0);
-    }
-    staging_end(it, wr);
-  };
-  if (total > 0) {
-    for (int it = 0; it <= total; it += 2) {
-      accumulate(it, sa, sb);
-      if (it + 1 <= total) accumulate(it + 1, sb, sa);
+      staging_end(it, wr);
+    };
+    if (total > 0) {
+      for (int it = 0; it <= total; it += 2) {
+        step_ds(it, sa, sb);
+        if (it + 1 <= total) step_ds(it + 1, sb, sa);
+      }
     }
   }
 
   if (!key_ok) return;
-  float *dvp = p.dv + (((int64_t)b * p.hkv + hk) * p.skv + my_key) * D;
-  float *dkp = p.dk + (((int64_t)b * p.hkv + hk) * p.skv + my_key) * D;
+  float *dst = (prole ? p.dv : p.dk) + (((int64_t)b * p.hkv + hk) * p.skv + my_key) * D;
+  const float mul = prole ? 1.0f : p.scale;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const int d = 32 * db + 8 * gq + 4 * half;
-      f32x4 a, c;
+      f32x4 a;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = dv[db][4 * gq + e];
-        c[e] = dk[db][4 * gq + e] * p.scale;
-      }
-      *reinterpret_cast<f32x4 *>(dvp + d) = a;
-      *reinterpret_cast<f32x4 *>(dkp + d) = c;
+      for (int e = 0; e < 4; ++e) a[e] = acc[db][4 * gq + e] * mul;
+      *reinterpret_cast<f32x4 *>(dst + d) = a;
     }
 }
 
