@@ -138,23 +138,26 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   int total = 0;
   for (int c = 0; c < p.n_q_chunks; ++c) total += (nq_tiles - first_tile(c)) * p.group;
   struct Cursor {
-    int c, t, h;
+    int c, t, h;       // chunk, query tile in the chunk, head in the group
+    int64_t cpos;      // global position of the chunk's first row
   };
-  auto skip_empty = [&](Cursor &u) {
-    while (u.c < p.n_q_chunks && u.t >= nq_tiles) {
-      ++u.c;
-      u.t = u.c < p.n_q_chunks ? first_tile(u.c) : 0;
+  // Moves to the next chunk with a tile to visit (or past the last chunk).
+  auto next_chunk = [&](Cursor &u) {
+    int t0 = nq_tiles;
+    while (t0 >= nq_tiles && ++u.c < p.n_q_chunks) t0 = first_tile(u.c);
+    if (u.c < p.n_q_chunks) {
+      u.t = t0;
+      u.cpos = p.chunk_pos[u.c];
     }
   };
   auto advance = [&](Cursor &u) {
     if (++u.h == p.group) {
       u.h = 0;
-      ++u.t;
-      skip_empty(u);
+      if (++u.t >= nq_tiles) next_chunk(u);
     }
   };
-  Cursor c0{0, first_tile(0), 0};
-  skip_empty(c0);
+  Cursor c0{0, first_tile(0), 0, p.chunk_pos[0]};
+  if (c0.t >= nq_tiles) next_chunk(c0);
 
   // Staging of query tiles (Q, dO and the rows' LSE and Delta): loaded into
   // registers two steps ahead and written to the LDS ring one step ahead of
@@ -180,22 +183,27 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   // Loads only: anything computed from the loaded values waits until swrite,
   // so the loads stay in flight. Every thread loads (the statistics too), so
   // that all paths carry the same number of loads.
+  // All addressing is a wave-uniform base (scalar registers) plus a 32-bit
+  // lane offset; row strides are bounded on the host so that the offsets
+  // within a tile fit in 31 bits.
   auto gload = [&](const Cursor &u, Staged &r) {
     const int head = hk * p.group + u.h;
     const int row0 = u.t * BQ;
-    const int last = p.chunk_len - 1;   // rows past the chunk end read its last row
-    const int64_t rbase = (int64_t)u.c * p.chunk_len;
-    const __bf16 *qg = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh;
-    const __bf16 *og = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh;
+    const int rows_left = p.chunk_len - 1 - row0;   // rows past the chunk end read its last row
+    const int64_t lrow0 = (int64_t)u.c * p.chunk_len + row0;
+    const char *qb = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.q) + b * p.q_sb +
+                                                    head * p.q_sh + lrow0 * p.q_ss);
+    const char *ob = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.dout) + b * p.o_sb +
+                                                    head * p.o_sh + lrow0 * p.o_ss);
 #pragma unroll
     for (int i = 0; i < Q_LOADS; ++i) {
-      const int64_t lr = rbase + min(row0 + grow[i], last);
-      r.q[i] = *reinterpret_cast<const u32x4 *>(qg + lr * p.q_ss + gcol[i]);
-      r.o[i] = *reinterpret_cast<const u32x4 *>(og + lr * p.o_ss + gcol[i]);
+      const int rw = min(grow[i], rows_left);
+      r.q[i] = *reinterpret_cast<const u32x4 *>(qb + 2 * (rw * (int)p.q_ss + gcol[i]));
+      r.o[i] = *reinterpret_cast<const u32x4 *>(ob + 2 * (rw * (int)p.o_ss + gcol[i]));
     }
-    r.ok = row0 + rr < p.chunk_len;
-    const int64_t idx = ((int64_t)b * p.hq + head) * p.sq + rbase + min(row0 + rr, last);
-    r.aux = (tid < BQ ? lse_ptr : delta_ptr)[idx];
+    r.ok = rr <= rows_left;
+    const int64_t sbase = ((int64_t)b * p.hq + head) * p.sq + lrow0;
+    r.aux = (tid < BQ ? lse_ptr : delta_ptr)[sbase + min(rr, rows_left)];
   };
   auto swrite = [&](int st, const Staged &r) {
 #pragma unroll
@@ -271,7 +279,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
         const int st = it % QSTAGES;
         const __bf16 *qs = q_s[st];
         const __bf16 *os = do_s[st];
-        const int64_t qpos0 = p.chunk_pos[cs.c] + cs.t * BQ;
+        const int64_t qpos0 = cs.cpos + cs.t * BQ;
         // S = Q K^T: register i holds query row 8*(i/4) + 4*half + i%4.
         f32x16 sacc;
 #pragma unroll
@@ -305,18 +313,19 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
           }
           t = key_ok ? rel - 4 * half : BQ;
         }
-        bf16x8 pf[2];
+        float pv[16];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[st][8 * gq + 4 * half]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * gq + e;
-            float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -l4[e]));
-            if (need_mask) pv = (8 * gq + e < t) ? 0.0f : pv;
-            pf[i >> 3][i & 7] = (__bf16)pv;
-          }
+          for (int e = 0; e < 4; ++e) pv[4 * gq + e] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * gq + e], c2, -l4[e]));
         }
+        if (need_mask) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pv[i] = (8 * (i >> 2) + (i & 3) < t) ? 0.0f : pv[i];
+        }
+        bf16x8 pf[2];
+        to_bf16_operands(pv, pf);
         const int xst = it & 1;
         xs[xst][kw][0][lane] = pf[0];
         xs[xst][kw][1][lane] = pf[1];
@@ -366,17 +375,18 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
 #pragma unroll
           for (int db = 0; db < DB; ++db) aq[k2][db] = tro.read(qs, 16 * k2, db);
         }
-        bf16x8 dsf[2];
+        float dsv[16];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl_s[st][8 * gq + 4 * half]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * gq + e;
-            const float pv = (float)pk[i >> 3][i & 7];
-            dsf[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - d4[e]));
+            dsv[i] = (float)pk[i >> 3][i & 7] * (pacc[i] - d4[e]);
           }
         }
+        bf16x8 dsf[2];
+        to_bf16_operands(dsv, dsf);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll

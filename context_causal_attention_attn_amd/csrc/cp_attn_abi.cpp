@@ -76,6 +76,10 @@ static int32_t validate(const cp_attn_desc *d) {
       if (st[i] < 0) return CP_ATTN_ERR_BAD_SHAPE;
       if (st[i] % vec != 0) return CP_ATTN_ERR_ALIGNMENT;
     }
+  // Row strides below 2^24 elements: the kernels address rows within a tile
+  // with 32-bit byte offsets from a per-tile base.
+  for (auto st : all)
+    if (st[2] >= (int64_t(1) << 24)) return CP_ATTN_ERR_UNSUPPORTED;
   return CP_ATTN_OK;
 }
 
@@ -153,7 +157,7 @@ const char *cp_attn_error_string(int32_t status) {
     case CP_ATTN_ERR_BAD_SHAPE: return "inconsistent sizes or strides (hq % hkv, chunk lengths, negative strides, non-finite or non-positive scale, causal flag)";
     case CP_ATTN_ERR_BAD_LAYOUT: return "layout does not match the chunk table (contiguous: 1 Q chunk, head_tail: 2)";
     case CP_ATTN_ERR_BAD_POSITIONS: return "chunk positions negative, too large, or overlapping";
-    case CP_ATTN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, size or KV chunk table";
+    case CP_ATTN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, size, row stride (>= 2^24 elements) or KV chunk table";
     case CP_ATTN_ERR_WORKSPACE: return "workspace missing or smaller than cp_attn_workspace_bytes()";
     case CP_ATTN_ERR_HIP: return "HIP launch or runtime error";
     case CP_ATTN_ERR_ABI: return "descriptor abi_version does not match the library";

@@ -8,6 +8,8 @@ namespace cpattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -98,6 +100,17 @@ __device__ __forceinline__ float pair_sum(float x) {
 // wait-count bookkeeping does not carry them into the main loop, where it
 // would otherwise wait on the in-flight prefetch of later tiles.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Round 16 floats to bf16 (nearest-even) into two MFMA operands, element i
+// going to lane-element i % 8 of operand i / 8; one conversion per pair.
+__device__ __forceinline__ void to_bf16_operands(const float (&v)[16], bf16x8 (&o)[2]) {
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const bf16x2 t = __builtin_convertvector((f32x2){v[j], v[j + 1]}, bf16x2);
+    o[j >> 3][j & 7] = t[0];
+    o[j >> 3][(j & 7) + 1] = t[1];
+  }
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -68,7 +68,7 @@ typedef enum {
   CP_ATTN_ERR_BAD_SHAPE = -2,     /* sizes/strides inconsistent (hq % hkv, chunk lengths, ...) */
   CP_ATTN_ERR_BAD_LAYOUT = -3,    /* layout vs chunk count, or unknown layout */
   CP_ATTN_ERR_BAD_POSITIONS = -4, /* negative or overlapping chunk positions */
-  CP_ATTN_ERR_UNSUPPORTED = -5,   /* head_dim / dtype / chunk table the library does not implement */
+  CP_ATTN_ERR_UNSUPPORTED = -5,   /* head_dim / dtype / chunk table / row stride >= 2^24 not implemented */
   CP_ATTN_ERR_WORKSPACE = -6,     /* workspace NULL or smaller than cp_attn_workspace_bytes() */
   CP_ATTN_ERR_HIP = -7,           /* a HIP launch or query failed */
   CP_ATTN_ERR_ABI = -8,           /* desc->abi_version != CP_ATTN_ABI_VERSION */
@@ -117,6 +117,7 @@ typedef struct cp_attn_desc {
   int64_t q_strides[3];        /* batch, head, row strides of q (elements) */
   int64_t kv_strides[3];       /* batch, head, row strides of k and v (elements) */
   int64_t o_strides[3];        /* batch, head, row strides of out, dout and dq (elements) */
+                               /* all strides >= 0, multiples of 16 bytes; row strides < 2^24 */
 } cp_attn_desc;
 
 /* ABI version of the loaded library (CP_ATTN_ABI_VERSION of its build). */

@@ -90,6 +90,8 @@ def test_validate_accepts_good_descriptors():
     (dict(q_strides=(8 * 2000 * 128, 2000 * 128, 132)), -9),   # row stride breaks 16-byte alignment
     (dict(kv_strides=(-1, 2000 * 128, 128)), -2),
     (dict(sq_local=2 ** 31), -5),
+    (dict(q_strides=(0, 0, 2 ** 24)), -5),                     # row stride beyond 32-bit tile offsets
+    (dict(o_strides=(0, 0, 2 ** 24 + 8)), -5),
 ])
 def test_validate_rejects(kw, code):
     assert status(desc(**kw)) == code
