@@ -36,7 +36,7 @@ namespace {
 constexpr int BK = kBwdBlockKV;   // keys per key-stationary workgroup
 constexpr int BQ = kBwdBlockQ;    // query rows per step of that workgroup
 constexpr int BN = kDqBlockKV;    // keys per tile of the query-stationary kernel
-constexpr int NT = kFwdWaves * 64;
+constexpr int NT = kDqWaves * 64;
 
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008;
@@ -422,8 +422,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
 // ---------------------------------------------------------------------------
 template <int D, int RB>
 __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
-  constexpr int HPW = kFwdWaves / RB;
-  constexpr int BM = kWaveRows * RB;
+  constexpr int HPW = kDqWaves / RB;
+  constexpr int BM = kDqWaveRows * RB;
   constexpr int NC = D / 8;
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
@@ -454,8 +454,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   const int64_t item_qhi = chunk_pos + item_row0 + item_rows - 1;
 
   const int head = head0 + wave / RB;
-  const int wrow0 = (wave % RB) * kWaveRows;
-  const int wrows = max(0, min(kWaveRows, item_rows - wrow0));
+  const int wrow0 = (wave % RB) * kDqWaveRows;
+  const int wrows = max(0, min(kDqWaveRows, item_rows - wrow0));
   const int64_t wave_qlo = chunk_pos + item_row0 + wrow0;
   const int64_t wave_qhi = wave_qlo + max(wrows, 1) - 1;
   const bool qvalid = col < wrows;
@@ -637,7 +637,7 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
   if (int e = mark(2)) return e;
   const int64_t items = (int64_t)p.n_head_packs * p.n_q_chunks * p.tiles_per_chunk;
   if (rows > 0 && items > 0) {
-    const int rb = kFwdWaves / p.heads_per_item;
+    const int rb = kDqWaves / p.heads_per_item;
     switch (rb) {
       case 2: hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3(items), dim3(NT), 0, s, p); break;
       case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3(items), dim3(NT), 0, s, p); break;

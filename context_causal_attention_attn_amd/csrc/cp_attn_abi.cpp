@@ -92,7 +92,7 @@ void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   p->hq = d->hq;
   p->hkv = d->hkv;
   p->group = d->hq / d->hkv;
-  p->heads_per_item = fwd_heads_per_item(p->group);
+  p->heads_per_item = item_heads(p->group);
   p->n_head_packs = d->batch * (d->hq / p->heads_per_item);
   p->sq = (int32_t)d->sq_local;
   p->skv = (int32_t)d->skv;
@@ -127,14 +127,13 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
   p->scale = d->softmax_scale;
   p->scale_log2 = d->softmax_scale * 1.4426950408889634f;
   for (int i = 0; i < s.n_q_chunks; ++i) p->chunk_pos[i] = s.chunk_pos[i];
-  FwdParams f;
-  fill_fwd_params(d, s, &f);
-  p->heads_per_item = f.heads_per_item;
-  p->n_head_packs = f.n_head_packs;
-  p->tiles_per_chunk = f.tiles_per_chunk;
+  p->heads_per_item = item_heads(p->group);
+  p->n_head_packs = d->batch * (d->hq / p->heads_per_item);
+  const int rows = dq_block_rows(p->group);
+  p->tiles_per_chunk = (int32_t)((s.chunk_len + rows - 1) / rows);
   for (int i = 0; i < s.n_q_chunks; ++i) {
-    p->lpt_chunk_pos[i] = f.chunk_pos[i];
-    p->lpt_chunk_idx[i] = f.chunk_idx[i];
+    p->lpt_chunk_pos[i] = s.chunk_pos[s.order[i]];
+    p->lpt_chunk_idx[i] = s.order[i];
   }
 }
 

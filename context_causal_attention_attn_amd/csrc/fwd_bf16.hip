@@ -6,23 +6,28 @@
 // v, plus the natural-log LSE ("新流程 CP 多通信模式迁移设计方案" §6.1 local-Q /
 // global-KV attention, §8 global-position causal mask, §9.2 GQA).
 //
-// How (one workgroup = 4 wavefronts = one work item):
+// How (one workgroup = 4 wavefronts = one work item, one wavefront per SIMD):
 //  * a work item is a tile of query rows of one chunk for a pack of query
-//    heads that read the same KV head (GQA); K/V tiles of 32 keys pass through
-//    a 3-stage LDS ring once per workgroup and are read by every head;
-//  * each wavefront owns 32 query rows of one head and computes the transposed
-//    score tile S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16, so
-//    that a lane holds one query column: the row max and sum of the online
-//    softmax are lane-local plus one permlane32 swap between the two halves of
-//    the wavefront;
+//    heads that read the same KV head (GQA); K/V tiles of 64 keys pass through
+//    a 4-stage LDS ring once per workgroup, loaded straight from global memory
+//    into LDS (global_load_lds_dwordx4), and are read by every head;
+//  * each wavefront owns 64 query rows (two 32-row blocks) of one head and
+//    computes transposed score tiles S^T = K Q^T (keys x queries) with
+//    v_mfma_f32_32x32x16_bf16, so that a lane holds one query column per
+//    block: the row max and sum of the online softmax are lane-local plus one
+//    permlane32 swap between the two halves of the wavefront. Every K or V
+//    operand read from LDS feeds both row blocks;
 //  * the probabilities P^T, converted to bf16 in registers, are the B operand
 //    of O^T += V^T P^T without any shuffle: the contraction index (keys) is
 //    permuted identically in both operands, and V^T is read from the
 //    row-major V tile with the gfx950 LDS transpose read ds_read_b64_tr_b16;
-//  * software pipeline: while the vector ALU exponentiates tile j, the matrix
-//    cores already compute S^T of tile j+1 (the two are interleaved
-//    instruction by instruction), and the global loads of tile j+2 are in
-//    flight;
+//  * three-way software pipeline: in step j the matrix core computes
+//    O^T += V^T P^T of tile j-1 and S^T of tile j+1 while the vector ALU turns
+//    the scores of tile j into probabilities. The three are independent; the
+//    step is written as slots of one matrix instruction plus a share of the
+//    vector work, so one wavefront keeps its matrix core fed while it
+//    exponentiates. A change of the running max found in step j rescales O
+//    after the step's PV products;
 //  * KV tiles wholly after the work item's last query are never visited; only
 //    tiles crossing the causal diagonal (or the ragged end of K/V) are masked;
 //    the running max is only moved (and O rescaled) when a new score exceeds
@@ -38,30 +43,45 @@
 namespace cpattn {
 namespace {
 
-constexpr int BN = kFwdBlockKV;          // keys per tile (32)
-constexpr int NT = kFwdWaves * 64;
-constexpr int STAGES = 3;
+constexpr int BN = kFwdBlockKV;          // keys per tile (64)
+constexpr int NW = kFwdWaves;            // wavefronts per workgroup (4)
+constexpr int NT = NW * 64;
+constexpr int QB = kFwdWaveRows / 32;    // 32-row query blocks per wavefront
+constexpr int KSTAGES = 2;               // K ring: tile t in stage t % 2
+constexpr int VSTAGES = 3;               // V ring: tile t in stage t % 3
+constexpr int UNROLL = 6;                // steps per loop trip (both ring indices fixed)
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 
-// sched_group_barrier masks
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedValu = 0x002;
-constexpr int kSchedDsRead = 0x100;
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Calls f(IC<0>{}), ..., f(IC<N-1>{}) in order (compile-time loop index).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 template <int D, int RB>
 __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
-  constexpr int HPW = kFwdWaves / RB;  // heads per work item
-  constexpr int BM = kWaveRows * RB;   // query rows per work item
-  constexpr int NC = D / 8;
-  constexpr int KSTEPS = D / 16;
-  constexpr int DB = D / 32;
+  constexpr int HPW = NW / RB;         // heads per work item
+  constexpr int BM = kFwdWaveRows * RB;  // query rows per work item
+  constexpr int NC = D / 8;            // 16-byte chunks per row
+  constexpr int KSTEPS = D / 16;       // k-steps of S^T (contraction over D)
+  constexpr int DB = D / 32;           // 32-row blocks of O^T
+  constexpr int KB = BN / 32;          // 32-key blocks of S^T
+  constexpr int PSTEPS = BN / 16;      // k-steps of O^T (contraction over keys)
   constexpr int TILE = BN * D;
-  constexpr int CHUNKS = BN * NC;      // 16-byte chunks per K (or V) tile
-  constexpr int LOADS = (CHUNKS + NT - 1) / NT;
-  static_assert(BN == 32 && (CHUNKS % NT == 0 || LOADS == 1), "tile shape");
+  static_assert(BN == 64 && (QB == 1 || QB == 2), "tile shape");
   using T = Tile<D>;
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES][2][TILE];  // [stage][K,V]
+  // K ring (2 stages) followed by the V ring (3 stages), in one LDS array:
+  // 80 KiB at D = 128, so two workgroups share a CU.
+  __shared__ __attribute__((aligned(16))) __bf16 smem[(KSTAGES + VSTAGES) * TILE];
+  static_assert((KSTAGES + VSTAGES) * TILE * 2 <= 80 * 1024, "LDS budget");
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;   // LDS byte address of smem
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,14 +106,21 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const int64_t item_qhi = chunk_pos + item_row0 + item_rows - 1;
 
   const int head = head0 + wave / RB;
-  const int wrow0 = (wave % RB) * kWaveRows;
-  const int wrows = max(0, min(kWaveRows, item_rows - wrow0));
+  const int wrow0 = (wave % RB) * kFwdWaveRows;
   const int64_t wave_qlo = chunk_pos + item_row0 + min(wrow0, item_rows - 1);
-  const bool qvalid = col < wrows;
-  // Lanes past the last row of the item act as its last row (never stored).
-  const int qrow = min(wrow0 + col, item_rows - 1);
-  const int64_t qpos = chunk_pos + item_row0 + qrow;
-  const int local_row = chunk * p.chunk_len + item_row0 + qrow;
+  // Lane rows of the two blocks; rows past the item's last act as its last
+  // row (never stored).
+  int local_row[QB];
+  int64_t qpos[QB];
+  bool qvalid[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = wrow0 + 32 * qb + col;
+    const int qrow = min(r, item_rows - 1);
+    qvalid[qb] = r < item_rows;
+    qpos[qb] = chunk_pos + item_row0 + qrow;
+    local_row[qb] = chunk * p.chunk_len + item_row0 + qrow;
+  }
 
   int nvis = p.skv;
   if (p.causal) {
@@ -102,222 +129,370 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   }
   const int ntiles = (nvis + BN - 1) / BN;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole item
-  bf16x8 qf[KSTEPS];
-  {
+  // ---- Q fragments (B operands of S^T = K Q^T), resident for the whole item
+  bf16x8 qf[QB][KSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
     const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh +
-                       (int64_t)local_row * p.q_ss + 8 * half;
+                       (int64_t)local_row[qb] * p.q_ss + 8 * half;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
-    wait_vmem_all();
+    for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
   }
+  wait_vmem_all();
 
-  // ---- per-lane addressing, computed once ----------------------------------
-  int koff[KSTEPS];                        // K-fragment reads: row col, chunk 2s+half
+  // ---- per-lane LDS addressing, computed once ------------------------------
+  // Byte addresses of this lane's operand reads in stage 0; the stage, key
+  // block and k-step only add constants, which become instruction immediates
+  // (every K read lies within 24 KiB of its base, every V read within 44 KiB).
+  uint32_t kaddr[KSTEPS];                  // K-fragment reads: row col, chunk 2s+half
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) koff[s] = T::chunk_off(col, 2 * s + half);
-  int troff[2][DB];                        // V^T transpose reads (k-step 1 adds 16 rows)
+  for (int s = 0; s < KSTEPS; ++s) kaddr[s] = lds0 + 2 * T::chunk_off(col, 2 * s + half);
+  uint32_t vaddr[2][DB];                   // V^T transpose reads (k-step ps adds 16 rows)
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      troff[u][db] = T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
-                                 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+      vaddr[u][db] = lds0 + 2 * (KSTAGES * TILE +
+                                 T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
+                                             32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)));
+  auto lds_b128 = [](uint32_t addr) -> bf16x8 {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
+  };
+  auto lds_tr = [](uint32_t addr) -> i16x4 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)addr);
+  };
+
+  // ---- staging of K/V tiles: global -> LDS directly --------------------------
+  // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS address
+  // M0 + 16*l, so one instruction of a wavefront fills RPI consecutive tile
+  // rows; each lane fetches the global chunk that the row's swizzle puts at its
+  // position (a permutation within the row: still one contiguous row read).
+  // Wavefront w's instruction i covers rows (i*NW + w)*RPI ...; the row
+  // modulo 16 (which fixes the swizzle) does not depend on i. The loads are
+  // issued from inline assembly so that the compiler does not make every LDS
+  // read wait for them; each step waits for its own loads (vmcnt(0)) right
+  // before the barrier that publishes the tile.
+  constexpr int RPI = 64 / NC;                       // rows per instruction
+  constexpr int INSTS = BN / (NW * RPI);             // instructions per wave per tile
+  static_assert(INSTS >= 1 && (NW * RPI) % 16 == 0, "staging shape");
   const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
-  // Staging: thread tid moves chunk (tid % NC) of rows tid / NC + i * RSTEP.
-  // Row steps of RSTEP (a multiple of 16) keep the swizzle, so every load's
-  // LDS and global offsets are the first one's plus a constant.
-  constexpr int RSTEP = NT / NC;
-  static_assert(RSTEP % 16 == 0, "row step must preserve the swizzle");
-  const int srow = tid / NC, scol = 8 * (tid % NC);
-  const int woff0 = T::chunk_off(srow, tid % NC);
-  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
+  const int srow = wave * RPI + lane / NC;           // tile row of instruction 0
+  const int scol = 8 * ((lane % NC) ^ T::swz(srow)); // logical column of this lane's chunk
   const int64_t tile_stride = (int64_t)BN * p.kv_ss;
-  const int64_t rstep_bytes = (int64_t)RSTEP * p.kv_ss * 2;
-  // Two register sets: tile t is loaded into set t % 2 two steps before it is
-  // written to the LDS ring, which gives each load two steps of latency cover.
-  u32x4 kreg[2][LOADS], vreg[2][LOADS];
-  // With fewer chunks than threads (D = 64) only the first CHUNKS threads stage.
-  const bool stager = (CHUNKS % NT == 0) || tid < CHUNKS;
-  auto gload = [&](int kt, auto set_tag) {
-    constexpr int SET = decltype(set_tag)::value;
-    if (!stager) return;
+  const int64_t istep_bytes = (int64_t)NW * RPI * p.kv_ss * 2;
+  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
+  const uint32_t dst0 = lds0 + 2 * wave * RPI * D;   // this wave's rows in K stage 0
+  // M0 is saved and restored around the load: the compiler owns it.
+  auto dma1 = [](uint32_t m0, uint32_t voff, const void *sbase) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
+  };
+  // Rows of tile kt of K (is_v = false) or V into LDS at dst (this wave's
+  // first row of the stage).
+  auto dma = [&](int kt, bool is_v, uint32_t dst) {
+    const __bf16 *base = is_v ? vbase : kbase;
     if (kt * BN + BN <= p.skv) {
-      // Full tile: scalar tile base plus a 32-bit per-lane byte offset.
-      const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride);
-      const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride);
+      const char *t_base = reinterpret_cast<const char *>(base + (int64_t)kt * tile_stride);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        kreg[SET][i] = *reinterpret_cast<const u32x4 *>(kt_base + i * rstep_bytes + goff0);
-        vreg[SET][i] = *reinterpret_cast<const u32x4 *>(vt_base + i * rstep_bytes + goff0);
-      }
+      for (int i = 0; i < INSTS; ++i) dma1(dst + 2 * i * NW * RPI * D, goff0, t_base + i * istep_bytes);
     } else {
       // Ragged last tile: rows past the end read the last row (always masked).
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int64_t o = (int64_t)min(kt * BN + srow + i * RSTEP, p.skv - 1) * p.kv_ss + scol;
-        kreg[SET][i] = *reinterpret_cast<const u32x4 *>(kbase + o);
-        vreg[SET][i] = *reinterpret_cast<const u32x4 *>(vbase + o);
+      for (int i = 0; i < INSTS; ++i) {
+        const int64_t o = (int64_t)min(kt * BN + srow + i * NW * RPI, p.skv - 1) * p.kv_ss + scol;
+        dma1(dst + 2 * i * NW * RPI * D, (uint32_t)(o * 2), base);
       }
     }
   };
-  auto swrite = [&](int stage, auto set_tag) {
-    constexpr int SET = decltype(set_tag)::value;
-    if (!stager) return;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      *reinterpret_cast<u32x4 *>(&smem[stage][0][woff0 + i * RSTEP * D]) = kreg[SET][i];
-      *reinterpret_cast<u32x4 *>(&smem[stage][1][woff0 + i * RSTEP * D]) = vreg[SET][i];
-    }
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
+  auto dma_k = [&](int kt, int stage) { dma(kt, false, dst0 + 2 * stage * TILE); };
+  auto dma_v = [&](int kt, int stage) { dma(kt, true, dst0 + 2 * (KSTAGES + stage) * TILE); };
 
-  f32x16 oacc[DB];
+  f32x16 oacc[QB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.0f;
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s (may lag the true max)
-  float l_part = 0.0f;      // this lane's partial row sum (its half of the keys)
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.0f;
+  // Running max of scale*log2(e)*s (may lag the true max) and this lane's
+  // partial row sum (its half of the keys), per row block.
+  float m_run[QB], l_part[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_part[qb] = 0.0f;
+  }
   const float c = p.scale_log2;
 
-  // ---- prologue: tiles 0 and 1 staged, S^T of tile 0 ----------------------
-  f32x16 sacc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
-  if (ntiles > 0) {
-    gload(0, I0{});
-    swrite(0, I0{});
-    if (ntiles > 1) {
-      gload(1, I1{});
-      swrite(1, I1{});
+  // Matrix-instruction slots of a step. Operand o (one LDS read, used by the
+  // QB row blocks in consecutive slots): o in [0, NPV) is V^T of k-step
+  // ps = o / DB, O^T block db = o % DB (two transpose reads); o in [NPV, NOP)
+  // is K of key block kb = u / KSTEPS, k-step s = u % KSTEPS (u = o - NPV).
+  constexpr int NPV = PSTEPS * DB;
+  constexpr int NOP = NPV + KB * KSTEPS;
+  constexpr int NSLOT = QB * NOP;
+  constexpr int AHEAD = 2;                 // operand reads run this many operands ahead
+  constexpr int NBUF = AHEAD + 1;
+  // Operand o of a step whose K stage is KS and V stage VS.
+  auto read_opnd = [&](auto ks_tag, auto vs_tag, auto o_tag) -> bf16x8 {
+    constexpr int KS = decltype(ks_tag)::value, VS = decltype(vs_tag)::value;
+    constexpr int o = decltype(o_tag)::value;
+    if constexpr (o < NPV) {
+      constexpr int ps = o / DB, db = o % DB;
+      constexpr uint32_t off = 2 * (VS * TILE + 16 * D * ps);
+      const i16x4 a0 = lds_tr(vaddr[0][db] + off);
+      const i16x4 a1 = lds_tr(vaddr[1][db] + off);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      constexpr int u = o - NPV, kb = u / KSTEPS, s = u % KSTEPS;
+      return lds_b128(kaddr[s] + 2 * (KS * TILE + kb * 32 * D));
     }
-    gload(min(2, ntiles - 1), I0{});
-  }
-  __syncthreads();
-  if (ntiles > 0) {
-    const __bf16 *ks = smem[0][0];
+  };
+  // S^T of one tile from K stage 0 (prologue only).
+  auto qk0 = [&](f32x16 (&sa)[QB][KB]) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      sacc = mfma32(*reinterpret_cast<const bf16x8 *>(ks + koff[s]), qf[s], sacc);
-  }
-
-  // One step of the pipeline on tile kt held in stage ST (kt % 3 == ST);
-  // PAR = kt % 2 selects the register set of tile kt + 2 (written to the ring
-  // at the end of this step); tile kt + 3 is loaded into the other set.
-  auto step = [&](auto st_tag, auto par_tag, int kt) {
-    constexpr int ST = decltype(st_tag)::value;
-    constexpr int PAR = decltype(par_tag)::value;
-    constexpr int NEXT = (ST + 1) % STAGES;
-    constexpr int FREE = (ST + 2) % STAGES;
-    // Unconditional (past the end it re-reads the last tile): every path then
-    // has the same number of loads in flight, so the wait before the ring
-    // write below covers only the older set.
-    gload(min(kt + 3, ntiles - 1), std::integral_constant<int, 1 - PAR>{});
-    const int64_t tile_plo = p.kv_pos0 + (int64_t)kt * BN;
-
-    // Mask (diagonal or ragged tiles only): key 8*(i/4) + 4*half + i%4 of the
-    // tile is visible iff it is <= lim.
-    const bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
-    if (need_mask) {
-      int lim = p.skv - 1 - kt * BN;
-      if (p.causal) {
-        const int64_t rel = qpos - tile_plo;
-        lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sa[qb][kb][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8 a = lds_b128(kaddr[s] + 2 * kb * 32 * D);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sa[qb][kb] = mfma32(a, qf[qb][s], sa[qb][kb]);
       }
-      const int t = lim - 4 * half;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3) > t) ? -INFINITY : sacc[i];
     }
-    // Online softmax bookkeeping for tile kt.
-    float mx = sacc[0];
+  };
+  // O^T += V^T P^T of one tile from V stage `stage` (epilogue only).
+  auto pv = [&](int stage, const bf16x8 (&pf)[QB][PSTEPS]) {
 #pragma unroll
-    for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), sacc[i + 1]);   // v_max3 chain
-    mx = fmaxf(mx, sacc[15]);
-    mx = pair_max(mx) * c;
-    const bool upd = mx > m_run + kRescaleSlack;
-    if (__any(upd)) {
-      const float m_new = upd ? mx : m_run;
-      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      m_run = m_new;
-    }
-    const float mneg = (m_run == -INFINITY) ? 0.0f : -m_run;
-
-    // S^T of tile kt+1 on the matrix cores, interleaved with exp2 of tile kt.
-    // (After the last tile this reads a stale stage; the result is unused.)
-    f32x16 snext;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) snext[i] = 0.0f;
-    const __bf16 *ksn = smem[NEXT][0];
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      snext = mfma32(*reinterpret_cast<const bf16x8 *>(ksn + koff[s]), qf[s], snext);
-    // The row sum uses the unrounded fp32 probabilities (summing the bf16
-    // values instead costs up to ~2^-9 relative error in short rows).
-    bf16x8 pf[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, mneg));
-      l_part += pv;
-      pf[i >> 3][i & 7] = (__bf16)pv;
-    }
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
-    }
-
-    // O^T += V^T P^T for tile kt.
-    const __bf16 *vs = smem[ST][1];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+    for (int ps = 0; ps < PSTEPS; ++ps)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vs + troff[0][db] + 16 * D * k2));
-        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vs + troff[1][db] + 16 * D * k2));
-        const i16x8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pf[k2], oacc[db]);
+        const uint32_t off = 2 * (stage * TILE + 16 * D * ps);
+        const i16x4 a0 = lds_tr(vaddr[0][db] + off);
+        const i16x4 a1 = lds_tr(vaddr[1][db] + off);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(a, pf[qb][ps], oacc[qb][db]);
       }
-    if (kt + 2 < ntiles) swrite(FREE, par_tag);
-    __syncthreads();
-    sacc = snext;
   };
 
-  for (int kt = 0; kt < ntiles; kt += 2 * STAGES) {
-    step(I0{}, I0{}, kt);
-    if (kt + 1 < ntiles) step(I1{}, I1{}, kt + 1);
-    if (kt + 2 < ntiles) step(I2{}, I0{}, kt + 2);
-    if (kt + 3 < ntiles) step(I0{}, I1{}, kt + 3);
-    if (kt + 4 < ntiles) step(I1{}, I0{}, kt + 4);
-    if (kt + 5 < ntiles) step(I2{}, I1{}, kt + 5);
+  // ---- prologue ---------------------------------------------------------------
+  // V stage 2 stands for "tile -1" in step 0 (its P is zero), so it must
+  // not hold NaN bit patterns: clear it.
+  {
+    constexpr int VEC = TILE / 8;
+    u32x4 *vlast = reinterpret_cast<u32x4 *>(smem + (KSTAGES + VSTAGES - 1) * TILE);
+    for (int i = tid; i < VEC; i += NT) vlast[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // Scores and probabilities alternate between two register sets by step
+  // parity: step j reads S^T(j) from set j%2 and writes S^T(j+1) into the
+  // other; it reads P(j-1) from set (j+1)%2 and writes P(j) into set j%2.
+  // (Sets are always chosen by a compile-time index: a runtime index would
+  // put them in scratch memory.)
+  f32x16 sbuf[2][QB][KB];
+  bf16x8 pbuf[2][QB][PSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ps = 0; ps < PSTEPS; ++ps)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pbuf[1][qb][ps][e] = (__bf16)0.0f;
+  if (ntiles > 0) {
+    dma_k(0, 0);
+    dma_v(0, 0);
+  }
+  if (ntiles > 1) dma_k(1, 1);
+  wait_vmem_all();
+  __syncthreads();
+  if (ntiles > 0) qk0(sbuf[0]);
+  __syncthreads();   // K stage 0 is refilled in step 0
+
+  // One step on tile j (J6 = j % 6): PV(j-1) and S^T(j+1) on the matrix
+  // core, softmax of S^T(j) on the VALU, and K of tile j+2 and V of tile j+1
+  // on their way into the rings. Slots are separated by scheduling fences so
+  // that the interleave is the one written here.
+  auto step = [&](auto j6_tag, int j) {
+    constexpr int J6 = decltype(j6_tag)::value;
+    constexpr int SET = J6 & 1;
+    f32x16 (&sacc)[QB][KB] = sbuf[SET];
+    f32x16 (&snext)[QB][KB] = sbuf[1 - SET];
+    const bf16x8 (&pprev)[QB][PSTEPS] = pbuf[1 - SET];
+    bf16x8 (&pcur)[QB][PSTEPS] = pbuf[SET];
+    using KS = IC<(J6 + 1) % KSTAGES>;   // K of tile j+1
+    using VS = IC<(J6 + 2) % VSTAGES>;   // V of tile j-1
+    // K of tile j+2 replaces K of tile j (read in step j-1); V of tile j+1
+    // replaces V of tile j-2 (read in step j-1).
+    if (j + 2 < ntiles) dma_k(j + 2, J6 % KSTAGES);
+    if (j + 1 < ntiles) dma_v(j + 1, (J6 + 1) % VSTAGES);
+    // Keep the operand bases opaque per step: otherwise the compiler hoists a
+    // base-plus-stage address per stage out of the loop (four times the
+    // registers) instead of folding the stage into the read's immediate.
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vaddr[u][db]));
+    const int64_t tile_plo = p.kv_pos0 + (int64_t)j * BN;
+
+    // Mask (diagonal or ragged tiles only): key 32*kb + 8*(i/4) + 4*half + i%4
+    // of the tile is visible to a row iff it is <= that row's limit.
+    const bool need_mask = (j * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        int lim = p.skv - 1 - j * BN;
+        if (p.causal) {
+          const int64_t rel = qpos[qb] - tile_plo;
+          lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
+        }
+        const int t = lim - 4 * half;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sacc[qb][kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) > t) ? -INFINITY : sacc[qb][kb][i];
+      }
+    }
+
+    bf16x8 opnd[NBUF];
+    float mx[QB], alpha[QB], mneg[QB];
+    bool upd[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      mx[qb] = 0.0f;
+      alpha[qb] = 1.0f;
+      mneg[qb] = 0.0f;
+      upd[qb] = false;
+    }
+    static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_opnd(KS{}, VS{}, o); });
+    static_for<NSLOT>([&](auto t_tag) {
+      constexpr int t = decltype(t_tag)::value;
+      constexpr int o = t / QB, qb = t % QB;
+      if constexpr (qb == 0 && o + AHEAD < NOP)
+        opnd[(o + AHEAD) % NBUF] = read_opnd(KS{}, VS{}, IC<o + AHEAD>{});
+      // matrix instruction of slot t
+      if constexpr (o < NPV) {
+        constexpr int ps = o / DB, db = o % DB;
+        oacc[qb][db] = mfma32(opnd[o % NBUF], pprev[qb][ps], oacc[qb][db]);
+      } else {
+        constexpr int u = o - NPV, kb = u / KSTEPS, s = u % KSTEPS;
+        if constexpr (s == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+          snext[qb][kb] = mfma32(opnd[o % NBUF], qf[qb][s], z);
+        } else {
+          snext[qb][kb] = mfma32(opnd[o % NBUF], qf[qb][s], snext[qb][kb]);
+        }
+      }
+      // Vector work of slot t: row maxima (slots 0..QB*KB-1), statistics
+      // (next QB slots), then pairs of probabilities spread over the rest.
+      constexpr int NMAX = QB * KB;
+      if constexpr (t < NMAX) {
+        constexpr int rq = t / KB, kb = t % KB;
+        float m = fmaxf(sacc[rq][kb][0], sacc[rq][kb][1]);
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) m = fmaxf(fmaxf(m, sacc[rq][kb][i]), sacc[rq][kb][i + 1]);
+        mx[rq] = (kb == 0) ? m : fmaxf(mx[rq], m);
+      } else if constexpr (t < NMAX + QB) {
+        constexpr int rq = t - NMAX;
+        const float mr = pair_max(mx[rq]) * c;
+        upd[rq] = mr > m_run[rq] + kRescaleSlack;
+        const float m_new = upd[rq] ? mr : m_run[rq];
+        alpha[rq] = upd[rq] ? __builtin_amdgcn_exp2f(m_run[rq] - m_new) : 1.0f;
+        m_run[rq] = m_new;
+        l_part[rq] *= alpha[rq];
+        mneg[rq] = (m_new == -INFINITY) ? 0.0f : -m_new;
+      } else {
+        // Pair u of the NPAIR pairs (row block u / (KB*8), key block
+        // (u / 8) % KB, elements 2(u%8), 2(u%8)+1) goes to slot
+        // FIRST + u * SPAN / NPAIR.
+        constexpr int NPAIR = QB * KB * 8, FIRST = NMAX + QB, SPAN = NSLOT - FIRST;
+        static_for<NPAIR>([&](auto u_tag) {
+          constexpr int u = decltype(u_tag)::value;
+          if constexpr (FIRST + u * SPAN / NPAIR == t) {
+            constexpr int rq = u / (KB * 8), kb = (u / 8) % KB, i = 2 * (u % 8);
+            // The row sum uses the unrounded fp32 probabilities (summing the
+            // bf16 values instead costs up to 2^-8 relative error in short rows).
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kb][i], c, mneg[rq]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kb][i + 1], c, mneg[rq]));
+            l_part[rq] += p0;
+            l_part[rq] += p1;
+            const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+            pcur[rq][2 * kb + (i >> 3)][i & 7] = t2[0];
+            pcur[rq][2 * kb + (i >> 3)][(i & 7) + 1] = t2[1];
+          }
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // Pin P(j) and the row sums to the slots above: without a use here the
+    // compiler sinks the exponentials past the branch below, away from the
+    // products they are meant to overlap.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int ps = 0; ps < PSTEPS; ++ps) asm volatile("" ::"v"(pcur[qb][ps]));
+      asm volatile("" ::"v"(l_part[qb]));
+    }
+
+    // A moved max rescales O (after the PV(j-1) products, which used the old one).
+    bool any_upd = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) any_upd = any_upd || upd[qb];
+    if (__any(any_upd)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha[qb];
+    }
+    wait_vmem_all();   // this wave's rows of the tiles loaded above are in LDS
+    __syncthreads();
+  };
+
+  for (int j = 0; j < ntiles; j += UNROLL) {
+    step(IC<0>{}, j);
+    if (j + 1 < ntiles) step(IC<1>{}, j + 1);
+    if (j + 2 < ntiles) step(IC<2>{}, j + 2);
+    if (j + 3 < ntiles) step(IC<3>{}, j + 3);
+    if (j + 4 < ntiles) step(IC<4>{}, j + 4);
+    if (j + 5 < ntiles) step(IC<5>{}, j + 5);
+  }
+  // The last tile's PV product.
+  if (ntiles > 0) {
+    const int last = ntiles - 1;
+    if (last & 1) pv(last % VSTAGES, pbuf[1]);
+    else pv(last % VSTAGES, pbuf[0]);
   }
 
   // ---- epilogue -------------------------------------------------------------
-  if (!qvalid) return;
-  const float l = pair_sum(l_part);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + head * p.o_sh + (int64_t)local_row * p.o_ss;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l = pair_sum(l_part[qb]);
+    if (!qvalid[qb]) continue;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + head * p.o_sh + (int64_t)local_row[qb] * p.o_ss;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 o4;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][4 * g + e] * inv);
-      *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g + 4 * half) = o4;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[qb][db][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g + 4 * half) = o4;
+      }
+    if (half == 0) {
+      const float lse = l > 0.0f ? (m_run[qb] + __log2f(l)) * kLn2 : -INFINITY;
+      p.lse[((int64_t)b * p.hq + head) * p.sq + local_row[qb]] = lse;
     }
-  if (half == 0) {
-    const float lse = l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
-    p.lse[((int64_t)b * p.hq + head) * p.sq + local_row] = lse;
   }
 }
 
@@ -325,12 +500,12 @@ template <int D>
 int launch_d(const FwdParams &p, void *stream) {
   const int64_t grid = fwd_grid_size(p);
   if (grid == 0) return 0;
-  const int rb = kFwdWaves / p.heads_per_item;
+  const int rb = NW / p.heads_per_item;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (rb) {
+    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<D, 1>), dim3(grid), dim3(NT), 0, s, p); break;
     case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2>), dim3(grid), dim3(NT), 0, s, p); break;
     case 4: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), dim3(grid), dim3(NT), 0, s, p); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -20,10 +20,11 @@ constexpr int kMaxQChunks = CP_ATTN_MAX_Q_CHUNKS;
 // ---------------------------------------------------------------------------
 // Forward, bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-// Keys per KV tile staged in LDS, and query rows per wavefront.
-constexpr int kFwdBlockKV = 32;
-constexpr int kWaveRows = 32;
-constexpr int kFwdWaves = 8;
+// Keys per KV tile staged in LDS, query rows per wavefront and wavefronts per
+// workgroup of the forward kernel.
+constexpr int kFwdBlockKV = 64;
+constexpr int kFwdWaveRows = 32;
+constexpr int kFwdWaves = 4;
 
 struct FwdParams {
   const void *q;
@@ -62,10 +63,11 @@ struct Share {
 
 int32_t make_share(const cp_attn_desc *d, Share *s);
 
-// Heads packed per forward work item for a GQA group of size g (a divisor of
-// g, at most kFwdWaves) and the query rows per item (per head).
-inline int fwd_heads_per_item(int g) { return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1; }
-inline int fwd_block_rows(int g) { return kWaveRows * (kFwdWaves / fwd_heads_per_item(g)); }
+// Heads packed per work item of the query-stationary kernels (forward, dQ)
+// for a GQA group of size g: a divisor of g, at most 4.
+inline int item_heads(int g) { return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1; }
+// Query rows per forward work item (per head).
+inline int fwd_block_rows(int g) { return kFwdWaveRows * (kFwdWaves / item_heads(g)); }
 
 // ---------------------------------------------------------------------------
 // Backward
@@ -79,6 +81,10 @@ inline int fwd_block_rows(int g) { return kWaveRows * (kFwdWaves / fwd_heads_per
 constexpr int kBwdBlockKV = 128;
 constexpr int kBwdBlockQ = 32;
 constexpr int kDqBlockKV = 64;    // keys per tile of the query-stationary dQ kernel
+constexpr int kDqWaveRows = 32;   // query rows per wavefront of the dQ kernel
+constexpr int kDqWaves = 8;       // wavefronts per dQ workgroup
+// Query rows per dQ work item (per head).
+inline int dq_block_rows(int g) { return kDqWaveRows * (kDqWaves / item_heads(g)); }
 
 struct BwdParams {
   const void *q;
@@ -102,7 +108,7 @@ struct BwdParams {
   float scale;
   float scale_log2;
   int64_t chunk_pos[kMaxQChunks];   // local chunk order
-  // Schedule of the query-stationary dQ kernel (same as the forward's).
+  // Schedule of the query-stationary dQ kernel (longest first, like the forward's).
   int32_t heads_per_item, n_head_packs, tiles_per_chunk;
   int64_t lpt_chunk_pos[kMaxQChunks];
   int32_t lpt_chunk_idx[kMaxQChunks];
