@@ -6,17 +6,17 @@
 // v, plus the natural-log LSE ("新流程 CP 多通信模式迁移设计方案" §6.1 local-Q /
 // global-KV attention, §8 global-position causal mask, §9.2 GQA).
 //
-// How (one workgroup = 4 wavefronts = one work item, one wavefront per SIMD):
+// How (one workgroup = 8 wavefronts = one work item, two wavefronts per SIMD):
 //  * a work item is a tile of query rows of one chunk for a pack of query
-//    heads that read the same KV head (GQA); K/V tiles of 64 keys pass through
-//    a 4-stage LDS ring once per workgroup, loaded straight from global memory
-//    into LDS (global_load_lds_dwordx4), and are read by every head;
-//  * each wavefront owns 64 query rows (two 32-row blocks) of one head and
-//    computes transposed score tiles S^T = K Q^T (keys x queries) with
-//    v_mfma_f32_32x32x16_bf16, so that a lane holds one query column per
-//    block: the row max and sum of the online softmax are lane-local plus one
-//    permlane32 swap between the two halves of the wavefront. Every K or V
-//    operand read from LDS feeds both row blocks;
+//    heads that read the same KV head (GQA); K/V tiles of 64 keys pass
+//    through LDS rings (2 stages for K, 3 for V) once per workgroup, loaded
+//    straight from global memory into LDS (global_load_lds_dwordx4), and are
+//    read by every head;
+//  * each wavefront owns 32 query rows of one head and computes transposed
+//    score tiles S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16,
+//    so that a lane holds one query column: the row statistics of the online
+//    softmax are lane-local plus one permlane32 swap between the two halves
+//    of the wavefront;
 //  * the probabilities P^T, converted to bf16 in registers, are the B operand
 //    of O^T += V^T P^T without any shuffle: the contraction index (keys) is
 //    permuted identically in both operands, and V^T is read from the
@@ -25,13 +25,14 @@
 //    O^T += V^T P^T of tile j-1 and S^T of tile j+1 while the vector ALU turns
 //    the scores of tile j into probabilities. The three are independent; the
 //    step is written as slots of one matrix instruction plus a share of the
-//    vector work, so one wavefront keeps its matrix core fed while it
-//    exponentiates. A change of the running max found in step j rescales O
-//    after the step's PV products;
+//    vector work, so a wavefront keeps its matrix core fed while it
+//    exponentiates;
 //  * KV tiles wholly after the work item's last query are never visited; only
 //    tiles crossing the causal diagonal (or the ragged end of K/V) are masked;
-//    the running max is only moved (and O rescaled) when a new score exceeds
-//    it by more than 2^8, which keeps every exp2 argument <= 8.
+//  * the running max is a reference point, not recomputed per tile: the
+//    probabilities of a tile are formed against the current reference, and
+//    only when a row's tile sum exceeds 2^16 (or the row has no reference
+//    yet) is its max taken, O rescaled and the tile redone.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -44,13 +45,13 @@ namespace cpattn {
 namespace {
 
 constexpr int BN = kFwdBlockKV;          // keys per tile (64)
-constexpr int NW = kFwdWaves;            // wavefronts per workgroup (4)
+constexpr int NW = kFwdWaves;            // wavefronts per workgroup (8)
 constexpr int NT = NW * 64;
 constexpr int QB = kFwdWaveRows / 32;    // 32-row query blocks per wavefront
 constexpr int KSTAGES = 2;               // K ring: tile t in stage t % 2
 constexpr int VSTAGES = 3;               // V ring: tile t in stage t % 3
 constexpr int UNROLL = 6;                // steps per loop trip (both ring indices fixed)
-constexpr float kRescaleSlack = 8.0f;    // log2 units
+constexpr float kSumLimit = 65536.0f;    // largest tile sum kept without a new max
 
 template <int N>
 using IC = std::integral_constant<int, N>;
@@ -78,7 +79,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   using T = Tile<D>;
 
   // K ring (2 stages) followed by the V ring (3 stages), in one LDS array:
-  // 80 KiB at D = 128, so two workgroups share a CU.
+  // 80 KiB at D = 128.
   __shared__ __attribute__((aligned(16))) __bf16 smem[(KSTAGES + VSTAGES) * TILE];
   static_assert((KSTAGES + VSTAGES) * TILE * 2 <= 80 * 1024, "LDS budget");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;   // LDS byte address of smem
@@ -360,16 +361,26 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       }
     }
 
+    // Probabilities of tile j against the current running max (no max is
+    // taken on this path: see the check after the slots).
     bf16x8 opnd[NBUF];
-    float mx[QB], alpha[QB], mneg[QB];
-    bool upd[QB];
+    float mneg[QB], tsum[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      mx[qb] = 0.0f;
-      alpha[qb] = 1.0f;
-      mneg[qb] = 0.0f;
-      upd[qb] = false;
+      mneg[qb] = (m_run[qb] == -INFINITY) ? 0.0f : -m_run[qb];
+      tsum[qb] = 0.0f;
     }
+    auto prob_pair = [&](int rq, int kb, int i, float mn, float &sum) {
+      // The row sum uses the unrounded fp32 probabilities (summing the bf16
+      // values instead costs up to 2^-8 relative error in short rows).
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kb][i], c, mn));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kb][i + 1], c, mn));
+      sum += p0;
+      sum += p1;
+      const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+      pcur[rq][2 * kb + (i >> 3)][i & 7] = t2[0];
+      pcur[rq][2 * kb + (i >> 3)][(i & 7) + 1] = t2[1];
+    };
     static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_opnd(KS{}, VS{}, o); });
     static_for<NSLOT>([&](auto t_tag) {
       constexpr int t = decltype(t_tag)::value;
@@ -391,69 +402,66 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
           snext[qb][kb] = mfma32(opnd[o % NBUF], qf[qb][s], snext[qb][kb]);
         }
       }
-      // Vector work of slot t: row maxima (slots 0..QB*KB-1), statistics
-      // (next QB slots), then pairs of probabilities spread over the rest.
-      constexpr int NMAX = QB * KB;
-      if constexpr (t < NMAX) {
-        constexpr int rq = t / KB, kb = t % KB;
-        float m = fmaxf(sacc[rq][kb][0], sacc[rq][kb][1]);
-#pragma unroll
-        for (int i = 2; i < 16; i += 2) m = fmaxf(fmaxf(m, sacc[rq][kb][i]), sacc[rq][kb][i + 1]);
-        mx[rq] = (kb == 0) ? m : fmaxf(mx[rq], m);
-      } else if constexpr (t < NMAX + QB) {
-        constexpr int rq = t - NMAX;
-        const float mr = pair_max(mx[rq]) * c;
-        upd[rq] = mr > m_run[rq] + kRescaleSlack;
-        const float m_new = upd[rq] ? mr : m_run[rq];
-        alpha[rq] = upd[rq] ? __builtin_amdgcn_exp2f(m_run[rq] - m_new) : 1.0f;
-        m_run[rq] = m_new;
-        l_part[rq] *= alpha[rq];
-        mneg[rq] = (m_new == -INFINITY) ? 0.0f : -m_new;
-      } else {
-        // Pair u of the NPAIR pairs (row block u / (KB*8), key block
-        // (u / 8) % KB, elements 2(u%8), 2(u%8)+1) goes to slot
-        // FIRST + u * SPAN / NPAIR.
-        constexpr int NPAIR = QB * KB * 8, FIRST = NMAX + QB, SPAN = NSLOT - FIRST;
-        static_for<NPAIR>([&](auto u_tag) {
-          constexpr int u = decltype(u_tag)::value;
-          if constexpr (FIRST + u * SPAN / NPAIR == t) {
-            constexpr int rq = u / (KB * 8), kb = (u / 8) % KB, i = 2 * (u % 8);
-            // The row sum uses the unrounded fp32 probabilities (summing the
-            // bf16 values instead costs up to 2^-8 relative error in short rows).
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kb][i], c, mneg[rq]));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kb][i + 1], c, mneg[rq]));
-            l_part[rq] += p0;
-            l_part[rq] += p1;
-            const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-            pcur[rq][2 * kb + (i >> 3)][i & 7] = t2[0];
-            pcur[rq][2 * kb + (i >> 3)][(i & 7) + 1] = t2[1];
-          }
-        });
-      }
+      // Vector work of slot t: pair u of the NPAIR pairs (row block
+      // u / (KB*8), key block (u / 8) % KB, elements 2(u%8), 2(u%8)+1) goes
+      // to slot u * NSLOT / NPAIR.
+      constexpr int NPAIR = QB * KB * 8;
+      static_for<NPAIR>([&](auto u_tag) {
+        constexpr int u = decltype(u_tag)::value;
+        if constexpr (u * NSLOT / NPAIR == t) {
+          constexpr int rq = u / (KB * 8), kb = (u / 8) % KB, i = 2 * (u % 8);
+          prob_pair(rq, kb, i, mneg[rq], tsum[rq]);
+        }
+      });
       __builtin_amdgcn_sched_barrier(0);
     });
-    // Pin P(j) and the row sums to the slots above: without a use here the
+    // Pin P(j) and the tile sums to the slots above: without a use here the
     // compiler sinks the exponentials past the branch below, away from the
     // products they are meant to overlap.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int ps = 0; ps < PSTEPS; ++ps) asm volatile("" ::"v"(pcur[qb][ps]));
-      asm volatile("" ::"v"(l_part[qb]));
+      asm volatile("" ::"v"(tsum[qb]));
     }
 
-    // A moved max rescales O (after the PV(j-1) products, which used the old one).
-    bool any_upd = false;
+    // The running max is only a reference point: the probabilities above are
+    // exact as long as none overflows. While every row's tile sum stays at
+    // most 2^16 (so every probability does), they are kept. Otherwise -- the
+    // first tile of a row (no reference yet), a score more than 16 (log2)
+    // above the reference, or a non-finite sum -- the row max is taken, O and
+    // the row sum are rescaled to it (after this step's PV(j-1) products, which
+    // used the old reference) and the tile's probabilities are recomputed.
+    bool redo = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) any_upd = any_upd || upd[qb];
-    if (__any(any_upd)) {
+    for (int qb = 0; qb < QB; ++qb) redo = redo || !(tsum[qb] <= kSumLimit) || m_run[qb] == -INFINITY;
+    if (__any(redo)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int qb = 0; qb < QB; ++qb) {
+        float m = sacc[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, sacc[qb][kb][i]);
+        const float mr = pair_max(m) * c;
+        const float m_new = fmaxf(m_run[qb], mr);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha[qb];
+          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+        l_part[qb] *= alpha;
+        m_run[qb] = m_new;
+        const float mn = (m_new == -INFINITY) ? 0.0f : -m_new;
+        tsum[qb] = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) prob_pair(qb, kb, i, mn, tsum[qb]);
+      }
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_part[qb] += tsum[qb];
     wait_vmem_all();   // this wave's rows of the tiles loaded above are in LDS
     __syncthreads();
   };
@@ -503,9 +511,9 @@ int launch_d(const FwdParams &p, void *stream) {
   const int rb = NW / p.heads_per_item;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (rb) {
-    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<D, 1>), dim3(grid), dim3(NT), 0, s, p); break;
     case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2>), dim3(grid), dim3(NT), 0, s, p); break;
     case 4: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), dim3(grid), dim3(NT), 0, s, p); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

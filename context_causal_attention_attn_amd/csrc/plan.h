@@ -24,7 +24,7 @@ constexpr int kMaxQChunks = CP_ATTN_MAX_Q_CHUNKS;
 // workgroup of the forward kernel.
 constexpr int kFwdBlockKV = 64;
 constexpr int kFwdWaveRows = 32;
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;
 
 struct FwdParams {
   const void *q;
