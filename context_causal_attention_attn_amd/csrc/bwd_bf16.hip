@@ -43,7 +43,7 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
 // ---------------------------------------------------------------------------
-// 1. Delta = rowsum(dO o O), 16 lanes per row.
+// 1. Delta = rowsum(dO o O), 16 lanes per row; also LSE in log2 units.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
@@ -65,7 +65,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-  if (row < rows && part == 0) p.delta[row] = acc;
+  if (row < rows && part == 0) {
+    p.delta[row] = acc;
+    const float l = p.lse[row];
+    p.lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -74,38 +78,50 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 // One workgroup of 8 wavefronts per 128-key tile of one KV head; wavefronts
 // w and w+4 (which share a SIMD) own the same 32 keys, in two roles:
 //  * P wavefronts (0..3) keep their keys' K rows and dV^T accumulators in
-//    registers; for query tile t they compute S = Q K^T, P = exp(S - LSE)
-//    (masked), add dV^T += dO^T P and hand P (bf16, in MFMA-operand layout)
-//    to LDS;
-//  * dS wavefronts (4..7) keep V rows and dK^T accumulators; one step behind,
-//    they compute dP = dO V^T, dS = P o (dP - Delta) with P from LDS, and add
-//    dK^T += Q^T dS.
-// Each role thus has the same matrix work per step (two products of 8
-// MFMAs) and half of the element-wise work, so the two wavefronts of a SIMD
-// keep its matrix core busy in turn. dO^T and Q^T come from transpose reads
-// of the staged tiles. Query tiles go through a 3-stage LDS ring (being
-// loaded / used by P wavefronts / used by dS wavefronts), P through a 2-stage
-// exchange; one barrier per step.
+//    registers; for the 64-row query tile of step t they compute
+//    P(t) = exp2(S(t) * scale*log2(e) - LSE*log2(e)) (masked), hand it to
+//    LDS and add dV^T += dO(t)^T P(t); S(t+1) = Q(t+1) K^T is computed in the
+//    same step, under the exponentials;
+//  * dS wavefronts (4..7) keep V rows and dK^T accumulators; in step t they
+//    add dK^T += Q(t-2)^T dS(t-2), compute dP(t) = dO(t) V^T and, under it,
+//    dS(t-1) = P(t-1) o (dP(t-1) - Delta) with P(t-1) from LDS.
+// Each role issues 32 matrix instructions per step: the P role's vector work
+// runs under its first 16, the dS role's under its last 16, so the two
+// wavefronts of a SIMD take turns with the vector ALU. Every step is written
+// as slots of one matrix instruction, one operand read a few slots ahead and
+// a share of the vector work, with scheduling fences between slots. Query
+// tiles (Q, dO and the rows' LSE*log2(e) and Delta) are loaded straight from
+// global memory into LDS rings; query tiles wholly before the keys are never
+// visited; one barrier per step.
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * 64;
 
 template <int D>
-__global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdParams p) {
-  constexpr int NT2 = kDkdvThreads;
+__global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int NW = kDkdvWaves;
   constexpr int NC = D / 8;
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int Q_CHUNKS = BQ * NC;           // 16-byte chunks per Q (and dO) tile
-  constexpr int Q_LOADS = (Q_CHUNKS + NT2 - 1) / NT2;
-  constexpr int QSTAGES = 3;
-  using TQ = Tile<D>;
+  constexpr int QT = BQ;                      // query rows per step (64)
+  constexpr int QB = QT / 32;                 // 32-row blocks per step
+  constexpr int QSTEPS = QT / 16;             // k-steps over rows (dV, dK)
+  constexpr int QTILE = QT * D;               // elements of a Q or dO tile
+  constexpr int QSTG = 5;                     // Q ring (with LSE2, Delta): tiles t-2 .. t+2
+  constexpr int OSTG = 2;                     // dO ring: tiles t, t+1
+  constexpr int XPER = QB * 16;               // P values per lane per step
+  // LDS layout (bytes)
+  constexpr int Q_OFF = 0;
+  constexpr int O_OFF = Q_OFF + QSTG * QTILE * 2;
+  constexpr int X_OFF = O_OFF + OSTG * QTILE * 2;                    // [2][4 waves][64 lanes][XPER] bf16
+  constexpr int L_OFF = X_OFF + 2 * 4 * 64 * XPER * 2;               // [QSTG][QT] LSE*log2(e)
+  constexpr int DL_OFF = L_OFF + QSTG * QT * 4;                      // [QSTG][QT] Delta
+  constexpr int LDS_BYTES = DL_OFF + QSTG * QT * 4;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(QT == 64 && XPER == 32, "step shape");
+  using T = Tile<D>;
 
-  __shared__ __attribute__((aligned(16))) __bf16 q_s[QSTAGES][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 do_s[QSTAGES][BQ * D];
-  __shared__ __attribute__((aligned(16))) float lse_s[QSTAGES][BQ];
-  __shared__ __attribute__((aligned(16))) float dl_s[QSTAGES][BQ];
-  // P exchange: [stage][key wavefront][k-step][lane] x 8 bf16
-  __shared__ __attribute__((aligned(16))) bf16x8 xs[2][4][2][64];
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,16 +140,17 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   const int wkey0 = key0 + 32 * kw;
   const int my_key = wkey0 + col;
   const bool key_ok = my_key < p.skv;
+  const bool wave_keys_ok = wkey0 + 31 < p.skv;
   const int64_t kv_lo = p.kv_pos0 + key0;
 
   // Query tiles this key tile meets: per chunk, tiles first_tile(c) ..
   // nq_tiles-1, each for every head of the GQA group. A cursor walks them in
   // that order (chunk, tile, head), one step per tile of one head.
-  const int nq_tiles = (p.chunk_len + BQ - 1) / BQ;
+  const int nq_tiles = (p.chunk_len + QT - 1) / QT;
   auto first_tile = [&](int c) {
     if (!p.causal) return 0;
     const int64_t rel = kv_lo - p.chunk_pos[c];
-    return rel <= 0 ? 0 : (int)min<int64_t>(nq_tiles, rel / BQ);
+    return rel <= 0 ? 0 : (int)min<int64_t>(nq_tiles, rel / QT);
   };
   int total = 0;
   for (int c = 0; c < p.n_q_chunks; ++c) total += (nq_tiles - first_tile(c)) * p.group;
@@ -141,7 +158,6 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     int c, t, h;       // chunk, query tile in the chunk, head in the group
     int64_t cpos;      // global position of the chunk's first row
   };
-  // Moves to the next chunk with a tile to visit (or past the last chunk).
   auto next_chunk = [&](Cursor &u) {
     int t0 = nq_tiles;
     while (t0 >= nq_tiles && ++u.c < p.n_q_chunks) t0 = first_tile(u.c);
@@ -159,103 +175,98 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   Cursor c0{0, first_tile(0), 0, p.chunk_pos[0]};
   if (c0.t >= nq_tiles) next_chunk(c0);
 
-  // Staging of query tiles (Q, dO and the rows' LSE and Delta): loaded into
-  // registers two steps ahead and written to the LDS ring one step ahead of
-  // use, through two register sets.
-  int woff[Q_LOADS], grow[Q_LOADS], gcol[Q_LOADS];
-#pragma unroll
-  for (int i = 0; i < Q_LOADS; ++i) {
-    const int idx = min(tid + NT2 * i, Q_CHUNKS - 1);
-    grow[i] = idx / NC;
-    gcol[i] = 8 * (idx % NC);
-    woff[i] = TQ::chunk_off(grow[i], idx % NC);
-  }
-  struct Staged {
-    u32x4 q[Q_LOADS], o[Q_LOADS];
-    float aux;   // raw LSE (threads 0..31) or Delta (threads 32..63) of one row
-    int ok;      // that row lies inside the chunk
+  // ---- staging: global -> LDS directly (see the forward kernel) -------------
+  // One instruction of a wavefront moves RPI rows of a Q or dO tile; lane l
+  // lands at LDS offset 16*l of them and fetches the chunk that the row's
+  // swizzle puts there. Wavefront w's instruction i covers rows
+  // (i*NW + w)*RPI ...; the row modulo 16 does not depend on i.
+  constexpr int RPI = 64 / NC;
+  constexpr int INSTS = QT / (NW * RPI);
+  static_assert(INSTS >= 1 && (NW * RPI) % 16 == 0, "staging shape");
+  const int srow = wave * RPI + lane / NC;
+  const int scol = 8 * ((lane % NC) ^ T::swz(srow));
+  auto dma16 = [](uint32_t m0, uint32_t voff, const void *sbase) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
   };
-  // Wave-uniform copies of the two row-statistics pointers: selecting between
-  // them per lane must not turn into a per-lane load of the pointer itself.
-  const float *const lse_ptr = p.lse;
-  const float *const delta_ptr = p.delta;
-  const int rr = tid % BQ;
-  // Loads only: anything computed from the loaded values waits until swrite,
-  // so the loads stay in flight. Every thread loads (the statistics too), so
-  // that all paths carry the same number of loads.
-  // All addressing is a wave-uniform base (scalar registers) plus a 32-bit
-  // lane offset; row strides are bounded on the host so that the offsets
-  // within a tile fit in 31 bits.
-  auto gload = [&](const Cursor &u, Staged &r) {
+  auto dma4 = [](uint32_t m0, uint32_t voff, const void *sbase) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
+  };
+  // Rows of step u's tile of `src` (Q: row stride q_ss; dO: o_ss) into LDS at
+  // byte offset dst; rows past the chunk end read its last row.
+  auto dma_tile = [&](const Cursor &u, bool is_q, uint32_t dst) {
     const int head = hk * p.group + u.h;
-    const int row0 = u.t * BQ;
-    const int rows_left = p.chunk_len - 1 - row0;   // rows past the chunk end read its last row
+    const int row0 = u.t * QT;
+    const int rows_left = p.chunk_len - 1 - row0;
     const int64_t lrow0 = (int64_t)u.c * p.chunk_len + row0;
-    const char *qb = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.q) + b * p.q_sb +
-                                                    head * p.q_sh + lrow0 * p.q_ss);
-    const char *ob = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.dout) + b * p.o_sb +
-                                                    head * p.o_sh + lrow0 * p.o_ss);
+    const int64_t ss = is_q ? p.q_ss : p.o_ss;
+    const __bf16 *base = is_q ? static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh
+                              : static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh;
+    const __bf16 *tbase = base + lrow0 * ss;
 #pragma unroll
-    for (int i = 0; i < Q_LOADS; ++i) {
-      const int rw = min(grow[i], rows_left);
-      r.q[i] = *reinterpret_cast<const u32x4 *>(qb + 2 * (rw * (int)p.q_ss + gcol[i]));
-      r.o[i] = *reinterpret_cast<const u32x4 *>(ob + 2 * (rw * (int)p.o_ss + gcol[i]));
+    for (int i = 0; i < INSTS; ++i) {
+      const int r = min(srow + i * NW * RPI, rows_left);
+      dma16(lds0 + dst + 2 * (i * NW * RPI + wave * RPI) * D, (uint32_t)((r * ss + scol) * 2), tbase);
     }
-    r.ok = rr <= rows_left;
-    const int64_t sbase = ((int64_t)b * p.hq + head) * p.sq + lrow0;
-    r.aux = (tid < BQ ? lse_ptr : delta_ptr)[sbase + min(rr, rows_left)];
   };
-  auto swrite = [&](int st, const Staged &r) {
-#pragma unroll
-    for (int i = 0; i < Q_LOADS; ++i) {
-      if (Q_CHUNKS % NT2 == 0 || tid + NT2 * i < Q_CHUNKS) {
-        *reinterpret_cast<u32x4 *>(q_s[st] + woff[i]) = r.q[i];
-        *reinterpret_cast<u32x4 *>(do_s[st] + woff[i]) = r.o[i];
-      }
-    }
-    // LSE is stored as LSE*log2(e), +inf for rows with no visible key or past
-    // the chunk end (P = 0); Delta is 0 past the chunk end.
-    if (tid < BQ) lse_s[st][tid] = (!r.ok || r.aux == -INFINITY) ? INFINITY : r.aux * kLog2e;
-    else if (tid < 2 * BQ) dl_s[st][tid - BQ] = r.ok ? r.aux : 0.0f;
+  // LSE*log2(e) (wave 0) and Delta (wave 1) of step u's rows.
+  auto dma_stats = [&](const Cursor &u, int stage) {
+    if (wave >= 2) return;
+    const int head = hk * p.group + u.h;
+    const int row0 = u.t * QT;
+    const int rows_left = p.chunk_len - 1 - row0;
+    const int64_t sbase = ((int64_t)b * p.hq + head) * p.sq + (int64_t)u.c * p.chunk_len + row0;
+    const float *src = (wave == 0 ? p.lse2 : p.delta) + sbase;
+    const uint32_t dst = lds0 + (wave == 0 ? L_OFF : DL_OFF) + stage * QT * 4;
+    dma4(dst, (uint32_t)(min(lane, rows_left) * 4), src);
   };
-  // Load cursor: the step whose tile the next gload fetches. Past the last
-  // step it stays on the last one (the loads are then repeated, unused).
-  Cursor cl = c0;
-  auto next_load = [&](int step_to_load) {
-    if (step_to_load < total) advance(cl);
+  Cursor cq = c0;   // step whose Q tile the next Q load fetches
+  Cursor co = c0;   // step whose dO tile the next dO load fetches
+  auto load_q = [&](int s) {   // Q tile (and statistics) of step s = cq's
+    const int st = s % QSTG;
+    dma_tile(cq, true, Q_OFF + st * QTILE * 2);
+    dma_stats(cq, st);
+    advance(cq);
   };
-  Staged sa, sb;   // register sets: step s is loaded into (s % 2 ? sb : sa)
-  const float c2 = p.scale_log2;
-  const bool wave_keys_ok = wkey0 + 31 < p.skv;
+  auto load_o = [&](int s) {   // dO tile of step s = co's
+    dma_tile(co, false, O_OFF + (s % OSTG) * QTILE * 2);
+    advance(co);
+  };
 
-  // Prologue: step 0 staged, step 1 in registers.
-  if (total > 0) {
-    gload(cl, sa);
-    swrite(0, sa);
-    next_load(1);
-    gload(cl, sb);
-  }
-  __syncthreads();
-
-  // Step it: P wavefronts handle query tile it (it < total), dS wavefronts
-  // tile it-1 (it >= 1); tile it+2 is loaded and tile it+1 written to the
-  // ring meanwhile. The two roles run separate loops (so their register sets
-  // do not add up) with the same barriers. Each loop is unrolled by two so
-  // that the register sets alternate at compile time.
-  // (Only called when total > 0, so the load cursor is always valid.)
-  auto staging_begin = [&](int it, Staged &ld) {
-    next_load(it + 2);
-    gload(cl, ld);
-  };
-  auto staging_end = [&](int it, const Staged &wr) {
-    if (it + 1 < total) swrite((it + 1) % QSTAGES, wr);
-    __syncthreads();
-  };
-  TrOffsets<D> tro;   // Q^T and dO^T transpose reads (same tile layout)
-  tro.init(lane);
-  int qoff[KSTEPS];   // A-operand reads of Q (P role) or dO (dS role) rows
+  // ---- per-lane LDS addressing ----------------------------------------------
+  // Row reads (A operands of S = Q K^T and dP = dO V^T): row col of the
+  // block, chunk 2s+half; transpose reads (A operands of dV^T = dO^T P and
+  // dK^T = Q^T dS): as in the forward's V^T.
+  const uint32_t rbase = lds0 + (prole ? Q_OFF : O_OFF);
+  const uint32_t tbase = lds0 + (prole ? O_OFF : Q_OFF);
+  uint32_t raddr[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) qoff[s] = TQ::chunk_off(col, 2 * s + half);
+  for (int s = 0; s < KSTEPS; ++s) raddr[s] = rbase + 2 * T::chunk_off(col, 2 * s + half);
+  uint32_t taddr[2][DB];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      taddr[u][db] = tbase + 2 * T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
+                                             32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  auto lds_b128 = [](uint32_t addr) -> bf16x8 {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
+  };
+  auto lds_f4 = [](uint32_t addr) -> f32x4 {
+    return *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>((uintptr_t)addr);
+  };
+  auto lds_tr = [&](int db, uint32_t off) -> bf16x8 {
+    const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[0][db] + off));
+    const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[1][db] + off));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // P exchange: lane l of key group kw, stage x holds XPER bf16 (4 operands).
+  const uint32_t xaddr = lds0 + X_OFF + (kw * 64 + lane) * XPER * 2;
+  constexpr uint32_t XSTAGE = 4 * 64 * XPER * 2;
+
   // This lane's key row of K (P role) or V (dS role): the B operand.
   bf16x8 kvf[KSTEPS];
   {
@@ -270,135 +281,227 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+  const float c2 = p.scale_log2;
+  constexpr int AHEAD = 2;
+  constexpr int NBUF = AHEAD + 1;
+  constexpr int NSA = QB * KSTEPS;      // S or dP products per step
+  constexpr int NSB = QSTEPS * DB;      // dV or dK products per step
+  constexpr int NPAIR = QB * 8;         // pairs of P (or dS) values per lane per step
+
+  // Prologue: Q of steps 0 and 1 (when there is a step 1), dO of step 0.
+  // Every load is of a step that exists: the cursors never run past the last.
+  if (total > 0) {
+    load_q(0);
+    if (total > 1) load_q(1);
+    load_o(0);
+  }
+  wait_vmem_all();
+  __syncthreads();
+  // Loads issued at the start of step it: Q of step it+2, dO of step it+1.
+  auto staging = [&](int it) {
+    if (it + 2 < total) load_q(it + 2);
+    if (it + 1 < total) load_o(it + 1);
+  };
+  auto finish = [&]() {
+    wait_vmem_all();   // this wave's rows of the tiles loaded in this step are in LDS
+    __syncthreads();
+  };
 
   if (prole) {
+    // Row-block scores alternate between two register sets by step parity.
+    f32x16 sbuf[2][QB];
     Cursor cs = c0;   // the step being processed
-    auto step_p = [&](int it, Staged &ld, const Staged &wr) {
-      staging_begin(it, ld);
-      if (it < total) {
-        const int st = it % QSTAGES;
-        const __bf16 *qs = q_s[st];
-        const __bf16 *os = do_s[st];
-        const int64_t qpos0 = cs.cpos + cs.t * BQ;
-        // S = Q K^T: register i holds query row 8*(i/4) + 4*half + i%4.
-        f32x16 sacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
-        bf16x8 qa[KSTEPS];
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) qa[s] = *reinterpret_cast<const bf16x8 *>(qs + qoff[s]);
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) sacc = mfma32(qa[s], kvf[s], sacc);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KSTEPS / 2, 0);
-#pragma unroll
-        for (int j = 0; j < KSTEPS / 2; ++j) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, KSTEPS / 2, 0);
-        // dO^T operands of dV^T += dO^T P, read while S completes.
-        bf16x8 ao[2][DB];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) ao[k2][db] = tro.read(os, 16 * k2, db);
-        // The lane's key is visible to rows >= its first visible row.
-        const bool need_mask = !wave_keys_ok || (p.causal && p.kv_pos0 + wkey0 + 31 > qpos0);
-        int t = -BQ;
-        if (need_mask) {
-          int rel = -1;
-          if (p.causal) {
-            const int64_t r = p.kv_pos0 + my_key - qpos0;
-            rel = (int)(r < -1 ? -1 : (r > BQ ? BQ : r));
-          }
-          t = key_ok ? rel - 4 * half : BQ;
-        }
-        float pv[16];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[st][8 * gq + 4 * half]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pv[4 * gq + e] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * gq + e], c2, -l4[e]));
-        }
-        if (need_mask) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) pv[i] = (8 * (i >> 2) + (i & 3) < t) ? 0.0f : pv[i];
-        }
-        bf16x8 pf[2];
-        to_bf16_operands(pv, pf);
-        const int xst = it & 1;
-        xs[xst][kw][0][lane] = pf[0];
-        xs[xst][kw][1][lane] = pf[1];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = mfma32(ao[k2][db], pf[k2], acc[db]);
-        advance(cs);
-      }
-      staging_end(it, wr);
-    };
     if (total > 0) {
-      for (int it = 0; it <= total; it += 2) {
-        step_p(it, sa, sb);
-        if (it + 1 <= total) step_p(it + 1, sb, sa);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sbuf[0][qb][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+          sbuf[0][qb] = mfma32(lds_b128(raddr[s] + 2 * qb * 32 * D), kvf[s], sbuf[0][qb]);
       }
     }
-  } else {
-    auto step_ds = [&](int it, Staged &ld, const Staged &wr) {
-      staging_begin(it, ld);
-      if (it >= 1) {
-        const int st = (it + QSTAGES - 1) % QSTAGES;
-        const int xst = (it - 1) & 1;
-        const __bf16 *qs = q_s[st];
-        const __bf16 *os = do_s[st];
-        // dP = dO V^T (same layout as S).
-        f32x16 pacc;
+    auto step_p = [&](auto par_tag, int it) {
+      constexpr int PAR = decltype(par_tag)::value;
+      staging(it);
+      if (it < total) {
+        f32x16 (&sacc)[QB] = sbuf[PAR];
+        f32x16 (&snext)[QB] = sbuf[1 - PAR];
+        const uint32_t qnext = 2 * ((it + 1) % QSTG) * QTILE;   // Q stage of step it+1
+        constexpr uint32_t ocur = 2 * PAR * QTILE;              // dO stage of step it
+        const int st = it % QSTG;
+        // LSE*log2(e) of this lane's rows 32qb + 8gq + 4half + e.
+        f32x4 l4[QB][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pacc[i] = 0.0f;
-        bf16x8 oa[KSTEPS];
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) oa[s] = *reinterpret_cast<const bf16x8 *>(os + qoff[s]);
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) pacc = mfma32(oa[s], kvf[s], pacc);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KSTEPS / 2, 0);
-#pragma unroll
-        for (int j = 0; j < KSTEPS / 2; ++j) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, KSTEPS / 2, 0);
-        // Q^T operands of dK^T += Q^T dS and P, read while dP completes.
-        bf16x8 aq[2][DB], pk[2];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          pk[k2] = xs[xst][kw][k2][lane];
-#pragma unroll
-          for (int db = 0; db < DB; ++db) aq[k2][db] = tro.read(qs, 16 * k2, db);
-        }
-        float dsv[16];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl_s[st][8 * gq + 4 * half]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * gq + e;
-            dsv[i] = (float)pk[i >> 3][i & 7] * (pacc[i] - d4[e]);
+          for (int gq = 0; gq < 4; ++gq)
+            l4[qb][gq] = lds_f4(lds0 + L_OFF + 4 * (st * QT + 32 * qb + 8 * gq + 4 * half));
+        // Mask: row r of the tile sees this lane's key iff lo <= r <= hi.
+        const int64_t qpos0 = cs.cpos + cs.t * QT;
+        const int rows_left = p.chunk_len - 1 - cs.t * QT;
+        const bool need_mask = !wave_keys_ok || rows_left < QT - 1 ||
+                               (p.causal && p.kv_pos0 + wkey0 + 31 > qpos0);
+        if (need_mask) {
+          int lo = 0;
+          if (p.causal) {
+            const int64_t r = p.kv_pos0 + my_key - qpos0;
+            lo = (int)(r < 0 ? 0 : (r > QT ? QT : r));
           }
+          if (!key_ok) lo = QT;
+          const int lo_h = lo - 4 * half, hi_h = rows_left - 4 * half;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = 32 * qb + 8 * (i >> 2) + (i & 3);
+              sacc[qb][i] = (r < lo_h || r > hi_h) ? -INFINITY : sacc[qb][i];
+            }
         }
-        bf16x8 dsf[2];
-        to_bf16_operands(dsv, dsf);
+        bf16x8 pcur[QSTEPS];
+        bf16x8 opnd[NBUF];
+        // Half A: S(it+1) (operand u: k-step u/QB of row block u%QB) under P(it).
+        auto read_a = [&](auto u_tag) -> bf16x8 {
+          constexpr int u = decltype(u_tag)::value, qb = u % QB, s = u / QB;
+          return lds_b128(raddr[s] + qnext + 2 * qb * 32 * D);
+        };
+        static_for<AHEAD>([&](auto u) { opnd[decltype(u)::value] = read_a(u); });
+        static_for<NSA>([&](auto t_tag) {
+          constexpr int t = decltype(t_tag)::value, qb = t % QB, s = t / QB;
+          if constexpr (t + AHEAD < NSA) opnd[(t + AHEAD) % NBUF] = read_a(IC<t + AHEAD>{});
+          if constexpr (s == 0) {
+            f32x16 z;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
+            for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+            snext[qb] = mfma32(opnd[t % NBUF], kvf[s], z);
+          } else {
+            snext[qb] = mfma32(opnd[t % NBUF], kvf[s], snext[qb]);
+          }
+          // Pair u (row block u / 8, elements 2(u%8), 2(u%8)+1) in slot u*NSA/NPAIR.
+          static_for<NPAIR>([&](auto u_tag) {
+            constexpr int u = decltype(u_tag)::value;
+            if constexpr (u * NSA / NPAIR == t) {
+              constexpr int rq = u / 8, i = 2 * (u % 8);
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][i], c2, -l4[rq][i >> 2][i & 3]));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][i + 1], c2, -l4[rq][(i + 1) >> 2][(i + 1) & 3]));
+              const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+              pcur[2 * rq + (i >> 3)][i & 7] = t2[0];
+              pcur[2 * rq + (i >> 3)][(i & 7) + 1] = t2[1];
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        // P(it) to the dS wavefront of these keys.
 #pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = mfma32(aq[k2][db], dsf[k2], acc[db]);
+        for (int ps = 0; ps < QSTEPS; ++ps)
+          *reinterpret_cast<__attribute__((address_space(3))) bf16x8 *>((uintptr_t)(xaddr + PAR * XSTAGE + 16 * ps)) = pcur[ps];
+        // Half B: dV^T += dO(it)^T P(it) (operand o: k-step o / DB, block o % DB).
+        auto read_b = [&](auto o_tag) -> bf16x8 {
+          constexpr int o = decltype(o_tag)::value, ps = o / DB, db = o % DB;
+          return lds_tr(db, ocur + 2 * 16 * D * ps);
+        };
+        static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_b(o); });
+        static_for<NSB>([&](auto t_tag) {
+          constexpr int t = decltype(t_tag)::value, ps = t / DB, db = t % DB;
+          if constexpr (t + AHEAD < NSB) opnd[(t + AHEAD) % NBUF] = read_b(IC<t + AHEAD>{});
+          acc[db] = mfma32(opnd[t % NBUF], pcur[ps], acc[db]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        advance(cs);
       }
-      staging_end(it, wr);
+      finish();
     };
-    if (total > 0) {
-      for (int it = 0; it <= total; it += 2) {
-        step_ds(it, sa, sb);
-        if (it + 1 <= total) step_ds(it + 1, sb, sa);
+    for (int it = 0; it <= total + 1; it += 2) {
+      step_p(IC<0>{}, it);
+      if (it + 1 <= total + 1) step_p(IC<1>{}, it + 1);
+    }
+  } else {
+    // dP alternates between two register sets by step parity; dS(it-1),
+    // made in the second half of step it, feeds the first half of step it+1.
+    f32x16 pbuf[2][QB];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pbuf[q][qb][i] = 0.0f;
+    bf16x8 dsf[QSTEPS];
+#pragma unroll
+    for (int ps = 0; ps < QSTEPS; ++ps)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsf[ps][e] = (__bf16)0.0f;
+    auto step_ds = [&](auto par_tag, int it) {
+      constexpr int PAR = decltype(par_tag)::value;
+      staging(it);
+      bf16x8 opnd[NBUF];
+      // Half A: dK^T += Q(it-2)^T dS(it-2).
+      if (it >= 2) {
+        const uint32_t qold = 2 * ((it - 2) % QSTG) * QTILE;
+        auto read_a = [&](auto o_tag) -> bf16x8 {
+          constexpr int o = decltype(o_tag)::value, ps = o / DB, db = o % DB;
+          return lds_tr(db, qold + 2 * 16 * D * ps);
+        };
+        static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_a(o); });
+        static_for<NSB>([&](auto t_tag) {
+          constexpr int t = decltype(t_tag)::value, ps = t / DB, db = t % DB;
+          if constexpr (t + AHEAD < NSB) opnd[(t + AHEAD) % NBUF] = read_a(IC<t + AHEAD>{});
+          acc[db] = mfma32(opnd[t % NBUF], dsf[ps], acc[db]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
+      // Half B: dP(it) = dO(it) V^T under dS(it-1) = P(it-1) o (dP(it-1) - Delta).
+      if (it <= total) {
+        f32x16 (&pnext)[QB] = pbuf[PAR];
+        f32x16 (&pprev)[QB] = pbuf[1 - PAR];
+        constexpr uint32_t ocur = 2 * PAR * QTILE;              // dO stage of step it
+        const int st = (it + QSTG - 1) % QSTG;                  // statistics of step it-1
+        bf16x8 pk[QSTEPS];
+#pragma unroll
+        for (int ps = 0; ps < QSTEPS; ++ps)
+          pk[ps] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
+              (uintptr_t)(xaddr + (1 - PAR) * XSTAGE + 16 * ps));
+        f32x4 d4[QB][4];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            d4[qb][gq] = lds_f4(lds0 + DL_OFF + 4 * (st * QT + 32 * qb + 8 * gq + 4 * half));
+        auto read_b = [&](auto u_tag) -> bf16x8 {
+          constexpr int u = decltype(u_tag)::value, qb = u % QB, s = u / QB;
+          return lds_b128(raddr[s] + ocur + 2 * qb * 32 * D);
+        };
+        static_for<AHEAD>([&](auto u) { opnd[decltype(u)::value] = read_b(u); });
+        static_for<NSA>([&](auto t_tag) {
+          constexpr int t = decltype(t_tag)::value, qb = t % QB, s = t / QB;
+          if constexpr (t + AHEAD < NSA) opnd[(t + AHEAD) % NBUF] = read_b(IC<t + AHEAD>{});
+          if constexpr (s == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+            pnext[qb] = mfma32(opnd[t % NBUF], kvf[s], z);
+          } else {
+            pnext[qb] = mfma32(opnd[t % NBUF], kvf[s], pnext[qb]);
+          }
+          static_for<NPAIR>([&](auto u_tag) {
+            constexpr int u = decltype(u_tag)::value;
+            if constexpr (u * NSA / NPAIR == t) {
+              constexpr int rq = u / 8, i = 2 * (u % 8), ps = 2 * rq + (i >> 3);
+              const float p0 = (float)pk[ps][i & 7], p1 = (float)pk[ps][(i & 7) + 1];
+              const float x0 = p0 * (pprev[rq][i] - d4[rq][i >> 2][i & 3]);
+              const float x1 = p1 * (pprev[rq][i + 1] - d4[rq][(i + 1) >> 2][(i + 1) & 3]);
+              const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+              dsf[ps][i & 7] = t2[0];
+              dsf[ps][(i & 7) + 1] = t2[1];
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      finish();
+    };
+    for (int it = 0; it <= total + 1; it += 2) {
+      step_ds(IC<0>{}, it);
+      if (it + 1 <= total + 1) step_ds(IC<1>{}, it + 1);
     }
   }
 

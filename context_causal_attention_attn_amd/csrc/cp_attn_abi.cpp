@@ -217,14 +217,19 @@ int32_t cp_attn_share_pairs(const cp_attn_desc *d, int64_t *pairs) {
   return CP_ATTN_OK;
 }
 
+static size_t bwd_stat_bytes(const cp_attn_desc *d) {
+  const size_t rows = (size_t)d->batch * d->hq * (size_t)d->sq_local;
+  return (rows * 4 + 255) & ~(size_t)255;
+}
+
 int32_t cp_attn_workspace_bytes(const cp_attn_desc *d, int32_t backward, size_t *bytes) {
   int32_t st = validate(d);
   if (st) return st;
   if (!bytes) return CP_ATTN_ERR_NULL_PTR;
   if (!backward) { *bytes = 0; return CP_ATTN_OK; }
-  // Backward: Delta = rowsum(dO o O), [B, Hq, Sq] fp32.
-  const size_t rows = (size_t)d->batch * d->hq * (size_t)d->sq_local;
-  *bytes = (rows * 4 + 255) & ~(size_t)255;
+  // Backward: Delta = rowsum(dO o O) and LSE * log2(e), each [B, Hq, Sq]
+  // fp32, each starting on a 256-byte boundary.
+  *bytes = 2 * bwd_stat_bytes(d);
   return CP_ATTN_OK;
 }
 
@@ -313,6 +318,7 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *d, const void *q, const void *k, c
   p.q = q; p.k = k; p.v = v; p.out = out; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.delta = static_cast<float *>(workspace);
+  p.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + bwd_stat_bytes(d));
   void *const *ev = n_events == 4 ? events : nullptr;
   const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream, ev)
                                            : launch_bwd_fp32(p, d->head_dim, stream, ev);

@@ -36,8 +36,6 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
-#include <type_traits>
-
 #include "gfx950_common.h"
 #include "plan.h"
 
@@ -53,17 +51,6 @@ constexpr int VSTAGES = 3;               // V ring: tile t in stage t % 3
 constexpr int UNROLL = 6;                // steps per loop trip (both ring indices fixed)
 constexpr float kSumLimit = 65536.0f;    // largest tile sum kept without a new max
 
-template <int N>
-using IC = std::integral_constant<int, N>;
-
-// Calls f(IC<0>{}), ..., f(IC<N-1>{}) in order (compile-time loop index).
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-  if constexpr (I < N) {
-    f(IC<I>{});
-    static_for<N, I + 1>(f);
-  }
-}
 
 template <int D, int RB>
 __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 namespace cpattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -115,6 +117,18 @@ __device__ __forceinline__ void to_bf16_operands(const float (&v)[16], bf16x8 (&
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Calls f(IC<0>{}), ..., f(IC<N-1>{}) in order (compile-time loop index).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 }  // namespace cpattn

@@ -79,7 +79,7 @@ inline int fwd_block_rows(int g) { return kFwdWaveRows * (kFwdWaves / item_heads
 // (scheduled exactly like the forward) and accumulates its dQ over the keys
 // it can see.
 constexpr int kBwdBlockKV = 128;
-constexpr int kBwdBlockQ = 32;
+constexpr int kBwdBlockQ = 64;
 constexpr int kDqBlockKV = 64;    // keys per tile of the query-stationary dQ kernel
 constexpr int kDqWaveRows = 32;   // query rows per wavefront of the dQ kernel
 constexpr int kDqWaves = 8;       // wavefronts per dQ workgroup
@@ -93,7 +93,8 @@ struct BwdParams {
   const void *out;
   const void *dout;
   const float *lse;
-  float *delta;                 // workspace [B, Hq, Sq]
+  float *delta;                 // workspace [B, Hq, Sq]: rowsum(dO o O)
+  float *lse2;                  // workspace [B, Hq, Sq]: LSE * log2(e), +inf for rows with no visible key
   void *dq;
   float *dk;                    // [B, Hkv, Skv, D]
   float *dv;

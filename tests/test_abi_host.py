@@ -173,7 +173,7 @@ def test_workspace_bytes():
     d = desc()
     assert cp_attn_workspace_bytes(d, False) == 0
     rows = 1 * 8 * 500
-    assert cp_attn_workspace_bytes(d, True) == ((rows * 4 + 255) // 256) * 256
+    assert cp_attn_workspace_bytes(d, True) == 2 * ((rows * 4 + 255) // 256) * 256
 
 
 def test_bwd_timed_rejects_bad_event_arrays_before_any_device_work():
