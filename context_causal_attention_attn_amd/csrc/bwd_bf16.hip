@@ -521,8 +521,18 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ (query-stationary; work items and K/V staging as in the forward)
+// 3. dQ (query-stationary; work items as in the forward)
 // ---------------------------------------------------------------------------
+// One workgroup = 8 wavefronts = one work item (a tile of query rows of one
+// chunk for a pack of query heads of one GQA group); each wavefront owns 32
+// query rows of one head. K/V tiles of 64 keys are loaded straight from
+// global memory into 4-stage LDS rings and read by every head. With the
+// query in the lane, S^T = K Q^T and dP^T = V dO^T give P^T = exp2(S^T *
+// scale*log2(e) - LSE*log2(e)) and dS^T = P^T o (dP^T - Delta) from per-lane
+// scalars, and dS^T feeds dQ^T += K^T dS^T straight from registers (K^T by
+// transpose reads). Software pipeline over 32-key blocks: in block b the
+// matrix core computes dQ^T of block b-1 and S^T, dP^T of block b+1 while
+// the vector ALU forms dS^T of block b; one barrier per 64-key tile.
 template <int D, int RB>
 __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int HPW = kDqWaves / RB;
@@ -530,10 +540,16 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int NC = D / 8;
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int LOADS = BN * NC / NT;
+  constexpr int TILE = BN * D;                 // elements of a K or V tile (64 keys)
+  constexpr int STG = 4;                       // ring stages (K and V)
+  constexpr int K_OFF = 0;
+  constexpr int V_OFF = STG * TILE * 2;
+  constexpr int LDS_BYTES = 2 * STG * TILE * 2;
+  static_assert(BN == 64 && LDS_BYTES <= 160 * 1024, "tile shape");
   using T = Tile<D>;
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BN * D];  // [stage][K,V]
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -560,7 +576,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   const int wrow0 = (wave % RB) * kDqWaveRows;
   const int wrows = max(0, min(kDqWaveRows, item_rows - wrow0));
   const int64_t wave_qlo = chunk_pos + item_row0 + wrow0;
-  const int64_t wave_qhi = wave_qlo + max(wrows, 1) - 1;
   const bool qvalid = col < wrows;
   const int64_t qpos = wave_qlo + min(col, max(wrows - 1, 0));
   const int local_row = chunk * p.chunk_len + item_row0 + wrow0 + col;
@@ -571,6 +586,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     nvis = (int)(n < 0 ? 0 : (n > p.skv ? p.skv : n));
   }
   const int ntiles = (nvis + BN - 1) / BN;
+  const int nblocks = 2 * ntiles;   // 32-key blocks
 
   // Q and dO rows of this lane's query: B operands of S^T and dP^T. Lanes past
   // the item's last row read its first row and get LSE = +inf (P = 0).
@@ -589,58 +605,78 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     }
     if (qvalid) {
       const int64_t row = ((int64_t)b * p.hq + head) * p.sq + local_row;
-      const float l = p.lse[row];
-      lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      lse2 = p.lse2[row];
       delta = p.delta[row];
     }
     wait_vmem_all();
   }
 
+  // ---- staging: global -> LDS directly (see the forward kernel) -------------
+  constexpr int RPI = 64 / NC;
+  constexpr int INSTS = BN / (kDqWaves * RPI);
+  static_assert(INSTS >= 1 && (kDqWaves * RPI) % 16 == 0, "staging shape");
   const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
-  // Per-lane addressing, computed once.
-  int koff[KSTEPS];                     // A-operand reads of K and V rows
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) koff[s] = T::chunk_off(col, 2 * s + half);
-  TrOffsets<D> tro;                     // K^T transpose reads
-  tro.init(lane);
-  // Staging: thread tid moves chunk (tid % NC) of rows tid / NC + i * RSTEP.
-  // Row steps of RSTEP (a multiple of 16) keep the swizzle, so every load's
-  // LDS and global offsets are the first one's plus a constant.
-  constexpr int RSTEP = NT / NC;
-  static_assert(RSTEP % 16 == 0, "row step must preserve the swizzle");
-  const int srow = tid / NC, scol = 8 * (tid % NC);
-  const int woff0 = T::chunk_off(srow, tid % NC);
-  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
+  const int srow = wave * RPI + lane / NC;
+  const int scol = 8 * ((lane % NC) ^ T::swz(srow));
   const int64_t tile_stride = (int64_t)BN * p.kv_ss;
-  const int64_t rstep_bytes = (int64_t)RSTEP * p.kv_ss * 2;
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int kt) {
+  const int64_t istep_bytes = (int64_t)kDqWaves * RPI * p.kv_ss * 2;
+  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
+  const uint32_t dst0 = lds0 + 2 * wave * RPI * D;
+  auto dma1 = [](uint32_t m0, uint32_t voff, const void *sbase) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
+  };
+  // K and V of tile kt into ring stage st.
+  auto dma = [&](int kt, int st) {
+    const uint32_t kd = dst0 + K_OFF + 2 * st * TILE;
+    const uint32_t vd = dst0 + V_OFF + 2 * st * TILE;
     if (kt * BN + BN <= p.skv) {
-      // Full tile: scalar tile base plus a 32-bit per-lane byte offset.
       const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride);
       const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        kreg[i] = *reinterpret_cast<const u32x4 *>(kt_base + i * rstep_bytes + goff0);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(vt_base + i * rstep_bytes + goff0);
+      for (int i = 0; i < INSTS; ++i) {
+        dma1(kd + 2 * i * kDqWaves * RPI * D, goff0, kt_base + i * istep_bytes);
+        dma1(vd + 2 * i * kDqWaves * RPI * D, goff0, vt_base + i * istep_bytes);
       }
     } else {
       // Ragged last tile: rows past the end read the last row (always masked).
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int64_t o = (int64_t)min(kt * BN + srow + i * RSTEP, p.skv - 1) * p.kv_ss + scol;
-        kreg[i] = *reinterpret_cast<const u32x4 *>(kbase + o);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(vbase + o);
+      for (int i = 0; i < INSTS; ++i) {
+        const int64_t o = (int64_t)min(kt * BN + srow + i * kDqWaves * RPI, p.skv - 1) * p.kv_ss + scol;
+        dma1(kd + 2 * i * kDqWaves * RPI * D, (uint32_t)(o * 2), kbase);
+        dma1(vd + 2 * i * kDqWaves * RPI * D, (uint32_t)(o * 2), vbase);
       }
     }
   };
-  auto swrite = [&](int stage) {
+
+  // ---- per-lane LDS addressing ----------------------------------------------
+  // Row reads of K and V (A operands of S^T and dP^T: key col of the block,
+  // chunk 2s+half) and transpose reads of K (A operand of dQ^T = K^T dS^T);
+  // stage, key block and k-step are immediates.
+  // (Separate K and V bases: the V ring starts 64 KiB in, beyond the reach
+  // of an immediate.)
+  uint32_t kaddr[KSTEPS], vaddr[KSTEPS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      *reinterpret_cast<u32x4 *>(&smem[stage][0][woff0 + i * RSTEP * D]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&smem[stage][1][woff0 + i * RSTEP * D]) = vreg[i];
-    }
+  for (int s = 0; s < KSTEPS; ++s) {
+    kaddr[s] = lds0 + K_OFF + 2 * T::chunk_off(col, 2 * s + half);
+    vaddr[s] = lds0 + V_OFF + 2 * T::chunk_off(col, 2 * s + half);
+  }
+  uint32_t taddr[2][DB];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      taddr[u][db] = lds0 + 2 * T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
+                                            32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  auto lds_b128 = [](uint32_t addr) -> bf16x8 {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
+  };
+  auto lds_tr = [&](int db, uint32_t off) -> bf16x8 {
+    const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[0][db] + off));
+    const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[1][db] + off));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
   f32x16 qacc[DB];
@@ -650,61 +686,157 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     for (int i = 0; i < 16; ++i) qacc[db][i] = 0.0f;
   const float c2 = p.scale_log2;
 
-  if (ntiles > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
+  // Block bb (key block kb = bb % 2 of tile bb / 2, ring stage (bb / 2) % 4)
+  // operand reads at compile-time offsets: K or V rows (k-step s), K^T
+  // (k-step k2 over the block's keys, O^T block db).
+  auto kv_row = [&](bool v, int st, int kb, int s) {
+    return lds_b128((v ? vaddr[s] : kaddr[s]) + 2 * (st * TILE + kb * 32 * D));
+  };
+  auto k_tr = [&](int st, int kb, int k2, int db) {
+    return lds_tr(db, K_OFF + 2 * (st * TILE + (32 * kb + 16 * k2) * D));
+  };
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
-    const int64_t tile_plo = p.kv_pos0 + (int64_t)kt * BN;
-    const bool active = wrows > 0 && (!p.causal || tile_plo <= wave_qhi);
-    if (active) {
-      const __bf16 *ks = smem[st][0];
-      const __bf16 *vs = smem[st][1];
-      const bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
-      int t = BN;   // key kb*32 + 8*(i/4) + 4*half + i%4 visible iff (that - 4*half) <= t
-      if (need_mask) {
-        int lim = p.skv - 1 - kt * BN;
-        if (p.causal) {
-          const int64_t rel = qpos - tile_plo;
-          lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
-        }
-        t = lim - 4 * half;
-      }
-      // One 32-key block at a time keeps only one S^T/dP^T pair live.
+  // ---- prologue ---------------------------------------------------------------
+  // K stage 3 stands for "tile -1" in block 0 (its dS is zero): clear it.
+  {
+    u32x4 *k3 = reinterpret_cast<u32x4 *>(smem + K_OFF + 2 * 3 * TILE);
+    for (int i = tid; i < TILE / 8; i += NT) k3[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // S^T, dP^T of a block alternate between two register sets by block parity.
+  f32x16 sbuf[2], pbuf[2];
+  bf16x8 dsbuf[2][2];   // dS^T of the last two blocks (bf16 B operands)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sacc, pacc;
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] = 0.0f;
-          pacc[i] = 0.0f;
-        }
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const int off = koff[s] + kb * 32 * D;
-          sacc = mfma32(*reinterpret_cast<const bf16x8 *>(ks + off), qf[s], sacc);
-          pacc = mfma32(*reinterpret_cast<const bf16x8 *>(vs + off), gf[s], pacc);
-        }
-        bf16x8 dsf[2];
+      for (int e = 0; e < 8; ++e) dsbuf[q][k2][e] = (__bf16)0.0f;
+  if (ntiles > 0) dma(0, 0);
+  if (ntiles > 1) dma(1, 1);
+  wait_vmem_all();
+  __syncthreads();
+  if (ntiles > 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -lse2));
-          if (need_mask) pv = (kb * 32 + 8 * (i >> 2) + (i & 3) > t) ? 0.0f : pv;
-          dsf[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - delta));
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2)
-            qacc[db] = mfma32(tro.read(ks, 32 * kb + 16 * k2, db), dsf[k2], qacc[db]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      sbuf[0][i] = 0.0f;
+      pbuf[0][i] = 0.0f;
     }
-    if (kt + 1 < ntiles) swrite(st ^ 1);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      sbuf[0] = mfma32(kv_row(false, 0, 0, s), qf[s], sbuf[0]);
+      pbuf[0] = mfma32(kv_row(true, 0, 0, s), gf[s], pbuf[0]);
+    }
+  }
+
+  constexpr int AHEAD = 2;
+  constexpr int NBUF = AHEAD + 1;
+  constexpr int NDQ = 2 * DB;            // dQ^T products of a block (k2, db)
+  constexpr int NSLOT = NDQ + 2 * KSTEPS;
+
+  // One block bb = 2*J + KB (tile J, key block KB; J4 = J % 4): dQ^T(bb-1)
+  // and S^T, dP^T(bb+1) on the matrix core, dS^T(bb) on the VALU.
+  auto block = [&](auto j4_tag, auto kb_tag, int bb) {
+    constexpr int J4 = decltype(j4_tag)::value, KB = decltype(kb_tag)::value;
+    constexpr int SET = KB;                       // block parity
+    constexpr int ST_PREV = KB == 0 ? (J4 + 3) % STG : J4;   // stage of block bb-1
+    constexpr int KB_PREV = 1 - KB;
+    constexpr int ST_NEXT = KB == 0 ? J4 : (J4 + 1) % STG;   // stage of block bb+1
+    constexpr int KB_NEXT = 1 - KB;
+    f32x16 &scur = sbuf[SET], &pcur = pbuf[SET];
+    f32x16 &snext = sbuf[1 - SET], &pnext = pbuf[1 - SET];
+    const bf16x8 (&dsprev)[2] = dsbuf[1 - SET];
+    bf16x8 (&dscur)[2] = dsbuf[SET];
+    // Mask of block bb (diagonal or ragged blocks only): key 8*(i/4) +
+    // 4*half + i%4 of the block is visible iff it is <= lim; masked scores
+    // become -inf (P = 0).
+    const int64_t blk_plo = p.kv_pos0 + (int64_t)bb * 32;
+    const bool need_mask = (bb * 32 + 32 > p.skv) || (p.causal && blk_plo + 31 > wave_qlo);
+    if (need_mask) {
+      int lim = p.skv - 1 - bb * 32;
+      if (p.causal) {
+        const int64_t rel = qpos - blk_plo;
+        lim = min(lim, (int)(rel < -1 ? -1 : (rel > 32 ? 32 : rel)));
+      }
+      const int t = lim - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) scur[i] = (8 * (i >> 2) + (i & 3) > t) ? -INFINITY : scur[i];
+    }
+    // Operand o: o < NDQ is K^T of block bb-1 (k2 = o / DB, db = o % DB);
+    // then K (even) and V (odd) rows of block bb+1 for k-step (o - NDQ) / 2.
+    auto read = [&](auto o_tag) -> bf16x8 {
+      constexpr int o = decltype(o_tag)::value;
+      if constexpr (o < NDQ) {
+        return k_tr(ST_PREV, KB_PREV, o / DB, o % DB);
+      } else {
+        constexpr int u = o - NDQ;
+        return kv_row(u & 1, ST_NEXT, KB_NEXT, u >> 1);
+      }
+    };
+    bf16x8 opnd[NBUF];
+    static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read(o); });
+    static_for<NSLOT>([&](auto t_tag) {
+      constexpr int o = decltype(t_tag)::value;
+      if constexpr (o + AHEAD < NSLOT) opnd[(o + AHEAD) % NBUF] = read(IC<o + AHEAD>{});
+      if constexpr (o < NDQ) {
+        constexpr int k2 = o / DB, db = o % DB;
+        qacc[db] = mfma32(opnd[o % NBUF], dsprev[k2], qacc[db]);
+      } else {
+        constexpr int u = o - NDQ, s = u >> 1;
+        f32x16 &dst = (u & 1) ? pnext : snext;
+        const bf16x8 &bop = (u & 1) ? gf[s] : qf[s];
+        if constexpr (s == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+          dst = mfma32(opnd[o % NBUF], bop, z);
+        } else {
+          dst = mfma32(opnd[o % NBUF], bop, dst);
+        }
+      }
+      // dS^T pair e (elements 2e, 2e+1 of block bb) in slot e * NSLOT / 8.
+      static_for<8>([&](auto e_tag) {
+        constexpr int e = decltype(e_tag)::value, i = 2 * e;
+        if constexpr (e * NSLOT / 8 == o) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[i], c2, -lse2));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[i + 1], c2, -lse2));
+          const float x0 = p0 * (pcur[i] - delta);
+          const float x1 = p1 * (pcur[i + 1] - delta);
+          const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+          dscur[i >> 3][i & 7] = t2[0];
+          dscur[i >> 3][(i & 7) + 1] = t2[1];
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // Pin dS^T(bb) to the slots above (otherwise the compiler sinks it past
+    // the next block's mask branch, away from the products it overlaps).
+    asm volatile("" ::"v"(dscur[0]), "v"(dscur[1]));
+  };
+
+  // Tile step J (J4 = J % 4): tile J+2 on its way into the rings (into the
+  // stage of tile J-2, last read in step J-1), then the tile's two blocks.
+  auto tile_step = [&](auto j4_tag, int J) {
+    constexpr int J4 = decltype(j4_tag)::value;
+    if (J + 2 < ntiles) dma(J + 2, (J4 + 2) % STG);
+    block(j4_tag, IC<0>{}, 2 * J);
+    block(j4_tag, IC<1>{}, 2 * J + 1);
+    wait_vmem_all();
     __syncthreads();
+  };
+  for (int J = 0; J < ntiles; J += STG) {
+    tile_step(IC<0>{}, J);
+    if (J + 1 < ntiles) tile_step(IC<1>{}, J + 1);
+    if (J + 2 < ntiles) tile_step(IC<2>{}, J + 2);
+    if (J + 3 < ntiles) tile_step(IC<3>{}, J + 3);
+  }
+  // dQ^T of the last block (tile ntiles-1, key block 1; dS^T in set 1).
+  if (ntiles > 0) {
+    const int st = (ntiles - 1) % STG;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        qacc[db] = mfma32(k_tr(st, 1, k2, db), dsbuf[1][k2], qacc[db]);
   }
 
   if (!qvalid) return;
