@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   // LDS layout (bytes)
   constexpr int Q_OFF = 0;
   constexpr int O_OFF = Q_OFF + QSTG * QTILE * 2;
-  constexpr int X_OFF = O_OFF + OSTG * QTILE * 2;                    // [2][4 waves][64 lanes][XPER] bf16
+  constexpr int X_OFF = O_OFF + OSTG * QTILE * 2;                    // [2][4 waves][QSTEPS][64 lanes] bf16x8
   constexpr int L_OFF = X_OFF + 2 * 4 * 64 * XPER * 2;               // [QSTG][QT] LSE*log2(e)
   constexpr int DL_OFF = L_OFF + QSTG * QT * 4;                      // [QSTG][QT] Delta
   constexpr int LDS_BYTES = DL_OFF + QSTG * QT * 4;
@@ -195,21 +195,33 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
   };
-  // Rows of step u's tile of `src` (Q: row stride q_ss; dO: o_ss) into LDS at
-  // byte offset dst; rows past the chunk end read its last row.
+  // Per-lane byte offsets of full tiles (Q rows q_ss apart, dO rows o_ss).
+  uint32_t goq[INSTS], goo[INSTS];
+#pragma unroll
+  for (int i = 0; i < INSTS; ++i) {
+    goq[i] = (uint32_t)(((int64_t)(srow + i * NW * RPI) * p.q_ss + scol) * 2);
+    goo[i] = (uint32_t)(((int64_t)(srow + i * NW * RPI) * p.o_ss + scol) * 2);
+  }
+  const __bf16 *qhead = static_cast<const __bf16 *>(p.q) + b * p.q_sb + (int64_t)hk * p.group * p.q_sh;
+  const __bf16 *ohead = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + (int64_t)hk * p.group * p.o_sh;
+  // Rows of step u's tile of Q (is_q) or dO into LDS at byte offset dst;
+  // rows past the chunk end read its last row.
   auto dma_tile = [&](const Cursor &u, bool is_q, uint32_t dst) {
-    const int head = hk * p.group + u.h;
     const int row0 = u.t * QT;
     const int rows_left = p.chunk_len - 1 - row0;
     const int64_t lrow0 = (int64_t)u.c * p.chunk_len + row0;
     const int64_t ss = is_q ? p.q_ss : p.o_ss;
-    const __bf16 *base = is_q ? static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh
-                              : static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh;
-    const __bf16 *tbase = base + lrow0 * ss;
+    const __bf16 *tbase = (is_q ? qhead + u.h * p.q_sh : ohead + u.h * p.o_sh) + lrow0 * ss;
+    if (rows_left >= QT - 1) {
 #pragma unroll
-    for (int i = 0; i < INSTS; ++i) {
-      const int r = min(srow + i * NW * RPI, rows_left);
-      dma16(lds0 + dst + 2 * (i * NW * RPI + wave * RPI) * D, (uint32_t)((r * ss + scol) * 2), tbase);
+      for (int i = 0; i < INSTS; ++i)
+        dma16(lds0 + dst + 2 * (i * NW * RPI + wave * RPI) * D, is_q ? goq[i] : goo[i], tbase);
+    } else {
+#pragma unroll
+      for (int i = 0; i < INSTS; ++i) {
+        const int r = min(srow + i * NW * RPI, rows_left);
+        dma16(lds0 + dst + 2 * (i * NW * RPI + wave * RPI) * D, (uint32_t)((r * ss + scol) * 2), tbase);
+      }
     }
   };
   // LSE*log2(e) (wave 0) and Delta (wave 1) of step u's rows.
@@ -263,9 +275,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[1][db] + off));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // P exchange: lane l of key group kw, stage x holds XPER bf16 (4 operands).
-  const uint32_t xaddr = lds0 + X_OFF + (kw * 64 + lane) * XPER * 2;
+  // P exchange: operand ps of lane l of key group kw at stage x; lanes are
+  // 16 bytes apart (conflict-free).
+  const uint32_t xaddr = lds0 + X_OFF + (kw * QSTEPS * 64 + lane) * 16;
   constexpr uint32_t XSTAGE = 4 * 64 * XPER * 2;
+  constexpr uint32_t XOP = 64 * 16;   // bytes between a lane's operands
 
   // This lane's key row of K (P role) or V (dS role): the B operand.
   bf16x8 kvf[KSTEPS];
@@ -360,10 +374,18 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         }
         bf16x8 pcur[QSTEPS];
         bf16x8 opnd[NBUF];
+        // Bases of this step's Q reads, made opaque so that the row-block
+        // offsets stay instruction immediates.
+        uint32_t rb[KSTEPS];
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          rb[s] = raddr[s] + qnext;
+          asm volatile("" : "+v"(rb[s]));
+        }
         // Half A: S(it+1) (operand u: k-step u/QB of row block u%QB) under P(it).
         auto read_a = [&](auto u_tag) -> bf16x8 {
           constexpr int u = decltype(u_tag)::value, qb = u % QB, s = u / QB;
-          return lds_b128(raddr[s] + qnext + 2 * qb * 32 * D);
+          return lds_b128(rb[s] + 2 * qb * 32 * D);
         };
         static_for<AHEAD>([&](auto u) { opnd[decltype(u)::value] = read_a(u); });
         static_for<NSA>([&](auto t_tag) {
@@ -394,7 +416,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         // P(it) to the dS wavefront of these keys.
 #pragma unroll
         for (int ps = 0; ps < QSTEPS; ++ps)
-          *reinterpret_cast<__attribute__((address_space(3))) bf16x8 *>((uintptr_t)(xaddr + PAR * XSTAGE + 16 * ps)) = pcur[ps];
+          *reinterpret_cast<__attribute__((address_space(3))) bf16x8 *>((uintptr_t)(xaddr + PAR * XSTAGE + XOP * ps)) = pcur[ps];
         // Half B: dV^T += dO(it)^T P(it) (operand o: k-step o / DB, block o % DB).
         auto read_b = [&](auto o_tag) -> bf16x8 {
           constexpr int o = decltype(o_tag)::value, ps = o / DB, db = o % DB;
@@ -437,9 +459,21 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       // Half A: dK^T += Q(it-2)^T dS(it-2).
       if (it >= 2) {
         const uint32_t qold = 2 * ((it - 2) % QSTG) * QTILE;
+        // Bases of this step's Q^T reads (opaque: see the P role).
+        uint32_t tb[2][DB];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            tb[u][db] = taddr[u][db] + qold;
+            asm volatile("" : "+v"(tb[u][db]));
+          }
         auto read_a = [&](auto o_tag) -> bf16x8 {
           constexpr int o = decltype(o_tag)::value, ps = o / DB, db = o % DB;
-          return lds_tr(db, qold + 2 * 16 * D * ps);
+          constexpr uint32_t off = 2 * 16 * D * ps;
+          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(tb[0][db] + off));
+          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(tb[1][db] + off));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_a(o); });
         static_for<NSB>([&](auto t_tag) {
@@ -459,7 +493,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 #pragma unroll
         for (int ps = 0; ps < QSTEPS; ++ps)
           pk[ps] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
-              (uintptr_t)(xaddr + (1 - PAR) * XSTAGE + 16 * ps));
+              (uintptr_t)(xaddr + (1 - PAR) * XSTAGE + XOP * ps));
         f32x4 d4[QB][4];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
