@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 // a share of the vector work, with scheduling fences between slots. Query
 // tiles (Q, dO and the rows' LSE*log2(e) and Delta) are loaded straight from
 // global memory into LDS rings; query tiles wholly before the keys are never
-// visited; one barrier per step.
+// visited; one barrier per step. Only the P wavefronts issue the loads.
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * 64;
 
@@ -176,14 +176,16 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   if (c0.t >= nq_tiles) next_chunk(c0);
 
   // ---- staging: global -> LDS directly (see the forward kernel) -------------
-  // One instruction of a wavefront moves RPI rows of a Q or dO tile; lane l
-  // lands at LDS offset 16*l of them and fetches the chunk that the row's
-  // swizzle puts there. Wavefront w's instruction i covers rows
-  // (i*NW + w)*RPI ...; the row modulo 16 does not depend on i.
+  // Only the P wavefronts stage (the dS wavefronts carry the longer chain of
+  // each step). One instruction of a wavefront moves RPI rows of a Q or dO
+  // tile; lane l lands at LDS offset 16*l of them and fetches the chunk that
+  // the row's swizzle puts there. P wavefront kw's instruction i covers rows
+  // (i*SW + kw)*RPI ...; the row modulo 16 does not depend on i.
+  constexpr int SW = 4;                       // staging wavefronts
   constexpr int RPI = 64 / NC;
-  constexpr int INSTS = QT / (NW * RPI);
-  static_assert(INSTS >= 1 && (NW * RPI) % 16 == 0, "staging shape");
-  const int srow = wave * RPI + lane / NC;
+  constexpr int INSTS = QT / (SW * RPI);
+  static_assert(INSTS >= 1 && (SW * RPI) % 16 == 0, "staging shape");
+  const int srow = kw * RPI + lane / NC;
   const int scol = 8 * ((lane % NC) ^ T::swz(srow));
   auto dma16 = [](uint32_t m0, uint32_t voff, const void *sbase) {
     uint32_t saved;
@@ -195,13 +197,10 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
   };
-  // Per-lane byte offsets of full tiles (Q rows q_ss apart, dO rows o_ss).
-  uint32_t goq[INSTS], goo[INSTS];
-#pragma unroll
-  for (int i = 0; i < INSTS; ++i) {
-    goq[i] = (uint32_t)(((int64_t)(srow + i * NW * RPI) * p.q_ss + scol) * 2);
-    goo[i] = (uint32_t)(((int64_t)(srow + i * NW * RPI) * p.o_ss + scol) * 2);
-  }
+  // Per-lane byte offsets of the first instruction's rows in full tiles (Q
+  // rows q_ss apart, dO rows o_ss); instruction i adds a wave-uniform step.
+  const uint32_t goq = (uint32_t)(((int64_t)srow * p.q_ss + scol) * 2);
+  const uint32_t goo = (uint32_t)(((int64_t)srow * p.o_ss + scol) * 2);
   const __bf16 *qhead = static_cast<const __bf16 *>(p.q) + b * p.q_sb + (int64_t)hk * p.group * p.q_sh;
   const __bf16 *ohead = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + (int64_t)hk * p.group * p.o_sh;
   // Rows of step u's tile of Q (is_q) or dO into LDS at byte offset dst;
@@ -215,12 +214,13 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     if (rows_left >= QT - 1) {
 #pragma unroll
       for (int i = 0; i < INSTS; ++i)
-        dma16(lds0 + dst + 2 * (i * NW * RPI + wave * RPI) * D, is_q ? goq[i] : goo[i], tbase);
+        dma16(lds0 + dst + 2 * (i * SW * RPI + kw * RPI) * D, (is_q ? goq : goo) + (uint32_t)(i * SW * RPI * ss * 2),
+              tbase);
     } else {
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) {
-        const int r = min(srow + i * NW * RPI, rows_left);
-        dma16(lds0 + dst + 2 * (i * NW * RPI + wave * RPI) * D, (uint32_t)((r * ss + scol) * 2), tbase);
+        const int r = min(srow + i * SW * RPI, rows_left);
+        dma16(lds0 + dst + 2 * (i * SW * RPI + kw * RPI) * D, (uint32_t)((r * ss + scol) * 2), tbase);
       }
     }
   };
@@ -304,7 +304,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 
   // Prologue: Q of steps 0 and 1 (when there is a step 1), dO of step 0.
   // Every load is of a step that exists: the cursors never run past the last.
-  if (total > 0) {
+  if (prole && total > 0) {
     load_q(0);
     if (total > 1) load_q(1);
     load_o(0);
@@ -344,13 +344,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         const uint32_t qnext = 2 * ((it + 1) % QSTG) * QTILE;   // Q stage of step it+1
         constexpr uint32_t ocur = 2 * PAR * QTILE;              // dO stage of step it
         const int st = it % QSTG;
-        // LSE*log2(e) of this lane's rows 32qb + 8gq + 4half + e.
-        f32x4 l4[QB][4];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            l4[qb][gq] = lds_f4(lds0 + L_OFF + 4 * (st * QT + 32 * qb + 8 * gq + 4 * half));
+        // LSE*log2(e) of this lane's rows, 4 at a time (group g: rows
+        // 32(g/4) + 8(g%4) + 4half + e), each group read one group ahead.
+        const uint32_t lbase = lds0 + L_OFF + 4 * (st * QT + 4 * half);
+        f32x4 lg[2];
+        lg[0] = lds_f4(lbase);
         // Mask: row r of the tile sees this lane's key iff lo <= r <= hi.
         const int64_t qpos0 = cs.cpos + cs.t * QT;
         const int rows_left = p.chunk_len - 1 - cs.t * QT;
@@ -403,9 +401,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           static_for<NPAIR>([&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
             if constexpr (u * NSA / NPAIR == t) {
-              constexpr int rq = u / 8, i = 2 * (u % 8);
-              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][i], c2, -l4[rq][i >> 2][i & 3]));
-              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][i + 1], c2, -l4[rq][(i + 1) >> 2][(i + 1) & 3]));
+              constexpr int rq = u / 8, i = 2 * (u % 8), g = u / 2;
+              if constexpr (u % 2 == 0 && g + 1 < NPAIR / 2)
+                lg[(g + 1) % 2] = lds_f4(lbase + 4 * (32 * ((g + 1) / 4) + 8 * ((g + 1) % 4)));
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][i], c2, -lg[g % 2][i & 3]));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][i + 1], c2, -lg[g % 2][(i + 1) & 3]));
               const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
               pcur[2 * rq + (i >> 3)][i & 7] = t2[0];
               pcur[2 * rq + (i >> 3)][(i & 7) + 1] = t2[1];
@@ -454,7 +454,6 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       for (int e = 0; e < 8; ++e) dsf[ps][e] = (__bf16)0.0f;
     auto step_ds = [&](auto par_tag, int it) {
       constexpr int PAR = decltype(par_tag)::value;
-      staging(it);
       bf16x8 opnd[NBUF];
       // Half A: dK^T += Q(it-2)^T dS(it-2).
       if (it >= 2) {
@@ -494,12 +493,10 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         for (int ps = 0; ps < QSTEPS; ++ps)
           pk[ps] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
               (uintptr_t)(xaddr + (1 - PAR) * XSTAGE + XOP * ps));
-        f32x4 d4[QB][4];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            d4[qb][gq] = lds_f4(lds0 + DL_OFF + 4 * (st * QT + 32 * qb + 8 * gq + 4 * half));
+        // Delta of this lane's rows, 4 at a time, one group ahead (as LSE).
+        const uint32_t dbase = lds0 + DL_OFF + 4 * (st * QT + 4 * half);
+        f32x4 dg[2];
+        dg[0] = lds_f4(dbase);
         auto read_b = [&](auto u_tag) -> bf16x8 {
           constexpr int u = decltype(u_tag)::value, qb = u % QB, s = u / QB;
           return lds_b128(raddr[s] + ocur + 2 * qb * 32 * D);
@@ -519,10 +516,12 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           static_for<NPAIR>([&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
             if constexpr (u * NSA / NPAIR == t) {
-              constexpr int rq = u / 8, i = 2 * (u % 8), ps = 2 * rq + (i >> 3);
+              constexpr int rq = u / 8, i = 2 * (u % 8), ps = 2 * rq + (i >> 3), g = u / 2;
+              if constexpr (u % 2 == 0 && g + 1 < NPAIR / 2)
+                dg[(g + 1) % 2] = lds_f4(dbase + 4 * (32 * ((g + 1) / 4) + 8 * ((g + 1) % 4)));
               const float p0 = (float)pk[ps][i & 7], p1 = (float)pk[ps][(i & 7) + 1];
-              const float x0 = p0 * (pprev[rq][i] - d4[rq][i >> 2][i & 3]);
-              const float x1 = p1 * (pprev[rq][i + 1] - d4[rq][(i + 1) >> 2][(i + 1) & 3]);
+              const float x0 = p0 * (pprev[rq][i] - dg[g % 2][i & 3]);
+              const float x1 = p1 * (pprev[rq][i + 1] - dg[g % 2][(i + 1) & 3]);
               const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
               dsf[ps][i & 7] = t2[0];
               dsf[ps][(i & 7) + 1] = t2[1];
