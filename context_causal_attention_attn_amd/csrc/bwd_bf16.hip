@@ -493,10 +493,14 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         for (int ps = 0; ps < QSTEPS; ++ps)
           pk[ps] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
               (uintptr_t)(xaddr + (1 - PAR) * XSTAGE + XOP * ps));
-        // Delta of this lane's rows, 4 at a time, one group ahead (as LSE).
-        const uint32_t dbase = lds0 + DL_OFF + 4 * (st * QT + 4 * half);
-        f32x4 dg[2];
-        dg[0] = lds_f4(dbase);
+        // Delta: lane 16r+e of row block qb reads the value of accumulator
+        // element e of the lanes of its row of 16 (row 32qb + 8(e/4) +
+        // 4(r/2) + e%4); element e then takes it by row broadcast.
+        float dl[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          dl[qb] = *reinterpret_cast<const __attribute__((address_space(3))) float *>(
+              (uintptr_t)(lds0 + DL_OFF + 4 * (st * QT + 32 * qb + 8 * ((lane & 15) >> 2) + 4 * half + (lane & 3))));
         auto read_b = [&](auto u_tag) -> bf16x8 {
           constexpr int u = decltype(u_tag)::value, qb = u % QB, s = u / QB;
           return lds_b128(raddr[s] + ocur + 2 * qb * 32 * D);
@@ -516,12 +520,10 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           static_for<NPAIR>([&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
             if constexpr (u * NSA / NPAIR == t) {
-              constexpr int rq = u / 8, i = 2 * (u % 8), ps = 2 * rq + (i >> 3), g = u / 2;
-              if constexpr (u % 2 == 0 && g + 1 < NPAIR / 2)
-                dg[(g + 1) % 2] = lds_f4(dbase + 4 * (32 * ((g + 1) / 4) + 8 * ((g + 1) % 4)));
+              constexpr int rq = u / 8, i = 2 * (u % 8), ps = 2 * rq + (i >> 3);
               const float p0 = (float)pk[ps][i & 7], p1 = (float)pk[ps][(i & 7) + 1];
-              const float x0 = p0 * (pprev[rq][i] - dg[g % 2][i & 3]);
-              const float x1 = p1 * (pprev[rq][i + 1] - dg[g % 2][(i + 1) & 3]);
+              const float x0 = p0 * (pprev[rq][i] - row_bcast<i>(dl[rq]));
+              const float x1 = p1 * (pprev[rq][i + 1] - row_bcast<i + 1>(dl[rq]));
               const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
               dsf[ps][i & 7] = t2[0];
               dsf[ps][(i & 7) + 1] = t2[1];
