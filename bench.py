@@ -18,8 +18,11 @@ roofline object describes the kernel with the largest average. Its "traffic"
 comes from the rocprofv3 counter summaries in profiles/ when one matches the
 kernel's current source text, else null.
 
-Prints ONE JSON line. `--detail` adds every other share of the workload list
-to that line under "detail".
+After the timed region the step keeps running for about 1.5 s while amd-smi
+reads the GFX clocks and socket power once ("clock"; the chip runs at its
+power cap, well below the 2.4 GHz the peak assumes). Prints ONE JSON line.
+`--detail` adds every other share of the workload list to that line under
+"detail".
 """
 from __future__ import annotations
 
@@ -45,7 +48,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--rank", type=int, default=None,
+                    help="CP rank of the workload's share (default: the workload's first listed rank)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock/power sample")
     ap.add_argument("--detail", action="store_true", help="also time every other share")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
@@ -166,8 +172,73 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd):
           "dkdv": (2 * B * Hq * Sq * D * el + 2 * B * Hkv * Skv * D * el + 8 * B * Hq * Sq
                    + 2 * B * Hkv * Skv * D * 4),
           "dq": (3 * B * Hq * Sq * D * el + 2 * B * Hkv * Skv * D * el + 8 * B * Hq * Sq)}
+    def step():
+        fwd()
+        if dout is not None:
+            bwd(new_events()[1:])
+
     return dict(pairs=pairs, flops=fl, bytes=io, ms=ms, total_ms=total_ms, wall_s=wall,
-                hq=Hq, batch=B, sq=Sq, has_bwd=dout is not None)
+                hq=Hq, batch=B, sq=Sq, has_bwd=dout is not None, step=step)
+
+
+def parse_smi_metric(text):
+    """GFX clocks (MHz, one per XCD) and socket power (W) from the text of
+    `amd-smi metric -c -p` (sections GFX_<n>: with a CLK: line each)."""
+    import re
+    clocks, power, in_gfx = [], None, False
+    for line in text.splitlines():
+        m = re.match(r"\s*SOCKET_POWER:\s*([0-9.]+)\s*W", line)
+        if m and power is None:
+            power = float(m.group(1))
+        if re.match(r"\s*GFX_\d+:\s*$", line):
+            in_gfx = True
+            continue
+        if re.match(r"\s*[A-Z][A-Z0-9_]*:\s*$", line):
+            in_gfx = False
+            continue
+        m = re.match(r"\s*CLK:\s*([0-9.]+)\s*MHz", line)
+        if m and in_gfx:
+            clocks.append(float(m.group(1)))
+            in_gfx = False
+    return clocks, power
+
+
+def sample_clock(step, seconds=1.5):
+    """Run `step` back to back for about `seconds` and read the GFX clocks and
+    socket power once, half-way, with amd-smi (the timed region itself is too
+    short for the tool). None when amd-smi is not available."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    out = {}
+
+    def probe():
+        time.sleep(seconds / 2)
+        try:
+            r = subprocess.run([exe, "metric", "-c", "-p"], capture_output=True, text=True, timeout=20)
+            out["text"] = r.stdout
+        except (OSError, subprocess.SubprocessError):
+            out["text"] = ""
+
+    th = threading.Thread(target=probe)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() or time.perf_counter() - t0 < seconds:
+        step()
+        torch.cuda.synchronize()
+    th.join()
+    clocks, power = parse_smi_metric(out.get("text", ""))
+    if not clocks:
+        return None
+    clocks.sort()
+    med = clocks[len(clocks) // 2] if len(clocks) % 2 else 0.5 * (clocks[len(clocks) // 2 - 1] + clocks[len(clocks) // 2])
+    return {"gfx_mhz_median": med, "gfx_mhz_min": clocks[0], "gfx_mhz_max": clocks[-1],
+            "socket_power_w": power, "source": "amd-smi metric -c -p while the step loop ran"}
 
 
 def copy_calibration(mib):
@@ -183,7 +254,7 @@ def copy_calibration(mib):
     del src, dst
 
 
-def cpu_baseline(spec, prob):
+def cpu_baseline(spec, prob, rank):
     """The oracle as it stands, on a bounded sample of the same share: query
     head 0 (its KV head 0), every local row, forward + backward."""
     import numpy as np
@@ -191,7 +262,7 @@ def cpu_baseline(spec, prob):
 
     import oracle.cp_share as oc
 
-    kind, cp, r, U = share_for(spec, spec["ranks"][0])
+    kind, cp, r, U = share_for(spec, rank)
     S, Hq, Hkv = spec["seq"], spec["hq"], spec["hkv"]
     if kind == "contiguous":
         sh = oc.contiguous_share(S, Hq, Hkv, cp, r)
@@ -244,7 +315,11 @@ def main():
         from synthetic import global_problem
         prob = global_problem(spec["batch"], spec["hq"], spec["hkv"], spec["seq"], spec["head_dim"],
                               spec["dtype"], 0, with_dout=True)
-    res = time_share(spec, prob, spec["ranks"][0], args.steps, args.warmup, with_bwd)
+    rank = spec["ranks"][0] if args.rank is None else args.rank
+    if not 0 <= rank < spec["cp"]:
+        print(f"--rank {rank} is outside 0..{spec['cp'] - 1} for {args.workload}", file=sys.stderr)
+        sys.exit(2)
+    res = time_share(spec, prob, rank, args.steps, args.warmup, with_bwd)
     ms, fl, io = res["ms"], res["flops"], res["bytes"]
     ms_per_step = res["total_ms"] / args.steps
     flops_step = fl["fwd"] + (fl["bwd"] if res["has_bwd"] else 0.0)
@@ -289,7 +364,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "kind": spec["kind"], "cp": spec["cp"],
-                   "rank": spec["ranks"][0], "batch": spec["batch"], "hq": spec["hq"], "hkv": spec["hkv"],
+                   "rank": rank, "batch": spec["batch"], "hq": spec["hq"], "hkv": spec["hkv"],
                    "head_dim": spec["head_dim"], "seq_global": spec["seq"], "sq_local": res["sq"],
                    "causal_pairs_per_head": res["pairs"],
                    "passes": "fwd+bwd" if res["has_bwd"] else "fwd"},
@@ -302,6 +377,15 @@ def main():
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.no_clock:
+        clk = sample_clock(res["step"])
+        if clk:
+            # the same achieved rates against the peak at the clock actually run
+            f = PEAK_BF16_TFLOPS * clk["gfx_mhz_median"] / 2400.0
+            clk["mfma_frac_at_clock"] = {p: round(kernels[p]["achieved"] / f, 4)
+                                         for p in kernels if kernels[p]["unit"] == "TFLOP/s"}
+        line["clock"] = clk
+    del res
     if args.detail:
         detail = {}
         for name, sp in WORKLOADS.items():
@@ -325,7 +409,7 @@ def main():
     if args.copy_calib_mib:
         copy_calibration(args.copy_calib_mib)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(spec, prob)
+        line["cpu_baseline"] = cpu_baseline(spec, prob, rank)
     print(json.dumps(line), flush=True)
 
 
