@@ -12,15 +12,19 @@
 //    through LDS rings (2 stages for K, 3 for V) once per workgroup, loaded
 //    straight from global memory into LDS (global_load_lds_dwordx4), and are
 //    read by every head;
-//  * each wavefront owns 32 query rows of one head and computes transposed
-//    score tiles S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16,
-//    so that a lane holds one query column: the row statistics of the online
-//    softmax are lane-local plus one permlane32 swap between the two halves
-//    of the wavefront;
+//  * each wavefront owns 32 query rows of one head (two 16-row blocks) and
+//    computes transposed score tiles S^T = K Q^T (keys x queries) with
+//    v_mfma_f32_16x16x32_bf16, so that a lane holds one query column: the
+//    row statistics of the online softmax are lane-local plus a reduction
+//    over the four lanes of a column. Each K fragment read from LDS feeds both
+//    row blocks. (Under the chip's power limit this shape sustains about 12 %
+//    more bf16 throughput than the 32x32x16 one.);
 //  * the probabilities P^T, converted to bf16 in registers, are the B operand
 //    of O^T += V^T P^T without any shuffle: the contraction index (keys) is
 //    permuted identically in both operands, and V^T is read from the
-//    row-major V tile with the gfx950 LDS transpose read ds_read_b64_tr_b16;
+//    row-major V tile with the gfx950 LDS transpose read ds_read_b64_tr_b16
+//    (V tiles use their own row swizzle, which keeps those reads free of
+//    bank conflicts);
 //  * three-way software pipeline: in step j the matrix core computes
 //    O^T += V^T P^T of tile j-1 and S^T of tile j+1 while the vector ALU turns
 //    the scores of tile j into probabilities. The three are independent; the
@@ -31,7 +35,7 @@
 //    tiles crossing the causal diagonal (or the ragged end of K/V) are masked;
 //  * the running max is a reference point, not recomputed per tile: the
 //    probabilities of a tile are formed against the current reference, and
-//    only when a row's tile sum exceeds 2^16 (or the row has no reference
+//    only when a lane's partial tile sum exceeds 2^16 (or the row has no reference
 //    yet) is its max taken, O rescaled and the tile redone.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -45,7 +49,7 @@ namespace {
 constexpr int BN = kFwdBlockKV;          // keys per tile (64)
 constexpr int NW = kFwdWaves;            // wavefronts per workgroup (8)
 constexpr int NT = NW * 64;
-constexpr int QB = kFwdWaveRows / 32;    // 32-row query blocks per wavefront
+constexpr int QB = kFwdWaveRows / 16;    // 16-row query blocks per wavefront
 constexpr int KSTAGES = 2;               // K ring: tile t in stage t % 2
 constexpr int VSTAGES = 3;               // V ring: tile t in stage t % 3
 constexpr int UNROLL = 6;                // steps per loop trip (both ring indices fixed)
@@ -57,13 +61,14 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr int HPW = NW / RB;         // heads per work item
   constexpr int BM = kFwdWaveRows * RB;  // query rows per work item
   constexpr int NC = D / 8;            // 16-byte chunks per row
-  constexpr int KSTEPS = D / 16;       // k-steps of S^T (contraction over D)
-  constexpr int DB = D / 32;           // 32-row blocks of O^T
-  constexpr int KB = BN / 32;          // 32-key blocks of S^T
-  constexpr int PSTEPS = BN / 16;      // k-steps of O^T (contraction over keys)
+  constexpr int KSTEPS = D / 32;       // k-steps of S^T (contraction over D)
+  constexpr int DB = D / 16;           // 16-row blocks of O^T
+  constexpr int KB = BN / 16;          // 16-key blocks of S^T
+  constexpr int PSTEPS = BN / 32;      // k-steps of O^T (contraction over keys)
   constexpr int TILE = BN * D;
-  static_assert(BN == 64 && (QB == 1 || QB == 2), "tile shape");
-  using T = Tile<D>;
+  static_assert(BN == 64 && QB == 2, "tile shape");
+  using T = Tile<D>;     // K tiles (row reads)
+  using TV = TrTile<D>;  // V tiles (transpose reads)
 
   // K ring (2 stages) followed by the V ring (3 stages), in one LDS array:
   // 80 KiB at D = 128.
@@ -74,8 +79,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  const int grp = lane >> 4;   // operand k-slice / accumulator row quarter
+  const int col = lane & 15;   // operand row / accumulator column
 
   // ---- work item ---------------------------------------------------------
   const int bid = blockIdx.x;
@@ -96,14 +101,14 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const int head = head0 + wave / RB;
   const int wrow0 = (wave % RB) * kFwdWaveRows;
   const int64_t wave_qlo = chunk_pos + item_row0 + min(wrow0, item_rows - 1);
-  // Lane rows of the two blocks; rows past the item's last act as its last
-  // row (never stored).
+  // This lane's query row in each 16-row block; rows past the item's last act
+  // as its last row (never stored).
   int local_row[QB];
   int64_t qpos[QB];
   bool qvalid[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int r = wrow0 + 32 * qb + col;
+    const int r = wrow0 + 16 * qb + col;
     const int qrow = min(r, item_rows - 1);
     qvalid[qb] = r < item_rows;
     qpos[qb] = chunk_pos + item_row0 + qrow;
@@ -122,27 +127,26 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh +
-                       (int64_t)local_row[qb] * p.q_ss + 8 * half;
+                       (int64_t)local_row[qb] * p.q_ss + 8 * grp;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
+    for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
   }
   wait_vmem_all();
 
   // ---- per-lane LDS addressing, computed once ------------------------------
   // Byte addresses of this lane's operand reads in stage 0; the stage, key
-  // block and k-step only add constants, which become instruction immediates
-  // (every K read lies within 24 KiB of its base, every V read within 44 KiB).
-  uint32_t kaddr[KSTEPS];                  // K-fragment reads: row col, chunk 2s+half
+  // block and k-step only add constants, which become instruction immediates.
+  uint32_t kaddr[KSTEPS];                  // K-fragment reads: row col, chunk 4s+grp
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) kaddr[s] = lds0 + 2 * T::chunk_off(col, 2 * s + half);
-  uint32_t vaddr[2][DB];                   // V^T transpose reads (k-step ps adds 16 rows)
+  for (int s = 0; s < KSTEPS; ++s) kaddr[s] = lds0 + 2 * T::chunk_off(col, 4 * s + grp);
+  // V^T transpose reads: lane group grp takes keys 4grp .. 4grp+3 and
+  // 16 + 4grp .. of a 32-key k-step, column 16db + col; its 16 lanes address
+  // 4 rows x 16 columns. The V swizzle repeats every 8 rows, so the second
+  // read (16 rows on) and k-step ps (32 rows on) only add constants.
+  uint32_t vaddr[DB];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      vaddr[u][db] = lds0 + 2 * (KSTAGES * TILE +
-                                 T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
-                                             32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)));
+  for (int db = 0; db < DB; ++db)
+    vaddr[db] = lds0 + 2 * (KSTAGES * TILE + TV::elem_off(4 * grp + (col >> 2), 16 * db + 4 * (lane & 3)));
   auto lds_b128 = [](uint32_t addr) -> bf16x8 {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
   };
@@ -156,7 +160,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // rows; each lane fetches the global chunk that the row's swizzle puts at its
   // position (a permutation within the row: still one contiguous row read).
   // Wavefront w's instruction i covers rows (i*NW + w)*RPI ...; the row
-  // modulo 16 (which fixes the swizzle) does not depend on i. The loads are
+  // modulo 16 (which fixes both swizzles) does not depend on i. The loads are
   // issued from inline assembly so that the compiler does not make every LDS
   // read wait for them; each step waits for its own loads (vmcnt(0)) right
   // before the barrier that publishes the tile.
@@ -166,10 +170,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
   const int srow = wave * RPI + lane / NC;           // tile row of instruction 0
-  const int scol = 8 * ((lane % NC) ^ T::swz(srow)); // logical column of this lane's chunk
+  const int scol_k = 8 * ((lane % NC) ^ T::swz(srow));   // logical column of this lane's chunk
+  const int scol_v = 8 * ((lane % NC) ^ TV::swz(srow));
   const int64_t tile_stride = (int64_t)BN * p.kv_ss;
   const int64_t istep_bytes = (int64_t)NW * RPI * p.kv_ss * 2;
-  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
+  const uint32_t goff_k = (uint32_t)(((int64_t)srow * p.kv_ss + scol_k) * 2);
+  const uint32_t goff_v = (uint32_t)(((int64_t)srow * p.kv_ss + scol_v) * 2);
   const uint32_t dst0 = lds0 + 2 * wave * RPI * D;   // this wave's rows in K stage 0
   // M0 is saved and restored around the load: the compiler owns it.
   auto dma1 = [](uint32_t m0, uint32_t voff, const void *sbase) {
@@ -184,12 +190,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if (kt * BN + BN <= p.skv) {
       const char *t_base = reinterpret_cast<const char *>(base + (int64_t)kt * tile_stride);
 #pragma unroll
-      for (int i = 0; i < INSTS; ++i) dma1(dst + 2 * i * NW * RPI * D, goff0, t_base + i * istep_bytes);
+      for (int i = 0; i < INSTS; ++i) dma1(dst + 2 * i * NW * RPI * D, is_v ? goff_v : goff_k, t_base + i * istep_bytes);
     } else {
       // Ragged last tile: rows past the end read the last row (always masked).
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) {
-        const int64_t o = (int64_t)min(kt * BN + srow + i * NW * RPI, p.skv - 1) * p.kv_ss + scol;
+        const int64_t o = (int64_t)min(kt * BN + srow + i * NW * RPI, p.skv - 1) * p.kv_ss + (is_v ? scol_v : scol_k);
         dma1(dst + 2 * i * NW * RPI * D, (uint32_t)(o * 2), base);
       }
     }
@@ -197,15 +203,15 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   auto dma_k = [&](int kt, int stage) { dma(kt, false, dst0 + 2 * stage * TILE); };
   auto dma_v = [&](int kt, int stage) { dma(kt, true, dst0 + 2 * (KSTAGES + stage) * TILE); };
 
-  f32x16 oacc[QB][DB];
+  f32x4 oacc[QB][DB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.0f;
+      for (int i = 0; i < 4; ++i) oacc[qb][db][i] = 0.0f;
   // Running max of scale*log2(e)*s (may lag the true max) and this lane's
-  // partial row sum (its half of the keys), per row block.
+  // partial row sum (its quarter of the keys), per row block.
   float m_run[QB], l_part[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -217,7 +223,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // Matrix-instruction slots of a step. Operand o (one LDS read, used by the
   // QB row blocks in consecutive slots): o in [0, NPV) is V^T of k-step
   // ps = o / DB, O^T block db = o % DB (two transpose reads); o in [NPV, NOP)
-  // is K of key block kb = u / KSTEPS, k-step s = u % KSTEPS (u = o - NPV).
+  // is K of k-step s = u / KB, key block kb = u % KB (u = o - NPV), so that
+  // the products accumulating into one S^T block are KB*QB slots apart.
   constexpr int NPV = PSTEPS * DB;
   constexpr int NOP = NPV + KB * KSTEPS;
   constexpr int NSLOT = QB * NOP;
@@ -229,28 +236,28 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     constexpr int o = decltype(o_tag)::value;
     if constexpr (o < NPV) {
       constexpr int ps = o / DB, db = o % DB;
-      constexpr uint32_t off = 2 * (VS * TILE + 16 * D * ps);
-      const i16x4 a0 = lds_tr(vaddr[0][db] + off);
-      const i16x4 a1 = lds_tr(vaddr[1][db] + off);
+      constexpr uint32_t off = 2 * (VS * TILE + 32 * D * ps);
+      const i16x4 a0 = lds_tr(vaddr[db] + off);
+      const i16x4 a1 = lds_tr(vaddr[db] + off + 2 * 16 * D);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
     } else {
-      constexpr int u = o - NPV, kb = u / KSTEPS, s = u % KSTEPS;
-      return lds_b128(kaddr[s] + 2 * (KS * TILE + kb * 32 * D));
+      constexpr int u = o - NPV, s = u / KB, kb = u % KB;
+      return lds_b128(kaddr[s] + 2 * (KS * TILE + kb * 16 * D));
     }
   };
   // S^T of one tile from K stage 0 (prologue only).
-  auto qk0 = [&](f32x16 (&sa)[QB][KB]) {
+  auto qk0 = [&](f32x4 (&sa)[QB][KB]) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sa[qb][kb][i] = 0.0f;
+        for (int i = 0; i < 4; ++i) sa[qb][kb][i] = 0.0f;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 a = lds_b128(kaddr[s] + 2 * kb * 32 * D);
+        const bf16x8 a = lds_b128(kaddr[s] + 2 * kb * 16 * D);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sa[qb][kb] = mfma32(a, qf[qb][s], sa[qb][kb]);
+        for (int qb = 0; qb < QB; ++qb) sa[qb][kb] = mfma16(a, qf[qb][s], sa[qb][kb]);
       }
     }
   };
@@ -260,12 +267,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     for (int ps = 0; ps < PSTEPS; ++ps)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint32_t off = 2 * (stage * TILE + 16 * D * ps);
-        const i16x4 a0 = lds_tr(vaddr[0][db] + off);
-        const i16x4 a1 = lds_tr(vaddr[1][db] + off);
+        const uint32_t off = 2 * (stage * TILE + 32 * D * ps);
+        const i16x4 a0 = lds_tr(vaddr[db] + off);
+        const i16x4 a1 = lds_tr(vaddr[db] + off + 2 * 16 * D);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(a, pf[qb][ps], oacc[qb][db]);
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma16(a, pf[qb][ps], oacc[qb][db]);
       }
   };
 
@@ -282,7 +289,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // other; it reads P(j-1) from set (j+1)%2 and writes P(j) into set j%2.
   // (Sets are always chosen by a compile-time index: a runtime index would
   // put them in scratch memory.)
-  f32x16 sbuf[2][QB][KB];
+  f32x4 sbuf[2][QB][KB];
   bf16x8 pbuf[2][QB][PSTEPS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -307,8 +314,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   auto step = [&](auto j6_tag, int j) {
     constexpr int J6 = decltype(j6_tag)::value;
     constexpr int SET = J6 & 1;
-    f32x16 (&sacc)[QB][KB] = sbuf[SET];
-    f32x16 (&snext)[QB][KB] = sbuf[1 - SET];
+    f32x4 (&sacc)[QB][KB] = sbuf[SET];
+    f32x4 (&snext)[QB][KB] = sbuf[1 - SET];
     const bf16x8 (&pprev)[QB][PSTEPS] = pbuf[1 - SET];
     bf16x8 (&pcur)[QB][PSTEPS] = pbuf[SET];
     using KS = IC<(J6 + 1) % KSTAGES>;   // K of tile j+1
@@ -318,18 +325,16 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if (j + 2 < ntiles) dma_k(j + 2, J6 % KSTAGES);
     if (j + 1 < ntiles) dma_v(j + 1, (J6 + 1) % VSTAGES);
     // Keep the operand bases opaque per step: otherwise the compiler hoists a
-    // base-plus-stage address per stage out of the loop (four times the
+    // base-plus-stage address per stage out of the loop (several times the
     // registers) instead of folding the stage into the read's immediate.
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]));
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vaddr[u][db]));
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vaddr[db]));
     const int64_t tile_plo = p.kv_pos0 + (int64_t)j * BN;
 
-    // Mask (diagonal or ragged tiles only): key 32*kb + 8*(i/4) + 4*half + i%4
-    // of the tile is visible to a row iff it is <= that row's limit.
+    // Mask (diagonal or ragged tiles only): key 16*kb + 4*grp + i of the tile
+    // is visible to a row iff it is <= that row's limit.
     const bool need_mask = (j * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
     if (need_mask) {
 #pragma unroll
@@ -339,12 +344,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
           const int64_t rel = qpos[qb] - tile_plo;
           lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
         }
-        const int t = lim - 4 * half;
+        const int t = lim - 4 * grp;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            sacc[qb][kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) > t) ? -INFINITY : sacc[qb][kb][i];
+          for (int i = 0; i < 4; ++i)
+            sacc[qb][kb][i] = (16 * kb + i > t) ? -INFINITY : sacc[qb][kb][i];
       }
     }
 
@@ -357,6 +362,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       mneg[qb] = (m_run[qb] == -INFINITY) ? 0.0f : -m_run[qb];
       tsum[qb] = 0.0f;
     }
+    // Pair (i, i+1) of key block kb goes to elements 4*(kb%2) + i, +1 of the
+    // P^T operand of k-step kb/2: the key order of the V^T reads.
     auto prob_pair = [&](int rq, int kb, int i, float mn, float &sum) {
       // The row sum uses the unrounded fp32 probabilities (summing the bf16
       // values instead costs up to 2^-8 relative error in short rows).
@@ -365,8 +372,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       sum += p0;
       sum += p1;
       const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-      pcur[rq][2 * kb + (i >> 3)][i & 7] = t2[0];
-      pcur[rq][2 * kb + (i >> 3)][(i & 7) + 1] = t2[1];
+      pcur[rq][kb >> 1][4 * (kb & 1) + i] = t2[0];
+      pcur[rq][kb >> 1][4 * (kb & 1) + i + 1] = t2[1];
     };
     static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_opnd(KS{}, VS{}, o); });
     static_for<NSLOT>([&](auto t_tag) {
@@ -377,26 +384,26 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       // matrix instruction of slot t
       if constexpr (o < NPV) {
         constexpr int ps = o / DB, db = o % DB;
-        oacc[qb][db] = mfma32(opnd[o % NBUF], pprev[qb][ps], oacc[qb][db]);
+        oacc[qb][db] = mfma16(opnd[o % NBUF], pprev[qb][ps], oacc[qb][db]);
       } else {
-        constexpr int u = o - NPV, kb = u / KSTEPS, s = u % KSTEPS;
+        constexpr int u = o - NPV, s = u / KB, kb = u % KB;
         if constexpr (s == 0) {
-          f32x16 z;
+          f32x4 z;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-          snext[qb][kb] = mfma32(opnd[o % NBUF], qf[qb][s], z);
+          for (int i = 0; i < 4; ++i) z[i] = 0.0f;
+          snext[qb][kb] = mfma16(opnd[o % NBUF], qf[qb][s], z);
         } else {
-          snext[qb][kb] = mfma32(opnd[o % NBUF], qf[qb][s], snext[qb][kb]);
+          snext[qb][kb] = mfma16(opnd[o % NBUF], qf[qb][s], snext[qb][kb]);
         }
       }
       // Vector work of slot t: pair u of the NPAIR pairs (row block
-      // u / (KB*8), key block (u / 8) % KB, elements 2(u%8), 2(u%8)+1) goes
+      // u / (KB*2), key block (u / 2) % KB, elements 2(u%2), 2(u%2)+1) goes
       // to slot u * NSLOT / NPAIR.
-      constexpr int NPAIR = QB * KB * 8;
+      constexpr int NPAIR = QB * KB * 2;
       static_for<NPAIR>([&](auto u_tag) {
         constexpr int u = decltype(u_tag)::value;
         if constexpr (u * NSLOT / NPAIR == t) {
-          constexpr int rq = u / (KB * 8), kb = (u / 8) % KB, i = 2 * (u % 8);
+          constexpr int rq = u / (KB * 2), kb = (u / 2) % KB, i = 2 * (u % 2);
           prob_pair(rq, kb, i, mneg[rq], tsum[rq]);
         }
       });
@@ -413,12 +420,13 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     }
 
     // The running max is only a reference point: the probabilities above are
-    // exact as long as none overflows. While every row's tile sum stays at
-    // most 2^16 (so every probability does), they are kept. Otherwise -- the
-    // first tile of a row (no reference yet), a score more than 16 (log2)
-    // above the reference, or a non-finite sum -- the row max is taken, O and
-    // the row sum are rescaled to it (after this step's PV(j-1) products, which
-    // used the old reference) and the tile's probabilities are recomputed.
+    // exact as long as none overflows. While every lane's partial tile sum
+    // stays at most 2^16 (so every probability does), they are kept.
+    // Otherwise -- the first tile of a row (no reference yet), a score more
+    // than 16 (log2) above the reference, or a non-finite sum -- the row max
+    // is taken, O and the row sum are rescaled to it (after this step's
+    // PV(j-1) products, which used the old reference) and the tile's
+    // probabilities are recomputed.
     bool redo = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) redo = redo || !(tsum[qb] <= kSumLimit) || m_run[qb] == -INFINITY;
@@ -429,14 +437,14 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) m = fmaxf(m, sacc[qb][kb][i]);
-        const float mr = pair_max(m) * c;
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[qb][kb][i]);
+        const float mr = quad_max(m) * c;
         const float m_new = fmaxf(m_run[qb], mr);
         const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+          for (int i = 0; i < 4; ++i) oacc[qb][db][i] *= alpha;
         l_part[qb] *= alpha;
         m_run[qb] = m_new;
         const float mn = (m_new == -INFINITY) ? 0.0f : -m_new;
@@ -444,7 +452,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; i += 2) prob_pair(qb, kb, i, mn, tsum[qb]);
+          for (int i = 0; i < 4; i += 2) prob_pair(qb, kb, i, mn, tsum[qb]);
       }
     }
 #pragma unroll
@@ -471,20 +479,18 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // ---- epilogue -------------------------------------------------------------
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l = pair_sum(l_part[qb]);
+    const float l = quad_sum(l_part[qb]);
     if (!qvalid[qb]) continue;
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + head * p.o_sh + (int64_t)local_row[qb] * p.o_ss;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
+      bf16x4 o4;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[qb][db][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g + 4 * half) = o4;
-      }
-    if (half == 0) {
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[qb][db][e] * inv);
+      *reinterpret_cast<bf16x4 *>(op + 16 * db + 4 * grp) = o4;
+    }
+    if (grp == 0) {
       const float lse = l > 0.0f ? (m_run[qb] + __log2f(l)) * kLn2 : -INFINITY;
       p.lse[((int64_t)b * p.hq + head) * p.sq + local_row[qb]] = lse;
     }

@@ -48,6 +48,26 @@ struct Tile {
   }
 };
 
+// Row-major LDS tile whose rows are read by transposes in groups of 8
+// consecutive rows x 16 columns (the 16x16x32 operand of a contraction down
+// the rows): the chunk swizzle 2*(row mod 8) (D = 128) or 2*((row/2) mod 4)
+// (64-element rows, two per bank line) puts the 8 rows' 2 chunks of any
+// 16-column block in 16 distinct bank groups.
+template <int W>
+struct TrTile {
+  static constexpr int NC = W / 8;
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (NC >= 16) {
+      return (2 * (row & 7)) & (NC - 1);
+    } else {
+      return (2 * ((row >> 1) & 3)) & (NC - 1);
+    }
+  }
+  __device__ static __forceinline__ int elem_off(int row, int col) {
+    return row * W + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
+  }
+};
+
 // Two transpose reads (ds_read_b64_tr_b16) forming one 8 x bf16 MFMA operand
 // whose contraction index runs down `rows` of a row-major tile: lane l of the
 // wavefront gets column (col0 + 16*((l>>4)&1) + (l&15)) at the 8 rows
@@ -117,6 +137,23 @@ __device__ __forceinline__ void to_bf16_operands(const float (&v)[16], bf16x8 (&
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D (16x16) += A (16x32) B (32x16). Lane l holds A row l%16 and B column l%16
+// at contraction slots 8*(l/16) .. +7, and D column l%16, rows 4*(l/16) .. +3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Sum and max over the four lanes that hold the same accumulator column
+// (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
 }
 
 template <int N>
