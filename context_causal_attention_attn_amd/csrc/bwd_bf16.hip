@@ -560,28 +560,31 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 // ---------------------------------------------------------------------------
 // One workgroup = 8 wavefronts = one work item (a tile of query rows of one
 // chunk for a pack of query heads of one GQA group); each wavefront owns 32
-// query rows of one head. K/V tiles of 64 keys are loaded straight from
-// global memory into 4-stage LDS rings and read by every head. With the
-// query in the lane, S^T = K Q^T and dP^T = V dO^T give P^T = exp2(S^T *
-// scale*log2(e) - LSE*log2(e)) and dS^T = P^T o (dP^T - Delta) from per-lane
-// scalars, and dS^T feeds dQ^T += K^T dS^T straight from registers (K^T by
-// transpose reads). Software pipeline over 32-key blocks: in block b the
-// matrix core computes dQ^T of block b-1 and S^T, dP^T of block b+1 while
-// the vector ALU forms dS^T of block b; one barrier per 64-key tile.
+// query rows of one head, as two 16-row blocks. K/V tiles of 64 keys are
+// loaded straight from global memory into 4-stage LDS rings and read by every
+// head. With the query in the lane (v_mfma_f32_16x16x32_bf16), S^T = K Q^T
+// and dP^T = V dO^T give P^T = exp2(S^T * scale*log2(e) - LSE*log2(e)) and
+// dS^T = P^T o (dP^T - Delta) from per-lane scalars, and dS^T feeds
+// dQ^T += K^T dS^T straight from registers (K^T by transpose reads; every K,
+// V or K^T fragment read from LDS feeds both row blocks). Software pipeline
+// over 32-key blocks: in block b the matrix core computes dQ^T of block b-1
+// and S^T, dP^T of block b+1 while the vector ALU forms dS^T of block b; one
+// barrier per 64-key tile.
 template <int D, int RB>
 __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int HPW = kDqWaves / RB;
   constexpr int BM = kDqWaveRows * RB;
   constexpr int NC = D / 8;
-  constexpr int KSTEPS = D / 16;
-  constexpr int DB = D / 32;
+  constexpr int QB = kDqWaveRows / 16;         // 16-row query blocks per wavefront
+  constexpr int KSTEPS = D / 32;               // k-steps of S^T, dP^T (over D)
+  constexpr int DB = D / 16;                   // 16-row blocks of dQ^T
   constexpr int TILE = BN * D;                 // elements of a K or V tile (64 keys)
   constexpr int STG = 4;                       // ring stages (K and V)
   constexpr int K_OFF = 0;
   constexpr int V_OFF = STG * TILE * 2;
   constexpr int LDS_BYTES = 2 * STG * TILE * 2;
-  static_assert(BN == 64 && LDS_BYTES <= 160 * 1024, "tile shape");
-  using T = Tile<D>;
+  static_assert(BN == 64 && QB == 2 && LDS_BYTES <= 160 * 1024, "tile shape");
+  using T = Tile16<D>;
 
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
@@ -589,8 +592,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  const int grp = lane >> 4;   // operand k-slice / accumulator row quarter
+  const int col = lane & 15;   // operand row / accumulator column
 
   const int bid = blockIdx.x;
   const int pack = bid % p.n_head_packs;
@@ -611,9 +614,17 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   const int wrow0 = (wave % RB) * kDqWaveRows;
   const int wrows = max(0, min(kDqWaveRows, item_rows - wrow0));
   const int64_t wave_qlo = chunk_pos + item_row0 + wrow0;
-  const bool qvalid = col < wrows;
-  const int64_t qpos = wave_qlo + min(col, max(wrows - 1, 0));
-  const int local_row = chunk * p.chunk_len + item_row0 + wrow0 + col;
+  // This lane's query in each 16-row block.
+  bool qvalid[QB];
+  int64_t qpos[QB];
+  int local_row[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = 16 * qb + col;
+    qvalid[qb] = r < wrows;
+    qpos[qb] = wave_qlo + min(r, max(wrows - 1, 0));
+    local_row[qb] = chunk * p.chunk_len + item_row0 + wrow0 + r;
+  }
 
   int nvis = p.skv;
   if (p.causal) {
@@ -621,30 +632,32 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     nvis = (int)(n < 0 ? 0 : (n > p.skv ? p.skv : n));
   }
   const int ntiles = (nvis + BN - 1) / BN;
-  const int nblocks = 2 * ntiles;   // 32-key blocks
 
-  // Q and dO rows of this lane's query: B operands of S^T and dP^T. Lanes past
-  // the item's last row read its first row and get LSE = +inf (P = 0).
-  bf16x8 qf[KSTEPS], gf[KSTEPS];
-  float lse2 = INFINITY, delta = 0.0f;
-  {
-    const int load_row = qvalid ? local_row : chunk * p.chunk_len + item_row0;
+  // Q and dO rows of this lane's queries: B operands of S^T and dP^T. Lanes
+  // past the item's last row read its first row and get LSE = +inf (P = 0).
+  bf16x8 qf[QB][KSTEPS], gf[QB][KSTEPS];
+  float lse2[QB], delta[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int load_row = qvalid[qb] ? local_row[qb] : chunk * p.chunk_len + item_row0;
     const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh +
-                       (int64_t)load_row * p.q_ss + 8 * half;
+                       (int64_t)load_row * p.q_ss + 8 * grp;
     const __bf16 *gp = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh +
-                       (int64_t)load_row * p.o_ss + 8 * half;
+                       (int64_t)load_row * p.o_ss + 8 * grp;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
-      gf[s] = *reinterpret_cast<const bf16x8 *>(gp + 16 * s);
+      qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+      gf[qb][s] = *reinterpret_cast<const bf16x8 *>(gp + 32 * s);
     }
-    if (qvalid) {
-      const int64_t row = ((int64_t)b * p.hq + head) * p.sq + local_row;
-      lse2 = p.lse2[row];
-      delta = p.delta[row];
+    lse2[qb] = INFINITY;
+    delta[qb] = 0.0f;
+    if (qvalid[qb]) {
+      const int64_t row = ((int64_t)b * p.hq + head) * p.sq + local_row[qb];
+      lse2[qb] = p.lse2[row];
+      delta[qb] = p.delta[row];
     }
-    wait_vmem_all();
   }
+  wait_vmem_all();
 
   // ---- staging: global -> LDS directly (see the forward kernel) -------------
   constexpr int RPI = 64 / NC;
@@ -687,49 +700,45 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   };
 
   // ---- per-lane LDS addressing ----------------------------------------------
-  // Row reads of K and V (A operands of S^T and dP^T: key col of the block,
-  // chunk 2s+half) and transpose reads of K (A operand of dQ^T = K^T dS^T);
-  // stage, key block and k-step are immediates.
+  // Row reads of K and V (A operands of S^T and dP^T: key row col of a 16-key
+  // block, chunk 4s+grp) and transpose reads of K (A operand of
+  // dQ^T = K^T dS^T: keys 4grp .. 4grp+3 and 16 + 4grp .. of a 32-key block,
+  // column 16db + col); stage, key block and k-step are immediates.
   // (Separate K and V bases: the V ring starts 64 KiB in, beyond the reach
   // of an immediate.)
   uint32_t kaddr[KSTEPS], vaddr[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
-    kaddr[s] = lds0 + K_OFF + 2 * T::chunk_off(col, 2 * s + half);
-    vaddr[s] = lds0 + V_OFF + 2 * T::chunk_off(col, 2 * s + half);
+    kaddr[s] = lds0 + K_OFF + 2 * T::chunk_off(col, 4 * s + grp);
+    vaddr[s] = lds0 + V_OFF + 2 * T::chunk_off(col, 4 * s + grp);
   }
-  uint32_t taddr[2][DB];
+  uint32_t taddr[DB];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      taddr[u][db] = lds0 + 2 * T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
-                                            32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  for (int db = 0; db < DB; ++db) taddr[db] = lds0 + 2 * T::elem_off(4 * grp + (col >> 2), 16 * db + 4 * (lane & 3));
   auto lds_b128 = [](uint32_t addr) -> bf16x8 {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
   };
   auto lds_tr = [&](int db, uint32_t off) -> bf16x8 {
-    const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[0][db] + off));
-    const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[1][db] + off));
+    const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[db] + off));
+    const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[db] + off + 2 * 16 * D));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  f32x16 qacc[DB];
+  f32x4 qacc[QB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) qacc[db][i] = 0.0f;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qacc[qb][db][i] = 0.0f;
   const float c2 = p.scale_log2;
 
-  // Block bb (key block kb = bb % 2 of tile bb / 2, ring stage (bb / 2) % 4)
-  // operand reads at compile-time offsets: K or V rows (k-step s), K^T
-  // (k-step k2 over the block's keys, O^T block db).
-  auto kv_row = [&](bool v, int st, int kb, int s) {
-    return lds_b128((v ? vaddr[s] : kaddr[s]) + 2 * (st * TILE + kb * 32 * D));
+  // Operand reads at compile-time offsets: K or V rows of 16-key block h of
+  // 32-key block kb (k-step s), K^T of 32-key block kb (O^T block db).
+  auto kv_row = [&](bool v, int st, int kb, int h, int s) {
+    return lds_b128((v ? vaddr[s] : kaddr[s]) + 2 * (st * TILE + (32 * kb + 16 * h) * D));
   };
-  auto k_tr = [&](int st, int kb, int k2, int db) {
-    return lds_tr(db, K_OFF + 2 * (st * TILE + (32 * kb + 16 * k2) * D));
-  };
+  auto k_tr = [&](int st, int kb, int db) { return lds_tr(db, K_OFF + 2 * (st * TILE + 32 * kb * D)); };
 
   // ---- prologue ---------------------------------------------------------------
   // K stage 3 stands for "tile -1" in block 0 (its dS is zero): clear it.
@@ -737,38 +746,51 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     u32x4 *k3 = reinterpret_cast<u32x4 *>(smem + K_OFF + 2 * 3 * TILE);
     for (int i = tid; i < TILE / 8; i += NT) k3[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  // S^T, dP^T of a block alternate between two register sets by block parity.
-  f32x16 sbuf[2], pbuf[2];
-  bf16x8 dsbuf[2][2];   // dS^T of the last two blocks (bf16 B operands)
+  // S^T, dP^T of a block ([16-key half][row block]) alternate between two
+  // register sets by block parity.
+  f32x4 sbuf[2][2][QB], pbuf[2][2][QB];
+  bf16x8 dsbuf[2][QB];   // dS^T of the last two blocks (bf16 B operands)
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dsbuf[q][k2][e] = (__bf16)0.0f;
+      for (int e = 0; e < 8; ++e) dsbuf[q][qb][e] = (__bf16)0.0f;
   if (ntiles > 0) dma(0, 0);
   if (ntiles > 1) dma(1, 1);
   wait_vmem_all();
   __syncthreads();
   if (ntiles > 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sbuf[0][i] = 0.0f;
-      pbuf[0][i] = 0.0f;
-    }
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      sbuf[0] = mfma32(kv_row(false, 0, 0, s), qf[s], sbuf[0]);
-      pbuf[0] = mfma32(kv_row(true, 0, 0, s), gf[s], pbuf[0]);
-    }
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sbuf[0][h][qb][i] = 0.0f;
+          pbuf[0][h][qb][i] = 0.0f;
+        }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 ka = kv_row(false, 0, 0, h, s), va = kv_row(true, 0, 0, h, s);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          sbuf[0][h][qb] = mfma16(ka, qf[qb][s], sbuf[0][h][qb]);
+          pbuf[0][h][qb] = mfma16(va, gf[qb][s], pbuf[0][h][qb]);
+        }
+      }
   }
 
   constexpr int AHEAD = 2;
   constexpr int NBUF = AHEAD + 1;
-  constexpr int NDQ = 2 * DB;            // dQ^T products of a block (k2, db)
-  constexpr int NSLOT = NDQ + 2 * KSTEPS;
+  constexpr int NDQ = DB;                // K^T operands of a block (db)
+  constexpr int NOP = NDQ + 4 * KSTEPS;  // + K and V rows of both 16-key halves
+  constexpr int NSLOT = QB * NOP;
+  constexpr int NPAIR = 2 * QB * 2;      // pairs of dS^T values per lane per block
 
-  // One block bb = 2*J + KB (tile J, key block KB; J4 = J % 4): dQ^T(bb-1)
+  // One block bb = 2*J + KB (tile J, 32-key block KB; J4 = J % 4): dQ^T(bb-1)
   // and S^T, dP^T(bb+1) on the matrix core, dS^T(bb) on the VALU.
   auto block = [&](auto j4_tag, auto kb_tag, int bb) {
     constexpr int J4 = decltype(j4_tag)::value, KB = decltype(kb_tag)::value;
@@ -777,75 +799,89 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     constexpr int KB_PREV = 1 - KB;
     constexpr int ST_NEXT = KB == 0 ? J4 : (J4 + 1) % STG;   // stage of block bb+1
     constexpr int KB_NEXT = 1 - KB;
-    f32x16 &scur = sbuf[SET], &pcur = pbuf[SET];
-    f32x16 &snext = sbuf[1 - SET], &pnext = pbuf[1 - SET];
-    const bf16x8 (&dsprev)[2] = dsbuf[1 - SET];
-    bf16x8 (&dscur)[2] = dsbuf[SET];
-    // Mask of block bb (diagonal or ragged blocks only): key 8*(i/4) +
-    // 4*half + i%4 of the block is visible iff it is <= lim; masked scores
-    // become -inf (P = 0).
+    f32x4 (&scur)[2][QB] = sbuf[SET];
+    f32x4 (&pcur)[2][QB] = pbuf[SET];
+    f32x4 (&snext)[2][QB] = sbuf[1 - SET];
+    f32x4 (&pnext)[2][QB] = pbuf[1 - SET];
+    const bf16x8 (&dsprev)[QB] = dsbuf[1 - SET];
+    bf16x8 (&dscur)[QB] = dsbuf[SET];
+    // Mask of block bb (diagonal or ragged blocks only): key 16*h + 4*grp + i
+    // of the block is visible iff it is <= lim; masked scores become -inf
+    // (P = 0).
     const int64_t blk_plo = p.kv_pos0 + (int64_t)bb * 32;
     const bool need_mask = (bb * 32 + 32 > p.skv) || (p.causal && blk_plo + 31 > wave_qlo);
     if (need_mask) {
-      int lim = p.skv - 1 - bb * 32;
-      if (p.causal) {
-        const int64_t rel = qpos - blk_plo;
-        lim = min(lim, (int)(rel < -1 ? -1 : (rel > 32 ? 32 : rel)));
-      }
-      const int t = lim - 4 * half;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) scur[i] = (8 * (i >> 2) + (i & 3) > t) ? -INFINITY : scur[i];
+      for (int qb = 0; qb < QB; ++qb) {
+        int lim = p.skv - 1 - bb * 32;
+        if (p.causal) {
+          const int64_t rel = qpos[qb] - blk_plo;
+          lim = min(lim, (int)(rel < -1 ? -1 : (rel > 32 ? 32 : rel)));
+        }
+        const int t = lim - 4 * grp;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) scur[h][qb][i] = (16 * h + i > t) ? -INFINITY : scur[h][qb][i];
+      }
     }
-    // Operand o: o < NDQ is K^T of block bb-1 (k2 = o / DB, db = o % DB);
-    // then K (even) and V (odd) rows of block bb+1 for k-step (o - NDQ) / 2.
+    // Operand o (used by both row blocks in consecutive slots): o < NDQ is
+    // K^T of block bb-1 (db = o); then, for u = o - NDQ, k-step s = u / 4 of
+    // the K (u even) or V (u odd) rows of 16-key half h = (u / 2) % 2 of
+    // block bb+1, so that products accumulating into one S^T or dP^T block
+    // are eight slots apart.
     auto read = [&](auto o_tag) -> bf16x8 {
       constexpr int o = decltype(o_tag)::value;
       if constexpr (o < NDQ) {
-        return k_tr(ST_PREV, KB_PREV, o / DB, o % DB);
+        return k_tr(ST_PREV, KB_PREV, o);
       } else {
         constexpr int u = o - NDQ;
-        return kv_row(u & 1, ST_NEXT, KB_NEXT, u >> 1);
+        return kv_row(u & 1, ST_NEXT, KB_NEXT, (u >> 1) & 1, u >> 2);
       }
     };
     bf16x8 opnd[NBUF];
     static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read(o); });
     static_for<NSLOT>([&](auto t_tag) {
-      constexpr int o = decltype(t_tag)::value;
-      if constexpr (o + AHEAD < NSLOT) opnd[(o + AHEAD) % NBUF] = read(IC<o + AHEAD>{});
+      constexpr int t = decltype(t_tag)::value;
+      constexpr int o = t / QB, qb = t % QB;
+      if constexpr (qb == 0 && o + AHEAD < NOP) opnd[(o + AHEAD) % NBUF] = read(IC<o + AHEAD>{});
       if constexpr (o < NDQ) {
-        constexpr int k2 = o / DB, db = o % DB;
-        qacc[db] = mfma32(opnd[o % NBUF], dsprev[k2], qacc[db]);
+        qacc[qb][o] = mfma16(opnd[o % NBUF], dsprev[qb], qacc[qb][o]);
       } else {
-        constexpr int u = o - NDQ, s = u >> 1;
-        f32x16 &dst = (u & 1) ? pnext : snext;
-        const bf16x8 &bop = (u & 1) ? gf[s] : qf[s];
+        constexpr int u = o - NDQ, s = u >> 2, h = (u >> 1) & 1;
+        f32x4 &dst = (u & 1) ? pnext[h][qb] : snext[h][qb];
+        const bf16x8 &bop = (u & 1) ? gf[qb][s] : qf[qb][s];
         if constexpr (s == 0) {
-          f32x16 z;
+          f32x4 z;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-          dst = mfma32(opnd[o % NBUF], bop, z);
+          for (int i = 0; i < 4; ++i) z[i] = 0.0f;
+          dst = mfma16(opnd[o % NBUF], bop, z);
         } else {
-          dst = mfma32(opnd[o % NBUF], bop, dst);
+          dst = mfma16(opnd[o % NBUF], bop, dst);
         }
       }
-      // dS^T pair e (elements 2e, 2e+1 of block bb) in slot e * NSLOT / 8.
-      static_for<8>([&](auto e_tag) {
-        constexpr int e = decltype(e_tag)::value, i = 2 * e;
-        if constexpr (e * NSLOT / 8 == o) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[i], c2, -lse2));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[i + 1], c2, -lse2));
-          const float x0 = p0 * (pcur[i] - delta);
-          const float x1 = p1 * (pcur[i + 1] - delta);
+      // dS^T pair e (row block e / 4, half (e / 2) % 2, elements 2(e%2),
+      // 2(e%2)+1) in slot e * NSLOT / NPAIR; it lands in elements 4h + i of
+      // the row block's B operand (the key order of the K^T reads).
+      static_for<NPAIR>([&](auto e_tag) {
+        constexpr int e = decltype(e_tag)::value;
+        if constexpr (e * NSLOT / NPAIR == t) {
+          constexpr int rq = e / 4, h = (e / 2) % 2, i = 2 * (e % 2);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[h][rq][i], c2, -lse2[rq]));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[h][rq][i + 1], c2, -lse2[rq]));
+          const float x0 = p0 * (pcur[h][rq][i] - delta[rq]);
+          const float x1 = p1 * (pcur[h][rq][i + 1] - delta[rq]);
           const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
-          dscur[i >> 3][i & 7] = t2[0];
-          dscur[i >> 3][(i & 7) + 1] = t2[1];
+          dscur[rq][4 * h + i] = t2[0];
+          dscur[rq][4 * h + i + 1] = t2[1];
         }
       });
       __builtin_amdgcn_sched_barrier(0);
     });
     // Pin dS^T(bb) to the slots above (otherwise the compiler sinks it past
     // the next block's mask branch, away from the products it overlaps).
-    asm volatile("" ::"v"(dscur[0]), "v"(dscur[1]));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" ::"v"(dscur[qb]));
   };
 
   // Tile step J (J4 = J % 4): tile J+2 on its way into the rings (into the
@@ -853,6 +889,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   auto tile_step = [&](auto j4_tag, int J) {
     constexpr int J4 = decltype(j4_tag)::value;
     if (J + 2 < ntiles) dma(J + 2, (J4 + 2) % STG);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(taddr[db]));
     block(j4_tag, IC<0>{}, 2 * J);
     block(j4_tag, IC<1>{}, 2 * J + 1);
     wait_vmem_all();
@@ -864,27 +902,29 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     if (J + 2 < ntiles) tile_step(IC<2>{}, J + 2);
     if (J + 3 < ntiles) tile_step(IC<3>{}, J + 3);
   }
-  // dQ^T of the last block (tile ntiles-1, key block 1; dS^T in set 1).
+  // dQ^T of the last block (tile ntiles-1, 32-key block 1; dS^T in set 1).
   if (ntiles > 0) {
     const int st = (ntiles - 1) % STG;
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 a = k_tr(st, 1, db);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        qacc[db] = mfma32(k_tr(st, 1, k2, db), dsbuf[1][k2], qacc[db]);
+      for (int qb = 0; qb < QB; ++qb) qacc[qb][db] = mfma16(a, dsbuf[1][qb], qacc[qb][db]);
+    }
   }
 
-  if (!qvalid) return;
-  __bf16 *dst = static_cast<__bf16 *>(p.dq) + b * p.o_sb + head * p.o_sh + (int64_t)local_row * p.o_ss;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    if (!qvalid[qb]) continue;
+    __bf16 *dst = static_cast<__bf16 *>(p.dq) + b * p.o_sb + head * p.o_sh + (int64_t)local_row[qb] * p.o_ss;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
+    for (int db = 0; db < DB; ++db) {
       bf16x4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(qacc[db][4 * gq + e] * p.scale);
-      *reinterpret_cast<bf16x4 *>(dst + 32 * db + 8 * gq + 4 * half) = o4;
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(qacc[qb][db][e] * p.scale);
+      *reinterpret_cast<bf16x4 *>(dst + 16 * db + 4 * grp) = o4;
     }
+  }
 }
 
 template <int D>

@@ -23,8 +23,8 @@
 //    of O^T += V^T P^T without any shuffle: the contraction index (keys) is
 //    permuted identically in both operands, and V^T is read from the
 //    row-major V tile with the gfx950 LDS transpose read ds_read_b64_tr_b16
-//    (V tiles use their own row swizzle, which keeps those reads free of
-//    bank conflicts);
+//    (the tiles' row swizzle keeps both the row reads of K and the
+//    transpose reads of V free of bank conflicts);
 //  * three-way software pipeline: in step j the matrix core computes
 //    O^T += V^T P^T of tile j-1 and S^T of tile j+1 while the vector ALU turns
 //    the scores of tile j into probabilities. The three are independent; the
@@ -67,8 +67,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr int PSTEPS = BN / 32;      // k-steps of O^T (contraction over keys)
   constexpr int TILE = BN * D;
   static_assert(BN == 64 && QB == 2, "tile shape");
-  using T = Tile<D>;     // K tiles (row reads)
-  using TV = TrTile<D>;  // V tiles (transpose reads)
+  using T = Tile16<D>;   // K tiles (row reads) and V tiles (transpose reads)
 
   // K ring (2 stages) followed by the V ring (3 stages), in one LDS array:
   // 80 KiB at D = 128.
@@ -141,12 +140,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   for (int s = 0; s < KSTEPS; ++s) kaddr[s] = lds0 + 2 * T::chunk_off(col, 4 * s + grp);
   // V^T transpose reads: lane group grp takes keys 4grp .. 4grp+3 and
   // 16 + 4grp .. of a 32-key k-step, column 16db + col; its 16 lanes address
-  // 4 rows x 16 columns. The V swizzle repeats every 8 rows, so the second
+  // 4 rows x 16 columns. The swizzle repeats every 16 rows, so the second
   // read (16 rows on) and k-step ps (32 rows on) only add constants.
   uint32_t vaddr[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-    vaddr[db] = lds0 + 2 * (KSTAGES * TILE + TV::elem_off(4 * grp + (col >> 2), 16 * db + 4 * (lane & 3)));
+    vaddr[db] = lds0 + 2 * (KSTAGES * TILE + T::elem_off(4 * grp + (col >> 2), 16 * db + 4 * (lane & 3)));
   auto lds_b128 = [](uint32_t addr) -> bf16x8 {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
   };
@@ -160,7 +159,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // rows; each lane fetches the global chunk that the row's swizzle puts at its
   // position (a permutation within the row: still one contiguous row read).
   // Wavefront w's instruction i covers rows (i*NW + w)*RPI ...; the row
-  // modulo 16 (which fixes both swizzles) does not depend on i. The loads are
+  // modulo 16 (which fixes the swizzle) does not depend on i. The loads are
   // issued from inline assembly so that the compiler does not make every LDS
   // read wait for them; each step waits for its own loads (vmcnt(0)) right
   // before the barrier that publishes the tile.
@@ -170,12 +169,10 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
   const int srow = wave * RPI + lane / NC;           // tile row of instruction 0
-  const int scol_k = 8 * ((lane % NC) ^ T::swz(srow));   // logical column of this lane's chunk
-  const int scol_v = 8 * ((lane % NC) ^ TV::swz(srow));
+  const int scol = 8 * ((lane % NC) ^ T::swz(srow));   // logical column of this lane's chunk
   const int64_t tile_stride = (int64_t)BN * p.kv_ss;
   const int64_t istep_bytes = (int64_t)NW * RPI * p.kv_ss * 2;
-  const uint32_t goff_k = (uint32_t)(((int64_t)srow * p.kv_ss + scol_k) * 2);
-  const uint32_t goff_v = (uint32_t)(((int64_t)srow * p.kv_ss + scol_v) * 2);
+  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
   const uint32_t dst0 = lds0 + 2 * wave * RPI * D;   // this wave's rows in K stage 0
   // M0 is saved and restored around the load: the compiler owns it.
   auto dma1 = [](uint32_t m0, uint32_t voff, const void *sbase) {
@@ -190,12 +187,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if (kt * BN + BN <= p.skv) {
       const char *t_base = reinterpret_cast<const char *>(base + (int64_t)kt * tile_stride);
 #pragma unroll
-      for (int i = 0; i < INSTS; ++i) dma1(dst + 2 * i * NW * RPI * D, is_v ? goff_v : goff_k, t_base + i * istep_bytes);
+      for (int i = 0; i < INSTS; ++i) dma1(dst + 2 * i * NW * RPI * D, goff0, t_base + i * istep_bytes);
     } else {
       // Ragged last tile: rows past the end read the last row (always masked).
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) {
-        const int64_t o = (int64_t)min(kt * BN + srow + i * NW * RPI, p.skv - 1) * p.kv_ss + (is_v ? scol_v : scol_k);
+        const int64_t o = (int64_t)min(kt * BN + srow + i * NW * RPI, p.skv - 1) * p.kv_ss + scol;
         dma1(dst + 2 * i * NW * RPI * D, (uint32_t)(o * 2), base);
       }
     }

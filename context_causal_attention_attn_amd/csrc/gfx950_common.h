@@ -48,23 +48,29 @@ struct Tile {
   }
 };
 
-// Row-major LDS tile whose rows are read by transposes in groups of 8
-// consecutive rows x 16 columns (the 16x16x32 operand of a contraction down
-// the rows): the chunk swizzle 2*(row mod 8) (D = 128) or 2*((row/2) mod 4)
-// (64-element rows, two per bank line) puts the 8 rows' 2 chunks of any
-// 16-column block in 16 distinct bank groups.
+// Row-major LDS tile for the 16x16x32 kernels, read both ways: as rows (16
+// consecutive rows, one 16-byte chunk each: an A/B operand) and by
+// transposes (8 consecutive rows x 16 columns: a contraction down the rows).
+// The chunk swizzle 2*(row mod 8) + (row/8 mod 2) -- 2*((row/2) mod 4) +
+// (row/8 mod 2) for 64-element rows, two per bank line -- is a permutation
+// over any 16 aligned rows and gives the 8 rows' 2 chunks of any 16-column
+// block 16 distinct bank groups, so neither read has bank conflicts. It
+// repeats every 16 rows.
 template <int W>
-struct TrTile {
+struct Tile16 {
   static constexpr int NC = W / 8;
   __device__ static __forceinline__ int swz(int row) {
     if constexpr (NC >= 16) {
-      return (2 * (row & 7)) & (NC - 1);
+      return (2 * (row & 7) + ((row >> 3) & 1)) & (NC - 1);
     } else {
-      return (2 * ((row >> 1) & 3)) & (NC - 1);
+      return (2 * ((row >> 1) & 3) + ((row >> 3) & 1)) & (NC - 1);
     }
   }
+  __device__ static __forceinline__ int chunk_off(int row, int c) {
+    return row * W + ((c ^ swz(row)) << 3);
+  }
   __device__ static __forceinline__ int elem_off(int row, int col) {
-    return row * W + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
+    return chunk_off(row, col >> 3) + (col & 7);
   }
 };
 
