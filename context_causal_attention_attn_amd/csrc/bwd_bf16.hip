@@ -76,7 +76,8 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 // 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------
 // One workgroup of 8 wavefronts per 128-key tile of one KV head; wavefronts
-// w and w+4 (which share a SIMD) own the same 32 keys, in two roles:
+// w and w+4 (which share a SIMD) own the same 32 keys (two 16-key blocks, the
+// columns of v_mfma_f32_16x16x32_bf16 products), in two roles:
 //  * P wavefronts (0..3) keep their keys' K rows and dV^T accumulators in
 //    registers; for the 64-row query tile of step t they compute
 //    P(t) = exp2(S(t) * scale*log2(e) - LSE*log2(e)) (masked), hand it to
@@ -85,11 +86,12 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 //  * dS wavefronts (4..7) keep V rows and dK^T accumulators; in step t they
 //    add dK^T += Q(t-2)^T dS(t-2), compute dP(t) = dO(t) V^T and, under it,
 //    dS(t-1) = P(t-1) o (dP(t-1) - Delta) with P(t-1) from LDS.
-// Each role issues 32 matrix instructions per step: the P role's vector work
-// runs under its first 16, the dS role's under its last 16, so the two
-// wavefronts of a SIMD take turns with the vector ALU. Every step is written
-// as slots of one matrix instruction, one operand read a few slots ahead and
-// a share of the vector work, with scheduling fences between slots. Query
+// Each role issues 64 matrix instructions per step: the P role's vector work
+// runs under its first 32, the dS role's under its last 32, so the two
+// wavefronts of a SIMD take turns with the vector ALU. Every Q, dO, Q^T or
+// dO^T fragment read from LDS feeds both key blocks. Every step is written
+// as slots of one matrix instruction, one operand read a few operands ahead
+// and a share of the vector work, with scheduling fences between slots. Query
 // tiles (Q, dO and the rows' LSE*log2(e) and Delta) are loaded straight from
 // global memory into LDS rings; query tiles wholly before the keys are never
 // visited; one barrier per step. Only the P wavefronts issue the loads.
@@ -100,25 +102,27 @@ template <int D>
 __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdParams p) {
   constexpr int NW = kDkdvWaves;
   constexpr int NC = D / 8;
-  constexpr int KSTEPS = D / 16;
-  constexpr int DB = D / 32;
+  constexpr int KSTEPS = D / 32;              // k-steps of S, dP (over D)
+  constexpr int DB = D / 16;                  // 16-row blocks of dV^T, dK^T
+  constexpr int KN = 2;                       // 16-key blocks per wavefront
   constexpr int QT = BQ;                      // query rows per step (64)
-  constexpr int QB = QT / 32;                 // 32-row blocks per step
-  constexpr int QSTEPS = QT / 16;             // k-steps over rows (dV, dK)
+  constexpr int RB = QT / 16;                 // 16-row blocks per step
+  constexpr int QSTEPS = QT / 32;             // k-steps over rows (dV, dK)
   constexpr int QTILE = QT * D;               // elements of a Q or dO tile
   constexpr int QSTG = 5;                     // Q ring (with LSE2, Delta): tiles t-2 .. t+2
   constexpr int OSTG = 2;                     // dO ring: tiles t, t+1
-  constexpr int XPER = QB * 16;               // P values per lane per step
+  constexpr int NXOP = KN * QSTEPS;           // P operands per lane per step
+  constexpr int XPER = NXOP * 8;              // P values per lane per step
   // LDS layout (bytes)
   constexpr int Q_OFF = 0;
   constexpr int O_OFF = Q_OFF + QSTG * QTILE * 2;
-  constexpr int X_OFF = O_OFF + OSTG * QTILE * 2;                    // [2][4 waves][QSTEPS][64 lanes] bf16x8
+  constexpr int X_OFF = O_OFF + OSTG * QTILE * 2;                    // [2][4 waves][NXOP][64 lanes] bf16x8
   constexpr int L_OFF = X_OFF + 2 * 4 * 64 * XPER * 2;               // [QSTG][QT] LSE*log2(e)
   constexpr int DL_OFF = L_OFF + QSTG * QT * 4;                      // [QSTG][QT] Delta
   constexpr int LDS_BYTES = DL_OFF + QSTG * QT * 4;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(QT == 64 && XPER == 32, "step shape");
-  using T = Tile<D>;
+  using T = Tile16<D>;
 
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
@@ -128,8 +132,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool prole = wave < 4;             // P role (else dS role)
   const int kw = wave & 3;                 // which 32 keys of the tile
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  const int grp = lane >> 4;               // operand k-slice / accumulator row quarter
+  const int col = lane & 15;               // operand row / accumulator column (key)
 
   const int groups = p.batch * p.hkv;
   const int g = blockIdx.x % groups;
@@ -138,8 +142,14 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   const int hk = g % p.hkv;
   const int key0 = kt * BK;
   const int wkey0 = key0 + 32 * kw;
-  const int my_key = wkey0 + col;
-  const bool key_ok = my_key < p.skv;
+  // This lane's key in each 16-key block of the wavefront's 32.
+  int my_key[KN];
+  bool key_ok[KN];
+#pragma unroll
+  for (int kn = 0; kn < KN; ++kn) {
+    my_key[kn] = wkey0 + 16 * kn + col;
+    key_ok[kn] = my_key[kn] < p.skv;
+  }
   const bool wave_keys_ok = wkey0 + 31 < p.skv;
   const int64_t kv_lo = p.kv_pos0 + key0;
 
@@ -249,58 +259,65 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   };
 
   // ---- per-lane LDS addressing ----------------------------------------------
-  // Row reads (A operands of S = Q K^T and dP = dO V^T): row col of the
-  // block, chunk 2s+half; transpose reads (A operands of dV^T = dO^T P and
-  // dK^T = Q^T dS): as in the forward's V^T.
+  // Row reads (A operands of S = Q K^T and dP = dO V^T): row col of a 16-row
+  // block, chunk 4s+grp; transpose reads (A operands of dV^T = dO^T P and
+  // dK^T = Q^T dS): rows 4grp .. 4grp+3 and 16 + 4grp .. of a 32-row k-step,
+  // column 16db + col, as in the forward's V^T. Row blocks, k-steps and the
+  // second transpose read only add constants (the swizzle repeats every 16
+  // rows).
   const uint32_t rbase = lds0 + (prole ? Q_OFF : O_OFF);
   const uint32_t tbase = lds0 + (prole ? O_OFF : Q_OFF);
   uint32_t raddr[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) raddr[s] = rbase + 2 * T::chunk_off(col, 2 * s + half);
-  uint32_t taddr[2][DB];
+  for (int s = 0; s < KSTEPS; ++s) raddr[s] = rbase + 2 * T::chunk_off(col, 4 * s + grp);
+  uint32_t taddr[DB];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      taddr[u][db] = tbase + 2 * T::elem_off(8 * u + 4 * half + ((lane & 15) >> 2),
-                                             32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  for (int db = 0; db < DB; ++db) taddr[db] = tbase + 2 * T::elem_off(4 * grp + (col >> 2), 16 * db + 4 * (lane & 3));
   auto lds_b128 = [](uint32_t addr) -> bf16x8 {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
   };
   auto lds_f4 = [](uint32_t addr) -> f32x4 {
     return *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>((uintptr_t)addr);
   };
-  auto lds_tr = [&](int db, uint32_t off) -> bf16x8 {
-    const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[0][db] + off));
-    const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(taddr[1][db] + off));
+  auto lds_tr2 = [](uint32_t addr) -> bf16x8 {
+    const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)addr);
+    const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(addr + 2 * 16 * D));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // P exchange: operand ps of lane l of key group kw at stage x; lanes are
-  // 16 bytes apart (conflict-free).
-  const uint32_t xaddr = lds0 + X_OFF + (kw * QSTEPS * 64 + lane) * 16;
+  // P exchange: operand x (key block x / QSTEPS, row k-step x % QSTEPS) of
+  // lane l of key group kw at stage s; lanes are 16 bytes apart
+  // (conflict-free).
+  const uint32_t xaddr = lds0 + X_OFF + (kw * NXOP * 64 + lane) * 16;
   constexpr uint32_t XSTAGE = 4 * 64 * XPER * 2;
   constexpr uint32_t XOP = 64 * 16;   // bytes between a lane's operands
 
-  // This lane's key row of K (P role) or V (dS role): the B operand.
-  bf16x8 kvf[KSTEPS];
+  // This lane's key rows of K (P role) or V (dS role): the B operands.
+  bf16x8 kvf[KN][KSTEPS];
   {
     const __bf16 *src = static_cast<const __bf16 *>(prole ? p.k : p.v) + b * p.kv_sb + hk * p.kv_sh;
-    const int64_t ro = (int64_t)min(my_key, p.skv - 1) * p.kv_ss + 8 * half;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) kvf[s] = *reinterpret_cast<const bf16x8 *>(src + ro + 16 * s);
+    for (int kn = 0; kn < KN; ++kn) {
+      const int64_t ro = (int64_t)min(my_key[kn], p.skv - 1) * p.kv_ss + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) kvf[kn][s] = *reinterpret_cast<const bf16x8 *>(src + ro + 32 * s);
+    }
     wait_vmem_all();
   }
-  f32x16 acc[DB];     // dV^T (P role) or dK^T (dS role) of the 32 keys
+  f32x4 acc[DB][KN];     // dV^T (P role) or dK^T (dS role) of the 32 keys
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+    for (int kn = 0; kn < KN; ++kn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[db][kn][i] = 0.0f;
   const float c2 = p.scale_log2;
   constexpr int AHEAD = 2;
   constexpr int NBUF = AHEAD + 1;
-  constexpr int NSA = QB * KSTEPS;      // S or dP products per step
-  constexpr int NSB = QSTEPS * DB;      // dV or dK products per step
-  constexpr int NPAIR = QB * 8;         // pairs of P (or dS) values per lane per step
+  constexpr int NOA = RB * KSTEPS;      // S or dP operands per step (each used by KN products)
+  constexpr int NOB = QSTEPS * DB;      // dV or dK operands per step
+  constexpr int NSA = KN * NOA;         // S or dP products per step
+  constexpr int NSB = KN * NOB;         // dV or dK products per step
+  constexpr int NPAIR = RB * KN * 2;    // pairs of P (or dS) values per lane per step
 
   // Prologue: Q of steps 0 and 1 (when there is a step 1), dO of step 0.
   // Every load is of a step that exists: the cursors never run past the last.
@@ -322,111 +339,129 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   };
 
   if (prole) {
-    // Row-block scores alternate between two register sets by step parity.
-    f32x16 sbuf[2][QB];
+    // Scores ([row block][key block]) alternate between two register sets by
+    // step parity.
+    f32x4 sbuf[2][RB][KN];
     Cursor cs = c0;   // the step being processed
     if (total > 0) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sbuf[0][qb][i] = 0.0f;
+        for (int kn = 0; kn < KN; ++kn)
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-          sbuf[0][qb] = mfma32(lds_b128(raddr[s] + 2 * qb * 32 * D), kvf[s], sbuf[0][qb]);
+          for (int i = 0; i < 4; ++i) sbuf[0][rb][kn][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const bf16x8 a = lds_b128(raddr[s] + 2 * 16 * rb * D);
+#pragma unroll
+          for (int kn = 0; kn < KN; ++kn) sbuf[0][rb][kn] = mfma16(a, kvf[kn][s], sbuf[0][rb][kn]);
+        }
       }
     }
     auto step_p = [&](auto par_tag, int it) {
       constexpr int PAR = decltype(par_tag)::value;
       staging(it);
       if (it < total) {
-        f32x16 (&sacc)[QB] = sbuf[PAR];
-        f32x16 (&snext)[QB] = sbuf[1 - PAR];
+        f32x4 (&sacc)[RB][KN] = sbuf[PAR];
+        f32x4 (&snext)[RB][KN] = sbuf[1 - PAR];
         const uint32_t qnext = 2 * ((it + 1) % QSTG) * QTILE;   // Q stage of step it+1
         constexpr uint32_t ocur = 2 * PAR * QTILE;              // dO stage of step it
         const int st = it % QSTG;
-        // LSE*log2(e) of this lane's rows, 4 at a time (group g: rows
-        // 32(g/4) + 8(g%4) + 4half + e), each group read one group ahead.
-        const uint32_t lbase = lds0 + L_OFF + 4 * (st * QT + 4 * half);
+        // LSE*log2(e) of this lane's rows: row block rb holds rows
+        // 16rb + 4grp .. +3, read one block ahead.
+        const uint32_t lbase = lds0 + L_OFF + 4 * (st * QT + 4 * grp);
         f32x4 lg[2];
         lg[0] = lds_f4(lbase);
-        // Mask: row r of the tile sees this lane's key iff lo <= r <= hi.
+        // Mask: row r of the tile sees this lane's key of block kn iff
+        // lo[kn] <= r <= hi.
         const int64_t qpos0 = cs.cpos + cs.t * QT;
         const int rows_left = p.chunk_len - 1 - cs.t * QT;
         const bool need_mask = !wave_keys_ok || rows_left < QT - 1 ||
                                (p.causal && p.kv_pos0 + wkey0 + 31 > qpos0);
         if (need_mask) {
-          int lo = 0;
-          if (p.causal) {
-            const int64_t r = p.kv_pos0 + my_key - qpos0;
-            lo = (int)(r < 0 ? 0 : (r > QT ? QT : r));
-          }
-          if (!key_ok) lo = QT;
-          const int lo_h = lo - 4 * half, hi_h = rows_left - 4 * half;
+          const int hi_g = rows_left - 4 * grp;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = 32 * qb + 8 * (i >> 2) + (i & 3);
-              sacc[qb][i] = (r < lo_h || r > hi_h) ? -INFINITY : sacc[qb][i];
+          for (int kn = 0; kn < KN; ++kn) {
+            int lo = 0;
+            if (p.causal) {
+              const int64_t r = p.kv_pos0 + my_key[kn] - qpos0;
+              lo = (int)(r < 0 ? 0 : (r > QT ? QT : r));
             }
+            if (!key_ok[kn]) lo = QT;
+            const int lo_g = lo - 4 * grp;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rb + i;
+                sacc[rb][kn][i] = (r < lo_g || r > hi_g) ? -INFINITY : sacc[rb][kn][i];
+              }
+          }
         }
-        bf16x8 pcur[QSTEPS];
+        bf16x8 pcur[KN][QSTEPS];
         bf16x8 opnd[NBUF];
         // Bases of this step's Q reads, made opaque so that the row-block
         // offsets stay instruction immediates.
-        uint32_t rb[KSTEPS];
+        uint32_t rbq[KSTEPS];
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          rb[s] = raddr[s] + qnext;
-          asm volatile("" : "+v"(rb[s]));
+          rbq[s] = raddr[s] + qnext;
+          asm volatile("" : "+v"(rbq[s]));
         }
-        // Half A: S(it+1) (operand u: k-step u/QB of row block u%QB) under P(it).
-        auto read_a = [&](auto u_tag) -> bf16x8 {
-          constexpr int u = decltype(u_tag)::value, qb = u % QB, s = u / QB;
-          return lds_b128(rb[s] + 2 * qb * 32 * D);
+        // Half A: S(it+1) (operand o: k-step o / RB of row block o % RB, so
+        // that products accumulating into one block are 2*RB slots apart)
+        // under P(it).
+        auto read_a = [&](auto o_tag) -> bf16x8 {
+          constexpr int o = decltype(o_tag)::value, rb = o % RB, s = o / RB;
+          return lds_b128(rbq[s] + 2 * 16 * rb * D);
         };
-        static_for<AHEAD>([&](auto u) { opnd[decltype(u)::value] = read_a(u); });
+        static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_a(o); });
         static_for<NSA>([&](auto t_tag) {
-          constexpr int t = decltype(t_tag)::value, qb = t % QB, s = t / QB;
-          if constexpr (t + AHEAD < NSA) opnd[(t + AHEAD) % NBUF] = read_a(IC<t + AHEAD>{});
+          constexpr int t = decltype(t_tag)::value, o = t / KN, kn = t % KN, rb = o % RB, s = o / RB;
+          if constexpr (kn == 0 && o + AHEAD < NOA) opnd[(o + AHEAD) % NBUF] = read_a(IC<o + AHEAD>{});
           if constexpr (s == 0) {
-            f32x16 z;
+            f32x4 z;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-            snext[qb] = mfma32(opnd[t % NBUF], kvf[s], z);
+            for (int i = 0; i < 4; ++i) z[i] = 0.0f;
+            snext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], z);
           } else {
-            snext[qb] = mfma32(opnd[t % NBUF], kvf[s], snext[qb]);
+            snext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], snext[rb][kn]);
           }
-          // Pair u (row block u / 8, elements 2(u%8), 2(u%8)+1) in slot u*NSA/NPAIR.
+          // Pair u (row block u / 4, key block (u / 2) % 2, elements 2(u%2),
+          // 2(u%2)+1) in slot u*NSA/NPAIR; it lands in elements 4(rb%2) + i
+          // of the key block's P operand of k-step rb/2 (the row order of the
+          // dO^T reads).
           static_for<NPAIR>([&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
             if constexpr (u * NSA / NPAIR == t) {
-              constexpr int rq = u / 8, i = 2 * (u % 8), g = u / 2;
-              if constexpr (u % 2 == 0 && g + 1 < NPAIR / 2)
-                lg[(g + 1) % 2] = lds_f4(lbase + 4 * (32 * ((g + 1) / 4) + 8 * ((g + 1) % 4)));
-              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][i], c2, -lg[g % 2][i & 3]));
-              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][i + 1], c2, -lg[g % 2][(i + 1) & 3]));
+              constexpr int rq = u / 4, kq = (u / 2) % 2, i = 2 * (u % 2);
+              if constexpr (u % 4 == 0 && rq + 1 < RB) lg[(rq + 1) % 2] = lds_f4(lbase + 4 * 16 * (rq + 1));
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kq][i], c2, -lg[rq % 2][i]));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kq][i + 1], c2, -lg[rq % 2][i + 1]));
               const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-              pcur[2 * rq + (i >> 3)][i & 7] = t2[0];
-              pcur[2 * rq + (i >> 3)][(i & 7) + 1] = t2[1];
+              pcur[kq][rq >> 1][4 * (rq & 1) + i] = t2[0];
+              pcur[kq][rq >> 1][4 * (rq & 1) + i + 1] = t2[1];
             }
           });
           __builtin_amdgcn_sched_barrier(0);
         });
         // P(it) to the dS wavefront of these keys.
 #pragma unroll
-        for (int ps = 0; ps < QSTEPS; ++ps)
-          *reinterpret_cast<__attribute__((address_space(3))) bf16x8 *>((uintptr_t)(xaddr + PAR * XSTAGE + XOP * ps)) = pcur[ps];
+        for (int kn = 0; kn < KN; ++kn)
+#pragma unroll
+          for (int ps = 0; ps < QSTEPS; ++ps)
+            *reinterpret_cast<__attribute__((address_space(3))) bf16x8 *>(
+                (uintptr_t)(xaddr + PAR * XSTAGE + XOP * (kn * QSTEPS + ps))) = pcur[kn][ps];
         // Half B: dV^T += dO(it)^T P(it) (operand o: k-step o / DB, block o % DB).
         auto read_b = [&](auto o_tag) -> bf16x8 {
           constexpr int o = decltype(o_tag)::value, ps = o / DB, db = o % DB;
-          return lds_tr(db, ocur + 2 * 16 * D * ps);
+          return lds_tr2(taddr[db] + ocur + 2 * 32 * D * ps);
         };
         static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_b(o); });
         static_for<NSB>([&](auto t_tag) {
-          constexpr int t = decltype(t_tag)::value, ps = t / DB, db = t % DB;
-          if constexpr (t + AHEAD < NSB) opnd[(t + AHEAD) % NBUF] = read_b(IC<t + AHEAD>{});
-          acc[db] = mfma32(opnd[t % NBUF], pcur[ps], acc[db]);
+          constexpr int t = decltype(t_tag)::value, o = t / KN, kn = t % KN, ps = o / DB, db = o % DB;
+          if constexpr (kn == 0 && o + AHEAD < NOB) opnd[(o + AHEAD) % NBUF] = read_b(IC<o + AHEAD>{});
+          acc[db][kn] = mfma16(opnd[o % NBUF], pcur[kn][ps], acc[db][kn]);
           __builtin_amdgcn_sched_barrier(0);
         });
         advance(cs);
@@ -440,18 +475,22 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   } else {
     // dP alternates between two register sets by step parity; dS(it-1),
     // made in the second half of step it, feeds the first half of step it+1.
-    f32x16 pbuf[2][QB];
+    f32x4 pbuf[2][RB][KN];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pbuf[q][qb][i] = 0.0f;
-    bf16x8 dsf[QSTEPS];
+        for (int kn = 0; kn < KN; ++kn)
 #pragma unroll
-    for (int ps = 0; ps < QSTEPS; ++ps)
+          for (int i = 0; i < 4; ++i) pbuf[q][rb][kn][i] = 0.0f;
+    bf16x8 dsf[KN][QSTEPS];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dsf[ps][e] = (__bf16)0.0f;
+    for (int kn = 0; kn < KN; ++kn)
+#pragma unroll
+      for (int ps = 0; ps < QSTEPS; ++ps)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsf[kn][ps][e] = (__bf16)0.0f;
     auto step_ds = [&](auto par_tag, int it) {
       constexpr int PAR = decltype(par_tag)::value;
       bf16x8 opnd[NBUF];
@@ -459,74 +498,69 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       if (it >= 2) {
         const uint32_t qold = 2 * ((it - 2) % QSTG) * QTILE;
         // Bases of this step's Q^T reads (opaque: see the P role).
-        uint32_t tb[2][DB];
+        uint32_t tb[DB];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            tb[u][db] = taddr[u][db] + qold;
-            asm volatile("" : "+v"(tb[u][db]));
-          }
+        for (int db = 0; db < DB; ++db) {
+          tb[db] = taddr[db] + qold;
+          asm volatile("" : "+v"(tb[db]));
+        }
         auto read_a = [&](auto o_tag) -> bf16x8 {
           constexpr int o = decltype(o_tag)::value, ps = o / DB, db = o % DB;
-          constexpr uint32_t off = 2 * 16 * D * ps;
-          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(tb[0][db] + off));
-          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(tb[1][db] + off));
-          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          return lds_tr2(tb[db] + 2 * 32 * D * ps);
         };
         static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_a(o); });
         static_for<NSB>([&](auto t_tag) {
-          constexpr int t = decltype(t_tag)::value, ps = t / DB, db = t % DB;
-          if constexpr (t + AHEAD < NSB) opnd[(t + AHEAD) % NBUF] = read_a(IC<t + AHEAD>{});
-          acc[db] = mfma32(opnd[t % NBUF], dsf[ps], acc[db]);
+          constexpr int t = decltype(t_tag)::value, o = t / KN, kn = t % KN, ps = o / DB, db = o % DB;
+          if constexpr (kn == 0 && o + AHEAD < NOB) opnd[(o + AHEAD) % NBUF] = read_a(IC<o + AHEAD>{});
+          acc[db][kn] = mfma16(opnd[o % NBUF], dsf[kn][ps], acc[db][kn]);
           __builtin_amdgcn_sched_barrier(0);
         });
       }
       // Half B: dP(it) = dO(it) V^T under dS(it-1) = P(it-1) o (dP(it-1) - Delta).
       if (it <= total) {
-        f32x16 (&pnext)[QB] = pbuf[PAR];
-        f32x16 (&pprev)[QB] = pbuf[1 - PAR];
+        f32x4 (&pnext)[RB][KN] = pbuf[PAR];
+        f32x4 (&pprev)[RB][KN] = pbuf[1 - PAR];
         constexpr uint32_t ocur = 2 * PAR * QTILE;              // dO stage of step it
         const int st = (it + QSTG - 1) % QSTG;                  // statistics of step it-1
-        bf16x8 pk[QSTEPS];
+        bf16x8 pk[KN][QSTEPS];
 #pragma unroll
-        for (int ps = 0; ps < QSTEPS; ++ps)
-          pk[ps] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
-              (uintptr_t)(xaddr + (1 - PAR) * XSTAGE + XOP * ps));
-        // Delta: lane 16r+e of row block qb reads the value of accumulator
-        // element e of the lanes of its row of 16 (row 32qb + 8(e/4) +
-        // 4(r/2) + e%4); element e then takes it by row broadcast.
-        float dl[QB];
+        for (int kn = 0; kn < KN; ++kn)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          dl[qb] = *reinterpret_cast<const __attribute__((address_space(3))) float *>(
-              (uintptr_t)(lds0 + DL_OFF + 4 * (st * QT + 32 * qb + 8 * ((lane & 15) >> 2) + 4 * half + (lane & 3))));
-        auto read_b = [&](auto u_tag) -> bf16x8 {
-          constexpr int u = decltype(u_tag)::value, qb = u % QB, s = u / QB;
-          return lds_b128(raddr[s] + ocur + 2 * qb * 32 * D);
+          for (int ps = 0; ps < QSTEPS; ++ps)
+            pk[kn][ps] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
+                (uintptr_t)(xaddr + (1 - PAR) * XSTAGE + XOP * (kn * QSTEPS + ps)));
+        // Delta: lane 16g+n reads the Delta of row 16(n/4) + 4g + n%4 (row
+        // block n/4, accumulator element n%4 of the lanes of its row of 16);
+        // element i of row block rb then takes it by row broadcast from lane
+        // 4rb + i.
+        const float dl = *reinterpret_cast<const __attribute__((address_space(3))) float *>(
+            (uintptr_t)(lds0 + DL_OFF + 4 * (st * QT + 16 * (col >> 2) + 4 * grp + (col & 3))));
+        auto read_b = [&](auto o_tag) -> bf16x8 {
+          constexpr int o = decltype(o_tag)::value, rb = o % RB, s = o / RB;
+          return lds_b128(raddr[s] + ocur + 2 * 16 * rb * D);
         };
-        static_for<AHEAD>([&](auto u) { opnd[decltype(u)::value] = read_b(u); });
+        static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_b(o); });
         static_for<NSA>([&](auto t_tag) {
-          constexpr int t = decltype(t_tag)::value, qb = t % QB, s = t / QB;
-          if constexpr (t + AHEAD < NSA) opnd[(t + AHEAD) % NBUF] = read_b(IC<t + AHEAD>{});
+          constexpr int t = decltype(t_tag)::value, o = t / KN, kn = t % KN, rb = o % RB, s = o / RB;
+          if constexpr (kn == 0 && o + AHEAD < NOA) opnd[(o + AHEAD) % NBUF] = read_b(IC<o + AHEAD>{});
           if constexpr (s == 0) {
-            f32x16 z;
+            f32x4 z;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-            pnext[qb] = mfma32(opnd[t % NBUF], kvf[s], z);
+            for (int i = 0; i < 4; ++i) z[i] = 0.0f;
+            pnext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], z);
           } else {
-            pnext[qb] = mfma32(opnd[t % NBUF], kvf[s], pnext[qb]);
+            pnext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], pnext[rb][kn]);
           }
           static_for<NPAIR>([&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
             if constexpr (u * NSA / NPAIR == t) {
-              constexpr int rq = u / 8, i = 2 * (u % 8), ps = 2 * rq + (i >> 3);
-              const float p0 = (float)pk[ps][i & 7], p1 = (float)pk[ps][(i & 7) + 1];
-              const float x0 = p0 * (pprev[rq][i] - row_bcast<i>(dl[rq]));
-              const float x1 = p1 * (pprev[rq][i + 1] - row_bcast<i + 1>(dl[rq]));
+              constexpr int rq = u / 4, kq = (u / 2) % 2, i = 2 * (u % 2), ps = rq >> 1, e = 4 * (rq & 1) + i;
+              const float p0 = (float)pk[kq][ps][e], p1 = (float)pk[kq][ps][e + 1];
+              const float x0 = p0 * (pprev[rq][kq][i] - row_bcast<4 * rq + i>(dl));
+              const float x1 = p1 * (pprev[rq][kq][i + 1] - row_bcast<4 * rq + i + 1>(dl));
               const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
-              dsf[ps][i & 7] = t2[0];
-              dsf[ps][(i & 7) + 1] = t2[1];
+              dsf[kq][ps][e] = t2[0];
+              dsf[kq][ps][e + 1] = t2[1];
             }
           });
           __builtin_amdgcn_sched_barrier(0);
@@ -540,19 +574,19 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     }
   }
 
-  if (!key_ok) return;
-  float *dst = (prole ? p.dv : p.dk) + (((int64_t)b * p.hkv + hk) * p.skv + my_key) * D;
+  float *dst = (prole ? p.dv : p.dk) + ((int64_t)b * p.hkv + hk) * p.skv * D;
   const float mul = prole ? 1.0f : p.scale;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int kn = 0; kn < KN; ++kn) {
+    if (!key_ok[kn]) continue;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int d = 32 * db + 8 * gq + 4 * half;
+    for (int db = 0; db < DB; ++db) {
       f32x4 a;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = acc[db][4 * gq + e] * mul;
-      *reinterpret_cast<f32x4 *>(dst + d) = a;
+      for (int e = 0; e < 4; ++e) a[e] = acc[db][kn][e] * mul;
+      *reinterpret_cast<f32x4 *>(dst + (int64_t)my_key[kn] * D + 16 * db + 4 * grp) = a;
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
