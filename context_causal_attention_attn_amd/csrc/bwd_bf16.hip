@@ -38,10 +38,6 @@ constexpr int BQ = kBwdBlockQ;    // query rows per step of that workgroup
 constexpr int BN = kDqBlockKV;    // keys per tile of the query-stationary kernel
 constexpr int NT = kDqWaves * 64;
 
-// sched_group_barrier masks
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
 // ---------------------------------------------------------------------------
 // 1. Delta = rowsum(dO o O), 16 lanes per row; also LSE in log2 units.
 // ---------------------------------------------------------------------------
