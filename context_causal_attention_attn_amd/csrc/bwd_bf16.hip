@@ -281,9 +281,10 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // P exchange: operand x (key block x / QSTEPS, row k-step x % QSTEPS) of
-  // lane l of key group kw at stage s; lanes are 16 bytes apart
-  // (conflict-free).
-  const uint32_t xaddr = lds0 + X_OFF + (kw * NXOP * 64 + lane) * 16;
+  // lane l of key group kw at stage s, 16 bytes per lane. Lane l takes slot
+  // l ^ 4*(l/32): each 16-lane pass of a 16-byte access (lanes sharing bits
+  // 2 and 4) then covers all 64 banks.
+  const uint32_t xaddr = lds0 + X_OFF + (kw * NXOP * 64 + (lane ^ ((lane >> 5) << 2))) * 16;
   constexpr uint32_t XSTAGE = 4 * 64 * XPER * 2;
   constexpr uint32_t XOP = 64 * 16;   // bytes between a lane's operands
 
