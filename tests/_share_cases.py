@@ -49,3 +49,16 @@ def oracle_rows(prob, sh, scale, rows=None, heads=None, causal=True):
         outs.append(o[:, 0])
         lses.append(l[:, 0])
     return np.stack(outs, 1), np.stack(lses, 1)
+
+
+def spiked_problem(seed=7, with_dout=False):
+    """A 1024-token bf16 problem whose keys 600..615 are scaled by 30. Rows
+    after them meet scores tens of log2 units above (and below) everything in
+    their earlier key tiles, so the forward's running reference must be
+    replaced, and O rescaled, on a tile after the first; the backward sees
+    rows whose LSE is dominated by a few keys."""
+    prob = global_problem(1, 4, 2, 1024, 128, dtype="bf16", seed=seed, with_dout=with_dout)
+    k = prob.k.float()
+    k[:, :, 600:616] *= 30.0
+    prob.k = k.to(torch.bfloat16)
+    return prob

@@ -16,7 +16,7 @@ import torch
 import oracle.cp_share as oc
 from context_causal_attention_attn_amd import cp_attn_bwd, cp_attn_fwd, cut_share
 from synthetic import global_problem, workload
-from tests._share_cases import oracle_share, to_f64
+from tests._share_cases import oracle_share, spiked_problem, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -126,6 +126,15 @@ def test_backward_edge_cases():
         sh, dq, dk, dv, scale = gpu_share_grads(prob, "head_tail", 4, r)
         osh = oracle_share("head_tail", 8, 4, 2, 4, r)
         check_grads((dq, dk, dv), oracle_share_grads(prob, osh, scale), REL_BF16, f"S=8 r{r}")
+
+
+@pytest.mark.parametrize("kind,cp,rank", [("contiguous", 2, 1), ("head_tail", 2, 0)])
+def test_backward_with_late_score_spike(kind, cp, rank):
+    """Gradients when a few keys dominate the rows after them (large LSE)."""
+    prob = spiked_problem(with_dout=True)
+    sh, dq, dk, dv, scale = gpu_share_grads(prob, kind, cp, rank)
+    osh = oracle_share(kind, 1024, 4, 2, cp, rank)
+    check_grads((dq, dk, dv), oracle_share_grads(prob, osh, scale), REL_BF16, f"spike {kind} r{rank}")
 
 
 @pytest.fixture(scope="module")

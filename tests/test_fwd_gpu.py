@@ -15,7 +15,7 @@ import torch
 
 from context_causal_attention_attn_amd import cp_attn_fwd, cut_share
 from synthetic import global_problem, workload
-from tests._share_cases import oracle_rows, oracle_share, to_f64
+from tests._share_cases import oracle_rows, oracle_share, spiked_problem, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +118,18 @@ def test_empty_share_and_single_row_chunks():
         osh = oracle_share("head_tail", 8, 4, 2, 4, r)
         ref_o, ref_l = oracle_rows(prob, osh, scale)
         check_close(out, lse, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, f"S=8 head_tail r{r}")
+
+
+@pytest.mark.parametrize("kind,cp,rank", [("contiguous", 2, 1), ("head_tail", 2, 0), ("head_tail", 2, 1)])
+def test_late_score_spike_rescales(kind, cp, rank):
+    """Scores far above the running reference in a later key tile: the max is
+    taken and O rescaled mid-row (random inputs never reach that path)."""
+    prob = spiked_problem()
+    sh, out, lse, scale = run_gpu_share(prob, kind, cp, rank)
+    osh = oracle_share(kind, 1024, 4, 2, cp, rank)
+    ref_o, ref_l = oracle_rows(prob, osh, scale)
+    assert float(np.max(ref_l)) > 20.0   # the spike dominates some rows
+    check_close(out, lse, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, f"spike {kind} r{rank}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
