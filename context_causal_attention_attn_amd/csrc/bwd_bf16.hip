@@ -10,9 +10,9 @@
 //     dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Three launches, no atomics:
-//  1. bwd_pre: Delta for every local row.
+//  1. bwd_pre: Delta (and LSE in log2 units) for every local row.
 //  2. bwd_dkdv (key-stationary): one workgroup of 8 wavefronts per 128-key
-//     tile of one KV head; it streams the 32-row query tiles -- of every
+//     tile of one KV head; it streams the 64-row query tiles -- of every
 //     head of the GQA group and every chunk -- that can see one of its keys.
 //     Wavefronts w and w+4 own the same 32 keys: the first keeps K rows and
 //     dV^T (S = Q K^T, P, dV^T += dO^T P), the second, one tile behind, V
@@ -471,7 +471,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     }
   } else {
     // dP alternates between two register sets by step parity; dS(it-1),
-    // made in the second half of step it, feeds the first half of step it+1.
+    // made in the second half of step it, feeds the first half of step it+1,
+    // where it meets Q(it-1), still held by the 5-stage Q ring.
     f32x4 pbuf[2][RB][KN];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
