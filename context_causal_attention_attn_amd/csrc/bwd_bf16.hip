@@ -10,7 +10,7 @@
 //     dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Three launches, no atomics:
-//  1. bwd_pre: Delta (and LSE in log2 units) for every local row.
+//  1. bwd_pre: -Delta (and LSE in log2 units) for every local row.
 //  2. bwd_dkdv (key-stationary): one workgroup of 8 wavefronts per 128-key
 //     tile of one KV head; it streams the 64-row query tiles -- of every
 //     head of the GQA group and every chunk -- that can see one of its keys.
@@ -39,7 +39,9 @@ constexpr int BN = kDqBlockKV;    // keys per tile of the query-stationary kerne
 constexpr int NT = kDqWaves * 64;
 
 // ---------------------------------------------------------------------------
-// 1. Delta = rowsum(dO o O), 16 lanes per row; also LSE in log2 units.
+// 1. Delta = rowsum(dO o O), 16 lanes per row, stored negated (the matrix
+//    kernels start their dP accumulators from -Delta, so the products come
+//    out as dP - Delta); also LSE in log2 units.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
@@ -62,7 +64,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
   if (row < rows && part == 0) {
-    p.delta[row] = acc;
+    p.delta[row] = -acc;
     const float l = p.lse[row];
     p.lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
   }
@@ -514,12 +516,13 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           __builtin_amdgcn_sched_barrier(0);
         });
       }
-      // Half B: dP(it) = dO(it) V^T under dS(it-1) = P(it-1) o (dP(it-1) - Delta).
+      // Half B: dP(it) - Delta = dO(it) V^T - Delta under
+      // dS(it-1) = P(it-1) o (dP(it-1) - Delta).
       if (it <= total) {
         f32x4 (&pnext)[RB][KN] = pbuf[PAR];
         f32x4 (&pprev)[RB][KN] = pbuf[1 - PAR];
         constexpr uint32_t ocur = 2 * PAR * QTILE;              // dO stage of step it
-        const int st = (it + QSTG - 1) % QSTG;                  // statistics of step it-1
+        const int st = it % QSTG;                               // statistics of step it
         bf16x8 pk[KN][QSTEPS];
 #pragma unroll
         for (int kn = 0; kn < KN; ++kn)
@@ -527,12 +530,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           for (int ps = 0; ps < QSTEPS; ++ps)
             pk[kn][ps] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
                 (uintptr_t)(xaddr + (1 - PAR) * XSTAGE + XOP * (kn * QSTEPS + ps)));
-        // Delta: lane 16g+n reads the Delta of row 16(n/4) + 4g + n%4 (row
-        // block n/4, accumulator element n%4 of the lanes of its row of 16);
-        // element i of row block rb then takes it by row broadcast from lane
-        // 4rb + i.
-        const float dl = *reinterpret_cast<const __attribute__((address_space(3))) float *>(
-            (uintptr_t)(lds0 + DL_OFF + 4 * (st * QT + 16 * (col >> 2) + 4 * grp + (col & 3))));
+        // -Delta of this step's rows (row block rb: rows 16rb + 4grp .. +3) is
+        // the starting value of dP(it), which so comes out as dP - Delta.
+        f32x4 nd[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) nd[rb] = lds_f4(lds0 + DL_OFF + 4 * (st * QT + 16 * rb + 4 * grp));
         auto read_b = [&](auto o_tag) -> bf16x8 {
           constexpr int o = decltype(o_tag)::value, rb = o % RB, s = o / RB;
           return lds_b128(raddr[s] + ocur + 2 * 16 * rb * D);
@@ -542,10 +544,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           constexpr int t = decltype(t_tag)::value, o = t / KN, kn = t % KN, rb = o % RB, s = o / RB;
           if constexpr (kn == 0 && o + AHEAD < NOA) opnd[(o + AHEAD) % NBUF] = read_b(IC<o + AHEAD>{});
           if constexpr (s == 0) {
-            f32x4 z;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] = 0.0f;
-            pnext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], z);
+            pnext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], nd[rb]);
           } else {
             pnext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], pnext[rb][kn]);
           }
@@ -554,8 +553,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
             if constexpr (u * NSA / NPAIR == t) {
               constexpr int rq = u / 4, kq = (u / 2) % 2, i = 2 * (u % 2), ps = rq >> 1, e = 4 * (rq & 1) + i;
               const float p0 = (float)pk[kq][ps][e], p1 = (float)pk[kq][ps][e + 1];
-              const float x0 = p0 * (pprev[rq][kq][i] - row_bcast<4 * rq + i>(dl));
-              const float x1 = p1 * (pprev[rq][kq][i + 1] - row_bcast<4 * rq + i + 1>(dl));
+              const float x0 = p0 * pprev[rq][kq][i];
+              const float x1 = p1 * pprev[rq][kq][i + 1];
               const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
               dsf[kq][ps][e] = t2[0];
               dsf[kq][ps][e + 1] = t2[1];
@@ -668,7 +667,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // Q and dO rows of this lane's queries: B operands of S^T and dP^T. Lanes
   // past the item's last row read its first row and get LSE = +inf (P = 0).
   bf16x8 qf[QB][KSTEPS], gf[QB][KSTEPS];
-  float lse2[QB], delta[QB];
+  float lse2[QB], ndelta[QB];   // LSE*log2(e) and -Delta of this lane's queries
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int load_row = qvalid[qb] ? local_row[qb] : chunk * p.chunk_len + item_row0;
@@ -682,11 +681,11 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
       gf[qb][s] = *reinterpret_cast<const bf16x8 *>(gp + 32 * s);
     }
     lse2[qb] = INFINITY;
-    delta[qb] = 0.0f;
+    ndelta[qb] = 0.0f;
     if (qvalid[qb]) {
       const int64_t row = ((int64_t)b * p.hq + head) * p.sq + local_row[qb];
       lse2[qb] = p.lse2[row];
-      delta[qb] = p.delta[row];
+      ndelta[qb] = p.delta[row];
     }
   }
   wait_vmem_all();
@@ -800,7 +799,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sbuf[0][h][qb][i] = 0.0f;
-          pbuf[0][h][qb][i] = 0.0f;
+          pbuf[0][h][qb][i] = ndelta[qb];   // dP^T - Delta, as in the blocks
         }
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
@@ -884,9 +883,11 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
         f32x4 &dst = (u & 1) ? pnext[h][qb] : snext[h][qb];
         const bf16x8 &bop = (u & 1) ? gf[qb][s] : qf[qb][s];
         if constexpr (s == 0) {
+          // dP^T starts from -Delta (so it comes out as dP^T - Delta), S^T from 0.
+          const float z0 = (u & 1) ? ndelta[qb] : 0.0f;
           f32x4 z;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) z[i] = 0.0f;
+          for (int i = 0; i < 4; ++i) z[i] = z0;
           dst = mfma16(opnd[o % NBUF], bop, z);
         } else {
           dst = mfma16(opnd[o % NBUF], bop, dst);
@@ -901,8 +902,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
           constexpr int rq = e / 4, h = (e / 2) % 2, i = 2 * (e % 2);
           const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[h][rq][i], c2, -lse2[rq]));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[h][rq][i + 1], c2, -lse2[rq]));
-          const float x0 = p0 * (pcur[h][rq][i] - delta[rq]);
-          const float x1 = p1 * (pcur[h][rq][i + 1] - delta[rq]);
+          const float x0 = p0 * pcur[h][rq][i];
+          const float x1 = p1 * pcur[h][rq][i + 1];
           const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
           dscur[rq][4 * h + i] = t2[0];
           dscur[rq][4 * h + i + 1] = t2[1];

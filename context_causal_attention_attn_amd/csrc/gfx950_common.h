@@ -80,14 +80,6 @@ __device__ __forceinline__ float quad_max(float x) {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-// Value of lane N of this lane's row of 16 lanes (DPP row_newbcast); used as
-// an operand, it folds into the consuming instruction.
-template <int N>
-__device__ __forceinline__ float row_bcast(float v) {
-  static_assert(N >= 0 && N < 16, "lane within a row of 16");
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xF, 0xF, false));
-}
-
 // Calls f(IC<0>{}), ..., f(IC<N-1>{}) in order (compile-time loop index).
 template <int N, int I = 0, class F>
 __device__ __forceinline__ void static_for(F &&f) {

@@ -93,7 +93,7 @@ struct BwdParams {
   const void *out;
   const void *dout;
   const float *lse;
-  float *delta;                 // workspace [B, Hq, Sq]: rowsum(dO o O)
+  float *delta;                 // workspace [B, Hq, Sq]: rowsum(dO o O) (fp32 kernels), its negative (bf16 kernels)
   float *lse2;                  // workspace [B, Hq, Sq]: LSE * log2(e), +inf for rows with no visible key
   void *dq;
   float *dk;                    // [B, Hkv, Skv, D]
