@@ -286,7 +286,17 @@ def cpu_baseline(spec, prob, rank):
     pairs = oc.share_pairs(sh["q_pos"], sh["kv_pos"])
     flops = 14.0 * D * pairs   # forward (4D) + backward (10D) per visible pair
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{kind} share rank {r}: query head {h} only (1 of {len(sh['q_heads'])}), "
                       f"all {len(sh['q_pos'])} local rows, forward+backward in fp64 NumPy; "
                       f"{dt:.1f} s for {flops / 1e9:.1f} causal-effective GFLOP",
