@@ -18,8 +18,9 @@ roofline object describes the kernel with the largest average. Its "traffic"
 comes from the rocprofv3 counter summaries in profiles/ when one matches the
 kernel's current source text, else null.
 
-After the timed region the step keeps running for about 1.5 s while amd-smi
-reads the GFX clocks and socket power once ("clock"; the chip runs at its
+After the timed region the step keeps running for about 2.5 s while amd-smi
+reads the GFX clocks and socket power three times ("clock": the read at the
+highest socket power, and every read; the chip runs at its
 power cap, well below the 2.4 GHz the peak assumes). Prints ONE JSON line.
 `--detail` adds every other share of the workload list to that line under
 "detail".
@@ -203,10 +204,12 @@ def parse_smi_metric(text):
     return clocks, power
 
 
-def sample_clock(step, seconds=1.5):
+def sample_clock(step, seconds=2.5, samples=3):
     """Run `step` back to back for about `seconds` and read the GFX clocks and
-    socket power once, half-way, with amd-smi (the timed region itself is too
-    short for the tool). None when amd-smi is not available."""
+    socket power `samples` times with amd-smi (the timed region itself is too
+    short for the tool). A read can land in a lull, so the sample drawn at the
+    highest socket power is the one reported; all reads are listed. None when
+    amd-smi is not available."""
     import shutil
     import subprocess
     import threading
@@ -215,30 +218,39 @@ def sample_clock(step, seconds=1.5):
     exe = shutil.which("amd-smi")
     if exe is None:
         return None
-    out = {}
+    texts = []
 
     def probe():
-        time.sleep(seconds / 2)
-        try:
-            r = subprocess.run([exe, "metric", "-c", "-p"], capture_output=True, text=True, timeout=20)
-            out["text"] = r.stdout
-        except (OSError, subprocess.SubprocessError):
-            out["text"] = ""
+        for i in range(samples):
+            time.sleep(seconds / (samples + 1))
+            try:
+                r = subprocess.run([exe, "metric", "-c", "-p"], capture_output=True, text=True, timeout=20)
+                texts.append(r.stdout)
+            except (OSError, subprocess.SubprocessError):
+                pass
 
     th = threading.Thread(target=probe)
     th.start()
     t0 = time.perf_counter()
     while th.is_alive() or time.perf_counter() - t0 < seconds:
-        step()
+        for _ in range(4):
+            step()
         torch.cuda.synchronize()
     th.join()
-    clocks, power = parse_smi_metric(out.get("text", ""))
-    if not clocks:
+    reads = []
+    for text in texts:
+        clocks, power = parse_smi_metric(text)
+        if clocks:
+            clocks.sort()
+            n = len(clocks)
+            med = clocks[n // 2] if n % 2 else 0.5 * (clocks[n // 2 - 1] + clocks[n // 2])
+            reads.append({"gfx_mhz_median": med, "gfx_mhz_min": clocks[0], "gfx_mhz_max": clocks[-1],
+                          "socket_power_w": power})
+    if not reads:
         return None
-    clocks.sort()
-    med = clocks[len(clocks) // 2] if len(clocks) % 2 else 0.5 * (clocks[len(clocks) // 2 - 1] + clocks[len(clocks) // 2])
-    return {"gfx_mhz_median": med, "gfx_mhz_min": clocks[0], "gfx_mhz_max": clocks[-1],
-            "socket_power_w": power, "source": "amd-smi metric -c -p while the step loop ran"}
+    best = max(reads, key=lambda r: r["socket_power_w"] or 0.0)
+    return dict(best, reads=reads, source="amd-smi metric -c -p while the step loop ran "
+                                          "(the read at the highest socket power)")
 
 
 def copy_calibration(mib):
@@ -389,8 +401,9 @@ def main():
     }
     if not args.no_clock:
         clk = sample_clock(res["step"])
-        if clk:
+        if clk and (clk["socket_power_w"] or 0.0) >= 900.0:
             # the same achieved rates against the peak at the clock actually run
+            # (only from a read taken under load)
             f = PEAK_BF16_TFLOPS * clk["gfx_mhz_median"] / 2400.0
             clk["mfma_frac_at_clock"] = {p: round(kernels[p]["achieved"] / f, 4)
                                          for p in kernels if kernels[p]["unit"] == "TFLOP/s"}
