@@ -142,17 +142,20 @@ def htbwd_problem():
     return workload("head_tail_bwd_b2_cp8_s32k_gqa32x8_d128")
 
 
-@pytest.mark.parametrize("rank", [0, 7])
-def test_full_size_head_tail_backward_sampled(htbwd_problem, rank):
-    spec, prob = htbwd_problem
-    S, Hq, Hkv, D = spec["seq"], spec["hq"], spec["hkv"], spec["head_dim"]
-    sh, dq, dk, dv, scale = gpu_share_grads(prob, "head_tail", spec["cp"], rank)
-    osh = oracle_share("head_tail", S, Hq, Hkv, spec["cp"], rank)
+def check_full_size_backward_sampled(spec, prob, kind, rank, b, hk, what):
+    """Full-size share backward in the launch configuration bench.py times,
+    checked on sampled outputs the oracle computes one by one: dQ of sampled
+    rows (every head of one GQA group) and dK/dV of sampled keys (which need
+    every local row of the group's heads)."""
+    S, Hq, Hkv = spec["seq"], spec["hq"], spec["hkv"]
+    sh, dq, dk, dv, scale = gpu_share_grads(prob, kind, spec["cp"], rank)
+    osh = oracle_share(kind, S, Hq, Hkv, spec["cp"], rank)
     rng = np.random.default_rng(rank)
-    b, hk = 1, 5
-    heads = list(range(hk * 4, hk * 4 + 4))
-    # dQ on sampled rows (every head of the group): exact row by row.
-    rows = np.unique(np.concatenate([[0, 31, 32, 2047, 2048, 4095], rng.integers(0, 4096, 40)]))
+    G = Hq // Hkv
+    heads = list(range(hk * G, hk * G + G))
+    nrows = len(osh["q_pos"])
+    rows = np.unique(np.concatenate([[0, 31, 32, nrows // 2 - 1, nrows // 2, nrows - 1],
+                                     rng.integers(0, nrows, 40)]))
     pos = osh["q_pos"][rows]
     qd = to_f64(prob.q[b:b + 1, heads][:, :, torch.from_numpy(pos)])
     dod = to_f64(prob.dout[b:b + 1, heads][:, :, torch.from_numpy(pos)])
@@ -161,8 +164,9 @@ def test_full_size_head_tail_backward_sampled(htbwd_problem, rank):
                                          kv_index=np.array([], dtype=np.int64))
     got_dq = to_f64(dq[b:b + 1, heads][:, :, torch.from_numpy(rows).cuda()])
     e_dq = rel_l2(got_dq, ref_dq)
-    # dK/dV of sampled keys: needs every local row of the group's heads.
-    keys = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 2048], rng.integers(0, S, 40)]))
+    last = int(osh["q_pos"].max())
+    keys = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 2048, last - 1, last],
+                                     rng.integers(0, last + 1, 40)]))
     qa = to_f64(prob.q[b:b + 1, heads][:, :, torch.from_numpy(osh["q_pos"])])
     doa = to_f64(prob.dout[b:b + 1, heads][:, :, torch.from_numpy(osh["q_pos"])])
     _, ref_dk, ref_dv = oc.attention_rows_bwd(qa, kd, vd, doa, osh["q_pos"], osh["kv_pos"], scale, True,
@@ -170,11 +174,24 @@ def test_full_size_head_tail_backward_sampled(htbwd_problem, rank):
     kt = torch.from_numpy(keys).cuda()
     e_dk = rel_l2(to_f64(dk[b:b + 1, hk:hk + 1][:, :, kt]), ref_dk)
     e_dv = rel_l2(to_f64(dv[b:b + 1, hk:hk + 1][:, :, kt]), ref_dv)
-    print(f"32K head_tail bwd r{rank}: dq {e_dq:.3e} dk {e_dk:.3e} dv {e_dv:.3e}", flush=True)
+    print(f"{what}: dq {e_dq:.3e} dk {e_dk:.3e} dv {e_dv:.3e}", flush=True)
     assert e_dq <= REL_BF16 and e_dk <= REL_BF16 and e_dv <= REL_BF16
-    last = int(osh["q_pos"].max())
     assert torch.all(dk[:, :, last + 1:] == 0) and torch.all(dv[:, :, last + 1:] == 0)
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_full_size_head_tail_backward_sampled(htbwd_problem, rank):
+    spec, prob = htbwd_problem
+    check_full_size_backward_sampled(spec, prob, "head_tail", rank, 1, 5, f"32K head_tail bwd r{rank}")
+
+
+def test_full_size_colossal_backward_sampled():
+    """The benchmarked share (Colossal cp=8 rank 7, S = 32768) backward."""
+    spec, _ = workload("colossal_cp8_r7_s32k_gqa32x8_d128")
+    prob = global_problem(spec["batch"], spec["hq"], spec["hkv"], spec["seq"], spec["head_dim"],
+                          spec["dtype"], 0, with_dout=True)
+    check_full_size_backward_sampled(spec, prob, "contiguous", spec["ranks"][0], 0, 3, "32K colossal bwd r7")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
