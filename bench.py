@@ -417,7 +417,9 @@ def main():
             bw = bool(sp.get("backward"))
             _, pr = workload(name, seed=0)
             for r in sp["ranks"]:
-                rr = time_share(sp, pr, r, max(5, args.steps // 2), 2, bw)
+                # Input generation leaves the GPU idle for seconds: warm it
+                # back up (clocks ramp over many steps) before timing.
+                rr = time_share(sp, pr, r, max(5, args.steps // 2), max(10, args.warmup), bw)
                 t = rr["ms"]
                 ent = {"fwd_ms": round(t["fwd"], 4), "fwd_tflops": round(tf(rr["flops"]["fwd"], t["fwd"]), 2),
                        "fwd_frac": round(tf(rr["flops"]["fwd"], t["fwd"]) / PEAK_BF16_TFLOPS, 4)}
