@@ -70,8 +70,8 @@ KERNEL_SOURCES = {   # files whose text determines each kernel's machine code
     "dkdv": ["bwd_bf16.hip", "gfx950_common.h", "plan.h"],
     "dq": ["bwd_bf16.hip", "gfx950_common.h", "plan.h"],
 }
-KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128, 2>", "pre": "bwd_pre_kernel<128>",
-                "dkdv": "bwd_dkdv_kernel<128>", "dq": "bwd_dq_kernel<128, 2>"}
+KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128, 2, false>", "pre": "bwd_pre_kernel<128>",
+                "dkdv": "bwd_dkdv_kernel<128>", "dq": "bwd_dq_kernel<128, 2, false>"}
 
 
 def sources_sha256(part):

@@ -15,6 +15,8 @@ LIB_PATH = os.environ.get("CPATTN_LIB") or os.path.join(HERE, "libcpattn.so")
 
 ABI_VERSION = 1
 MAX_Q_CHUNKS = 16
+MAX_KV_CHUNKS = 64
+KV_CHUNK_ALIGN = 128
 
 LAYOUT_CONTIGUOUS = 0
 LAYOUT_HEAD_TAIL = 1

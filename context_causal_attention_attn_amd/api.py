@@ -122,7 +122,10 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
 
     q is the local query shard (rows in chunk order), k/v the gathered K/V.
     q_chunk_pos gives each chunk's global start position (see
-    cp_attn_share_positions); kv_chunk_pos the global position of key row 0.
+    cp_attn_share_positions). kv_chunk_pos gives the global start position of
+    each of the equal KV chunks in storage order: (p0,) for keys in natural
+    order from p0, or one entry per chunk for K/V in any chunk order (e.g. as
+    an all-gather delivers them; chunk length a multiple of 128 then).
     """
     lib = _lib.load()
     _check_inputs(q, k, v)
@@ -148,7 +151,8 @@ def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="
     """Backward of one share: returns (dq in q's dtype, dk, dv float32 partials over the gathered K/V).
 
     grads, if given, is a (dq, dk, dv) triple of preallocated outputs: dq with
-    out's strides, dk/dv contiguous float32 [B, Hkv, Skv, D].
+    out's strides, dk/dv contiguous float32 [B, Hkv, Skv, D]. dk/dv rows follow
+    the k/v rows (the KV chunk table's storage order).
     """
     return _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal,
                 softmax_scale, workspace, grads, None)

@@ -149,7 +149,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     key_ok[kn] = my_key[kn] < p.skv;
   }
   const bool wave_keys_ok = wkey0 + 31 < p.skv;
-  const int64_t kv_lo = p.kv_pos0 + key0;
+  // Global position of storage row 0 as seen from this tile's KV chunk (a
+  // tile never straddles two chunks): key j sits at kv_base + j.
+  const int kc = key0 / p.kv.len;
+  const int64_t kv_base = p.kv.pos[kc] - (int64_t)kc * p.kv.len;
+  const int64_t kv_lo = kv_base + key0;
 
   // Query tiles this key tile meets: per chunk, tiles first_tile(c) ..
   // nq_tiles-1, each for every head of the GQA group. A cursor walks them in
@@ -376,14 +380,14 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         const int64_t qpos0 = cs.cpos + cs.t * QT;
         const int rows_left = p.chunk_len - 1 - cs.t * QT;
         const bool need_mask = !wave_keys_ok || rows_left < QT - 1 ||
-                               (p.causal && p.kv_pos0 + wkey0 + 31 > qpos0);
+                               (p.causal && kv_base + wkey0 + 31 > qpos0);
         if (need_mask) {
           const int hi_g = rows_left - 4 * grp;
 #pragma unroll
           for (int kn = 0; kn < KN; ++kn) {
             int lo = 0;
             if (p.causal) {
-              const int64_t r = p.kv_pos0 + my_key[kn] - qpos0;
+              const int64_t r = kv_base + my_key[kn] - qpos0;
               lo = (int)(r < 0 ? 0 : (r > QT ? QT : r));
             }
             if (!key_ok[kn]) lo = QT;
@@ -601,7 +605,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 // over 32-key blocks: in block b the matrix core computes dQ^T of block b-1
 // and S^T, dP^T of block b+1 while the vector ALU forms dS^T of block b; one
 // barrier per 64-key tile.
-template <int D, int RB>
+template <int D, int RB, bool MKV>
 __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int HPW = kDqWaves / RB;
   constexpr int BM = kDqWaveRows * RB;
@@ -657,12 +661,44 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     local_row[qb] = chunk * p.chunk_len + item_row0 + wrow0 + r;
   }
 
-  int nvis = p.skv;
-  if (p.causal) {
-    const int64_t n = item_qhi - p.kv_pos0 + 1;
-    nvis = (int)(n < 0 ? 0 : (n > p.skv ? p.skv : n));
+  // KV tiles to visit: per KV chunk the prefix its rows can see. One chunk
+  // (MKV false): pipeline tile J is storage tile J. Several: the chunks'
+  // prefixes one after another, handed out by a scalar cursor as (storage
+  // tile, global position of storage row 0 seen from the tile's chunk), as in
+  // the forward kernel.
+  auto vis_tiles = [&](int c) {
+    int nv = p.kv.len;
+    if (p.causal) {
+      const int64_t n = item_qhi - p.kv.pos[c] + 1;
+      nv = (int)(n < 0 ? 0 : (n > p.kv.len ? p.kv.len : n));
+    }
+    return (nv + BN - 1) / BN;
+  };
+  int ntiles = 0;
+  if constexpr (MKV) {
+    for (int c = 0; c < p.kv.n; ++c) ntiles += vis_tiles(c);
+  } else {
+    ntiles = vis_tiles(0);
   }
-  const int ntiles = (nvis + BN - 1) / BN;
+  const int64_t kv_pos0 = p.kv.pos[0];
+  struct TileRef {
+    int kt;
+    int64_t base;
+  };
+  int cur_c = 0, cur_left = vis_tiles(0), cur_kt = 0;
+  auto next_tile = [&]() -> TileRef {
+    // At most ntiles calls: a chunk with tiles left always follows (the bound
+    // only guards the loop; the ragged-tile staging clamps rows into K/V).
+    while (cur_left == 0 && cur_c + 1 < p.kv.n) {
+      ++cur_c;
+      cur_left = vis_tiles(cur_c);
+      cur_kt = cur_c * (p.kv.len / BN);
+    }
+    const TileRef r{cur_kt, p.kv.pos[cur_c] - (int64_t)cur_c * p.kv.len};
+    ++cur_kt;
+    --cur_left;
+    return r;
+  };
 
   // Q and dO rows of this lane's queries: B operands of S^T and dP^T. Lanes
   // past the item's last row read its first row and get LSE = +inf (P = 0).
@@ -787,8 +823,15 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsbuf[q][qb][e] = (__bf16)0.0f;
-  if (ntiles > 0) dma(0, 0);
-  if (ntiles > 1) dma(1, 1);
+  // Tiles J, J+1, J+2 of the pipeline.
+  TileRef t_cur{0, kv_pos0}, t_nx1{1, kv_pos0}, t_nx2{2, kv_pos0};
+  if constexpr (MKV) {
+    if (ntiles > 0) t_cur = next_tile();
+    if (ntiles > 1) t_nx1 = next_tile();
+    if (ntiles > 2) t_nx2 = next_tile();
+  }
+  if (ntiles > 0) dma(t_cur.kt, 0);
+  if (ntiles > 1) dma(t_nx1.kt, 1);
   wait_vmem_all();
   __syncthreads();
   if (ntiles > 0) {
@@ -822,8 +865,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int NPAIR = 2 * QB * 2;      // pairs of dS^T values per lane per block
 
   // One block bb = 2*J + KB (tile J, 32-key block KB; J4 = J % 4): dQ^T(bb-1)
-  // and S^T, dP^T(bb+1) on the matrix core, dS^T(bb) on the VALU.
-  auto block = [&](auto j4_tag, auto kb_tag, int bb) {
+  // and S^T, dP^T(bb+1) on the matrix core, dS^T(bb) on the VALU. sb is the
+  // block's index in storage, base the position of storage row 0 seen from it.
+  auto block = [&](auto j4_tag, auto kb_tag, int sb, int64_t base) {
     constexpr int J4 = decltype(j4_tag)::value, KB = decltype(kb_tag)::value;
     constexpr int SET = KB;                       // block parity
     constexpr int ST_PREV = KB == 0 ? (J4 + 3) % STG : J4;   // stage of block bb-1
@@ -839,12 +883,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     // Mask of block bb (diagonal or ragged blocks only): key 16*h + 4*grp + i
     // of the block is visible iff it is <= lim; masked scores become -inf
     // (P = 0).
-    const int64_t blk_plo = p.kv_pos0 + (int64_t)bb * 32;
-    const bool need_mask = (bb * 32 + 32 > p.skv) || (p.causal && blk_plo + 31 > wave_qlo);
+    const int64_t blk_plo = base + (int64_t)sb * 32;
+    const bool need_mask = (sb * 32 + 32 > p.skv) || (p.causal && blk_plo + 31 > wave_qlo);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        int lim = p.skv - 1 - bb * 32;
+        int lim = p.skv - 1 - sb * 32;
         if (p.causal) {
           const int64_t rel = qpos[qb] - blk_plo;
           lim = min(lim, (int)(rel < -1 ? -1 : (rel > 32 ? 32 : rel)));
@@ -921,11 +965,18 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // stage of tile J-2, last read in step J-1), then the tile's two blocks.
   auto tile_step = [&](auto j4_tag, int J) {
     constexpr int J4 = decltype(j4_tag)::value;
-    if (J + 2 < ntiles) dma(J + 2, (J4 + 2) % STG);
+    if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : J + 2, (J4 + 2) % STG);
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(taddr[db]));
-    block(j4_tag, IC<0>{}, 2 * J);
-    block(j4_tag, IC<1>{}, 2 * J + 1);
+    TileRef t{J, kv_pos0};
+    if constexpr (MKV) {
+      t = t_cur;
+      t_cur = t_nx1;
+      t_nx1 = t_nx2;
+      if (J + 3 < ntiles) t_nx2 = next_tile();
+    }
+    block(j4_tag, IC<0>{}, 2 * t.kt, t.base);
+    block(j4_tag, IC<1>{}, 2 * t.kt + 1, t.base);
     wait_vmem_all();
     __syncthreads();
   };
@@ -981,10 +1032,14 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
   const int64_t items = (int64_t)p.n_head_packs * p.n_q_chunks * p.tiles_per_chunk;
   if (rows > 0 && items > 0) {
     const int rb = kDqWaves / p.heads_per_item;
-    switch (rb) {
-      case 2: hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3(items), dim3(NT), 0, s, p); break;
-      case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3(items), dim3(NT), 0, s, p); break;
-      case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, 8>), dim3(items), dim3(NT), 0, s, p); break;
+    const bool mkv = p.kv.n > 1;
+    switch (rb * 2 + (mkv ? 1 : 0)) {
+      case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, false>), dim3(items), dim3(NT), 0, s, p); break;
+      case 5: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, true>), dim3(items), dim3(NT), 0, s, p); break;
+      case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, false>), dim3(items), dim3(NT), 0, s, p); break;
+      case 9: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, true>), dim3(items), dim3(NT), 0, s, p); break;
+      case 16: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, false>), dim3(items), dim3(NT), 0, s, p); break;
+      case 17: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, true>), dim3(items), dim3(NT), 0, s, p); break;
       default: return (int)hipErrorInvalidValue;
     }
   }

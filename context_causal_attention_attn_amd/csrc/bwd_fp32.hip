@@ -21,6 +21,11 @@ __device__ __forceinline__ int64_t row_pos(const BwdParams &p, int r) {
   return p.chunk_pos[r / p.chunk_len] + r % p.chunk_len;
 }
 
+// Global position of key row j (its KV chunk's position plus the offset in it).
+__device__ __forceinline__ int64_t key_pos(const BwdParams &p, int j) {
+  return p.kv.pos[j / p.kv.len] + j % p.kv.len;
+}
+
 template <int D>
 __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p) {
   const int r = blockIdx.x * 64 + threadIdx.x;   // local query row
@@ -44,7 +49,10 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
   const float *vb = static_cast<const float *>(p.v) + b * p.kv_sb + hk * p.kv_sh;
   if (lse != -INFINITY) {
     for (int j = 0; j < p.skv; ++j) {
-      if (p.causal && p.kv_pos0 + j > qp) break;
+      if (p.causal && key_pos(p, j) > qp) {
+        if (p.kv.n == 1) break;   // natural order: every later key is later still
+        continue;
+      }
       const float *kj = kb + (int64_t)j * p.kv_ss;
       const float *vj = vb + (int64_t)j * p.kv_ss;
       float s = 0.0f, dp = 0.0f;
@@ -74,7 +82,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
     dk[d] = 0.0f;
     dv[d] = 0.0f;
   }
-  const int64_t kp = p.kv_pos0 + j;
+  const int64_t kp = key_pos(p, j);
   for (int hh = 0; hh < p.group; ++hh) {
     const int h = hk * p.group + hh;
     for (int r = 0; r < p.sq; ++r) {

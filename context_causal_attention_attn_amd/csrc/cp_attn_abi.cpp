@@ -31,7 +31,6 @@ int32_t make_share(const cp_attn_desc *d, Share *s) {
   // most keys, so their work items are dispatched first (longest first).
   std::stable_sort(s->order, s->order + d->n_q_chunks,
                    [&](int a, int b) { return s->chunk_pos[a] > s->chunk_pos[b]; });
-  s->kv_pos0 = d->kv_chunk_pos[0];
   return CP_ATTN_OK;
 }
 
@@ -49,9 +48,11 @@ static int32_t validate(const cp_attn_desc *d) {
   if (d->layout == CP_ATTN_LAYOUT_CONTIGUOUS && d->n_q_chunks != 1) return CP_ATTN_ERR_BAD_LAYOUT;
   if (d->layout == CP_ATTN_LAYOUT_HEAD_TAIL && d->n_q_chunks != 2) return CP_ATTN_ERR_BAD_LAYOUT;
   if (!d->q_chunk_pos || !d->kv_chunk_pos) return CP_ATTN_ERR_NULL_PTR;
-  if (d->n_kv_chunks < 1) return CP_ATTN_ERR_BAD_LAYOUT;
-  if (d->n_kv_chunks != 1) return CP_ATTN_ERR_UNSUPPORTED;
+  if (d->n_kv_chunks < 1 || d->n_kv_chunks > CP_ATTN_MAX_KV_CHUNKS) return CP_ATTN_ERR_BAD_LAYOUT;
   if (d->sq_local % d->n_q_chunks != 0 || d->skv % d->n_kv_chunks != 0) return CP_ATTN_ERR_BAD_SHAPE;
+  // Several KV chunks: no key tile of any kernel may straddle two of them.
+  if (d->n_kv_chunks > 1 && (d->skv / d->n_kv_chunks) % CP_ATTN_KV_CHUNK_ALIGN != 0)
+    return CP_ATTN_ERR_UNSUPPORTED;
   if (d->causal != 0 && d->causal != 1) return CP_ATTN_ERR_BAD_SHAPE;
   if (!isfinite(d->softmax_scale) || !(d->softmax_scale > 0.0f)) return CP_ATTN_ERR_BAD_SHAPE;
   // Positions: non-negative, far from overflow, and the query chunks disjoint.
@@ -65,8 +66,15 @@ static int32_t validate(const cp_attn_desc *d) {
       if (L > 0 && p < o + L && o < p + L) return CP_ATTN_ERR_BAD_POSITIONS;
     }
   }
-  for (int c = 0; c < d->n_kv_chunks; ++c)
-    if (d->kv_chunk_pos[c] < 0 || d->kv_chunk_pos[c] > lim) return CP_ATTN_ERR_BAD_POSITIONS;
+  const int64_t Lkv = d->skv / d->n_kv_chunks;
+  for (int c = 0; c < d->n_kv_chunks; ++c) {
+    const int64_t p = d->kv_chunk_pos[c];
+    if (p < 0 || p > lim) return CP_ATTN_ERR_BAD_POSITIONS;
+    for (int e = 0; e < c; ++e) {
+      const int64_t o = d->kv_chunk_pos[e];
+      if (Lkv > 0 && p < o + Lkv && o < p + Lkv) return CP_ATTN_ERR_BAD_POSITIONS;
+    }
+  }
   // Strides: non-negative, and every row start 16-byte aligned given an
   // aligned base pointer (the kernels move 16-byte vectors along the dim).
   const int64_t vec = 16 / elem_bytes(d->dtype);
@@ -83,12 +91,18 @@ static int32_t validate(const cp_attn_desc *d) {
   return CP_ATTN_OK;
 }
 
+static void fill_kv_chunks(const cp_attn_desc *d, KvChunks *kv) {
+  kv->n = d->n_kv_chunks;
+  kv->len = (int32_t)(d->skv / d->n_kv_chunks);
+  for (int c = 0; c < d->n_kv_chunks; ++c) kv->pos[c] = d->kv_chunk_pos[c];
+}
+
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   memset(p, 0, sizeof(*p));
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
-  p->kv_pos0 = s.kv_pos0;
+  fill_kv_chunks(d, &p->kv);
   p->hq = d->hq;
   p->hkv = d->hkv;
   p->group = d->hq / d->hkv;
@@ -114,7 +128,7 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
-  p->kv_pos0 = s.kv_pos0;
+  fill_kv_chunks(d, &p->kv);
   p->batch = d->batch;
   p->hq = d->hq;
   p->hkv = d->hkv;
@@ -154,9 +168,9 @@ const char *cp_attn_error_string(int32_t status) {
     case CP_ATTN_OK: return "ok";
     case CP_ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
     case CP_ATTN_ERR_BAD_SHAPE: return "inconsistent sizes or strides (hq % hkv, chunk lengths, negative strides, non-finite or non-positive scale, causal flag)";
-    case CP_ATTN_ERR_BAD_LAYOUT: return "layout does not match the chunk table (contiguous: 1 Q chunk, head_tail: 2)";
+    case CP_ATTN_ERR_BAD_LAYOUT: return "layout does not match the chunk table (contiguous: 1 Q chunk, head_tail: 2; 1..64 KV chunks)";
     case CP_ATTN_ERR_BAD_POSITIONS: return "chunk positions negative, too large, or overlapping";
-    case CP_ATTN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, size, row stride (>= 2^24 elements) or KV chunk table";
+    case CP_ATTN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, size, row stride (>= 2^24 elements), or KV chunk length not a multiple of 128 with several KV chunks";
     case CP_ATTN_ERR_WORKSPACE: return "workspace missing or smaller than cp_attn_workspace_bytes()";
     case CP_ATTN_ERR_HIP: return "HIP launch or runtime error";
     case CP_ATTN_ERR_ABI: return "descriptor abi_version does not match the library";
@@ -198,20 +212,23 @@ int32_t cp_attn_share_pairs(const cp_attn_desc *d, int64_t *pairs) {
   if (st) return st;
   if (!pairs) return CP_ATTN_ERR_NULL_PTR;
   const int64_t L = d->sq_local / d->n_q_chunks;
-  const int64_t kv0 = d->kv_chunk_pos[0], skv = d->skv;
+  const int64_t skv = d->skv / d->n_kv_chunks;   // keys per KV chunk
   int64_t total = 0;
-  for (int c = 0; c < d->n_q_chunks; ++c) {
-    if (!d->causal) { total += L * skv; continue; }
-    // Row at position p sees keys kv0..min(p, kv0+skv-1): clamp(p-kv0+1, 0, skv).
-    const int64_t p0 = d->q_chunk_pos[c], p1 = p0 + L - 1;
-    // Rows with p < kv0 see nothing; rows with p >= kv0+skv-1 see all skv.
-    const int64_t a = std::max(p0, kv0), b = std::min(p1, kv0 + skv - 1);
-    if (a <= b) {
-      const int64_t n = b - a + 1, f = a - kv0 + 1;  // counts f, f+1, ..., f+n-1
-      total += n * f + n * (n - 1) / 2;
+  for (int kc = 0; kc < d->n_kv_chunks; ++kc) {
+    const int64_t kv0 = d->kv_chunk_pos[kc];
+    for (int c = 0; c < d->n_q_chunks; ++c) {
+      if (!d->causal) { total += L * skv; continue; }
+      // Row at position p sees keys kv0..min(p, kv0+skv-1): clamp(p-kv0+1, 0, skv).
+      const int64_t p0 = d->q_chunk_pos[c], p1 = p0 + L - 1;
+      // Rows with p < kv0 see nothing; rows with p >= kv0+skv-1 see all skv.
+      const int64_t a = std::max(p0, kv0), b = std::min(p1, kv0 + skv - 1);
+      if (a <= b) {
+        const int64_t n = b - a + 1, f = a - kv0 + 1;  // counts f, f+1, ..., f+n-1
+        total += n * f + n * (n - 1) / 2;
+      }
+      const int64_t full_from = std::max(p0, kv0 + skv);
+      if (full_from <= p1) total += (p1 - full_from + 1) * skv;
     }
-    const int64_t full_from = std::max(p0, kv0 + skv - 1 + 1);
-    if (full_from <= p1) total += (p1 - full_from + 1) * skv;
   }
   *pairs = total;
   return CP_ATTN_OK;
@@ -243,19 +260,24 @@ int32_t cp_attn_plan_stats_fwd(const cp_attn_desc *d, cp_attn_plan_stats *out) {
   fill_fwd_params(d, s, &p);
   const int rows = fwd_block_rows(p.group);
   const int bn = kFwdBlockKV;
+  // The kernel's visit order: per KV chunk, the prefix of its tiles that
+  // the item's last row can see.
   int64_t visits = 0, masked = 0;
   for (int c = 0; c < p.n_q_chunks; ++c)
     for (int t = 0; t < p.tiles_per_chunk; ++t) {
       const int64_t r0 = (int64_t)t * rows;
       const int64_t nrow = std::min<int64_t>(rows, p.chunk_len - r0);
       const int64_t qlo = p.chunk_pos[c] + r0, qhi = qlo + nrow - 1;
-      int64_t nvis = p.skv;
-      if (p.causal) nvis = std::min<int64_t>(p.skv, std::max<int64_t>(0, qhi - p.kv_pos0 + 1));
-      const int64_t nt = (nvis + bn - 1) / bn;
-      visits += nt;
-      for (int64_t kt = 0; kt < nt; ++kt) {
-        const int64_t klast = kt * bn + bn - 1;
-        if (klast >= p.skv || (p.causal && p.kv_pos0 + klast > qlo)) ++masked;
+      for (int kc = 0; kc < p.kv.n; ++kc) {
+        const int64_t kpos = p.kv.pos[kc], krow0 = (int64_t)kc * p.kv.len;
+        int64_t nvis = p.kv.len;
+        if (p.causal) nvis = std::min<int64_t>(p.kv.len, std::max<int64_t>(0, qhi - kpos + 1));
+        const int64_t nt = (nvis + bn - 1) / bn;
+        visits += nt;
+        for (int64_t kt = 0; kt < nt; ++kt) {
+          const int64_t klast = kt * bn + bn - 1;
+          if (krow0 + klast >= p.skv || (p.causal && kpos + klast > qlo)) ++masked;
+        }
       }
     }
   out->work_items = fwd_grid_size(p);

@@ -56,7 +56,7 @@ constexpr int UNROLL = 6;                // steps per loop trip (both ring indic
 constexpr float kSumLimit = 65536.0f;    // largest tile sum kept without a new max
 
 
-template <int D, int RB>
+template <int D, int RB, bool MKV>
 __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr int HPW = NW / RB;         // heads per work item
   constexpr int BM = kFwdWaveRows * RB;  // query rows per work item
@@ -114,12 +114,49 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     local_row[qb] = chunk * p.chunk_len + item_row0 + qrow;
   }
 
-  int nvis = p.skv;
-  if (p.causal) {
-    const int64_t n = item_qhi - p.kv_pos0 + 1;
-    nvis = (int)(n < 0 ? 0 : (n > p.skv ? p.skv : n));
+  // ---- KV tiles to visit ---------------------------------------------------
+  // Per KV chunk, the prefix of its tiles that the item's last row can see.
+  // With one chunk (MKV false: the natural order) that prefix is the whole
+  // visit list and pipeline tile j is storage tile j. With several (MKV), the
+  // pipeline runs over the chunks' prefixes one after another and a scalar
+  // cursor hands out the next tile as its storage tile and the global
+  // position of storage row 0 as seen from its chunk. The softmax state
+  // carries over between chunks, so the chunk order does not change the
+  // result.
+  auto vis_tiles = [&](int c) {
+    int nv = p.kv.len;
+    if (p.causal) {
+      const int64_t n = item_qhi - p.kv.pos[c] + 1;
+      nv = (int)(n < 0 ? 0 : (n > p.kv.len ? p.kv.len : n));
+    }
+    return (nv + BN - 1) / BN;
+  };
+  int ntiles = 0;
+  if constexpr (MKV) {
+    for (int c = 0; c < p.kv.n; ++c) ntiles += vis_tiles(c);
+  } else {
+    ntiles = vis_tiles(0);
   }
-  const int ntiles = (nvis + BN - 1) / BN;
+  const int64_t kv_pos0 = p.kv.pos[0];
+  struct TileRef {
+    int kt;          // storage tile
+    int64_t base;    // global position of storage row 0 (this tile's chunk)
+  };
+  int cur_c = 0, cur_left = vis_tiles(0), cur_kt = 0;
+  auto next_tile = [&]() -> TileRef {
+    // Called at most ntiles times, so a chunk with tiles left always follows;
+    // the bound keeps a stray call on the last chunk (its ragged-tile path
+    // clamps every row into the tensor).
+    while (cur_left == 0 && cur_c + 1 < p.kv.n) {
+      ++cur_c;
+      cur_left = vis_tiles(cur_c);
+      cur_kt = cur_c * (p.kv.len / BN);
+    }
+    const TileRef r{cur_kt, p.kv.pos[cur_c] - (int64_t)cur_c * p.kv.len};
+    ++cur_kt;
+    --cur_left;
+    return r;
+  };
 
   // ---- Q fragments (B operands of S^T = K Q^T), resident for the whole item
   bf16x8 qf[QB][KSTEPS];
@@ -294,11 +331,19 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     for (int ps = 0; ps < PSTEPS; ++ps)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pbuf[1][qb][ps][e] = (__bf16)0.0f;
-  if (ntiles > 0) {
-    dma_k(0, 0);
-    dma_v(0, 0);
+  // Tiles j, j+1, j+2 of the pipeline (step j masks tile j, prefetches V of
+  // j+1 and K of j+2).
+  TileRef t_cur{0, kv_pos0}, t_nx1{1, kv_pos0}, t_nx2{2, kv_pos0};
+  if constexpr (MKV) {
+    if (ntiles > 0) t_cur = next_tile();
+    if (ntiles > 1) t_nx1 = next_tile();
+    if (ntiles > 2) t_nx2 = next_tile();
   }
-  if (ntiles > 1) dma_k(1, 1);
+  if (ntiles > 0) {
+    dma_k(t_cur.kt, 0);
+    dma_v(t_cur.kt, 0);
+  }
+  if (ntiles > 1) dma_k(t_nx1.kt, 1);
   wait_vmem_all();
   __syncthreads();
   if (ntiles > 0) qk0(sbuf[0]);
@@ -319,8 +364,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     using VS = IC<(J6 + 2) % VSTAGES>;   // V of tile j-1
     // K of tile j+2 replaces K of tile j (read in step j-1); V of tile j+1
     // replaces V of tile j-2 (read in step j-1).
-    if (j + 2 < ntiles) dma_k(j + 2, J6 % KSTAGES);
-    if (j + 1 < ntiles) dma_v(j + 1, (J6 + 1) % VSTAGES);
+    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : j + 2, J6 % KSTAGES);
+    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : j + 1, (J6 + 1) % VSTAGES);
     // Keep the operand bases opaque per step: otherwise the compiler hoists a
     // base-plus-stage address per stage out of the loop (several times the
     // registers) instead of folding the stage into the read's immediate.
@@ -328,15 +373,23 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]));
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vaddr[db]));
-    const int64_t tile_plo = p.kv_pos0 + (int64_t)j * BN;
+    int kt = j;
+    int64_t tile_plo = kv_pos0 + (int64_t)j * BN;
+    if constexpr (MKV) {
+      kt = t_cur.kt;
+      tile_plo = t_cur.base + (int64_t)kt * BN;
+      t_cur = t_nx1;
+      t_nx1 = t_nx2;
+      if (j + 3 < ntiles) t_nx2 = next_tile();
+    }
 
     // Mask (diagonal or ragged tiles only): key 16*kb + 4*grp + i of the tile
     // is visible to a row iff it is <= that row's limit.
-    const bool need_mask = (j * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
+    const bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        int lim = p.skv - 1 - j * BN;
+        int lim = p.skv - 1 - kt * BN;
         if (p.causal) {
           const int64_t rel = qpos[qb] - tile_plo;
           lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
@@ -500,10 +553,14 @@ int launch_d(const FwdParams &p, void *stream) {
   if (grid == 0) return 0;
   const int rb = NW / p.heads_per_item;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (rb) {
-    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), dim3(grid), dim3(NT), 0, s, p); break;
+  const bool mkv = p.kv.n > 1;
+  switch (rb * 2 + (mkv ? 1 : 0)) {
+    case 4: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, false>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 5: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, true>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, false>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 9: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, true>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, false>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 17: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, true>), dim3(grid), dim3(NT), 0, s, p); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

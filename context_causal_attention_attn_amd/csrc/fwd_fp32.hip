@@ -50,37 +50,42 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
   const float scale = p.scale;
   float m = -INFINITY, l = 0.0f;
 
-  int nvis = p.skv;
-  if (p.causal) {
-    const int64_t n = qhi - p.kv_pos0 + 1;
-    nvis = (int)(n < 0 ? 0 : (n > p.skv ? p.skv : n));
-  }
   const float *kb = static_cast<const float *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const float *vb = static_cast<const float *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
-  for (int j0 = 0; j0 < nvis; j0 += kKeys) {
-    __syncthreads();
-    for (int e = t; e < kKeys * D; e += kRows) {
-      const int r = e / D, d = e % D;
-      const int key = j0 + r;
-      ks[r][d] = key < p.skv ? kb[(int64_t)key * p.kv_ss + d] : 0.0f;
-      vs[r][d] = key < p.skv ? vb[(int64_t)key * p.kv_ss + d] : 0.0f;
+  // KV chunk by KV chunk (the natural order is one chunk): the keys of chunk
+  // kc at positions kpos.. that the block's last row can see.
+  for (int kc = 0; kc < p.kv.n; ++kc) {
+    const int64_t kpos = p.kv.pos[kc];
+    const int krow0 = kc * p.kv.len;
+    int nvis = p.kv.len;
+    if (p.causal) {
+      const int64_t n = qhi - kpos + 1;
+      nvis = (int)(n < 0 ? 0 : (n > p.kv.len ? p.kv.len : n));
     }
-    __syncthreads();
-    const int nk = min(kKeys, nvis - j0);
-    for (int r = 0; r < nk; ++r) {
-      const int key = j0 + r;
-      if (p.causal && p.kv_pos0 + key > qpos) continue;
-      float s = 0.0f;
+    for (int j0 = 0; j0 < nvis; j0 += kKeys) {
+      __syncthreads();
+      for (int e = t; e < kKeys * D; e += kRows) {
+        const int r = e / D, d = e % D;
+        const int key = krow0 + j0 + r;
+        ks[r][d] = j0 + r < p.kv.len ? kb[(int64_t)key * p.kv_ss + d] : 0.0f;
+        vs[r][d] = j0 + r < p.kv.len ? vb[(int64_t)key * p.kv_ss + d] : 0.0f;
+      }
+      __syncthreads();
+      const int nk = min(kKeys, nvis - j0);
+      for (int r = 0; r < nk; ++r) {
+        if (p.causal && kpos + j0 + r > qpos) continue;
+        float s = 0.0f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[r][d], s);
-      s *= scale;
-      const float m_new = fmaxf(m, s);
-      const float alpha = expf(m - m_new);   // 0 on the first visible key
-      const float w = expf(s - m_new);
-      l = l * alpha + w;
+        for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[r][d], s);
+        s *= scale;
+        const float m_new = fmaxf(m, s);
+        const float alpha = expf(m - m_new);   // 0 on the first visible key
+        const float w = expf(s - m_new);
+        l = l * alpha + w;
 #pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = fmaf(w, vs[r][d], o[d] * alpha);
-      m = m_new;
+        for (int d = 0; d < D; ++d) o[d] = fmaf(w, vs[r][d], o[d] * alpha);
+        m = m_new;
+      }
     }
   }
   if (!valid) return;

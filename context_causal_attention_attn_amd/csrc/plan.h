@@ -16,6 +16,18 @@
 namespace cpattn {
 
 constexpr int kMaxQChunks = CP_ATTN_MAX_Q_CHUNKS;
+constexpr int kMaxKvChunks = CP_ATTN_MAX_KV_CHUNKS;
+
+// KV chunk table as the kernels see it: chunk c holds key rows
+// [c*len, (c+1)*len) at global positions pos[c] .. pos[c]+len-1. One chunk
+// (len = skv) is the natural order. With several, len is a multiple of every
+// kernel's key tile, so a key tile lies in one chunk and its positions are
+// consecutive: row j of chunk c sits at (pos[c] - c*len) + j.
+struct KvChunks {
+  int32_t n;
+  int32_t len;
+  int64_t pos[kMaxKvChunks];
+};
 
 // ---------------------------------------------------------------------------
 // Forward, bf16 MFMA kernel
@@ -35,7 +47,7 @@ struct FwdParams {
   int64_t q_sb, q_sh, q_ss;     // element strides of q (batch, head, row)
   int64_t kv_sb, kv_sh, kv_ss;  // of k and v
   int64_t o_sb, o_sh, o_ss;     // of out
-  int64_t kv_pos0;              // global position of key row 0
+  KvChunks kv;                  // positions of the key rows
   int32_t hq, hkv, group;       // group = hq / hkv
   int32_t heads_per_item;       // query heads of one KV group packed in a work item
   int32_t n_head_packs;         // batch * hq / heads_per_item
@@ -58,7 +70,6 @@ struct Share {
   int64_t chunk_len;
   int64_t chunk_pos[kMaxQChunks];   // local chunk order
   int32_t order[kMaxQChunks];       // chunk indices, latest position first
-  int64_t kv_pos0;
 };
 
 int32_t make_share(const cp_attn_desc *d, Share *s);
@@ -83,6 +94,9 @@ constexpr int kBwdBlockQ = 64;
 constexpr int kDqBlockKV = 64;    // keys per tile of the query-stationary dQ kernel
 constexpr int kDqWaveRows = 32;   // query rows per wavefront of the dQ kernel
 constexpr int kDqWaves = 8;       // wavefronts per dQ workgroup
+static_assert(CP_ATTN_KV_CHUNK_ALIGN % kBwdBlockKV == 0 && CP_ATTN_KV_CHUNK_ALIGN % kDqBlockKV == 0 &&
+                  CP_ATTN_KV_CHUNK_ALIGN % kFwdBlockKV == 0,
+              "a key tile must not straddle two KV chunks");
 // Query rows per dQ work item (per head).
 inline int dq_block_rows(int g) { return kDqWaveRows * (kDqWaves / item_heads(g)); }
 
@@ -101,7 +115,7 @@ struct BwdParams {
   int64_t q_sb, q_sh, q_ss;
   int64_t kv_sb, kv_sh, kv_ss;
   int64_t o_sb, o_sh, o_ss;     // out, dout and dq
-  int64_t kv_pos0;
+  KvChunks kv;                  // positions of the key rows
   int32_t batch, hq, hkv, group;
   int32_t sq, skv;
   int32_t chunk_len, n_q_chunks;

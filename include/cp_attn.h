@@ -45,6 +45,13 @@ extern "C" {
 
 #define CP_ATTN_ABI_VERSION 1
 #define CP_ATTN_MAX_Q_CHUNKS 16
+/* Most KV chunks a descriptor may list (a Head-Tail all-gather at cp = 32
+ * delivers 64 chunks). */
+#define CP_ATTN_MAX_KV_CHUNKS 64
+/* With more than one KV chunk, each chunk's length must be a multiple of this
+ * many rows (the largest key tile of the kernels, so no tile straddles two
+ * chunks). */
+#define CP_ATTN_KV_CHUNK_ALIGN 128
 
 /* Local row order of the query shard. */
 typedef enum {
@@ -68,7 +75,7 @@ typedef enum {
   CP_ATTN_ERR_BAD_SHAPE = -2,     /* sizes/strides inconsistent (hq % hkv, chunk lengths, ...) */
   CP_ATTN_ERR_BAD_LAYOUT = -3,    /* layout vs chunk count, or unknown layout */
   CP_ATTN_ERR_BAD_POSITIONS = -4, /* negative or overlapping chunk positions */
-  CP_ATTN_ERR_UNSUPPORTED = -5,   /* head_dim / dtype / chunk table / row stride >= 2^24 not implemented */
+  CP_ATTN_ERR_UNSUPPORTED = -5,   /* head_dim / dtype / KV chunk length / row stride >= 2^24 not implemented */
   CP_ATTN_ERR_WORKSPACE = -6,     /* workspace NULL or smaller than cp_attn_workspace_bytes() */
   CP_ATTN_ERR_HIP = -7,           /* a HIP launch or query failed */
   CP_ATTN_ERR_ABI = -8,           /* desc->abi_version != CP_ATTN_ABI_VERSION */
@@ -94,7 +101,13 @@ typedef enum {
  * c = j / Lkv (Lkv = skv / n_kv_chunks) and has global position
  * kv_chunk_pos[c] + j % Lkv. With causal != 0, key j is visible to query i iff
  * pos(j) <= pos(i) (the diagonal included); with causal == 0 every key is
- * visible. Query head h reads KV head h / (hq / hkv) (contiguous GQA groups,
+ * visible. One KV chunk is the natural order (keys at kv_chunk_pos[0],
+ * kv_chunk_pos[0]+1, ...). Several KV chunks describe K/V in any chunk order,
+ * for example straight from a Head-Tail all-gather, where rank r contributes
+ * its chunks r and 2cp-1-r ([Trainer-CP] §4.4 zigzag order): kv_chunk_pos =
+ * {0, (2cp-1)L, L, (2cp-2)L, ...}. The result does not depend on the order;
+ * dk/dv rows follow the k/v rows (storage order). KV chunk positions must be
+ * pairwise disjoint ranges. Query head h reads KV head h / (hq / hkv) (contiguous GQA groups,
  * [CP-migration] §9.2).
  *
  * The LSE is the natural log of the sum of exp(softmax_scale * q.k) over the
@@ -109,8 +122,9 @@ typedef struct cp_attn_desc {
   int64_t skv;                 /* gathered key/value rows */
   int32_t n_q_chunks;          /* 1..CP_ATTN_MAX_Q_CHUNKS, equal lengths */
   const int64_t *q_chunk_pos;  /* host array [n_q_chunks]: global position of each chunk's row 0 */
-  int32_t n_kv_chunks;         /* must be 1 (keys in natural order from kv_chunk_pos[0]) */
-  const int64_t *kv_chunk_pos; /* host array [n_kv_chunks] */
+  int32_t n_kv_chunks;         /* 1..CP_ATTN_MAX_KV_CHUNKS, equal lengths; with more than one, */
+                               /* skv / n_kv_chunks must be a multiple of CP_ATTN_KV_CHUNK_ALIGN */
+  const int64_t *kv_chunk_pos; /* host array [n_kv_chunks]: global position of each KV chunk's row 0 */
   int32_t layout;              /* cp_attn_layout: contiguous needs 1 Q chunk, head_tail needs 2 */
   int32_t causal;              /* 1: global-position causal mask, 0: no mask */
   float softmax_scale;         /* scale applied to q.k, finite and > 0 (1/sqrt(head_dim) is SDPA's default) */

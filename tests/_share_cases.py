@@ -24,18 +24,37 @@ def oracle_share(kind, S, Hq, Hkv, cp, rank, U=2):
     raise ValueError(kind)
 
 
+def gathered_key_rows(kind, S, cp, U=2):
+    """Global key rows in the order a K/V all-gather delivers them, from the
+    oracle's own chunk geometry: rank after rank of the gathering group (all
+    CP ranks, or the Colossal sub-group of a Hybrid share), each rank's chunks
+    in its local order. The global problem is in natural order, so a row
+    index is also the key's global position."""
+    group, layout = (cp // U, "contiguous") if kind == "hybrid" else (cp, kind)
+    parts = []
+    for r in range(group):
+        pos, n = oc.share_chunks(layout, S, group, r)
+        parts += [np.arange(p, p + n, dtype=np.int64) for p in pos]
+    return np.concatenate(parts)
+
+
 def to_f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def oracle_rows(prob, sh, scale, rows=None, heads=None, causal=True):
+def oracle_rows(prob, sh, scale, rows=None, heads=None, causal=True, key_rows=None):
     """Oracle out/lse of a share, optionally only for some local rows/heads.
-    Returns arrays indexed [b, local_head, local_row]."""
+    key_rows, if given, lists the global key rows in storage order (the keys
+    and their positions are taken in that order). Returns arrays indexed
+    [b, local_head, local_row]."""
     q = prob.q[:, sh["q_heads"]]
     q_pos = sh["q_pos"]
     qsel = q[:, :, torch.from_numpy(q_pos)]
     k = prob.k[:, sh["kv_heads"]]
     v = prob.v[:, sh["kv_heads"]]
+    kv_pos = sh["kv_pos"]
+    if key_rows is not None:
+        k, v, kv_pos = k[:, :, torch.from_numpy(key_rows)], v[:, :, torch.from_numpy(key_rows)], kv_pos[key_rows]
     hq_loc = len(sh["q_heads"])
     G = hq_loc // len(sh["kv_heads"])
     heads = list(range(hq_loc)) if heads is None else list(heads)
@@ -45,7 +64,7 @@ def oracle_rows(prob, sh, scale, rows=None, heads=None, causal=True):
         hk = h // G
         o, l = oc.attention_rows(to_f64(qsel[:, h:h + 1, torch.from_numpy(rows)]),
                                  to_f64(k[:, hk:hk + 1]), to_f64(v[:, hk:hk + 1]),
-                                 q_pos[rows], sh["kv_pos"], scale, causal)
+                                 q_pos[rows], kv_pos, scale, causal)
         outs.append(o[:, 0])
         lses.append(l[:, 0])
     return np.stack(outs, 1), np.stack(lses, 1)

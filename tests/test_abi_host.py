@@ -71,6 +71,10 @@ def test_validate_accepts_good_descriptors():
     assert status(desc(layout="head_tail", q_chunk_pos=[250, 1750], sq_local=500)) == 0
     assert status(desc(dtype=1, head_dim=64, q_strides=(0, 0, 64), kv_strides=(0, 0, 64), o_strides=(0, 0, 64))) == 0
     assert status(desc(sq_local=0)) == 0
+    # K/V in any chunk order: equal chunks of a multiple of 128 rows, disjoint positions.
+    assert status(desc(skv=2048, kv_chunk_pos=[1024, 0])) == 0
+    assert status(desc(skv=64 * 128, kv_chunk_pos=[128 * (63 - c) for c in range(64)])) == 0
+    assert status(desc(skv=1024, kv_chunk_pos=[0, 4096])) == 0          # gaps between chunks
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -84,7 +88,11 @@ def test_validate_accepts_good_descriptors():
     (dict(layout="head_tail", q_chunk_pos=[0, 100], sq_local=500), -4),   # overlapping chunks
     (dict(q_chunk_pos=[-1]), -4),
     (dict(layout="head_tail", q_chunk_pos=[0, 300], sq_local=501), -2),   # unequal chunks
-    (dict(kv_chunk_pos=[0, 1000]), -5),                       # KV chunk tables: not implemented
+    (dict(kv_chunk_pos=[0, 1000]), -5),                       # KV chunks of 1000 rows: not a multiple of 128
+    (dict(skv=65 * 128, kv_chunk_pos=[128 * c for c in range(65)]), -3),   # more than 64 KV chunks
+    (dict(skv=2048, kv_chunk_pos=[0, 512]), -4),               # overlapping KV chunks
+    (dict(skv=2048, kv_chunk_pos=[1024, -1024]), -4),
+    (dict(skv=2001, kv_chunk_pos=[0, 1000]), -2),              # unequal KV chunks
     (dict(softmax_scale=float("nan")), -2),
     (dict(softmax_scale=0.0), -2),
     (dict(q_strides=(8 * 2000 * 128, 2000 * 128, 132)), -9),   # row stride breaks 16-byte alignment
@@ -128,13 +136,13 @@ def _share(kind, S, cp, r, Hq, Hkv):
     return oc.hybrid_share(S, Hq, Hkv, cp, 2, r)
 
 
-def _desc_for(sh, S, Hq, Hkv, D=128, causal=True):
+def _desc_for(sh, S, Hq, Hkv, D=128, causal=True, kv_chunk_pos=(0,)):
     hq, hkv = len(sh["q_heads"]), len(sh["kv_heads"])
     n = sh["chunk_len"]
     layout = "head_tail" if len(sh["q_chunk_pos"]) == 2 else "contiguous"
     sq = n * len(sh["q_chunk_pos"])
     return desc(hq=hq, hkv=hkv, head_dim=D, sq_local=sq, skv=S, q_chunk_pos=sh["q_chunk_pos"],
-                layout=layout, causal=causal, q_strides=(0, 0, D), kv_strides=(0, 0, D), o_strides=(0, 0, D))
+                kv_chunk_pos=list(kv_chunk_pos), layout=layout, causal=causal, q_strides=(0, 0, D), kv_strides=(0, 0, D), o_strides=(0, 0, D))
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
@@ -151,6 +159,45 @@ def test_share_pairs_with_kv_offset_and_masked_rows():
     d = desc(sq_local=100, skv=50, q_chunk_pos=[10], kv_chunk_pos=[40])
     exp = oc.share_pairs(np.arange(10, 110), np.arange(40, 90), True)
     assert cp_attn_share_pairs(d) == exp
+
+
+def gathered_kv_pos(kind, S, cp):
+    """KV chunk table of an all-gather over the CP group: rank after rank, each
+    rank's chunks in its local order."""
+    out = []
+    for r in range(cp):
+        out += cp_attn_share_positions(kind, S, cp, r)[0]
+    return out
+
+
+@pytest.mark.parametrize("kind,S,cp,rank", [("head_tail", 32768, 8, 0), ("head_tail", 32768, 8, 5),
+                                            ("head_tail", 2048, 4, 3), ("contiguous", 32768, 8, 7)])
+def test_gathered_kv_order_pairs_and_schedule(kind, S, cp, rank):
+    """K/V in all-gather order: the same visible pairs as the natural order
+    (checked against the oracle with per-key positions) and the same number
+    of KV tile visits (chunk boundaries fall on tile boundaries)."""
+    sh = _share(kind, S, cp, rank, 32, 8)
+    table = gathered_kv_pos(kind, S, cp)
+    n_kv = S // len(table)
+    kv_pos = np.concatenate([np.arange(p, p + n_kv) for p in table])
+    assert sorted(kv_pos.tolist()) == list(range(S))
+    natural = _desc_for(sh, S, 32, 8)
+    gathered = _desc_for(sh, S, 32, 8, kv_chunk_pos=table)
+    for causal in (True, False):
+        d_nat = _desc_for(sh, S, 32, 8, causal=causal)
+        d_gat = _desc_for(sh, S, 32, 8, causal=causal, kv_chunk_pos=table)
+        assert cp_attn_share_pairs(d_gat) == cp_attn_share_pairs(d_nat) == \
+            oc.share_pairs(sh["q_pos"], kv_pos, causal)
+    st_n, st_g = cp_attn_plan_stats_fwd(natural), cp_attn_plan_stats_fwd(gathered)
+    assert st_g["kv_tile_visits"] == st_n["kv_tile_visits"]
+    assert st_g["masked_tile_visits"] >= st_n["masked_tile_visits"]
+
+
+def test_share_pairs_with_kv_chunk_gaps():
+    # Two KV chunks with a gap between them, listed out of order.
+    d = desc(sq_local=300, skv=256, q_chunk_pos=[100], kv_chunk_pos=[350, 0])
+    kv_pos = np.concatenate([np.arange(350, 478), np.arange(0, 128)])
+    assert cp_attn_share_pairs(d) == oc.share_pairs(np.arange(100, 400), kv_pos, True)
 
 
 def test_head_tail_tile_schedule_is_balanced():
@@ -189,3 +236,25 @@ def test_bwd_timed_rejects_bad_event_arrays_before_any_device_work():
     assert lib.cp_attn_bwd_timed(*args, ev_null, 4) == -1
     bad = desc(batch=0)
     assert lib.cp_attn_bwd_timed(bad.ref(), *args[1:], ev4, 4) == -2
+
+
+@pytest.mark.parametrize("kind,cp,U", [("head_tail", 4, 1), ("contiguous", 4, 1), ("hybrid", 4, 2)])
+def test_cut_share_gathered_kv_order(kind, cp, U):
+    """cut_share(kv_order="gathered") on CPU tensors: K/V rows are the global
+    rows at the positions the KV chunk table gives (the oracle's gathered key
+    order), every position exactly once."""
+    import torch
+    from context_causal_attention_attn_amd import cut_share
+    from tests._share_cases import gathered_key_rows
+    S = 1024
+    g = torch.Generator().manual_seed(0)
+    q = torch.randn(1, 4, S, 8, generator=g)
+    k = torch.randn(1, 2, S, 8, generator=g)
+    for r in range(cp):
+        sh = cut_share(kind, q, k, k, cp, r, ulysses=U, kv_order="gathered")
+        pos = sh.kv_positions()
+        assert sorted(pos) == list(range(S))
+        assert pos == gathered_key_rows(kind, S, cp, U).tolist()
+        assert torch.equal(sh.k, k[:, sh.kv_heads[0]:sh.kv_heads[-1] + 1][:, :, pos])
+    with pytest.raises(ValueError):
+        cut_share("ulysses", q, k, k, 2, 0, kv_order="gathered")

@@ -16,7 +16,7 @@ import torch
 import oracle.cp_share as oc
 from context_causal_attention_attn_amd import cp_attn_bwd, cp_attn_fwd, cut_share
 from synthetic import global_problem, workload
-from tests._share_cases import oracle_share, spiked_problem, to_f64
+from tests._share_cases import gathered_key_rows, oracle_share, spiked_problem, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -30,27 +30,32 @@ def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-def gpu_share_grads(prob, kind, cp, rank, U=2, causal=True):
+def gpu_share_grads(prob, kind, cp, rank, U=2, causal=True, kv_order="natural"):
     dev = torch.device("cuda")
     q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
-    sh = cut_share(kind, q, k, v, cp, rank, ulysses=U)
+    sh = cut_share(kind, q, k, v, cp, rank, ulysses=U, kv_order=kv_order)
     scale = 1.0 / math.sqrt(q.shape[-1])
     out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, causal=causal,
-                           softmax_scale=scale)
+                           softmax_scale=scale, kv_chunk_pos=sh.kv_chunk_pos)
     dout = sh.take_rows(prob.dout.to(dev))
     dq, dk, dv = cp_attn_bwd(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, layout=sh.layout,
-                             causal=causal, softmax_scale=scale)
+                             causal=causal, softmax_scale=scale, kv_chunk_pos=sh.kv_chunk_pos)
     torch.cuda.synchronize()
     return sh, dq, dk, dv, scale
 
 
-def oracle_share_grads(prob, osh, scale, causal=True):
+def oracle_share_grads(prob, osh, scale, causal=True, key_rows=None):
+    """Oracle dq, dk, dv of a share; key_rows lists the global key rows in
+    storage order (dk/dv come out in that order)."""
     qh, kh = osh["q_heads"], osh["kv_heads"]
     rows = torch.from_numpy(osh["q_pos"])
     q = to_f64(prob.q[:, qh][:, :, rows])
     do = to_f64(prob.dout[:, qh][:, :, rows])
-    k, v = to_f64(prob.k[:, kh]), to_f64(prob.v[:, kh])
-    return oc.attention_rows_bwd(q, k, v, do, osh["q_pos"], osh["kv_pos"], scale, causal)
+    k, v = prob.k[:, kh], prob.v[:, kh]
+    kv_pos = osh["kv_pos"]
+    if key_rows is not None:
+        k, v, kv_pos = k[:, :, torch.from_numpy(key_rows)], v[:, :, torch.from_numpy(key_rows)], kv_pos[key_rows]
+    return oc.attention_rows_bwd(q, to_f64(k), to_f64(v), do, osh["q_pos"], kv_pos, scale, causal)
 
 
 def check_grads(got, ref, tol, what):
@@ -104,6 +109,50 @@ def test_bf16_mid_backward_all_ranks(case):
         full = oc.contiguous_share(S, Hq, Hkv, 1, 0)
         ref_full = oracle_share_grads(prob, full, 1.0 / math.sqrt(D), causal)
         assert rel_l2(dk_sum.numpy(), ref_full[1]) <= REL_BF16
+
+
+GATHERED = [
+    # kind, S, Hq, Hkv, D, cp, causal, dtype
+    ("head_tail", 2048, 8, 2, 128, 4, True, "bf16"),
+    ("head_tail", 1024, 4, 4, 64, 4, True, "bf16"),
+    ("hybrid", 2048, 8, 2, 128, 4, True, "bf16"),
+    ("head_tail", 2048, 8, 2, 128, 4, False, "bf16"),
+    ("head_tail", 1024, 2, 2, 64, 4, True, "fp32"),
+]
+
+
+@pytest.mark.parametrize("case", GATHERED, ids=[f"{c[0]}-S{c[1]}-D{c[4]}-cp{c[5]}-{'c' if c[6] else 'nc'}-{c[7]}" for c in GATHERED])
+def test_gathered_kv_order_backward_all_ranks(case):
+    """K/V in all-gather order: dQ as in the natural order, partial dK/dV in
+    the storage order of the K/V rows."""
+    kind, S, Hq, Hkv, D, cp, causal, dtype = case
+    prob = global_problem(1, Hq, Hkv, S, D, dtype=dtype, seed=10, with_dout=True)
+    keys = gathered_key_rows(kind, S, cp)
+    tol = REL_BF16 if dtype == "bf16" else REL_FP32
+    for r in range(cp):
+        sh, dq, dk, dv, scale = gpu_share_grads(prob, kind, cp, r, causal=causal, kv_order="gathered")
+        osh = oracle_share(kind, S, Hq, Hkv, cp, r)
+        ref = oracle_share_grads(prob, osh, scale, causal, key_rows=keys)
+        check_grads((dq, dk, dv), ref, tol, f"gathered {case} r{r}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_kv_chunks_with_gap_and_invisible_chunk(dtype):
+    """The forward test's scrambled table (positions 1280, 0, 2048, 512): the
+    chunk no query sees gets exact-zero dK/dV rows."""
+    prob = global_problem(1, 4, 2, 1024, 128, dtype=dtype, seed=11, with_dout=True)
+    table = [1280, 0, 2048, 512]
+    kv_pos = np.concatenate([np.arange(p, p + 256) for p in table])
+    dev = torch.device("cuda")
+    q, k, v = prob.q[:, :, :256].to(dev), prob.k.to(dev), prob.v.to(dev)
+    do = prob.dout[:, :, :256].to(dev)
+    out, lse = cp_attn_fwd(q, k, v, [1200], kv_chunk_pos=table, softmax_scale=0.1)
+    dq, dk, dv = cp_attn_bwd(q, k, v, out, lse, do, [1200], kv_chunk_pos=table, softmax_scale=0.1)
+    torch.cuda.synchronize()
+    ref = oc.attention_rows_bwd(to_f64(prob.q[:, :, :256]), to_f64(prob.k), to_f64(prob.v),
+                                to_f64(prob.dout[:, :, :256]), np.arange(1200, 1456), kv_pos, 0.1, True)
+    check_grads((dq, dk, dv), ref, REL_BF16 if dtype == "bf16" else REL_FP32, f"kv chunk gap {dtype}")
+    assert torch.all(dk[:, :, 512:768] == 0) and torch.all(dv[:, :, 512:768] == 0)
 
 
 def test_backward_edge_cases():

@@ -15,7 +15,7 @@ import torch
 
 from context_causal_attention_attn_amd import cp_attn_fwd, cut_share
 from synthetic import global_problem, workload
-from tests._share_cases import oracle_rows, oracle_share, spiked_problem, to_f64
+from tests._share_cases import gathered_key_rows, oracle_rows, oracle_share, spiked_problem, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -23,14 +23,14 @@ OUT_TOL_BF16, LSE_TOL_BF16 = 2e-2, 1e-3
 TOL_FP32 = 1e-4
 
 
-def run_gpu_share(prob, kind, cp, rank, U=2, causal=True, scale=None):
+def run_gpu_share(prob, kind, cp, rank, U=2, causal=True, scale=None, kv_order="natural"):
     dev = torch.device("cuda")
     q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
-    sh = cut_share(kind, q, k, v, cp, rank, ulysses=U)
+    sh = cut_share(kind, q, k, v, cp, rank, ulysses=U, kv_order=kv_order)
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, causal=causal,
-                           softmax_scale=scale)
+                           softmax_scale=scale, kv_chunk_pos=sh.kv_chunk_pos)
     torch.cuda.synchronize()
     return sh, out, lse, scale
 
@@ -91,6 +91,51 @@ def test_bf16_mid_shares_all_ranks(case):
         osh = oracle_share(kind, S, Hq, Hkv, cp, r, U)
         ref_o, ref_l = oracle_rows(prob, osh, scale, causal=causal)
         check_close(out, lse, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, f"{case} r{r}")
+
+
+# K/V in the order an all-gather delivers them (several KV chunks, out of
+# position order for Head-Tail): kind, S, Hq, Hkv, D, cp, causal, dtype.
+GATHERED = [
+    ("head_tail", 2048, 8, 2, 128, 4, True, "bf16"),     # chunks 0, 7, 1, 6, ... of 256 rows
+    ("head_tail", 1024, 4, 4, 64, 4, True, "bf16"),      # 128-row chunks, MHA, D = 64
+    ("contiguous", 2048, 8, 2, 128, 4, True, "bf16"),    # 4 chunks in position order
+    ("hybrid", 2048, 8, 2, 128, 4, True, "bf16"),        # gathered over the Colossal sub-group (C = 2)
+    ("head_tail", 2048, 8, 2, 128, 4, False, "bf16"),
+    ("head_tail", 1024, 2, 2, 64, 4, True, "fp32"),
+]
+
+
+@pytest.mark.parametrize("case", GATHERED, ids=[f"{c[0]}-S{c[1]}-D{c[4]}-cp{c[5]}-{'c' if c[6] else 'nc'}-{c[7]}" for c in GATHERED])
+def test_gathered_kv_order_all_ranks(case):
+    kind, S, Hq, Hkv, D, cp, causal, dtype = case
+    prob = global_problem(1, Hq, Hkv, S, D, dtype=dtype, seed=8)
+    keys = gathered_key_rows(kind, S, cp)
+    tol = (OUT_TOL_BF16, LSE_TOL_BF16) if dtype == "bf16" else (TOL_FP32, TOL_FP32)
+    for r in range(cp):
+        sh, out, lse, scale = run_gpu_share(prob, kind, cp, r, causal=causal, kv_order="gathered")
+        assert len(sh.kv_chunk_pos) > 1
+        osh = oracle_share(kind, S, Hq, Hkv, cp, r)
+        ref_o, ref_l = oracle_rows(prob, osh, scale, causal=causal, key_rows=keys)
+        check_close(out, lse, ref_o, ref_l, *tol, f"gathered {case} r{r}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_kv_chunks_with_gap_and_invisible_chunk(dtype):
+    """Four 256-key chunks listed out of order at positions 1280, 0, 2048, 512
+    (a gap, a chunk no query sees, the causal diagonal inside the first one)
+    against 256 queries at 1200.."""
+    import oracle.cp_share as oc
+    prob = global_problem(1, 4, 2, 1024, 128, dtype=dtype, seed=9)
+    table = [1280, 0, 2048, 512]
+    kv_pos = np.concatenate([np.arange(p, p + 256) for p in table])
+    dev = torch.device("cuda")
+    q, k, v = prob.q[:, :, :256].to(dev), prob.k.to(dev), prob.v.to(dev)
+    out, lse = cp_attn_fwd(q, k, v, [1200], kv_chunk_pos=table, softmax_scale=0.1)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oc.attention_rows(to_f64(prob.q[:, :, :256]), to_f64(prob.k), to_f64(prob.v),
+                                     np.arange(1200, 1456), kv_pos, 0.1, True)
+    tol = (OUT_TOL_BF16, LSE_TOL_BF16) if dtype == "bf16" else (TOL_FP32, TOL_FP32)
+    check_close(out, lse, ref_o, ref_l, *tol, f"kv chunk gap {dtype}")
 
 
 def test_bf16_batch2_and_strided_views():
