@@ -291,6 +291,23 @@ def test_kv_permutation_invariance():
     np.testing.assert_allclose(lse2, lse, atol=1e-12)
 
 
+def test_kv_permutation_equivariance_of_backward():
+    """The backward with K/V rows permuted together with their positions: dQ
+    is unchanged and dK/dV are the natural-order rows in the permuted order
+    (the storage-order convention of the GPU path's partial dK/dV)."""
+    p = small_problem(S=24, Hq=2, Hkv=1, D=4, seed=10, dout=True)
+    q, k, v, do = _np(p.q), _np(p.k), _np(p.v), _np(p.dout)
+    sh = oc.head_tail_share(24, 2, 1, 3, 2)
+    qs, dos = q[:, :, sh["q_pos"]], do[:, :, sh["q_pos"]]
+    dq, dk, dv = oc.attention_rows_bwd(qs, k, v, dos, sh["q_pos"], sh["kv_pos"], 0.6, True)
+    perm = np.random.default_rng(4).permutation(24)
+    dq2, dk2, dv2 = oc.attention_rows_bwd(qs, k[:, :, perm], v[:, :, perm], dos, sh["q_pos"], perm, 0.6, True)
+    np.testing.assert_allclose(dq2, dq, atol=1e-12)
+    np.testing.assert_allclose(dk2, dk[:, :, perm], atol=1e-12)
+    np.testing.assert_allclose(dv2, dv[:, :, perm], atol=1e-12)
+    assert np.abs(dk).max() > 1e-3   # not vacuous
+
+
 # ----------------------------------------------------------------------------
 # Reassembly and gradient-sharding invariants
 # ----------------------------------------------------------------------------
