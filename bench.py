@@ -23,7 +23,8 @@ reads the GFX clocks and socket power three times ("clock": the read at the
 highest socket power, and every read; the chip runs at its
 power cap, well below the 2.4 GHz the peak assumes). Prints ONE JSON line.
 `--detail` adds every other share of the workload list to that line under
-"detail".
+"detail"; the Head-Tail backward shares appear twice, the second time with
+K/V in all-gather order (".../gathered_kv": a 16-entry KV chunk table).
 """
 from __future__ import annotations
 
@@ -100,17 +101,18 @@ def traffic_record(part):
     return None
 
 
-def time_share(spec, prob, rank, steps, warmup, with_bwd):
+def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", warm_s=0.0):
     import torch
     from context_causal_attention_attn_amd import api, cut_share
 
     dev = torch.device("cuda")
     q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
     kind, cp, r, U = share_for(spec, rank)
-    sh = cut_share(kind, q, k, v, cp, r, ulysses=U)
+    sh = cut_share(kind, q, k, v, cp, r, ulysses=U, kv_order=kv_order)
+    kvp = sh.kv_chunk_pos
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D)
-    d = api.make_desc(sh.q, sh.k, sh.v, sh.q.stride(), sh.q_chunk_pos, [0], sh.layout, True, scale)
+    d = api.make_desc(sh.q, sh.k, sh.v, sh.q.stride(), sh.q_chunk_pos, kvp, sh.layout, True, scale)
     pairs = api.cp_attn_share_pairs(d)
     B, Hq, Sq = sh.q.shape[0], sh.q.shape[1], sh.q.shape[2]
     Hkv, Skv = sh.k.shape[1], sh.k.shape[2]
@@ -124,20 +126,28 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd):
 
     def fwd():
         api.cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,
-                        out=out, lse=lse)
+                        out=out, lse=lse, kv_chunk_pos=kvp)
 
     def bwd(events):
         api.cp_attn_bwd_timed(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, events,
-                              layout=sh.layout, softmax_scale=scale, workspace=ws, grads=grads)
+                              layout=sh.layout, softmax_scale=scale, workspace=ws, grads=grads,
+                              kv_chunk_pos=kvp)
 
     def new_events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
-    for _ in range(warmup):
+    # `warmup` steps, then more until warm_s seconds have passed (clocks
+    # ramp up over a few hundred milliseconds after the GPU idled).
+    t_warm = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_warm < warm_s:
         ev = new_events()
         fwd()
         if dout is not None:
             bwd(ev[1:])
+        done += 1
+        if done >= warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [new_events() for _ in range(steps)]
@@ -416,10 +426,13 @@ def main():
                 continue
             bw = bool(sp.get("backward"))
             _, pr = workload(name, seed=0)
-            for r in sp["ranks"]:
+            # The Head-Tail backward shares also run with K/V in all-gather
+            # order (16 KV chunks out of position order).
+            orders = ["natural", "gathered"] if (bw and sp["kind"] == "head_tail") else ["natural"]
+            for r, order in [(r, o) for r in sp["ranks"] for o in orders]:
                 # Input generation leaves the GPU idle for seconds: warm it
-                # back up (clocks ramp over many steps) before timing.
-                rr = time_share(sp, pr, r, max(5, args.steps // 2), max(10, args.warmup), bw)
+                # back up for half a second before timing.
+                rr = time_share(sp, pr, r, max(5, args.steps // 2), args.warmup, bw, order, warm_s=0.5)
                 t = rr["ms"]
                 ent = {"fwd_ms": round(t["fwd"], 4), "fwd_tflops": round(tf(rr["flops"]["fwd"], t["fwd"]), 2),
                        "fwd_frac": round(tf(rr["flops"]["fwd"], t["fwd"]) / PEAK_BF16_TFLOPS, 4)}
@@ -428,7 +441,7 @@ def main():
                     ent.update({"bwd_ms": round(t["bwd"], 4), "bwd_tflops": round(btf, 2),
                                 "bwd_frac": round(btf / PEAK_BF16_TFLOPS, 4),
                                 "dkdv_ms": round(t["dkdv"], 4), "dq_ms": round(t["dq"], 4)})
-                detail[f"{name}/r{r}"] = ent
+                detail[f"{name}/r{r}" + ("" if order == "natural" else "/gathered_kv")] = ent
             del pr
         line["detail"] = detail
     if args.copy_calib_mib:

@@ -261,6 +261,26 @@ def test_full_size_share_sampled_rows(big_problem, kind, cp, rank):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("rank", [0, 7])
+def test_full_size_head_tail_gathered_kv_sampled_rows(big_problem, rank):
+    """The 32K Head-Tail share with K/V in all-gather order (16 chunks of 2048
+    keys at positions 0, 15L, L, 14L, ...), in the launch configuration the
+    benchmark times for the natural order: sampled rows against the oracle
+    given the same key order."""
+    spec, prob = big_problem
+    S, Hq, Hkv = spec["seq"], spec["hq"], spec["hkv"]
+    sh, out, lse, scale = run_gpu_share(prob, "head_tail", 8, rank, kv_order="gathered")
+    assert len(sh.kv_chunk_pos) == 16
+    osh = oracle_share("head_tail", S, Hq, Hkv, 8, rank)
+    rows = sample_rows(out.shape[2], 2, np.random.default_rng(100 + rank))
+    heads = [0, 13, 31]
+    ref_o, ref_l = oracle_rows(prob, osh, scale, rows=rows, heads=heads,
+                               key_rows=gathered_key_rows("head_tail", S, 8))
+    r_t = torch.from_numpy(rows).to(out.device)
+    check_close(out[:, heads][:, :, r_t], lse[:, heads][:, :, r_t], ref_o, ref_l,
+                OUT_TOL_BF16, LSE_TOL_BF16, f"32K head_tail gathered r{rank}")
+
+
 @pytest.mark.parametrize("kind,cp,rank", [("contiguous", 8, 7), ("head_tail", 8, 2)])
 def test_full_size_closed_form_uniform(big_problem, kind, cp, rank):
     """q = 0 gives uniform weights over the visible prefix: out = prefix mean
