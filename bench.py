@@ -277,8 +277,9 @@ def copy_calibration(mib):
 
 
 def cpu_baseline(spec, prob, rank):
-    """The oracle as it stands, on a bounded sample of the same share: query
-    head 0 (its KV head 0), every local row, forward + backward."""
+    """The oracle as it stands, on a bounded sample of the same share: the
+    query heads of the first GQA group (they read KV head 0), every local row,
+    forward + backward (about 10 s on 16 host threads)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -294,19 +295,20 @@ def cpu_baseline(spec, prob, rank):
         sh = oc.ulysses_share(S, Hq, Hkv, cp, r)
     else:
         sh = oc.hybrid_share(S, Hq, Hkv, cp, U, r)
+    G = len(sh["q_heads"]) // len(sh["kv_heads"])
     h, hk = int(sh["q_heads"][0]), int(sh["kv_heads"][0])
     D = spec["head_dim"]
-    q = prob.q[:1, h:h + 1].double().numpy()[:, :, sh["q_pos"]]
+    q = prob.q[:1, h:h + G].double().numpy()[:, :, sh["q_pos"]]
     k = prob.k[:1, hk:hk + 1].double().numpy()
     v = prob.v[:1, hk:hk + 1].double().numpy()
-    do = (prob.dout[:1, h:h + 1].double().numpy()[:, :, sh["q_pos"]] if prob.dout is not None
+    do = (prob.dout[:1, h:h + G].double().numpy()[:, :, sh["q_pos"]] if prob.dout is not None
           else np.random.default_rng(0).standard_normal(q.shape))
     scale = 1.0 / math.sqrt(D)
     t0 = time.perf_counter()
     oc.attention_rows_bwd(q, k, v, do, sh["q_pos"], sh["kv_pos"], scale, True)
     dt = time.perf_counter() - t0
     pairs = oc.share_pairs(sh["q_pos"], sh["kv_pos"])
-    flops = 14.0 * D * pairs   # forward (4D) + backward (10D) per visible pair
+    flops = 14.0 * D * G * pairs   # forward (4D) + backward (10D) per visible pair and head
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     cpu_model = None
     try:
@@ -319,7 +321,8 @@ def cpu_baseline(spec, prob, rank):
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "cpu_model": cpu_model,
-            "sample": f"{kind} share rank {r}: query head {h} only (1 of {len(sh['q_heads'])}), "
+            "sample": f"{kind} share rank {r}: query heads {h}..{h + G - 1} (the GQA group of KV head {hk}; "
+                      f"{G} of {len(sh['q_heads'])}), "
                       f"all {len(sh['q_pos'])} local rows, forward+backward in fp64 NumPy; "
                       f"{dt:.1f} s for {flops / 1e9:.1f} causal-effective GFLOP",
             "seconds": dt}
@@ -444,6 +447,15 @@ def main():
                 detail[f"{name}/r{r}" + ("" if order == "natural" else "/gathered_kv")] = ent
             del pr
         line["detail"] = detail
+        # Balance across the ranks of one CP layout (the Head-Tail claim):
+        # forward time of every timed rank, and the max/min spread.
+        bal = {}
+        for name, sp in WORKLOADS.items():
+            ms = [detail[f"{name}/r{r}"]["fwd_ms"] for r in sp["ranks"] if f"{name}/r{r}" in detail]
+            if len(ms) > 1:
+                bal[name] = {"fwd_ms_min": min(ms), "fwd_ms_max": max(ms),
+                             "spread": round(max(ms) / min(ms) - 1.0, 4)}
+        line["balance"] = bal
     if args.copy_calib_mib:
         copy_calibration(args.copy_calib_mib)
     if not args.no_cpu_baseline:
