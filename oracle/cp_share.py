@@ -39,6 +39,7 @@ __all__ = [
     "kv_head_of", "visible", "share_chunks", "chunk_row_positions",
     "attention_rows", "attention_rows_bwd", "contiguous_share",
     "head_tail_share", "ulysses_share", "hybrid_share", "share_pairs",
+    "ulysses_seq_to_head", "ulysses_head_to_seq",
 ]
 
 
@@ -317,3 +318,39 @@ def share_pairs(q_pos, kv_pos, causal: bool = True) -> int:
     if not causal:
         return int(q_pos.size * kv_sorted.size)
     return int(np.searchsorted(kv_sorted, q_pos, side="right").sum())
+
+
+# ----------------------------------------------------------------------------
+# Ulysses exchange (the data movement around the all-to-all)
+# ----------------------------------------------------------------------------
+def ulysses_seq_to_head(shards: Sequence[np.ndarray]) -> list:
+    """Sequence-to-head exchange of a Ulysses group of U ranks ([CP-migration]
+    §6.2: ``[B, N, S/P, D]`` -- split heads, all-to-all -> ``[B, N/P, S, D]``;
+    §6.3 runs the same exchange inside the ``cp_ulysses`` sub-group).
+
+    ``shards[p]`` is rank p's sequence shard ``[B, N, L, D]`` (rows p*L ..
+    p*L+L-1 of the group's sequence). Rank u ends up with heads
+    ``[u*N/U, (u+1)*N/U)`` of every shard, the shards in rank order along the
+    sequence: ``[B, N/U, U*L, D]``. Pure data movement, exact for any dtype.
+    """
+    U = len(shards)
+    N = shards[0].shape[1]
+    if N % U:
+        raise ValueError("the head count must divide by the Ulysses degree")
+    n = N // U
+    return [np.concatenate([shards[p][:, u * n:(u + 1) * n] for p in range(U)], axis=2)
+            for u in range(U)]
+
+
+def ulysses_head_to_seq(head_shards: Sequence[np.ndarray]) -> list:
+    """The inverse exchange ([CP-migration] §6.2 "inverse all_to_all" of the
+    output): rank u holds heads ``[u*n, (u+1)*n)`` over the group's whole
+    sequence ``[B, n, U*L, D]``; afterwards rank p holds every head of its
+    sequence shard p, ``[B, U*n, L, D]``."""
+    U = len(head_shards)
+    S = head_shards[0].shape[2]
+    if S % U:
+        raise ValueError("the sequence length must divide by the Ulysses degree")
+    L = S // U
+    return [np.concatenate([head_shards[u][:, :, p * L:(p + 1) * L] for u in range(U)], axis=1)
+            for p in range(U)]

@@ -437,3 +437,54 @@ def test_planted_head_tail_off_by_one_is_caught(monkeypatch):
         return pos, n
     monkeypatch.setattr(oc, "share_chunks", bad)
     assert _fails(test_share_geometry_golden)
+
+
+# ----------------------------------------------------------------------------
+# Ulysses exchange
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("U", [2, 4])
+def test_ulysses_exchange_matches_the_share_definition(U):
+    """Sequence shards of one global tensor, exchanged, give each rank the
+    global tensor's head slice over the whole sequence -- the Ulysses share
+    the oracle defines independently (ulysses_share) -- and the inverse
+    exchange restores the shards."""
+    rng = np.random.default_rng(U)
+    B, N, S, D = 2, 8, 24, 3
+    X = rng.standard_normal((B, N, S, D))
+    L = S // U
+    shards = [X[:, :, p * L:(p + 1) * L] for p in range(U)]
+    heads = oc.ulysses_seq_to_head(shards)
+    for u in range(U):
+        sh = oc.ulysses_share(S, N, N, U, u)
+        np.testing.assert_array_equal(heads[u], X[:, sh["q_heads"]][:, :, sh["q_pos"]])
+    back = oc.ulysses_head_to_seq(heads)
+    for p in range(U):
+        np.testing.assert_array_equal(back[p], shards[p])
+
+
+def test_ulysses_exchange_brute_force_and_hybrid_subgroup():
+    """Element by element: rank u's row p*L+t of local head h is rank p's row t
+    of global head u*N/U+h. Inside a Hybrid co-group (U = 2 of P = 4) the
+    exchange then the K/V all-gather over the co-group give hybrid_share's
+    heads and rows."""
+    rng = np.random.default_rng(7)
+    U, B, N, L, D = 3, 1, 6, 2, 2
+    shards = [rng.standard_normal((B, N, L, D)) for _ in range(U)]
+    heads = oc.ulysses_seq_to_head(shards)
+    n = N // U
+    for u in range(U):
+        for p in range(U):
+            for h in range(n):
+                for t in range(L):
+                    assert np.array_equal(heads[u][0, h, p * L + t], shards[p][0, u * n + h, t])
+    # Hybrid: P = 4 ranks, U = 2, C = 2; rank r = co*U + u holds rows of its
+    # sequence shard r (length S/P) before the exchange.
+    S, P, Uh = 16, 4, 2
+    X = rng.standard_normal((1, 4, S, 2))
+    Lr = S // P
+    for co in range(P // Uh):
+        group = [X[:, :, (co * Uh + u) * Lr:(co * Uh + u + 1) * Lr] for u in range(Uh)]
+        after = oc.ulysses_seq_to_head(group)
+        for u in range(Uh):
+            sh = oc.hybrid_share(S, 4, 4, P, Uh, co * Uh + u)
+            np.testing.assert_array_equal(after[u], X[:, sh["q_heads"]][:, :, sh["q_pos"]])
