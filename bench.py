@@ -24,7 +24,9 @@ highest socket power, and every read; the chip runs at its
 power cap, well below the 2.4 GHz the peak assumes). Prints ONE JSON line.
 `--detail` adds every other share of the workload list to that line under
 "detail"; the Head-Tail backward shares appear twice, the second time with
-K/V in all-gather order (".../gathered_kv": a 16-entry KV chunk table).
+K/V in all-gather order (".../gathered_kv": a 16-entry KV chunk table),
+and "ulysses_relayout" times the four local steps of the Ulysses exchange on
+the Ulysses workload's tensors against the HBM roofline.
 """
 from __future__ import annotations
 
@@ -55,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock/power sample")
     ap.add_argument("--detail", action="store_true", help="also time every other share")
+    ap.add_argument("--relayout-only", action="store_true",
+                    help="only time the Ulysses exchange re-layouts (prints their JSON object)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -276,6 +280,48 @@ def copy_calibration(mib):
     del src, dst
 
 
+def time_ulysses_relayout(prob, U, reps=24, sets=6):
+    """The four local steps of the Ulysses exchange on one rank's share of the
+    Ulysses workload (its sequence shard of Q [B, N, S/U, D] and, in the
+    inverse direction, a head shard [B, N/U, S, D] of the output): HIP-event
+    time per call and the HBM rate counting every byte read once and written
+    once. The calls rotate over `sets` independent buffer sets (6 x 96 MiB),
+    more than the 256 MB Infinity Cache holds, so each call streams from HBM."""
+    import torch
+    from context_causal_attention_attn_amd import (head_to_seq_pack, head_to_seq_unpack, seq_to_head_pack,
+                                                   seq_to_head_unpack)
+
+    dev = torch.device("cuda")
+    B, N, S, D = prob.q.shape
+    L = S // U
+    xs = [prob.q[:, :, :L].to(dev).contiguous() for _ in range(sets)]
+    bs = [seq_to_head_pack(x, U) for x in xs]
+    ys = [seq_to_head_unpack(b) for b in bs]
+    steps = {"seq_to_head_pack": lambda i: seq_to_head_pack(xs[i], U, out=bs[i]),
+             "seq_to_head_unpack": lambda i: seq_to_head_unpack(bs[i], out=ys[i]),
+             "head_to_seq_pack": lambda i: head_to_seq_pack(ys[i], U, out=bs[i]),
+             "head_to_seq_unpack": lambda i: head_to_seq_unpack(bs[i], out=xs[i])}
+    x = xs[0]
+    nbytes = 2 * x.numel() * x.element_size()
+    res = {}
+    for name, fn in steps.items():
+        for i in range(sets):
+            fn(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(reps):
+            fn(i % sets)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bytes": nbytes, "achieved": round(gbs, 1), "unit": "GB/s",
+                     "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return {"tensor": f"[{B}, {N}, {L}, {D}] <-> [{B}, {N // U}, {S}, {D}] {str(x.dtype).split('.')[-1]}, u = {U}",
+            "steps": res}
+
+
 def cpu_baseline(spec, prob, rank):
     """The oracle as it stands, on a bounded sample of the same share: the
     query heads of the first GQA group (they read KV head 0), every local row,
@@ -344,6 +390,12 @@ def main():
     from synthetic import WORKLOADS, workload
 
     lib = _lib.load()
+    if args.relayout_only:
+        usp, upr = workload("ulysses_cp8_s32k_gqa32x8_d128", seed=0)
+        print(json.dumps({"ulysses_relayout": time_ulysses_relayout(upr, usp["cp"])}), flush=True)
+        if args.copy_calib_mib:
+            copy_calibration(args.copy_calib_mib)
+        return
     spec, prob = workload(args.workload, seed=0)
     with_bwd = True
     if with_bwd and prob.dout is None:
@@ -456,6 +508,9 @@ def main():
                 bal[name] = {"fwd_ms_min": min(ms), "fwd_ms_max": max(ms),
                              "spread": round(max(ms) / min(ms) - 1.0, 4)}
         line["balance"] = bal
+        usp, upr = workload("ulysses_cp8_s32k_gqa32x8_d128", seed=0)
+        line["ulysses_relayout"] = time_ulysses_relayout(upr, usp["cp"])
+        del upr
     if args.copy_calib_mib:
         copy_calibration(args.copy_calib_mib)
     if not args.no_cpu_baseline:

@@ -17,3 +17,5 @@ from .api import (  # noqa: F401
     make_desc,
 )
 from .shares import Share, cut_share  # noqa: F401
+from .ulysses import (cp_attn_ulysses_relayout, head_to_seq_pack, head_to_seq_unpack,  # noqa: F401
+                      seq_to_head_pack, seq_to_head_unpack)

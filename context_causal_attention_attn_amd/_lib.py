@@ -75,7 +75,12 @@ SIGNATURES = {
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                  ctypes.POINTER(ctypes.c_void_p), _i32]),
+    "cp_attn_ulysses_relayout": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, _i32, ctypes.c_void_p,
+                                        ctypes.c_void_p, _p64, ctypes.c_void_p]),
 }
+
+ULYSSES_STEPS = {"seq_to_head_pack": 0, "seq_to_head_unpack": 1,
+                 "head_to_seq_pack": 2, "head_to_seq_unpack": 3}
 
 _lib = None
 

@@ -226,6 +226,48 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *desc, const void *q, const void *k
                           void *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
                           void *stream, void *const *events, int32_t n_events);
 
+/* ------------------------------------------------------------------------
+ * Ulysses exchange: the local steps on either side of the all-to-all
+ * ([CP-migration] §6.2: Q/K/V [B, N, S/P, D] are split by head and exchanged
+ * into [B, N/P, S, D], the output goes back by the inverse exchange; §6.3 runs
+ * the same exchange inside the Hybrid's cp_ulysses sub-group). The collective
+ * (an all_to_all_single over the u ranks of the group) moves block p of every
+ * rank's send buffer to rank p, where it lands as block "source rank". These
+ * functions are the re-layouts around it; they do not communicate.
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  CP_ATTN_ULYSSES_SEQ_TO_HEAD_PACK = 0,    /* src x,      dst blocks */
+  CP_ATTN_ULYSSES_SEQ_TO_HEAD_UNPACK = 1,  /* src blocks, dst y      */
+  CP_ATTN_ULYSSES_HEAD_TO_SEQ_PACK = 2,    /* src y,      dst blocks */
+  CP_ATTN_ULYSSES_HEAD_TO_SEQ_UNPACK = 3   /* src blocks, dst x      */
+} cp_attn_ulysses_step;
+
+/*
+ * Tensors, element type `dtype` (cp_attn_dtype), head_dim contiguous:
+ *   x       [batch, u*heads, rows, head_dim]   a rank's sequence shard, every head
+ *   y       [batch, heads, u*rows, head_dim]   its head shard over the group's sequence
+ *   blocks  [u, batch, heads, rows, head_dim]  contiguous; block p goes to / came from rank p
+ * Steps (p < u, b < batch, h < heads, t < rows):
+ *   SEQ_TO_HEAD_PACK    blocks[p][b][h][t] = x[b][p*heads + h][t]
+ *   SEQ_TO_HEAD_UNPACK  y[b][h][p*rows + t] = blocks[p][b][h][t]
+ *   HEAD_TO_SEQ_PACK    blocks[p][b][h][t] = y[b][h][p*rows + t]
+ *   HEAD_TO_SEQ_UNPACK  x[b][p*heads + h][t] = blocks[p][b][h][t]
+ * `strides` are the (batch, head, row) strides in ELEMENTS of the x or y side
+ * the step names (host array, read during the call); the blocks side is
+ * contiguous. Every row is copied bit-exactly; work is enqueued on `stream`
+ * (hipStream_t, NULL = default stream). The caller owns both buffers, which
+ * must not overlap. Errors (nothing is enqueued): CP_ATTN_ERR_BAD_LAYOUT
+ * (unknown step), CP_ATTN_ERR_BAD_SHAPE (u, batch or heads < 1, rows < 0,
+ * negative strides, overlapping buffers), CP_ATTN_ERR_UNSUPPORTED (dtype;
+ * head_dim * element size not a power of two in [16, 4096] bytes; rows >= 2^31),
+ * CP_ATTN_ERR_NULL_PTR, CP_ATTN_ERR_ALIGNMENT (pointers or strides not 16-byte
+ * multiples), CP_ATTN_ERR_HIP.
+ */
+int32_t cp_attn_ulysses_relayout(int32_t step, int32_t dtype, int32_t u, int32_t batch,
+                                 int32_t heads, int64_t rows, int32_t head_dim,
+                                 const void *src, void *dst, const int64_t *strides,
+                                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif

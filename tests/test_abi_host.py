@@ -258,3 +258,32 @@ def test_cut_share_gathered_kv_order(kind, cp, U):
         assert torch.equal(sh.k, k[:, sh.kv_heads[0]:sh.kv_heads[-1] + 1][:, :, pos])
     with pytest.raises(ValueError):
         cut_share("ulysses", q, k, k, 2, 0, kv_order="gathered")
+
+
+def _relayout_status(step=1, dtype=0, u=4, batch=1, heads=2, rows=64, head_dim=128, src=64, dst=1 << 40,
+                     strides=(2 * 256 * 128, 256 * 128, 128)):
+    st = None if strides is None else (ctypes.c_int64 * 3)(*strides)
+    return _lib.load().cp_attn_ulysses_relayout(step, dtype, u, batch, heads, rows, head_dim, src, dst, st, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(step=4), -3), (dict(step=-1), -3),                  # unknown step
+    (dict(dtype=7), -5),
+    (dict(u=0), -2), (dict(batch=0), -2), (dict(heads=0), -2), (dict(rows=-1), -2),
+    (dict(head_dim=96), -5),                                  # 192-byte rows: not a power of two
+    (dict(head_dim=4), -5),                                   # 8-byte rows: below one 16-byte vector
+    (dict(rows=2 ** 31), -5),
+    (dict(strides=None), -1),
+    (dict(strides=(-128, 128, 128)), -2),
+    (dict(strides=(128, 128, 132)), -9),                      # row stride not a 16-byte multiple
+    (dict(src=0), -1), (dict(dst=0), -1),
+    (dict(src=72), -9),                                       # misaligned pointer
+    (dict(src=1 << 40, dst=(1 << 40) + 4096), -2),            # overlapping buffers
+])
+def test_ulysses_relayout_rejects(kw, code):
+    """Every rejected call returns before any device work (no GPU here)."""
+    assert _relayout_status(**kw) == code
+
+
+def test_ulysses_relayout_empty_is_a_no_op():
+    assert _relayout_status(rows=0, src=0, dst=0) == 0
