@@ -39,7 +39,7 @@ __all__ = [
     "kv_head_of", "visible", "share_chunks", "chunk_row_positions",
     "attention_rows", "attention_rows_bwd", "contiguous_share",
     "head_tail_share", "ulysses_share", "hybrid_share", "share_pairs",
-    "ulysses_seq_to_head", "ulysses_head_to_seq",
+    "ulysses_seq_to_head", "ulysses_head_to_seq", "doc_of",
 ]
 
 
@@ -60,7 +60,17 @@ def kv_head_of(hq: int, n_q_heads: int, n_kv_heads: int) -> int:
     return hq // (n_q_heads // n_kv_heads)
 
 
-def visible(q_pos: np.ndarray, kv_pos: np.ndarray, causal: bool) -> np.ndarray:
+def doc_of(pos: np.ndarray, doc_starts: Sequence[int]) -> np.ndarray:
+    """Index of the packed sequence (document) holding each global position:
+    the sequences start at ``doc_starts`` (a global cu_seqlens without its
+    final total, [FLA-CP] §3.1), each running up to the next start. Positions
+    before the first start form document -1."""
+    return np.searchsorted(np.asarray(doc_starts, dtype=np.int64), np.asarray(pos, dtype=np.int64),
+                           side="right") - 1
+
+
+def visible(q_pos: np.ndarray, kv_pos: np.ndarray, causal: bool,
+            doc_starts: Optional[Sequence[int]] = None) -> np.ndarray:
     """Boolean [Sq, Skv]: may the query at global position q_pos[i] see the key
     at global position kv_pos[j]?
 
@@ -69,12 +79,21 @@ def visible(q_pos: np.ndarray, kv_pos: np.ndarray, causal: bool) -> np.ndarray:
     when its position is not after the query's, the diagonal included, as in
     standard ``is_causal`` attention which Ulysses keeps unchanged. Without the
     causal flag every key is visible.
+
+    With ``doc_starts`` (packed variable-length sequences, [FLA-CP] §3.1 and
+    §3.3: a global cu_seqlens partitioned across ranks) a key must also lie in
+    the query's own sequence: each sequence is causal attention on its own.
     """
     q_pos = np.asarray(q_pos, dtype=np.int64)
     kv_pos = np.asarray(kv_pos, dtype=np.int64)
     if not causal:
+        if doc_starts is not None:
+            raise ValueError("packed sequences are defined for causal attention only")
         return np.ones((q_pos.size, kv_pos.size), dtype=bool)
-    return kv_pos[None, :] <= q_pos[:, None]
+    vis = kv_pos[None, :] <= q_pos[:, None]
+    if doc_starts is not None:
+        vis &= doc_of(kv_pos, doc_starts)[None, :] == doc_of(q_pos, doc_starts)[:, None]
+    return vis
 
 
 # ----------------------------------------------------------------------------
@@ -126,7 +145,7 @@ def _as_f64(x) -> np.ndarray:
 
 
 def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
-                   row_block: int = 1024):
+                   row_block: int = 1024, doc_starts: Optional[Sequence[int]] = None):
     """Attention of local query rows against the gathered keys/values.
 
     q: [B, Hq, Sq, D]; k, v: [B, Hkv, Skv, D]; q_pos [Sq] and kv_pos [Skv] are
@@ -139,7 +158,8 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
         s_ij  = scale * sum_d q[i, d] k[j, d]
         LSE_i = ln sum_{j in A_i} exp(s_ij)      (with the row max subtracted)
         out_i = sum_{j in A_i} exp(s_ij - LSE_i) v_j
-    A row with no visible key gets out = 0 and LSE = -inf.
+    A row with no visible key gets out = 0 and LSE = -inf. ``doc_starts``
+    restricts A_i to the row's own packed sequence (see ``visible``).
 
     Rows are independent, so they are visited in blocks of ``row_block`` only to
     bound memory; nothing is reordered within a row.
@@ -158,7 +178,7 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
             hk = kv_head_of(h, Hq, Hkv)
             for r0 in range(0, Sq, row_block):
                 r1 = min(Sq, r0 + row_block)
-                vis = visible(q_pos[r0:r1], kv_pos, causal)
+                vis = visible(q_pos[r0:r1], kv_pos, causal, doc_starts)
                 s = scale * (q[b, h, r0:r1] @ k[b, hk].T)
                 s = np.where(vis, s, -np.inf)
                 m = s.max(axis=1)
@@ -177,7 +197,8 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
 # ----------------------------------------------------------------------------
 def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
                        causal: bool = True, kv_index: Optional[np.ndarray] = None,
-                       row_block: int = 1024, want_dq: bool = True):
+                       row_block: int = 1024, want_dq: bool = True,
+                       doc_starts: Optional[Sequence[int]] = None):
     """Gradients of ``sum(dout * out)`` for one share.
 
     Returns (dq [B, Hq, Sq, D], dk, dv) in float64, where dk/dv are this share's
@@ -206,7 +227,7 @@ def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
     kv_pos = np.asarray(kv_pos, dtype=np.int64)
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
-    out, lse = attention_rows(q, k, v, q_pos, kv_pos, scale, causal, row_block)
+    out, lse = attention_rows(q, k, v, q_pos, kv_pos, scale, causal, row_block, doc_starts)
     sel = np.arange(Skv) if kv_index is None else np.asarray(kv_index, dtype=np.int64)
     dq = np.zeros_like(q)
     dk = np.zeros((B, Hkv, sel.size, D))
@@ -214,7 +235,7 @@ def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
 
     def grads(qb, dob, delta, lse_b, has, pos_b, kk, vv, kpos):
         """P and dS of a block of rows against the keys kk/vv at positions kpos."""
-        vis = visible(pos_b, kpos, causal) & has[:, None]
+        vis = visible(pos_b, kpos, causal, doc_starts) & has[:, None]
         s = scale * (qb @ kk.T)
         lse_safe = np.where(has, lse_b, 0.0)
         p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
@@ -310,14 +331,21 @@ def hybrid_share(s_global: int, hq: int, hkv: int, cp_size: int, ulysses: int,
                   np.arange(co * n, (co + 1) * n), np.arange(s_global), [co * n], n)
 
 
-def share_pairs(q_pos, kv_pos, causal: bool = True) -> int:
+def share_pairs(q_pos, kv_pos, causal: bool = True, doc_starts: Optional[Sequence[int]] = None) -> int:
     """Number of visible (query, key) pairs per head: the causal work of a
-    share, which Head-Tail balancing equalises across ranks ([Trainer-CP] §0)."""
+    share, which Head-Tail balancing equalises across ranks ([Trainer-CP] §0).
+    With packed sequences a row counts only the keys of its own sequence."""
     q_pos = np.asarray(q_pos, np.int64)
     kv_sorted = np.sort(np.asarray(kv_pos, np.int64))
     if not causal:
         return int(q_pos.size * kv_sorted.size)
-    return int(np.searchsorted(kv_sorted, q_pos, side="right").sum())
+    upto = np.searchsorted(kv_sorted, q_pos, side="right")
+    if doc_starts is None:
+        return int(upto.sum())
+    starts = np.asarray(doc_starts, np.int64)
+    d = doc_of(q_pos, starts)
+    lo = np.where(d >= 0, starts[np.maximum(d, 0)], np.iinfo(np.int64).min)
+    return int((upto - np.searchsorted(kv_sorted, lo, side="left")).sum())
 
 
 # ----------------------------------------------------------------------------

@@ -411,14 +411,14 @@ def _fails(fn):
 
 
 def test_planted_strict_causal_is_caught(monkeypatch):
-    monkeypatch.setattr(oc, "visible", lambda qp, kp, c: np.asarray(kp)[None, :] < np.asarray(qp)[:, None])
+    monkeypatch.setattr(oc, "visible", lambda qp, kp, c, docs=None: np.asarray(kp)[None, :] < np.asarray(qp)[:, None])
     assert _fails(lambda: test_share_equals_rows_of_bruteforce_full("contiguous", 4, None))
 
 
 def test_planted_local_offset_is_caught(monkeypatch):
     """The bug [CP-migration] §8 warns about: masking with local row indices."""
     real = oc.visible
-    monkeypatch.setattr(oc, "visible", lambda qp, kp, c: real(np.asarray(qp) - np.asarray(qp)[0], kp, c))
+    monkeypatch.setattr(oc, "visible", lambda qp, kp, c, docs=None: real(np.asarray(qp) - np.asarray(qp)[0], kp, c, docs))
     assert _fails(lambda: test_share_equals_rows_of_bruteforce_full("contiguous", 4, None))
 
 
@@ -488,3 +488,83 @@ def test_ulysses_exchange_brute_force_and_hybrid_subgroup():
         for u in range(Uh):
             sh = oc.hybrid_share(S, 4, 4, P, Uh, co * Uh + u)
             np.testing.assert_array_equal(after[u], X[:, sh["q_heads"]][:, :, sh["q_pos"]])
+
+
+# ----------------------------------------------------------------------------
+# Packed variable-length sequences
+# ----------------------------------------------------------------------------
+PACKED = [[7, 9, 8], [24], [3, 1, 5, 2, 13], [12, 12]]
+
+
+def _starts(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)
+
+
+@pytest.mark.parametrize("lengths", PACKED, ids=["-".join(map(str, l)) for l in PACKED])
+def test_packed_sequences_are_independent_causal_attentions(lengths):
+    """Packed attention = each sequence's own causal attention (torch float64
+    SDPA on the sequence alone), forward and backward (autograd), GQA."""
+    S = 24
+    p = small_problem(Hq=4, Hkv=2, S=S, D=5, seed=21, dout=True)
+    q, k, v, do = p.q.double(), p.k.double(), p.v.double(), p.dout.double()
+    starts = _starts(lengths)
+    pos = np.arange(S)
+    out, _ = oc.attention_rows(q.numpy(), k.numpy(), v.numpy(), pos, pos, 0.7, True, doc_starts=starts)
+    dq, dk, dv = oc.attention_rows_bwd(q.numpy(), k.numpy(), v.numpy(), do.numpy(), pos, pos, 0.7, True,
+                                       doc_starts=starts)
+    qr, kr, vr = (t.clone().requires_grad_(True) for t in (q, k, v))
+    outs = []
+    for a, n in zip(starts, lengths):
+        kk = kr[:, :, a:a + n].repeat_interleave(2, dim=1)
+        vv = vr[:, :, a:a + n].repeat_interleave(2, dim=1)
+        outs.append(F.scaled_dot_product_attention(qr[:, :, a:a + n], kk, vv, is_causal=True, scale=0.7))
+    ref = torch.cat(outs, dim=2)
+    ref.backward(do)
+    np.testing.assert_allclose(out, ref.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, qr.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dk, kr.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dv, vr.grad.numpy(), atol=1e-10)
+
+
+def test_packed_closed_form_and_pair_count():
+    """Q = 0: each row averages v over its own sequence up to itself, and
+    LSE = ln(number of those keys). share_pairs counts the same keys."""
+    S, lengths = 24, [3, 1, 5, 2, 13]
+    starts = _starts(lengths)
+    p = small_problem(Hq=2, Hkv=1, S=S, D=3, seed=22)
+    v = p.v.double().numpy()
+    pos = np.arange(S)
+    out, lse = oc.attention_rows(np.zeros((1, 2, S, 3)), p.k.double().numpy(), v, pos, pos, 1.0, True,
+                                 doc_starts=starts)
+    for i in range(S):
+        a = starts[starts <= i].max()
+        np.testing.assert_allclose(out[0, :, i], np.broadcast_to(v[0, 0, a:i + 1].mean(axis=0), (2, 3)), atol=1e-13)
+        np.testing.assert_allclose(lse[0, :, i], np.log(i - a + 1), atol=1e-13)
+    brute = sum(1 for i in range(S) for j in range(S) if j <= i and starts[starts <= i].max() <= j)
+    assert oc.share_pairs(pos, pos, True, starts) == brute
+    # Keys permuted with their positions: same count.
+    perm = np.random.default_rng(3).permutation(S)
+    assert oc.share_pairs(pos[::-1], perm, True, starts) == brute
+
+
+@pytest.mark.parametrize("kind,cp", [("contiguous", 3), ("head_tail", 3)])
+def test_packed_shares_reassemble(kind, cp):
+    """Every rank's share of a packed sequence (sequences cut at rank
+    boundaries) equals the matching rows of the full packed attention."""
+    S, lengths = 24, [7, 9, 8]
+    starts = _starts(lengths)
+    p = small_problem(Hq=2, Hkv=1, S=S, D=4, seed=23)
+    q, k, v = _np(p.q), _np(p.k), _np(p.v)
+    full, full_l = oc.attention_rows(q, k, v, np.arange(S), np.arange(S), 0.5, True, doc_starts=starts)
+    for r in range(cp):
+        sh = share_of(kind, S, 2, 1, cp, r)
+        out, lse = oc.attention_rows(q[:, :, sh["q_pos"]], k, v, sh["q_pos"], sh["kv_pos"], 0.5, True,
+                                     doc_starts=starts)
+        np.testing.assert_allclose(out, full[:, :, sh["q_pos"]], atol=1e-13)
+        np.testing.assert_allclose(lse, full_l[:, :, sh["q_pos"]], atol=1e-13)
+
+
+def test_planted_sequence_boundary_off_by_one_is_caught(monkeypatch):
+    real = oc.doc_of
+    monkeypatch.setattr(oc, "doc_of", lambda pos, starts: real(np.asarray(pos) - 1, starts))
+    assert _fails(lambda: test_packed_sequences_are_independent_causal_attentions([7, 9, 8]))
