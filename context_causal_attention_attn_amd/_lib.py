@@ -13,10 +13,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # with different tuning flags); by default the in-tree build is used.
 LIB_PATH = os.environ.get("CPATTN_LIB") or os.path.join(HERE, "libcpattn.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_Q_CHUNKS = 16
 MAX_KV_CHUNKS = 64
 KV_CHUNK_ALIGN = 128
+MAX_DOC_BOUNDS = 256
 
 LAYOUT_CONTIGUOUS = 0
 LAYOUT_HEAD_TAIL = 1
@@ -44,6 +45,7 @@ class CpAttnDesc(ctypes.Structure):
         ("n_kv_chunks", _i32), ("kv_chunk_pos", _p64),
         ("layout", _i32), ("causal", _i32), ("softmax_scale", _f32),
         ("q_strides", _i64 * 3), ("kv_strides", _i64 * 3), ("o_strides", _i64 * 3),
+        ("n_docs", _i32), ("doc_starts", _p64),
     ]
 
 

@@ -35,9 +35,12 @@ class _Desc:
     """A filled cp_attn_desc plus the host arrays it points to."""
 
     def __init__(self, *, dtype, batch, hq, hkv, head_dim, sq_local, skv, q_chunk_pos,
-                 kv_chunk_pos, layout, causal, softmax_scale, q_strides, kv_strides, o_strides):
+                 kv_chunk_pos, layout, causal, softmax_scale, q_strides, kv_strides, o_strides,
+                 doc_starts=()):
         self.qpos = (ctypes.c_int64 * max(1, len(q_chunk_pos)))(*q_chunk_pos)
         self.kvpos = (ctypes.c_int64 * max(1, len(kv_chunk_pos)))(*kv_chunk_pos)
+        doc_starts = [int(x) for x in doc_starts]
+        self.docs = (ctypes.c_int64 * max(1, len(doc_starts)))(*doc_starts)
         d = CpAttnDesc()
         d.abi_version = _lib.ABI_VERSION
         d.dtype = dtype
@@ -52,6 +55,8 @@ class _Desc:
         d.softmax_scale = float(softmax_scale)
         for i in range(3):
             d.q_strides[i], d.kv_strides[i], d.o_strides[i] = q_strides[i], kv_strides[i], o_strides[i]
+        d.n_docs = len(doc_starts)
+        d.doc_starts = ctypes.cast(self.docs, ctypes.POINTER(ctypes.c_int64))
         self.desc = d
 
     def ref(self):
@@ -75,14 +80,14 @@ def _check_inputs(q, k, v):
 
 
 def make_desc(q, k, v, o_strides, q_chunk_pos: Sequence[int], kv_chunk_pos: Sequence[int],
-              layout, causal: bool, softmax_scale: Optional[float]) -> _Desc:
+              layout, causal: bool, softmax_scale: Optional[float], doc_starts: Sequence[int] = ()) -> _Desc:
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
     return _Desc(dtype=_DT.get(q.dtype, -1), batch=B, hq=Hq, hkv=Hkv, head_dim=D, sq_local=Sq, skv=Skv,
                  q_chunk_pos=list(q_chunk_pos), kv_chunk_pos=list(kv_chunk_pos), layout=layout,
                  causal=causal, softmax_scale=scale, q_strides=q.stride()[:3],
-                 kv_strides=k.stride()[:3], o_strides=tuple(o_strides)[:3])
+                 kv_strides=k.stride()[:3], o_strides=tuple(o_strides)[:3], doc_starts=doc_starts)
 
 
 def _stream_handle(t: torch.Tensor) -> int:
@@ -90,8 +95,8 @@ def _stream_handle(t: torch.Tensor) -> int:
 
 
 def cp_attn_validate(q, k, v, q_chunk_pos, *, layout="contiguous", kv_chunk_pos=(0,), causal=True,
-                     softmax_scale=None) -> None:
-    d = make_desc(q, k, v, q.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale)
+                     softmax_scale=None, doc_starts=()) -> None:
+    d = make_desc(q, k, v, q.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts)
     check(_lib.load().cp_attn_validate(d.ref()), "cp_attn_validate")
 
 
@@ -117,7 +122,7 @@ def cp_attn_plan_stats_fwd(d: _Desc) -> dict:
 def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: Sequence[int], *,
                 layout="contiguous", kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
                 softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None):
+                lse: Optional[torch.Tensor] = None, doc_starts: Sequence[int] = ()):
     """Forward of one share: returns (out [B, Hq, Sq, D] in q's dtype, lse [B, Hq, Sq] float32).
 
     q is the local query shard (rows in chunk order), k/v the gathered K/V.
@@ -126,6 +131,9 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
     each of the equal KV chunks in storage order: (p0,) for keys in natural
     order from p0, or one entry per chunk for K/V in any chunk order (e.g. as
     an all-gather delivers them; chunk length a multiple of 128 then).
+    doc_starts, if not empty, gives the global start positions of packed
+    variable-length sequences (a global cu_seqlens without its final total):
+    a key is then visible only to queries of its own sequence.
     """
     lib = _lib.load()
     _check_inputs(q, k, v)
@@ -138,7 +146,7 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
         raise ValueError("out must match q's shape, dtype and device, with a contiguous head_dim")
     if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
-    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale)
+    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts)
     check(lib.cp_attn_fwd(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), None, 0, _stream_handle(q)), "cp_attn_fwd")
     return out, lse
@@ -147,7 +155,7 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
 def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="contiguous",
                 kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
                 softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-                grads: Optional[tuple] = None):
+                grads: Optional[tuple] = None, doc_starts: Sequence[int] = ()):
     """Backward of one share: returns (dq in q's dtype, dk, dv float32 partials over the gathered K/V).
 
     grads, if given, is a (dq, dk, dv) triple of preallocated outputs: dq with
@@ -155,13 +163,13 @@ def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="
     the k/v rows (the KV chunk table's storage order).
     """
     return _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal,
-                softmax_scale, workspace, grads, None)
+                softmax_scale, workspace, grads, None, doc_starts)
 
 
 def cp_attn_bwd_timed(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], events, *,
                       layout="contiguous", kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
                       softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-                      grads: Optional[tuple] = None):
+                      grads: Optional[tuple] = None, doc_starts: Sequence[int] = ()):
     """cp_attn_bwd with four torch.cuda.Event (enable_timing=True) recorded by the
     library on the current stream around its phases (for bf16: Delta pass,
     dK/dV kernel, dQ kernel), so events[i].elapsed_time(events[i+1]) is phase i+1."""
@@ -173,11 +181,11 @@ def cp_attn_bwd_timed(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], event
             e.record(stream)
     handles = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
     return _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal,
-                softmax_scale, workspace, grads, handles)
+                softmax_scale, workspace, grads, handles, doc_starts)
 
 
 def _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal, softmax_scale,
-         workspace, grads, events):
+         workspace, grads, events, doc_starts=()):
     lib = _lib.load()
     _check_inputs(q, k, v)
     B, Hq, Sq, D = q.shape
@@ -199,7 +207,7 @@ def _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal, sof
         for t in (dk, dv):
             if t.shape != (B, Hkv, Skv, D) or t.dtype != torch.float32 or not t.is_contiguous():
                 raise ValueError("dk and dv must be contiguous float32 [B, Hkv, Skv, D] tensors")
-    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale)
+    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts)
     need = cp_attn_workspace_bytes(d, True)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

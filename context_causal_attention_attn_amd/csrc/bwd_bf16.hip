@@ -96,7 +96,9 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * 64;
 
-template <int D>
+// DOCS: packed-sequence boundaries (keys are visible only to rows of their
+// own sequence).
+template <int D, bool DOCS>
 __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdParams p) {
   constexpr int NW = kDkdvWaves;
   constexpr int NC = D / 8;
@@ -154,25 +156,56 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   const int kc = key0 / p.kv.len;
   const int64_t kv_base = p.kv.pos[kc] - (int64_t)kc * p.kv.len;
   const int64_t kv_lo = kv_base + key0;
+  // Packed sequences: a key is seen only by rows before the end of its
+  // sequence (the first bound > its position; none: +inf), per lane key
+  // (de_key), for the wave's first key (the earliest end among the wave's
+  // keys: de_wave) and the tile's last key (the latest: de_tile). The scan over
+  // the bounds is wave-uniform.
+  int64_t de_key[KN], de_wave = INT64_MAX, de_tile = INT64_MAX;
+  if constexpr (DOCS) {
+#pragma unroll
+    for (int kn = 0; kn < KN; ++kn) de_key[kn] = INT64_MAX;
+    const int64_t wave_k0 = kv_base + wkey0, tile_k1 = kv_base + key0 + BK - 1;
+    for (int i = p.docs.n - 1; i >= 0; --i) {
+      const int64_t bd = p.docs.pos[i];
+#pragma unroll
+      for (int kn = 0; kn < KN; ++kn) de_key[kn] = bd > kv_base + my_key[kn] ? bd : de_key[kn];
+      if (bd > wave_k0) de_wave = bd;
+      if (bd > tile_k1) de_tile = bd;
+    }
+  }
 
   // Query tiles this key tile meets: per chunk, tiles first_tile(c) ..
-  // nq_tiles-1, each for every head of the GQA group. A cursor walks them in
-  // that order (chunk, tile, head), one step per tile of one head.
+  // end_tile(c)-1, each for every head of the GQA group. A cursor walks them
+  // in that order (chunk, tile, head), one step per tile of one head.
   const int nq_tiles = (p.chunk_len + QT - 1) / QT;
   auto first_tile = [&](int c) {
     if (!p.causal) return 0;
     const int64_t rel = kv_lo - p.chunk_pos[c];
     return rel <= 0 ? 0 : (int)min<int64_t>(nq_tiles, rel / QT);
   };
+  auto end_tile = [&](int c) {
+    if constexpr (DOCS) {
+      if (de_tile == INT64_MAX) return nq_tiles;
+      const int64_t rel = de_tile - p.chunk_pos[c];   // rows before it may see the tile
+      const int e = rel <= 0 ? 0 : (int)min<int64_t>(nq_tiles, (rel + QT - 1) / QT);
+      return max(e, first_tile(c));
+    } else {
+      return nq_tiles;
+    }
+  };
   int total = 0;
-  for (int c = 0; c < p.n_q_chunks; ++c) total += (nq_tiles - first_tile(c)) * p.group;
+  for (int c = 0; c < p.n_q_chunks; ++c) total += (end_tile(c) - first_tile(c)) * p.group;
   struct Cursor {
     int c, t, h;       // chunk, query tile in the chunk, head in the group
     int64_t cpos;      // global position of the chunk's first row
   };
   auto next_chunk = [&](Cursor &u) {
-    int t0 = nq_tiles;
-    while (t0 >= nq_tiles && ++u.c < p.n_q_chunks) t0 = first_tile(u.c);
+    int t0 = 0, t1 = 0;
+    while (t0 >= t1 && ++u.c < p.n_q_chunks) {
+      t0 = first_tile(u.c);
+      t1 = end_tile(u.c);
+    }
     if (u.c < p.n_q_chunks) {
       u.t = t0;
       u.cpos = p.chunk_pos[u.c];
@@ -181,11 +214,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   auto advance = [&](Cursor &u) {
     if (++u.h == p.group) {
       u.h = 0;
-      if (++u.t >= nq_tiles) next_chunk(u);
+      if (++u.t >= end_tile(u.c)) next_chunk(u);
     }
   };
   Cursor c0{0, first_tile(0), 0, p.chunk_pos[0]};
-  if (c0.t >= nq_tiles) next_chunk(c0);
+  if (c0.t >= end_tile(0)) next_chunk(c0);
 
   // ---- staging: global -> LDS directly (see the forward kernel) -------------
   // Only the P wavefronts stage (the dS wavefronts carry the longer chain of
@@ -379,12 +412,19 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         // lo[kn] <= r <= hi.
         const int64_t qpos0 = cs.cpos + cs.t * QT;
         const int rows_left = p.chunk_len - 1 - cs.t * QT;
-        const bool need_mask = !wave_keys_ok || rows_left < QT - 1 ||
-                               (p.causal && kv_base + wkey0 + 31 > qpos0);
+        bool need_mask = !wave_keys_ok || rows_left < QT - 1 ||
+                         (p.causal && kv_base + wkey0 + 31 > qpos0);
+        if constexpr (DOCS) need_mask = need_mask || qpos0 + QT - 1 >= de_wave;
         if (need_mask) {
-          const int hi_g = rows_left - 4 * grp;
 #pragma unroll
           for (int kn = 0; kn < KN; ++kn) {
+            int hi = rows_left;
+            if constexpr (DOCS) {
+              // ... and rows before the end of the key's sequence.
+              const int64_t e = de_key[kn] - qpos0 - 1;
+              hi = (int)min<int64_t>(hi, e < -1 ? -1 : e);
+            }
+            const int hi_g = hi - 4 * grp;
             int lo = 0;
             if (p.causal) {
               const int64_t r = kv_base + my_key[kn] - qpos0;
@@ -605,8 +645,12 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 // over 32-key blocks: in block b the matrix core computes dQ^T of block b-1
 // and S^T, dP^T of block b+1 while the vector ALU forms dS^T of block b; one
 // barrier per 64-key tile.
-template <int D, int RB, bool MKV>
+// MODE 0: keys in natural order; 1: several KV chunks; 2: natural order with
+// packed-sequence boundaries.
+template <int D, int RB, int MODE>
 __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
+  constexpr bool MKV = MODE == 1;
+  constexpr bool DOCS = MODE == 2;
   constexpr int HPW = kDqWaves / RB;
   constexpr int BM = kDqWaveRows * RB;
   constexpr int NC = D / 8;
@@ -681,6 +725,32 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     ntiles = vis_tiles(0);
   }
   const int64_t kv_pos0 = p.kv.pos[0];
+  // Packed sequences, as in the forward kernel: this lane's rows see keys
+  // from their sequence's start (lo_key, a key row index); the item skips the
+  // tiles before its first row's sequence start (t0); a block that starts
+  // before the wave's last row's sequence start (wave_ds) is masked.
+  int t0 = 0;
+  int lo_key[QB];
+  int64_t wave_ds = INT64_MIN;
+  if constexpr (DOCS) {
+    int64_t ds[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ds[qb] = INT64_MIN;
+    int64_t item_ds = INT64_MIN;
+    const int64_t item_qlo = chunk_pos + item_row0;
+    const int64_t wave_qhi = wave_qlo + max(wrows - 1, 0);
+    for (int i = 0; i < p.docs.n; ++i) {
+      const int64_t bd = p.docs.pos[i];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) ds[qb] = bd <= qpos[qb] ? bd : ds[qb];
+      if (bd <= item_qlo) item_ds = bd;
+      if (bd <= wave_qhi) wave_ds = bd;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lo_key[qb] = ds[qb] > kv_pos0 ? (int)min<int64_t>(ds[qb] - kv_pos0, p.skv) : 0;
+    if (item_ds > kv_pos0) t0 = (int)min<int64_t>(ntiles, (item_ds - kv_pos0) / BN);
+    ntiles -= t0;
+  }
   struct TileRef {
     int kt;
     int64_t base;
@@ -824,7 +894,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsbuf[q][qb][e] = (__bf16)0.0f;
   // Tiles J, J+1, J+2 of the pipeline.
-  TileRef t_cur{0, kv_pos0}, t_nx1{1, kv_pos0}, t_nx2{2, kv_pos0};
+  TileRef t_cur{t0, kv_pos0}, t_nx1{t0 + 1, kv_pos0}, t_nx2{t0 + 2, kv_pos0};
   if constexpr (MKV) {
     if (ntiles > 0) t_cur = next_tile();
     if (ntiles > 1) t_nx1 = next_tile();
@@ -884,7 +954,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     // of the block is visible iff it is <= lim; masked scores become -inf
     // (P = 0).
     const int64_t blk_plo = base + (int64_t)sb * 32;
-    const bool need_mask = (sb * 32 + 32 > p.skv) || (p.causal && blk_plo + 31 > wave_qlo);
+    bool need_mask = (sb * 32 + 32 > p.skv) || (p.causal && blk_plo + 31 > wave_qlo);
+    if constexpr (DOCS) need_mask = need_mask || blk_plo < wave_ds;
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -894,10 +965,20 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
           lim = min(lim, (int)(rel < -1 ? -1 : (rel > 32 ? 32 : rel)));
         }
         const int t = lim - 4 * grp;
+        if constexpr (DOCS) {
+          // ... and >= the row's sequence start.
+          const int tl = min(max(lo_key[qb] - sb * 32, 0), 32) - 4 * grp;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) scur[h][qb][i] = (16 * h + i > t) ? -INFINITY : scur[h][qb][i];
+            for (int i = 0; i < 4; ++i)
+              scur[h][qb][i] = (16 * h + i > t || 16 * h + i < tl) ? -INFINITY : scur[h][qb][i];
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) scur[h][qb][i] = (16 * h + i > t) ? -INFINITY : scur[h][qb][i];
+        }
       }
     }
     // Operand o (used by both row blocks in consecutive slots): o < NDQ is
@@ -965,10 +1046,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // stage of tile J-2, last read in step J-1), then the tile's two blocks.
   auto tile_step = [&](auto j4_tag, int J) {
     constexpr int J4 = decltype(j4_tag)::value;
-    if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : J + 2, (J4 + 2) % STG);
+    if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : t0 + J + 2, (J4 + 2) % STG);
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(taddr[db]));
-    TileRef t{J, kv_pos0};
+    TileRef t{t0 + J, kv_pos0};
     if constexpr (MKV) {
       t = t_cur;
       t_cur = t_nx1;
@@ -1026,20 +1107,26 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
   if (int e = mark(1)) return e;
   const int64_t kv_tiles = (p.skv + BK - 1) / BK;
   if (kv_tiles > 0) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(kv_tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
+    if (p.docs.n > 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(kv_tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(kv_tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
   }
   if (int e = mark(2)) return e;
   const int64_t items = (int64_t)p.n_head_packs * p.n_q_chunks * p.tiles_per_chunk;
   if (rows > 0 && items > 0) {
     const int rb = kDqWaves / p.heads_per_item;
-    const bool mkv = p.kv.n > 1;
-    switch (rb * 2 + (mkv ? 1 : 0)) {
-      case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, false>), dim3(items), dim3(NT), 0, s, p); break;
-      case 5: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, true>), dim3(items), dim3(NT), 0, s, p); break;
-      case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, false>), dim3(items), dim3(NT), 0, s, p); break;
-      case 9: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, true>), dim3(items), dim3(NT), 0, s, p); break;
-      case 16: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, false>), dim3(items), dim3(NT), 0, s, p); break;
-      case 17: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, true>), dim3(items), dim3(NT), 0, s, p); break;
+    const int mode = p.docs.n > 0 ? 2 : (p.kv.n > 1 ? 1 : 0);
+    switch (rb * 4 + mode) {
+      case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, 0>), dim3(items), dim3(NT), 0, s, p); break;
+      case 9: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, 1>), dim3(items), dim3(NT), 0, s, p); break;
+      case 10: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, 2>), dim3(items), dim3(NT), 0, s, p); break;
+      case 16: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, 0>), dim3(items), dim3(NT), 0, s, p); break;
+      case 17: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, 1>), dim3(items), dim3(NT), 0, s, p); break;
+      case 18: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, 2>), dim3(items), dim3(NT), 0, s, p); break;
+      case 32: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, 0>), dim3(items), dim3(NT), 0, s, p); break;
+      case 33: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, 1>), dim3(items), dim3(NT), 0, s, p); break;
+      case 34: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, 2>), dim3(items), dim3(NT), 0, s, p); break;
       default: return (int)hipErrorInvalidValue;
     }
   }

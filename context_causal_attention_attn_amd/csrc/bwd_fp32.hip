@@ -26,6 +26,15 @@ __device__ __forceinline__ int64_t key_pos(const BwdParams &p, int j) {
   return p.kv.pos[j / p.kv.len] + j % p.kv.len;
 }
 
+// Start of the packed sequence holding position pos (the last bound <= pos;
+// INT64_MIN without bounds). The loop runs over every bound, so it is uniform
+// across threads whatever pos is.
+__device__ __forceinline__ int64_t seq_start(const BwdParams &p, int64_t pos) {
+  int64_t ds = INT64_MIN;
+  for (int i = 0; i < p.docs.n; ++i) ds = p.docs.pos[i] <= pos ? p.docs.pos[i] : ds;
+  return ds;
+}
+
 template <int D>
 __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p) {
   const int r = blockIdx.x * 64 + threadIdx.x;   // local query row
@@ -45,6 +54,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
   float dq[D];
   for (int d = 0; d < D; ++d) dq[d] = 0.0f;
   const int64_t qp = row_pos(p, r);
+  const int64_t qds = seq_start(p, qp);
   const float *kb = static_cast<const float *>(p.k) + b * p.kv_sb + hk * p.kv_sh;
   const float *vb = static_cast<const float *>(p.v) + b * p.kv_sb + hk * p.kv_sh;
   if (lse != -INFINITY) {
@@ -53,6 +63,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
         if (p.kv.n == 1) break;   // natural order: every later key is later still
         continue;
       }
+      if (key_pos(p, j) < qds) continue;   // before this row's sequence
       const float *kj = kb + (int64_t)j * p.kv_ss;
       const float *vj = vb + (int64_t)j * p.kv_ss;
       float s = 0.0f, dp = 0.0f;
@@ -87,6 +98,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
     const int h = hk * p.group + hh;
     for (int r = 0; r < p.sq; ++r) {
       if (p.causal && kp > row_pos(p, r)) continue;
+      if (kp < seq_start(p, row_pos(p, r))) continue;   // not in the row's sequence
       const int64_t row = ((int64_t)b * p.hq + h) * p.sq + r;
       const float lse = p.lse[row];
       if (lse == -INFINITY) continue;

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "cp_attn.h"
 #include "plan.h"
@@ -31,6 +32,36 @@ int32_t make_share(const cp_attn_desc *d, Share *s) {
   // most keys, so their work items are dispatched first (longest first).
   std::stable_sort(s->order, s->order + d->n_q_chunks,
                    [&](int a, int b) { return s->chunk_pos[a] > s->chunk_pos[b]; });
+  return CP_ATTN_OK;
+}
+
+// The sequence boundaries that can decide anything for this share: per query
+// chunk [lo, hi], the last start <= lo (its first rows' sequence), every start
+// in (lo, hi], and the first start > hi (where the sequence of the chunk's last
+// rows, and of every key visible to the chunk, ends). A query's sequence start
+// is the last kept bound <= it; a key visible to some local query ends its
+// sequence at the first kept bound > it (keys of sequences no local row
+// touches are cut off by the query side). Ascending, duplicates dropped.
+int32_t collect_doc_bounds(const cp_attn_desc *d, DocBounds *out) {
+  out->n = 0;
+  if (d->n_docs <= 0) return CP_ATTN_OK;
+  const int64_t *b = d->doc_starts, *e = d->doc_starts + d->n_docs;
+  const int64_t L = d->sq_local / d->n_q_chunks;
+  std::vector<int64_t> keep;
+  for (int c = 0; c < d->n_q_chunks; ++c) {
+    if (L == 0) break;
+    const int64_t lo = d->q_chunk_pos[c], hi = lo + L - 1;
+    const int64_t *first_after_lo = std::upper_bound(b, e, lo);
+    if (first_after_lo != b) keep.push_back(*(first_after_lo - 1));
+    const int64_t *first_after_hi = std::upper_bound(b, e, hi);
+    keep.insert(keep.end(), first_after_lo, first_after_hi);
+    if (first_after_hi != e) keep.push_back(*first_after_hi);
+  }
+  std::sort(keep.begin(), keep.end());
+  keep.erase(std::unique(keep.begin(), keep.end()), keep.end());
+  if ((int64_t)keep.size() > kMaxDocBounds) return CP_ATTN_ERR_UNSUPPORTED;
+  out->n = (int32_t)keep.size();
+  for (size_t i = 0; i < keep.size(); ++i) out->pos[i] = keep[i];
   return CP_ATTN_OK;
 }
 
@@ -75,6 +106,18 @@ static int32_t validate(const cp_attn_desc *d) {
       if (Lkv > 0 && p < o + Lkv && o < p + Lkv) return CP_ATTN_ERR_BAD_POSITIONS;
     }
   }
+  // Packed sequences: causal only, natural key order, ascending starts.
+  if (d->n_docs < 0) return CP_ATTN_ERR_BAD_SHAPE;
+  if (d->n_docs > 0) {
+    if (!d->doc_starts) return CP_ATTN_ERR_NULL_PTR;
+    if (!d->causal || d->n_kv_chunks != 1) return CP_ATTN_ERR_UNSUPPORTED;
+    for (int i = 0; i < d->n_docs; ++i) {
+      const int64_t p = d->doc_starts[i];
+      if (p < 0 || p > lim || (i > 0 && p <= d->doc_starts[i - 1])) return CP_ATTN_ERR_BAD_POSITIONS;
+    }
+    DocBounds db;
+    if (collect_doc_bounds(d, &db) != CP_ATTN_OK) return CP_ATTN_ERR_UNSUPPORTED;
+  }
   // Strides: non-negative, and every row start 16-byte aligned given an
   // aligned base pointer (the kernels move 16-byte vectors along the dim).
   const int64_t vec = 16 / elem_bytes(d->dtype);
@@ -99,6 +142,7 @@ static void fill_kv_chunks(const cp_attn_desc *d, KvChunks *kv) {
 
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   memset(p, 0, sizeof(*p));
+  collect_doc_bounds(d, &p->docs);
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
@@ -125,6 +169,7 @@ void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
 
 void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
   memset(p, 0, sizeof(*p));
+  collect_doc_bounds(d, &p->docs);
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
@@ -214,6 +259,21 @@ int32_t cp_attn_share_pairs(const cp_attn_desc *d, int64_t *pairs) {
   const int64_t L = d->sq_local / d->n_q_chunks;
   const int64_t skv = d->skv / d->n_kv_chunks;   // keys per KV chunk
   int64_t total = 0;
+  if (d->n_docs > 0) {
+    // Row at position p sees keys max(kv0, start of its sequence) .. min(p, kv0+skv-1).
+    const int64_t kv0 = d->kv_chunk_pos[0];
+    const int64_t *b = d->doc_starts, *e = d->doc_starts + d->n_docs;
+    for (int c = 0; c < d->n_q_chunks; ++c)
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t p = d->q_chunk_pos[c] + t;
+        const int64_t *up = std::upper_bound(b, e, p);
+        const int64_t lo = std::max(kv0, up == b ? kv0 : *(up - 1));
+        const int64_t hi = std::min(p, kv0 + skv - 1);
+        if (hi >= lo) total += hi - lo + 1;
+      }
+    *pairs = total;
+    return CP_ATTN_OK;
+  }
   for (int kc = 0; kc < d->n_kv_chunks; ++kc) {
     const int64_t kv0 = d->kv_chunk_pos[kc];
     for (int c = 0; c < d->n_q_chunks; ++c) {
@@ -268,15 +328,24 @@ int32_t cp_attn_plan_stats_fwd(const cp_attn_desc *d, cp_attn_plan_stats *out) {
       const int64_t r0 = (int64_t)t * rows;
       const int64_t nrow = std::min<int64_t>(rows, p.chunk_len - r0);
       const int64_t qlo = p.chunk_pos[c] + r0, qhi = qlo + nrow - 1;
+      // Packed sequences: tiles before the sequence start of the item's first
+      // row are skipped; a tile starting before the last row's sequence start
+      // is masked.
+      int64_t ds_first = INT64_MIN, ds_last = INT64_MIN;
+      for (int i = 0; i < p.docs.n; ++i) {
+        if (p.docs.pos[i] <= qlo) ds_first = p.docs.pos[i];
+        if (p.docs.pos[i] <= qhi) ds_last = p.docs.pos[i];
+      }
       for (int kc = 0; kc < p.kv.n; ++kc) {
         const int64_t kpos = p.kv.pos[kc], krow0 = (int64_t)kc * p.kv.len;
         int64_t nvis = p.kv.len;
         if (p.causal) nvis = std::min<int64_t>(p.kv.len, std::max<int64_t>(0, qhi - kpos + 1));
         const int64_t nt = (nvis + bn - 1) / bn;
-        visits += nt;
-        for (int64_t kt = 0; kt < nt; ++kt) {
+        const int64_t t0 = ds_first > kpos ? std::min<int64_t>(nt, (ds_first - kpos) / bn) : 0;
+        visits += nt - t0;
+        for (int64_t kt = t0; kt < nt; ++kt) {
           const int64_t klast = kt * bn + bn - 1;
-          if (krow0 + klast >= p.skv || (p.causal && kpos + klast > qlo)) ++masked;
+          if (krow0 + klast >= p.skv || (p.causal && kpos + klast > qlo) || kpos + kt * bn < ds_last) ++masked;
         }
       }
     }

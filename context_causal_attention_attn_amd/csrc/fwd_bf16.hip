@@ -56,8 +56,12 @@ constexpr int UNROLL = 6;                // steps per loop trip (both ring indic
 constexpr float kSumLimit = 65536.0f;    // largest tile sum kept without a new max
 
 
-template <int D, int RB, bool MKV>
+// MODE 0: keys in natural order (one KV chunk); 1: several KV chunks; 2:
+// natural order with packed-sequence boundaries.
+template <int D, int RB, int MODE>
 __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
+  constexpr bool MKV = MODE == 1;
+  constexpr bool DOCS = MODE == 2;
   constexpr int HPW = NW / RB;         // heads per work item
   constexpr int BM = kFwdWaveRows * RB;  // query rows per work item
   constexpr int NC = D / 8;            // 16-byte chunks per row
@@ -116,7 +120,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 
   // ---- KV tiles to visit ---------------------------------------------------
   // Per KV chunk, the prefix of its tiles that the item's last row can see.
-  // With one chunk (MKV false: the natural order) that prefix is the whole
+  // With one chunk (MODE 0 and 2: the natural order) that prefix is the whole
   // visit list and pipeline tile j is storage tile j. With several (MKV), the
   // pipeline runs over the chunks' prefixes one after another and a scalar
   // cursor hands out the next tile as its storage tile and the global
@@ -138,6 +142,33 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     ntiles = vis_tiles(0);
   }
   const int64_t kv_pos0 = p.kv.pos[0];
+  // Packed sequences: each of this lane's rows sees keys from its sequence's
+  // start (the last bound <= its position) on, as a key row index (lo_key);
+  // the item skips the tiles before its first row's sequence start (t0), and a
+  // tile that starts before the wave's last row's sequence start (wave_ds) is
+  // masked. The scan over the bounds is wave-uniform.
+  int t0 = 0;
+  int lo_key[QB];
+  int64_t wave_ds = INT64_MIN;
+  if constexpr (DOCS) {
+    int64_t ds[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ds[qb] = INT64_MIN;
+    int64_t item_ds = INT64_MIN;
+    const int64_t item_qlo = chunk_pos + item_row0;
+    const int64_t wave_qhi = chunk_pos + item_row0 + min(wrow0 + kFwdWaveRows, item_rows) - 1;
+    for (int i = 0; i < p.docs.n; ++i) {
+      const int64_t bd = p.docs.pos[i];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) ds[qb] = bd <= qpos[qb] ? bd : ds[qb];
+      if (bd <= item_qlo) item_ds = bd;
+      if (bd <= wave_qhi) wave_ds = bd;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lo_key[qb] = ds[qb] > kv_pos0 ? (int)min<int64_t>(ds[qb] - kv_pos0, p.skv) : 0;
+    if (item_ds > kv_pos0) t0 = (int)min<int64_t>(ntiles, (item_ds - kv_pos0) / BN);
+    ntiles -= t0;
+  }
   struct TileRef {
     int kt;          // storage tile
     int64_t base;    // global position of storage row 0 (this tile's chunk)
@@ -333,7 +364,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       for (int e = 0; e < 8; ++e) pbuf[1][qb][ps][e] = (__bf16)0.0f;
   // Tiles j, j+1, j+2 of the pipeline (step j masks tile j, prefetches V of
   // j+1 and K of j+2).
-  TileRef t_cur{0, kv_pos0}, t_nx1{1, kv_pos0}, t_nx2{2, kv_pos0};
+  TileRef t_cur{t0, kv_pos0}, t_nx1{t0 + 1, kv_pos0}, t_nx2{t0 + 2, kv_pos0};
   if constexpr (MKV) {
     if (ntiles > 0) t_cur = next_tile();
     if (ntiles > 1) t_nx1 = next_tile();
@@ -364,8 +395,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     using VS = IC<(J6 + 2) % VSTAGES>;   // V of tile j-1
     // K of tile j+2 replaces K of tile j (read in step j-1); V of tile j+1
     // replaces V of tile j-2 (read in step j-1).
-    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : j + 2, J6 % KSTAGES);
-    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : j + 1, (J6 + 1) % VSTAGES);
+    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : t0 + j + 2, J6 % KSTAGES);
+    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : t0 + j + 1, (J6 + 1) % VSTAGES);
     // Keep the operand bases opaque per step: otherwise the compiler hoists a
     // base-plus-stage address per stage out of the loop (several times the
     // registers) instead of folding the stage into the read's immediate.
@@ -373,8 +404,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]));
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vaddr[db]));
-    int kt = j;
-    int64_t tile_plo = kv_pos0 + (int64_t)j * BN;
+    int kt = t0 + j;
+    int64_t tile_plo = kv_pos0 + (int64_t)kt * BN;
     if constexpr (MKV) {
       kt = t_cur.kt;
       tile_plo = t_cur.base + (int64_t)kt * BN;
@@ -385,7 +416,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 
     // Mask (diagonal or ragged tiles only): key 16*kb + 4*grp + i of the tile
     // is visible to a row iff it is <= that row's limit.
-    const bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
+    bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
+    if constexpr (DOCS) need_mask = need_mask || tile_plo < wave_ds;
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -395,11 +427,21 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
           lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
         }
         const int t = lim - 4 * grp;
+        if constexpr (DOCS) {
+          // ... and >= the row's sequence start.
+          const int tl = min(max(lo_key[qb] - kt * BN, 0), BN) - 4 * grp;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+          for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sacc[qb][kb][i] = (16 * kb + i > t) ? -INFINITY : sacc[qb][kb][i];
+            for (int i = 0; i < 4; ++i)
+              sacc[qb][kb][i] = (16 * kb + i > t || 16 * kb + i < tl) ? -INFINITY : sacc[qb][kb][i];
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sacc[qb][kb][i] = (16 * kb + i > t) ? -INFINITY : sacc[qb][kb][i];
+        }
       }
     }
 
@@ -553,14 +595,17 @@ int launch_d(const FwdParams &p, void *stream) {
   if (grid == 0) return 0;
   const int rb = NW / p.heads_per_item;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool mkv = p.kv.n > 1;
-  switch (rb * 2 + (mkv ? 1 : 0)) {
-    case 4: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, false>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 5: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, true>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, false>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 9: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, true>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, false>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 17: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, true>), dim3(grid), dim3(NT), 0, s, p); break;
+  const int mode = p.docs.n > 0 ? 2 : (p.kv.n > 1 ? 1 : 0);
+  switch (rb * 4 + mode) {
+    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 0>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 9: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 1>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 10: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 0>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 17: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 1>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 18: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 2>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 0>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 33: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 1>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 34: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 2>), dim3(grid), dim3(NT), 0, s, p); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -49,6 +49,10 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
   }
   const float scale = p.scale;
   float m = -INFINITY, l = 0.0f;
+  // Packed sequences: keys before the start of this row's sequence (the last
+  // bound <= its position; the scan is uniform over the block) are hidden.
+  int64_t ds = INT64_MIN;
+  for (int i = 0; i < p.docs.n; ++i) ds = p.docs.pos[i] <= qpos ? p.docs.pos[i] : ds;
 
   const float *kb = static_cast<const float *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const float *vb = static_cast<const float *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
@@ -73,7 +77,7 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
       __syncthreads();
       const int nk = min(kKeys, nvis - j0);
       for (int r = 0; r < nk; ++r) {
-        if (p.causal && kpos + j0 + r > qpos) continue;
+        if (p.causal && (kpos + j0 + r > qpos || kpos + j0 + r < ds)) continue;
         float s = 0.0f;
 #pragma unroll
         for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[r][d], s);

@@ -18,6 +18,16 @@ namespace cpattn {
 constexpr int kMaxQChunks = CP_ATTN_MAX_Q_CHUNKS;
 constexpr int kMaxKvChunks = CP_ATTN_MAX_KV_CHUNKS;
 
+// Packed-sequence boundaries a share can meet (global positions, ascending).
+// Query row q's sequence starts at the last bound <= q (none: -inf); key k's
+// sequence ends before the first bound > k (none: +inf). The host keeps every
+// bound that can decide either for this share.
+constexpr int kMaxDocBounds = CP_ATTN_MAX_DOC_BOUNDS;
+struct DocBounds {
+  int32_t n;
+  int64_t pos[kMaxDocBounds];
+};
+
 // KV chunk table as the kernels see it: chunk c holds key rows
 // [c*len, (c+1)*len) at global positions pos[c] .. pos[c]+len-1. One chunk
 // (len = skv) is the natural order. With several, len is a multiple of every
@@ -48,6 +58,7 @@ struct FwdParams {
   int64_t kv_sb, kv_sh, kv_ss;  // of k and v
   int64_t o_sb, o_sh, o_ss;     // of out
   KvChunks kv;                  // positions of the key rows
+  DocBounds docs;               // packed-sequence boundaries (n = 0: none)
   int32_t hq, hkv, group;       // group = hq / hkv
   int32_t heads_per_item;       // query heads of one KV group packed in a work item
   int32_t n_head_packs;         // batch * hq / heads_per_item
@@ -73,6 +84,7 @@ struct Share {
 };
 
 int32_t make_share(const cp_attn_desc *d, Share *s);
+int32_t collect_doc_bounds(const cp_attn_desc *d, DocBounds *out);
 
 // Heads packed per work item of the query-stationary kernels (forward, dQ)
 // for a GQA group of size g: a divisor of g, at most 4.
@@ -116,6 +128,7 @@ struct BwdParams {
   int64_t kv_sb, kv_sh, kv_ss;
   int64_t o_sb, o_sh, o_ss;     // out, dout and dq
   KvChunks kv;                  // positions of the key rows
+  DocBounds docs;               // packed-sequence boundaries (n = 0: none)
   int32_t batch, hq, hkv, group;
   int32_t sq, skv;
   int32_t chunk_len, n_q_chunks;

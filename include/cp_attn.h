@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CP_ATTN_ABI_VERSION 1
+#define CP_ATTN_ABI_VERSION 2
 #define CP_ATTN_MAX_Q_CHUNKS 16
 /* Most KV chunks a descriptor may list (a Head-Tail all-gather at cp = 32
  * delivers 64 chunks). */
@@ -52,6 +52,8 @@ extern "C" {
  * many rows (the largest key tile of the kernels, so no tile straddles two
  * chunks). */
 #define CP_ATTN_KV_CHUNK_ALIGN 128
+/* Most packed-sequence boundaries a share may meet (see cp_attn_desc.doc_starts). */
+#define CP_ATTN_MAX_DOC_BOUNDS 256
 
 /* Local row order of the query shard. */
 typedef enum {
@@ -74,7 +76,7 @@ typedef enum {
   CP_ATTN_ERR_NULL_PTR = -1,      /* a required pointer is NULL */
   CP_ATTN_ERR_BAD_SHAPE = -2,     /* sizes/strides inconsistent (hq % hkv, chunk lengths, ...) */
   CP_ATTN_ERR_BAD_LAYOUT = -3,    /* layout vs chunk count, or unknown layout */
-  CP_ATTN_ERR_BAD_POSITIONS = -4, /* negative or overlapping chunk positions */
+  CP_ATTN_ERR_BAD_POSITIONS = -4, /* negative or overlapping chunk positions, unsorted doc_starts */
   CP_ATTN_ERR_UNSUPPORTED = -5,   /* head_dim / dtype / KV chunk length / row stride >= 2^24 not implemented */
   CP_ATTN_ERR_WORKSPACE = -6,     /* workspace NULL or smaller than cp_attn_workspace_bytes() */
   CP_ATTN_ERR_HIP = -7,           /* a HIP launch or query failed */
@@ -110,6 +112,16 @@ typedef enum {
  * pairwise disjoint ranges. Query head h reads KV head h / (hq / hkv) (contiguous GQA groups,
  * [CP-migration] §9.2).
  *
+ * Packed variable-length sequences ([FLA-CP] §3.1, §3.3: a global cu_seqlens
+ * split across ranks): with n_docs > 0 the global positions are cut into
+ * sequences starting at doc_starts[0] < doc_starts[1] < ... (a cu_seqlens
+ * without its final total; positions before doc_starts[0] form one more
+ * sequence), and key j is visible to query i only if it also lies in the
+ * query's sequence. Requires causal != 0 and one KV chunk. The library keeps
+ * only the boundaries the share can meet (per query chunk: the last start at
+ * or before it, every start inside it, the first start after it); more than
+ * CP_ATTN_MAX_DOC_BOUNDS of them is CP_ATTN_ERR_UNSUPPORTED.
+ *
  * The LSE is the natural log of the sum of exp(softmax_scale * q.k) over the
  * visible keys; a row with no visible key gets out = 0 and lse = -inf.
  */
@@ -132,6 +144,8 @@ typedef struct cp_attn_desc {
   int64_t kv_strides[3];       /* batch, head, row strides of k and v (elements) */
   int64_t o_strides[3];        /* batch, head, row strides of out, dout and dq (elements) */
                                /* all strides >= 0, multiples of 16 bytes; row strides < 2^24 */
+  int32_t n_docs;              /* 0: one sequence; > 0: packed sequences (needs causal, one KV chunk) */
+  const int64_t *doc_starts;   /* host array [n_docs]: strictly increasing global start positions, >= 0 */
 } cp_attn_desc;
 
 /* ABI version of the loaded library (CP_ATTN_ABI_VERSION of its build). */

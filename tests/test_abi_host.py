@@ -107,7 +107,7 @@ def test_validate_rejects(kw, code):
 
 def test_validate_abi_version_causal_flag_and_null():
     d = desc()
-    d.desc.abi_version = 2
+    d.desc.abi_version = 1
     assert status(d) == -8
     d = desc()
     d.desc.causal = 2
@@ -287,3 +287,56 @@ def test_ulysses_relayout_rejects(kw, code):
 
 def test_ulysses_relayout_empty_is_a_no_op():
     assert _relayout_status(rows=0, src=0, dst=0) == 0
+
+
+# Packed variable-length sequences: sequence-length mixes after the FLA CP
+# test matrix (a sequence cut by rank boundaries, boundaries on rank
+# boundaries, one sequence across several ranks, many short sequences).
+PACKED_MIXES = {
+    "cut": [3000, 4000, 3240, 5120, 5120, 7000, 3240, 2048],
+    "aligned": [4096] * 8,
+    "long_first": [21000, 11768],
+    "short": [100] * 327 + [68],
+}
+
+
+def _doc_starts(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64).tolist()
+
+
+def test_validate_packed_sequences():
+    starts = _doc_starts([700, 800, 500])
+    assert status(desc(doc_starts=starts)) == 0
+    assert status(desc(doc_starts=[5])) == 0                           # positions before 5: one more sequence
+    assert status(desc(doc_starts=[0, 700, 700])) == -4               # not strictly increasing
+    assert status(desc(doc_starts=[-3, 700])) == -4
+    assert status(desc(doc_starts=starts, causal=False)) == -5        # packed sequences are causal
+    assert status(desc(doc_starts=starts, skv=2048, kv_chunk_pos=[0, 1024])) == -5
+    # More than 256 boundaries that the share meets: unsupported.
+    many = list(range(0, 2000, 3))
+    assert status(desc(doc_starts=many)) == 0                          # 169 of them in the share
+    many = list(range(0, 2000))
+    assert status(desc(doc_starts=many)) == -5
+    d = desc(doc_starts=starts)
+    d.desc.doc_starts = None
+    assert status(d) == -1
+
+
+@pytest.mark.parametrize("mix", list(PACKED_MIXES), ids=list(PACKED_MIXES))
+@pytest.mark.parametrize("kind,rank", [("contiguous", 7), ("contiguous", 2), ("head_tail", 0), ("head_tail", 5)])
+def test_packed_share_pairs_match_oracle(mix, kind, rank):
+    S = 32768
+    starts = _doc_starts(PACKED_MIXES[mix])
+    sh = _share(kind, S, 8, rank, 32, 8)
+    d = _desc_for(sh, S, 32, 8)
+    d = desc(hq=32, hkv=8, head_dim=128, sq_local=d.desc.sq_local, skv=S, q_chunk_pos=sh["q_chunk_pos"],
+             layout="head_tail" if kind == "head_tail" else "contiguous", doc_starts=starts,
+             q_strides=(0, 0, 128), kv_strides=(0, 0, 128), o_strides=(0, 0, 128))
+    if mix == "short" and status(d) == -5:
+        pytest.skip("more boundaries than the kernels take for this share")
+    assert status(d) == 0
+    pairs = cp_attn_share_pairs(d)
+    assert pairs == oc.share_pairs(sh["q_pos"], sh["kv_pos"], True, starts)
+    st = cp_attn_plan_stats_fwd(d)
+    area = st["kv_tile_visits"] * st["block_q_rows"] * st["block_kv_rows"]
+    assert pairs * 32 <= area * st["heads_per_item"]
