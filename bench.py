@@ -75,8 +75,8 @@ KERNEL_SOURCES = {   # files whose text determines each kernel's machine code
     "dkdv": ["bwd_bf16.hip", "gfx950_common.h", "plan.h"],
     "dq": ["bwd_bf16.hip", "gfx950_common.h", "plan.h"],
 }
-KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128, 2, false>", "pre": "bwd_pre_kernel<128>",
-                "dkdv": "bwd_dkdv_kernel<128>", "dq": "bwd_dq_kernel<128, 2, false>"}
+KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128, 2, 0>", "pre": "bwd_pre_kernel<128>",
+                "dkdv": "bwd_dkdv_kernel<128, false>", "dq": "bwd_dq_kernel<128, 2, 0>"}
 
 
 def sources_sha256(part):
@@ -112,11 +112,13 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", wa
     dev = torch.device("cuda")
     q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
     kind, cp, r, U = share_for(spec, rank)
+    from synthetic import doc_starts
     sh = cut_share(kind, q, k, v, cp, r, ulysses=U, kv_order=kv_order)
     kvp = sh.kv_chunk_pos
+    docs = doc_starts(spec)
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D)
-    d = api.make_desc(sh.q, sh.k, sh.v, sh.q.stride(), sh.q_chunk_pos, kvp, sh.layout, True, scale)
+    d = api.make_desc(sh.q, sh.k, sh.v, sh.q.stride(), sh.q_chunk_pos, kvp, sh.layout, True, scale, docs)
     pairs = api.cp_attn_share_pairs(d)
     B, Hq, Sq = sh.q.shape[0], sh.q.shape[1], sh.q.shape[2]
     Hkv, Skv = sh.k.shape[1], sh.k.shape[2]
@@ -130,12 +132,12 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", wa
 
     def fwd():
         api.cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,
-                        out=out, lse=lse, kv_chunk_pos=kvp)
+                        out=out, lse=lse, kv_chunk_pos=kvp, doc_starts=docs)
 
     def bwd(events):
         api.cp_attn_bwd_timed(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, events,
                               layout=sh.layout, softmax_scale=scale, workspace=ws, grads=grads,
-                              kv_chunk_pos=kvp)
+                              kv_chunk_pos=kvp, doc_starts=docs)
 
     def new_events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(5)]

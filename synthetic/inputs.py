@@ -77,7 +77,26 @@ WORKLOADS = {
     "head_tail_bwd_b2_cp8_s32k_gqa32x8_d128": dict(
         batch=2, hq=32, hkv=8, seq=32768, head_dim=128, dtype="bf16",
         kind="head_tail", cp=8, ranks=[0, 7], backward=True),
+    # Eight packed sequences over the 32K tokens (a global cu_seqlens), with a
+    # length mix after the FLA CP tests: sequences cut by rank boundaries,
+    # boundaries on rank boundaries, one sequence over two ranks.
+    "colossal_packed_cp8_r7_s32k_gqa32x8_d128": dict(
+        batch=1, hq=32, hkv=8, seq=32768, head_dim=128, dtype="bf16",
+        kind="contiguous", cp=8, ranks=[7], backward=True,
+        doc_lengths=[3000, 4000, 3240, 5120, 5120, 7000, 3240, 2048]),
 }
+
+
+def doc_starts(spec: dict) -> list:
+    """Global start positions of a workload's packed sequences ([] for one sequence)."""
+    lengths = spec.get("doc_lengths")
+    if not lengths:
+        return []
+    out, pos = [], 0
+    for n in lengths:
+        out.append(pos)
+        pos += n
+    return out
 
 
 def workload(name: str, seed: int = 0) -> tuple[dict, GlobalProblem]:
