@@ -127,3 +127,41 @@ def test_packed_full_size_sampled_rows():
     r_t = torch.from_numpy(rows).to(out.device)
     check_fwd(out[:, heads][:, :, r_t], lse[:, heads][:, :, r_t], ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16,
               "32K packed colossal r7")
+
+
+OTHER = [
+    # kind, S, Hq, Hkv, D, cp, B: the other kernel instantiations
+    ("head_tail", 1024, 6, 3, 64, 2, 1),     # D = 64, GQA groups of 2
+    ("contiguous", 1024, 4, 4, 128, 4, 2),   # MHA (one head per work item), B = 2
+]
+
+
+@pytest.mark.parametrize("case", OTHER, ids=[f"{c[0]}-D{c[4]}-{c[2]}x{c[3]}-B{c[6]}" for c in OTHER])
+def test_packed_other_shapes(case):
+    kind, S, Hq, Hkv, D, cp, B = case
+    starts = starts_of([200, 63, 129, 1, 631])
+    prob = global_problem(B, Hq, Hkv, S, D, dtype="bf16", seed=15, with_dout=True)
+    for r in range(cp):
+        sh, out, lse, grads, scale = run_share(prob, kind, cp, r, starts, True)
+        osh = oracle_share(kind, S, Hq, Hkv, cp, r)
+        ref_o, ref_l, ref_g = oracle_fwd_bwd(prob, osh, scale, starts, True)
+        check_fwd(out, lse, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, f"packed {case} r{r}")
+        errs = [rel_l2(to_f64(g), rg) for g, rg in zip(grads, ref_g)]
+        print(f"  dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}", flush=True)
+        assert max(errs) <= 1e-2
+
+
+def test_packed_full_size_head_tail_sampled_rows():
+    """32K Head-Tail rank 2 with the eight-sequence mix: rows of both chunks
+    (4096.. inside one sequence; 26624.. crossing the boundary at 27480)."""
+    spec, prob = workload("colossal_cp8_r7_s32k_gqa32x8_d128")
+    starts = starts_of([3000, 4000, 3240, 5120, 5120, 7000, 3240, 2048])
+    sh, out, lse, _, scale = run_share(prob, "head_tail", 8, 2, starts, False)
+    osh = oracle_share("head_tail", spec["seq"], spec["hq"], spec["hkv"], 8, 2)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 2047, 2048, 4095], rng.integers(0, 4096, 28)]))
+    heads = [1, 2]
+    ref_o, ref_l, _ = oracle_fwd_bwd(prob, osh, scale, starts, False, rows=rows, heads=heads)
+    r_t = torch.from_numpy(rows).to(out.device)
+    check_fwd(out[:, heads][:, :, r_t], lse[:, heads][:, :, r_t], ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16,
+              "32K packed head_tail r2")
