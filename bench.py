@@ -433,7 +433,10 @@ def main():
         ent["algorithmic_bytes"] = io[part]
         kernels[part] = ent
     dom = max(kernels, key=lambda p: ms[p])
-    tr = traffic_record(dom)
+    # The committed counter summaries were measured on the Colossal cp=8 rank-7
+    # share in natural order: other shares report no traffic.
+    measured = (args.workload, rank) == ("colossal_cp8_r7_s32k_gqa32x8_d128", 7)
+    tr = traffic_record(dom) if measured else None
     roof = dict(kernels[dom])
     roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if tr else None
     if tr:
