@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock/power sample")
     ap.add_argument("--detail", action="store_true", help="also time every other share")
+    ap.add_argument("--kv-order", choices=["natural", "gathered"], default="natural",
+                    help="K/V in natural order, or as an all-gather delivers them (a KV chunk table)")
     ap.add_argument("--relayout-only", action="store_true",
                     help="only time the Ulysses exchange re-layouts (prints their JSON object)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -86,6 +88,20 @@ def sources_sha256(part):
         with open(os.path.join(ROOT, "context_causal_attention_attn_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def kernel_name(part, spec, kv_order):
+    """The instantiation a share runs: mode 0 for keys in natural order, 1 for
+    a KV chunk table, 2 for packed sequences (the dK/dV kernel: false / true
+    for packed sequences). The workloads all have GQA groups of 4 (two row
+    blocks per forward and dQ work item)."""
+    name = KERNEL_NAMES[part]
+    mode = 2 if spec.get("doc_lengths") else (1 if kv_order == "gathered" else 0)
+    if part in ("fwd", "dq"):
+        return name.replace(", 0>", f", {mode}>")
+    if part == "dkdv" and mode == 2:
+        return name.replace("false>", "true>")
+    return name
 
 
 def traffic_record(part):
@@ -408,7 +424,7 @@ def main():
     if not 0 <= rank < spec["cp"]:
         print(f"--rank {rank} is outside 0..{spec['cp'] - 1} for {args.workload}", file=sys.stderr)
         sys.exit(2)
-    res = time_share(spec, prob, rank, args.steps, args.warmup, with_bwd)
+    res = time_share(spec, prob, rank, args.steps, args.warmup, with_bwd, args.kv_order)
     ms, fl, io = res["ms"], res["flops"], res["bytes"]
     ms_per_step = res["total_ms"] / args.steps
     flops_step = fl["fwd"] + (fl["bwd"] if res["has_bwd"] else 0.0)
@@ -421,7 +437,7 @@ def main():
     for part in ("fwd", "pre", "dkdv", "dq"):
         if part not in ms:
             continue
-        ent = {"kernel": KERNEL_NAMES[part], "ms": round(ms[part], 4)}
+        ent = {"kernel": kernel_name(part, spec, args.kv_order), "ms": round(ms[part], 4)}
         if part == "pre":
             gbs = io[part] / (ms[part] * 1e-3) / 1e9
             ent.update(bound="hbm", achieved=round(gbs, 1), unit="GB/s", peak=PEAK_HBM_GBS,
@@ -435,7 +451,7 @@ def main():
     dom = max(kernels, key=lambda p: ms[p])
     # The committed counter summaries were measured on the Colossal cp=8 rank-7
     # share in natural order: other shares report no traffic.
-    measured = (args.workload, rank) == ("colossal_cp8_r7_s32k_gqa32x8_d128", 7)
+    measured = (args.workload, rank, args.kv_order) == ("colossal_cp8_r7_s32k_gqa32x8_d128", 7, "natural")
     tr = traffic_record(dom) if measured else None
     roof = dict(kernels[dom])
     roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if tr else None
@@ -459,7 +475,9 @@ def main():
                    "rank": rank, "batch": spec["batch"], "hq": spec["hq"], "hkv": spec["hkv"],
                    "head_dim": spec["head_dim"], "seq_global": spec["seq"], "sq_local": res["sq"],
                    "causal_pairs_per_head": res["pairs"],
-                   "passes": "fwd+bwd" if res["has_bwd"] else "fwd"},
+                   "passes": "fwd+bwd" if res["has_bwd"] else "fwd",
+                   **({"kv_order": args.kv_order} if args.kv_order != "natural" else {}),
+                   **({"packed_sequences": len(spec["doc_lengths"])} if spec.get("doc_lengths") else {})},
         "fwd": {"ms": round(ms["fwd"], 4), "tflops": round(tf(fl["fwd"], ms["fwd"]), 2),
                 "frac_of_peak": round(tf(fl["fwd"], ms["fwd"]) / PEAK_BF16_TFLOPS, 4)},
         "bwd": ({"ms": round(ms["bwd"], 4), "tflops": round(tf(fl["bwd"], ms["bwd"]), 2),
