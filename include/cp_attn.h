@@ -175,7 +175,8 @@ int32_t cp_attn_share_positions(int32_t layout, int64_t s_global, int32_t cp_siz
 int32_t cp_attn_validate(const cp_attn_desc *desc);
 
 /* Number of visible (query, key) pairs per (batch, query head) of the share:
- * the causal work that FLOP counts are based on. Host only. */
+ * the causal work that FLOP counts are based on, under the causal flag, the
+ * KV chunk table and the packed sequences. Host only. */
 int32_t cp_attn_share_pairs(const cp_attn_desc *desc, int64_t *pairs);
 
 /* Bytes of device workspace cp_attn_fwd (backward == 0) or cp_attn_bwd
@@ -184,7 +185,9 @@ int32_t cp_attn_workspace_bytes(const cp_attn_desc *desc, int32_t backward, size
 
 /* Work-list statistics of the forward tile scheduler (host only), for tests
  * and reports: number of work items (one workgroup each), the KV tiles they
- * visit in total, and the tile shape. */
+ * visit in total (per KV chunk, the prefix the item's last row can see; with
+ * packed sequences, from the first row's sequence start on), and the tile
+ * shape. */
 typedef struct cp_attn_plan_stats {
   int64_t work_items;
   int64_t kv_tile_visits;      /* summed over work items */
