@@ -165,3 +165,25 @@ def test_packed_full_size_head_tail_sampled_rows():
     r_t = torch.from_numpy(rows).to(out.device)
     check_fwd(out[:, heads][:, :, r_t], lse[:, heads][:, :, r_t], ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16,
               "32K packed head_tail r2")
+
+
+@pytest.mark.parametrize("kind", ["contiguous", "head_tail"])
+def test_tail_padding_needs_no_mask(kind):
+    """A 2000-token sequence padded to 2048 so that it divides by cp (or 2cp)
+    ([Trainer-CP] §4.2 padding policy): under the global-position causal mask
+    no real token sees a padding key, so every real row equals the oracle's
+    attention over the unpadded sequence, on every rank."""
+    S, S_real, Hq, Hkv, D, cp = 2048, 2000, 8, 2, 128, 4
+    prob = global_problem(1, Hq, Hkv, S, D, dtype="bf16", seed=16)
+    for r in range(cp):
+        sh, out, lse, _, scale = run_share(prob, kind, cp, r, [], False)
+        osh = oracle_share(kind, S, Hq, Hkv, cp, r)
+        real = np.nonzero(osh["q_pos"] < S_real)[0]
+        if real.size == 0:
+            continue
+        q = to_f64(prob.q[:, :, torch.from_numpy(osh["q_pos"][real])])
+        ref_o, ref_l = oc.attention_rows(q, to_f64(prob.k[:, :, :S_real]), to_f64(prob.v[:, :, :S_real]),
+                                         osh["q_pos"][real], np.arange(S_real), scale, True)
+        r_t = torch.from_numpy(real).to(out.device)
+        check_fwd(out[:, :, r_t], lse[:, :, r_t], ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16,
+                  f"padded {kind} r{r}")
