@@ -145,7 +145,8 @@ def _as_f64(x) -> np.ndarray:
 
 
 def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
-                   row_block: int = 1024, doc_starts: Optional[Sequence[int]] = None):
+                   row_block: int = 1024, doc_starts: Optional[Sequence[int]] = None,
+                   user_mask: Optional[np.ndarray] = None):
     """Attention of local query rows against the gathered keys/values.
 
     q: [B, Hq, Sq, D]; k, v: [B, Hkv, Skv, D]; q_pos [Sq] and kv_pos [Skv] are
@@ -160,6 +161,9 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
         out_i = sum_{j in A_i} exp(s_ij - LSE_i) v_j
     A row with no visible key gets out = 0 and LSE = -inf. ``doc_starts``
     restricts A_i to the row's own packed sequence (see ``visible``).
+    ``user_mask`` (bool, broadcastable to [B, Hq, Sq, Skv]) is the caller's
+    attention mask: [CP-migration] §8 merges a boolean mask with the CP mask
+    by logical AND (a key must be visible under both), never replacing it.
 
     Rows are independent, so they are visited in blocks of ``row_block`` only to
     bound memory; nothing is reordered within a row.
@@ -179,6 +183,9 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
             for r0 in range(0, Sq, row_block):
                 r1 = min(Sq, r0 + row_block)
                 vis = visible(q_pos[r0:r1], kv_pos, causal, doc_starts)
+                if user_mask is not None:
+                    um = np.broadcast_to(user_mask, (B, Hq, Sq, Skv))
+                    vis = vis & um[b, h, r0:r1]
                 s = scale * (q[b, h, r0:r1] @ k[b, hk].T)
                 s = np.where(vis, s, -np.inf)
                 m = s.max(axis=1)
@@ -198,7 +205,8 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
 def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
                        causal: bool = True, kv_index: Optional[np.ndarray] = None,
                        row_block: int = 1024, want_dq: bool = True,
-                       doc_starts: Optional[Sequence[int]] = None):
+                       doc_starts: Optional[Sequence[int]] = None,
+                       user_mask: Optional[np.ndarray] = None):
     """Gradients of ``sum(dout * out)`` for one share.
 
     Returns (dq [B, Hq, Sq, D], dk, dv) in float64, where dk/dv are this share's
@@ -227,15 +235,20 @@ def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
     kv_pos = np.asarray(kv_pos, dtype=np.int64)
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
-    out, lse = attention_rows(q, k, v, q_pos, kv_pos, scale, causal, row_block, doc_starts)
+    out, lse = attention_rows(q, k, v, q_pos, kv_pos, scale, causal, row_block, doc_starts, user_mask)
     sel = np.arange(Skv) if kv_index is None else np.asarray(kv_index, dtype=np.int64)
     dq = np.zeros_like(q)
     dk = np.zeros((B, Hkv, sel.size, D))
     dv = np.zeros((B, Hkv, sel.size, D))
 
-    def grads(qb, dob, delta, lse_b, has, pos_b, kk, vv, kpos):
-        """P and dS of a block of rows against the keys kk/vv at positions kpos."""
+    um_all = None if user_mask is None else np.broadcast_to(user_mask, (B, Hq, Sq, Skv))
+
+    def grads(qb, dob, delta, lse_b, has, pos_b, kk, vv, kpos, um=None):
+        """P and dS of a block of rows against the keys kk/vv at positions kpos
+        (um: the user mask of those rows and keys)."""
         vis = visible(pos_b, kpos, causal, doc_starts) & has[:, None]
+        if um is not None:
+            vis = vis & um
         s = scale * (qb @ kk.T)
         lse_safe = np.where(has, lse_b, 0.0)
         p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
@@ -251,12 +264,14 @@ def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
                 has = np.isfinite(lse_b)
                 delta = np.sum(dout[b, h, r0:r1] * out[b, h, r0:r1], axis=1)
                 qb, dob = q[b, h, r0:r1], dout[b, h, r0:r1]
+                um = None if um_all is None else um_all[b, h, r0:r1]
                 if want_dq:
-                    _, ds = grads(qb, dob, delta, lse_b, has, q_pos[r0:r1], k[b, hk], v[b, hk], kv_pos)
+                    _, ds = grads(qb, dob, delta, lse_b, has, q_pos[r0:r1], k[b, hk], v[b, hk], kv_pos, um)
                     dq[b, h, r0:r1] = scale * (ds @ k[b, hk])
                 if sel.size:
                     p_sel, ds_sel = grads(qb, dob, delta, lse_b, has, q_pos[r0:r1],
-                                          k[b, hk][sel], v[b, hk][sel], kv_pos[sel])
+                                          k[b, hk][sel], v[b, hk][sel], kv_pos[sel],
+                                          None if um is None else um[:, sel])
                     dv[b, hk] += p_sel.T @ dob
                     dk[b, hk] += scale * (ds_sel.T @ qb)
     return dq, dk, dv

@@ -568,3 +568,37 @@ def test_planted_sequence_boundary_off_by_one_is_caught(monkeypatch):
     real = oc.doc_of
     monkeypatch.setattr(oc, "doc_of", lambda pos, starts: real(np.asarray(pos) - 1, starts))
     assert _fails(lambda: test_packed_sequences_are_independent_causal_attentions([7, 9, 8]))
+
+
+# ----------------------------------------------------------------------------
+# User attention masks merged with the CP mask
+# ----------------------------------------------------------------------------
+def test_user_mask_is_anded_with_the_cp_mask():
+    """A boolean user mask ([B, 1, S, S], broadcast over heads) merged by AND
+    with the causal mask equals torch float64 SDPA given the AND of the two as
+    its mask, forward and autograd backward; a share (global offset) sees the
+    same rows of it."""
+    S = 24
+    p = small_problem(B=2, Hq=4, Hkv=2, S=S, D=5, seed=31, dout=True)
+    q, k, v, do = p.q.double(), p.k.double(), p.v.double(), p.dout.double()
+    rng = np.random.default_rng(31)
+    um = rng.random((2, 1, S, S)) < 0.7
+    um[:, :, np.arange(S), np.arange(S)] = True          # every row keeps its own key
+    pos = np.arange(S)
+    out, _ = oc.attention_rows(q.numpy(), k.numpy(), v.numpy(), pos, pos, 0.6, True, user_mask=um)
+    dq, dk, dv = oc.attention_rows_bwd(q.numpy(), k.numpy(), v.numpy(), do.numpy(), pos, pos, 0.6, True,
+                                       user_mask=um)
+    both = torch.from_numpy(um & np.tril(np.ones((S, S), dtype=bool)))
+    qr, kr, vr = (t.clone().requires_grad_(True) for t in (q, k, v))
+    ref = F.scaled_dot_product_attention(qr, kr.repeat_interleave(2, dim=1), vr.repeat_interleave(2, dim=1),
+                                         attn_mask=both, scale=0.6)
+    ref.backward(do)
+    np.testing.assert_allclose(out, ref.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, qr.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dk, kr.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dv, vr.grad.numpy(), atol=1e-10)
+    # A Head-Tail share with the mask rows of its own queries.
+    sh = oc.head_tail_share(S, 4, 2, 3, 1)
+    o2, _ = oc.attention_rows(q.numpy()[:, :, sh["q_pos"]], k.numpy(), v.numpy(), sh["q_pos"], pos, 0.6, True,
+                              user_mask=um[:, :, sh["q_pos"]])
+    np.testing.assert_allclose(o2, out[:, :, sh["q_pos"]], atol=1e-13)
