@@ -78,7 +78,7 @@ KERNEL_SOURCES = {   # files whose text determines each kernel's machine code
     "dq": ["bwd_bf16.hip", "gfx950_common.h", "plan.h"],
 }
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128, 2, 0>", "pre": "bwd_pre_kernel<128>",
-                "dkdv": "bwd_dkdv_kernel<128, false>", "dq": "bwd_dq_kernel<128, 2, 0>"}
+                "dkdv": "bwd_dkdv_kernel<128, 0>", "dq": "bwd_dq_kernel<128, 2, 0>"}
 
 
 def sources_sha256(part):
@@ -92,15 +92,15 @@ def sources_sha256(part):
 
 def kernel_name(part, spec, kv_order):
     """The instantiation a share runs: mode 0 for keys in natural order, 1 for
-    a KV chunk table, 2 for packed sequences (the dK/dV kernel: false / true
-    for packed sequences). The workloads all have GQA groups of 4 (two row
-    blocks per forward and dQ work item)."""
+    a KV chunk table, 2 for packed sequences (the dK/dV kernel: 0, or 1 for
+    packed sequences). The workloads all have GQA groups of 4 (two row blocks
+    per forward and dQ work item)."""
     name = KERNEL_NAMES[part]
     mode = 2 if spec.get("doc_lengths") else (1 if kv_order == "gathered" else 0)
     if part in ("fwd", "dq"):
         return name.replace(", 0>", f", {mode}>")
     if part == "dkdv" and mode == 2:
-        return name.replace("false>", "true>")
+        return name.replace(", 0>", ", 1>")
     return name
 
 

@@ -36,7 +36,7 @@ class _Desc:
 
     def __init__(self, *, dtype, batch, hq, hkv, head_dim, sq_local, skv, q_chunk_pos,
                  kv_chunk_pos, layout, causal, softmax_scale, q_strides, kv_strides, o_strides,
-                 doc_starts=()):
+                 doc_starts=(), attn_mask=None, mask_strides=(0, 0, 0)):
         self.qpos = (ctypes.c_int64 * max(1, len(q_chunk_pos)))(*q_chunk_pos)
         self.kvpos = (ctypes.c_int64 * max(1, len(kv_chunk_pos)))(*kv_chunk_pos)
         doc_starts = [int(x) for x in doc_starts]
@@ -57,6 +57,10 @@ class _Desc:
             d.q_strides[i], d.kv_strides[i], d.o_strides[i] = q_strides[i], kv_strides[i], o_strides[i]
         d.n_docs = len(doc_starts)
         d.doc_starts = ctypes.cast(self.docs, ctypes.POINTER(ctypes.c_int64))
+        self.mask = attn_mask   # keeps the tensor alive as long as the descriptor
+        d.attn_mask = attn_mask.data_ptr() if attn_mask is not None else None
+        for i in range(3):
+            d.mask_strides[i] = int(mask_strides[i])
         self.desc = d
 
     def ref(self):
@@ -79,15 +83,36 @@ def _check_inputs(q, k, v):
             raise ValueError("tensors must be on the GPU")
 
 
+def _mask_args(attn_mask, q, k):
+    """A user attention mask as (tensor, byte strides): bool or uint8,
+    [B or 1, Hq or 1, Sq, Skv] on q's device with the key dim contiguous;
+    size-1 batch or head dims broadcast (stride 0)."""
+    if attn_mask is None:
+        return None, (0, 0, 0)
+    if attn_mask.dtype not in (torch.bool, torch.uint8) or attn_mask.dim() != 4:
+        raise ValueError("attn_mask must be a 4-D bool or uint8 tensor [B|1, Hq|1, Sq, Skv]")
+    B, Hq, Sq, _ = q.shape
+    if (attn_mask.shape[0] not in (1, B) or attn_mask.shape[1] not in (1, Hq) or attn_mask.shape[2] != Sq
+            or attn_mask.shape[3] != k.shape[2]):
+        raise ValueError(f"attn_mask shape {tuple(attn_mask.shape)} does not broadcast to {(B, Hq, Sq, k.shape[2])}")
+    if attn_mask.device != q.device or attn_mask.stride(3) != 1:
+        raise ValueError("attn_mask must be on q's device with a contiguous key dim")
+    st = tuple(0 if attn_mask.shape[i] == 1 else attn_mask.stride(i) for i in range(3))
+    return attn_mask, st
+
+
 def make_desc(q, k, v, o_strides, q_chunk_pos: Sequence[int], kv_chunk_pos: Sequence[int],
-              layout, causal: bool, softmax_scale: Optional[float], doc_starts: Sequence[int] = ()) -> _Desc:
+              layout, causal: bool, softmax_scale: Optional[float], doc_starts: Sequence[int] = (),
+              attn_mask=None) -> _Desc:
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+    m, mst = _mask_args(attn_mask, q, k)
     return _Desc(dtype=_DT.get(q.dtype, -1), batch=B, hq=Hq, hkv=Hkv, head_dim=D, sq_local=Sq, skv=Skv,
                  q_chunk_pos=list(q_chunk_pos), kv_chunk_pos=list(kv_chunk_pos), layout=layout,
                  causal=causal, softmax_scale=scale, q_strides=q.stride()[:3],
-                 kv_strides=k.stride()[:3], o_strides=tuple(o_strides)[:3], doc_starts=doc_starts)
+                 kv_strides=k.stride()[:3], o_strides=tuple(o_strides)[:3], doc_starts=doc_starts,
+                 attn_mask=m, mask_strides=mst)
 
 
 def _stream_handle(t: torch.Tensor) -> int:
@@ -95,8 +120,9 @@ def _stream_handle(t: torch.Tensor) -> int:
 
 
 def cp_attn_validate(q, k, v, q_chunk_pos, *, layout="contiguous", kv_chunk_pos=(0,), causal=True,
-                     softmax_scale=None, doc_starts=()) -> None:
-    d = make_desc(q, k, v, q.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts)
+                     softmax_scale=None, doc_starts=(), attn_mask=None) -> None:
+    d = make_desc(q, k, v, q.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
+                  attn_mask)
     check(_lib.load().cp_attn_validate(d.ref()), "cp_attn_validate")
 
 
@@ -122,7 +148,8 @@ def cp_attn_plan_stats_fwd(d: _Desc) -> dict:
 def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: Sequence[int], *,
                 layout="contiguous", kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
                 softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None, doc_starts: Sequence[int] = ()):
+                lse: Optional[torch.Tensor] = None, doc_starts: Sequence[int] = (),
+                attn_mask: Optional[torch.Tensor] = None):
     """Forward of one share: returns (out [B, Hq, Sq, D] in q's dtype, lse [B, Hq, Sq] float32).
 
     q is the local query shard (rows in chunk order), k/v the gathered K/V.
@@ -133,7 +160,9 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
     an all-gather delivers them; chunk length a multiple of 128 then).
     doc_starts, if not empty, gives the global start positions of packed
     variable-length sequences (a global cu_seqlens without its final total):
-    a key is then visible only to queries of its own sequence.
+    a key is then visible only to queries of its own sequence. attn_mask, if
+    given, is a bool/uint8 [B|1, Hq|1, Sq, Skv] device tensor ANDed with the
+    CP mask (True / nonzero: may attend).
     """
     lib = _lib.load()
     _check_inputs(q, k, v)
@@ -146,7 +175,8 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
         raise ValueError("out must match q's shape, dtype and device, with a contiguous head_dim")
     if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
-    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts)
+    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
+                  attn_mask)
     check(lib.cp_attn_fwd(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), None, 0, _stream_handle(q)), "cp_attn_fwd")
     return out, lse
@@ -155,7 +185,8 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
 def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="contiguous",
                 kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
                 softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-                grads: Optional[tuple] = None, doc_starts: Sequence[int] = ()):
+                grads: Optional[tuple] = None, doc_starts: Sequence[int] = (),
+                attn_mask: Optional[torch.Tensor] = None):
     """Backward of one share: returns (dq in q's dtype, dk, dv float32 partials over the gathered K/V).
 
     grads, if given, is a (dq, dk, dv) triple of preallocated outputs: dq with
@@ -163,13 +194,14 @@ def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="
     the k/v rows (the KV chunk table's storage order).
     """
     return _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal,
-                softmax_scale, workspace, grads, None, doc_starts)
+                softmax_scale, workspace, grads, None, doc_starts, attn_mask)
 
 
 def cp_attn_bwd_timed(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], events, *,
                       layout="contiguous", kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
                       softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-                      grads: Optional[tuple] = None, doc_starts: Sequence[int] = ()):
+                      grads: Optional[tuple] = None, doc_starts: Sequence[int] = (),
+                      attn_mask: Optional[torch.Tensor] = None):
     """cp_attn_bwd with four torch.cuda.Event (enable_timing=True) recorded by the
     library on the current stream around its phases (for bf16: Delta pass,
     dK/dV kernel, dQ kernel), so events[i].elapsed_time(events[i+1]) is phase i+1."""
@@ -181,11 +213,11 @@ def cp_attn_bwd_timed(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], event
             e.record(stream)
     handles = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
     return _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal,
-                softmax_scale, workspace, grads, handles, doc_starts)
+                softmax_scale, workspace, grads, handles, doc_starts, attn_mask)
 
 
 def _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal, softmax_scale,
-         workspace, grads, events, doc_starts=()):
+         workspace, grads, events, doc_starts=(), attn_mask=None):
     lib = _lib.load()
     _check_inputs(q, k, v)
     B, Hq, Sq, D = q.shape
@@ -207,7 +239,8 @@ def _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal, sof
         for t in (dk, dv):
             if t.shape != (B, Hkv, Skv, D) or t.dtype != torch.float32 or not t.is_contiguous():
                 raise ValueError("dk and dv must be contiguous float32 [B, Hkv, Skv, D] tensors")
-    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts)
+    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
+                  attn_mask)
     need = cp_attn_workspace_bytes(d, True)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

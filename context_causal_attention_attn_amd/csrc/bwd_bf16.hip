@@ -96,10 +96,12 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * 64;
 
-// DOCS: packed-sequence boundaries (keys are visible only to rows of their
-// own sequence).
-template <int D, bool DOCS>
+// KMODE 0: plain; 1: packed-sequence boundaries (keys are visible only to
+// rows of their own sequence); 2: a user attention mask.
+template <int D, int KMODE>
 __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdParams p) {
+  constexpr bool DOCS = KMODE == 1;
+  constexpr bool UMASK = KMODE == 2;
   constexpr int NW = kDkdvWaves;
   constexpr int NC = D / 8;
   constexpr int KSTEPS = D / 32;              // k-steps of S, dP (over D)
@@ -415,6 +417,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         bool need_mask = !wave_keys_ok || rows_left < QT - 1 ||
                          (p.causal && kv_base + wkey0 + 31 > qpos0);
         if constexpr (DOCS) need_mask = need_mask || qpos0 + QT - 1 >= de_wave;
+        if constexpr (UMASK) need_mask = true;
         if (need_mask) {
 #pragma unroll
           for (int kn = 0; kn < KN; ++kn) {
@@ -439,6 +442,21 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
                 const int r = 16 * rb + i;
                 sacc[rb][kn][i] = (r < lo_g || r > hi_g) ? -INFINITY : sacc[rb][kn][i];
               }
+            if constexpr (UMASK) {
+              // ... and allowed by the user mask: rows 16rb + 4grp + i of the
+              // query tile (of head cs.h of the group), this lane's key.
+              if (key_ok[kn]) {
+                const uint8_t *mb = p.mask + b * p.m_sb + (int64_t)(hk * p.group + cs.h) * p.m_sh +
+                                    ((int64_t)cs.c * p.chunk_len + cs.t * QT) * p.m_ss + my_key[kn];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * rb + 4 * grp + i;
+                    if (r <= rows_left && mb[(int64_t)r * p.m_ss] == 0) sacc[rb][kn][i] = -INFINITY;
+                  }
+              }
+            }
           }
         }
         bf16x8 pcur[KN][QSTEPS];
@@ -646,11 +664,12 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 // and S^T, dP^T of block b+1 while the vector ALU forms dS^T of block b; one
 // barrier per 64-key tile.
 // MODE 0: keys in natural order; 1: several KV chunks; 2: natural order with
-// packed-sequence boundaries.
+// packed-sequence boundaries; 3: natural order with a user attention mask.
 template <int D, int RB, int MODE>
 __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr bool MKV = MODE == 1;
   constexpr bool DOCS = MODE == 2;
+  constexpr bool UMASK = MODE == 3;
   constexpr int HPW = kDqWaves / RB;
   constexpr int BM = kDqWaveRows * RB;
   constexpr int NC = D / 8;
@@ -725,6 +744,16 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     ntiles = vis_tiles(0);
   }
   const int64_t kv_pos0 = p.kv.pos[0];
+  // User mask: this lane's mask row per row block (lanes past the wave's last
+  // row read the item's first row, like Q).
+  const uint8_t *mrow[QB];
+  if constexpr (UMASK) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int mr = qvalid[qb] ? local_row[qb] : chunk * p.chunk_len + item_row0;
+      mrow[qb] = p.mask + b * p.m_sb + head * p.m_sh + (int64_t)mr * p.m_ss;
+    }
+  }
   // Packed sequences, as in the forward kernel: this lane's rows see keys
   // from their sequence's start (lo_key, a key row index); the item skips the
   // tiles before its first row's sequence start (t0); a block that starts
@@ -956,6 +985,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     const int64_t blk_plo = base + (int64_t)sb * 32;
     bool need_mask = (sb * 32 + 32 > p.skv) || (p.causal && blk_plo + 31 > wave_qlo);
     if constexpr (DOCS) need_mask = need_mask || blk_plo < wave_ds;
+    if constexpr (UMASK) need_mask = true;
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -978,6 +1008,24 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) scur[h][qb][i] = (16 * h + i > t) ? -INFINITY : scur[h][qb][i];
+        }
+        if constexpr (UMASK) {
+          // ... and allowed by the user mask (keys 16*h + 4*grp .. +3 of the block).
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int k0 = sb * 32 + 16 * h + 4 * grp;
+            uint32_t w = 0;
+            if (k0 + 4 <= p.skv) {
+              w = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (k0 + i < p.skv) w |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              scur[h][qb][i] = ((w >> (8 * i)) & 0xffu) ? scur[h][qb][i] : -INFINITY;
+          }
         }
       }
     }
@@ -1107,26 +1155,32 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
   if (int e = mark(1)) return e;
   const int64_t kv_tiles = (p.skv + BK - 1) / BK;
   if (kv_tiles > 0) {
-    if (p.docs.n > 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(kv_tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
+    const dim3 grid(kv_tiles * p.batch * p.hkv);
+    if (p.mask)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2>), grid, dim3(kDkdvThreads), 0, s, p);
+    else if (p.docs.n > 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1>), grid, dim3(kDkdvThreads), 0, s, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(kv_tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 0>), grid, dim3(kDkdvThreads), 0, s, p);
   }
   if (int e = mark(2)) return e;
   const int64_t items = (int64_t)p.n_head_packs * p.n_q_chunks * p.tiles_per_chunk;
   if (rows > 0 && items > 0) {
     const int rb = kDqWaves / p.heads_per_item;
-    const int mode = p.docs.n > 0 ? 2 : (p.kv.n > 1 ? 1 : 0);
+    const int mode = p.mask ? 3 : p.docs.n > 0 ? 2 : (p.kv.n > 1 ? 1 : 0);
     switch (rb * 4 + mode) {
       case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, 0>), dim3(items), dim3(NT), 0, s, p); break;
       case 9: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, 1>), dim3(items), dim3(NT), 0, s, p); break;
       case 10: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, 2>), dim3(items), dim3(NT), 0, s, p); break;
+      case 11: hipLaunchKernelGGL((bwd_dq_kernel<D, 2, 3>), dim3(items), dim3(NT), 0, s, p); break;
       case 16: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, 0>), dim3(items), dim3(NT), 0, s, p); break;
       case 17: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, 1>), dim3(items), dim3(NT), 0, s, p); break;
       case 18: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, 2>), dim3(items), dim3(NT), 0, s, p); break;
+      case 19: hipLaunchKernelGGL((bwd_dq_kernel<D, 4, 3>), dim3(items), dim3(NT), 0, s, p); break;
       case 32: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, 0>), dim3(items), dim3(NT), 0, s, p); break;
       case 33: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, 1>), dim3(items), dim3(NT), 0, s, p); break;
       case 34: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, 2>), dim3(items), dim3(NT), 0, s, p); break;
+      case 35: hipLaunchKernelGGL((bwd_dq_kernel<D, 8, 3>), dim3(items), dim3(NT), 0, s, p); break;
       default: return (int)hipErrorInvalidValue;
     }
   }

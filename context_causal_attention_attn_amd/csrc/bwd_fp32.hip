@@ -64,6 +64,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
         continue;
       }
       if (key_pos(p, j) < qds) continue;   // before this row's sequence
+      if (p.mask && p.mask[b * p.m_sb + h * p.m_sh + (int64_t)r * p.m_ss + j] == 0) continue;
       const float *kj = kb + (int64_t)j * p.kv_ss;
       const float *vj = vb + (int64_t)j * p.kv_ss;
       float s = 0.0f, dp = 0.0f;
@@ -99,6 +100,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
     for (int r = 0; r < p.sq; ++r) {
       if (p.causal && kp > row_pos(p, r)) continue;
       if (kp < seq_start(p, row_pos(p, r))) continue;   // not in the row's sequence
+      if (p.mask && p.mask[b * p.m_sb + h * p.m_sh + (int64_t)r * p.m_ss + j] == 0) continue;
       const int64_t row = ((int64_t)b * p.hq + h) * p.sq + r;
       const float lse = p.lse[row];
       if (lse == -INFINITY) continue;

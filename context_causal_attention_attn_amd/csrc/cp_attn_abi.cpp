@@ -118,6 +118,15 @@ static int32_t validate(const cp_attn_desc *d) {
     DocBounds db;
     if (collect_doc_bounds(d, &db) != CP_ATTN_OK) return CP_ATTN_ERR_UNSUPPORTED;
   }
+  // User mask: natural key order, no packed sequences, 4-byte words.
+  if (d->attn_mask) {
+    if (d->n_kv_chunks != 1 || d->n_docs > 0) return CP_ATTN_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(d->attn_mask) & 3u) return CP_ATTN_ERR_ALIGNMENT;
+    for (int i = 0; i < 3; ++i) {
+      if (d->mask_strides[i] < 0) return CP_ATTN_ERR_BAD_SHAPE;
+      if (d->mask_strides[i] % 4 != 0) return CP_ATTN_ERR_ALIGNMENT;
+    }
+  }
   // Strides: non-negative, and every row start 16-byte aligned given an
   // aligned base pointer (the kernels move 16-byte vectors along the dim).
   const int64_t vec = 16 / elem_bytes(d->dtype);
@@ -143,6 +152,8 @@ static void fill_kv_chunks(const cp_attn_desc *d, KvChunks *kv) {
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   memset(p, 0, sizeof(*p));
   collect_doc_bounds(d, &p->docs);
+  p->mask = d->attn_mask;
+  p->m_sb = d->mask_strides[0]; p->m_sh = d->mask_strides[1]; p->m_ss = d->mask_strides[2];
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
@@ -170,6 +181,8 @@ void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
 void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
   memset(p, 0, sizeof(*p));
   collect_doc_bounds(d, &p->docs);
+  p->mask = d->attn_mask;
+  p->m_sb = d->mask_strides[0]; p->m_sh = d->mask_strides[1]; p->m_ss = d->mask_strides[2];
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];

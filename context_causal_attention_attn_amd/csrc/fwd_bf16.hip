@@ -57,11 +57,13 @@ constexpr float kSumLimit = 65536.0f;    // largest tile sum kept without a new 
 
 
 // MODE 0: keys in natural order (one KV chunk); 1: several KV chunks; 2:
-// natural order with packed-sequence boundaries.
+// natural order with packed-sequence boundaries; 3: natural order with a user
+// attention mask.
 template <int D, int RB, int MODE>
 __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr bool MKV = MODE == 1;
   constexpr bool DOCS = MODE == 2;
+  constexpr bool UMASK = MODE == 3;
   constexpr int HPW = NW / RB;         // heads per work item
   constexpr int BM = kFwdWaveRows * RB;  // query rows per work item
   constexpr int NC = D / 8;            // 16-byte chunks per row
@@ -142,6 +144,14 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     ntiles = vis_tiles(0);
   }
   const int64_t kv_pos0 = p.kv.pos[0];
+  // User mask: this lane's mask row per row block (rows past the item's last
+  // read its last row, like Q).
+  const uint8_t *mrow[QB];
+  if constexpr (UMASK) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      mrow[qb] = p.mask + b * p.m_sb + head * p.m_sh + (int64_t)local_row[qb] * p.m_ss;
+  }
   // Packed sequences: each of this lane's rows sees keys from its sequence's
   // start (the last bound <= its position) on, as a key row index (lo_key);
   // the item skips the tiles before its first row's sequence start (t0), and a
@@ -418,6 +428,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     // is visible to a row iff it is <= that row's limit.
     bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
     if constexpr (DOCS) need_mask = need_mask || tile_plo < wave_ds;
+    if constexpr (UMASK) need_mask = true;
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -441,6 +452,25 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               sacc[qb][kb][i] = (16 * kb + i > t) ? -INFINITY : sacc[qb][kb][i];
+        }
+        if constexpr (UMASK) {
+          // ... and allowed by the user mask: the 4 bytes of this lane's keys
+          // 16*kb + 4*grp .. +3 (byte reads past the last key row).
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const int k0 = kt * BN + 16 * kb + 4 * grp;
+            uint32_t w = 0;
+            if (k0 + 4 <= p.skv) {
+              w = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (k0 + i < p.skv) w |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sacc[qb][kb][i] = ((w >> (8 * i)) & 0xffu) ? sacc[qb][kb][i] : -INFINITY;
+          }
         }
       }
     }
@@ -595,17 +625,20 @@ int launch_d(const FwdParams &p, void *stream) {
   if (grid == 0) return 0;
   const int rb = NW / p.heads_per_item;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int mode = p.docs.n > 0 ? 2 : (p.kv.n > 1 ? 1 : 0);
+  const int mode = p.mask ? 3 : p.docs.n > 0 ? 2 : (p.kv.n > 1 ? 1 : 0);
   switch (rb * 4 + mode) {
     case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 0>), dim3(grid), dim3(NT), 0, s, p); break;
     case 9: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 1>), dim3(grid), dim3(NT), 0, s, p); break;
     case 10: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 11: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 3>), dim3(grid), dim3(NT), 0, s, p); break;
     case 16: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 0>), dim3(grid), dim3(NT), 0, s, p); break;
     case 17: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 1>), dim3(grid), dim3(NT), 0, s, p); break;
     case 18: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 2>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 19: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 3>), dim3(grid), dim3(NT), 0, s, p); break;
     case 32: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 0>), dim3(grid), dim3(NT), 0, s, p); break;
     case 33: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 1>), dim3(grid), dim3(NT), 0, s, p); break;
     case 34: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 2>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 35: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 3>), dim3(grid), dim3(NT), 0, s, p); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

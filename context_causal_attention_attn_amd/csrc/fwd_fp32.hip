@@ -53,6 +53,8 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
   // bound <= its position; the scan is uniform over the block) are hidden.
   int64_t ds = INT64_MIN;
   for (int i = 0; i < p.docs.n; ++i) ds = p.docs.pos[i] <= qpos ? p.docs.pos[i] : ds;
+  // User mask row of this query (NULL: no mask).
+  const uint8_t *mrow = p.mask ? p.mask + b * p.m_sb + head * p.m_sh + (int64_t)local_row * p.m_ss : nullptr;
 
   const float *kb = static_cast<const float *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
   const float *vb = static_cast<const float *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
@@ -78,6 +80,7 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
       const int nk = min(kKeys, nvis - j0);
       for (int r = 0; r < nk; ++r) {
         if (p.causal && (kpos + j0 + r > qpos || kpos + j0 + r < ds)) continue;
+        if (mrow && mrow[krow0 + j0 + r] == 0) continue;
         float s = 0.0f;
 #pragma unroll
         for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[r][d], s);

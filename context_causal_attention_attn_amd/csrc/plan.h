@@ -59,6 +59,8 @@ struct FwdParams {
   int64_t o_sb, o_sh, o_ss;     // of out
   KvChunks kv;                  // positions of the key rows
   DocBounds docs;               // packed-sequence boundaries (n = 0: none)
+  const uint8_t *mask;          // user attention mask (NULL: none), [b][h][row][key]
+  int64_t m_sb, m_sh, m_ss;     // its byte strides (batch, head, row)
   int32_t hq, hkv, group;       // group = hq / hkv
   int32_t heads_per_item;       // query heads of one KV group packed in a work item
   int32_t n_head_packs;         // batch * hq / heads_per_item
@@ -129,6 +131,8 @@ struct BwdParams {
   int64_t o_sb, o_sh, o_ss;     // out, dout and dq
   KvChunks kv;                  // positions of the key rows
   DocBounds docs;               // packed-sequence boundaries (n = 0: none)
+  const uint8_t *mask;          // user attention mask (NULL: none), [b][h][row][key]
+  int64_t m_sb, m_sh, m_ss;     // its byte strides (batch, head, row)
   int32_t batch, hq, hkv, group;
   int32_t sq, skv;
   int32_t chunk_len, n_q_chunks;

@@ -122,6 +122,14 @@ typedef enum {
  * or before it, every start inside it, the first start after it); more than
  * CP_ATTN_MAX_DOC_BOUNDS of them is CP_ATTN_ERR_UNSUPPORTED.
  *
+ * A user attention mask ([CP-migration] §8: a boolean mask is merged with the
+ * CP mask by logical AND, never replaced): with attn_mask != NULL, key j is
+ * visible to query i only if also attn_mask[b][h][i][j] != 0 (i the local
+ * row, j the key row). Requires one KV chunk and no packed sequences; the
+ * pointer and the strides must be multiples of 4 bytes. The mask is read by
+ * the kernels during the call's work on the stream; the caller keeps it alive
+ * like the other device buffers.
+ *
  * The LSE is the natural log of the sum of exp(softmax_scale * q.k) over the
  * visible keys; a row with no visible key gets out = 0 and lse = -inf.
  */
@@ -146,6 +154,8 @@ typedef struct cp_attn_desc {
                                /* all strides >= 0, multiples of 16 bytes; row strides < 2^24 */
   int32_t n_docs;              /* 0: one sequence; > 0: packed sequences (needs causal, one KV chunk) */
   const int64_t *doc_starts;   /* host array [n_docs]: strictly increasing global start positions, >= 0 */
+  const uint8_t *attn_mask;    /* NULL, or DEVICE bytes [batch][hq][sq_local][skv]: nonzero = may attend */
+  int64_t mask_strides[3];     /* batch, head, row strides of attn_mask in bytes (0 broadcasts); key stride 1 */
 } cp_attn_desc;
 
 /* ABI version of the loaded library (CP_ATTN_ABI_VERSION of its build). */

@@ -340,3 +340,28 @@ def test_packed_share_pairs_match_oracle(mix, kind, rank):
     st = cp_attn_plan_stats_fwd(d)
     area = st["kv_tile_visits"] * st["block_q_rows"] * st["block_kv_rows"]
     assert pairs * 32 <= area * st["heads_per_item"]
+
+
+def test_validate_user_mask():
+    """A user attention mask (device bytes; validation reads only the pointer
+    value and the strides): 4-byte alignment, natural key order, no packed
+    sequences."""
+    base = 1 << 40
+    d = desc()
+    d.desc.attn_mask = base
+    for i, st in enumerate((0, 0, 2048)):
+        d.desc.mask_strides[i] = st
+    assert status(d) == 0
+    d.desc.attn_mask = base + 2
+    assert status(d) == -9
+    d.desc.attn_mask = base
+    d.desc.mask_strides[2] = 2046
+    assert status(d) == -9
+    d.desc.mask_strides[2] = -4
+    assert status(d) == -2
+    d2 = desc(skv=2048, kv_chunk_pos=[1024, 0])
+    d2.desc.attn_mask = base
+    assert status(d2) == -5
+    d3 = desc(doc_starts=[0, 700])
+    d3.desc.attn_mask = base
+    assert status(d3) == -5
