@@ -1,655 +1,17 @@
-// Forward of one CP rank's attention share, bf16 inputs, fp32 accumulation,
-// on gfx950 matrix cores.
-//
-// What is computed: for every local query row (global position from its
-// chunk) the softmax over the visible gathered keys of scale * q.k, applied to
-// v, plus the natural-log LSE ("新流程 CP 多通信模式迁移设计方案" §6.1 local-Q /
-// global-KV attention, §8 global-position causal mask, §9.2 GQA).
-//
-// How (one workgroup = 8 wavefronts = one work item, two wavefronts per SIMD):
-//  * a work item is a tile of query rows of one chunk for a pack of query
-//    heads that read the same KV head (GQA); K/V tiles of 64 keys pass
-//    through LDS rings (2 stages for K, 3 for V) once per workgroup, loaded
-//    straight from global memory into LDS (global_load_lds_dwordx4), and are
-//    read by every head;
-//  * each wavefront owns 32 query rows of one head (two 16-row blocks) and
-//    computes transposed score tiles S^T = K Q^T (keys x queries) with
-//    v_mfma_f32_16x16x32_bf16, so that a lane holds one query column: the
-//    row statistics of the online softmax are lane-local plus a reduction
-//    over the four lanes of a column. Each K fragment read from LDS feeds both
-//    row blocks. (Under the chip's power limit this shape sustains about 12 %
-//    more bf16 throughput than the 32x32x16 one.);
-//  * the probabilities P^T, converted to bf16 in registers, are the B operand
-//    of O^T += V^T P^T without any shuffle: the contraction index (keys) is
-//    permuted identically in both operands, and V^T is read from the
-//    row-major V tile with the gfx950 LDS transpose read ds_read_b64_tr_b16
-//    (the tiles' row swizzle keeps both the row reads of K and the
-//    transpose reads of V free of bank conflicts);
-//  * three-way software pipeline: in step j the matrix core computes
-//    O^T += V^T P^T of tile j-1 and S^T of tile j+1 while the vector ALU turns
-//    the scores of tile j into probabilities. The three are independent; the
-//    step is written as slots of one matrix instruction plus a share of the
-//    vector work, so a wavefront keeps its matrix core fed while it
-//    exponentiates;
-//  * KV tiles wholly after the work item's last query are never visited; only
-//    tiles crossing the causal diagonal (or the ragged end of K/V) are masked;
-//  * the running max is a reference point, not recomputed per tile: the
-//    probabilities of a tile are formed against the current reference, and
-//    only when a lane's partial tile sum exceeds 2^16 (or the row has no reference
-//    yet) is its max taken, O rescaled and the tile redone.
+// Forward dispatch: the instantiation of the share's mode (keys in natural
+// order, a KV chunk table, packed sequences, a user mask). The kernel lives in
+// fwd_bf16_kernel.h; each mode is compiled in a file of its own.
 #include <hip/hip_runtime.h>
-#include <math.h>
 
-#include "gfx950_common.h"
 #include "plan.h"
 
 namespace cpattn {
-namespace {
-
-constexpr int BN = kFwdBlockKV;          // keys per tile (64)
-constexpr int NW = kFwdWaves;            // wavefronts per workgroup (8)
-constexpr int NT = NW * 64;
-constexpr int QB = kFwdWaveRows / 16;    // 16-row query blocks per wavefront
-constexpr int KSTAGES = 2;               // K ring: tile t in stage t % 2
-constexpr int VSTAGES = 3;               // V ring: tile t in stage t % 3
-constexpr int UNROLL = 6;                // steps per loop trip (both ring indices fixed)
-constexpr float kSumLimit = 65536.0f;    // largest tile sum kept without a new max
-
-
-// MODE 0: keys in natural order (one KV chunk); 1: several KV chunks; 2:
-// natural order with packed-sequence boundaries; 3: natural order with a user
-// attention mask.
-template <int D, int RB, int MODE>
-__global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
-  constexpr bool MKV = MODE == 1;
-  constexpr bool DOCS = MODE == 2;
-  constexpr bool UMASK = MODE == 3;
-  constexpr int HPW = NW / RB;         // heads per work item
-  constexpr int BM = kFwdWaveRows * RB;  // query rows per work item
-  constexpr int NC = D / 8;            // 16-byte chunks per row
-  constexpr int KSTEPS = D / 32;       // k-steps of S^T (contraction over D)
-  constexpr int DB = D / 16;           // 16-row blocks of O^T
-  constexpr int KB = BN / 16;          // 16-key blocks of S^T
-  constexpr int PSTEPS = BN / 32;      // k-steps of O^T (contraction over keys)
-  constexpr int TILE = BN * D;
-  static_assert(BN == 64 && QB == 2, "tile shape");
-  using T = Tile16<D>;   // K tiles (row reads) and V tiles (transpose reads)
-
-  // K ring (2 stages) followed by the V ring (3 stages), in one LDS array:
-  // 80 KiB at D = 128.
-  __shared__ __attribute__((aligned(16))) __bf16 smem[(KSTAGES + VSTAGES) * TILE];
-  static_assert((KSTAGES + VSTAGES) * TILE * 2 <= 80 * 1024, "LDS budget");
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;   // LDS byte address of smem
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
-  const int grp = lane >> 4;   // operand k-slice / accumulator row quarter
-  const int col = lane & 15;   // operand row / accumulator column
-
-  // ---- work item ---------------------------------------------------------
-  const int bid = blockIdx.x;
-  const int pack = bid % p.n_head_packs;
-  const int rank = bid / p.n_head_packs;
-  const int ci = rank / p.tiles_per_chunk;
-  const int tile = p.tiles_per_chunk - 1 - (rank % p.tiles_per_chunk);
-  const int chunk = p.chunk_idx[ci];
-  const int64_t chunk_pos = p.chunk_pos[ci];
-  const int packs_per_batch = p.hq / HPW;
-  const int b = pack / packs_per_batch;
-  const int head0 = (pack % packs_per_batch) * HPW;
-  const int hkv = head0 / p.group;
-  const int item_row0 = tile * BM;                          // row within the chunk
-  const int item_rows = min(BM, p.chunk_len - item_row0);
-  const int64_t item_qhi = chunk_pos + item_row0 + item_rows - 1;
-
-  const int head = head0 + wave / RB;
-  const int wrow0 = (wave % RB) * kFwdWaveRows;
-  const int64_t wave_qlo = chunk_pos + item_row0 + min(wrow0, item_rows - 1);
-  // This lane's query row in each 16-row block; rows past the item's last act
-  // as its last row (never stored).
-  int local_row[QB];
-  int64_t qpos[QB];
-  bool qvalid[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r = wrow0 + 16 * qb + col;
-    const int qrow = min(r, item_rows - 1);
-    qvalid[qb] = r < item_rows;
-    qpos[qb] = chunk_pos + item_row0 + qrow;
-    local_row[qb] = chunk * p.chunk_len + item_row0 + qrow;
-  }
-
-  // ---- KV tiles to visit ---------------------------------------------------
-  // Per KV chunk, the prefix of its tiles that the item's last row can see.
-  // With one chunk (MODE 0 and 2: the natural order) that prefix is the whole
-  // visit list and pipeline tile j is storage tile j. With several (MKV), the
-  // pipeline runs over the chunks' prefixes one after another and a scalar
-  // cursor hands out the next tile as its storage tile and the global
-  // position of storage row 0 as seen from its chunk. The softmax state
-  // carries over between chunks, so the chunk order does not change the
-  // result.
-  auto vis_tiles = [&](int c) {
-    int nv = p.kv.len;
-    if (p.causal) {
-      const int64_t n = item_qhi - p.kv.pos[c] + 1;
-      nv = (int)(n < 0 ? 0 : (n > p.kv.len ? p.kv.len : n));
-    }
-    return (nv + BN - 1) / BN;
-  };
-  int ntiles = 0;
-  if constexpr (MKV) {
-    for (int c = 0; c < p.kv.n; ++c) ntiles += vis_tiles(c);
-  } else {
-    ntiles = vis_tiles(0);
-  }
-  const int64_t kv_pos0 = p.kv.pos[0];
-  // User mask: this lane's mask row per row block (rows past the item's last
-  // read its last row, like Q).
-  const uint8_t *mrow[QB];
-  if constexpr (UMASK) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      mrow[qb] = p.mask + b * p.m_sb + head * p.m_sh + (int64_t)local_row[qb] * p.m_ss;
-  }
-  // Packed sequences: each of this lane's rows sees keys from its sequence's
-  // start (the last bound <= its position) on, as a key row index (lo_key);
-  // the item skips the tiles before its first row's sequence start (t0), and a
-  // tile that starts before the wave's last row's sequence start (wave_ds) is
-  // masked. The scan over the bounds is wave-uniform.
-  int t0 = 0;
-  int lo_key[QB];
-  int64_t wave_ds = INT64_MIN;
-  if constexpr (DOCS) {
-    int64_t ds[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) ds[qb] = INT64_MIN;
-    int64_t item_ds = INT64_MIN;
-    const int64_t item_qlo = chunk_pos + item_row0;
-    const int64_t wave_qhi = chunk_pos + item_row0 + min(wrow0 + kFwdWaveRows, item_rows) - 1;
-    for (int i = 0; i < p.docs.n; ++i) {
-      const int64_t bd = p.docs.pos[i];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) ds[qb] = bd <= qpos[qb] ? bd : ds[qb];
-      if (bd <= item_qlo) item_ds = bd;
-      if (bd <= wave_qhi) wave_ds = bd;
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lo_key[qb] = ds[qb] > kv_pos0 ? (int)min<int64_t>(ds[qb] - kv_pos0, p.skv) : 0;
-    if (item_ds > kv_pos0) t0 = (int)min<int64_t>(ntiles, (item_ds - kv_pos0) / BN);
-    ntiles -= t0;
-  }
-  struct TileRef {
-    int kt;          // storage tile
-    int64_t base;    // global position of storage row 0 (this tile's chunk)
-  };
-  int cur_c = 0, cur_left = vis_tiles(0), cur_kt = 0;
-  auto next_tile = [&]() -> TileRef {
-    // Called at most ntiles times, so a chunk with tiles left always follows;
-    // the bound keeps a stray call on the last chunk (its ragged-tile path
-    // clamps every row into the tensor).
-    while (cur_left == 0 && cur_c + 1 < p.kv.n) {
-      ++cur_c;
-      cur_left = vis_tiles(cur_c);
-      cur_kt = cur_c * (p.kv.len / BN);
-    }
-    const TileRef r{cur_kt, p.kv.pos[cur_c] - (int64_t)cur_c * p.kv.len};
-    ++cur_kt;
-    --cur_left;
-    return r;
-  };
-
-  // ---- Q fragments (B operands of S^T = K Q^T), resident for the whole item
-  bf16x8 qf[QB][KSTEPS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh +
-                       (int64_t)local_row[qb] * p.q_ss + 8 * grp;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
-  }
-  wait_vmem_all();
-
-  // ---- per-lane LDS addressing, computed once ------------------------------
-  // Byte addresses of this lane's operand reads in stage 0; the stage, key
-  // block and k-step only add constants, which become instruction immediates.
-  uint32_t kaddr[KSTEPS];                  // K-fragment reads: row col, chunk 4s+grp
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) kaddr[s] = lds0 + 2 * T::chunk_off(col, 4 * s + grp);
-  // V^T transpose reads: lane group grp takes keys 4grp .. 4grp+3 and
-  // 16 + 4grp .. of a 32-key k-step, column 16db + col; its 16 lanes address
-  // 4 rows x 16 columns. The swizzle repeats every 16 rows, so the second
-  // read (16 rows on) and k-step ps (32 rows on) only add constants.
-  uint32_t vaddr[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-    vaddr[db] = lds0 + 2 * (KSTAGES * TILE + T::elem_off(4 * grp + (col >> 2), 16 * db + 4 * (lane & 3)));
-  auto lds_b128 = [](uint32_t addr) -> bf16x8 {
-    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
-  };
-  auto lds_tr = [](uint32_t addr) -> i16x4 {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)addr);
-  };
-
-  // ---- staging of K/V tiles: global -> LDS directly --------------------------
-  // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS address
-  // M0 + 16*l, so one instruction of a wavefront fills RPI consecutive tile
-  // rows; each lane fetches the global chunk that the row's swizzle puts at its
-  // position (a permutation within the row: still one contiguous row read).
-  // Wavefront w's instruction i covers rows (i*NW + w)*RPI ...; the row
-  // modulo 16 (which fixes the swizzle) does not depend on i. The loads are
-  // issued from inline assembly so that the compiler does not make every LDS
-  // read wait for them; each step waits for its own loads (vmcnt(0)) right
-  // before the barrier that publishes the tile.
-  constexpr int RPI = 64 / NC;                       // rows per instruction
-  constexpr int INSTS = BN / (NW * RPI);             // instructions per wave per tile
-  static_assert(INSTS >= 1 && (NW * RPI) % 16 == 0, "staging shape");
-  const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + hkv * p.kv_sh;
-  const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + hkv * p.kv_sh;
-  const int srow = wave * RPI + lane / NC;           // tile row of instruction 0
-  const int scol = 8 * ((lane % NC) ^ T::swz(srow));   // logical column of this lane's chunk
-  const int64_t tile_stride = (int64_t)BN * p.kv_ss;
-  const int64_t istep_bytes = (int64_t)NW * RPI * p.kv_ss * 2;
-  const uint32_t goff0 = (uint32_t)(((int64_t)srow * p.kv_ss + scol) * 2);
-  const uint32_t dst0 = lds0 + 2 * wave * RPI * D;   // this wave's rows in K stage 0
-  // M0 is saved and restored around the load: the compiler owns it.
-  auto dma1 = [](uint32_t m0, uint32_t voff, const void *sbase) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
-  };
-  // Rows of tile kt of K (is_v = false) or V into LDS at dst (this wave's
-  // first row of the stage).
-  auto dma = [&](int kt, bool is_v, uint32_t dst) {
-    const __bf16 *base = is_v ? vbase : kbase;
-    if (kt * BN + BN <= p.skv) {
-      const char *t_base = reinterpret_cast<const char *>(base + (int64_t)kt * tile_stride);
-#pragma unroll
-      for (int i = 0; i < INSTS; ++i) dma1(dst + 2 * i * NW * RPI * D, goff0, t_base + i * istep_bytes);
-    } else {
-      // Ragged last tile: rows past the end read the last row (always masked).
-#pragma unroll
-      for (int i = 0; i < INSTS; ++i) {
-        const int64_t o = (int64_t)min(kt * BN + srow + i * NW * RPI, p.skv - 1) * p.kv_ss + scol;
-        dma1(dst + 2 * i * NW * RPI * D, (uint32_t)(o * 2), base);
-      }
-    }
-  };
-  auto dma_k = [&](int kt, int stage) { dma(kt, false, dst0 + 2 * stage * TILE); };
-  auto dma_v = [&](int kt, int stage) { dma(kt, true, dst0 + 2 * (KSTAGES + stage) * TILE); };
-
-  f32x4 oacc[QB][DB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[qb][db][i] = 0.0f;
-  // Running max of scale*log2(e)*s (may lag the true max) and this lane's
-  // partial row sum (its quarter of the keys), per row block.
-  float m_run[QB], l_part[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_part[qb] = 0.0f;
-  }
-  const float c = p.scale_log2;
-
-  // Matrix-instruction slots of a step. Operand o (one LDS read, used by the
-  // QB row blocks in consecutive slots): o in [0, NPV) is V^T of k-step
-  // ps = o / DB, O^T block db = o % DB (two transpose reads); o in [NPV, NOP)
-  // is K of k-step s = u / KB, key block kb = u % KB (u = o - NPV), so that
-  // the products accumulating into one S^T block are KB*QB slots apart.
-  constexpr int NPV = PSTEPS * DB;
-  constexpr int NOP = NPV + KB * KSTEPS;
-  constexpr int NSLOT = QB * NOP;
-  constexpr int AHEAD = 2;                 // operand reads run this many operands ahead
-  constexpr int NBUF = AHEAD + 1;
-  // Operand o of a step whose K stage is KS and V stage VS.
-  auto read_opnd = [&](auto ks_tag, auto vs_tag, auto o_tag) -> bf16x8 {
-    constexpr int KS = decltype(ks_tag)::value, VS = decltype(vs_tag)::value;
-    constexpr int o = decltype(o_tag)::value;
-    if constexpr (o < NPV) {
-      constexpr int ps = o / DB, db = o % DB;
-      constexpr uint32_t off = 2 * (VS * TILE + 32 * D * ps);
-      const i16x4 a0 = lds_tr(vaddr[db] + off);
-      const i16x4 a1 = lds_tr(vaddr[db] + off + 2 * 16 * D);
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-    } else {
-      constexpr int u = o - NPV, s = u / KB, kb = u % KB;
-      return lds_b128(kaddr[s] + 2 * (KS * TILE + kb * 16 * D));
-    }
-  };
-  // S^T of one tile from K stage 0 (prologue only).
-  auto qk0 = [&](f32x4 (&sa)[QB][KB]) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sa[qb][kb][i] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 a = lds_b128(kaddr[s] + 2 * kb * 16 * D);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sa[qb][kb] = mfma16(a, qf[qb][s], sa[qb][kb]);
-      }
-    }
-  };
-  // O^T += V^T P^T of one tile from V stage `stage` (epilogue only).
-  auto pv = [&](int stage, const bf16x8 (&pf)[QB][PSTEPS]) {
-#pragma unroll
-    for (int ps = 0; ps < PSTEPS; ++ps)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint32_t off = 2 * (stage * TILE + 32 * D * ps);
-        const i16x4 a0 = lds_tr(vaddr[db] + off);
-        const i16x4 a1 = lds_tr(vaddr[db] + off + 2 * 16 * D);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma16(a, pf[qb][ps], oacc[qb][db]);
-      }
-  };
-
-  // ---- prologue ---------------------------------------------------------------
-  // V stage 2 stands for "tile -1" in step 0 (its P is zero), so it must
-  // not hold NaN bit patterns: clear it.
-  {
-    constexpr int VEC = TILE / 8;
-    u32x4 *vlast = reinterpret_cast<u32x4 *>(smem + (KSTAGES + VSTAGES - 1) * TILE);
-    for (int i = tid; i < VEC; i += NT) vlast[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  // Scores and probabilities alternate between two register sets by step
-  // parity: step j reads S^T(j) from set j%2 and writes S^T(j+1) into the
-  // other; it reads P(j-1) from set (j+1)%2 and writes P(j) into set j%2.
-  // (Sets are always chosen by a compile-time index: a runtime index would
-  // put them in scratch memory.)
-  f32x4 sbuf[2][QB][KB];
-  bf16x8 pbuf[2][QB][PSTEPS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int ps = 0; ps < PSTEPS; ++ps)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pbuf[1][qb][ps][e] = (__bf16)0.0f;
-  // Tiles j, j+1, j+2 of the pipeline (step j masks tile j, prefetches V of
-  // j+1 and K of j+2).
-  TileRef t_cur{t0, kv_pos0}, t_nx1{t0 + 1, kv_pos0}, t_nx2{t0 + 2, kv_pos0};
-  if constexpr (MKV) {
-    if (ntiles > 0) t_cur = next_tile();
-    if (ntiles > 1) t_nx1 = next_tile();
-    if (ntiles > 2) t_nx2 = next_tile();
-  }
-  if (ntiles > 0) {
-    dma_k(t_cur.kt, 0);
-    dma_v(t_cur.kt, 0);
-  }
-  if (ntiles > 1) dma_k(t_nx1.kt, 1);
-  wait_vmem_all();
-  __syncthreads();
-  if (ntiles > 0) qk0(sbuf[0]);
-  __syncthreads();   // K stage 0 is refilled in step 0
-
-  // One step on tile j (J6 = j % 6): PV(j-1) and S^T(j+1) on the matrix
-  // core, softmax of S^T(j) on the VALU, and K of tile j+2 and V of tile j+1
-  // on their way into the rings. Slots are separated by scheduling fences so
-  // that the interleave is the one written here.
-  auto step = [&](auto j6_tag, int j) {
-    constexpr int J6 = decltype(j6_tag)::value;
-    constexpr int SET = J6 & 1;
-    f32x4 (&sacc)[QB][KB] = sbuf[SET];
-    f32x4 (&snext)[QB][KB] = sbuf[1 - SET];
-    const bf16x8 (&pprev)[QB][PSTEPS] = pbuf[1 - SET];
-    bf16x8 (&pcur)[QB][PSTEPS] = pbuf[SET];
-    using KS = IC<(J6 + 1) % KSTAGES>;   // K of tile j+1
-    using VS = IC<(J6 + 2) % VSTAGES>;   // V of tile j-1
-    // K of tile j+2 replaces K of tile j (read in step j-1); V of tile j+1
-    // replaces V of tile j-2 (read in step j-1).
-    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : t0 + j + 2, J6 % KSTAGES);
-    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : t0 + j + 1, (J6 + 1) % VSTAGES);
-    // Keep the operand bases opaque per step: otherwise the compiler hoists a
-    // base-plus-stage address per stage out of the loop (several times the
-    // registers) instead of folding the stage into the read's immediate.
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]));
-#pragma unroll
-    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vaddr[db]));
-    int kt = t0 + j;
-    int64_t tile_plo = kv_pos0 + (int64_t)kt * BN;
-    if constexpr (MKV) {
-      kt = t_cur.kt;
-      tile_plo = t_cur.base + (int64_t)kt * BN;
-      t_cur = t_nx1;
-      t_nx1 = t_nx2;
-      if (j + 3 < ntiles) t_nx2 = next_tile();
-    }
-
-    // Mask (diagonal or ragged tiles only): key 16*kb + 4*grp + i of the tile
-    // is visible to a row iff it is <= that row's limit.
-    bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
-    if constexpr (DOCS) need_mask = need_mask || tile_plo < wave_ds;
-    if constexpr (UMASK) need_mask = true;
-    if (need_mask) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        int lim = p.skv - 1 - kt * BN;
-        if (p.causal) {
-          const int64_t rel = qpos[qb] - tile_plo;
-          lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
-        }
-        const int t = lim - 4 * grp;
-        if constexpr (DOCS) {
-          // ... and >= the row's sequence start.
-          const int tl = min(max(lo_key[qb] - kt * BN, 0), BN) - 4 * grp;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sacc[qb][kb][i] = (16 * kb + i > t || 16 * kb + i < tl) ? -INFINITY : sacc[qb][kb][i];
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sacc[qb][kb][i] = (16 * kb + i > t) ? -INFINITY : sacc[qb][kb][i];
-        }
-        if constexpr (UMASK) {
-          // ... and allowed by the user mask: the 4 bytes of this lane's keys
-          // 16*kb + 4*grp .. +3 (byte reads past the last key row).
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const int k0 = kt * BN + 16 * kb + 4 * grp;
-            uint32_t w = 0;
-            if (k0 + 4 <= p.skv) {
-              w = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (k0 + i < p.skv) w |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sacc[qb][kb][i] = ((w >> (8 * i)) & 0xffu) ? sacc[qb][kb][i] : -INFINITY;
-          }
-        }
-      }
-    }
-
-    // Probabilities of tile j against the current running max (no max is
-    // taken on this path: see the check after the slots).
-    bf16x8 opnd[NBUF];
-    float mneg[QB], tsum[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      mneg[qb] = (m_run[qb] == -INFINITY) ? 0.0f : -m_run[qb];
-      tsum[qb] = 0.0f;
-    }
-    // Pair (i, i+1) of key block kb goes to elements 4*(kb%2) + i, +1 of the
-    // P^T operand of k-step kb/2: the key order of the V^T reads.
-    auto prob_pair = [&](int rq, int kb, int i, float mn, float &sum) {
-      // The row sum uses the unrounded fp32 probabilities (summing the bf16
-      // values instead costs up to 2^-8 relative error in short rows).
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kb][i], c, mn));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kb][i + 1], c, mn));
-      sum += p0;
-      sum += p1;
-      const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-      pcur[rq][kb >> 1][4 * (kb & 1) + i] = t2[0];
-      pcur[rq][kb >> 1][4 * (kb & 1) + i + 1] = t2[1];
-    };
-    static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_opnd(KS{}, VS{}, o); });
-    static_for<NSLOT>([&](auto t_tag) {
-      constexpr int t = decltype(t_tag)::value;
-      constexpr int o = t / QB, qb = t % QB;
-      if constexpr (qb == 0 && o + AHEAD < NOP)
-        opnd[(o + AHEAD) % NBUF] = read_opnd(KS{}, VS{}, IC<o + AHEAD>{});
-      // matrix instruction of slot t
-      if constexpr (o < NPV) {
-        constexpr int ps = o / DB, db = o % DB;
-        oacc[qb][db] = mfma16(opnd[o % NBUF], pprev[qb][ps], oacc[qb][db]);
-      } else {
-        constexpr int u = o - NPV, s = u / KB, kb = u % KB;
-        if constexpr (s == 0) {
-          f32x4 z;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[i] = 0.0f;
-          snext[qb][kb] = mfma16(opnd[o % NBUF], qf[qb][s], z);
-        } else {
-          snext[qb][kb] = mfma16(opnd[o % NBUF], qf[qb][s], snext[qb][kb]);
-        }
-      }
-      // Vector work of slot t: pair u of the NPAIR pairs (row block
-      // u / (KB*2), key block (u / 2) % KB, elements 2(u%2), 2(u%2)+1) goes
-      // to slot u * NSLOT / NPAIR.
-      constexpr int NPAIR = QB * KB * 2;
-      static_for<NPAIR>([&](auto u_tag) {
-        constexpr int u = decltype(u_tag)::value;
-        if constexpr (u * NSLOT / NPAIR == t) {
-          constexpr int rq = u / (KB * 2), kb = (u / 2) % KB, i = 2 * (u % 2);
-          prob_pair(rq, kb, i, mneg[rq], tsum[rq]);
-        }
-      });
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    // Pin P(j) and the tile sums to the slots above: without a use here the
-    // compiler sinks the exponentials past the branch below, away from the
-    // products they are meant to overlap.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int ps = 0; ps < PSTEPS; ++ps) asm volatile("" ::"v"(pcur[qb][ps]));
-      asm volatile("" ::"v"(tsum[qb]));
-    }
-
-    // The running max is only a reference point: the probabilities above are
-    // exact as long as none overflows. While every lane's partial tile sum
-    // stays at most 2^16 (so every probability does), they are kept.
-    // Otherwise -- the first tile of a row (no reference yet), a score more
-    // than 16 (log2) above the reference, or a non-finite sum -- the row max
-    // is taken, O and the row sum are rescaled to it (after this step's
-    // PV(j-1) products, which used the old reference) and the tile's
-    // probabilities are recomputed.
-    bool redo = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) redo = redo || !(tsum[qb] <= kSumLimit) || m_run[qb] == -INFINITY;
-    if (__any(redo)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float m = sacc[qb][0][0];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[qb][kb][i]);
-        const float mr = quad_max(m) * c;
-        const float m_new = fmaxf(m_run[qb], mr);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[qb][db][i] *= alpha;
-        l_part[qb] *= alpha;
-        m_run[qb] = m_new;
-        const float mn = (m_new == -INFINITY) ? 0.0f : -m_new;
-        tsum[qb] = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; i += 2) prob_pair(qb, kb, i, mn, tsum[qb]);
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_part[qb] += tsum[qb];
-    wait_vmem_all();   // this wave's rows of the tiles loaded above are in LDS
-    __syncthreads();
-  };
-
-  for (int j = 0; j < ntiles; j += UNROLL) {
-    step(IC<0>{}, j);
-    if (j + 1 < ntiles) step(IC<1>{}, j + 1);
-    if (j + 2 < ntiles) step(IC<2>{}, j + 2);
-    if (j + 3 < ntiles) step(IC<3>{}, j + 3);
-    if (j + 4 < ntiles) step(IC<4>{}, j + 4);
-    if (j + 5 < ntiles) step(IC<5>{}, j + 5);
-  }
-  // The last tile's PV product.
-  if (ntiles > 0) {
-    const int last = ntiles - 1;
-    if (last & 1) pv(last % VSTAGES, pbuf[1]);
-    else pv(last % VSTAGES, pbuf[0]);
-  }
-
-  // ---- epilogue -------------------------------------------------------------
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = quad_sum(l_part[qb]);
-    if (!qvalid[qb]) continue;
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + head * p.o_sh + (int64_t)local_row[qb] * p.o_ss;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      bf16x4 o4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[qb][db][e] * inv);
-      *reinterpret_cast<bf16x4 *>(op + 16 * db + 4 * grp) = o4;
-    }
-    if (grp == 0) {
-      const float lse = l > 0.0f ? (m_run[qb] + __log2f(l)) * kLn2 : -INFINITY;
-      p.lse[((int64_t)b * p.hq + head) * p.sq + local_row[qb]] = lse;
-    }
-  }
-}
-
-template <int D>
-int launch_d(const FwdParams &p, void *stream) {
-  const int64_t grid = fwd_grid_size(p);
-  if (grid == 0) return 0;
-  const int rb = NW / p.heads_per_item;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int mode = p.mask ? 3 : p.docs.n > 0 ? 2 : (p.kv.n > 1 ? 1 : 0);
-  switch (rb * 4 + mode) {
-    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 0>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 9: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 1>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 10: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 11: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 3>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 0>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 17: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 1>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 18: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 2>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 19: hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 3>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 0>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 33: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 1>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 34: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 2>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 35: hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, 3>), dim3(grid), dim3(NT), 0, s, p); break;
-    default: return (int)hipErrorInvalidValue;
-  }
-  return (int)hipGetLastError();
-}
-
-}  // namespace
 
 int launch_fwd_bf16(const FwdParams &p, int head_dim, void *stream) {
-  if (head_dim == 128) return launch_d<128>(p, stream);
-  if (head_dim == 64) return launch_d<64>(p, stream);
-  return (int)hipErrorInvalidValue;
+  if (p.mask) return launch_fwd_bf16_m3(p, head_dim, stream);
+  if (p.docs.n > 0) return launch_fwd_bf16_m2(p, head_dim, stream);
+  if (p.kv.n > 1) return launch_fwd_bf16_m1(p, head_dim, stream);
+  return launch_fwd_bf16_m0(p, head_dim, stream);
 }
 
 }  // namespace cpattn

@@ -152,6 +152,20 @@ int64_t fwd_grid_size(const FwdParams &p);
 
 // Launchers (defined with their kernels); return a hipError_t as int.
 int launch_fwd_bf16(const FwdParams &p, int head_dim, void *stream);
+// Per-mode instantiations (0: natural order, 1: KV chunk table, 2: packed
+// sequences, 3: user mask), each compiled in a file of its own.
+int launch_fwd_bf16_m0(const FwdParams &p, int head_dim, void *stream);
+int launch_fwd_bf16_m1(const FwdParams &p, int head_dim, void *stream);
+int launch_fwd_bf16_m2(const FwdParams &p, int head_dim, void *stream);
+int launch_fwd_bf16_m3(const FwdParams &p, int head_dim, void *stream);
+int launch_bwd_dq_m0(const BwdParams &p, int head_dim, void *stream);
+int launch_bwd_dq_m1(const BwdParams &p, int head_dim, void *stream);
+int launch_bwd_dq_m2(const BwdParams &p, int head_dim, void *stream);
+int launch_bwd_dq_m3(const BwdParams &p, int head_dim, void *stream);
+// dK/dV: 0 plain (natural order or a KV chunk table), 1 packed sequences, 2 user mask.
+int launch_bwd_dkdv_m0(const BwdParams &p, int head_dim, void *stream);
+int launch_bwd_dkdv_m1(const BwdParams &p, int head_dim, void *stream);
+int launch_bwd_dkdv_m2(const BwdParams &p, int head_dim, void *stream);
 int launch_fwd_fp32(const FwdParams &p, int head_dim, void *stream);
 // `events` is NULL or four hipEvent_t recorded at the phase boundaries.
 int launch_bwd_bf16(const BwdParams &p, int head_dim, void *stream, void *const *events);
