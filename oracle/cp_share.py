@@ -161,9 +161,11 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
         out_i = sum_{j in A_i} exp(s_ij - LSE_i) v_j
     A row with no visible key gets out = 0 and LSE = -inf. ``doc_starts``
     restricts A_i to the row's own packed sequence (see ``visible``).
-    ``user_mask`` (bool, broadcastable to [B, Hq, Sq, Skv]) is the caller's
-    attention mask: [CP-migration] §8 merges a boolean mask with the CP mask
-    by logical AND (a key must be visible under both), never replacing it.
+    ``user_mask`` (broadcastable to [B, Hq, Sq, Skv]) is the caller's
+    attention mask, merged with the CP mask and never replacing it
+    ([CP-migration] §8): a boolean mask by logical AND (a key must be visible
+    under both); a floating-point mask is additive (added to the scaled
+    scores, -inf hides a key) and the CP mask hides what it hides.
 
     Rows are independent, so they are visited in blocks of ``row_block`` only to
     bound memory; nothing is reordered within a row.
@@ -183,10 +185,14 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
             for r0 in range(0, Sq, row_block):
                 r1 = min(Sq, r0 + row_block)
                 vis = visible(q_pos[r0:r1], kv_pos, causal, doc_starts)
-                if user_mask is not None:
-                    um = np.broadcast_to(user_mask, (B, Hq, Sq, Skv))
-                    vis = vis & um[b, h, r0:r1]
                 s = scale * (q[b, h, r0:r1] @ k[b, hk].T)
+                if user_mask is not None:
+                    um = np.broadcast_to(user_mask, (B, Hq, Sq, Skv))[b, h, r0:r1]
+                    if um.dtype == bool:
+                        vis = vis & um
+                    else:
+                        s = s + um
+                        vis = vis & (um != -np.inf)
                 s = np.where(vis, s, -np.inf)
                 m = s.max(axis=1)
                 has = np.isfinite(m)
@@ -247,9 +253,13 @@ def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
         """P and dS of a block of rows against the keys kk/vv at positions kpos
         (um: the user mask of those rows and keys)."""
         vis = visible(pos_b, kpos, causal, doc_starts) & has[:, None]
-        if um is not None:
-            vis = vis & um
         s = scale * (qb @ kk.T)
+        if um is not None:
+            if um.dtype == bool:
+                vis = vis & um
+            else:
+                s = s + np.where(um == -np.inf, 0.0, um)
+                vis = vis & (um != -np.inf)
         lse_safe = np.where(has, lse_b, 0.0)
         p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
         dp = dob @ vv.T

@@ -602,3 +602,32 @@ def test_user_mask_is_anded_with_the_cp_mask():
     o2, _ = oc.attention_rows(q.numpy()[:, :, sh["q_pos"]], k.numpy(), v.numpy(), sh["q_pos"], pos, 0.6, True,
                               user_mask=um[:, :, sh["q_pos"]])
     np.testing.assert_allclose(o2, out[:, :, sh["q_pos"]], atol=1e-13)
+
+
+def test_additive_user_mask_matches_sdpa():
+    """An additive float mask (finite biases and -inf) on top of the causal
+    mask equals torch float64 SDPA given causal -inf plus the same bias,
+    forward and autograd backward."""
+    S = 20
+    p = small_problem(B=1, Hq=2, Hkv=1, S=S, D=4, seed=32, dout=True)
+    q, k, v, do = p.q.double(), p.k.double(), p.v.double(), p.dout.double()
+    rng = np.random.default_rng(32)
+    bias = rng.normal(0.0, 2.0, (1, 2, S, S))
+    bias[rng.random((1, 2, S, S)) < 0.2] = -np.inf
+    bias[:, :, np.arange(S), np.arange(S)] = 0.0                     # every row keeps its own key
+    pos = np.arange(S)
+    out, lse = oc.attention_rows(q.numpy(), k.numpy(), v.numpy(), pos, pos, 0.5, True, user_mask=bias)
+    dq, dk, dv = oc.attention_rows_bwd(q.numpy(), k.numpy(), v.numpy(), do.numpy(), pos, pos, 0.5, True,
+                                       user_mask=bias)
+    full = torch.from_numpy(np.where(np.tril(np.ones((S, S), dtype=bool)), bias, -np.inf))
+    qr, kr, vr = (t.clone().requires_grad_(True) for t in (q, k, v))
+    ref = F.scaled_dot_product_attention(qr, kr.repeat_interleave(2, dim=1), vr.repeat_interleave(2, dim=1),
+                                         attn_mask=full, scale=0.5)
+    ref.backward(do)
+    np.testing.assert_allclose(out, ref.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, qr.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dk, kr.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dv, vr.grad.numpy(), atol=1e-10)
+    # LSE: logsumexp of the biased scaled scores (torch's own).
+    sc = 0.5 * (q @ k.repeat_interleave(2, dim=1).transpose(-1, -2)) + full
+    np.testing.assert_allclose(lse, torch.logsumexp(sc, dim=-1).numpy(), atol=1e-12)
