@@ -46,7 +46,7 @@ class CpAttnDesc(ctypes.Structure):
         ("layout", _i32), ("causal", _i32), ("softmax_scale", _f32),
         ("q_strides", _i64 * 3), ("kv_strides", _i64 * 3), ("o_strides", _i64 * 3),
         ("n_docs", _i32), ("doc_starts", _p64),
-        ("attn_mask", ctypes.c_void_p), ("mask_strides", _i64 * 3),
+        ("attn_mask", ctypes.c_void_p), ("mask_strides", _i64 * 3), ("mask_additive", _i32),
     ]
 
 

@@ -37,6 +37,7 @@ class _Desc:
     def __init__(self, *, dtype, batch, hq, hkv, head_dim, sq_local, skv, q_chunk_pos,
                  kv_chunk_pos, layout, causal, softmax_scale, q_strides, kv_strides, o_strides,
                  doc_starts=(), attn_mask=None, mask_strides=(0, 0, 0)):
+        additive = attn_mask is not None and attn_mask.dtype == torch.float32
         self.qpos = (ctypes.c_int64 * max(1, len(q_chunk_pos)))(*q_chunk_pos)
         self.kvpos = (ctypes.c_int64 * max(1, len(kv_chunk_pos)))(*kv_chunk_pos)
         doc_starts = [int(x) for x in doc_starts]
@@ -60,7 +61,8 @@ class _Desc:
         self.mask = attn_mask   # keeps the tensor alive as long as the descriptor
         d.attn_mask = attn_mask.data_ptr() if attn_mask is not None else None
         for i in range(3):
-            d.mask_strides[i] = int(mask_strides[i])
+            d.mask_strides[i] = int(mask_strides[i]) * (4 if additive else 1)   # elements -> bytes
+        d.mask_additive = 1 if additive else 0
         self.desc = d
 
     def ref(self):
@@ -89,8 +91,8 @@ def _mask_args(attn_mask, q, k):
     size-1 batch or head dims broadcast (stride 0)."""
     if attn_mask is None:
         return None, (0, 0, 0)
-    if attn_mask.dtype not in (torch.bool, torch.uint8) or attn_mask.dim() != 4:
-        raise ValueError("attn_mask must be a 4-D bool or uint8 tensor [B|1, Hq|1, Sq, Skv]")
+    if attn_mask.dtype not in (torch.bool, torch.uint8, torch.float32) or attn_mask.dim() != 4:
+        raise ValueError("attn_mask must be a 4-D bool, uint8 or float32 (additive) tensor [B|1, Hq|1, Sq, Skv]")
     B, Hq, Sq, _ = q.shape
     if (attn_mask.shape[0] not in (1, B) or attn_mask.shape[1] not in (1, Hq) or attn_mask.shape[2] != Sq
             or attn_mask.shape[3] != k.shape[2]):
@@ -162,7 +164,8 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
     variable-length sequences (a global cu_seqlens without its final total):
     a key is then visible only to queries of its own sequence. attn_mask, if
     given, is a bool/uint8 [B|1, Hq|1, Sq, Skv] device tensor ANDed with the
-    CP mask (True / nonzero: may attend).
+    CP mask (True / nonzero: may attend), or a float32 one added to the scaled
+    scores (-inf hides a key).
     """
     lib = _lib.load()
     _check_inputs(q, k, v)

@@ -449,13 +449,21 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
               // query tile (of head cs.h of the group), this lane's key.
               if (key_ok[kn]) {
                 const uint8_t *mb = p.mask + b * p.m_sb + (int64_t)(hk * p.group + cs.h) * p.m_sh +
-                                    ((int64_t)cs.c * p.chunk_len + cs.t * QT) * p.m_ss + my_key[kn];
+                                    ((int64_t)cs.c * p.chunk_len + cs.t * QT) * p.m_ss;
+                const float inv = 1.0f / p.scale;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                   for (int i = 0; i < 4; ++i) {
                     const int r = 16 * rb + 4 * grp + i;
-                    if (r <= rows_left && mb[(int64_t)r * p.m_ss] == 0) sacc[rb][kn][i] = -INFINITY;
+                    if (r > rows_left) continue;
+                    if (p.mask_add) {
+                      // additive mask, in the raw score's units
+                      const float a = reinterpret_cast<const float *>(mb + (int64_t)r * p.m_ss)[my_key[kn]];
+                      sacc[rb][kn][i] = fmaf(a, inv, sacc[rb][kn][i]);
+                    } else if (mb[(int64_t)r * p.m_ss + my_key[kn]] == 0) {
+                      sacc[rb][kn][i] = -INFINITY;
+                    }
                   }
               }
             }
@@ -1012,6 +1020,27 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
             for (int i = 0; i < 4; ++i) scur[h][qb][i] = (16 * h + i > t) ? -INFINITY : scur[h][qb][i];
         }
         if constexpr (UMASK) {
+          if (p.mask_add) {
+            // ... plus the additive mask (value / softmax_scale).
+            const float inv = 1.0f / p.scale;
+            const float *mf = reinterpret_cast<const float *>(mrow[qb]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int k0 = sb * 32 + 16 * h + 4 * grp;
+              f32x4 a;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) a[i] = 0.0f;
+              if (k0 + 4 <= p.skv) {
+                a = *reinterpret_cast<const f32x4 *>(mf + k0);
+              } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (k0 + i < p.skv) a[i] = mf[k0 + i];
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) scur[h][qb][i] = fmaf(a[i], inv, scur[h][qb][i]);
+            }
+          } else {
           // ... and allowed by the user mask (keys 16*h + 4*grp .. +3 of the block).
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -1027,6 +1056,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               scur[h][qb][i] = ((w >> (8 * i)) & 0xffu) ? scur[h][qb][i] : -INFINITY;
+          }
           }
         }
       }

@@ -64,7 +64,16 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
         continue;
       }
       if (key_pos(p, j) < qds) continue;   // before this row's sequence
-      if (p.mask && p.mask[b * p.m_sb + h * p.m_sh + (int64_t)r * p.m_ss + j] == 0) continue;
+      float madd = 0.0f;   // additive user mask (natural units)
+      if (p.mask) {
+        const uint8_t *mr = p.mask + b * p.m_sb + h * p.m_sh + (int64_t)r * p.m_ss;
+        if (p.mask_add) {
+          madd = reinterpret_cast<const float *>(mr)[j];
+          if (madd == -INFINITY) continue;
+        } else if (mr[j] == 0) {
+          continue;
+        }
+      }
       const float *kj = kb + (int64_t)j * p.kv_ss;
       const float *vj = vb + (int64_t)j * p.kv_ss;
       float s = 0.0f, dp = 0.0f;
@@ -72,7 +81,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
         s = fmaf(q[d], kj[d], s);
         dp = fmaf(g[d], vj[d], dp);
       }
-      const float pij = expf(s * p.scale - lse);
+      const float pij = expf(s * p.scale + madd - lse);
       const float ds = pij * (dp - delta);
       for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, kj[d], dq[d]);
     }
@@ -100,7 +109,16 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
     for (int r = 0; r < p.sq; ++r) {
       if (p.causal && kp > row_pos(p, r)) continue;
       if (kp < seq_start(p, row_pos(p, r))) continue;   // not in the row's sequence
-      if (p.mask && p.mask[b * p.m_sb + h * p.m_sh + (int64_t)r * p.m_ss + j] == 0) continue;
+      float madd = 0.0f;   // additive user mask (natural units)
+      if (p.mask) {
+        const uint8_t *mr = p.mask + b * p.m_sb + h * p.m_sh + (int64_t)r * p.m_ss;
+        if (p.mask_add) {
+          madd = reinterpret_cast<const float *>(mr)[j];
+          if (madd == -INFINITY) continue;
+        } else if (mr[j] == 0) {
+          continue;
+        }
+      }
       const int64_t row = ((int64_t)b * p.hq + h) * p.sq + r;
       const float lse = p.lse[row];
       if (lse == -INFINITY) continue;
@@ -111,7 +129,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
         s = fmaf(q[d], kj[d], s);
         dp = fmaf(g[d], vj[d], dp);
       }
-      const float pij = expf(s * p.scale - lse);
+      const float pij = expf(s * p.scale + madd - lse);
       const float ds = pij * (dp - p.delta[row]);
       for (int d = 0; d < D; ++d) {
         dv[d] = fmaf(pij, g[d], dv[d]);

@@ -121,10 +121,12 @@ static int32_t validate(const cp_attn_desc *d) {
   // User mask: natural key order, no packed sequences, 4-byte words.
   if (d->attn_mask) {
     if (d->n_kv_chunks != 1 || d->n_docs > 0) return CP_ATTN_ERR_UNSUPPORTED;
-    if (reinterpret_cast<uintptr_t>(d->attn_mask) & 3u) return CP_ATTN_ERR_ALIGNMENT;
+    if (d->mask_additive != 0 && d->mask_additive != 1) return CP_ATTN_ERR_BAD_SHAPE;
+    const int64_t al = d->mask_additive ? 16 : 4;
+    if (reinterpret_cast<uintptr_t>(d->attn_mask) % al) return CP_ATTN_ERR_ALIGNMENT;
     for (int i = 0; i < 3; ++i) {
       if (d->mask_strides[i] < 0) return CP_ATTN_ERR_BAD_SHAPE;
-      if (d->mask_strides[i] % 4 != 0) return CP_ATTN_ERR_ALIGNMENT;
+      if (d->mask_strides[i] % al != 0) return CP_ATTN_ERR_ALIGNMENT;
     }
   }
   // Strides: non-negative, and every row start 16-byte aligned given an
@@ -152,7 +154,8 @@ static void fill_kv_chunks(const cp_attn_desc *d, KvChunks *kv) {
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   memset(p, 0, sizeof(*p));
   collect_doc_bounds(d, &p->docs);
-  p->mask = d->attn_mask;
+  p->mask = static_cast<const uint8_t *>(d->attn_mask);
+  p->mask_add = d->mask_additive;
   p->m_sb = d->mask_strides[0]; p->m_sh = d->mask_strides[1]; p->m_ss = d->mask_strides[2];
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
@@ -181,7 +184,8 @@ void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
 void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
   memset(p, 0, sizeof(*p));
   collect_doc_bounds(d, &p->docs);
-  p->mask = d->attn_mask;
+  p->mask = static_cast<const uint8_t *>(d->attn_mask);
+  p->mask_add = d->mask_additive;
   p->m_sb = d->mask_strides[0]; p->m_sh = d->mask_strides[1]; p->m_ss = d->mask_strides[2];
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];

@@ -457,6 +457,28 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
               sacc[qb][kb][i] = (16 * kb + i > t) ? -INFINITY : sacc[qb][kb][i];
         }
         if constexpr (UMASK) {
+          if (p.mask_add) {
+            // ... plus the additive mask: 4 floats of this lane's keys per
+            // block, in the raw score's units (value / softmax_scale).
+            const float inv = 1.0f / p.scale;
+            const float *mf = reinterpret_cast<const float *>(mrow[qb]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              const int k0 = kt * BN + 16 * kb + 4 * grp;
+              f32x4 a;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) a[i] = 0.0f;
+              if (k0 + 4 <= p.skv) {
+                a = *reinterpret_cast<const f32x4 *>(mf + k0);
+              } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (k0 + i < p.skv) a[i] = mf[k0 + i];
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sacc[qb][kb][i] = fmaf(a[i], inv, sacc[qb][kb][i]);
+            }
+          } else {
           // ... and allowed by the user mask: the 4 bytes of this lane's keys
           // 16*kb + 4*grp .. +3 (byte reads past the last key row).
 #pragma unroll
@@ -473,6 +495,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               sacc[qb][kb][i] = ((w >> (8 * i)) & 0xffu) ? sacc[qb][kb][i] : -INFINITY;
+          }
           }
         }
       }

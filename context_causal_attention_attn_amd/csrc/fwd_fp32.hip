@@ -80,11 +80,19 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
       const int nk = min(kKeys, nvis - j0);
       for (int r = 0; r < nk; ++r) {
         if (p.causal && (kpos + j0 + r > qpos || kpos + j0 + r < ds)) continue;
-        if (mrow && mrow[krow0 + j0 + r] == 0) continue;
+        float madd = 0.0f;   // additive user mask (natural units)
+        if (mrow) {
+          if (p.mask_add) {
+            madd = reinterpret_cast<const float *>(mrow)[krow0 + j0 + r];
+            if (madd == -INFINITY) continue;
+          } else if (mrow[krow0 + j0 + r] == 0) {
+            continue;
+          }
+        }
         float s = 0.0f;
 #pragma unroll
         for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[r][d], s);
-        s *= scale;
+        s = s * scale + madd;
         const float m_new = fmaxf(m, s);
         const float alpha = expf(m - m_new);   // 0 on the first visible key
         const float w = expf(s - m_new);

@@ -61,6 +61,7 @@ struct FwdParams {
   DocBounds docs;               // packed-sequence boundaries (n = 0: none)
   const uint8_t *mask;          // user attention mask (NULL: none), [b][h][row][key]
   int64_t m_sb, m_sh, m_ss;     // its byte strides (batch, head, row)
+  int32_t mask_add;             // 0: bytes (nonzero = may attend); 1: float32 added to the scaled score
   int32_t hq, hkv, group;       // group = hq / hkv
   int32_t heads_per_item;       // query heads of one KV group packed in a work item
   int32_t n_head_packs;         // batch * hq / heads_per_item
@@ -133,6 +134,7 @@ struct BwdParams {
   DocBounds docs;               // packed-sequence boundaries (n = 0: none)
   const uint8_t *mask;          // user attention mask (NULL: none), [b][h][row][key]
   int64_t m_sb, m_sh, m_ss;     // its byte strides (batch, head, row)
+  int32_t mask_add;             // 0: bytes (nonzero = may attend); 1: float32 added to the scaled score
   int32_t batch, hq, hkv, group;
   int32_t sq, skv;
   int32_t chunk_len, n_q_chunks;

@@ -122,11 +122,13 @@ typedef enum {
  * or before it, every start inside it, the first start after it); more than
  * CP_ATTN_MAX_DOC_BOUNDS of them is CP_ATTN_ERR_UNSUPPORTED.
  *
- * A user attention mask ([CP-migration] §8: a boolean mask is merged with the
- * CP mask by logical AND, never replaced): with attn_mask != NULL, key j is
- * visible to query i only if also attn_mask[b][h][i][j] != 0 (i the local
- * row, j the key row). Requires one KV chunk and no packed sequences; the
- * pointer and the strides must be multiples of 4 bytes. The mask is read by
+ * A user attention mask ([CP-migration] §8: merged with the CP mask, never
+ * replacing it): with attn_mask != NULL and mask_additive == 0, key j is
+ * visible to query i only if also attn_mask[b][h][i][j] != 0 (bytes; i the
+ * local row, j the key row); with mask_additive == 1 the float32 value is
+ * added to softmax_scale * q.k (-inf hides the key). Requires one KV chunk and
+ * no packed sequences; the pointer and strides must be multiples of 4 bytes
+ * (16 for an additive mask). The mask is read by
  * the kernels during the call's work on the stream; the caller keeps it alive
  * like the other device buffers.
  *
@@ -154,8 +156,9 @@ typedef struct cp_attn_desc {
                                /* all strides >= 0, multiples of 16 bytes; row strides < 2^24 */
   int32_t n_docs;              /* 0: one sequence; > 0: packed sequences (needs causal, one KV chunk) */
   const int64_t *doc_starts;   /* host array [n_docs]: strictly increasing global start positions, >= 0 */
-  const uint8_t *attn_mask;    /* NULL, or DEVICE bytes [batch][hq][sq_local][skv]: nonzero = may attend */
+  const void *attn_mask;       /* NULL, or DEVICE [batch][hq][sq_local][skv] mask of mask_additive's kind */
   int64_t mask_strides[3];     /* batch, head, row strides of attn_mask in bytes (0 broadcasts); key stride 1 */
+  int32_t mask_additive;       /* 0: bytes, nonzero = may attend; 1: float32 added to the scaled score */
 } cp_attn_desc;
 
 /* ABI version of the loaded library (CP_ATTN_ABI_VERSION of its build). */

@@ -27,6 +27,10 @@ def make_mask(kind, osh, B, Hq, S, rng):
     if kind == "window":            # keys at most 300 positions back, all heads
         m = (q_pos[:, None] - np.arange(S)[None, :]) < 300
         m = np.broadcast_to(m, (B, 1) + m.shape).copy()
+    elif kind == "additive":        # float biases, 15 % -inf, some rows fully hidden
+        m = rng.normal(0.0, 1.5, (B, Hq, q_pos.size, S)).astype(np.float32)
+        m[rng.random(m.shape) < 0.15] = -np.inf
+        m[:, :, ::37] = -np.inf
     else:                           # random per head, 25 % hidden, some rows fully hidden
         m = rng.random((B, Hq, q_pos.size, S)) < 0.75
         m[:, :, ::37] = False
@@ -40,6 +44,9 @@ CASES = [
     ("random", "contiguous", 1000, 4, 2, 64, 2, "bf16"),     # ragged key count (1000)
     ("random", "head_tail", 1024, 4, 4, 128, 4, "bf16"),
     ("random", "head_tail", 512, 2, 1, 64, 4, "fp32"),
+    ("additive", "head_tail", 2048, 8, 2, 128, 4, "bf16"),
+    ("additive", "contiguous", 1000, 4, 2, 64, 2, "bf16"),    # ragged key count
+    ("additive", "contiguous", 512, 2, 1, 64, 4, "fp32"),
 ]
 
 
@@ -66,10 +73,11 @@ def test_user_mask_fwd_bwd_all_ranks(case):
         torch.cuda.synchronize()
         rows = torch.from_numpy(osh["q_pos"])
         qs, dos = to_f64(prob.q[:, :, rows]), to_f64(prob.dout[:, :, rows])
+        mo = m if m.dtype == bool else m.astype(np.float64)
         ref_o, ref_l = oc.attention_rows(qs, to_f64(prob.k), to_f64(prob.v), osh["q_pos"], osh["kv_pos"], scale,
-                                         True, user_mask=m)
+                                         True, user_mask=mo)
         ref_g = oc.attention_rows_bwd(qs, to_f64(prob.k), to_f64(prob.v), dos, osh["q_pos"], osh["kv_pos"],
-                                      scale, True, user_mask=m)
+                                      scale, True, user_mask=mo)
         o, l = to_f64(out), to_f64(lse)
         assert np.array_equal(np.isneginf(l), np.isneginf(ref_l)), "fully masked rows differ"
         fin = np.isfinite(ref_l)
@@ -79,5 +87,5 @@ def test_user_mask_fwd_bwd_all_ranks(case):
         print(f"mask {case} r{r}: out {err_o:.3e} lse {err_l:.3e} dq {errs[0]:.3e} dk {errs[1]:.3e} "
               f"dv {errs[2]:.3e}", flush=True)
         assert err_o <= tol_o and err_l <= tol_l and max(errs) <= tol_g
-        if mask_kind == "random":
+        if mask_kind in ("random", "additive"):
             assert torch.all(out[:, :, ::37] == 0) and torch.all(dq[:, :, ::37] == 0)
