@@ -43,6 +43,14 @@ __all__ = [
 ]
 
 
+# Reading of the additive user mask ([CP-migration] §8: a float attn_mask is
+# added to the scores and hidden keys get -inf): padding masks write "hidden"
+# as -inf or as a large negative number (-1e4, -1e9, the float32 minimum).
+# Values at or below MASK_HIDE hide their key exactly like -inf; values above
+# it are biases added to the scaled score.
+MASK_HIDE = -1.0e4
+
+
 # ----------------------------------------------------------------------------
 # Head mapping and visibility
 # ----------------------------------------------------------------------------
@@ -165,7 +173,9 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
     attention mask, merged with the CP mask and never replacing it
     ([CP-migration] §8): a boolean mask by logical AND (a key must be visible
     under both); a floating-point mask is additive (added to the scaled
-    scores, -inf hides a key) and the CP mask hides what it hides.
+    scores; a value at or below MASK_HIDE, -inf included, hides the key) and
+    the CP mask hides what it hides. The LSE then includes the bias:
+    LSE_i = ln sum_{j in A_i} exp(s_ij + mask_ij).
 
     Rows are independent, so they are visited in blocks of ``row_block`` only to
     bound memory; nothing is reordered within a row.
@@ -191,8 +201,9 @@ def attention_rows(q, k, v, q_pos, kv_pos, scale: float, causal: bool = True,
                     if um.dtype == bool:
                         vis = vis & um
                     else:
-                        s = s + um
-                        vis = vis & (um != -np.inf)
+                        hidden = um <= MASK_HIDE
+                        s = s + np.where(hidden, 0.0, um)
+                        vis = vis & ~hidden
                 s = np.where(vis, s, -np.inf)
                 m = s.max(axis=1)
                 has = np.isfinite(m)
@@ -258,8 +269,9 @@ def attention_rows_bwd(q, k, v, dout, q_pos, kv_pos, scale: float,
             if um.dtype == bool:
                 vis = vis & um
             else:
-                s = s + np.where(um == -np.inf, 0.0, um)
-                vis = vis & (um != -np.inf)
+                hidden = um <= MASK_HIDE
+                s = s + np.where(hidden, 0.0, um)
+                vis = vis & ~hidden
         lse_safe = np.where(has, lse_b, 0.0)
         p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
         dp = dob @ vv.T

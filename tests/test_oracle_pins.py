@@ -631,3 +631,56 @@ def test_additive_user_mask_matches_sdpa():
     # LSE: logsumexp of the biased scaled scores (torch's own).
     sc = 0.5 * (q @ k.repeat_interleave(2, dim=1).transpose(-1, -2)) + full
     np.testing.assert_allclose(lse, torch.logsumexp(sc, dim=-1).numpy(), atol=1e-12)
+
+
+def test_additive_hide_values_equal_the_boolean_mask():
+    """Additive values at or below the hide threshold (-1e4, -1e9, -1e30, the
+    float32 minimum, -inf) hide their key: such a mask (with 0 elsewhere)
+    gives the same out, LSE and gradients as the boolean mask of its 0
+    entries, whose AND with the CP mask is pinned against torch SDPA above.
+    Rows where every key is hidden get out = 0, LSE = -inf and no gradient."""
+    S = 24
+    p = small_problem(B=1, Hq=4, Hkv=2, S=S, D=6, seed=33, dout=True)
+    q, k, v, do = (t.double().numpy() for t in (p.q, p.k, p.v, p.dout))
+    rng = np.random.default_rng(33)
+    keep = rng.random((1, 4, S, S)) < 0.6
+    keep[:, :, 5] = False                                          # a fully padded row
+    hides = np.array([-1e4, -1e9, -1e30, float(np.finfo(np.float32).min), -np.inf])
+    bias = np.where(keep, 0.0, hides[rng.integers(0, hides.size, keep.shape)])
+    pos = np.arange(S)
+    ob, lb = oc.attention_rows(q, k, v, pos, pos, 0.4, True, user_mask=keep)
+    oa, la = oc.attention_rows(q, k, v, pos, pos, 0.4, True, user_mask=bias)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+    gb = oc.attention_rows_bwd(q, k, v, do, pos, pos, 0.4, True, user_mask=keep)
+    ga = oc.attention_rows_bwd(q, k, v, do, pos, pos, 0.4, True, user_mask=bias)
+    for x, y in zip(ga, gb):
+        np.testing.assert_array_equal(x, y)
+    assert np.all(oa[:, :, 5] == 0) and np.all(la[:, :, 5] == -np.inf)
+    assert np.all(ga[0][:, :, 5] == 0)
+
+
+def test_additive_bias_above_the_threshold_shifts_the_lse():
+    """A bias just above the hide threshold is a bias: when every key of a
+    row carries the same bias c, softmax is unchanged and the LSE moves by
+    exactly c (closed form), for c = -9999 and for a large positive c."""
+    S = 16
+    p = small_problem(B=1, Hq=2, Hkv=1, S=S, D=4, seed=34, dout=True)
+    q, k, v, do = (t.double().numpy() for t in (p.q, p.k, p.v, p.dout))
+    pos = np.arange(S)
+    o0, l0 = oc.attention_rows(q, k, v, pos, pos, 0.5, True)
+    g0 = oc.attention_rows_bwd(q, k, v, do, pos, pos, 0.5, True)
+    for c in (-9999.0, 5000.0):
+        bias = np.full((1, 1, S, S), c)
+        o1, l1 = oc.attention_rows(q, k, v, pos, pos, 0.5, True, user_mask=bias)
+        np.testing.assert_allclose(o1, o0, atol=1e-12)
+        np.testing.assert_allclose(l1, l0 + c, atol=1e-9)
+        g1 = oc.attention_rows_bwd(q, k, v, do, pos, pos, 0.5, True, user_mask=bias)
+        for x, y in zip(g1, g0):
+            np.testing.assert_allclose(x, y, atol=1e-10)
+
+
+def test_planted_hide_threshold_mistake_is_caught(monkeypatch):
+    """Hiding only -inf (the threshold ignored) breaks the boolean-mask pin."""
+    monkeypatch.setattr(oc, "MASK_HIDE", -np.inf)
+    assert _fails(test_additive_hide_values_equal_the_boolean_mask)
