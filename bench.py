@@ -6,11 +6,13 @@ forward (out + LSE) and the backward (Delta pass, dK/dV kernel, dQ kernel) of
 the Colossal (all-gather) share of rank 7 of cp=8 at S = 32768: B = 1, 32 query
 heads over 8 KV heads (GQA), head_dim 128, bf16 inputs with fp32 accumulation,
 query rows 28672..32767 against all 32768 keys. Inputs are iid N(0, 1) rounded
-to bf16 (seed 0) and resident in HBM before timing starts.
+to bf16 (seed 0) and resident in HBM before timing starts. `value` is that
+step's throughput.
 
 FLOPs are causal-effective: only visible (query, key) pairs count, 4*D per pair
 for the forward and 10*D per pair for the backward (its five contractions,
-including the recomputed Q K^T). Peak: 2.5 PFLOP/s dense bf16 MFMA.
+including the recomputed Q K^T). Peak: 2516.6 TFLOP/s dense bf16 MFMA (256 CUs x
+4096 flop per clock x 2.4 GHz).
 
 Each kernel's time is the average, over the timed steps, of HIP events the
 library records on the launch stream around it (cp_attn_bwd_timed); the
@@ -18,15 +20,17 @@ roofline object describes the kernel with the largest average. Its "traffic"
 comes from the rocprofv3 counter summaries in profiles/ when one matches the
 kernel's current source text, else null.
 
-After the timed region the step keeps running for about 2.5 s while amd-smi
-reads the GFX clocks and socket power three times ("clock": the read at the
-highest socket power, and every read; the chip runs at its
-power cap, well below the 2.4 GHz the peak assumes). Prints ONE JSON line.
-`--detail` adds every other share of the workload list to that line under
-"detail"; the Head-Tail backward shares appear twice, the second time with
-K/V in all-gather order (".../gathered_kv": a 16-entry KV chunk table),
-and "ulysses_relayout" times the four local steps of the Ulysses exchange on
-the Ulysses workload's tensors against the HBM roofline.
+After the headline share, the line times every other share the workloads
+state a target for ("configs", forward and backward each): the Head-Tail
+shares of all 8 ranks (with their max/min spread under "balance"), the Ulysses
+cp=8 rank-0 share, the Hybrid U=2 x C=4 rank-4 share and the Head-Tail B = 2
+backward shares of ranks 0 and 7, and the Colossal rank-7 share over eight
+packed sequences. While the headline step keeps running for
+about 2.5 s, amd-smi reads the GFX clocks and socket power ("clock"; the chip
+runs at its power cap, below the 2.4 GHz the peak assumes). The oracle's CPU
+baseline runs last, in a child process. Prints ONE JSON line. `--detail` adds
+every bf16 workload share (K/V in all-gather order, packed sequences) and the
+Ulysses re-layouts under "detail".
 """
 from __future__ import annotations
 
@@ -41,7 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 flop/clock x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "colossal_cp8_r7_s32k_gqa32x8_d128"
 
@@ -56,7 +60,11 @@ def parse():
                     help="CP rank of the workload's share (default: the workload's first listed rank)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock/power sample")
-    ap.add_argument("--detail", action="store_true", help="also time every other share")
+    ap.add_argument("--detail", action="store_true",
+                    help="also time every bf16 workload share (gathered K/V orders, packed sequences) "
+                         "and the Ulysses re-layouts")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the headline share (skip the other target shares)")
     ap.add_argument("--kv-order", choices=["natural", "gathered"], default="natural",
                     help="K/V in natural order, or as an all-gather delivers them (a KV chunk table)")
     ap.add_argument("--relayout-only", action="store_true",
@@ -340,56 +348,142 @@ def time_ulysses_relayout(prob, U, reps=24, sets=6):
             "steps": res}
 
 
-def cpu_baseline(spec, prob, rank):
-    """The oracle as it stands, on a bounded sample of the same share: the
-    query heads of the first GQA group (they read KV head 0), every local row,
-    forward + backward (about 10 s on 16 host threads)."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+CPU_SAMPLE = r"""
+import json, math, os, sys, time
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+from threadpoolctl import threadpool_info
+import oracle.cp_share as oc
+from synthetic import workload
+spec, prob = workload(sys.argv[2], seed=0)
+rank = int(sys.argv[3])
+kind, cp, U = spec["kind"], spec["cp"], spec.get("ulysses", 2)
+S, Hq, Hkv, D = spec["seq"], spec["hq"], spec["hkv"], spec["head_dim"]
+if kind == "contiguous":
+    sh = oc.contiguous_share(S, Hq, Hkv, cp, rank)
+elif kind == "head_tail":
+    sh = oc.head_tail_share(S, Hq, Hkv, cp, rank)
+elif kind == "ulysses":
+    sh = oc.ulysses_share(S, Hq, Hkv, cp, rank)
+else:
+    sh = oc.hybrid_share(S, Hq, Hkv, cp, U, rank)
+G = len(sh["q_heads"]) // len(sh["kv_heads"])
+h, hk = int(sh["q_heads"][0]), int(sh["kv_heads"][0])
+q = prob.q[:1, h:h + G].double().numpy()[:, :, sh["q_pos"]]
+k = prob.k[:1, hk:hk + 1].double().numpy()
+v = prob.v[:1, hk:hk + 1].double().numpy()
+do = np.random.default_rng(0).standard_normal(q.shape)
+t0 = time.perf_counter()
+oc.attention_rows_bwd(q, k, v, do, sh["q_pos"], sh["kv_pos"], 1.0 / math.sqrt(D), True)
+dt = time.perf_counter() - t0
+pairs = oc.share_pairs(sh["q_pos"], sh["kv_pos"])
+threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+print(json.dumps({"seconds": dt, "pairs": int(pairs), "G": G, "h": h, "hk": hk, "threads": threads,
+                  "rows": int(len(sh["q_pos"])), "heads": int(len(sh["q_heads"]))}))
+"""
 
-    import oracle.cp_share as oc
 
-    kind, cp, r, U = share_for(spec, rank)
-    S, Hq, Hkv = spec["seq"], spec["hq"], spec["hkv"]
-    if kind == "contiguous":
-        sh = oc.contiguous_share(S, Hq, Hkv, cp, r)
-    elif kind == "head_tail":
-        sh = oc.head_tail_share(S, Hq, Hkv, cp, r)
-    elif kind == "ulysses":
-        sh = oc.ulysses_share(S, Hq, Hkv, cp, r)
-    else:
-        sh = oc.hybrid_share(S, Hq, Hkv, cp, U, r)
-    G = len(sh["q_heads"]) // len(sh["kv_heads"])
-    h, hk = int(sh["q_heads"][0]), int(sh["kv_heads"][0])
-    D = spec["head_dim"]
-    q = prob.q[:1, h:h + G].double().numpy()[:, :, sh["q_pos"]]
-    k = prob.k[:1, hk:hk + 1].double().numpy()
-    v = prob.v[:1, hk:hk + 1].double().numpy()
-    do = (prob.dout[:1, h:h + G].double().numpy()[:, :, sh["q_pos"]] if prob.dout is not None
-          else np.random.default_rng(0).standard_normal(q.shape))
-    scale = 1.0 / math.sqrt(D)
-    t0 = time.perf_counter()
-    oc.attention_rows_bwd(q, k, v, do, sh["q_pos"], sh["kv_pos"], scale, True)
-    dt = time.perf_counter() - t0
-    pairs = oc.share_pairs(sh["q_pos"], sh["kv_pos"])
-    flops = 14.0 * D * G * pairs   # forward (4D) + backward (10D) per visible pair and head
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    cpu_model = None
+def cpu_model_name():
     try:
         with open("/proc/cpuinfo") as fh:
             for ln in fh:
                 if ln.startswith("model name"):
-                    cpu_model = ln.split(":", 1)[1].strip()
-                    break
+                    return ln.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model,
-            "sample": f"{kind} share rank {r}: query heads {h}..{h + G - 1} (the GQA group of KV head {hk}; "
-                      f"{G} of {len(sh['q_heads'])}), "
-                      f"all {len(sh['q_pos'])} local rows, forward+backward in fp64 NumPy; "
+    return None
+
+
+def cpu_baseline(spec, name, rank):
+    """The oracle as it stands, on a bounded sample of the same share, in a
+    child process of its own (NumPy fp64 with its BLAS threads over every CPU
+    this process may run on): the query heads of the first GQA group (they
+    read KV head 0), every local row, forward + backward (about 10 s on 16
+    host threads). The child regenerates the seeded problem; only the oracle
+    call is timed."""
+    import subprocess
+    D = spec["head_dim"]
+    r = subprocess.run([sys.executable, "-c", CPU_SAMPLE, ROOT, name, str(rank)], capture_output=True,
+                       text=True, timeout=600)
+    if r.returncode != 0:
+        return {"value": None, "error": r.stderr[-400:]}
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    flops = 14.0 * D * res["G"] * res["pairs"]   # forward (4D) + backward (10D) per visible pair and head
+    dt = res["seconds"]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": res["threads"], "kind": "oracle",
+            "cpu_model": cpu_model_name(), "cpus_available": len(os.sched_getaffinity(0)),
+            "sample": f"{spec['kind']} share rank {rank}: query heads {res['h']}..{res['h'] + res['G'] - 1} "
+                      f"(the GQA group of KV head {res['hk']}; {res['G']} of {res['heads']}), all {res['rows']} "
+                      f"local rows, forward+backward in fp64 NumPy in a child process; "
                       f"{dt:.1f} s for {flops / 1e9:.1f} causal-effective GFLOP",
             "seconds": dt}
+
+
+# Every other share the workload list states a target for, timed on the
+# default line after the headline share: (workload, ranks), plus the
+# packed-sequence Colossal share. The Colossal, Head-Tail, Ulysses, Hybrid and
+# packed shares are all cut from the same seeded B = 1 problem; the Head-Tail
+# backward shares from their own B = 2 one.
+CONFIG_SHARES = [
+    ("head_tail_cp8_s32k_gqa32x8_d128", list(range(8))),
+    ("ulysses_cp8_s32k_gqa32x8_d128", [0]),
+    ("hybrid_u2_c4_s32k_gqa32x8_d128", [4]),
+    ("head_tail_bwd_b2_cp8_s32k_gqa32x8_d128", [0, 7]),
+    ("colossal_packed_cp8_r7_s32k_gqa32x8_d128", [7]),
+]
+
+
+def share_entry(rr):
+    """Per-share timing record: forward and (when timed) backward, with the
+    three backward kernels."""
+    t, fl = rr["ms"], rr["flops"]
+
+    def tf(f, ms):
+        return f / (ms * 1e-3) / 1e12
+
+    ent = {"fwd_ms": round(t["fwd"], 4), "fwd_tflops": round(tf(fl["fwd"], t["fwd"]), 2),
+           "fwd_frac": round(tf(fl["fwd"], t["fwd"]) / PEAK_BF16_TFLOPS, 4)}
+    if rr["has_bwd"]:
+        btf = tf(fl["bwd"], t["bwd"])
+        ent.update({"bwd_ms": round(t["bwd"], 4), "bwd_tflops": round(btf, 2),
+                    "bwd_frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                    "dkdv_ms": round(t["dkdv"], 4), "dq_ms": round(t["dq"], 4),
+                    "dkdv_frac": round(tf(fl["dkdv"], t["dkdv"]) / PEAK_BF16_TFLOPS, 4),
+                    "dq_frac": round(tf(fl["dq"], t["dq"]) / PEAK_BF16_TFLOPS, 4)})
+    return ent
+
+
+def time_configs(steps, warmup, shared=None):
+    """Time every share of CONFIG_SHARES (forward and backward) after a short
+    warm-up each; `shared` is (spec, problem) of the headline problem, reused
+    by the shares cut from the same global problem."""
+    from synthetic import WORKLOADS, global_problem
+    out, cache = {}, {}
+    for name, ranks in CONFIG_SHARES:
+        sp = dict(WORKLOADS[name])
+        key = (sp["batch"], sp["hq"], sp["hkv"], sp["seq"], sp["head_dim"], sp["dtype"])
+        if shared is not None and key == tuple(shared[0][k] for k in ("batch", "hq", "hkv", "seq",
+                                                                       "head_dim", "dtype")):
+            pr = shared[1]
+        else:
+            if key not in cache:
+                cache.clear()
+                cache[key] = global_problem(*key, 0, with_dout=True)
+            pr = cache[key]
+        for r in ranks:
+            rr = time_share(sp, pr, r, steps, warmup, True, warm_s=0.3)
+            out[f"{name}/r{r}"] = share_entry(rr)
+            del rr
+    bal = {}
+    for name, ranks in CONFIG_SHARES:
+        fw = [out[f"{name}/r{r}"]["fwd_ms"] for r in ranks]
+        if len(fw) > 1:
+            bal[name] = {"fwd_ms_min": min(fw), "fwd_ms_max": max(fw), "spread": round(max(fw) / min(fw) - 1.0, 4)}
+            if all("bwd_ms" in out[f"{name}/r{r}"] for r in ranks):
+                bw = [out[f"{name}/r{r}"]["bwd_ms"] for r in ranks]
+                bal[name].update(bwd_ms_min=min(bw), bwd_ms_max=max(bw),
+                                 bwd_spread=round(max(bw) / min(bw) - 1.0, 4))
+    return out, bal
 
 
 def main():
@@ -402,12 +496,12 @@ def main():
     import torch
 
     from context_causal_attention_attn_amd import build as b
-    if not os.path.exists(b.LIB_PATH):
+    if not b.is_current():
         b.build()
     from context_causal_attention_attn_amd import _lib
     from synthetic import WORKLOADS, workload
 
-    lib = _lib.load()
+    _lib.load()
     if args.relayout_only:
         usp, upr = workload("ulysses_cp8_s32k_gqa32x8_d128", seed=0)
         print(json.dumps({"ulysses_relayout": time_ulysses_relayout(upr, usp["cp"])}), flush=True)
@@ -415,8 +509,7 @@ def main():
             copy_calibration(args.copy_calib_mib)
         return
     spec, prob = workload(args.workload, seed=0)
-    with_bwd = True
-    if with_bwd and prob.dout is None:
+    if prob.dout is None:
         from synthetic import global_problem
         prob = global_problem(spec["batch"], spec["hq"], spec["hkv"], spec["seq"], spec["head_dim"],
                               spec["dtype"], 0, with_dout=True)
@@ -424,7 +517,7 @@ def main():
     if not 0 <= rank < spec["cp"]:
         print(f"--rank {rank} is outside 0..{spec['cp'] - 1} for {args.workload}", file=sys.stderr)
         sys.exit(2)
-    res = time_share(spec, prob, rank, args.steps, args.warmup, with_bwd, args.kv_order)
+    res = time_share(spec, prob, rank, args.steps, args.warmup, True, args.kv_order)
     ms, fl, io = res["ms"], res["flops"], res["bytes"]
     ms_per_step = res["total_ms"] / args.steps
     flops_step = fl["fwd"] + (fl["bwd"] if res["has_bwd"] else 0.0)
@@ -486,17 +579,16 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
+        "peak_bf16_tflops": PEAK_BF16_TFLOPS,
     }
     if not args.no_clock:
         clk = sample_clock(res["step"])
-        if clk and (clk["socket_power_w"] or 0.0) >= 900.0:
-            # the same achieved rates against the peak at the clock actually run
-            # (only from a read taken under load)
-            f = PEAK_BF16_TFLOPS * clk["gfx_mhz_median"] / 2400.0
-            clk["mfma_frac_at_clock"] = {p: round(kernels[p]["achieved"] / f, 4)
-                                         for p in kernels if kernels[p]["unit"] == "TFLOP/s"}
         line["clock"] = clk
     del res
+    if not args.no_configs and args.workload == WORKLOAD:
+        cfg, bal = time_configs(max(5, args.steps // 2), args.warmup, shared=(spec, prob))
+        line["configs"] = cfg
+        line["balance"] = bal
     if args.detail:
         detail = {}
         for name, sp in WORKLOADS.items():
@@ -511,33 +603,17 @@ def main():
                 # Input generation leaves the GPU idle for seconds: warm it
                 # back up for half a second before timing.
                 rr = time_share(sp, pr, r, max(5, args.steps // 2), args.warmup, bw, order, warm_s=0.5)
-                t = rr["ms"]
-                ent = {"fwd_ms": round(t["fwd"], 4), "fwd_tflops": round(tf(rr["flops"]["fwd"], t["fwd"]), 2),
-                       "fwd_frac": round(tf(rr["flops"]["fwd"], t["fwd"]) / PEAK_BF16_TFLOPS, 4)}
-                if rr["has_bwd"]:
-                    btf = tf(rr["flops"]["bwd"], t["bwd"])
-                    ent.update({"bwd_ms": round(t["bwd"], 4), "bwd_tflops": round(btf, 2),
-                                "bwd_frac": round(btf / PEAK_BF16_TFLOPS, 4),
-                                "dkdv_ms": round(t["dkdv"], 4), "dq_ms": round(t["dq"], 4)})
-                detail[f"{name}/r{r}" + ("" if order == "natural" else "/gathered_kv")] = ent
+                detail[f"{name}/r{r}" + ("" if order == "natural" else "/gathered_kv")] = share_entry(rr)
             del pr
         line["detail"] = detail
-        # Balance across the ranks of one CP layout (the Head-Tail claim):
-        # forward time of every timed rank, and the max/min spread.
-        bal = {}
-        for name, sp in WORKLOADS.items():
-            ms = [detail[f"{name}/r{r}"]["fwd_ms"] for r in sp["ranks"] if f"{name}/r{r}" in detail]
-            if len(ms) > 1:
-                bal[name] = {"fwd_ms_min": min(ms), "fwd_ms_max": max(ms),
-                             "spread": round(max(ms) / min(ms) - 1.0, 4)}
-        line["balance"] = bal
         usp, upr = workload("ulysses_cp8_s32k_gqa32x8_d128", seed=0)
         line["ulysses_relayout"] = time_ulysses_relayout(upr, usp["cp"])
         del upr
     if args.copy_calib_mib:
         copy_calibration(args.copy_calib_mib)
+    del prob
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(spec, prob, rank)
+        line["cpu_baseline"] = cpu_baseline(spec, args.workload, rank)
     print(json.dumps(line), flush=True)
 
 

@@ -9,11 +9,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# CPATTN_LIB may point at another build of the same library (e.g. one compiled
-# with different tuning flags); by default the in-tree build is used.
-LIB_PATH = os.environ.get("CPATTN_LIB") or os.path.join(HERE, "libcpattn.so")
+LIB_PATH = os.path.join(HERE, "libcpattn.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_Q_CHUNKS = 16
 MAX_KV_CHUNKS = 64
 KV_CHUNK_ALIGN = 128
@@ -99,6 +97,11 @@ def load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
             "(python -m context_causal_attention_attn_amd.build). There is no fallback path.")
+    from . import build as _build
+    if not _build.is_current(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} was built from other sources than the ones on disk: rebuild it "
+            "(python -m context_causal_attention_attn_amd.build).")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -3,7 +3,9 @@
 Every HIP source under ``csrc/`` and the C ABI source are compiled by hipcc
 for gfx950 only, with packed-FP32 instruction selection switched off, and
 linked into one shared library next to this file. Objects go to
-``_build/`` (not part of the repository).
+``_build/`` (not part of the repository). Next to the library,
+``libcpattn.so.sha256`` records a digest of the sources and flags it was
+built from; ``is_current()`` compares it with the sources on disk.
 
 Usage: ``python -m context_causal_attention_attn_amd.build`` or ``build()``.
 """
@@ -30,6 +32,36 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+
+
+STAMP_SUFFIX = ".sha256"
+
+
+def sources_digest(extra_flags=()) -> str:
+    """SHA-256 over every source the library is built from (kernels, C ABI,
+    the public header) and the compile flags: a library whose stamp differs
+    was built from other code."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
+                   + glob.glob(os.path.join(CSRC, "*.cpp")) + [os.path.join(INCLUDE, "cp_attn.h")])
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    flags = [f for f in COMMON_FLAGS if f not in ("-I", INCLUDE, CSRC)]   # include paths differ per checkout
+    h.update(" ".join(flags + list(extra_flags)).encode())
+    return h.hexdigest()
+
+
+def is_current(lib_path: str = None) -> bool:
+    """True when the library exists and its stamp matches the sources."""
+    lib_path = lib_path or LIB_PATH
+    try:
+        with open(lib_path + STAMP_SUFFIX) as fh:
+            return os.path.exists(lib_path) and fh.read().strip() == sources_digest()
+    except OSError:
+        return False
 
 
 def _hipcc() -> str:
@@ -71,6 +103,8 @@ def build(verbose: bool = False, extra_flags=(), out_path: str = None, build_dir
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib_path)
+    with open(lib_path + STAMP_SUFFIX, "w") as fh:
+        fh.write(sources_digest(extra_flags) + "\n")
     if verbose:
         print(f"built {lib_path} from {len(srcs)} sources", file=sys.stderr)
     return lib_path

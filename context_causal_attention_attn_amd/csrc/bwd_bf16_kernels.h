@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 
   const int groups = p.batch * p.hkv;
   const int g = blockIdx.x % groups;
-  const int kt = blockIdx.x / groups;      // ascending: earliest keys (most work) first
+  const int kt = p.kt0 + blockIdx.x / groups;   // ascending: earliest keys (most work) first
   const int b = g / p.hkv;
   const int hk = g % p.hkv;
   const int key0 = kt * BK;
@@ -458,9 +458,10 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
                     const int r = 16 * rb + 4 * grp + i;
                     if (r > rows_left) continue;
                     if (p.mask_add) {
-                      // additive mask, in the raw score's units
+                      // additive mask, in the raw score's units (at or
+                      // below kMaskHide: hidden)
                       const float a = reinterpret_cast<const float *>(mb + (int64_t)r * p.m_ss)[my_key[kn]];
-                      sacc[rb][kn][i] = fmaf(a, inv, sacc[rb][kn][i]);
+                      sacc[rb][kn][i] = a <= kMaskHide ? -INFINITY : fmaf(a, inv, sacc[rb][kn][i]);
                     } else if (mb[(int64_t)r * p.m_ss + my_key[kn]] == 0) {
                       sacc[rb][kn][i] = -INFINITY;
                     }
@@ -856,9 +857,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   auto dma = [&](int kt, int st) {
     const uint32_t kd = dst0 + K_OFF + 2 * st * TILE;
     const uint32_t vd = dst0 + V_OFF + 2 * st * TILE;
+    const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride);
+    const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride);
     if (kt * BN + BN <= p.skv) {
-      const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride);
-      const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride);
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) {
         dma1(kd + 2 * i * kDqWaves * RPI * D, goff0, kt_base + i * istep_bytes);
@@ -866,11 +867,15 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
       }
     } else {
       // Ragged last tile: rows past the end read the last row (always masked).
+      // Offsets count from the tile's own 64-bit base, so they stay below BN
+      // row strides (< 2^31 bytes) however far the tile lies from the head's.
+      const int last = p.skv - 1 - kt * BN;
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) {
-        const int64_t o = (int64_t)min(kt * BN + srow + i * kDqWaves * RPI, p.skv - 1) * p.kv_ss + scol;
-        dma1(kd + 2 * i * kDqWaves * RPI * D, (uint32_t)(o * 2), kbase);
-        dma1(vd + 2 * i * kDqWaves * RPI * D, (uint32_t)(o * 2), vbase);
+        const uint32_t r = (uint32_t)min(srow + i * kDqWaves * RPI, last);
+        const uint32_t o = (r * (uint32_t)p.kv_ss + (uint32_t)scol) * 2u;
+        dma1(kd + 2 * i * kDqWaves * RPI * D, o, kt_base);
+        dma1(vd + 2 * i * kDqWaves * RPI * D, o, vt_base);
       }
     }
   };
@@ -1021,7 +1026,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
         }
         if constexpr (UMASK) {
           if (p.mask_add) {
-            // ... plus the additive mask (value / softmax_scale).
+            // ... plus the additive mask (value / softmax_scale; at or below
+            // kMaskHide: hidden).
             const float inv = 1.0f / p.scale;
             const float *mf = reinterpret_cast<const float *>(mrow[qb]);
 #pragma unroll
@@ -1038,7 +1044,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
                   if (k0 + i < p.skv) a[i] = mf[k0 + i];
               }
 #pragma unroll
-              for (int i = 0; i < 4; ++i) scur[h][qb][i] = fmaf(a[i], inv, scur[h][qb][i]);
+              for (int i = 0; i < 4; ++i)
+                scur[h][qb][i] = a[i] <= kMaskHide ? -INFINITY : fmaf(a[i], inv, scur[h][qb][i]);
             }
           } else {
           // ... and allowed by the user mask (keys 16*h + 4*grp .. +3 of the block).
@@ -1172,12 +1179,38 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   }
 }
 
+// Zero dK/dV rows outside the key tiles [kt0, kt1) the key-stationary kernel
+// runs on (keys no local query can see): 16-byte stores of both, grid-stride
+// over the rows of one (batch, KV head) per blockIdx.y.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_zero_keys_kernel(const BwdParams p) {
+  constexpr int VPR = D / 4;                        // float4 per row
+  const int64_t front = (int64_t)p.kt0 * BK;        // rows [0, front) and [back, skv)
+  const int64_t back = min((int64_t)p.kt1 * BK, (int64_t)p.skv);
+  const int64_t n = (front + (p.skv - back)) * VPR;
+  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / VPR;
+    const int64_t row = r < front ? r : back + (r - front);
+    const int64_t off = ((int64_t)blockIdx.y * p.skv + row) * D + (i % VPR) * 4;
+    *reinterpret_cast<f32x4 *>(p.dk + off) = z;
+    *reinterpret_cast<f32x4 *>(p.dv + off) = z;
+  }
+}
+
 // Launches of one mode's instantiations.
 template <int D, int KMODE>
 void launch_dkdv_mode(const BwdParams &p, hipStream_t s) {
-  const int64_t kv_tiles = (p.skv + BK - 1) / BK;
-  if (kv_tiles > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KMODE>), dim3(kv_tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
+  const int64_t tiles = p.kt1 - p.kt0;
+  if (tiles > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KMODE>), dim3(tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
+  const int64_t back = (int64_t)p.kt1 * BK < p.skv ? (int64_t)p.kt1 * BK : (int64_t)p.skv;
+  const int64_t zrows = (int64_t)p.kt0 * BK + (p.skv - back);
+  if (zrows > 0) {
+    const int64_t want = (zrows * (D / 4) + 255) / 256;
+    const int64_t blocks = want < 4096 ? want : 4096;
+    hipLaunchKernelGGL(bwd_zero_keys_kernel<D>, dim3(blocks, p.batch * p.hkv), dim3(256), 0, s, p);
+  }
 }
 
 template <int D, int MODE>

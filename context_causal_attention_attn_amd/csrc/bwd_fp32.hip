@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
         const uint8_t *mr = p.mask + b * p.m_sb + h * p.m_sh + (int64_t)r * p.m_ss;
         if (p.mask_add) {
           madd = reinterpret_cast<const float *>(mr)[j];
-          if (madd == -INFINITY) continue;
+          if (madd <= kMaskHide) continue;   // hidden (-inf included)
         } else if (mr[j] == 0) {
           continue;
         }
@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
         const uint8_t *mr = p.mask + b * p.m_sb + h * p.m_sh + (int64_t)r * p.m_ss;
         if (p.mask_add) {
           madd = reinterpret_cast<const float *>(mr)[j];
-          if (madd == -INFINITY) continue;
+          if (madd <= kMaskHide) continue;   // hidden (-inf included)
         } else if (mr[j] == 0) {
           continue;
         }

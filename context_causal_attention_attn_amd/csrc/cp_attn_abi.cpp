@@ -211,6 +211,35 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
     p->lpt_chunk_pos[i] = s.chunk_pos[s.order[i]];
     p->lpt_chunk_idx[i] = s.order[i];
   }
+  // Key tiles some local query can see. With keys in natural order, a key is
+  // visible only if it is not after the last local row (causal) and not
+  // before the sequence start of the earliest local row (packed sequences);
+  // a user mask can only hide more. Several KV chunks: every tile.
+  const int64_t n_tiles = (d->skv + kBwdBlockKV - 1) / kBwdBlockKV;
+  p->kt0 = 0;
+  p->kt1 = (int32_t)n_tiles;
+  if (d->n_kv_chunks == 1 && s.chunk_len > 0 && d->skv > 0) {
+    const int64_t kv0 = d->kv_chunk_pos[0];
+    int64_t qlo = INT64_MAX, qhi = INT64_MIN;
+    for (int c = 0; c < s.n_q_chunks; ++c) {
+      qlo = std::min(qlo, s.chunk_pos[c]);
+      qhi = std::max(qhi, s.chunk_pos[c] + s.chunk_len - 1);
+    }
+    int64_t lo = 0, hi = d->skv - 1;                 // key rows
+    if (d->causal) hi = std::min(hi, qhi - kv0);
+    if (d->n_docs > 0) {
+      int64_t start = INT64_MIN;                     // sequence start of the earliest local row
+      for (int i = 0; i < p->docs.n; ++i)
+        if (p->docs.pos[i] <= qlo) start = p->docs.pos[i];
+      if (start != INT64_MIN) lo = std::max<int64_t>(0, start - kv0);
+    }
+    if (hi < lo) {
+      p->kt0 = p->kt1 = 0;
+    } else {
+      p->kt0 = (int32_t)(lo / kBwdBlockKV);
+      p->kt1 = (int32_t)(hi / kBwdBlockKV + 1);
+    }
+  }
 }
 
 int64_t fwd_grid_size(const FwdParams &p) {

@@ -265,16 +265,19 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // first row of the stage).
   auto dma = [&](int kt, bool is_v, uint32_t dst) {
     const __bf16 *base = is_v ? vbase : kbase;
+    const char *t_base = reinterpret_cast<const char *>(base + (int64_t)kt * tile_stride);
     if (kt * BN + BN <= p.skv) {
-      const char *t_base = reinterpret_cast<const char *>(base + (int64_t)kt * tile_stride);
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) dma1(dst + 2 * i * NW * RPI * D, goff0, t_base + i * istep_bytes);
     } else {
       // Ragged last tile: rows past the end read the last row (always masked).
+      // Offsets count from the tile's own 64-bit base, so they stay below BN
+      // row strides (< 2^31 bytes) however far the tile lies from the head's.
+      const int last = p.skv - 1 - kt * BN;
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) {
-        const int64_t o = (int64_t)min(kt * BN + srow + i * NW * RPI, p.skv - 1) * p.kv_ss + scol;
-        dma1(dst + 2 * i * NW * RPI * D, (uint32_t)(o * 2), base);
+        const uint32_t r = (uint32_t)min(srow + i * NW * RPI, last);
+        dma1(dst + 2 * i * NW * RPI * D, (r * (uint32_t)p.kv_ss + (uint32_t)scol) * 2u, t_base);
       }
     }
   };
@@ -459,7 +462,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
         if constexpr (UMASK) {
           if (p.mask_add) {
             // ... plus the additive mask: 4 floats of this lane's keys per
-            // block, in the raw score's units (value / softmax_scale).
+            // block, in the raw score's units (value / softmax_scale); a value
+            // at or below kMaskHide hides the key.
             const float inv = 1.0f / p.scale;
             const float *mf = reinterpret_cast<const float *>(mrow[qb]);
 #pragma unroll
@@ -476,7 +480,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
                   if (k0 + i < p.skv) a[i] = mf[k0 + i];
               }
 #pragma unroll
-              for (int i = 0; i < 4; ++i) sacc[qb][kb][i] = fmaf(a[i], inv, sacc[qb][kb][i]);
+              for (int i = 0; i < 4; ++i)
+                sacc[qb][kb][i] = a[i] <= kMaskHide ? -INFINITY : fmaf(a[i], inv, sacc[qb][kb][i]);
             }
           } else {
           // ... and allowed by the user mask: the 4 bytes of this lane's keys

@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
         if (mrow) {
           if (p.mask_add) {
             madd = reinterpret_cast<const float *>(mrow)[krow0 + j0 + r];
-            if (madd == -INFINITY) continue;
+            if (madd <= kMaskHide) continue;   // hidden (-inf included)
           } else if (mrow[krow0 + j0 + r] == 0) {
             continue;
           }

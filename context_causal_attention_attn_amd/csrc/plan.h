@@ -16,6 +16,8 @@
 namespace cpattn {
 
 constexpr int kMaxQChunks = CP_ATTN_MAX_Q_CHUNKS;
+// Additive user-mask values at or below this hide their key, like -inf.
+constexpr float kMaskHide = CP_ATTN_MASK_HIDE;
 constexpr int kMaxKvChunks = CP_ATTN_MAX_KV_CHUNKS;
 
 // Packed-sequence boundaries a share can meet (global positions, ascending).
@@ -146,6 +148,11 @@ struct BwdParams {
   int32_t heads_per_item, n_head_packs, tiles_per_chunk;
   int64_t lpt_chunk_pos[kMaxQChunks];
   int32_t lpt_chunk_idx[kMaxQChunks];
+  // Key tiles (of kBwdBlockKV keys) the key-stationary kernel runs on:
+  // [kt0, kt1). Keys outside them are seen by no local query (before the
+  // first local row's sequence, after the last local row) and get zero
+  // dK/dV from a plain fill instead.
+  int32_t kt0, kt1;
 };
 
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p);

@@ -43,7 +43,10 @@
 extern "C" {
 #endif
 
-#define CP_ATTN_ABI_VERSION 2
+/* Bumped whenever cp_attn_desc's layout or a declaration's meaning changes
+ * (3: the user-mask fields attn_mask, mask_strides, mask_additive and the
+ * additive-mask hide threshold). */
+#define CP_ATTN_ABI_VERSION 3
 #define CP_ATTN_MAX_Q_CHUNKS 16
 /* Most KV chunks a descriptor may list (a Head-Tail all-gather at cp = 32
  * delivers 64 chunks). */
@@ -54,6 +57,12 @@ extern "C" {
 #define CP_ATTN_KV_CHUNK_ALIGN 128
 /* Most packed-sequence boundaries a share may meet (see cp_attn_desc.doc_starts). */
 #define CP_ATTN_MAX_DOC_BOUNDS 256
+/* An additive user-mask value at or below this hides its key exactly like
+ * -inf. Padding masks use -1e4, -1e9 or the float32 minimum for "hidden"; a
+ * row whose every key carries such a bias has no representable float32 LSE
+ * near the bias (one ulp of 1e9 is 64) and its backward would be meaningless,
+ * so all of them are treated as hidden keys. */
+#define CP_ATTN_MASK_HIDE (-1.0e4f)
 
 /* Local row order of the query shard. */
 typedef enum {
@@ -125,15 +134,20 @@ typedef enum {
  * A user attention mask ([CP-migration] §8: merged with the CP mask, never
  * replacing it): with attn_mask != NULL and mask_additive == 0, key j is
  * visible to query i only if also attn_mask[b][h][i][j] != 0 (bytes; i the
- * local row, j the key row); with mask_additive == 1 the float32 value is
- * added to softmax_scale * q.k (-inf hides the key). Requires one KV chunk and
- * no packed sequences; the pointer and strides must be multiples of 4 bytes
- * (16 for an additive mask). The mask is read by
+ * local row, j the key row); with mask_additive == 1 the float32 value
+ * a = attn_mask[b][h][i][j] is added to softmax_scale * q.k, and a value
+ * a <= CP_ATTN_MASK_HIDE (-inf, -1e9, the float32 minimum, ...) hides the key.
+ * Finite values above it are biases; the stated precision holds for
+ * |a| < 1e4, larger positive values and NaN are outside the supported range.
+ * Requires one KV chunk and no packed sequences; the pointer and strides must
+ * be multiples of 4 bytes (16 for an additive mask). The mask is read by
  * the kernels during the call's work on the stream; the caller keeps it alive
  * like the other device buffers.
  *
- * The LSE is the natural log of the sum of exp(softmax_scale * q.k) over the
- * visible keys; a row with no visible key gets out = 0 and lse = -inf.
+ * The LSE of query i is the natural log of the sum, over its visible keys j,
+ * of exp(softmax_scale * q_i.k_j + a_ij), with a_ij the additive mask value
+ * (0 without an additive mask); a row with no visible key gets out = 0 and
+ * lse = -inf.
  */
 typedef struct cp_attn_desc {
   int32_t abi_version;         /* must be CP_ATTN_ABI_VERSION */
@@ -184,7 +198,13 @@ int32_t cp_attn_share_positions(int32_t layout, int64_t s_global, int32_t cp_siz
                                 int32_t *n_q_chunks, int64_t *chunk_len);
 
 /* Validate a descriptor (host only; no GPU needed). Checks everything that
- * does not need device pointers. */
+ * does not need device pointers: the fail-fast checks of [CP-migration] §13.2
+ * (shape and layout errors are reported before any work, never worked around)
+ * and the divisibility and chunk rules of [Trainer-CP] §4.2 / [FLA-CP] §3.3.
+ * Returns CP_ATTN_OK or the first failing check's status (see cp_attn_status):
+ * ABI, UNSUPPORTED (dtype, head_dim, sizes >= 2^31, row strides >= 2^24, KV
+ * chunk length), BAD_SHAPE, BAD_LAYOUT, BAD_POSITIONS, NULL_PTR (host arrays),
+ * ALIGNMENT (strides, mask pointer). `desc` is read only during the call. */
 int32_t cp_attn_validate(const cp_attn_desc *desc);
 
 /* Number of visible (query, key) pairs per (batch, query head) of the share:
@@ -213,10 +233,18 @@ int32_t cp_attn_plan_stats_fwd(const cp_attn_desc *desc, cp_attn_plan_stats *sta
 
 /*
  * Forward of the share: out = softmax(scale * q k^T, masked) v and the LSE.
- * q, k, v: device pointers of `dtype`; out: device, `dtype`, o_strides;
- * lse: device float32 [batch, hq, sq_local] contiguous.
+ * This is the local-Q / gathered-K/V attention call of [CP-migration] §6.1
+ * (and of §6.2 / §6.3 on head-sliced inputs), under the global-position
+ * causal mask of §8 and the GQA head mapping of §9.2; the Head-Tail share's
+ * two chunks ([Trainer-CP] §4.4) are computed in one call.
+ * q, k, v: device pointers of `dtype`, caller-owned, read only; out: device,
+ * `dtype`, o_strides, written; lse: device float32 [batch, hq, sq_local]
+ * contiguous, written. Pointers must be 16-byte aligned (lse 4-byte).
  * Needs no workspace (workspace may be NULL when cp_attn_workspace_bytes
- * reports 0). Deterministic: the same inputs give bitwise the same outputs.
+ * reports 0). Returns CP_ATTN_OK once the kernel is enqueued on `stream`;
+ * validation errors (cp_attn_validate's, NULL_PTR, ALIGNMENT) return before
+ * anything is enqueued or written; CP_ATTN_ERR_HIP if the launch fails.
+ * Deterministic: the same inputs give bitwise the same outputs.
  */
 int32_t cp_attn_fwd(const cp_attn_desc *desc, const void *q, const void *k, const void *v,
                     void *out, float *lse, void *workspace, size_t workspace_bytes,

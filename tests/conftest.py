@@ -30,8 +30,8 @@ def pytest_collection_modifyitems(config, items):
 
 
 def pytest_sessionstart(session):
-    """Build the HIP library once if nothing is built yet (a built library is
-    used as is; rebuilding after a source change is the caller's job)."""
+    """Build the HIP library when it is missing or was built from other
+    sources than the ones on disk (its stamp does not match)."""
     from context_causal_attention_attn_amd import build as b
-    if not os.path.exists(b.LIB_PATH):
+    if not b.is_current():
         b.build()

@@ -365,3 +365,49 @@ def test_validate_user_mask():
     d3 = desc(doc_starts=[0, 700])
     d3.desc.attn_mask = base
     assert status(d3) == -5
+
+
+def test_validate_additive_user_mask():
+    """An additive float32 mask is read with 16-byte vector loads: its pointer
+    and every stride must be 16-byte multiples (4- or 8-byte alignment is
+    CP_ATTN_ERR_ALIGNMENT); mask_additive must be 0 or 1."""
+    base = 1 << 40
+    d = desc()
+    d.desc.attn_mask = base
+    d.desc.mask_additive = 1
+    for i, st in enumerate((0, 4 * 2048 * 1024, 4 * 2048)):
+        d.desc.mask_strides[i] = st
+    assert status(d) == 0
+    for off in (4, 8, 12):
+        d.desc.attn_mask = base + off
+        assert status(d) == -9, off
+    d.desc.attn_mask = base
+    for i in range(3):
+        for bad in (4, 8, 4 * 2048 + 4):
+            saved = d.desc.mask_strides[i]
+            d.desc.mask_strides[i] = bad
+            assert status(d) == -9, (i, bad)
+            d.desc.mask_strides[i] = saved
+    assert status(d) == 0
+    d.desc.mask_additive = 2
+    assert status(d) == -2
+    d.desc.mask_additive = -1
+    assert status(d) == -2
+    # The byte mask keeps its 4-byte rule: 4-aligned pointers pass.
+    d.desc.mask_additive = 0
+    d.desc.attn_mask = base + 4
+    assert status(d) == 0
+
+
+def test_header_constants_match_the_binding():
+    """The binding's ABI version and limits are the header's."""
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "cp_attn.h")).read()
+    def define(name):
+        return re.search(rf"#define {name} \(?(-?[0-9.e]+)f?\)?", hdr).group(1)
+    assert int(define("CP_ATTN_ABI_VERSION")) == _lib.ABI_VERSION
+    assert int(define("CP_ATTN_MAX_Q_CHUNKS")) == _lib.MAX_Q_CHUNKS
+    assert int(define("CP_ATTN_MAX_KV_CHUNKS")) == _lib.MAX_KV_CHUNKS
+    assert float(define("CP_ATTN_MASK_HIDE")) == oc.MASK_HIDE
+    assert _lib.load().cp_attn_abi_version() == _lib.ABI_VERSION
+

@@ -51,3 +51,13 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_child_runs_the_oracle():
+    """The CPU baseline leg runs the oracle in a child process and reports its
+    throughput with the threads it used (tiny fp32 share: milliseconds)."""
+    from synthetic import WORKLOADS
+    name = "tiny_fp32_contiguous_cp4_r1"
+    res = bench.cpu_baseline(dict(WORKLOADS[name]), name, 1)
+    assert res["value"] > 0 and res["cores"] >= 1 and res["kind"] == "oracle", res
+    assert "rank 1" in res["sample"] and res["seconds"] > 0

@@ -243,6 +243,26 @@ def test_full_size_colossal_backward_sampled():
     check_full_size_backward_sampled(spec, prob, "contiguous", spec["ranks"][0], 0, 3, "32K colossal bwd r7")
 
 
+@pytest.fixture(scope="module")
+def s32k_dout_problem():
+    spec, _ = workload("ulysses_cp8_s32k_gqa32x8_d128")
+    prob = global_problem(spec["batch"], spec["hq"], spec["hkv"], spec["seq"], spec["head_dim"],
+                          spec["dtype"], 0, with_dout=True)
+    return spec, prob
+
+
+@pytest.mark.parametrize("name,hk", [("ulysses_cp8_s32k_gqa32x8_d128", 0),
+                                     ("hybrid_u2_c4_s32k_gqa32x8_d128", 2)])
+def test_full_size_head_sharded_backward_sampled(s32k_dout_problem, name, hk):
+    """Backward of the 32K head-sharded shares (Ulysses cp=8 rank 0: 4 query
+    heads over the whole sequence; Hybrid U=2 x C=4 rank 4: 16 query heads,
+    rows 16384..24575) in the launch configuration the benchmark times."""
+    spec, _ = workload(name)
+    _, prob = s32k_dout_problem
+    check_full_size_backward_sampled(spec, prob, spec["kind"], spec["ranks"][0], 0, hk,
+                                     f"32K {spec['kind']} bwd r{spec['ranks'][0]}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_timed_backward_matches_untimed(dtype):
     # cp_attn_bwd_timed runs the same kernels with events between them: the

@@ -236,8 +236,7 @@ def sample_rows(n_local, chunks, rng, per=24):
     return np.array(sorted(rows))
 
 
-FULL = [("contiguous", 8, 7), ("head_tail", 8, 0), ("head_tail", 8, 3), ("head_tail", 8, 7),
-        ("ulysses", 8, 0), ("hybrid", 8, 4)]
+FULL = [("contiguous", 8, 7)] + [("head_tail", 8, r) for r in range(8)] + [("ulysses", 8, 0), ("hybrid", 8, 4)]
 
 
 @pytest.mark.parametrize("kind,cp,rank", FULL)
@@ -300,3 +299,29 @@ def test_full_size_closed_form_uniform(big_problem, kind, cp, rank):
     err_l = (lse.double().cpu() - exp_l).abs().max().item()
     print(f"closed form {kind} r{rank}: out {err_o:.3e} lse {err_l:.3e}")
     assert err_o <= OUT_TOL_BF16 and err_l <= LSE_TOL_BF16
+
+
+def test_ragged_tile_with_rows_beyond_4gib():
+    """K/V rows 16 MiB apart (row stride 2^23 elements, the largest power of
+    two the descriptor accepts) with a ragged key count: the last key tile
+    lies more than 4 GiB past the head's base, so its per-row offsets must be
+    taken from a 64-bit tile base. Whole output against the oracle."""
+    dev = torch.device("cuda")
+    S, Hq, Hkv, D, stride = 300, 4, 1, 128, 1 << 23
+    prob = global_problem(1, Hq, Hkv, S, D, dtype="bf16", seed=41)
+    kbuf = torch.zeros((S, stride), dtype=torch.bfloat16, device=dev)
+    vbuf = torch.zeros((S, stride), dtype=torch.bfloat16, device=dev)
+    kbuf[:, :D] = prob.k[0, 0].to(dev)
+    vbuf[:, :D] = prob.v[0, 0].to(dev)
+    k = kbuf.as_strided((1, 1, S, D), (0, 0, stride, 1))
+    v = vbuf.as_strided((1, 1, S, D), (0, 0, stride, 1))
+    assert (S - 1) * stride * 2 >= 1 << 32
+    q = prob.q.to(dev)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = cp_attn_fwd(q, k, v, [0], softmax_scale=scale)
+    torch.cuda.synchronize()
+    import oracle.cp_share as oc
+    ref_o, ref_l = oc.attention_rows(to_f64(prob.q), to_f64(prob.k), to_f64(prob.v), np.arange(S),
+                                     np.arange(S), scale, True)
+    check_close(out, lse, ref_o, ref_l, OUT_TOL_BF16, LSE_TOL_BF16, "rows beyond 4 GiB")
+    del kbuf, vbuf

@@ -2,7 +2,11 @@
 ("新流程 CP 多通信模式迁移设计方案" §8: a boolean attn_mask and the CP mask are
 combined, the user mask is never replaced) against the oracle, forward and
 backward, on every rank: a sliding window broadcast over heads, a random
-per-head mask, fully masked rows, a ragged key count and the fp32 path."""
+per-head mask, fully masked rows, a ragged key count and the fp32 path;
+additive masks with finite biases, -inf, and the large negative values
+padding masks use for "hidden" (-1e4, -1e9, -1e30, the float32 minimum: at or
+below the hide threshold, so rows of them come out empty in both dtypes), plus
+large positive biases."""
 import math
 
 import numpy as np
@@ -21,8 +25,9 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def make_mask(kind, osh, B, Hq, S, rng):
-    """Mask rows of the share's local queries: [B, 1 or Hq, Sq, S] bool."""
+def make_mask(kind, osh, B, Hq, S, rng, dtype="bf16"):
+    """Mask rows of the share's local queries: [B, 1 or Hq, Sq, S], bool or
+    float32 (additive)."""
     q_pos = osh["q_pos"]
     if kind == "window":            # keys at most 300 positions back, all heads
         m = (q_pos[:, None] - np.arange(S)[None, :]) < 300
@@ -31,6 +36,20 @@ def make_mask(kind, osh, B, Hq, S, rng):
         m = rng.normal(0.0, 1.5, (B, Hq, q_pos.size, S)).astype(np.float32)
         m[rng.random(m.shape) < 0.15] = -np.inf
         m[:, :, ::37] = -np.inf
+    elif kind == "padding":         # additive: every padding style of "hidden", large biases
+        shape = (B, Hq, q_pos.size, S)
+        m = rng.normal(0.0, 1.5, shape).astype(np.float32)
+        hides = np.array([-1e4, -1e9, -1e30, np.finfo(np.float32).min, -np.inf], dtype=np.float32)
+        sel = rng.random(shape) < 0.15
+        m[sel] = hides[rng.integers(0, hides.size, int(sel.sum()))]
+        m[:, :, ::37] = -1e9                                # padding rows of each style
+        m[:, :, 5::37] = np.finfo(np.float32).min
+        m[:, :, 9::37] = -1e30
+        m[rng.random(shape) < 0.003] = 60.0                 # late score spikes (the forward's redo path)
+        # Rows that see these keys get an LSE near the bias (bf16: 1000; fp32,
+        # whose LSE gate is 1e-4 absolute, 100: float32 keeps 1e-5 there).
+        m[:, :, :, S // 2:S // 2 + 4] = 1000.0 if dtype == "bf16" else 100.0
+        m[:, :, ::37] = -1e9
     else:                           # random per head, 25 % hidden, some rows fully hidden
         m = rng.random((B, Hq, q_pos.size, S)) < 0.75
         m[:, :, ::37] = False
@@ -47,6 +66,9 @@ CASES = [
     ("additive", "head_tail", 2048, 8, 2, 128, 4, "bf16"),
     ("additive", "contiguous", 1000, 4, 2, 64, 2, "bf16"),    # ragged key count
     ("additive", "contiguous", 512, 2, 1, 64, 4, "fp32"),
+    ("padding", "head_tail", 2048, 8, 2, 128, 4, "bf16"),
+    ("padding", "contiguous", 1000, 4, 2, 64, 2, "bf16"),     # ragged key count
+    ("padding", "head_tail", 512, 2, 1, 64, 4, "fp32"),
 ]
 
 
@@ -62,7 +84,7 @@ def test_user_mask_fwd_bwd_all_ranks(case):
         q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
         sh = cut_share(kind, q, k, v, cp, r)
         osh = oracle_share(kind, S, Hq, Hkv, cp, r)
-        m = make_mask(mask_kind, osh, B, Hq, S, rng)
+        m = make_mask(mask_kind, osh, B, Hq, S, rng, dtype)
         mt = torch.from_numpy(m).to(dev)
         scale = 1.0 / math.sqrt(D)
         out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,
@@ -87,5 +109,5 @@ def test_user_mask_fwd_bwd_all_ranks(case):
         print(f"mask {case} r{r}: out {err_o:.3e} lse {err_l:.3e} dq {errs[0]:.3e} dk {errs[1]:.3e} "
               f"dv {errs[2]:.3e}", flush=True)
         assert err_o <= tol_o and err_l <= tol_l and max(errs) <= tol_g
-        if mask_kind in ("random", "additive"):
+        if mask_kind in ("random", "additive", "padding"):
             assert torch.all(out[:, :, ::37] == 0) and torch.all(dq[:, :, ::37] == 0)
