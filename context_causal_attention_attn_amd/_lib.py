@@ -27,8 +27,9 @@ DTYPE_FP32 = 1
 STATUS = {
     0: "OK", -1: "ERR_NULL_PTR", -2: "ERR_BAD_SHAPE", -3: "ERR_BAD_LAYOUT",
     -4: "ERR_BAD_POSITIONS", -5: "ERR_UNSUPPORTED", -6: "ERR_WORKSPACE", -7: "ERR_HIP",
-    -8: "ERR_ABI", -9: "ERR_ALIGNMENT", -10: "ERR_DIVISIBILITY",
+    -8: "ERR_ABI", -9: "ERR_ALIGNMENT", -10: "ERR_DIVISIBILITY", -11: "ERR_SCRATCH_LIMIT",
 }
+NOALLOC_MAX_ROWS = 1 << 21
 
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _p64 = ctypes.POINTER(ctypes.c_int64)
@@ -76,6 +77,9 @@ SIGNATURES = {
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                  ctypes.POINTER(ctypes.c_void_p), _i32]),
+    "cp_attn_bwd_noalloc": (_i32, [ctypes.POINTER(CpAttnDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "cp_attn_ulysses_relayout": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, _i32, ctypes.c_void_p,
                                         ctypes.c_void_p, _p64, ctypes.c_void_p]),
 }

@@ -267,6 +267,7 @@ const char *cp_attn_error_string(int32_t status) {
     case CP_ATTN_ERR_ABI: return "descriptor abi_version does not match the library";
     case CP_ATTN_ERR_ALIGNMENT: return "device pointer or stride not 16-byte aligned";
     case CP_ATTN_ERR_DIVISIBILITY: return "sequence length not divisible by cp_size (contiguous) or 2*cp_size (head_tail)";
+    case CP_ATTN_ERR_SCRATCH_LIMIT: return "batch*hq*sq_local exceeds the fixed scratch of cp_attn_bwd_noalloc (CP_ATTN_NOALLOC_MAX_ROWS); use cp_attn_bwd with a workspace";
     default: return "unknown status";
   }
 }

@@ -91,7 +91,8 @@ typedef enum {
   CP_ATTN_ERR_HIP = -7,           /* a HIP launch or query failed */
   CP_ATTN_ERR_ABI = -8,           /* desc->abi_version != CP_ATTN_ABI_VERSION */
   CP_ATTN_ERR_ALIGNMENT = -9,     /* a device pointer or stride breaks the 16-byte vector alignment */
-  CP_ATTN_ERR_DIVISIBILITY = -10  /* cp_attn_share_positions: S not divisible by cp (or 2*cp) */
+  CP_ATTN_ERR_DIVISIBILITY = -10, /* cp_attn_share_positions: S not divisible by cp (or 2*cp) */
+  CP_ATTN_ERR_SCRATCH_LIMIT = -11 /* cp_attn_bwd_noalloc: more rows than its fixed scratch holds */
 } cp_attn_status;
 
 /*
@@ -283,6 +284,27 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *desc, const void *q, const void *k
                           const void *out, const float *lse, const void *dout,
                           void *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
                           void *stream, void *const *events, int32_t n_events);
+
+/*
+ * cp_attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation. Same arguments, results (bitwise) and
+ * errors as cp_attn_bwd; the backward's per-row statistics (-Delta and
+ * LSE * log2(e)) live in a fixed scratch array inside the library instead
+ * (2 x CP_ATTN_NOALLOC_MAX_ROWS float32, 16 MiB, held by every GPU the
+ * library runs on until the process ends). Calls no allocating routine; the
+ * first call on a device looks up that device's array once.
+ * batch * hq * sq_local above CP_ATTN_NOALLOC_MAX_ROWS returns
+ * CP_ATTN_ERR_SCRATCH_LIMIT before anything is enqueued. `stream`'s device
+ * (the current device for NULL) selects the array. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams,
+ * or host threads) race and must be serialised by the caller; calls in order
+ * on one stream are safe (each call rewrites every row it reads).
+ */
+#define CP_ATTN_NOALLOC_MAX_ROWS (1 << 21)
+int32_t cp_attn_bwd_noalloc(const cp_attn_desc *desc, const void *q, const void *k, const void *v,
+                            const void *out, const float *lse, const void *dout,
+                            void *dq, float *dk, float *dv, void *stream);
 
 /* ------------------------------------------------------------------------
  * Ulysses exchange: the local steps on either side of the all-to-all

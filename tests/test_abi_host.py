@@ -411,3 +411,17 @@ def test_header_constants_match_the_binding():
     assert float(define("CP_ATTN_MASK_HIDE")) == oc.MASK_HIDE
     assert _lib.load().cp_attn_abi_version() == _lib.ABI_VERSION
 
+
+def test_noalloc_backward_rejects_beyond_its_scratch_before_device_work():
+    """cp_attn_bwd_noalloc: a share with more than CP_ATTN_NOALLOC_MAX_ROWS rows
+    (batch * hq * sq_local) is refused with CP_ATTN_ERR_SCRATCH_LIMIT before any
+    HIP call (no GPU needed); an invalid descriptor gets validation's status."""
+    lib = _lib.load()
+    fake = 1 << 40
+    big = desc(sq_local=_lib.NOALLOC_MAX_ROWS // 4 + 256)     # hq = 8 in desc(): twice the limit
+    args = [fake] * 9 + [None]
+    assert lib.cp_attn_bwd_noalloc(big.ref(), *args) == -11
+    assert "scratch" in lib.cp_attn_error_string(-11).decode()
+    bad = desc()
+    bad.desc.abi_version = 1
+    assert lib.cp_attn_bwd_noalloc(bad.ref(), *args) == -8

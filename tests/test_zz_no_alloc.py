@@ -1,0 +1,68 @@
+"""GPU check of cp_attn_bwd_noalloc, the backward entry point that takes no
+workspace (its per-row statistics live in a fixed scratch array inside the
+library), called through the C ABI: two calls in a row, the second with a
+smaller share, each compared with cp_attn_bwd given a caller workspace on the
+same inputs (same kernels, so the gradients must agree bit for bit)."""
+import ctypes
+import math
+
+import pytest
+import torch
+
+from context_causal_attention_attn_amd import _lib, cp_attn_bwd, cp_attn_fwd, cut_share
+from context_causal_attention_attn_amd.api import make_desc
+from synthetic import global_problem
+
+pytestmark = pytest.mark.gpu
+
+
+def noalloc_bwd(sh, out, lse, dout, scale):
+    """dq, dk, dv from cp_attn_bwd_noalloc through the C ABI."""
+    lib = _lib.load()
+    q, k, v = sh.q, sh.k, sh.v
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    dq = torch.full_like(out, float("nan"))
+    dk = torch.full((B, Hkv, Skv, D), float("nan"), dtype=torch.float32, device=q.device)
+    dv = torch.full_like(dk, float("nan"))
+    d = make_desc(q, k, v, out.stride(), sh.q_chunk_pos, sh.kv_chunk_pos, sh.layout, True, scale)
+    st = lib.cp_attn_bwd_noalloc(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+    _lib.check(st, "cp_attn_bwd_noalloc")
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_noalloc_backward_matches_workspace_backward_twice(dtype):
+    dev = torch.device("cuda")
+    # First a larger share, then a smaller one: the second call must not see
+    # anything of the first in the shared scratch array.
+    cases = [(2, 8, 2, 2048, 128, "head_tail", 4, 1), (1, 4, 2, 640, 64, "contiguous", 2, 1)]
+    if dtype == "fp32":
+        cases = [(1, 4, 2, 512, 64, "head_tail", 2, 0), (1, 2, 1, 256, 64, "contiguous", 4, 1)]
+    for B, Hq, Hkv, S, D, kind, cp, r in cases:
+        prob = global_problem(B, Hq, Hkv, S, D, dtype=dtype, seed=61, with_dout=True)
+        sh = cut_share(kind, prob.q.to(dev), prob.k.to(dev), prob.v.to(dev), cp, r)
+        scale = 1.0 / math.sqrt(D)
+        out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale)
+        dout = sh.take_rows(prob.dout.to(dev)).contiguous()
+        ref = cp_attn_bwd(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, layout=sh.layout,
+                          softmax_scale=scale)
+        got = noalloc_bwd(sh, out, lse, dout, scale)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(a, b), f"{dtype} {kind} S={S}: {name} differs from cp_attn_bwd"
+        print(f"noalloc {dtype} {kind} B={B} S={S} r{r}: bitwise equal to cp_attn_bwd", flush=True)
+
+
+def test_noalloc_rejects_shares_beyond_its_scratch():
+    dev = torch.device("cuda")
+    rows = _lib.NOALLOC_MAX_ROWS // 8 + 64        # B * Hq * Sq just above the limit with Hq = 8
+    q = torch.empty((1, 8, rows, 64), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((1, 2, 128, 64), dtype=torch.bfloat16, device=dev)
+    d = make_desc(q, k, k, q.stride(), [0], [0], "contiguous", True, 0.125)
+    st = _lib.load().cp_attn_bwd_noalloc(d.ref(), q.data_ptr(), k.data_ptr(), k.data_ptr(), q.data_ptr(),
+                                         q.data_ptr(), q.data_ptr(), q.data_ptr(), k.data_ptr(), k.data_ptr(),
+                                         None)
+    assert st == -11
