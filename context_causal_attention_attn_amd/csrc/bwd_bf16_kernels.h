@@ -141,7 +141,9 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
 
   const int groups = p.batch * p.hkv;
   const int g = blockIdx.x % groups;
-  const int kt = p.kt0 + blockIdx.x / groups;   // ascending: earliest keys (most work) first
+  const int unit = blockIdx.x / groups;          // key tile, then part: earliest keys (most work) first
+  const int part = unit % p.kv_parts;
+  const int kt = p.kt0 + unit / p.kv_parts;
   const int b = g / p.hkv;
   const int hk = g % p.hkv;
   const int key0 = kt * BK;
@@ -198,8 +200,12 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       return nq_tiles;
     }
   };
-  int total = 0;
-  for (int c = 0; c < p.n_q_chunks; ++c) total += (end_tile(c) - first_tile(c)) * p.group;
+  int all_steps = 0;
+  for (int c = 0; c < p.n_q_chunks; ++c) all_steps += (end_tile(c) - first_tile(c)) * p.group;
+  // This workgroup's part of the tile's steps (all of them unless the tile is
+  // split over kv_parts workgroups).
+  const int s_begin = (int)((int64_t)all_steps * part / p.kv_parts);
+  const int total = (int)((int64_t)all_steps * (part + 1) / p.kv_parts) - s_begin;
   struct Cursor {
     int c, t, h;       // chunk, query tile in the chunk, head in the group
     int64_t cpos;      // global position of the chunk's first row
@@ -221,8 +227,18 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       if (++u.t >= end_tile(u.c)) next_chunk(u);
     }
   };
+  // The cursor at step s_begin: skip whole chunks, then tiles of G steps.
   Cursor c0{0, first_tile(0), 0, p.chunk_pos[0]};
-  if (c0.t >= end_tile(0)) next_chunk(c0);
+  {
+    int rem = s_begin, c = 0;
+    for (; c < p.n_q_chunks; ++c) {
+      const int n = (end_tile(c) - first_tile(c)) * p.group;
+      if (rem < n) break;
+      rem -= n;
+    }
+    if (c < p.n_q_chunks) c0 = Cursor{c, first_tile(c) + rem / p.group, rem % p.group, p.chunk_pos[c]};
+    else if (c0.t >= end_tile(0)) next_chunk(c0);   // no step left (total == 0)
+  }
 
   // ---- staging: global -> LDS directly (see the forward kernel) -------------
   // Only the P wavefronts stage (the dS wavefronts carry the longer chain of
@@ -644,7 +660,13 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     }
   }
 
-  float *dst = (prole ? p.dv : p.dk) + ((int64_t)b * p.hkv + hk) * p.skv * D;
+  // Part 0 writes dK/dV; the other parts of a split tile write partials for
+  // the reduction kernel ([part-1][tile][group][dk, dv][key in tile][D]).
+  float *dst = part == 0
+                   ? (prole ? p.dv : p.dk) + ((int64_t)b * p.hkv + hk) * p.skv * D
+                   : p.kv_partial +
+                         ((((int64_t)(part - 1) * (p.kt1 - p.kt0) + (kt - p.kt0)) * groups + g) * 2 + (prole ? 1 : 0)) *
+                             BK * D - (int64_t)key0 * D;
   const float mul = prole ? 1.0f : p.scale;
 #pragma unroll
   for (int kn = 0; kn < KN; ++kn) {
@@ -657,6 +679,34 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       *reinterpret_cast<f32x4 *>(dst + (int64_t)my_key[kn] * D + 16 * db + 4 * grp) = a;
     }
   }
+}
+
+// Adds the partial dK/dV of the split key tiles' parts 1.. into dK/dV: one
+// float4 of dK and of dV per thread; grid (key tiles x groups, BK*D/4/256).
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_reduce_kernel(const BwdParams p) {
+  const int groups = p.batch * p.hkv;
+  const int tiles = p.kt1 - p.kt0;
+  const int tg = blockIdx.x;                                  // tile * groups + group
+  const int e = (blockIdx.y * 256 + threadIdx.x) * 4;         // element of the tile's BK x D block
+  const int64_t key = (int64_t)(p.kt0 + tg / groups) * BK + e / D;
+  if (e >= BK * D || key >= p.skv) return;
+  const int g = tg % groups;
+  const int64_t out = ((int64_t)g * p.skv + key) * D + e % D;   // g = b * hkv + hk
+  f32x4 sk = *reinterpret_cast<const f32x4 *>(p.dk + out);
+  f32x4 sv = *reinterpret_cast<const f32x4 *>(p.dv + out);
+  for (int j = 1; j < p.kv_parts; ++j) {
+    const float *slot = p.kv_partial + (((int64_t)(j - 1) * tiles + tg / groups) * groups + g) * 2 * BK * D;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(slot + e);
+    const f32x4 c = *reinterpret_cast<const f32x4 *>(slot + BK * D + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sk[i] += a[i];
+      sv[i] += c[i];
+    }
+  }
+  *reinterpret_cast<f32x4 *>(p.dk + out) = sk;
+  *reinterpret_cast<f32x4 *>(p.dv + out) = sv;
 }
 
 // ---------------------------------------------------------------------------
@@ -1202,8 +1252,13 @@ __global__ void __launch_bounds__(256) bwd_zero_keys_kernel(const BwdParams p) {
 template <int D, int KMODE>
 void launch_dkdv_mode(const BwdParams &p, hipStream_t s) {
   const int64_t tiles = p.kt1 - p.kt0;
-  if (tiles > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KMODE>), dim3(tiles * p.batch * p.hkv), dim3(kDkdvThreads), 0, s, p);
+  if (tiles > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KMODE>), dim3(tiles * p.kv_parts * p.batch * p.hkv),
+                       dim3(kDkdvThreads), 0, s, p);
+    if (p.kv_parts > 1)
+      hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<D>, dim3(tiles * p.batch * p.hkv, (BK * D / 4 + 255) / 256),
+                         dim3(256), 0, s, p);
+  }
   const int64_t back = (int64_t)p.kt1 * BK < p.skv ? (int64_t)p.kt1 * BK : (int64_t)p.skv;
   const int64_t zrows = (int64_t)p.kt0 * BK + (p.skv - back);
   if (zrows > 0) {

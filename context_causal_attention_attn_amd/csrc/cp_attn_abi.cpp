@@ -10,6 +10,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
+#include <queue>
 #include <vector>
 
 #include "cp_attn.h"
@@ -181,7 +183,75 @@ void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   }
 }
 
-void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
+// Workgroups that run at once on the chip for the key-stationary dK/dV kernel
+// (one per compute unit: its LDS use leaves room for one): MI355X's 256 CUs.
+constexpr int kDkdvSlots = 256;
+
+// How many workgroups share each key tile of the dK/dV kernel. A key tile's
+// work is the query steps (64-row query tiles of every head of its GQA group)
+// that can see it; under the causal mask early key tiles have many times the
+// steps of late ones. With few KV heads (a Ulysses share has one) there are
+// few workgroups, and the longest tiles decide the kernel's time. The launch
+// order is tile by tile, longest first; this simulates that list schedule on
+// the chip's workgroup slots for 1, 2, 4 and 8 parts per tile (each part
+// also pays a fixed start-up and, beyond the first, an fp32 partial written
+// and reduced) and keeps the fastest.
+static int32_t dkdv_parts(const cp_attn_desc *d, const Share &s, int kt0, int kt1) {
+  if (d->dtype != CP_ATTN_BF16 || kt1 <= kt0 || s.chunk_len == 0) return 1;
+  const int64_t groups = (int64_t)d->batch * d->hkv;
+  // Grids of many workgroups balance by themselves (and would make the
+  // simulation long).
+  if ((int64_t)(kt1 - kt0) * groups > 16 * kDkdvSlots) return 1;
+  const int G = d->hq / d->hkv;
+  const int64_t nq = (s.chunk_len + kBwdBlockQ - 1) / kBwdBlockQ;
+  const int64_t Lkv = d->skv / d->n_kv_chunks;
+  std::vector<double> steps;
+  steps.reserve(kt1 - kt0);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int64_t key0 = (int64_t)kt * kBwdBlockKV;
+    const int64_t kc = key0 / Lkv;
+    const int64_t kv_lo = d->kv_chunk_pos[kc] + (key0 - kc * Lkv);
+    int64_t n = 0;
+    for (int c = 0; c < s.n_q_chunks; ++c) {
+      int64_t first = 0;
+      if (d->causal) {
+        const int64_t rel = kv_lo - s.chunk_pos[c];
+        first = rel <= 0 ? 0 : std::min<int64_t>(nq, rel / kBwdBlockQ);
+      }
+      n += nq - first;
+    }
+    steps.push_back((double)(n * G));
+  }
+  const double kStartup = 2.0;   // steps' worth of a workgroup's fixed work
+  // Writing and reducing one partial (2 x 64 KiB of fp32, written and read
+  // back) costs about this many steps of one workgroup when spread over the chip.
+  const double kPartial = 0.03;
+  int best = 1;
+  double best_t = 0.0;
+  for (int parts = 1; parts <= 8; parts *= 2) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> slots;
+    for (int i = 0; i < kDkdvSlots; ++i) slots.push(0.0);
+    double span = 0.0;
+    for (double st : steps)
+      for (int j = 0; j < parts; ++j) {
+        const double w = kStartup + st / parts;
+        for (int64_t g = 0; g < groups; ++g) {
+          const double t = slots.top() + w;
+          slots.pop();
+          slots.push(t);
+          span = std::max(span, t);
+        }
+      }
+    const double t = span + kPartial * (parts - 1) * groups * (double)steps.size();
+    if (parts == 1 || t < best_t * 0.97) {
+      best = parts;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool allow_split) {
   memset(p, 0, sizeof(*p));
   collect_doc_bounds(d, &p->docs);
   p->mask = static_cast<const uint8_t *>(d->attn_mask);
@@ -240,6 +310,15 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p) {
       p->kt1 = (int32_t)(hi / kBwdBlockKV + 1);
     }
   }
+  p->kv_parts = allow_split ? dkdv_parts(d, s, p->kt0, p->kt1) : 1;
+  p->kv_partial = nullptr;
+}
+
+// fp32 partial dK/dV of the split key tiles (see BwdParams::kv_parts).
+static size_t bwd_partial_bytes(const BwdParams &p, int head_dim) {
+  if (p.kv_parts <= 1) return 0;
+  return (size_t)(p.kv_parts - 1) * (size_t)(p.kt1 - p.kt0) * (size_t)p.batch * p.hkv * 2 *
+         (size_t)kBwdBlockKV * head_dim * sizeof(float);
 }
 
 int64_t fwd_grid_size(const FwdParams &p) {
@@ -346,14 +425,20 @@ static size_t bwd_stat_bytes(const cp_attn_desc *d) {
   return (rows * 4 + 255) & ~(size_t)255;
 }
 
+
 int32_t cp_attn_workspace_bytes(const cp_attn_desc *d, int32_t backward, size_t *bytes) {
   int32_t st = validate(d);
   if (st) return st;
   if (!bytes) return CP_ATTN_ERR_NULL_PTR;
   if (!backward) { *bytes = 0; return CP_ATTN_OK; }
   // Backward: Delta = rowsum(dO o O) and LSE * log2(e), each [B, Hq, Sq]
-  // fp32, each starting on a 256-byte boundary.
-  *bytes = 2 * bwd_stat_bytes(d);
+  // fp32, each starting on a 256-byte boundary; then the fp32 partial dK/dV
+  // of key tiles split over several workgroups (none for most shares).
+  Share s;
+  make_share(d, &s);
+  BwdParams p;
+  fill_bwd_params(d, s, &p);
+  *bytes = 2 * bwd_stat_bytes(d) + bwd_partial_bytes(p, d->head_dim);
   return CP_ATTN_OK;
 }
 
@@ -432,6 +517,27 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *d, const void *q, const void *k, c
                           const void *out, const float *lse, const void *dout, void *dq, float *dk,
                           float *dv, void *workspace, size_t workspace_bytes, void *stream,
                           void *const *events, int32_t n_events) {
+  return bwd_run(d, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream, events,
+                 n_events, true);
+}
+
+int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
+                    const void *out, const float *lse, const void *dout, void *dq, float *dk,
+                    float *dv, void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_run(d, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream, nullptr, 0,
+                 true);
+}
+
+}  // extern "C"
+
+namespace cpattn {
+
+size_t bwd_stats_bytes(const cp_attn_desc *d) { return 2 * bwd_stat_bytes(d); }
+
+int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void *v, const void *out,
+                const float *lse, const void *dout, void *dq, float *dk, float *dv, void *workspace,
+                size_t workspace_bytes, void *stream, void *const *events, int32_t n_events,
+                bool allow_split) {
   int32_t st = validate(d);
   if (st) return st;
   if (!(n_events == 0 && events == nullptr) && n_events != 4) return CP_ATTN_ERR_BAD_SHAPE;
@@ -440,8 +546,11 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *d, const void *q, const void *k, c
     for (int i = 0; i < 4; ++i)
       if (!events[i]) return CP_ATTN_ERR_NULL_PTR;
   }
-  size_t need = 0;
-  cp_attn_workspace_bytes(d, 1, &need);
+  Share s;
+  make_share(d, &s);
+  BwdParams p;
+  fill_bwd_params(d, s, &p, allow_split);
+  const size_t need = 2 * bwd_stat_bytes(d) + bwd_partial_bytes(p, d->head_dim);
   if (d->sq_local > 0 && (!q || !out || !lse || !dout || !dq)) return CP_ATTN_ERR_NULL_PTR;
   if (d->skv > 0 && (!k || !v || !dk || !dv)) return CP_ATTN_ERR_NULL_PTR;
   if (need > 0 && (!workspace || workspace_bytes < need)) return CP_ATTN_ERR_WORKSPACE;
@@ -449,25 +558,16 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *d, const void *q, const void *k, c
   for (const void *ptr : ptrs16)
     if (ptr && !aligned16(ptr)) return CP_ATTN_ERR_ALIGNMENT;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return CP_ATTN_ERR_ALIGNMENT;
-  Share s;
-  make_share(d, &s);
-  BwdParams p;
-  fill_bwd_params(d, s, &p);
   p.q = q; p.k = k; p.v = v; p.out = out; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.delta = static_cast<float *>(workspace);
   p.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + bwd_stat_bytes(d));
+  if (p.kv_parts > 1)
+    p.kv_partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d));
   void *const *ev = n_events == 4 ? events : nullptr;
   const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream, ev)
                                            : launch_bwd_fp32(p, d->head_dim, stream, ev);
   return e == 0 ? CP_ATTN_OK : CP_ATTN_ERR_HIP;
 }
 
-int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
-                    const void *out, const float *lse, const void *dout, void *dq, float *dk,
-                    float *dv, void *workspace, size_t workspace_bytes, void *stream) {
-  return cp_attn_bwd_timed(d, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes,
-                           stream, nullptr, 0);
-}
-
-}  // extern "C"
+}  // namespace cpattn

@@ -14,6 +14,7 @@
 #include <mutex>
 
 #include "cp_attn.h"
+#include "plan.h"
 
 namespace {
 
@@ -52,13 +53,11 @@ extern "C" int32_t cp_attn_bwd_noalloc(const cp_attn_desc *desc, const void *q, 
                                        const void *v, const void *out, const float *lse,
                                        const void *dout, void *dq, float *dk, float *dv,
                                        void *stream) {
-  int32_t st = cp_attn_validate(desc);
-  if (st) return st;
-  size_t need = 0;
-  st = cp_attn_workspace_bytes(desc, 1, &need);
+  const int32_t st = cp_attn_validate(desc);
   if (st) return st;
   const int64_t rows = (int64_t)desc->batch * desc->hq * desc->sq_local;
-  if (rows > CP_ATTN_NOALLOC_MAX_ROWS || need > kScratchBytes) return CP_ATTN_ERR_SCRATCH_LIMIT;
+  if (rows > CP_ATTN_NOALLOC_MAX_ROWS || cpattn::bwd_stats_bytes(desc) > kScratchBytes)
+    return CP_ATTN_ERR_SCRATCH_LIMIT;
   if (rows == 0 && desc->skv == 0) return CP_ATTN_OK;
   int dev = -1;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -66,6 +65,8 @@ extern "C" int32_t cp_attn_bwd_noalloc(const cp_attn_desc *desc, const void *q, 
   void *ws = scratch_of(dev);
   if (!ws) return CP_ATTN_ERR_HIP;
   // The statistics pass writes every row of both arrays before the main
-  // kernels read them, so nothing needs clearing between calls.
-  return cp_attn_bwd(desc, q, k, v, out, lse, dout, dq, dk, dv, ws, kScratchBytes, stream);
+  // kernels read them, so nothing needs clearing between calls. Key tiles are
+  // never split here (the scratch holds no partial dK/dV).
+  return cpattn::bwd_run(desc, q, k, v, out, lse, dout, dq, dk, dv, ws, kScratchBytes, stream, nullptr, 0,
+                         false);
 }

@@ -153,10 +153,25 @@ struct BwdParams {
   // first local row's sequence, after the last local row) and get zero
   // dK/dV from a plain fill instead.
   int32_t kt0, kt1;
+  // Each key tile's query steps are split over kv_parts workgroups (1, 2, 4
+  // or 8); part 0 writes dK/dV, parts 1.. write fp32 partials to kv_partial
+  // ([kv_parts-1][tile][batch*hkv][dk, dv][kBwdBlockKV][D]), which a
+  // reduction kernel adds into dK/dV.
+  int32_t kv_parts;
+  float *kv_partial;
 };
 
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p);
-void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p);
+// allow_split = false keeps every key tile in one workgroup (kv_parts = 1).
+void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool allow_split = true);
+// Bytes of the backward's per-row statistics (-Delta and LSE*log2e, each on a
+// 256-byte boundary), the part of the workspace every backward needs.
+size_t bwd_stats_bytes(const cp_attn_desc *d);
+// cp_attn_bwd_timed with the choice of splitting key tiles (the no-alloc
+// entry point passes allow_split = false: its scratch holds no partials).
+int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void *v, const void *out,
+                const float *lse, const void *dout, void *dq, float *dk, float *dv, void *workspace,
+                size_t workspace_bytes, void *stream, void *const *events, int32_t n_events, bool allow_split);
 int64_t fwd_grid_size(const FwdParams &p);
 
 // Launchers (defined with their kernels); return a hipError_t as int.

@@ -217,10 +217,16 @@ def test_head_tail_tile_schedule_is_balanced():
 
 
 def test_workspace_bytes():
+    """Forward: none. Backward: -Delta and LSE*log2e per row (each on a
+    256-byte boundary), plus whole fp32 partial dK/dV tiles when the key tiles
+    are split (this small share: 2 KV heads, 8 key tiles)."""
     d = desc()
     assert cp_attn_workspace_bytes(d, False) == 0
     rows = 1 * 8 * 500
-    assert cp_attn_workspace_bytes(d, True) == 2 * ((rows * 4 + 255) // 256) * 256
+    stats = 2 * ((rows * 4 + 255) // 256) * 256
+    extra = cp_attn_workspace_bytes(d, True) - stats
+    unit = 2 * 2 * 128 * 128 * 4                        # dK and dV of one key tile of both KV heads
+    assert extra >= 0 and extra % unit == 0 and extra // unit in (0, 8, 24, 56)   # (parts - 1) x 8 tiles
 
 
 def test_bwd_timed_rejects_bad_event_arrays_before_any_device_work():
@@ -425,3 +431,22 @@ def test_noalloc_backward_rejects_beyond_its_scratch_before_device_work():
     bad = desc()
     bad.desc.abi_version = 1
     assert lib.cp_attn_bwd_noalloc(bad.ref(), *args) == -8
+
+
+def test_workspace_holds_split_key_tile_partials():
+    """The backward splits the key tiles of shares with few KV heads over
+    several workgroups and needs room for their fp32 partial dK/dV; shares
+    with many workgroups (the Colossal and Head-Tail cp=8 shares) need only
+    the per-row statistics."""
+    def ws(B, Hq, Hkv, sq, skv, qpos):
+        d = desc(batch=B, hq=Hq, hkv=Hkv, sq_local=sq, skv=skv, q_chunk_pos=qpos,
+                 layout="contiguous" if len(qpos) == 1 else "head_tail",
+                 q_strides=(Hq * sq * 128, sq * 128, 128), kv_strides=(Hkv * skv * 128, skv * 128, 128),
+                 o_strides=(Hq * sq * 128, sq * 128, 128))
+        stats = 2 * ((B * Hq * sq * 4 + 255) // 256 * 256)
+        return cp_attn_workspace_bytes(d, True) - stats
+    assert ws(1, 32, 8, 4096, 32768, [28672]) == 0                       # Colossal cp=8 rank 7
+    assert ws(2, 32, 8, 4096, 32768, [0, 30720]) == 0                     # Head-Tail B=2 rank 0
+    part = ws(1, 4, 1, 32768, 32768, [0])                                  # Ulysses cp=8 rank 0
+    unit = 2 * 128 * 128 * 4                                               # dK and dV of one key tile
+    assert part > 0 and part % (256 * unit) == 0                           # whole extra parts of 256 tiles
