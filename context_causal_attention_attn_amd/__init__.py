@@ -18,4 +18,4 @@ from .api import (  # noqa: F401
 )
 from .shares import Share, cut_share  # noqa: F401
 from .ulysses import (cp_attn_ulysses_relayout, head_to_seq_pack, head_to_seq_unpack,  # noqa: F401
-                      seq_to_head_pack, seq_to_head_unpack)
+                      seq_to_head_pack, seq_to_head_unpack, ulysses_bwd_in_place, ulysses_fwd_in_place)

@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcpattn.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_Q_CHUNKS = 16
 MAX_KV_CHUNKS = 64
 KV_CHUNK_ALIGN = 128
@@ -19,7 +19,8 @@ MAX_DOC_BOUNDS = 256
 
 LAYOUT_CONTIGUOUS = 0
 LAYOUT_HEAD_TAIL = 1
-LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "head_tail": LAYOUT_HEAD_TAIL}
+LAYOUT_CHUNKED = 2
+LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "head_tail": LAYOUT_HEAD_TAIL, "chunked": LAYOUT_CHUNKED}
 
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
@@ -46,6 +47,7 @@ class CpAttnDesc(ctypes.Structure):
         ("q_strides", _i64 * 3), ("kv_strides", _i64 * 3), ("o_strides", _i64 * 3),
         ("n_docs", _i32), ("doc_starts", _p64),
         ("attn_mask", ctypes.c_void_p), ("mask_strides", _i64 * 3), ("mask_additive", _i32),
+        ("chunk_strides", _i64 * 3),
     ]
 
 

@@ -36,7 +36,7 @@ class _Desc:
 
     def __init__(self, *, dtype, batch, hq, hkv, head_dim, sq_local, skv, q_chunk_pos,
                  kv_chunk_pos, layout, causal, softmax_scale, q_strides, kv_strides, o_strides,
-                 doc_starts=(), attn_mask=None, mask_strides=(0, 0, 0)):
+                 doc_starts=(), attn_mask=None, mask_strides=(0, 0, 0), chunk_strides=(0, 0, 0)):
         additive = attn_mask is not None and attn_mask.dtype == torch.float32
         self.qpos = (ctypes.c_int64 * max(1, len(q_chunk_pos)))(*q_chunk_pos)
         self.kvpos = (ctypes.c_int64 * max(1, len(kv_chunk_pos)))(*kv_chunk_pos)
@@ -63,23 +63,38 @@ class _Desc:
         for i in range(3):
             d.mask_strides[i] = int(mask_strides[i]) * (4 if additive else 1)   # elements -> bytes
         d.mask_additive = 1 if additive else 0
+        for i in range(3):
+            d.chunk_strides[i] = int(chunk_strides[i])
         self.desc = d
 
     def ref(self):
         return ctypes.byref(self.desc)
 
 
+def _geom(t):
+    """(batch, heads, rows, head_dim, (batch, head, row) strides, chunk stride,
+    chunks) of a [batch, heads, rows, head_dim] tensor, or of a
+    [chunks, batch, heads, rows per chunk, head_dim] one whose chunks lie
+    stride(0) elements apart (e.g. the blocks a Ulysses all-to-all delivers)."""
+    if t.dim() == 4:
+        B, H, S, D = t.shape
+        return B, H, S, D, tuple(t.stride()[:3]), 0, None
+    if t.dim() == 5:
+        C, B, H, L, D = t.shape
+        return B, H, C * L, D, tuple(t.stride()[1:4]), t.stride(0), C
+    raise ValueError("tensors must be [batch, heads, rows, head_dim] or [chunks, batch, heads, rows, head_dim]")
+
+
 def _check_inputs(q, k, v):
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be [batch, heads, rows, head_dim]")
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must all be bfloat16 or all float32")
     if k.shape != v.shape or k.stride() != v.stride():
         raise ValueError("k and v must have the same shape and strides")
-    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+    gq, gk = _geom(q), _geom(k)
+    if gq[0] != gk[0] or gq[3] != gk[3]:
         raise ValueError("q and k/v disagree on batch or head_dim")
     for t in (q, k, v):
-        if t.stride(3) != 1:
+        if t.stride(-1) != 1:
             raise ValueError("the head_dim axis must be contiguous")
         if not t.is_cuda:
             raise ValueError("tensors must be on the GPU")
@@ -93,28 +108,40 @@ def _mask_args(attn_mask, q, k):
         return None, (0, 0, 0)
     if attn_mask.dtype not in (torch.bool, torch.uint8, torch.float32) or attn_mask.dim() != 4:
         raise ValueError("attn_mask must be a 4-D bool, uint8 or float32 (additive) tensor [B|1, Hq|1, Sq, Skv]")
-    B, Hq, Sq, _ = q.shape
+    B, Hq, Sq = _geom(q)[:3]
+    Skv = _geom(k)[2]
     if (attn_mask.shape[0] not in (1, B) or attn_mask.shape[1] not in (1, Hq) or attn_mask.shape[2] != Sq
-            or attn_mask.shape[3] != k.shape[2]):
-        raise ValueError(f"attn_mask shape {tuple(attn_mask.shape)} does not broadcast to {(B, Hq, Sq, k.shape[2])}")
+            or attn_mask.shape[3] != Skv):
+        raise ValueError(f"attn_mask shape {tuple(attn_mask.shape)} does not broadcast to {(B, Hq, Sq, Skv)}")
     if attn_mask.device != q.device or attn_mask.stride(3) != 1:
         raise ValueError("attn_mask must be on q's device with a contiguous key dim")
     st = tuple(0 if attn_mask.shape[i] == 1 else attn_mask.stride(i) for i in range(3))
     return attn_mask, st
 
 
-def make_desc(q, k, v, o_strides, q_chunk_pos: Sequence[int], kv_chunk_pos: Sequence[int],
+def make_desc(q, k, v, o, q_chunk_pos: Sequence[int], kv_chunk_pos: Sequence[int],
               layout, causal: bool, softmax_scale: Optional[float], doc_starts: Sequence[int] = (),
               attn_mask=None) -> _Desc:
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    """Descriptor of a share. q, k, v (and o, whose strides out, dout and dq
+    share: a tensor, or a stride tuple of a 4-D one) are 4-D, or 5-D with
+    their chunks stride(0) apart; a 5-D q or o needs one chunk per entry of
+    q_chunk_pos, a 5-D k one per entry of kv_chunk_pos."""
+    B, Hq, Sq, D, q_st, q_cs, q_nc = _geom(q)
+    _, Hkv, Skv, _, kv_st, kv_cs, kv_nc = _geom(k)
+    if isinstance(o, torch.Tensor):
+        _, _, _, _, o_st, o_cs, o_nc = _geom(o)
+    else:
+        o_st, o_cs, o_nc = tuple(o)[:3], 0, None
+    for n, want, what in ((q_nc, len(q_chunk_pos), "q"), (o_nc, len(q_chunk_pos), "out"),
+                          (kv_nc, len(kv_chunk_pos), "k/v")):
+        if n is not None and n != want:
+            raise ValueError(f"a 5-D {what} has {n} chunks, its chunk table {want}")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
     m, mst = _mask_args(attn_mask, q, k)
     return _Desc(dtype=_DT.get(q.dtype, -1), batch=B, hq=Hq, hkv=Hkv, head_dim=D, sq_local=Sq, skv=Skv,
                  q_chunk_pos=list(q_chunk_pos), kv_chunk_pos=list(kv_chunk_pos), layout=layout,
-                 causal=causal, softmax_scale=scale, q_strides=q.stride()[:3],
-                 kv_strides=k.stride()[:3], o_strides=tuple(o_strides)[:3], doc_starts=doc_starts,
-                 attn_mask=m, mask_strides=mst)
+                 causal=causal, softmax_scale=scale, q_strides=q_st, kv_strides=kv_st, o_strides=o_st,
+                 doc_starts=doc_starts, attn_mask=m, mask_strides=mst, chunk_strides=(q_cs, kv_cs, o_cs))
 
 
 def _stream_handle(t: torch.Tensor) -> int:
@@ -123,8 +150,7 @@ def _stream_handle(t: torch.Tensor) -> int:
 
 def cp_attn_validate(q, k, v, q_chunk_pos, *, layout="contiguous", kv_chunk_pos=(0,), causal=True,
                      softmax_scale=None, doc_starts=(), attn_mask=None) -> None:
-    d = make_desc(q, k, v, q.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
-                  attn_mask)
+    d = make_desc(q, k, v, q, q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts, attn_mask)
     check(_lib.load().cp_attn_validate(d.ref()), "cp_attn_validate")
 
 
@@ -166,19 +192,25 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
     given, is a bool/uint8 [B|1, Hq|1, Sq, Skv] device tensor ANDed with the
     CP mask (True / nonzero: may attend), or a float32 one added to the scaled
     scores (-inf hides a key).
+
+    q (and out) may also be 5-D [chunks, B, Hq, L, D], one chunk per entry of
+    q_chunk_pos stride(0) apart (layout "chunked"), and k/v 5-D
+    [chunks, B, Hkv, Lkv, D], one per entry of kv_chunk_pos: e.g. the blocks
+    a Ulysses all-to-all delivers, read in place; out then defaults to q's
+    shape, the layout the reverse exchange sends. lse is always [B, Hq, Sq].
     """
     lib = _lib.load()
     _check_inputs(q, k, v)
-    B, Hq, Sq, D = q.shape
+    B, Hq, Sq, D = _geom(q)[:4]
     if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=q.dtype, device=q.device)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or out.stride(3) != 1 or out.device != q.device:
+    if out.shape != q.shape or out.dtype != q.dtype or out.stride(-1) != 1 or out.device != q.device:
         raise ValueError("out must match q's shape, dtype and device, with a contiguous head_dim")
     if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
-    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
+    d = make_desc(q, k, v, out, q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
                   attn_mask)
     check(lib.cp_attn_fwd(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), None, 0, _stream_handle(q)), "cp_attn_fwd")
@@ -193,8 +225,9 @@ def cp_attn_bwd(q, k, v, out, lse, dout, q_chunk_pos: Sequence[int], *, layout="
     """Backward of one share: returns (dq in q's dtype, dk, dv float32 partials over the gathered K/V).
 
     grads, if given, is a (dq, dk, dv) triple of preallocated outputs: dq with
-    out's strides, dk/dv contiguous float32 [B, Hkv, Skv, D]. dk/dv rows follow
-    the k/v rows (the KV chunk table's storage order).
+    out's shape and strides, dk/dv contiguous float32 [B, Hkv, Skv, D]. dk/dv
+    rows follow the k/v rows (the KV chunk table's storage order). q, out,
+    dout (and dq) may be 5-D chunked like in cp_attn_fwd, and so may k/v.
     """
     return _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal,
                 softmax_scale, workspace, grads, None, doc_starts, attn_mask)
@@ -223,11 +256,11 @@ def _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal, sof
          workspace, grads, events, doc_starts=(), attn_mask=None):
     lib = _lib.load()
     _check_inputs(q, k, v)
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    B, Hq, Sq, D = _geom(q)[:4]
+    Hkv, Skv = _geom(k)[1:3]
     if dout.shape != q.shape or out.shape != q.shape or dout.dtype != q.dtype or out.dtype != q.dtype:
         raise ValueError("out and dout must match q's shape and dtype")
-    if dout.stride() != out.stride() or out.stride(3) != 1:
+    if dout.stride() != out.stride() or out.stride(-1) != 1:
         out, dout = out.contiguous(), dout.contiguous()
     if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
@@ -242,7 +275,7 @@ def _bwd(q, k, v, out, lse, dout, q_chunk_pos, layout, kv_chunk_pos, causal, sof
         for t in (dk, dv):
             if t.shape != (B, Hkv, Skv, D) or t.dtype != torch.float32 or not t.is_contiguous():
                 raise ValueError("dk and dv must be contiguous float32 [B, Hkv, Skv, D] tensors")
-    d = make_desc(q, k, v, out.stride(), q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
+    d = make_desc(q, k, v, out, q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
                   attn_mask)
     need = cp_attn_workspace_bytes(d, True)
     if workspace is None or workspace.numel() * workspace.element_size() < need:

@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
     const int64_t bh = row / p.sq;
     const int r = (int)(row % p.sq);
     const int b = (int)(bh / p.hq), h = (int)(bh % p.hq);
-    const int64_t off = b * p.o_sb + h * p.o_sh + (int64_t)r * p.o_ss + part * EPL;
+    const int64_t off = b * p.o_sb + h * p.o_sh + (int64_t)r * p.o_ss + (r / p.chunk_len) * p.o_cadj + part * EPL;
     const __bf16 *o = static_cast<const __bf16 *>(p.out) + off;
     const __bf16 *g = static_cast<const __bf16 *>(p.dout) + off;
 #pragma unroll
@@ -275,7 +275,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     const int rows_left = p.chunk_len - 1 - row0;
     const int64_t lrow0 = (int64_t)u.c * p.chunk_len + row0;
     const int64_t ss = is_q ? p.q_ss : p.o_ss;
-    const __bf16 *tbase = (is_q ? qhead + u.h * p.q_sh : ohead + u.h * p.o_sh) + lrow0 * ss;
+    const __bf16 *tbase = (is_q ? qhead + u.h * p.q_sh : ohead + u.h * p.o_sh) + lrow0 * ss +
+                          u.c * (is_q ? p.q_cadj : p.o_cadj);
     if (rows_left >= QT - 1) {
 #pragma unroll
       for (int i = 0; i < INSTS; ++i)
@@ -350,7 +351,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   // This lane's key rows of K (P role) or V (dS role): the B operands.
   bf16x8 kvf[KN][KSTEPS];
   {
-    const __bf16 *src = static_cast<const __bf16 *>(prole ? p.k : p.v) + b * p.kv_sb + hk * p.kv_sh;
+    const __bf16 *src = static_cast<const __bf16 *>(prole ? p.k : p.v) + b * p.kv_sb + hk * p.kv_sh + kc * p.kv.cadj;
 #pragma unroll
     for (int kn = 0; kn < KN; ++kn) {
       const int64_t ro = (int64_t)min(my_key[kn], p.skv - 1) * p.kv_ss + 8 * grp;
@@ -842,8 +843,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     ntiles -= t0;
   }
   struct TileRef {
-    int kt;
-    int64_t base;
+    int kt;          // storage tile
+    int64_t base;    // global position of storage row 0 (this tile's chunk)
+    int64_t adj;     // extra elements of its chunk's storage (chunk strides)
   };
   int cur_c = 0, cur_left = vis_tiles(0), cur_kt = 0;
   auto next_tile = [&]() -> TileRef {
@@ -854,7 +856,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
       cur_left = vis_tiles(cur_c);
       cur_kt = cur_c * (p.kv.len / BN);
     }
-    const TileRef r{cur_kt, p.kv.pos[cur_c] - (int64_t)cur_c * p.kv.len};
+    const TileRef r{cur_kt, p.kv.pos[cur_c] - (int64_t)cur_c * p.kv.len, (int64_t)cur_c * p.kv.cadj};
     ++cur_kt;
     --cur_left;
     return r;
@@ -867,9 +869,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int load_row = qvalid[qb] ? local_row[qb] : chunk * p.chunk_len + item_row0;
-    const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh +
+    const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh + chunk * p.q_cadj +
                        (int64_t)load_row * p.q_ss + 8 * grp;
-    const __bf16 *gp = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh +
+    const __bf16 *gp = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + head * p.o_sh + chunk * p.o_cadj +
                        (int64_t)load_row * p.o_ss + 8 * grp;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
@@ -903,12 +905,13 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
   };
-  // K and V of tile kt into ring stage st.
-  auto dma = [&](int kt, int st) {
+  // K and V of storage tile kt (adj: its KV chunk's extra elements) into
+  // ring stage st.
+  auto dma = [&](int kt, int64_t adj, int st) {
     const uint32_t kd = dst0 + K_OFF + 2 * st * TILE;
     const uint32_t vd = dst0 + V_OFF + 2 * st * TILE;
-    const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride);
-    const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride);
+    const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride + adj);
+    const char *vt_base = reinterpret_cast<const char *>(vbase + (int64_t)kt * tile_stride + adj);
     if (kt * BN + BN <= p.skv) {
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) {
@@ -988,14 +991,14 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsbuf[q][qb][e] = (__bf16)0.0f;
   // Tiles J, J+1, J+2 of the pipeline.
-  TileRef t_cur{t0, kv_pos0}, t_nx1{t0 + 1, kv_pos0}, t_nx2{t0 + 2, kv_pos0};
+  TileRef t_cur{t0, kv_pos0, 0}, t_nx1{t0 + 1, kv_pos0, 0}, t_nx2{t0 + 2, kv_pos0, 0};
   if constexpr (MKV) {
     if (ntiles > 0) t_cur = next_tile();
     if (ntiles > 1) t_nx1 = next_tile();
     if (ntiles > 2) t_nx2 = next_tile();
   }
-  if (ntiles > 0) dma(t_cur.kt, 0);
-  if (ntiles > 1) dma(t_nx1.kt, 1);
+  if (ntiles > 0) dma(t_cur.kt, MKV ? t_cur.adj : 0, 0);
+  if (ntiles > 1) dma(t_nx1.kt, MKV ? t_nx1.adj : 0, 1);
   wait_vmem_all();
   __syncthreads();
   if (ntiles > 0) {
@@ -1183,10 +1186,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // stage of tile J-2, last read in step J-1), then the tile's two blocks.
   auto tile_step = [&](auto j4_tag, int J) {
     constexpr int J4 = decltype(j4_tag)::value;
-    if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : t0 + J + 2, (J4 + 2) % STG);
+    if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : t0 + J + 2, MKV ? t_nx2.adj : 0, (J4 + 2) % STG);
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(taddr[db]));
-    TileRef t{t0 + J, kv_pos0};
+    TileRef t{t0 + J, kv_pos0, 0};
     if constexpr (MKV) {
       t = t_cur;
       t_cur = t_nx1;
@@ -1218,7 +1221,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (!qvalid[qb]) continue;
-    __bf16 *dst = static_cast<__bf16 *>(p.dq) + b * p.o_sb + head * p.o_sh + (int64_t)local_row[qb] * p.o_ss;
+    __bf16 *dst = static_cast<__bf16 *>(p.dq) + b * p.o_sb + head * p.o_sh + chunk * p.o_cadj +
+                  (int64_t)local_row[qb] * p.o_ss;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       bf16x4 o4;

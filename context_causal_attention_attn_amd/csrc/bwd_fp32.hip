@@ -41,8 +41,8 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
   const int h = blockIdx.y, b = blockIdx.z;
   if (r >= p.sq) return;
   const int hk = h / p.group;
-  const int64_t qoff = b * p.q_sb + h * p.q_sh + (int64_t)r * p.q_ss;
-  const int64_t ooff = b * p.o_sb + h * p.o_sh + (int64_t)r * p.o_ss;
+  const int64_t qoff = b * p.q_sb + h * p.q_sh + (int64_t)r * p.q_ss + (r / p.chunk_len) * p.q_cadj;
+  const int64_t ooff = b * p.o_sb + h * p.o_sh + (int64_t)r * p.o_ss + (r / p.chunk_len) * p.o_cadj;
   const float *q = static_cast<const float *>(p.q) + qoff;
   const float *o = static_cast<const float *>(p.out) + ooff;
   const float *g = static_cast<const float *>(p.dout) + ooff;
@@ -74,8 +74,8 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
           continue;
         }
       }
-      const float *kj = kb + (int64_t)j * p.kv_ss;
-      const float *vj = vb + (int64_t)j * p.kv_ss;
+      const float *kj = kb + (int64_t)j * p.kv_ss + (j / p.kv.len) * p.kv.cadj;
+      const float *vj = vb + (int64_t)j * p.kv_ss + (j / p.kv.len) * p.kv.cadj;
       float s = 0.0f, dp = 0.0f;
       for (int d = 0; d < D; ++d) {
         s = fmaf(q[d], kj[d], s);
@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
   const int j = blockIdx.x * 64 + threadIdx.x;   // key row
   const int hk = blockIdx.y, b = blockIdx.z;
   if (j >= p.skv) return;
-  const int64_t koff = b * p.kv_sb + hk * p.kv_sh + (int64_t)j * p.kv_ss;
+  const int64_t koff = b * p.kv_sb + hk * p.kv_sh + (int64_t)j * p.kv_ss + (j / p.kv.len) * p.kv.cadj;
   const float *kj = static_cast<const float *>(p.k) + koff;
   const float *vj = static_cast<const float *>(p.v) + koff;
   float dk[D], dv[D];
@@ -122,8 +122,10 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
       const int64_t row = ((int64_t)b * p.hq + h) * p.sq + r;
       const float lse = p.lse[row];
       if (lse == -INFINITY) continue;
-      const float *q = static_cast<const float *>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)r * p.q_ss;
-      const float *g = static_cast<const float *>(p.dout) + b * p.o_sb + h * p.o_sh + (int64_t)r * p.o_ss;
+      const float *q = static_cast<const float *>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)r * p.q_ss +
+                       (r / p.chunk_len) * p.q_cadj;
+      const float *g = static_cast<const float *>(p.dout) + b * p.o_sb + h * p.o_sh + (int64_t)r * p.o_ss +
+                       (r / p.chunk_len) * p.o_cadj;
       float s = 0.0f, dp = 0.0f;
       for (int d = 0; d < D; ++d) {
         s = fmaf(q[d], kj[d], s);

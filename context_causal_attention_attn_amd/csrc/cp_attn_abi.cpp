@@ -75,7 +75,8 @@ static int32_t validate(const cp_attn_desc *d) {
   if (d->head_dim != 64 && d->head_dim != 128) return CP_ATTN_ERR_UNSUPPORTED;
   if (d->sq_local < 0 || d->skv < 0) return CP_ATTN_ERR_BAD_SHAPE;
   if (d->sq_local > INT32_MAX || d->skv > INT32_MAX) return CP_ATTN_ERR_UNSUPPORTED;
-  if (d->layout != CP_ATTN_LAYOUT_CONTIGUOUS && d->layout != CP_ATTN_LAYOUT_HEAD_TAIL)
+  if (d->layout != CP_ATTN_LAYOUT_CONTIGUOUS && d->layout != CP_ATTN_LAYOUT_HEAD_TAIL &&
+      d->layout != CP_ATTN_LAYOUT_CHUNKED)
     return CP_ATTN_ERR_BAD_LAYOUT;
   if (d->n_q_chunks < 1 || d->n_q_chunks > CP_ATTN_MAX_Q_CHUNKS) return CP_ATTN_ERR_BAD_LAYOUT;
   if (d->layout == CP_ATTN_LAYOUT_CONTIGUOUS && d->n_q_chunks != 1) return CP_ATTN_ERR_BAD_LAYOUT;
@@ -144,13 +145,25 @@ static int32_t validate(const cp_attn_desc *d) {
   // with 32-bit byte offsets from a per-tile base.
   for (auto st : all)
     if (st[2] >= (int64_t(1) << 24)) return CP_ATTN_ERR_UNSUPPORTED;
+  // Chunk strides: non-negative element counts that keep rows 16-byte aligned.
+  for (int i = 0; i < 3; ++i) {
+    if (d->chunk_strides[i] < 0) return CP_ATTN_ERR_BAD_SHAPE;
+    if (d->chunk_strides[i] % vec != 0) return CP_ATTN_ERR_ALIGNMENT;
+  }
   return CP_ATTN_OK;
+}
+
+// Extra elements per chunk index when a chunk stride is given: chunk c's row
+// t sits at c * stride + t * row stride instead of (c * len + t) * row stride.
+static int64_t chunk_adj(int64_t chunk_stride, int64_t len, int64_t row_stride) {
+  return chunk_stride == 0 ? 0 : chunk_stride - len * row_stride;
 }
 
 static void fill_kv_chunks(const cp_attn_desc *d, KvChunks *kv) {
   kv->n = d->n_kv_chunks;
   kv->len = (int32_t)(d->skv / d->n_kv_chunks);
   for (int c = 0; c < d->n_kv_chunks; ++c) kv->pos[c] = d->kv_chunk_pos[c];
+  kv->cadj = chunk_adj(d->chunk_strides[1], kv->len, d->kv_strides[2]);
 }
 
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
@@ -163,6 +176,8 @@ void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
   fill_kv_chunks(d, &p->kv);
+  p->q_cadj = chunk_adj(d->chunk_strides[0], d->sq_local / d->n_q_chunks, d->q_strides[2]);
+  p->o_cadj = chunk_adj(d->chunk_strides[2], d->sq_local / d->n_q_chunks, d->o_strides[2]);
   p->hq = d->hq;
   p->hkv = d->hkv;
   p->group = d->hq / d->hkv;
@@ -261,6 +276,8 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool a
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
   fill_kv_chunks(d, &p->kv);
+  p->q_cadj = chunk_adj(d->chunk_strides[0], d->sq_local / d->n_q_chunks, d->q_strides[2]);
+  p->o_cadj = chunk_adj(d->chunk_strides[2], d->sq_local / d->n_q_chunks, d->o_strides[2]);
   p->batch = d->batch;
   p->hq = d->hq;
   p->hkv = d->hkv;
@@ -338,7 +355,7 @@ const char *cp_attn_error_string(int32_t status) {
     case CP_ATTN_OK: return "ok";
     case CP_ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
     case CP_ATTN_ERR_BAD_SHAPE: return "inconsistent sizes or strides (hq % hkv, chunk lengths, negative strides, non-finite or non-positive scale, causal flag)";
-    case CP_ATTN_ERR_BAD_LAYOUT: return "layout does not match the chunk table (contiguous: 1 Q chunk, head_tail: 2; 1..64 KV chunks)";
+    case CP_ATTN_ERR_BAD_LAYOUT: return "layout does not match the chunk table (contiguous: 1 Q chunk, head_tail: 2, chunked: 1..16; 1..64 KV chunks)";
     case CP_ATTN_ERR_BAD_POSITIONS: return "chunk positions negative, too large, or overlapping";
     case CP_ATTN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, size, row stride (>= 2^24 elements), or KV chunk length not a multiple of 128 with several KV chunks";
     case CP_ATTN_ERR_WORKSPACE: return "workspace missing or smaller than cp_attn_workspace_bytes()";

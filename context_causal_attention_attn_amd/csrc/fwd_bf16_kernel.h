@@ -185,6 +185,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   struct TileRef {
     int kt;          // storage tile
     int64_t base;    // global position of storage row 0 (this tile's chunk)
+    int64_t adj;     // extra elements of its chunk's storage (chunk strides)
   };
   int cur_c = 0, cur_left = vis_tiles(0), cur_kt = 0;
   auto next_tile = [&]() -> TileRef {
@@ -196,7 +197,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       cur_left = vis_tiles(cur_c);
       cur_kt = cur_c * (p.kv.len / BN);
     }
-    const TileRef r{cur_kt, p.kv.pos[cur_c] - (int64_t)cur_c * p.kv.len};
+    const TileRef r{cur_kt, p.kv.pos[cur_c] - (int64_t)cur_c * p.kv.len, (int64_t)cur_c * p.kv.cadj};
     ++cur_kt;
     --cur_left;
     return r;
@@ -206,7 +207,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   bf16x8 qf[QB][KSTEPS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh +
+    const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + head * p.q_sh + chunk * p.q_cadj +
                        (int64_t)local_row[qb] * p.q_ss + 8 * grp;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
@@ -261,11 +262,11 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
   };
-  // Rows of tile kt of K (is_v = false) or V into LDS at dst (this wave's
-  // first row of the stage).
-  auto dma = [&](int kt, bool is_v, uint32_t dst) {
+  // Rows of storage tile kt of K (is_v = false) or V into LDS at dst (this
+  // wave's first row of the stage); adj: its KV chunk's extra elements.
+  auto dma = [&](int kt, int64_t adj, bool is_v, uint32_t dst) {
     const __bf16 *base = is_v ? vbase : kbase;
-    const char *t_base = reinterpret_cast<const char *>(base + (int64_t)kt * tile_stride);
+    const char *t_base = reinterpret_cast<const char *>(base + (int64_t)kt * tile_stride + adj);
     if (kt * BN + BN <= p.skv) {
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) dma1(dst + 2 * i * NW * RPI * D, goff0, t_base + i * istep_bytes);
@@ -281,8 +282,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       }
     }
   };
-  auto dma_k = [&](int kt, int stage) { dma(kt, false, dst0 + 2 * stage * TILE); };
-  auto dma_v = [&](int kt, int stage) { dma(kt, true, dst0 + 2 * (KSTAGES + stage) * TILE); };
+  auto dma_k = [&](int kt, int64_t adj, int stage) { dma(kt, adj, false, dst0 + 2 * stage * TILE); };
+  auto dma_v = [&](int kt, int64_t adj, int stage) { dma(kt, adj, true, dst0 + 2 * (KSTAGES + stage) * TILE); };
 
   f32x4 oacc[QB][DB];
 #pragma unroll
@@ -380,17 +381,17 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       for (int e = 0; e < 8; ++e) pbuf[1][qb][ps][e] = (__bf16)0.0f;
   // Tiles j, j+1, j+2 of the pipeline (step j masks tile j, prefetches V of
   // j+1 and K of j+2).
-  TileRef t_cur{t0, kv_pos0}, t_nx1{t0 + 1, kv_pos0}, t_nx2{t0 + 2, kv_pos0};
+  TileRef t_cur{t0, kv_pos0, 0}, t_nx1{t0 + 1, kv_pos0, 0}, t_nx2{t0 + 2, kv_pos0, 0};
   if constexpr (MKV) {
     if (ntiles > 0) t_cur = next_tile();
     if (ntiles > 1) t_nx1 = next_tile();
     if (ntiles > 2) t_nx2 = next_tile();
   }
   if (ntiles > 0) {
-    dma_k(t_cur.kt, 0);
-    dma_v(t_cur.kt, 0);
+    dma_k(t_cur.kt, MKV ? t_cur.adj : 0, 0);
+    dma_v(t_cur.kt, MKV ? t_cur.adj : 0, 0);
   }
-  if (ntiles > 1) dma_k(t_nx1.kt, 1);
+  if (ntiles > 1) dma_k(t_nx1.kt, MKV ? t_nx1.adj : 0, 1);
   wait_vmem_all();
   __syncthreads();
   if (ntiles > 0) qk0(sbuf[0]);
@@ -411,8 +412,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     using VS = IC<(J6 + 2) % VSTAGES>;   // V of tile j-1
     // K of tile j+2 replaces K of tile j (read in step j-1); V of tile j+1
     // replaces V of tile j-2 (read in step j-1).
-    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : t0 + j + 2, J6 % KSTAGES);
-    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : t0 + j + 1, (J6 + 1) % VSTAGES);
+    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : t0 + j + 2, MKV ? t_nx2.adj : 0, J6 % KSTAGES);
+    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : t0 + j + 1, MKV ? t_nx1.adj : 0, (J6 + 1) % VSTAGES);
     // Keep the operand bases opaque per step: otherwise the compiler hoists a
     // base-plus-stage address per stage out of the loop (several times the
     // registers) instead of folding the stage into the read's immediate.
@@ -635,7 +636,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     const float l = quad_sum(l_part[qb]);
     if (!qvalid[qb]) continue;
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + head * p.o_sh + (int64_t)local_row[qb] * p.o_ss;
+    __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + head * p.o_sh + chunk * p.o_cadj +
+                 (int64_t)local_row[qb] * p.o_ss;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       bf16x4 o4;

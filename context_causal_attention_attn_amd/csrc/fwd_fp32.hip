@@ -41,7 +41,8 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
   const int64_t qhi = chunk_pos + row0 + nrows - 1;
 
   float q[D], o[D];
-  const float *qp = static_cast<const float *>(p.q) + b * p.q_sb + head * p.q_sh + (int64_t)local_row * p.q_ss;
+  const float *qp = static_cast<const float *>(p.q) + b * p.q_sb + head * p.q_sh + chunk * p.q_cadj +
+                    (int64_t)local_row * p.q_ss;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     q[d] = valid ? qp[d] : 0.0f;
@@ -73,8 +74,8 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
       for (int e = t; e < kKeys * D; e += kRows) {
         const int r = e / D, d = e % D;
         const int key = krow0 + j0 + r;
-        ks[r][d] = j0 + r < p.kv.len ? kb[(int64_t)key * p.kv_ss + d] : 0.0f;
-        vs[r][d] = j0 + r < p.kv.len ? vb[(int64_t)key * p.kv_ss + d] : 0.0f;
+        ks[r][d] = j0 + r < p.kv.len ? kb[(int64_t)key * p.kv_ss + kc * p.kv.cadj + d] : 0.0f;
+        vs[r][d] = j0 + r < p.kv.len ? vb[(int64_t)key * p.kv_ss + kc * p.kv.cadj + d] : 0.0f;
       }
       __syncthreads();
       const int nk = min(kKeys, nvis - j0);
@@ -104,7 +105,8 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
     }
   }
   if (!valid) return;
-  float *op = static_cast<float *>(p.out) + b * p.o_sb + head * p.o_sh + (int64_t)local_row * p.o_ss;
+  float *op = static_cast<float *>(p.out) + b * p.o_sb + head * p.o_sh + chunk * p.o_cadj +
+              (int64_t)local_row * p.o_ss;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = o[d] * inv;

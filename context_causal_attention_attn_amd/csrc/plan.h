@@ -39,6 +39,10 @@ struct KvChunks {
   int32_t n;
   int32_t len;
   int64_t pos[kMaxKvChunks];
+  // Storage: key row j of chunk c = j / len sits at j * row stride + c * cadj
+  // elements from its head's base (cadj = chunk stride - len * row stride; 0
+  // when the rows follow on).
+  int64_t cadj;
 };
 
 // ---------------------------------------------------------------------------
@@ -59,6 +63,7 @@ struct FwdParams {
   int64_t q_sb, q_sh, q_ss;     // element strides of q (batch, head, row)
   int64_t kv_sb, kv_sh, kv_ss;  // of k and v
   int64_t o_sb, o_sh, o_ss;     // of out
+  int64_t q_cadj, o_cadj;       // extra elements per query chunk index (chunk strides; 0: rows follow on)
   KvChunks kv;                  // positions of the key rows
   DocBounds docs;               // packed-sequence boundaries (n = 0: none)
   const uint8_t *mask;          // user attention mask (NULL: none), [b][h][row][key]
@@ -132,6 +137,7 @@ struct BwdParams {
   int64_t q_sb, q_sh, q_ss;
   int64_t kv_sb, kv_sh, kv_ss;
   int64_t o_sb, o_sh, o_ss;     // out, dout and dq
+  int64_t q_cadj, o_cadj;       // extra elements per query chunk index (chunk strides; 0: rows follow on)
   KvChunks kv;                  // positions of the key rows
   DocBounds docs;               // packed-sequence boundaries (n = 0: none)
   const uint8_t *mask;          // user attention mask (NULL: none), [b][h][row][key]

@@ -11,6 +11,12 @@ Ulysses sub-group).
 An all_to_all_single over the group (not part of this package) moves block p of
 every rank's packed buffer to rank p. These functions only marshal arguments;
 every copy runs in the library's kernel.
+
+The share kernels can also take the received blocks as they are
+(`ulysses_fwd_in_place`, `ulysses_bwd_in_place`): block p holds sequence rows
+p*L .. p*L+L-1 of the head shard, so it is query (and key) chunk p of a
+"chunked" share, and the output comes back in the blocks layout the reverse
+exchange sends. No unpack or pack pass runs around the attention.
 """
 from __future__ import annotations
 
@@ -20,7 +26,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from .api import _stream_handle
+from .api import _stream_handle, cp_attn_bwd, cp_attn_fwd
 
 _DTYPES = {torch.bfloat16: _lib.DTYPE_BF16, torch.float32: _lib.DTYPE_FP32}
 
@@ -94,3 +100,27 @@ def head_to_seq_unpack(blocks: torch.Tensor, out: Optional[torch.Tensor] = None)
         raise ValueError("out must be a [B, u*H, L, D] tensor of the blocks' dtype")
     cp_attn_ulysses_relayout("head_to_seq_unpack", blocks, x, x, u, H, L)
     return x
+
+
+def _chunk_pos(blocks: torch.Tensor, offset: int):
+    return [offset + p * blocks.shape[3] for p in range(blocks.shape[0])]
+
+
+def ulysses_fwd_in_place(qb: torch.Tensor, kb: torch.Tensor, vb: torch.Tensor, *, causal: bool = True,
+                         softmax_scale: Optional[float] = None, q_offset: int = 0, kv_offset: int = 0,
+                         out: Optional[torch.Tensor] = None):
+    """Forward of a Ulysses head shard read straight from the received blocks
+    qb [u, B, H, L, D] and kb, vb [u, B, Hkv, L, D] (block p: sequence rows
+    p*L.., global positions offset + p*L..; with several K/V blocks, L a
+    multiple of 128). Returns (out [u, B, H, L, D], the blocks the head->seq
+    exchange sends, and lse [B, H, u*L])."""
+    return cp_attn_fwd(qb, kb, vb, _chunk_pos(qb, q_offset), layout="chunked", kv_chunk_pos=_chunk_pos(kb, kv_offset),
+                       causal=causal, softmax_scale=softmax_scale, out=out)
+
+
+def ulysses_bwd_in_place(qb, kb, vb, outb, lse, doutb, *, causal: bool = True,
+                         softmax_scale: Optional[float] = None, q_offset: int = 0, kv_offset: int = 0):
+    """Backward of the same share from blocks: returns (dq [u, B, H, L, D] in
+    the blocks layout, dk, dv float32 [B, Hkv, u*L, D] in sequence order)."""
+    return cp_attn_bwd(qb, kb, vb, outb, lse, doutb, _chunk_pos(qb, q_offset), layout="chunked",
+                       kv_chunk_pos=_chunk_pos(kb, kv_offset), causal=causal, softmax_scale=softmax_scale)

@@ -45,8 +45,8 @@ extern "C" {
 
 /* Bumped whenever cp_attn_desc's layout or a declaration's meaning changes
  * (3: the user-mask fields attn_mask, mask_strides, mask_additive and the
- * additive-mask hide threshold). */
-#define CP_ATTN_ABI_VERSION 3
+ * additive-mask hide threshold; 4: chunk_strides and the chunked layout). */
+#define CP_ATTN_ABI_VERSION 4
 #define CP_ATTN_MAX_Q_CHUNKS 16
 /* Most KV chunks a descriptor may list (a Head-Tail all-gather at cp = 32
  * delivers 64 chunks). */
@@ -72,7 +72,13 @@ typedef enum {
   CP_ATTN_LAYOUT_CONTIGUOUS = 0,
   /* Head-Tail (zigzag): exactly two equal chunks, front = chunk r, back =
    * chunk 2*cp-1-r of 2*cp chunks. [Trainer-CP] §4.4, [FLA-CP] §3.2. */
-  CP_ATTN_LAYOUT_HEAD_TAIL = 1
+  CP_ATTN_LAYOUT_HEAD_TAIL = 1,
+  /* Any number (1..CP_ATTN_MAX_Q_CHUNKS) of equal chunks at the listed,
+   * pairwise disjoint positions. With chunk_strides it describes a Ulysses
+   * head shard still laid out as the sequence->head all-to-all delivered it:
+   * chunk p (rows p*L .. p*L+L-1 of the sequence) is block p of the received
+   * buffer [u, batch, heads, L, head_dim] ([CP-migration] §6.2, §6.3). */
+  CP_ATTN_LAYOUT_CHUNKED = 2
 } cp_attn_layout;
 
 /* Element type of q, k, v, out, dout and dq. lse, the backward workspace and
@@ -107,6 +113,16 @@ typedef enum {
  *   dq          [batch, hq,  sq_local, head_dim]  o_strides (shared by the three)
  *   lse         [batch, hq,  sq_local]            contiguous float32
  *   dk, dv      [batch, hkv, skv, head_dim]       contiguous float32
+ *
+ * With chunk_strides[0] = C != 0, row i of q (chunk c = i / L, t = i % L) is
+ * at batch/head offset + c * C + t * q_strides[2] instead of i * q_strides[2];
+ * likewise out, dout and dq with chunk_strides[2], and key row j of k and v
+ * (KV chunk c = j / Lkv) with chunk_strides[1]. lse, dk and dv keep the
+ * plain row order. This lets the kernels read a Ulysses all-to-all's
+ * received blocks [u, batch, heads, L, head_dim] in place (batch stride
+ * heads*L*head_dim, head stride L*head_dim, row stride head_dim, chunk stride
+ * batch*heads*L*head_dim) and write out in the layout the reverse exchange
+ * sends.
  *
  * Query row i lies in chunk c = i / L (L = sq_local / n_q_chunks) and has
  * global position q_chunk_pos[c] + i % L. Key row j lies in KV chunk
@@ -174,6 +190,9 @@ typedef struct cp_attn_desc {
   const void *attn_mask;       /* NULL, or DEVICE [batch][hq][sq_local][skv] mask of mask_additive's kind */
   int64_t mask_strides[3];     /* batch, head, row strides of attn_mask in bytes (0 broadcasts); key stride 1 */
   int32_t mask_additive;       /* 0: bytes, nonzero = may attend; 1: float32 added to the scaled score */
+  int64_t chunk_strides[3];    /* q, k/v, out/dout/dq: elements from one chunk's row 0 to the next */
+                               /* chunk's (Q chunks for q and out, KV chunks for k/v); 0: the rows */
+                               /* follow on (chunk length x row stride). Multiples of 16 bytes, >= 0. */
 } cp_attn_desc;
 
 /* ABI version of the loaded library (CP_ATTN_ABI_VERSION of its build). */

@@ -450,3 +450,29 @@ def test_workspace_holds_split_key_tile_partials():
     part = ws(1, 4, 1, 32768, 32768, [0])                                  # Ulysses cp=8 rank 0
     unit = 2 * 128 * 128 * 4                                               # dK and dV of one key tile
     assert part > 0 and part % (256 * unit) == 0                           # whole extra parts of 256 tiles
+
+
+def test_validate_chunked_layout_and_chunk_strides():
+    """The chunked layout takes 1..16 equal query chunks at disjoint
+    positions; chunk strides (q, k/v, out) are non-negative element counts
+    that keep rows 16-byte aligned (bf16: multiples of 8 elements)."""
+    u, H, L, D = 8, 4, 256, 128
+    blocks = (1 * H * L * D, L * D, D)            # batch, head, row strides of one received block
+    d = desc(hq=H, hkv=1, sq_local=u * L, skv=u * L, q_chunk_pos=[p * L for p in range(u)],
+             kv_chunk_pos=[p * L for p in range(u)], layout="chunked", q_strides=blocks, kv_strides=(L * D, L * D, D),
+             o_strides=blocks, chunk_strides=(H * L * D, L * D, H * L * D))
+    assert status(d) == 0
+    for i in range(3):
+        saved = d.desc.chunk_strides[i]
+        d.desc.chunk_strides[i] = -8
+        assert status(d) == -2
+        d.desc.chunk_strides[i] = saved + 4
+        assert status(d) == -9
+        d.desc.chunk_strides[i] = saved
+    assert status(d) == 0
+    over = desc(sq_local=17 * 16, q_chunk_pos=[p * 16 for p in range(17)], layout="chunked")
+    assert status(over) == -3                       # more than 16 query chunks
+    two = desc(sq_local=512, q_chunk_pos=[0, 1000], layout="contiguous")
+    assert status(two) == -3                        # contiguous takes exactly one chunk
+    d.desc.layout = 3
+    assert status(d) == -3
