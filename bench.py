@@ -25,7 +25,8 @@ state a target for ("configs", forward and backward each): the Head-Tail
 shares of all 8 ranks (with their max/min spread under "balance"), the Ulysses
 cp=8 rank-0 share, the Hybrid U=2 x C=4 rank-4 share and the Head-Tail B = 2
 backward shares of ranks 0 and 7, and the Colossal rank-7 share over eight
-packed sequences. While the headline step keeps running for
+packed sequences; the Ulysses share also runs straight from the all-to-all's
+received blocks (".../in_place": no unpack or pack pass). While the headline step keeps running for
 about 2.5 s, amd-smi reads the GFX clocks and socket power ("clock"; the chip
 runs at its power cap, below the 2.4 GHz the peak assumes). The oracle's CPU
 baseline runs last, in a child process. Prints ONE JSON line. `--detail` adds
@@ -55,6 +56,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-s", type=float, default=1.0,
+                    help="seconds of untimed steps of the headline share before its warm-up steps")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--rank", type=int, default=None,
                     help="CP rank of the workload's share (default: the workload's first listed rank)")
@@ -129,26 +132,55 @@ def traffic_record(part):
     return None
 
 
-def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", warm_s=0.0):
+class BlockShare:
+    """A Ulysses head shard as the sequence->head all-to-all delivers it: the
+    received blocks [u, B, H, L, D] of Q, K, V (and dO), read in place by the
+    share kernels (chunked layout, block p at positions p*L..)."""
+
+    def __init__(self, prob, U, rank, dev):
+        import torch
+        from context_causal_attention_attn_amd import seq_to_head_pack
+        L = prob.q.shape[2] // U
+
+        def recv(t):
+            # rank `rank`'s receive buffer: block `rank` of every source rank's send buffer
+            return torch.stack([seq_to_head_pack(t[:, :, p * L:(p + 1) * L].to(dev), U)[rank]
+                                for p in range(U)]).contiguous()
+
+        self.q, self.k, self.v = recv(prob.q), recv(prob.k), recv(prob.v)
+        self._dout = recv(prob.dout) if prob.dout is not None else None
+        self.q_chunk_pos = [p * L for p in range(U)]
+        self.kv_chunk_pos = list(self.q_chunk_pos)
+        self.layout = "chunked"
+
+    def take_rows(self, _dout):
+        return self._dout
+
+
+def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", warm_s=0.0, in_place=False):
     import torch
     from context_causal_attention_attn_amd import api, cut_share
 
     dev = torch.device("cuda")
-    q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
     kind, cp, r, U = share_for(spec, rank)
     from synthetic import doc_starts
-    sh = cut_share(kind, q, k, v, cp, r, ulysses=U, kv_order=kv_order)
+    if in_place:   # Ulysses share straight from the exchange's blocks
+        sh = BlockShare(prob, cp, r, dev)
+    else:
+        q, k, v = prob.q.to(dev), prob.k.to(dev), prob.v.to(dev)
+        sh = cut_share(kind, q, k, v, cp, r, ulysses=U, kv_order=kv_order)
     kvp = sh.kv_chunk_pos
     docs = doc_starts(spec)
-    D = q.shape[-1]
+    D = sh.q.shape[-1]
     scale = 1.0 / math.sqrt(D)
-    d = api.make_desc(sh.q, sh.k, sh.v, sh.q.stride(), sh.q_chunk_pos, kvp, sh.layout, True, scale, docs)
+    d = api.make_desc(sh.q, sh.k, sh.v, sh.q, sh.q_chunk_pos, kvp, sh.layout, True, scale, docs)
     pairs = api.cp_attn_share_pairs(d)
-    B, Hq, Sq = sh.q.shape[0], sh.q.shape[1], sh.q.shape[2]
-    Hkv, Skv = sh.k.shape[1], sh.k.shape[2]
+    B, Hq, Sq = api._geom(sh.q)[:3]
+    Hkv, Skv = api._geom(sh.k)[1:3]
     out = torch.empty(sh.q.shape, dtype=sh.q.dtype, device=dev)
-    lse = torch.empty(sh.q.shape[:3], dtype=torch.float32, device=dev)
-    dout = sh.take_rows(prob.dout.to(dev)).contiguous() if (with_bwd and prob.dout is not None) else None
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    dout = (sh.take_rows(prob.dout.to(dev)).contiguous() if not in_place else sh.take_rows(None)) \
+        if (with_bwd and prob.dout is not None) else None
     if dout is not None:
         grads = (torch.empty_like(out), torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=dev),
                  torch.empty((B, Hkv, Skv, D), dtype=torch.float32, device=dev))
@@ -166,18 +198,21 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", wa
     def new_events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
-    # `warmup` steps, then more until warm_s seconds have passed (clocks
-    # ramp up over a few hundred milliseconds after the GPU idled).
-    t_warm = time.perf_counter()
-    done = 0
-    while done < warmup or time.perf_counter() - t_warm < warm_s:
+    # Steps for warm_s seconds (clocks ramp up over a few hundred
+    # milliseconds after the GPU idled), then exactly `warmup` steps.
+    def untimed():
         ev = new_events()
         fwd()
         if dout is not None:
             bwd(ev[1:])
-        done += 1
-        if done >= warmup:
-            torch.cuda.synchronize()
+
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < warm_s:
+        for _ in range(4):
+            untimed()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        untimed()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [new_events() for _ in range(steps)]
@@ -453,27 +488,40 @@ def share_entry(rr):
     return ent
 
 
-def time_configs(steps, warmup, shared=None):
-    """Time every share of CONFIG_SHARES (forward and backward) after a short
-    warm-up each; `shared` is (spec, problem) of the headline problem, reused
-    by the shares cut from the same global problem."""
+def problem_key(sp):
+    return (sp["batch"], sp["hq"], sp["hkv"], sp["seq"], sp["head_dim"], sp["dtype"])
+
+
+def config_problems(shared):
+    """The seeded global problems of CONFIG_SHARES (with dO), generated before
+    any timing starts, so that no share is timed on a GPU that sat idle while
+    the host drew its inputs; `shared` is (spec, problem) of the headline."""
     from synthetic import WORKLOADS, global_problem
-    out, cache = {}, {}
+    probs = {problem_key(shared[0]): shared[1]}
+    for name, _ in CONFIG_SHARES:
+        key = problem_key(WORKLOADS[name])
+        if key not in probs:
+            probs[key] = global_problem(*key, 0, with_dout=True)
+    return probs
+
+
+def time_configs(steps, warmup, probs):
+    """Time every share of CONFIG_SHARES (forward and backward) after a
+    0.3 s warm-up each."""
+    from synthetic import WORKLOADS
+    out = {}
     for name, ranks in CONFIG_SHARES:
         sp = dict(WORKLOADS[name])
-        key = (sp["batch"], sp["hq"], sp["hkv"], sp["seq"], sp["head_dim"], sp["dtype"])
-        if shared is not None and key == tuple(shared[0][k] for k in ("batch", "hq", "hkv", "seq",
-                                                                       "head_dim", "dtype")):
-            pr = shared[1]
-        else:
-            if key not in cache:
-                cache.clear()
-                cache[key] = global_problem(*key, 0, with_dout=True)
-            pr = cache[key]
+        pr = probs[problem_key(sp)]
         for r in ranks:
             rr = time_share(sp, pr, r, steps, warmup, True, warm_s=0.3)
             out[f"{name}/r{r}"] = share_entry(rr)
             del rr
+            if sp["kind"] == "ulysses":
+                # The same share read straight from the all-to-all's blocks.
+                rr = time_share(sp, pr, r, steps, warmup, True, warm_s=0.3, in_place=True)
+                out[f"{name}/r{r}/in_place"] = share_entry(rr)
+                del rr
     bal = {}
     for name, ranks in CONFIG_SHARES:
         fw = [out[f"{name}/r{r}"]["fwd_ms"] for r in ranks]
@@ -517,7 +565,12 @@ def main():
     if not 0 <= rank < spec["cp"]:
         print(f"--rank {rank} is outside 0..{spec['cp'] - 1} for {args.workload}", file=sys.stderr)
         sys.exit(2)
-    res = time_share(spec, prob, rank, args.steps, args.warmup, True, args.kv_order)
+    configs = not args.no_configs and args.workload == WORKLOAD
+    probs = config_problems((spec, prob)) if configs else None
+    # The W warm-up steps run after at least args.warm_s seconds of the same
+    # step, so the timed steps see the clocks of a busy GPU, not of one that
+    # idled while the host drew the inputs.
+    res = time_share(spec, prob, rank, args.steps, args.warmup, True, args.kv_order, warm_s=args.warm_s)
     ms, fl, io = res["ms"], res["flops"], res["bytes"]
     ms_per_step = res["total_ms"] / args.steps
     flops_step = fl["fwd"] + (fl["bwd"] if res["has_bwd"] else 0.0)
@@ -580,13 +633,15 @@ def main():
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
         "peak_bf16_tflops": PEAK_BF16_TFLOPS,
+        "warm_s": args.warm_s,
     }
     if not args.no_clock:
         clk = sample_clock(res["step"])
         line["clock"] = clk
     del res
-    if not args.no_configs and args.workload == WORKLOAD:
-        cfg, bal = time_configs(max(5, args.steps // 2), args.warmup, shared=(spec, prob))
+    if configs:
+        cfg, bal = time_configs(max(5, args.steps // 2), args.warmup, probs)
+        del probs
         line["configs"] = cfg
         line["balance"] = bal
     if args.detail:

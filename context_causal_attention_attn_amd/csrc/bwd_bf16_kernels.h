@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "gfx950_common.h"
 #include "plan.h"
 
@@ -98,6 +100,27 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * 64;
 
+// Zero dK/dV rows outside the key tiles [kt0, kt1) the key-stationary kernel
+// computes (keys no local query can see), as workgroup `w` of `nw` doing this:
+// 16-byte stores of both, grid-stride over every (batch, KV head)'s rows.
+template <int D>
+__device__ __forceinline__ void zero_unseen_keys(const BwdParams &p, int w, int nw, int tid, int nthreads) {
+  constexpr int VPR = D / 4;                        // float4 per row
+  const int64_t front = (int64_t)p.kt0 * BK;        // rows [0, front) and [back, skv)
+  const int64_t back = min((int64_t)p.kt1 * BK, (int64_t)p.skv);
+  const int64_t per_head = (front + (p.skv - back)) * VPR;
+  const int64_t n = per_head * p.batch * p.hkv;
+  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t i = (int64_t)w * nthreads + tid; i < n; i += (int64_t)nw * nthreads) {
+    const int64_t g = i / per_head, e = i % per_head;
+    const int64_t r = e / VPR;
+    const int64_t row = r < front ? r : back + (r - front);
+    const int64_t off = (g * p.skv + row) * D + (e % VPR) * 4;
+    *reinterpret_cast<f32x4 *>(p.dk + off) = z;
+    *reinterpret_cast<f32x4 *>(p.dv + off) = z;
+  }
+}
+
 // KMODE 0: plain; 1: packed-sequence boundaries (keys are visible only to
 // rows of their own sequence); 2: a user attention mask.
 template <int D, int KMODE>
@@ -140,6 +163,13 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   const int col = lane & 15;               // operand row / accumulator column (key)
 
   const int groups = p.batch * p.hkv;
+  // Workgroups past the key tiles' zero dK/dV of the keys no local row sees
+  // (they run last, in the tail of the grid).
+  const int n_compute = (p.kt1 - p.kt0) * p.kv_parts * groups;
+  if ((int)blockIdx.x >= n_compute) {
+    zero_unseen_keys<D>(p, (int)blockIdx.x - n_compute, (int)gridDim.x - n_compute, threadIdx.x, kDkdvThreads);
+    return;
+  }
   const int g = blockIdx.x % groups;
   const int unit = blockIdx.x / groups;          // key tile, then part: earliest keys (most work) first
   const int part = unit % p.kv_parts;
@@ -351,7 +381,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   // This lane's key rows of K (P role) or V (dS role): the B operands.
   bf16x8 kvf[KN][KSTEPS];
   {
-    const __bf16 *src = static_cast<const __bf16 *>(prole ? p.k : p.v) + b * p.kv_sb + hk * p.kv_sh + kc * p.kv.cadj;
+    const int64_t adj = (p.kv.store_lg < 31 ? (int64_t)key0 >> p.kv.store_lg : (int64_t)kc) * p.kv.cadj;
+    const __bf16 *src = static_cast<const __bf16 *>(prole ? p.k : p.v) + b * p.kv_sb + hk * p.kv_sh + adj;
 #pragma unroll
     for (int kn = 0; kn < KN; ++kn) {
       const int64_t ro = (int64_t)min(my_key[kn], p.skv - 1) * p.kv_ss + 8 * grp;
@@ -997,8 +1028,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     if (ntiles > 1) t_nx1 = next_tile();
     if (ntiles > 2) t_nx2 = next_tile();
   }
-  if (ntiles > 0) dma(t_cur.kt, MKV ? t_cur.adj : 0, 0);
-  if (ntiles > 1) dma(t_nx1.kt, MKV ? t_nx1.adj : 0, 1);
+  // Storage offset of a natural-order tile (merged chunks; 0 for one chunk).
+  auto nat_adj = [&](int kt) { return ((int64_t)kt * BN >> p.kv.store_lg) * p.kv.cadj; };
+  if (ntiles > 0) dma(t_cur.kt, MKV ? t_cur.adj : nat_adj(t_cur.kt), 0);
+  if (ntiles > 1) dma(t_nx1.kt, MKV ? t_nx1.adj : nat_adj(t_nx1.kt), 1);
   wait_vmem_all();
   __syncthreads();
   if (ntiles > 0) {
@@ -1186,7 +1219,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // stage of tile J-2, last read in step J-1), then the tile's two blocks.
   auto tile_step = [&](auto j4_tag, int J) {
     constexpr int J4 = decltype(j4_tag)::value;
-    if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : t0 + J + 2, MKV ? t_nx2.adj : 0, (J4 + 2) % STG);
+    if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : t0 + J + 2, MKV ? t_nx2.adj : nat_adj(t0 + J + 2), (J4 + 2) % STG);
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(taddr[db]));
     TileRef t{t0 + J, kv_pos0, 0};
@@ -1255,21 +1288,18 @@ __global__ void __launch_bounds__(256) bwd_zero_keys_kernel(const BwdParams p) {
 // Launches of one mode's instantiations.
 template <int D, int KMODE>
 void launch_dkdv_mode(const BwdParams &p, hipStream_t s) {
+  // Key tiles (and their parts) first, then workgroups that zero the dK/dV
+  // rows of the keys no local row sees: about 64 KiB of stores each, at most
+  // one per compute unit.
   const int64_t tiles = p.kt1 - p.kt0;
-  if (tiles > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KMODE>), dim3(tiles * p.kv_parts * p.batch * p.hkv),
-                       dim3(kDkdvThreads), 0, s, p);
-    if (p.kv_parts > 1)
-      hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<D>, dim3(tiles * p.batch * p.hkv, (BK * D / 4 + 255) / 256),
-                         dim3(256), 0, s, p);
-  }
   const int64_t back = (int64_t)p.kt1 * BK < p.skv ? (int64_t)p.kt1 * BK : (int64_t)p.skv;
-  const int64_t zrows = (int64_t)p.kt0 * BK + (p.skv - back);
-  if (zrows > 0) {
-    const int64_t want = (zrows * (D / 4) + 255) / 256;
-    const int64_t blocks = want < 4096 ? want : 4096;
-    hipLaunchKernelGGL(bwd_zero_keys_kernel<D>, dim3(blocks, p.batch * p.hkv), dim3(256), 0, s, p);
-  }
+  const int64_t zbytes = ((int64_t)p.kt0 * BK + (p.skv - back)) * D * 4 * 2 * p.batch * p.hkv;
+  const int64_t zw = zbytes > 0 ? std::min<int64_t>((zbytes + 65535) / 65536, 256) : 0;
+  const int64_t grid = tiles * p.kv_parts * p.batch * p.hkv + zw;
+  if (grid > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D, KMODE>), dim3(grid), dim3(kDkdvThreads), 0, s, p);
+  if (tiles > 0 && p.kv_parts > 1)
+    hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<D>, dim3(tiles * p.batch * p.hkv, (BK * D / 4 + 255) / 256),
+                       dim3(256), 0, s, p);
 }
 
 template <int D, int MODE>

@@ -17,6 +17,11 @@
 namespace cpattn {
 namespace {
 
+// Storage offset (elements) of key row j beyond j * row stride.
+__device__ __forceinline__ int64_t kv_row_adj(const KvChunks &kv, int64_t j) {
+  return (kv.store_lg < 31 ? j >> kv.store_lg : j / kv.len) * kv.cadj;
+}
+
 __device__ __forceinline__ int64_t row_pos(const BwdParams &p, int r) {
   return p.chunk_pos[r / p.chunk_len] + r % p.chunk_len;
 }
@@ -74,8 +79,8 @@ __global__ void __launch_bounds__(64) bwd_fp32_delta_dq_kernel(const BwdParams p
           continue;
         }
       }
-      const float *kj = kb + (int64_t)j * p.kv_ss + (j / p.kv.len) * p.kv.cadj;
-      const float *vj = vb + (int64_t)j * p.kv_ss + (j / p.kv.len) * p.kv.cadj;
+      const float *kj = kb + (int64_t)j * p.kv_ss + kv_row_adj(p.kv, j);
+      const float *vj = vb + (int64_t)j * p.kv_ss + kv_row_adj(p.kv, j);
       float s = 0.0f, dp = 0.0f;
       for (int d = 0; d < D; ++d) {
         s = fmaf(q[d], kj[d], s);
@@ -95,7 +100,7 @@ __global__ void __launch_bounds__(64) bwd_fp32_dkv_kernel(const BwdParams p) {
   const int j = blockIdx.x * 64 + threadIdx.x;   // key row
   const int hk = blockIdx.y, b = blockIdx.z;
   if (j >= p.skv) return;
-  const int64_t koff = b * p.kv_sb + hk * p.kv_sh + (int64_t)j * p.kv_ss + (j / p.kv.len) * p.kv.cadj;
+  const int64_t koff = b * p.kv_sb + hk * p.kv_sh + (int64_t)j * p.kv_ss + kv_row_adj(p.kv, j);
   const float *kj = static_cast<const float *>(p.k) + koff;
   const float *vj = static_cast<const float *>(p.v) + koff;
   float dk[D], dv[D];

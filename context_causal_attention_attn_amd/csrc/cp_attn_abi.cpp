@@ -164,6 +164,19 @@ static void fill_kv_chunks(const cp_attn_desc *d, KvChunks *kv) {
   kv->len = (int32_t)(d->skv / d->n_kv_chunks);
   for (int c = 0; c < d->n_kv_chunks; ++c) kv->pos[c] = d->kv_chunk_pos[c];
   kv->cadj = chunk_adj(d->chunk_strides[1], kv->len, d->kv_strides[2]);
+  kv->store_lg = 31;
+  // Chunks that follow each other in position order with power-of-two
+  // lengths (e.g. the blocks a Ulysses all-to-all delivers) are one chunk in
+  // natural order for the kernels; only their storage offset stays per chunk.
+  bool natural = kv->n > 1 && (kv->len & (kv->len - 1)) == 0;
+  for (int c = 1; natural && c < kv->n; ++c) natural = kv->pos[c] == kv->pos[0] + (int64_t)c * kv->len;
+  if (natural) {
+    int lg = 0;
+    while ((1 << lg) < kv->len) ++lg;
+    kv->store_lg = lg;
+    kv->n = 1;
+    kv->len = (int32_t)d->skv;
+  }
 }
 
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
@@ -301,12 +314,13 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool a
   // Key tiles some local query can see. With keys in natural order, a key is
   // visible only if it is not after the last local row (causal) and not
   // before the sequence start of the earliest local row (packed sequences);
-  // a user mask can only hide more. Several KV chunks: every tile.
+  // a user mask can only hide more. Several KV chunks out of position order:
+  // every tile.
   const int64_t n_tiles = (d->skv + kBwdBlockKV - 1) / kBwdBlockKV;
   p->kt0 = 0;
   p->kt1 = (int32_t)n_tiles;
-  if (d->n_kv_chunks == 1 && s.chunk_len > 0 && d->skv > 0) {
-    const int64_t kv0 = d->kv_chunk_pos[0];
+  if (p->kv.n == 1 && s.chunk_len > 0 && d->skv > 0) {
+    const int64_t kv0 = p->kv.pos[0];
     int64_t qlo = INT64_MAX, qhi = INT64_MIN;
     for (int c = 0; c < s.n_q_chunks; ++c) {
       qlo = std::min(qlo, s.chunk_pos[c]);

@@ -387,11 +387,13 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if (ntiles > 1) t_nx1 = next_tile();
     if (ntiles > 2) t_nx2 = next_tile();
   }
+  // Storage offset of a natural-order tile (merged chunks; 0 for one chunk).
+  auto nat_adj = [&](int kt) { return ((int64_t)kt * BN >> p.kv.store_lg) * p.kv.cadj; };
   if (ntiles > 0) {
-    dma_k(t_cur.kt, MKV ? t_cur.adj : 0, 0);
-    dma_v(t_cur.kt, MKV ? t_cur.adj : 0, 0);
+    dma_k(t_cur.kt, MKV ? t_cur.adj : nat_adj(t_cur.kt), 0);
+    dma_v(t_cur.kt, MKV ? t_cur.adj : nat_adj(t_cur.kt), 0);
   }
-  if (ntiles > 1) dma_k(t_nx1.kt, MKV ? t_nx1.adj : 0, 1);
+  if (ntiles > 1) dma_k(t_nx1.kt, MKV ? t_nx1.adj : nat_adj(t_nx1.kt), 1);
   wait_vmem_all();
   __syncthreads();
   if (ntiles > 0) qk0(sbuf[0]);
@@ -412,8 +414,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     using VS = IC<(J6 + 2) % VSTAGES>;   // V of tile j-1
     // K of tile j+2 replaces K of tile j (read in step j-1); V of tile j+1
     // replaces V of tile j-2 (read in step j-1).
-    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : t0 + j + 2, MKV ? t_nx2.adj : 0, J6 % KSTAGES);
-    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : t0 + j + 1, MKV ? t_nx1.adj : 0, (J6 + 1) % VSTAGES);
+    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : t0 + j + 2, MKV ? t_nx2.adj : nat_adj(t0 + j + 2), J6 % KSTAGES);
+    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : t0 + j + 1, MKV ? t_nx1.adj : nat_adj(t0 + j + 1), (J6 + 1) % VSTAGES);
     // Keep the operand bases opaque per step: otherwise the compiler hoists a
     // base-plus-stage address per stage out of the loop (several times the
     // registers) instead of folding the stage into the read's immediate.

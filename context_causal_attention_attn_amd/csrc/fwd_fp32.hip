@@ -14,6 +14,11 @@
 namespace cpattn {
 namespace {
 
+// Storage offset (elements) of key row j beyond j * row stride.
+__device__ __forceinline__ int64_t kv_row_adj(const KvChunks &kv, int64_t j) {
+  return (kv.store_lg < 31 ? j >> kv.store_lg : j / kv.len) * kv.cadj;
+}
+
 constexpr int kRows = 64;     // query rows per workgroup (one per thread)
 constexpr int kKeys = 32;     // keys per LDS tile
 
@@ -74,8 +79,8 @@ __global__ void __launch_bounds__(kRows) fwd_fp32_kernel(const FwdParams p) {
       for (int e = t; e < kKeys * D; e += kRows) {
         const int r = e / D, d = e % D;
         const int key = krow0 + j0 + r;
-        ks[r][d] = j0 + r < p.kv.len ? kb[(int64_t)key * p.kv_ss + kc * p.kv.cadj + d] : 0.0f;
-        vs[r][d] = j0 + r < p.kv.len ? vb[(int64_t)key * p.kv_ss + kc * p.kv.cadj + d] : 0.0f;
+        ks[r][d] = j0 + r < p.kv.len ? kb[(int64_t)key * p.kv_ss + kv_row_adj(p.kv, key) + d] : 0.0f;
+        vs[r][d] = j0 + r < p.kv.len ? vb[(int64_t)key * p.kv_ss + kv_row_adj(p.kv, key) + d] : 0.0f;
       }
       __syncthreads();
       const int nk = min(kKeys, nvis - j0);

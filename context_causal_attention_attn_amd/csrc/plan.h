@@ -39,10 +39,13 @@ struct KvChunks {
   int32_t n;
   int32_t len;
   int64_t pos[kMaxKvChunks];
-  // Storage: key row j of chunk c = j / len sits at j * row stride + c * cadj
-  // elements from its head's base (cadj = chunk stride - len * row stride; 0
-  // when the rows follow on).
+  // Storage: key row j sits at j * row stride + s(j) * cadj elements from its
+  // head's base, s(j) its storage chunk: j >> store_lg when store_lg < 31
+  // (the host merged a table of consecutive, equally strided chunks of
+  // 2^store_lg rows into one chunk), else j / len (cadj = chunk stride - chunk
+  // length * row stride; 0 when the rows follow on).
   int64_t cadj;
+  int32_t store_lg;
 };
 
 // ---------------------------------------------------------------------------
