@@ -83,10 +83,10 @@ def share_for(spec, rank):
 
 
 KERNEL_SOURCES = {   # files whose text determines each kernel's machine code
-    "fwd": ["fwd_bf16_kernel.h", "fwd_bf16_m0.hip", "gfx950_common.h", "plan.h"],
-    "pre": ["bwd_bf16_kernels.h", "bwd_bf16.hip", "gfx950_common.h", "plan.h"],
-    "dkdv": ["bwd_bf16_kernels.h", "bwd_dkdv_m0.hip", "gfx950_common.h", "plan.h"],
-    "dq": ["bwd_bf16_kernels.h", "bwd_dq_m0.hip", "gfx950_common.h", "plan.h"],
+    "fwd": ["fwd_bf16_kernel.h", "fwd_bf16_m0.hip", "gfx950_common.h", "plan.h", "../../include/cp_attn.h"],
+    "pre": ["bwd_bf16_kernels.h", "bwd_bf16.hip", "gfx950_common.h", "plan.h", "../../include/cp_attn.h"],
+    "dkdv": ["bwd_bf16_kernels.h", "bwd_dkdv_m0.hip", "gfx950_common.h", "plan.h", "../../include/cp_attn.h"],
+    "dq": ["bwd_bf16_kernels.h", "bwd_dq_m0.hip", "gfx950_common.h", "plan.h", "../../include/cp_attn.h"],
 }
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128, 2, 0>", "pre": "bwd_pre_kernel<128>",
                 "dkdv": "bwd_dkdv_kernel<128, 0>", "dq": "bwd_dq_kernel<128, 2, 0>"}
