@@ -1266,25 +1266,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   }
 }
 
-// Zero dK/dV rows outside the key tiles [kt0, kt1) the key-stationary kernel
-// runs on (keys no local query can see): 16-byte stores of both, grid-stride
-// over the rows of one (batch, KV head) per blockIdx.y.
-template <int D>
-__global__ void __launch_bounds__(256) bwd_zero_keys_kernel(const BwdParams p) {
-  constexpr int VPR = D / 4;                        // float4 per row
-  const int64_t front = (int64_t)p.kt0 * BK;        // rows [0, front) and [back, skv)
-  const int64_t back = min((int64_t)p.kt1 * BK, (int64_t)p.skv);
-  const int64_t n = (front + (p.skv - back)) * VPR;
-  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / VPR;
-    const int64_t row = r < front ? r : back + (r - front);
-    const int64_t off = ((int64_t)blockIdx.y * p.skv + row) * D + (i % VPR) * 4;
-    *reinterpret_cast<f32x4 *>(p.dk + off) = z;
-    *reinterpret_cast<f32x4 *>(p.dv + off) = z;
-  }
-}
-
 // Launches of one mode's instantiations.
 template <int D, int KMODE>
 void launch_dkdv_mode(const BwdParams &p, hipStream_t s) {

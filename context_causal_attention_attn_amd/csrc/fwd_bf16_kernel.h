@@ -10,9 +10,11 @@
 // How (one workgroup = 8 wavefronts = one work item, two wavefronts per SIMD):
 //  * a work item is a tile of query rows of one chunk for a pack of query
 //    heads that read the same KV head (GQA); K/V tiles of 64 keys pass
-//    through LDS rings (2 stages for K, 3 for V) once per workgroup, loaded
-//    straight from global memory into LDS (global_load_lds_dwordx4), and are
-//    read by every head;
+//    through 4-stage LDS rings once per workgroup, loaded straight from
+//    global memory into LDS (global_load_lds_dwordx4), and are read by every
+//    head; the workgroup synchronises once per two tiles (K is loaded three
+//    tiles ahead, V one, so that no stage is refilled or read across a step
+//    without a barrier between);
 //  * each wavefront owns 32 query rows of one head (two 16-row blocks) and
 //    computes transposed score tiles S^T = K Q^T (keys x queries) with
 //    v_mfma_f32_16x16x32_bf16, so that a lane holds one query column: the
@@ -53,9 +55,11 @@ constexpr int BN = kFwdBlockKV;          // keys per tile (64)
 constexpr int NW = kFwdWaves;            // wavefronts per workgroup (8)
 constexpr int NT = NW * 64;
 constexpr int QB = kFwdWaveRows / 16;    // 16-row query blocks per wavefront
-constexpr int KSTAGES = 2;               // K ring: tile t in stage t % 2
-constexpr int VSTAGES = 3;               // V ring: tile t in stage t % 3
-constexpr int UNROLL = 6;                // steps per loop trip (both ring indices fixed)
+constexpr int KSTAGES = 4;               // K ring: tile t in stage t % 4
+constexpr int VSTAGES = 4;               // V ring: tile t in stage t % 4
+constexpr int K_AHEAD = 3;               // step j loads K of tile j+3 ...
+constexpr int V_AHEAD = 1;               // ... and V of tile j+1
+constexpr int UNROLL = 4;                // steps per loop trip (both ring indices fixed)
 constexpr float kSumLimit = 65536.0f;    // largest tile sum kept without a new max
 
 
@@ -78,10 +82,18 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   static_assert(BN == 64 && QB == 2, "tile shape");
   using T = Tile16<D>;   // K tiles (row reads) and V tiles (transpose reads)
 
-  // K ring (2 stages) followed by the V ring (3 stages), in one LDS array:
-  // 80 KiB at D = 128.
+  // K ring followed by the V ring, in one LDS array: 128 KiB at D = 128.
+  // Barriers close the odd steps only. Step j reads K of tile j+1 and V of
+  // tile j-1; K of tile t is loaded in step t-3 into the stage that K of
+  // tile t-4 left in step t-5, and V of tile t in step t-1 into the stage
+  // that V of tile t-4 left in step t-3: of any two consecutive steps one
+  // ends in a barrier, so every load is published before its tile is read
+  // and starts after the previous occupant's last reader passed a barrier.
   __shared__ __attribute__((aligned(16))) __bf16 smem[(KSTAGES + VSTAGES) * TILE];
-  static_assert((KSTAGES + VSTAGES) * TILE * 2 <= 80 * 1024, "LDS budget");
+  static_assert((KSTAGES + VSTAGES) * TILE * 2 <= 128 * 1024, "LDS budget");
+  static_assert(KSTAGES >= K_AHEAD + 1 && VSTAGES >= V_AHEAD + 3 && K_AHEAD >= 3 && V_AHEAD >= 1 &&
+                    UNROLL % KSTAGES == 0 && UNROLL % VSTAGES == 0 && UNROLL % 2 == 0,
+                "ring depths for one barrier per two steps");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;   // LDS byte address of smem
 
   const int tid = threadIdx.x;
@@ -379,13 +391,15 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     for (int ps = 0; ps < PSTEPS; ++ps)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pbuf[1][qb][ps][e] = (__bf16)0.0f;
-  // Tiles j, j+1, j+2 of the pipeline (step j masks tile j, prefetches V of
-  // j+1 and K of j+2).
-  TileRef t_cur{t0, kv_pos0, 0}, t_nx1{t0 + 1, kv_pos0, 0}, t_nx2{t0 + 2, kv_pos0, 0};
+  // Tiles j .. j+3 of the pipeline (step j masks tile j, loads V of j+1 and
+  // K of j+3).
+  TileRef t_cur{t0, kv_pos0, 0}, t_nx1{t0 + 1, kv_pos0, 0}, t_nx2{t0 + 2, kv_pos0, 0},
+      t_nx3{t0 + 3, kv_pos0, 0};
   if constexpr (MKV) {
     if (ntiles > 0) t_cur = next_tile();
     if (ntiles > 1) t_nx1 = next_tile();
     if (ntiles > 2) t_nx2 = next_tile();
+    if (ntiles > 3) t_nx3 = next_tile();
   }
   // Storage offset of a natural-order tile (merged chunks; 0 for one chunk).
   auto nat_adj = [&](int kt) { return ((int64_t)kt * BN >> p.kv.store_lg) * p.kv.cadj; };
@@ -394,28 +408,33 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     dma_v(t_cur.kt, MKV ? t_cur.adj : nat_adj(t_cur.kt), 0);
   }
   if (ntiles > 1) dma_k(t_nx1.kt, MKV ? t_nx1.adj : nat_adj(t_nx1.kt), 1);
+  if (ntiles > 2) dma_k(t_nx2.kt, MKV ? t_nx2.adj : nat_adj(t_nx2.kt), 2);
   wait_vmem_all();
   __syncthreads();
   if (ntiles > 0) qk0(sbuf[0]);
-  __syncthreads();   // K stage 0 is refilled in step 0
+  // The S^T product above reads K stage 0 as an odd "step -1" would: K of
+  // tile 4 refills that stage in step 1.
+  __syncthreads();
 
-  // One step on tile j (J6 = j % 6): PV(j-1) and S^T(j+1) on the matrix
-  // core, softmax of S^T(j) on the VALU, and K of tile j+2 and V of tile j+1
+  // One step on tile j (J4 = j % 4): PV(j-1) and S^T(j+1) on the matrix
+  // core, softmax of S^T(j) on the VALU, and K of tile j+3 and V of tile j+1
   // on their way into the rings. Slots are separated by scheduling fences so
   // that the interleave is the one written here.
-  auto step = [&](auto j6_tag, int j) {
-    constexpr int J6 = decltype(j6_tag)::value;
-    constexpr int SET = J6 & 1;
+  auto step = [&](auto j4_tag, int j) {
+    constexpr int J4 = decltype(j4_tag)::value;
+    constexpr int SET = J4 & 1;
     f32x4 (&sacc)[QB][KB] = sbuf[SET];
     f32x4 (&snext)[QB][KB] = sbuf[1 - SET];
     const bf16x8 (&pprev)[QB][PSTEPS] = pbuf[1 - SET];
     bf16x8 (&pcur)[QB][PSTEPS] = pbuf[SET];
-    using KS = IC<(J6 + 1) % KSTAGES>;   // K of tile j+1
-    using VS = IC<(J6 + 2) % VSTAGES>;   // V of tile j-1
-    // K of tile j+2 replaces K of tile j (read in step j-1); V of tile j+1
-    // replaces V of tile j-2 (read in step j-1).
-    if (j + 2 < ntiles) dma_k(MKV ? t_nx2.kt : t0 + j + 2, MKV ? t_nx2.adj : nat_adj(t0 + j + 2), J6 % KSTAGES);
-    if (j + 1 < ntiles) dma_v(MKV ? t_nx1.kt : t0 + j + 1, MKV ? t_nx1.adj : nat_adj(t0 + j + 1), (J6 + 1) % VSTAGES);
+    using KS = IC<(J4 + 1) % KSTAGES>;             // K of tile j+1
+    using VS = IC<(J4 + VSTAGES - 1) % VSTAGES>;   // V of tile j-1
+    // K of tile j+3 replaces K of tile j-1 (read in step j-2); V of tile j+1
+    // replaces V of tile j-3 (read in step j-2).
+    if (j + K_AHEAD < ntiles)
+      dma_k(MKV ? t_nx3.kt : t0 + j + K_AHEAD, MKV ? t_nx3.adj : nat_adj(t0 + j + K_AHEAD), (J4 + K_AHEAD) % KSTAGES);
+    if (j + V_AHEAD < ntiles)
+      dma_v(MKV ? t_nx1.kt : t0 + j + V_AHEAD, MKV ? t_nx1.adj : nat_adj(t0 + j + V_AHEAD), (J4 + V_AHEAD) % VSTAGES);
     // Keep the operand bases opaque per step: otherwise the compiler hoists a
     // base-plus-stage address per stage out of the loop (several times the
     // registers) instead of folding the stage into the read's immediate.
@@ -430,7 +449,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       tile_plo = t_cur.base + (int64_t)kt * BN;
       t_cur = t_nx1;
       t_nx1 = t_nx2;
-      if (j + 3 < ntiles) t_nx2 = next_tile();
+      t_nx2 = t_nx3;
+      if (j + 4 < ntiles) t_nx3 = next_tile();
     }
 
     // Mask (diagonal or ragged tiles only): key 16*kb + 4*grp + i of the tile
@@ -613,8 +633,10 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_part[qb] += tsum[qb];
-    wait_vmem_all();   // this wave's rows of the tiles loaded above are in LDS
-    __syncthreads();
+    if constexpr (J4 & 1) {
+      wait_vmem_all();   // this wave's rows of every tile loaded so far are in LDS
+      __syncthreads();
+    }
   };
 
   for (int j = 0; j < ntiles; j += UNROLL) {
@@ -622,10 +644,10 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if (j + 1 < ntiles) step(IC<1>{}, j + 1);
     if (j + 2 < ntiles) step(IC<2>{}, j + 2);
     if (j + 3 < ntiles) step(IC<3>{}, j + 3);
-    if (j + 4 < ntiles) step(IC<4>{}, j + 4);
-    if (j + 5 < ntiles) step(IC<5>{}, j + 5);
   }
-  // The last tile's PV product.
+  // The last tile's PV product. Its V tile was loaded in the step before the
+  // last one (or before step 0), and whichever of those two steps is odd
+  // published it.
   if (ntiles > 0) {
     const int last = ntiles - 1;
     if (last & 1) pv(last % VSTAGES, pbuf[1]);
