@@ -307,8 +307,11 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *desc, const void *q, const void *k
 /*
  * cp_attn_bwd without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops and
- * harnesses that forbid allocation. Same arguments, results (bitwise) and
- * errors as cp_attn_bwd; the backward's per-row statistics (-Delta and
+ * harnesses that forbid allocation. Same arguments and errors as
+ * cp_attn_bwd, and the same results: dq bitwise; dk and dv up to the order
+ * of float32 additions (cp_attn_bwd may split a key tile's queries over
+ * several workgroups and add their partial sums; this entry point never
+ * splits). The backward's per-row statistics (-Delta and
  * LSE * log2(e)) live in a fixed scratch array inside the library instead
  * (2 x CP_ATTN_NOALLOC_MAX_ROWS float32, 16 MiB, held by every GPU the
  * library runs on until the process ends). Calls no allocating routine; the
