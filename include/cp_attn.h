@@ -195,10 +195,13 @@ typedef struct cp_attn_desc {
                                /* follow on (chunk length x row stride). Multiples of 16 bytes, >= 0. */
 } cp_attn_desc;
 
-/* ABI version of the loaded library (CP_ATTN_ABI_VERSION of its build). */
+/* ABI version of the loaded library (CP_ATTN_ABI_VERSION of its build). A
+ * descriptor whose abi_version differs is rejected (CP_ATTN_ERR_ABI), in line
+ * with the fail-fast rule of [CP-migration] §13.2. */
 int32_t cp_attn_abi_version(void);
 
-/* Human-readable text of a status code; never NULL, static storage. */
+/* Human-readable text of a status code ([CP-migration] §13.2: every rejected
+ * configuration is reported with its reason); never NULL, static storage. */
 const char *cp_attn_error_string(int32_t status);
 
 /*
@@ -228,19 +231,28 @@ int32_t cp_attn_share_positions(int32_t layout, int64_t s_global, int32_t cp_siz
 int32_t cp_attn_validate(const cp_attn_desc *desc);
 
 /* Number of visible (query, key) pairs per (batch, query head) of the share:
- * the causal work that FLOP counts are based on, under the causal flag, the
- * KV chunk table and the packed sequences. Host only. */
+ * the causal work that FLOP counts are based on, under the global-position
+ * causal mask ([CP-migration] §8), the KV chunk table and the packed
+ * sequences ([FLA-CP] §3.3). Equal for every rank of a Head-Tail split
+ * ([Trainer-CP] §0, Head-Tail: each rank gets the same causal work). Errors:
+ * cp_attn_validate's, NULL_PTR for `pairs`. Host only. */
 int32_t cp_attn_share_pairs(const cp_attn_desc *desc, int64_t *pairs);
 
-/* Bytes of device workspace cp_attn_fwd (backward == 0) or cp_attn_bwd
- * (backward != 0) needs for this descriptor; may be 0. Host only. */
+/* Bytes of device workspace cp_attn_fwd (backward == 0: none) or cp_attn_bwd
+ * (backward != 0) needs for this descriptor; may be 0. The backward's holds
+ * the per-row statistics of the recompute-based gradient of [CP-migration]
+ * §6.1 (-Delta and LSE*log2(e)) and, for shares whose key tiles are split over
+ * several workgroups, their float32 partial dK/dV. Errors: cp_attn_validate's,
+ * NULL_PTR for `bytes`. Host only. */
 int32_t cp_attn_workspace_bytes(const cp_attn_desc *desc, int32_t backward, size_t *bytes);
 
 /* Work-list statistics of the forward tile scheduler (host only), for tests
  * and reports: number of work items (one workgroup each), the KV tiles they
  * visit in total (per KV chunk, the prefix the item's last row can see; with
  * packed sequences, from the first row's sequence start on), and the tile
- * shape. */
+ * shape. The scheduler maps both Head-Tail chunks ([Trainer-CP] §4.4) and
+ * their causal KV ranges ([CP-migration] §8) onto one launch. Errors:
+ * cp_attn_validate's, NULL_PTR for `stats`. */
 typedef struct cp_attn_plan_stats {
   int64_t work_items;
   int64_t kv_tile_visits;      /* summed over work items */
@@ -277,9 +289,14 @@ int32_t cp_attn_fwd(const cp_attn_desc *desc, const void *q, const void *k, cons
  *   PARTIAL gradients over the gathered K/V, to be summed across ranks by a
  *   reduce-scatter ([CP-migration] §6.1 backward). Key rows no query of the
  *   share can see are written as zeros.
- * out and lse are the forward's outputs for the same inputs. The workspace
- * (cp_attn_workspace_bytes with backward != 0) is caller-owned device memory;
- * its contents on entry do not matter.
+ * out and lse are the forward's outputs for the same inputs. q, k, v, out,
+ * lse, dout: device, caller-owned, read only; dq, dk, dv: device, written.
+ * The workspace (cp_attn_workspace_bytes with backward != 0) is caller-owned
+ * device memory; its contents on entry do not matter. Returns CP_ATTN_OK once
+ * the kernels are enqueued on `stream`; validation errors (as cp_attn_fwd)
+ * and CP_ATTN_ERR_WORKSPACE (workspace NULL or too small) return before
+ * anything is enqueued or written; CP_ATTN_ERR_HIP if a launch fails.
+ * Deterministic: split key tiles add their partial sums in a fixed order.
  */
 int32_t cp_attn_bwd(const cp_attn_desc *desc, const void *q, const void *k, const void *v,
                     const void *out, const float *lse, const void *dout,
@@ -287,8 +304,8 @@ int32_t cp_attn_bwd(const cp_attn_desc *desc, const void *q, const void *k, cons
                     void *stream);
 
 /*
- * cp_attn_bwd with its phases bracketed by caller-owned HIP events, for
- * per-kernel timing on the caller's stream. `events` holds n_events
+ * cp_attn_bwd ([CP-migration] §6.1 backward) with its phases bracketed by
+ * caller-owned HIP events, for per-kernel timing on the caller's stream. `events` holds n_events
  * hipEvent_t handles (n_events must be 4, or events NULL and n_events 0,
  * which makes this call identical to cp_attn_bwd). They are recorded on
  * `stream` before phase 1 and after phases 1, 2 and 3:
