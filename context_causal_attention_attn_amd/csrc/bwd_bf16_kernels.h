@@ -236,9 +236,21 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   // split over kv_parts workgroups).
   const int s_begin = (int)((int64_t)all_steps * part / p.kv_parts);
   const int total = (int)((int64_t)all_steps * (part + 1) / p.kv_parts) - s_begin;
+  // A cursor also carries the element offsets of its step's first row from
+  // the group's first head: `off` in the tensor it loads (Q or dO), `soff` in
+  // the per-row statistics. Steps move them by additions; only a new chunk
+  // recomputes them.
   struct Cursor {
     int c, t, h;       // chunk, query tile in the chunk, head in the group
     int64_t cpos;      // global position of the chunk's first row
+    int64_t off, soff;
+  };
+  struct Walk {
+    int64_t sh, ss, cadj;   // head, row and chunk strides (elements)
+  };
+  const Walk wq{p.q_sh, p.q_ss, p.q_cadj}, wo{p.o_sh, p.o_ss, p.o_cadj}, wst{p.sq, 1, 0};
+  auto offset = [&](const Walk &w, int c, int t, int h) {
+    return (int64_t)h * w.sh + ((int64_t)c * p.chunk_len + (int64_t)t * QT) * w.ss + (int64_t)c * w.cadj;
   };
   auto next_chunk = [&](Cursor &u) {
     int t0 = 0, t1 = 0;
@@ -251,14 +263,26 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       u.cpos = p.chunk_pos[u.c];
     }
   };
-  auto advance = [&](Cursor &u) {
+  // One step on: the next head of the group, then the next query tile, then
+  // the next chunk with tiles to visit. `w` walks `off`; `stats`: also soff.
+  auto advance = [&](Cursor &u, const Walk &w, bool stats) {
     if (++u.h == p.group) {
       u.h = 0;
-      if (++u.t >= end_tile(u.c)) next_chunk(u);
+      if (++u.t >= end_tile(u.c)) {
+        next_chunk(u);
+        u.off = offset(w, u.c, u.t, 0);
+        if (stats) u.soff = offset(wst, u.c, u.t, 0);
+      } else {
+        u.off += (int64_t)QT * w.ss - (int64_t)(p.group - 1) * w.sh;
+        if (stats) u.soff += QT - (int64_t)(p.group - 1) * p.sq;
+      }
+    } else {
+      u.off += w.sh;
+      if (stats) u.soff += p.sq;
     }
   };
   // The cursor at step s_begin: skip whole chunks, then tiles of G steps.
-  Cursor c0{0, first_tile(0), 0, p.chunk_pos[0]};
+  Cursor c0{0, first_tile(0), 0, p.chunk_pos[0], 0, 0};
   {
     int rem = s_begin, c = 0;
     for (; c < p.n_q_chunks; ++c) {
@@ -266,7 +290,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       if (rem < n) break;
       rem -= n;
     }
-    if (c < p.n_q_chunks) c0 = Cursor{c, first_tile(c) + rem / p.group, rem % p.group, p.chunk_pos[c]};
+    if (c < p.n_q_chunks) c0 = Cursor{c, first_tile(c) + rem / p.group, rem % p.group, p.chunk_pos[c], 0, 0};
     else if (c0.t >= end_tile(0)) next_chunk(c0);   // no step left (total == 0)
   }
 
@@ -301,12 +325,9 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   // Rows of step u's tile of Q (is_q) or dO into LDS at byte offset dst;
   // rows past the chunk end read its last row.
   auto dma_tile = [&](const Cursor &u, bool is_q, uint32_t dst) {
-    const int row0 = u.t * QT;
-    const int rows_left = p.chunk_len - 1 - row0;
-    const int64_t lrow0 = (int64_t)u.c * p.chunk_len + row0;
+    const int rows_left = p.chunk_len - 1 - u.t * QT;
     const int64_t ss = is_q ? p.q_ss : p.o_ss;
-    const __bf16 *tbase = (is_q ? qhead + u.h * p.q_sh : ohead + u.h * p.o_sh) + lrow0 * ss +
-                          u.c * (is_q ? p.q_cadj : p.o_cadj);
+    const __bf16 *tbase = (is_q ? qhead : ohead) + u.off;
     if (rows_left >= QT - 1) {
 #pragma unroll
       for (int i = 0; i < INSTS; ++i)
@@ -321,27 +342,27 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
     }
   };
   // LSE*log2(e) (wave 0) and Delta (wave 1) of step u's rows.
+  const float *stat0 = (wave == 0 ? p.lse2 : p.delta) + ((int64_t)b * p.hq + (int64_t)hk * p.group) * p.sq;
   auto dma_stats = [&](const Cursor &u, int stage) {
     if (wave >= 2) return;
-    const int head = hk * p.group + u.h;
-    const int row0 = u.t * QT;
-    const int rows_left = p.chunk_len - 1 - row0;
-    const int64_t sbase = ((int64_t)b * p.hq + head) * p.sq + (int64_t)u.c * p.chunk_len + row0;
-    const float *src = (wave == 0 ? p.lse2 : p.delta) + sbase;
+    const int rows_left = p.chunk_len - 1 - u.t * QT;
     const uint32_t dst = lds0 + (wave == 0 ? L_OFF : DL_OFF) + stage * QT * 4;
-    dma4(dst, (uint32_t)(min(lane, rows_left) * 4), src);
+    dma4(dst, (uint32_t)(min(lane, rows_left) * 4), stat0 + u.soff);
   };
   Cursor cq = c0;   // step whose Q tile the next Q load fetches
+  cq.off = offset(wq, c0.c, c0.t, c0.h);
+  cq.soff = offset(wst, c0.c, c0.t, c0.h);
   Cursor co = c0;   // step whose dO tile the next dO load fetches
+  co.off = offset(wo, c0.c, c0.t, c0.h);
   auto load_q = [&](int s) {   // Q tile (and statistics) of step s = cq's
     const int st = s % QSTG;
     dma_tile(cq, true, Q_OFF + st * QTILE * 2);
     dma_stats(cq, st);
-    advance(cq);
+    advance(cq, wq, true);
   };
   auto load_o = [&](int s) {   // dO tile of step s = co's
     dma_tile(co, false, O_OFF + (s % OSTG) * QTILE * 2);
-    advance(co);
+    advance(co, wo, false);
   };
 
   // ---- per-lane LDS addressing ----------------------------------------------
@@ -584,7 +605,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           acc[db][kn] = mfma16(opnd[o % NBUF], pcur[kn][ps], acc[db][kn]);
           __builtin_amdgcn_sched_barrier(0);
         });
-        advance(cs);
+        advance(cs, wq, false);
       }
       finish();
     };

@@ -224,7 +224,7 @@ constexpr int kDkdvSlots = 256;
 // the chip's workgroup slots for 1, 2, 4 and 8 parts per tile (each part
 // also pays a fixed start-up and, beyond the first, an fp32 partial written
 // and reduced) and keeps the fastest.
-static int32_t dkdv_parts(const cp_attn_desc *d, const Share &s, const DocBounds &docs, int kt0, int kt1) {
+static int32_t dkdv_parts(const cp_attn_desc *d, const Share &s, int kt0, int kt1) {
   if (d->dtype != CP_ATTN_BF16 || kt1 <= kt0 || s.chunk_len == 0) return 1;
   const int64_t groups = (int64_t)d->batch * d->hkv;
   // Grids of many workgroups balance by themselves (and would make the
@@ -239,11 +239,11 @@ static int32_t dkdv_parts(const cp_attn_desc *d, const Share &s, const DocBounds
     const int64_t key0 = (int64_t)kt * kBwdBlockKV;
     const int64_t kc = key0 / Lkv;
     const int64_t kv_lo = d->kv_chunk_pos[kc] + (key0 - kc * Lkv);
-    // Packed sequences: rows from the end of the sequence of the tile's last
-    // key on see none of its keys (as the kernel bounds its query tiles).
-    int64_t de_tile = INT64_MAX;
-    for (int i = docs.n - 1; i >= 0; --i)
-      if (docs.pos[i] > kv_lo + kBwdBlockKV - 1) de_tile = docs.pos[i];
+    // Steps from the tile's causal first query tile to the end of each chunk.
+    // With packed sequences that overcounts the tiles whose sequence ends
+    // before the chunk does (the kernel stops there); counting exactly made
+    // the planner keep a packed share's tiles whole, which measured slower
+    // than the split this count picks.
     int64_t n = 0;
     for (int c = 0; c < s.n_q_chunks; ++c) {
       int64_t first = 0;
@@ -251,12 +251,7 @@ static int32_t dkdv_parts(const cp_attn_desc *d, const Share &s, const DocBounds
         const int64_t rel = kv_lo - s.chunk_pos[c];
         first = rel <= 0 ? 0 : std::min<int64_t>(nq, rel / kBwdBlockQ);
       }
-      int64_t end = nq;
-      if (de_tile != INT64_MAX) {
-        const int64_t rel = de_tile - s.chunk_pos[c];
-        end = std::max(first, rel <= 0 ? 0 : std::min<int64_t>(nq, (rel + kBwdBlockQ - 1) / kBwdBlockQ));
-      }
-      n += end - first;
+      n += nq - first;
     }
     steps.push_back((double)(n * G));
   }
@@ -351,7 +346,7 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool a
       p->kt1 = (int32_t)(hi / kBwdBlockKV + 1);
     }
   }
-  p->kv_parts = allow_split ? dkdv_parts(d, s, p->docs, p->kt0, p->kt1) : 1;
+  p->kv_parts = allow_split ? dkdv_parts(d, s, p->kt0, p->kt1) : 1;
   p->kv_partial = nullptr;
 }
 
