@@ -255,8 +255,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // Wavefront w's instruction i covers rows (i*NW + w)*RPI ...; the row
   // modulo 16 (which fixes the swizzle) does not depend on i. The loads are
   // issued from inline assembly so that the compiler does not make every LDS
-  // read wait for them; each step waits for its own loads (vmcnt(0)) right
-  // before the barrier that publishes the tile.
+  // read wait for them; before each barrier (after odd steps) a wavefront
+  // waits for all of its loads (vmcnt(0)), and the barrier publishes them.
   constexpr int RPI = 64 / NC;                       // rows per instruction
   constexpr int INSTS = BN / (NW * RPI);             // instructions per wave per tile
   static_assert(INSTS >= 1 && (NW * RPI) % 16 == 0, "staging shape");
