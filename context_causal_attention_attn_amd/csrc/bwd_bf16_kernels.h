@@ -473,7 +473,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       if (it < total) {
         f32x4 (&sacc)[RB][KN] = sbuf[PAR];
         f32x4 (&snext)[RB][KN] = sbuf[1 - PAR];
-        const uint32_t qnext = 2 * ((it + 1) % QSTG) * QTILE;   // Q stage of step it+1
+        uint32_t qnext = 2 * ((it + 1) % QSTG) * QTILE;         // Q stage of step it+1
+        asm volatile("" : "+s"(qnext));   // one scalar: each address below takes one add
         constexpr uint32_t ocur = 2 * PAR * QTILE;              // dO stage of step it
         const int st = it % QSTG;
         // LSE*log2(e) of this lane's rows: row block rb holds rows
@@ -638,7 +639,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
       bf16x8 opnd[NBUF];
       // Half A: dK^T += Q(it-2)^T dS(it-2).
       if (it >= 2) {
-        const uint32_t qold = 2 * ((it - 2) % QSTG) * QTILE;
+        uint32_t qold = 2 * ((it - 2) % QSTG) * QTILE;
+        asm volatile("" : "+s"(qold));    // one scalar: each address below takes one add
         // Bases of this step's Q^T reads (opaque: see the P role).
         uint32_t tb[DB];
 #pragma unroll
