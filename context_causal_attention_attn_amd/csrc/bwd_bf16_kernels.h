@@ -324,20 +324,26 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   const __bf16 *ohead = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + (int64_t)hk * p.group * p.o_sh;
   // Rows of step u's tile of Q (is_q) or dO into LDS at byte offset dst;
   // rows past the chunk end read its last row.
+  // LDS destination of this wavefront's first row of a tile at byte offset
+  // 0, kept in one scalar register (otherwise the compiler keeps one
+  // destination per instruction and stage, beyond the scalar registers).
+  uint32_t m0w = lds0 + 2 * kw * RPI * D;
+  asm volatile("" : "+s"(m0w));
   auto dma_tile = [&](const Cursor &u, bool is_q, uint32_t dst) {
     const int rows_left = p.chunk_len - 1 - u.t * QT;
     const int64_t ss = is_q ? p.q_ss : p.o_ss;
     const __bf16 *tbase = (is_q ? qhead : ohead) + u.off;
+    uint32_t m0 = m0w + dst;
+    asm volatile("" : "+s"(m0));
     if (rows_left >= QT - 1) {
 #pragma unroll
       for (int i = 0; i < INSTS; ++i)
-        dma16(lds0 + dst + 2 * (i * SW * RPI + kw * RPI) * D, (is_q ? goq : goo) + (uint32_t)(i * SW * RPI * ss * 2),
-              tbase);
+        dma16(m0 + 2 * i * SW * RPI * D, (is_q ? goq : goo) + (uint32_t)(i * SW * RPI * ss * 2), tbase);
     } else {
 #pragma unroll
       for (int i = 0; i < INSTS; ++i) {
         const int r = min(srow + i * SW * RPI, rows_left);
-        dma16(lds0 + dst + 2 * (i * SW * RPI + kw * RPI) * D, (uint32_t)((r * ss + scol) * 2), tbase);
+        dma16(m0 + 2 * i * SW * RPI * D, (uint32_t)((r * ss + scol) * 2), tbase);
       }
     }
   };
@@ -395,9 +401,17 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   // lane l of key group kw at stage s, 16 bytes per lane. Lane l takes slot
   // l ^ 4*(l/32): each 16-lane pass of a 16-byte access (lanes sharing bits
   // 2 and 4) then covers all 64 banks.
-  const uint32_t xaddr = lds0 + X_OFF + (kw * NXOP * 64 + (lane ^ ((lane >> 5) << 2))) * 16;
+  // The exchange and the statistics lie beyond the reach of an instruction
+  // offset (16 bits) from LDS 0: their bases are made opaque registers that
+  // hold the region start, so the per-read displacements fold into offsets.
+  uint32_t xaddr = lds0 + X_OFF + (kw * NXOP * 64 + (lane ^ ((lane >> 5) << 2))) * 16;
+  asm volatile("" : "+v"(xaddr));
   constexpr uint32_t XSTAGE = 4 * 64 * XPER * 2;
   constexpr uint32_t XOP = 64 * 16;   // bytes between a lane's operands
+  // This lane's rows 4grp .. 4grp+3 of the statistics of stage 0 (LSE*log2(e)
+  // at lstat, -Delta at dstat).
+  uint32_t lstat = lds0 + L_OFF + 16 * grp, dstat = lds0 + DL_OFF + 16 * grp;
+  asm volatile("" : "+v"(lstat), "+v"(dstat));
 
   // This lane's key rows of K (P role) or V (dS role): the B operands.
   bf16x8 kvf[KN][KSTEPS];
@@ -479,7 +493,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         const int st = it % QSTG;
         // LSE*log2(e) of this lane's rows: row block rb holds rows
         // 16rb + 4grp .. +3, read one block ahead.
-        const uint32_t lbase = lds0 + L_OFF + 4 * (st * QT + 4 * grp);
+        const uint32_t lbase = lstat + 4 * st * QT;
         f32x4 lg[2];
         lg[0] = lds_f4(lbase);
         // Mask: row r of the tile sees this lane's key of block kn iff
@@ -678,7 +692,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         // the starting value of dP(it), which so comes out as dP - Delta.
         f32x4 nd[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) nd[rb] = lds_f4(lds0 + DL_OFF + 4 * (st * QT + 16 * rb + 4 * grp));
+        for (int rb = 0; rb < RB; ++rb) nd[rb] = lds_f4(dstat + 4 * st * QT + 4 * 16 * rb);
         auto read_b = [&](auto o_tag) -> bf16x8 {
           constexpr int o = decltype(o_tag)::value, rb = o % RB, s = o / RB;
           return lds_b128(raddr[s] + ocur + 2 * 16 * rb * D);
