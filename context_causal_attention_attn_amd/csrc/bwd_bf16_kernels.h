@@ -1257,8 +1257,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   auto tile_step = [&](auto j4_tag, int J) {
     constexpr int J4 = decltype(j4_tag)::value;
     if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : t0 + J + 2, MKV ? t_nx2.adj : nat_adj(t0 + J + 2), (J4 + 2) % STG);
+    // Opaque bases: the V ring's start (64 KiB) and the stage offsets then
+    // stay instruction offsets instead of per-read address arithmetic.
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(taddr[db]));
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]), "+v"(vaddr[s]));
     TileRef t{t0 + J, kv_pos0, 0};
     if constexpr (MKV) {
       t = t_cur;
