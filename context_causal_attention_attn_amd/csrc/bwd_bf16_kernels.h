@@ -322,13 +322,13 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   const uint32_t goo = (uint32_t)(((int64_t)srow * p.o_ss + scol) * 2);
   const __bf16 *qhead = static_cast<const __bf16 *>(p.q) + b * p.q_sb + (int64_t)hk * p.group * p.q_sh;
   const __bf16 *ohead = static_cast<const __bf16 *>(p.dout) + b * p.o_sb + (int64_t)hk * p.group * p.o_sh;
-  // Rows of step u's tile of Q (is_q) or dO into LDS at byte offset dst;
-  // rows past the chunk end read its last row.
   // LDS destination of this wavefront's first row of a tile at byte offset
   // 0, kept in one scalar register (otherwise the compiler keeps one
   // destination per instruction and stage, beyond the scalar registers).
   uint32_t m0w = lds0 + 2 * kw * RPI * D;
   asm volatile("" : "+s"(m0w));
+  // Rows of step u's tile of Q (is_q) or dO into LDS at byte offset dst;
+  // rows past the chunk end read its last row.
   auto dma_tile = [&](const Cursor &u, bool is_q, uint32_t dst) {
     const int rows_left = p.chunk_len - 1 - u.t * QT;
     const int64_t ss = is_q ? p.q_ss : p.o_ss;
