@@ -441,6 +441,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   constexpr int NSA = KN * NOA;         // S or dP products per step
   constexpr int NSB = KN * NOB;         // dV or dK products per step
   constexpr int NPAIR = RB * KN * 2;    // pairs of P (or dS) values per lane per step
+  constexpr int SPP = NSA / NPAIR;      // slots per pair
+  static_assert(NSA == SPP * NPAIR, "whole slots per pair");
 
   // Prologue: Q of steps 0 and 1 (when there is a step 1), dO of step 0.
   // Every load is of a step that exists: the cursors never run past the last.
@@ -572,6 +574,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           return lds_b128(rbq[s] + 2 * 16 * rb * D);
         };
         static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_a(o); });
+        float xp[NPAIR][2];   // a pair's probabilities between its two slots
         static_for<NSA>([&](auto t_tag) {
           constexpr int t = decltype(t_tag)::value, o = t / KN, kn = t % KN, rb = o % RB, s = o / RB;
           if constexpr (kn == 0 && o + AHEAD < NOA) opnd[(o + AHEAD) % NBUF] = read_a(IC<o + AHEAD>{});
@@ -583,18 +586,26 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           } else {
             snext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], snext[rb][kn]);
           }
+          // The slot's vector work is issued after its matrix instruction.
+          __builtin_amdgcn_sched_barrier(0);
           // Pair u (row block u / 4, key block (u / 2) % 2, elements 2(u%2),
-          // 2(u%2)+1) in slot u*NSA/NPAIR; it lands in elements 4(rb%2) + i
-          // of the key block's P operand of k-step rb/2 (the row order of the
-          // dO^T reads).
+          // 2(u%2)+1): exponentials in slot SPP*u, bf16 conversion two slots
+          // later (at D = 128 the next slot with an operand read; the last
+          // pair's in the last slot); it lands in elements 4(rb%2) + i of the
+          // key block's P operand of k-step rb/2 (the row order of the dO^T
+          // reads).
           static_for<NPAIR>([&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
-            if constexpr (u * NSA / NPAIR == t) {
-              constexpr int rq = u / 4, kq = (u / 2) % 2, i = 2 * (u % 2);
+            constexpr int rq = u / 4, kq = (u / 2) % 2, i = 2 * (u % 2);
+            if constexpr (SPP * u == t) {
               if constexpr (u % 4 == 0 && rq + 1 < RB) lg[(rq + 1) % 2] = lds_f4(lbase + 4 * 16 * (rq + 1));
-              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kq][i], c2, -lg[rq % 2][i]));
-              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rq][kq][i + 1], c2, -lg[rq % 2][i + 1]));
-              const bf16x2 t2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+              xp[u][0] = fmaf(sacc[rq][kq][i], c2, -lg[rq % 2][i]);
+              xp[u][1] = fmaf(sacc[rq][kq][i + 1], c2, -lg[rq % 2][i + 1]);
+              xp[u][0] = __builtin_amdgcn_exp2f(xp[u][0]);
+              xp[u][1] = __builtin_amdgcn_exp2f(xp[u][1]);
+            }
+            if constexpr ((SPP * u + 2 < NSA ? SPP * u + 2 : NSA - 1) == t) {
+              const bf16x2 t2 = __builtin_convertvector((f32x2){xp[u][0], xp[u][1]}, bf16x2);
               pcur[kq][rq >> 1][4 * (rq & 1) + i] = t2[0];
               pcur[kq][rq >> 1][4 * (rq & 1) + i + 1] = t2[1];
             }
@@ -698,6 +709,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           return lds_b128(raddr[s] + ocur + 2 * 16 * rb * D);
         };
         static_for<AHEAD>([&](auto o) { opnd[decltype(o)::value] = read_b(o); });
+        float xd[NPAIR][2];   // a pair's dS values between its two slots
         static_for<NSA>([&](auto t_tag) {
           constexpr int t = decltype(t_tag)::value, o = t / KN, kn = t % KN, rb = o % RB, s = o / RB;
           if constexpr (kn == 0 && o + AHEAD < NOA) opnd[(o + AHEAD) % NBUF] = read_b(IC<o + AHEAD>{});
@@ -706,14 +718,19 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
           } else {
             pnext[rb][kn] = mfma16(opnd[o % NBUF], kvf[kn][s], pnext[rb][kn]);
           }
+          __builtin_amdgcn_sched_barrier(0);
+          // Pair u as in the P role: products in slot SPP*u, conversion two
+          // slots later.
           static_for<NPAIR>([&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
-            if constexpr (u * NSA / NPAIR == t) {
-              constexpr int rq = u / 4, kq = (u / 2) % 2, i = 2 * (u % 2), ps = rq >> 1, e = 4 * (rq & 1) + i;
+            constexpr int rq = u / 4, kq = (u / 2) % 2, i = 2 * (u % 2), ps = rq >> 1, e = 4 * (rq & 1) + i;
+            if constexpr (SPP * u == t) {
               const float p0 = (float)pk[kq][ps][e], p1 = (float)pk[kq][ps][e + 1];
-              const float x0 = p0 * pprev[rq][kq][i];
-              const float x1 = p1 * pprev[rq][kq][i + 1];
-              const bf16x2 t2 = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+              xd[u][0] = p0 * pprev[rq][kq][i];
+              xd[u][1] = p1 * pprev[rq][kq][i + 1];
+            }
+            if constexpr ((SPP * u + 2 < NSA ? SPP * u + 2 : NSA - 1) == t) {
+              const bf16x2 t2 = __builtin_convertvector((f32x2){xd[u][0], xd[u][1]}, bf16x2);
               dsf[kq][ps][e] = t2[0];
               dsf[kq][ps][e + 1] = t2[1];
             }
@@ -1228,6 +1245,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
           dst = mfma16(opnd[o % NBUF], bop, dst);
         }
       }
+      // The slot's vector work is issued after its matrix instruction.
+      __builtin_amdgcn_sched_barrier(0);
       // dS^T pair e (row block e / 4, half (e / 2) % 2, elements 2(e%2),
       // 2(e%2)+1) in slot e * NSLOT / NPAIR; it lands in elements 4h + i of
       // the row block's B operand (the key order of the K^T reads).
