@@ -194,6 +194,19 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if (item_ds > kv_pos0) t0 = (int)min<int64_t>(ntiles, (item_ds - kv_pos0) / BN);
     ntiles -= t0;
   }
+  // Natural order: the first tile that needs a mask (crossing the causal
+  // diagonal of the wave's first row, or the ragged end of K/V); every later
+  // tile needs one too.
+  int mask_from = INT32_MAX;
+  if constexpr (!MKV) {
+    const int64_t rag = (int64_t)p.skv - BN;                 // kt*BN > rag: ragged
+    int64_t mf = rag < 0 ? 0 : rag / BN + 1;
+    if (p.causal) {
+      const int64_t lim = wave_qlo - kv_pos0 - BN + 1;       // kt*BN > lim: crosses the diagonal
+      mf = min(mf, lim < 0 ? (int64_t)0 : lim / BN + 1);
+    }
+    mask_from = (int)min(mf, (int64_t)INT32_MAX);
+  }
   struct TileRef {
     int kt;          // storage tile
     int64_t base;    // global position of storage row 0 (this tile's chunk)
@@ -430,11 +443,18 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     using KS = IC<(J4 + 1) % KSTAGES>;             // K of tile j+1
     using VS = IC<(J4 + VSTAGES - 1) % VSTAGES>;   // V of tile j-1
     // K of tile j+3 replaces K of tile j-1 (read in step j-2); V of tile j+1
-    // replaces V of tile j-3 (read in step j-2).
-    if (j + K_AHEAD < ntiles)
-      dma_k(MKV ? t_nx3.kt : t0 + j + K_AHEAD, MKV ? t_nx3.adj : nat_adj(t0 + j + K_AHEAD), (J4 + K_AHEAD) % KSTAGES);
-    if (j + V_AHEAD < ntiles)
-      dma_v(MKV ? t_nx1.kt : t0 + j + V_AHEAD, MKV ? t_nx1.adj : nat_adj(t0 + j + V_AHEAD), (J4 + V_AHEAD) % VSTAGES);
+    // replaces V of tile j-3 (read in step j-2). In natural order the last
+    // steps load the item's last tile again instead of branching around the
+    // loads (those stages are never read; the epilogue waits for them).
+    if constexpr (!MKV) {
+      const int ktk = min(t0 + j + K_AHEAD, t0 + ntiles - 1);
+      const int ktv = min(t0 + j + V_AHEAD, t0 + ntiles - 1);
+      dma_k(ktk, nat_adj(ktk), (J4 + K_AHEAD) % KSTAGES);
+      dma_v(ktv, nat_adj(ktv), (J4 + V_AHEAD) % VSTAGES);
+    } else {
+      if (j + K_AHEAD < ntiles) dma_k(t_nx3.kt, t_nx3.adj, (J4 + K_AHEAD) % KSTAGES);
+      if (j + V_AHEAD < ntiles) dma_v(t_nx1.kt, t_nx1.adj, (J4 + V_AHEAD) % VSTAGES);
+    }
     // Keep the operand bases opaque per step: otherwise the compiler hoists a
     // base-plus-stage address per stage out of the loop (several times the
     // registers) instead of folding the stage into the read's immediate.
@@ -455,7 +475,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 
     // Mask (diagonal or ragged tiles only): key 16*kb + 4*grp + i of the tile
     // is visible to a row iff it is <= that row's limit.
-    bool need_mask = (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo);
+    bool need_mask = MKV ? (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo) : kt >= mask_from;
     if constexpr (DOCS) need_mask = need_mask || tile_plo < wave_ds;
     if constexpr (UMASK) need_mask = true;
     if (need_mask) {
@@ -672,6 +692,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if (last & 1) pv(last % VSTAGES, pbuf[1]);
     else pv(last % VSTAGES, pbuf[0]);
   }
+
+  wait_vmem_all();   // the repeated loads of the last steps land before the workgroup ends
 
   // ---- epilogue -------------------------------------------------------------
 #pragma unroll
