@@ -505,53 +505,90 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
         bool need_mask = !wave_keys_ok || rows_left < QT - 1 ||
                          (p.causal && kv_base + wkey0 + 31 > qpos0);
         if constexpr (DOCS) need_mask = need_mask || qpos0 + QT - 1 >= de_wave;
-        if constexpr (UMASK) need_mask = true;
-        if (need_mask) {
+        // (A user mask is applied to every step, the range mask only where needed.)
+        if (need_mask || UMASK) {
 #pragma unroll
           for (int kn = 0; kn < KN; ++kn) {
-            int hi = rows_left;
-            if constexpr (DOCS) {
-              // ... and rows before the end of the key's sequence.
-              const int64_t e = de_key[kn] - qpos0 - 1;
-              hi = (int)min<int64_t>(hi, e < -1 ? -1 : e);
-            }
-            const int hi_g = hi - 4 * grp;
-            int lo = 0;
-            if (p.causal) {
-              const int64_t r = kv_base + my_key[kn] - qpos0;
-              lo = (int)(r < 0 ? 0 : (r > QT ? QT : r));
-            }
-            if (!key_ok[kn]) lo = QT;
-            const int lo_g = lo - 4 * grp;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int r = 16 * rb + i;
-                sacc[rb][kn][i] = (r < lo_g || r > hi_g) ? -INFINITY : sacc[rb][kn][i];
+            if (!UMASK || need_mask) {
+              int hi = rows_left;
+              if constexpr (DOCS) {
+                // ... and rows before the end of the key's sequence.
+                const int64_t e = de_key[kn] - qpos0 - 1;
+                hi = (int)min<int64_t>(hi, e < -1 ? -1 : e);
               }
+              const int hi_g = hi - 4 * grp;
+              int lo = 0;
+              if (p.causal) {
+                const int64_t r = kv_base + my_key[kn] - qpos0;
+                lo = (int)(r < 0 ? 0 : (r > QT ? QT : r));
+              }
+              if (!key_ok[kn]) lo = QT;
+              const int lo_g = lo - 4 * grp;
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int r = 16 * rb + i;
+                  sacc[rb][kn][i] = (r < lo_g || r > hi_g) ? -INFINITY : sacc[rb][kn][i];
+                }
+            }
             if constexpr (UMASK) {
               // ... and allowed by the user mask: rows 16rb + 4grp + i of the
-              // query tile (of head cs.h of the group), this lane's key.
-              if (key_ok[kn]) {
-                const uint8_t *mb = p.mask + b * p.m_sb + (int64_t)(hk * p.group + cs.h) * p.m_sh +
-                                    ((int64_t)cs.c * p.chunk_len + cs.t * QT) * p.m_ss;
+              // query tile (of head cs.h of the group), this lane's key. The
+              // sixteen reads are issued before any is used. A key past the
+              // end reads the last key and, in a partial tile, a row past the
+              // chunk end its last row: both are hidden above and stay so.
+              // The reads go through a buffer descriptor of the tile's mask
+              // rows: a full tile's row offsets (16rb + i) * m_ss are
+              // wave-uniform scalar offsets and each lane adds one 32-bit
+              // offset (the host bounds 64 mask rows below 2^31 bytes).
+              const uint8_t *mb = p.mask + b * p.m_sb + (int64_t)(hk * p.group + cs.h) * p.m_sh +
+                                  ((int64_t)cs.c * p.chunk_len + cs.t * QT) * p.m_ss;
+              const __amdgpu_buffer_rsrc_t mrs =
+                  __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mb), 0, 0x7fffffff, kBufferFlags);
+              const int kcl = min(my_key[kn], p.skv - 1);
+              const uint32_t esz = p.mask_add ? 4u : 1u;
+              const int mss = (int)p.m_ss;
+              // The mask value of row 16rb + 4grp + i (clamped in a partial tile).
+              auto mask_at = [&](auto ld, auto &v) {
+                if (rows_left >= QT - 1) {
+                  const uint32_t lane_off = (uint32_t)(4 * grp * mss) + (uint32_t)kcl * esz;
+#pragma unroll
+                  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[rb][i] = ld(lane_off, (16 * rb + i) * mss);
+                } else {
+#pragma unroll
+                  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                      const int r = min(16 * rb + 4 * grp + i, rows_left);
+                      v[rb][i] = ld((uint32_t)(r * mss) + (uint32_t)kcl * esz, 0);
+                    }
+                }
+              };
+              if (p.mask_add) {
+                // additive mask, in the raw score's units (at or below
+                // kMaskHide: hidden); a hidden score stays -inf
                 const float inv = 1.0f / p.scale;
+                float a[RB][4];
+                mask_at([&](uint32_t off, int soff) {
+                  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(mrs, off, soff, 0));
+                }, a);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                   for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + 4 * grp + i;
-                    if (r > rows_left) continue;
-                    if (p.mask_add) {
-                      // additive mask, in the raw score's units (at or
-                      // below kMaskHide: hidden)
-                      const float a = reinterpret_cast<const float *>(mb + (int64_t)r * p.m_ss)[my_key[kn]];
-                      sacc[rb][kn][i] = a <= kMaskHide ? -INFINITY : fmaf(a, inv, sacc[rb][kn][i]);
-                    } else if (mb[(int64_t)r * p.m_ss + my_key[kn]] == 0) {
-                      sacc[rb][kn][i] = -INFINITY;
-                    }
+                    const float sv = sacc[rb][kn][i];
+                    sacc[rb][kn][i] = (a[rb][i] <= kMaskHide || sv == -INFINITY) ? -INFINITY : fmaf(a[rb][i], inv, sv);
                   }
+              } else {
+                uint32_t m[RB][4];
+                mask_at([&](uint32_t off, int soff) { return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(mrs, off, soff, 0); }, m);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) sacc[rb][kn][i] = m[rb][i] ? sacc[rb][kn][i] : -INFINITY;
               }
             }
           }
@@ -1140,70 +1177,77 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     const int64_t blk_plo = base + (int64_t)sb * 32;
     bool need_mask = (sb * 32 + 32 > p.skv) || (p.causal && blk_plo + 31 > wave_qlo);
     if constexpr (DOCS) need_mask = need_mask || blk_plo < wave_ds;
-    if constexpr (UMASK) need_mask = true;
-    if (need_mask) {
+    // (A user mask is applied to every block, the range mask only where needed.)
+    if (need_mask || UMASK) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        int lim = p.skv - 1 - sb * 32;
-        if (p.causal) {
-          const int64_t rel = qpos[qb] - blk_plo;
-          lim = min(lim, (int)(rel < -1 ? -1 : (rel > 32 ? 32 : rel)));
-        }
-        const int t = lim - 4 * grp;
-        if constexpr (DOCS) {
-          // ... and >= the row's sequence start.
-          const int tl = min(max(lo_key[qb] - sb * 32, 0), 32) - 4 * grp;
+        if (!UMASK || need_mask) {
+          int lim = p.skv - 1 - sb * 32;
+          if (p.causal) {
+            const int64_t rel = qpos[qb] - blk_plo;
+            lim = min(lim, (int)(rel < -1 ? -1 : (rel > 32 ? 32 : rel)));
+          }
+          const int t = lim - 4 * grp;
+          if constexpr (DOCS) {
+            // ... and >= the row's sequence start.
+            const int tl = min(max(lo_key[qb] - sb * 32, 0), 32) - 4 * grp;
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              scur[h][qb][i] = (16 * h + i > t || 16 * h + i < tl) ? -INFINITY : scur[h][qb][i];
-        } else {
+              for (int i = 0; i < 4; ++i)
+                scur[h][qb][i] = (16 * h + i > t || 16 * h + i < tl) ? -INFINITY : scur[h][qb][i];
+          } else {
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) scur[h][qb][i] = (16 * h + i > t) ? -INFINITY : scur[h][qb][i];
+              for (int i = 0; i < 4; ++i) scur[h][qb][i] = (16 * h + i > t) ? -INFINITY : scur[h][qb][i];
+          }
         }
         if constexpr (UMASK) {
+          // ... and the user mask: the 4 bytes (or 4 floats) of this lane's
+          // keys 16*h + 4*grp .. +3 of the block, every read issued before any
+          // is used. In a ragged block keys past the end read nothing (0:
+          // hidden, or no bias on a score the range mask hid).
+          const bool full = sb * 32 + 32 <= p.skv;
           if (p.mask_add) {
-            // ... plus the additive mask (value / softmax_scale; at or below
-            // kMaskHide: hidden).
+            // Additive: value / softmax_scale; at or below kMaskHide: hidden.
             const float inv = 1.0f / p.scale;
             const float *mf = reinterpret_cast<const float *>(mrow[qb]);
+            f32x4 a[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int k0 = sb * 32 + 16 * h + 4 * grp;
-              f32x4 a;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) a[i] = 0.0f;
-              if (k0 + 4 <= p.skv) {
-                a = *reinterpret_cast<const f32x4 *>(mf + k0);
+              if (full) {
+                a[h] = *reinterpret_cast<const f32x4 *>(mf + k0);
               } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (k0 + i < p.skv) a[i] = mf[k0 + i];
+                for (int i = 0; i < 4; ++i) a[h][i] = k0 + i < p.skv ? mf[k0 + i] : 0.0f;
               }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                scur[h][qb][i] = a[i] <= kMaskHide ? -INFINITY : fmaf(a[i], inv, scur[h][qb][i]);
-            }
+                scur[h][qb][i] = a[h][i] <= kMaskHide ? -INFINITY : fmaf(a[h][i], inv, scur[h][qb][i]);
           } else {
-          // ... and allowed by the user mask (keys 16*h + 4*grp .. +3 of the block).
+            uint32_t w[2];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int k0 = sb * 32 + 16 * h + 4 * grp;
-            uint32_t w = 0;
-            if (k0 + 4 <= p.skv) {
-              w = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
-            } else {
+            for (int h = 0; h < 2; ++h) {
+              const int k0 = sb * 32 + 16 * h + 4 * grp;
+              if (full) {
+                w[h] = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
+              } else {
+                w[h] = 0;
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (k0 + i < p.skv) w |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
+                for (int i = 0; i < 4; ++i)
+                  if (k0 + i < p.skv) w[h] |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
+              }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              scur[h][qb][i] = ((w >> (8 * i)) & 0xffu) ? scur[h][qb][i] : -INFINITY;
-          }
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                scur[h][qb][i] = ((w[h] >> (8 * i)) & 0xffu) ? scur[h][qb][i] : -INFINITY;
           }
         }
       }

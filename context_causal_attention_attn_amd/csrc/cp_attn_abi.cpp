@@ -131,6 +131,8 @@ static int32_t validate(const cp_attn_desc *d) {
       if (d->mask_strides[i] < 0) return CP_ATTN_ERR_BAD_SHAPE;
       if (d->mask_strides[i] % al != 0) return CP_ATTN_ERR_ALIGNMENT;
     }
+    // The key-stationary kernel addresses 64 mask rows with 32-bit offsets.
+    if (d->mask_strides[2] >= ((int64_t)1 << 25)) return CP_ATTN_ERR_BAD_SHAPE;
   }
   // Strides: non-negative, and every row start 16-byte aligned given an
   // aligned base pointer (the kernels move 16-byte vectors along the dim).

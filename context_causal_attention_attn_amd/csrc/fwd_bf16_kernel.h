@@ -477,73 +477,79 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     // is visible to a row iff it is <= that row's limit.
     bool need_mask = MKV ? (kt * BN + BN > p.skv) || (p.causal && tile_plo + BN - 1 > wave_qlo) : kt >= mask_from;
     if constexpr (DOCS) need_mask = need_mask || tile_plo < wave_ds;
-    if constexpr (UMASK) need_mask = true;
-    if (need_mask) {
+    // (A user mask is applied to every tile, the range mask only where needed.)
+    if (need_mask || UMASK) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        int lim = p.skv - 1 - kt * BN;
-        if (p.causal) {
-          const int64_t rel = qpos[qb] - tile_plo;
-          lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
-        }
-        const int t = lim - 4 * grp;
-        if constexpr (DOCS) {
-          // ... and >= the row's sequence start.
-          const int tl = min(max(lo_key[qb] - kt * BN, 0), BN) - 4 * grp;
+        if (!UMASK || need_mask) {
+          int lim = p.skv - 1 - kt * BN;
+          if (p.causal) {
+            const int64_t rel = qpos[qb] - tile_plo;
+            lim = min(lim, (int)(rel < -1 ? -1 : (rel > BN ? BN : rel)));
+          }
+          const int t = lim - 4 * grp;
+          if constexpr (DOCS) {
+            // ... and >= the row's sequence start.
+            const int tl = min(max(lo_key[qb] - kt * BN, 0), BN) - 4 * grp;
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sacc[qb][kb][i] = (16 * kb + i > t || 16 * kb + i < tl) ? -INFINITY : sacc[qb][kb][i];
-        } else {
+              for (int i = 0; i < 4; ++i)
+                sacc[qb][kb][i] = (16 * kb + i > t || 16 * kb + i < tl) ? -INFINITY : sacc[qb][kb][i];
+          } else {
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sacc[qb][kb][i] = (16 * kb + i > t) ? -INFINITY : sacc[qb][kb][i];
+              for (int i = 0; i < 4; ++i)
+                sacc[qb][kb][i] = (16 * kb + i > t) ? -INFINITY : sacc[qb][kb][i];
+          }
         }
         if constexpr (UMASK) {
+          // ... and the user mask: the 4 bytes (or 4 floats) of this lane's
+          // keys 16*kb + 4*grp .. +3 per block, every read issued before any
+          // is used. In the ragged last tile keys past the end read nothing
+          // (0: hidden, or no bias on a score the range mask hid).
+          const bool full = kt * BN + BN <= p.skv;
           if (p.mask_add) {
-            // ... plus the additive mask: 4 floats of this lane's keys per
-            // block, in the raw score's units (value / softmax_scale); a value
-            // at or below kMaskHide hides the key.
+            // Additive: in the raw score's units (value / softmax_scale); a
+            // value at or below kMaskHide hides the key.
             const float inv = 1.0f / p.scale;
             const float *mf = reinterpret_cast<const float *>(mrow[qb]);
+            f32x4 a[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
               const int k0 = kt * BN + 16 * kb + 4 * grp;
-              f32x4 a;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) a[i] = 0.0f;
-              if (k0 + 4 <= p.skv) {
-                a = *reinterpret_cast<const f32x4 *>(mf + k0);
+              if (full) {
+                a[kb] = *reinterpret_cast<const f32x4 *>(mf + k0);
               } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (k0 + i < p.skv) a[i] = mf[k0 + i];
+                for (int i = 0; i < 4; ++i) a[kb][i] = k0 + i < p.skv ? mf[k0 + i] : 0.0f;
               }
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                sacc[qb][kb][i] = a[i] <= kMaskHide ? -INFINITY : fmaf(a[i], inv, sacc[qb][kb][i]);
-            }
+                sacc[qb][kb][i] = a[kb][i] <= kMaskHide ? -INFINITY : fmaf(a[kb][i], inv, sacc[qb][kb][i]);
           } else {
-          // ... and allowed by the user mask: the 4 bytes of this lane's keys
-          // 16*kb + 4*grp .. +3 (byte reads past the last key row).
+            uint32_t w[KB];
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const int k0 = kt * BN + 16 * kb + 4 * grp;
-            uint32_t w = 0;
-            if (k0 + 4 <= p.skv) {
-              w = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
-            } else {
+            for (int kb = 0; kb < KB; ++kb) {
+              const int k0 = kt * BN + 16 * kb + 4 * grp;
+              if (full) {
+                w[kb] = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
+              } else {
+                w[kb] = 0;
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (k0 + i < p.skv) w |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
+                for (int i = 0; i < 4; ++i)
+                  if (k0 + i < p.skv) w[kb] |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
+              }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sacc[qb][kb][i] = ((w >> (8 * i)) & 0xffu) ? sacc[qb][kb][i] : -INFINITY;
-          }
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                sacc[qb][kb][i] = ((w[kb] >> (8 * i)) & 0xffu) ? sacc[qb][kb][i] : -INFINITY;
           }
         }
       }

@@ -23,6 +23,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a gfx9-family buffer resource for raw byte addressing (32-bit
+// data format, no swizzle): the form the mask reads use.
+constexpr int kBufferFlags = 0x00020000;
 
 // Row-major LDS tile for the 16x16x32 kernels, read both ways: as rows (16
 // consecutive rows, one 16-byte chunk per lane and lane/16 choosing among 4

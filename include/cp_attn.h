@@ -188,7 +188,7 @@ typedef struct cp_attn_desc {
   int32_t n_docs;              /* 0: one sequence; > 0: packed sequences (needs causal, one KV chunk) */
   const int64_t *doc_starts;   /* host array [n_docs]: strictly increasing global start positions, >= 0 */
   const void *attn_mask;       /* NULL, or DEVICE [batch][hq][sq_local][skv] mask of mask_additive's kind */
-  int64_t mask_strides[3];     /* batch, head, row strides of attn_mask in bytes (0 broadcasts); key stride 1 */
+  int64_t mask_strides[3];     /* batch, head, row strides of attn_mask in bytes (0 broadcasts; row stride < 32 MiB); key stride 1 */
   int32_t mask_additive;       /* 0: bytes, nonzero = may attend; 1: float32 added to the scaled score */
   int64_t chunk_strides[3];    /* q, k/v, out/dout/dq: elements from one chunk's row 0 to the next */
                                /* chunk's (Q chunks for q and out, KV chunks for k/v); 0: the rows */

@@ -350,8 +350,8 @@ def test_packed_share_pairs_match_oracle(mix, kind, rank):
 
 def test_validate_user_mask():
     """A user attention mask (device bytes; validation reads only the pointer
-    value and the strides): 4-byte alignment, natural key order, no packed
-    sequences."""
+    value and the strides): 4-byte alignment, a row stride below 32 MiB,
+    natural key order, no packed sequences."""
     base = 1 << 40
     d = desc()
     d.desc.attn_mask = base
@@ -364,6 +364,10 @@ def test_validate_user_mask():
     d.desc.mask_strides[2] = 2046
     assert status(d) == -9
     d.desc.mask_strides[2] = -4
+    assert status(d) == -2
+    d.desc.mask_strides[2] = (1 << 25) - 4       # 64 rows stay below 2^31 bytes
+    assert status(d) == 0
+    d.desc.mask_strides[2] = 1 << 25
     assert status(d) == -2
     d2 = desc(skv=2048, kv_chunk_pos=[1024, 0])
     d2.desc.attn_mask = base
