@@ -1,4 +1,5 @@
-// Backward dispatch: the Delta pre-pass, then the dK/dV and dQ instantiations
+// Backward dispatch: the Delta pre-pass (and the bit table of a boolean user
+// mask), then the dK/dV and dQ instantiations
 // of the share's mode (keys in natural order, a KV chunk table, packed
 // sequences, a user mask). The kernels live in bwd_bf16_kernels.h; each mode
 // is compiled in a file of its own.
@@ -18,6 +19,10 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
   if (rows > 0) {
     const int64_t blocks = (rows * 16 + 255) / 256;
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(blocks), dim3(256), 0, s, p);
+  }
+  if (p.mask_bits && p.skv > 0 && p.sq > 0) {
+    const int64_t blocks = (int64_t)((p.skv + 255) / 256) * p.n_q_chunks * p.mb_tpc * p.mb_batches * p.mb_heads;
+    hipLaunchKernelGGL(bwd_mask_bits_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p);
   }
   if (int e = mark(1)) return e;
   int e = p.mask ? launch_bwd_dkdv_m2(p, D, stream)

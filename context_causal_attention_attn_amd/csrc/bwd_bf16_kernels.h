@@ -75,6 +75,30 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 1b. A boolean user mask as bits (see BwdParams::mask_bits): one thread per
+//     key and 64-row query tile, consecutive threads on consecutive keys (the
+//     mask's bytes of one row, and the table's words, are contiguous in keys).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_mask_bits_kernel(const BwdParams p) {
+  const int nkb = (p.skv + 255) / 256;
+  const int ntiles = p.n_q_chunks * p.mb_tpc;
+  const int64_t blk = blockIdx.x;
+  const int key = (int)(blk % nkb) * 256 + threadIdx.x;
+  const int n = (int)((blk / nkb) % ntiles);
+  const int bh = (int)(blk / ((int64_t)nkb * ntiles));
+  if (key >= p.skv) return;
+  const int c = n / p.mb_tpc, t = n % p.mb_tpc;
+  const int rows = min(kBwdBlockQ, p.chunk_len - t * kBwdBlockQ);
+  const int bm = bh / p.mb_heads, hm = bh % p.mb_heads;
+  const uint8_t *col = p.mask + bm * p.m_sb + hm * p.m_sh +
+                       ((int64_t)c * p.chunk_len + (int64_t)t * kBwdBlockQ) * p.m_ss + key;
+  uint64_t w = 0;
+  for (int r = 0; r < rows; ++r)
+    if (col[(int64_t)r * p.m_ss]) w |= (uint64_t)1 << (16 * ((r >> 2) & 3) + 4 * (r >> 4) + (r & 3));
+  p.mask_bits[((int64_t)bh * ntiles + n) * p.skv + key] = w;
+}
+
+// ---------------------------------------------------------------------------
 // 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------
 // One workgroup of 8 wavefronts per 128-key tile of one KV head; wavefronts
@@ -533,48 +557,44 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
                 }
             }
             if constexpr (UMASK) {
-              // ... and allowed by the user mask: rows 16rb + 4grp + i of the
-              // query tile (of head cs.h of the group), this lane's key. The
-              // sixteen reads are issued before any is used. A key past the
-              // end reads the last key and, in a partial tile, a row past the
-              // chunk end its last row: both are hidden above and stay so.
-              // The reads go through a buffer descriptor of the tile's mask
-              // rows: a full tile's row offsets (16rb + i) * m_ss are
-              // wave-uniform scalar offsets and each lane adds one 32-bit
-              // offset (the host bounds 64 mask rows below 2^31 bytes).
-              const uint8_t *mb = p.mask + b * p.m_sb + (int64_t)(hk * p.group + cs.h) * p.m_sh +
-                                  ((int64_t)cs.c * p.chunk_len + cs.t * QT) * p.m_ss;
-              const __amdgpu_buffer_rsrc_t mrs =
-                  __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mb), 0, 0x7fffffff, kBufferFlags);
-              const int kcl = min(my_key[kn], p.skv - 1);
-              const uint32_t esz = p.mask_add ? 4u : 1u;
-              const int mss = (int)p.m_ss;
-              // The mask value of row 16rb + 4grp + i (clamped in a partial tile).
-              auto mask_at = [&](auto ld, auto &v) {
+              if (p.mask_add) {
+                // ... plus an additive user mask: rows 16rb + 4grp + i of the
+                // query tile (of head cs.h of the group), this lane's key, in
+                // the raw score's units (at or below kMaskHide: hidden; a
+                // hidden score stays -inf). The sixteen reads are issued
+                // before any is used. A key past the end reads the last key
+                // and, in a partial tile, a row past the chunk end its last
+                // row: both are hidden above. The reads go through a buffer
+                // descriptor of the tile's mask rows: a full tile's row offsets
+                // (16rb + i) * m_ss are wave-uniform scalar offsets and each
+                // lane adds one 32-bit offset (the host bounds 64 mask rows
+                // below 2^31 bytes).
+                const uint8_t *mb = p.mask + b * p.m_sb + (int64_t)(hk * p.group + cs.h) * p.m_sh +
+                                    ((int64_t)cs.c * p.chunk_len + cs.t * QT) * p.m_ss;
+                const __amdgpu_buffer_rsrc_t mrs =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mb), 0, 0x7fffffff, kBufferFlags);
+                const uint32_t koff = 4u * (uint32_t)min(my_key[kn], p.skv - 1);
+                const int mss = (int)p.m_ss;
+                auto ld = [&](uint32_t off, int soff) {
+                  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(mrs, off, soff, 0));
+                };
+                float a[RB][4];
                 if (rows_left >= QT - 1) {
-                  const uint32_t lane_off = (uint32_t)(4 * grp * mss) + (uint32_t)kcl * esz;
+                  const uint32_t lane_off = (uint32_t)(4 * grp * mss) + koff;
 #pragma unroll
                   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[rb][i] = ld(lane_off, (16 * rb + i) * mss);
+                    for (int i = 0; i < 4; ++i) a[rb][i] = ld(lane_off, (16 * rb + i) * mss);
                 } else {
 #pragma unroll
                   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                       const int r = min(16 * rb + 4 * grp + i, rows_left);
-                      v[rb][i] = ld((uint32_t)(r * mss) + (uint32_t)kcl * esz, 0);
+                      a[rb][i] = ld((uint32_t)(r * mss) + koff, 0);
                     }
                 }
-              };
-              if (p.mask_add) {
-                // additive mask, in the raw score's units (at or below
-                // kMaskHide: hidden); a hidden score stays -inf
                 const float inv = 1.0f / p.scale;
-                float a[RB][4];
-                mask_at([&](uint32_t off, int soff) {
-                  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(mrs, off, soff, 0));
-                }, a);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -583,12 +603,19 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
                     sacc[rb][kn][i] = (a[rb][i] <= kMaskHide || sv == -INFINITY) ? -INFINITY : fmaf(a[rb][i], inv, sv);
                   }
               } else {
-                uint32_t m[RB][4];
-                mask_at([&](uint32_t off, int soff) { return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(mrs, off, soff, 0); }, m);
+                // ... and allowed by a boolean user mask: one word of its bit
+                // table per key and query tile, bit 16grp + 4rb + i for row
+                // 16rb + 4grp + i (a key past the end reads the last key's:
+                // hidden above).
+                const int bh = (p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? hk * p.group + cs.h : 0);
+                const int64_t tile = (int64_t)bh * p.n_q_chunks * p.mb_tpc + cs.c * p.mb_tpc + cs.t;
+                const uint64_t word = p.mask_bits[tile * p.skv + min(my_key[kn], p.skv - 1)];
+                const uint32_t w16 = (uint32_t)(word >> (16 * grp));
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                  for (int i = 0; i < 4; ++i) sacc[rb][kn][i] = m[rb][i] ? sacc[rb][kn][i] : -INFINITY;
+                  for (int i = 0; i < 4; ++i)
+                    sacc[rb][kn][i] = ((w16 >> (4 * rb + i)) & 1u) ? sacc[rb][kn][i] : -INFINITY;
               }
             }
           }

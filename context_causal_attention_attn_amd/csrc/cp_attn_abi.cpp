@@ -350,6 +350,18 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool a
   }
   p->kv_parts = allow_split ? dkdv_parts(d, s, p->kt0, p->kt1) : 1;
   p->kv_partial = nullptr;
+  p->mask_bits = nullptr;
+  p->mb_batches = d->mask_strides[0] ? d->batch : 1;
+  p->mb_heads = d->mask_strides[1] ? d->hq : 1;
+  p->mb_tpc = (int32_t)((p->chunk_len + kBwdBlockQ - 1) / kBwdBlockQ);
+}
+
+// The bit table of a boolean user mask for the bf16 key-stationary kernel
+// (see BwdParams::mask_bits), 256-byte aligned.
+static size_t bwd_mask_bits_bytes(const cp_attn_desc *d, const BwdParams &p) {
+  if (!d->attn_mask || d->mask_additive || d->dtype != CP_ATTN_BF16) return 0;
+  const size_t words = (size_t)p.mb_batches * p.mb_heads * (size_t)p.n_q_chunks * p.mb_tpc * (size_t)d->skv;
+  return (words * 8 + 255) & ~(size_t)255;
 }
 
 // fp32 partial dK/dV of the split key tiles (see BwdParams::kv_parts).
@@ -384,7 +396,7 @@ const char *cp_attn_error_string(int32_t status) {
     case CP_ATTN_ERR_ABI: return "descriptor abi_version does not match the library";
     case CP_ATTN_ERR_ALIGNMENT: return "device pointer or stride not 16-byte aligned";
     case CP_ATTN_ERR_DIVISIBILITY: return "sequence length not divisible by cp_size (contiguous) or 2*cp_size (head_tail)";
-    case CP_ATTN_ERR_SCRATCH_LIMIT: return "batch*hq*sq_local exceeds the fixed scratch of cp_attn_bwd_noalloc (CP_ATTN_NOALLOC_MAX_ROWS); use cp_attn_bwd with a workspace";
+    case CP_ATTN_ERR_SCRATCH_LIMIT: return "the share's rows (CP_ATTN_NOALLOC_MAX_ROWS) or workspace exceed the fixed scratch of cp_attn_bwd_noalloc; use cp_attn_bwd with a workspace";
     default: return "unknown status";
   }
 }
@@ -471,12 +483,9 @@ int32_t cp_attn_workspace_bytes(const cp_attn_desc *d, int32_t backward, size_t 
   if (!backward) { *bytes = 0; return CP_ATTN_OK; }
   // Backward: Delta = rowsum(dO o O) and LSE * log2(e), each [B, Hq, Sq]
   // fp32, each starting on a 256-byte boundary; then the fp32 partial dK/dV
-  // of key tiles split over several workgroups (none for most shares).
-  Share s;
-  make_share(d, &s);
-  BwdParams p;
-  fill_bwd_params(d, s, &p);
-  *bytes = 2 * bwd_stat_bytes(d) + bwd_partial_bytes(p, d->head_dim);
+  // of key tiles split over several workgroups (none for most shares); then
+  // the bit table of a boolean user mask (bf16).
+  *bytes = cpattn::bwd_workspace_bytes(d, true);
   return CP_ATTN_OK;
 }
 
@@ -570,7 +579,13 @@ int32_t cp_attn_bwd(const cp_attn_desc *d, const void *q, const void *k, const v
 
 namespace cpattn {
 
-size_t bwd_stats_bytes(const cp_attn_desc *d) { return 2 * bwd_stat_bytes(d); }
+size_t bwd_workspace_bytes(const cp_attn_desc *d, bool allow_split) {
+  Share s;
+  make_share(d, &s);
+  BwdParams p;
+  fill_bwd_params(d, s, &p, allow_split);
+  return 2 * bwd_stat_bytes(d) + bwd_partial_bytes(p, d->head_dim) + bwd_mask_bits_bytes(d, p);
+}
 
 int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void *v, const void *out,
                 const float *lse, const void *dout, void *dq, float *dk, float *dv, void *workspace,
@@ -588,7 +603,12 @@ int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void 
   make_share(d, &s);
   BwdParams p;
   fill_bwd_params(d, s, &p, allow_split);
-  const size_t need = 2 * bwd_stat_bytes(d) + bwd_partial_bytes(p, d->head_dim);
+  const size_t partial = bwd_partial_bytes(p, d->head_dim);
+  const size_t bits = bwd_mask_bits_bytes(d, p);
+  const size_t need = 2 * bwd_stat_bytes(d) + partial + bits;
+  // The bit table's pass runs one workgroup per 256 keys, query tile and mask head.
+  if (bits > 0 && (int64_t)((d->skv + 255) / 256) * p.n_q_chunks * p.mb_tpc * p.mb_batches * p.mb_heads > INT32_MAX)
+    return CP_ATTN_ERR_UNSUPPORTED;
   if (d->sq_local > 0 && (!q || !out || !lse || !dout || !dq)) return CP_ATTN_ERR_NULL_PTR;
   if (d->skv > 0 && (!k || !v || !dk || !dv)) return CP_ATTN_ERR_NULL_PTR;
   if (need > 0 && (!workspace || workspace_bytes < need)) return CP_ATTN_ERR_WORKSPACE;
@@ -602,6 +622,8 @@ int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void 
   p.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + bwd_stat_bytes(d));
   if (p.kv_parts > 1)
     p.kv_partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d));
+  if (bits > 0)
+    p.mask_bits = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d) + partial);
   void *const *ev = n_events == 4 ? events : nullptr;
   const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream, ev)
                                            : launch_bwd_fp32(p, d->head_dim, stream, ev);

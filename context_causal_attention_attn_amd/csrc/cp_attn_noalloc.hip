@@ -56,7 +56,7 @@ extern "C" int32_t cp_attn_bwd_noalloc(const cp_attn_desc *desc, const void *q, 
   const int32_t st = cp_attn_validate(desc);
   if (st) return st;
   const int64_t rows = (int64_t)desc->batch * desc->hq * desc->sq_local;
-  if (rows > CP_ATTN_NOALLOC_MAX_ROWS || cpattn::bwd_stats_bytes(desc) > kScratchBytes)
+  if (rows > CP_ATTN_NOALLOC_MAX_ROWS || cpattn::bwd_workspace_bytes(desc, false) > kScratchBytes)
     return CP_ATTN_ERR_SCRATCH_LIMIT;
   if (rows == 0 && desc->skv == 0) return CP_ATTN_OK;
   int dev = -1;

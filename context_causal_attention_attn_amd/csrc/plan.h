@@ -168,6 +168,14 @@ struct BwdParams {
   // reduction kernel adds into dK/dV.
   int32_t kv_parts;
   float *kv_partial;
+  // A boolean user mask as bits, for the key-stationary bf16 kernel (NULL:
+  // none, or the mask is additive, or the fp32 kernels): word
+  // [(bm * mb_heads + hm) * n_q_chunks * mb_tpc + c * mb_tpc + t][key] holds
+  // the 64 rows of query tile t of chunk c, bit 16*g + 4*rb + i for row
+  // 16*rb + 4*g + i of the tile (1: the key may be attended; 0 also past the
+  // chunk end); bm, hm index the mask's batch and head (0 where it broadcasts).
+  uint64_t *mask_bits;
+  int32_t mb_batches, mb_heads, mb_tpc;
 };
 
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p);
@@ -175,7 +183,9 @@ void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p);
 void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool allow_split = true);
 // Bytes of the backward's per-row statistics (-Delta and LSE*log2e, each on a
 // 256-byte boundary), the part of the workspace every backward needs.
-size_t bwd_stats_bytes(const cp_attn_desc *d);
+// Workspace bytes of the backward: the per-row statistics, the partial dK/dV
+// of split key tiles (allow_split) and the bit table of a boolean user mask.
+size_t bwd_workspace_bytes(const cp_attn_desc *d, bool allow_split);
 // cp_attn_bwd_timed with the choice of splitting key tiles (the no-alloc
 // entry point passes allow_split = false: its scratch holds no partials).
 int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void *v, const void *out,

@@ -98,7 +98,7 @@ typedef enum {
   CP_ATTN_ERR_ABI = -8,           /* desc->abi_version != CP_ATTN_ABI_VERSION */
   CP_ATTN_ERR_ALIGNMENT = -9,     /* a device pointer or stride breaks the 16-byte vector alignment */
   CP_ATTN_ERR_DIVISIBILITY = -10, /* cp_attn_share_positions: S not divisible by cp (or 2*cp) */
-  CP_ATTN_ERR_SCRATCH_LIMIT = -11 /* cp_attn_bwd_noalloc: more rows than its fixed scratch holds */
+  CP_ATTN_ERR_SCRATCH_LIMIT = -11 /* cp_attn_bwd_noalloc: the share's workspace exceeds its fixed scratch */
 } cp_attn_status;
 
 /*
@@ -241,9 +241,11 @@ int32_t cp_attn_share_pairs(const cp_attn_desc *desc, int64_t *pairs);
 /* Bytes of device workspace cp_attn_fwd (backward == 0: none) or cp_attn_bwd
  * (backward != 0) needs for this descriptor; may be 0. The backward's holds
  * the per-row statistics of the recompute-based gradient of [CP-migration]
- * §6.1 (-Delta and LSE*log2(e)) and, for shares whose key tiles are split over
- * several workgroups, their float32 partial dK/dV. Errors: cp_attn_validate's,
- * NULL_PTR for `bytes`. Host only. */
+ * §6.1 (-Delta and LSE*log2(e)), for shares whose key tiles are split over
+ * several workgroups their float32 partial dK/dV, and with a boolean user
+ * mask (bf16) the mask as bits: one 64-bit word per key, 64-row query tile
+ * and mask batch/head, i.e. about an eighth of the mask's bytes. Errors:
+ * cp_attn_validate's, NULL_PTR for `bytes`. Host only. */
 int32_t cp_attn_workspace_bytes(const cp_attn_desc *desc, int32_t backward, size_t *bytes);
 
 /* Work-list statistics of the forward tile scheduler (host only), for tests
@@ -333,7 +335,9 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *desc, const void *q, const void *k
  * (2 x CP_ATTN_NOALLOC_MAX_ROWS float32, 16 MiB, held by every GPU the
  * library runs on until the process ends). Calls no allocating routine; the
  * first call on a device looks up that device's array once.
- * batch * hq * sq_local above CP_ATTN_NOALLOC_MAX_ROWS returns
+ * batch * hq * sq_local above CP_ATTN_NOALLOC_MAX_ROWS, or a share whose
+ * workspace (cp_attn_workspace_bytes without split key tiles, e.g. with the
+ * bit table of a large boolean user mask) exceeds the 16 MiB, returns
  * CP_ATTN_ERR_SCRATCH_LIMIT before anything is enqueued. `stream`'s device
  * (the current device for NULL) selects the array. Every call on one GPU
  * shares that GPU's array: calls that overlap on one GPU (different streams,

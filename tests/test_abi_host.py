@@ -229,6 +229,50 @@ def test_workspace_bytes():
     assert extra >= 0 and extra % unit == 0 and extra // unit in (0, 8, 24, 56)   # (parts - 1) x 8 tiles
 
 
+def test_workspace_holds_the_bit_table_of_a_boolean_mask():
+    """bf16 backward with a boolean user mask: the workspace also holds one
+    64-bit word per key, 64-row query tile of each chunk and mask batch/head
+    (256-byte aligned); an additive mask or the fp32 path adds none."""
+    def extra(**kw):
+        d0, dm = desc(**kw), desc(**kw)
+        dm.desc.attn_mask = 1 << 40
+        return cp_attn_workspace_bytes(dm, True) - cp_attn_workspace_bytes(d0, True), dm
+    # contiguous 500 rows: 8 query tiles; broadcast mask: one batch, one head
+    e, _ = extra()
+    assert e == (8 * 2000 * 8 + 255) // 256 * 256
+    # Head-Tail, two chunks of 250 rows: 4 tiles each; a per-head mask (stride != 0)
+    d = desc(layout="head_tail", q_chunk_pos=[250, 1750], sq_local=500)
+    d0 = cp_attn_workspace_bytes(d, True)
+    d.desc.attn_mask = 1 << 40
+    d.desc.mask_strides[1] = 500 * 2000
+    d.desc.mask_strides[2] = 2000
+    assert cp_attn_workspace_bytes(d, True) - d0 == (8 * 2 * 4 * 2000 * 8 + 255) // 256 * 256
+    # additive: none
+    d = desc()
+    d0 = cp_attn_workspace_bytes(d, True)
+    d.desc.attn_mask = 1 << 40
+    d.desc.mask_additive = 1
+    assert cp_attn_workspace_bytes(d, True) == d0
+    # fp32: none
+    e, _ = extra(dtype=1, head_dim=64, q_strides=(0, 0, 64), kv_strides=(0, 0, 64), o_strides=(0, 0, 64))
+    assert e == 0
+
+
+def test_noalloc_rejects_a_bit_table_beyond_its_scratch():
+    """cp_attn_bwd_noalloc holds the bit table of a boolean mask in its fixed
+    scratch: a share whose table does not fit is refused with
+    CP_ATTN_ERR_SCRATCH_LIMIT before any HIP call."""
+    lib = _lib.load()
+    fake = 1 << 40
+    S = 1 << 20                                          # 1 Mi keys x 8 tiles x 8 bytes = 64 MiB
+    big = desc(skv=S, q_strides=(8 * S * 128, S * 128, 128), kv_strides=(2 * S * 128, S * 128, 128),
+               q_chunk_pos=[S - 500])
+    big.desc.attn_mask = fake
+    big.desc.mask_strides[2] = S
+    args = [fake] * 9 + [None]
+    assert lib.cp_attn_bwd_noalloc(big.ref(), *args) == -11
+
+
 def test_bwd_timed_rejects_bad_event_arrays_before_any_device_work():
     # Host-side checks only: every call below returns before touching a device.
     lib = _lib.load()
