@@ -26,7 +26,9 @@ shares of all 8 ranks (with their max/min spread under "balance"), the Ulysses
 cp=8 rank-0 share, the Hybrid U=2 x C=4 rank-4 share and the Head-Tail B = 2
 backward shares of ranks 0 and 7, and the Colossal rank-7 share over eight
 packed sequences; the Ulysses share also runs straight from the all-to-all's
-received blocks (".../in_place": no unpack or pack pass). While the headline step keeps running for
+received blocks (".../in_place": no unpack or pack pass); the headline share
+also runs under a boolean and an additive user mask (".../user_mask_*": 10 %
+of the pairs hidden at random, FLOPs still over the causal pairs). While the headline step keeps running for
 about 2.5 s, amd-smi reads the GFX clocks and socket power ("clock"; the chip
 runs at its power cap, below the 2.4 GHz the peak assumes). The oracle's CPU
 baseline runs last, in a child process. Prints ONE JSON line. `--detail` adds
@@ -157,7 +159,21 @@ class BlockShare:
         return self._dout
 
 
-def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", warm_s=0.0, in_place=False):
+def share_user_mask(kind, B, Sq, Skv, dev):
+    """A seeded user mask for a share, broadcast over heads: "bool", 10 % of
+    the (row, key) pairs hidden at random; "additive", N(0, 1) biases with the
+    same 10 % at -inf."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(11)
+    keep = torch.rand((1, 1, Sq, Skv), generator=g) >= 0.1
+    if kind == "bool":
+        return keep.to(dev)
+    bias = torch.randn((1, 1, Sq, Skv), generator=g)
+    return torch.where(keep, bias, torch.full((), float("-inf"))).to(dev)
+
+
+def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", warm_s=0.0, in_place=False,
+               user_mask=None):
     import torch
     from context_causal_attention_attn_amd import api, cut_share
 
@@ -173,10 +189,11 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", wa
     docs = doc_starts(spec)
     D = sh.q.shape[-1]
     scale = 1.0 / math.sqrt(D)
-    d = api.make_desc(sh.q, sh.k, sh.v, sh.q, sh.q_chunk_pos, kvp, sh.layout, True, scale, docs)
-    pairs = api.cp_attn_share_pairs(d)
     B, Hq, Sq = api._geom(sh.q)[:3]
     Hkv, Skv = api._geom(sh.k)[1:3]
+    mask = share_user_mask(user_mask, B, Sq, Skv, dev) if user_mask else None
+    d = api.make_desc(sh.q, sh.k, sh.v, sh.q, sh.q_chunk_pos, kvp, sh.layout, True, scale, docs, mask)
+    pairs = api.cp_attn_share_pairs(d)
     out = torch.empty(sh.q.shape, dtype=sh.q.dtype, device=dev)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
     dout = (sh.take_rows(prob.dout.to(dev)).contiguous() if not in_place else sh.take_rows(None)) \
@@ -188,12 +205,12 @@ def time_share(spec, prob, rank, steps, warmup, with_bwd, kv_order="natural", wa
 
     def fwd():
         api.cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,
-                        out=out, lse=lse, kv_chunk_pos=kvp, doc_starts=docs)
+                        out=out, lse=lse, kv_chunk_pos=kvp, doc_starts=docs, attn_mask=mask)
 
     def bwd(events):
         api.cp_attn_bwd_timed(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, events,
                               layout=sh.layout, softmax_scale=scale, workspace=ws, grads=grads,
-                              kv_chunk_pos=kvp, doc_starts=docs)
+                              kv_chunk_pos=kvp, doc_starts=docs, attn_mask=mask)
 
     def new_events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -522,6 +539,13 @@ def time_configs(steps, warmup, probs):
                 rr = time_share(sp, pr, r, steps, warmup, True, warm_s=0.3, in_place=True)
                 out[f"{name}/r{r}/in_place"] = share_entry(rr)
                 del rr
+    # The headline share under a user mask (FLOPs still counted over the causal
+    # pairs: the kernels visit every causal tile whatever the mask hides).
+    for kind in ("bool", "additive"):
+        sp = dict(WORKLOADS[WORKLOAD])
+        rr = time_share(sp, probs[problem_key(sp)], 7, steps, warmup, True, warm_s=0.3, user_mask=kind)
+        out[f"{WORKLOAD}/r7/user_mask_{kind}"] = share_entry(rr)
+        del rr
     bal = {}
     for name, ranks in CONFIG_SHARES:
         fw = [out[f"{name}/r{r}"]["fwd_ms"] for r in ranks]
