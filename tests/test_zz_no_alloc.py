@@ -6,7 +6,8 @@ same inputs. dQ comes from the same kernel and must agree bit for bit; dK/dV
 too wherever cp_attn_bwd keeps each key tile in one workgroup. Where it splits
 key tiles over several workgroups (few KV heads; partials summed afterwards),
 the no-alloc call, whose scratch holds no partials, does not: only the fp32
-summation order differs, so dK/dV agree to 1e-5 relative."""
+summation order differs, so dK/dV agree to 1e-5 relative. A boolean user
+mask's bit table shares the scratch too."""
 import ctypes
 import math
 
@@ -20,7 +21,7 @@ from synthetic import global_problem
 pytestmark = pytest.mark.gpu
 
 
-def noalloc_bwd(sh, out, lse, dout, scale):
+def noalloc_bwd(sh, out, lse, dout, scale, mask=None):
     """dq, dk, dv from cp_attn_bwd_noalloc through the C ABI."""
     lib = _lib.load()
     q, k, v = sh.q, sh.k, sh.v
@@ -29,7 +30,7 @@ def noalloc_bwd(sh, out, lse, dout, scale):
     dq = torch.full_like(out, float("nan"))
     dk = torch.full((B, Hkv, Skv, D), float("nan"), dtype=torch.float32, device=q.device)
     dv = torch.full_like(dk, float("nan"))
-    d = make_desc(q, k, v, out.stride(), sh.q_chunk_pos, sh.kv_chunk_pos, sh.layout, True, scale)
+    d = make_desc(q, k, v, out.stride(), sh.q_chunk_pos, sh.kv_chunk_pos, sh.layout, True, scale, (), mask)
     st = lib.cp_attn_bwd_noalloc(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                  torch.cuda.current_stream().cuda_stream)
@@ -61,6 +62,33 @@ def test_noalloc_backward_matches_workspace_backward_twice(dtype):
             rel = float((a - b).norm() / b.norm().clamp_min(1e-30))
             assert rel <= 1e-5, f"{dtype} {kind} S={S}: {name} relative difference {rel}"
         print(f"noalloc {dtype} {kind} B={B} S={S} r{r}: dq bitwise, dk/dv within 1e-5 of cp_attn_bwd", flush=True)
+
+
+def test_noalloc_backward_with_a_boolean_mask():
+    """A boolean user mask: the backward's bit table of it lives in the same
+    scratch; a masked call, then an unmasked smaller one, each against
+    cp_attn_bwd."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device="cpu").manual_seed(62)
+    cases = [(2, 8, 2, 2048, 128, "head_tail", 4, 1, True), (1, 4, 2, 640, 64, "contiguous", 2, 1, False)]
+    for B, Hq, Hkv, S, D, kind, cp, r, masked in cases:
+        prob = global_problem(B, Hq, Hkv, S, D, dtype="bf16", seed=63, with_dout=True)
+        sh = cut_share(kind, prob.q.to(dev), prob.k.to(dev), prob.v.to(dev), cp, r)
+        scale = 1.0 / math.sqrt(D)
+        m = (torch.rand((B, Hq, sh.q.shape[2], S), generator=g) < 0.75).to(dev) if masked else None
+        out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,
+                               attn_mask=m)
+        dout = sh.take_rows(prob.dout.to(dev)).contiguous()
+        ref = cp_attn_bwd(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, layout=sh.layout,
+                          softmax_scale=scale, attn_mask=m)
+        got = noalloc_bwd(sh, out, lse, dout, scale, m)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]), f"{kind} S={S} masked={masked}: dq differs from cp_attn_bwd"
+        for name, a, b in zip(("dk", "dv"), got[1:], ref[1:]):
+            assert torch.isfinite(a).all(), name
+            rel = float((a - b).norm() / b.norm().clamp_min(1e-30))
+            assert rel <= 1e-5, f"{kind} S={S} masked={masked}: {name} relative difference {rel}"
+        print(f"noalloc {kind} B={B} S={S} masked={masked}: dq bitwise, dk/dv within 1e-5", flush=True)
 
 
 def test_noalloc_rejects_shares_beyond_its_scratch():
