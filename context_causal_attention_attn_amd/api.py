@@ -177,7 +177,7 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
                 layout="contiguous", kv_chunk_pos: Sequence[int] = (0,), causal: bool = True,
                 softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, doc_starts: Sequence[int] = (),
-                attn_mask: Optional[torch.Tensor] = None):
+                attn_mask: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Forward of one share: returns (out [B, Hq, Sq, D] in q's dtype, lse [B, Hq, Sq] float32).
 
     q is the local query shard (rows in chunk order), k/v the gathered K/V.
@@ -198,6 +198,9 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
     [chunks, B, Hkv, Lkv, D], one per entry of kv_chunk_pos: e.g. the blocks
     a Ulysses all-to-all delivers, read in place; out then defaults to q's
     shape, the layout the reverse exchange sends. lse is always [B, Hq, Sq].
+
+    A boolean attn_mask is first packed into a bit table in device memory:
+    workspace, if given and large enough, holds it, else one is allocated.
     """
     lib = _lib.load()
     _check_inputs(q, k, v)
@@ -212,8 +215,14 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
         raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
     d = make_desc(q, k, v, out, q_chunk_pos, kv_chunk_pos, layout, causal, softmax_scale, doc_starts,
                   attn_mask)
+    need = cp_attn_workspace_bytes(d, False)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     check(lib.cp_attn_fwd(d.ref(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          lse.data_ptr(), None, 0, _stream_handle(q)), "cp_attn_fwd")
+                          lse.data_ptr(), ws_ptr, ws_bytes, _stream_handle(q)), "cp_attn_fwd")
     return out, lse
 
 

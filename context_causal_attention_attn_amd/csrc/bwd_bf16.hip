@@ -24,6 +24,11 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
     const int64_t blocks = (int64_t)((p.skv + 255) / 256) * p.n_q_chunks * p.mb_tpc * p.mb_batches * p.mb_heads;
     hipLaunchKernelGGL(bwd_mask_bits_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p);
   }
+  if (p.mask_rowbits) {
+    if (int e = launch_mask_rowbits(p.mask, p.m_sb, p.m_sh, p.m_ss, p.mb_batches, p.mb_heads, p.sq, p.skv,
+                                    const_cast<uint64_t *>(p.mask_rowbits), stream))
+      return e;
+  }
   if (int e = mark(1)) return e;
   int e = p.mask ? launch_bwd_dkdv_m2(p, D, stream)
                  : p.docs.n > 0 ? launch_bwd_dkdv_m1(p, D, stream) : launch_bwd_dkdv_m0(p, D, stream);

@@ -957,12 +957,21 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   const int64_t kv_pos0 = p.kv.pos[0];
   // User mask: this lane's mask row per row block (lanes past the wave's last
   // row read the item's first row, like Q).
+  // A boolean mask comes as row bits instead (FwdParams::mask_rowbits'
+  // layout; mrow then points at the row's word of key tile 0, those of tile
+  // kt following kt * sq words on): the lane's 16 bits of a 64-key tile at
+  // bit 16*grp + 4*kb + i for key 16*kb + 4*grp + i, kb = 2 * (32-key block)
+  // + half; each tile's word is read during the tile before.
   const uint8_t *mrow[QB];
+  uint64_t rbits[QB];
   if constexpr (UMASK) {
+    static_assert(BN == 64, "row-bit words cover 64-key tiles");
+    const int64_t bh = (int64_t)(p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? head : 0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int mr = qvalid[qb] ? local_row[qb] : chunk * p.chunk_len + item_row0;
-      mrow[qb] = p.mask + b * p.m_sb + head * p.m_sh + (int64_t)mr * p.m_ss;
+      mrow[qb] = p.mask_add ? p.mask + b * p.m_sb + head * p.m_sh + (int64_t)mr * p.m_ss
+                            : reinterpret_cast<const uint8_t *>(p.mask_rowbits + bh * p.mb_ktiles * p.sq + mr);
     }
   }
   // Packed sequences, as in the forward kernel: this lane's rows see keys
@@ -1231,12 +1240,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
           }
         }
         if constexpr (UMASK) {
-          // ... and the user mask: the 4 bytes (or 4 floats) of this lane's
-          // keys 16*h + 4*grp .. +3 of the block, every read issued before any
-          // is used. In a ragged block keys past the end read nothing (0:
-          // hidden, or no bias on a score the range mask hid).
-          const bool full = sb * 32 + 32 <= p.skv;
+          // ... and the user mask. Additive: the 4 floats of this lane's keys
+          // 16*h + 4*grp .. +3 of the block, every read issued before any is
+          // used; in a ragged block keys past the end read nothing (no bias on
+          // a score the range mask hid).
           if (p.mask_add) {
+            const bool full = sb * 32 + 32 <= p.skv;
             // Additive: value / softmax_scale; at or below kMaskHide: hidden.
             const float inv = 1.0f / p.scale;
             const float *mf = reinterpret_cast<const float *>(mrow[qb]);
@@ -1257,24 +1266,16 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
               for (int i = 0; i < 4; ++i)
                 scur[h][qb][i] = a[h][i] <= kMaskHide ? -INFINITY : fmaf(a[h][i], inv, scur[h][qb][i]);
           } else {
-            uint32_t w[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int k0 = sb * 32 + 16 * h + 4 * grp;
-              if (full) {
-                w[h] = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
-              } else {
-                w[h] = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (k0 + i < p.skv) w[h] |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
-              }
-            }
+            // Boolean: the block's 8 bits of the tile's word; the second
+            // block then reads the next tile's word.
+            const uint32_t w8 = (uint32_t)(rbits[qb] >> (16 * grp + 8 * KB));
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                scur[h][qb][i] = ((w[h] >> (8 * i)) & 0xffu) ? scur[h][qb][i] : -INFINITY;
+                scur[h][qb][i] = ((w8 >> (4 * h + i)) & 1u) ? scur[h][qb][i] : -INFINITY;
+            if (KB == 1 && (sb >> 1) + 1 < t0 + ntiles)
+              rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)((sb >> 1) + 1) * p.sq * 8);
           }
         }
       }
@@ -1365,6 +1366,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     wait_vmem_all();
     __syncthreads();
   };
+  if constexpr (UMASK) {
+    if (!p.mask_add && ntiles > 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)t0 * p.sq * 8);
+    }
+  }
   for (int J = 0; J < ntiles; J += STG) {
     tile_step(IC<0>{}, J);
     if (J + 1 < ntiles) tile_step(IC<1>{}, J + 1);

@@ -181,12 +181,32 @@ static void fill_kv_chunks(const cp_attn_desc *d, KvChunks *kv) {
   }
 }
 
+// A boolean user mask's row bits (FwdParams::mask_rowbits; bf16), 256-byte
+// aligned: one 64-bit word per mask batch/head, 64-key tile and local row.
+static size_t mask_rowbits_bytes(const cp_attn_desc *d) {
+  if (!d->attn_mask || d->mask_additive || d->dtype != CP_ATTN_BF16) return 0;
+  const size_t words = (size_t)(d->mask_strides[0] ? d->batch : 1) * (d->mask_strides[1] ? d->hq : 1) *
+                       (size_t)((d->skv + 63) / 64) * (size_t)d->sq_local;
+  return (words * 8 + 255) & ~(size_t)255;
+}
+
+// A launch's grid counts its work-items in 32 bits.
+static bool fits_grid(int64_t blocks, int64_t threads) { return blocks * threads <= (int64_t)UINT32_MAX; }
+
+// The row-bit pass runs one thread per word, 256 per workgroup.
+static bool mask_rowbits_grid_ok(const cp_attn_desc *d) {
+  return fits_grid((int64_t)(mask_rowbits_bytes(d) / 8 + 255) / 256, 256);
+}
+
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p) {
   memset(p, 0, sizeof(*p));
   collect_doc_bounds(d, &p->docs);
   p->mask = static_cast<const uint8_t *>(d->attn_mask);
   p->mask_add = d->mask_additive;
   p->m_sb = d->mask_strides[0]; p->m_sh = d->mask_strides[1]; p->m_ss = d->mask_strides[2];
+  p->mb_batches = d->mask_strides[0] ? d->batch : 1;
+  p->mb_heads = d->mask_strides[1] ? d->hq : 1;
+  p->mb_ktiles = (int32_t)((d->skv + 63) / 64);
   p->q_sb = d->q_strides[0]; p->q_sh = d->q_strides[1]; p->q_ss = d->q_strides[2];
   p->kv_sb = d->kv_strides[0]; p->kv_sh = d->kv_strides[1]; p->kv_ss = d->kv_strides[2];
   p->o_sb = d->o_strides[0]; p->o_sh = d->o_strides[1]; p->o_ss = d->o_strides[2];
@@ -354,6 +374,8 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool a
   p->mb_batches = d->mask_strides[0] ? d->batch : 1;
   p->mb_heads = d->mask_strides[1] ? d->hq : 1;
   p->mb_tpc = (int32_t)((p->chunk_len + kBwdBlockQ - 1) / kBwdBlockQ);
+  p->mask_rowbits = nullptr;
+  p->mb_ktiles = (int32_t)((d->skv + 63) / 64);
 }
 
 // The bit table of a boolean user mask for the bf16 key-stationary kernel
@@ -480,11 +502,12 @@ int32_t cp_attn_workspace_bytes(const cp_attn_desc *d, int32_t backward, size_t 
   int32_t st = validate(d);
   if (st) return st;
   if (!bytes) return CP_ATTN_ERR_NULL_PTR;
-  if (!backward) { *bytes = 0; return CP_ATTN_OK; }
+  if (!backward) { *bytes = mask_rowbits_bytes(d); return CP_ATTN_OK; }
   // Backward: Delta = rowsum(dO o O) and LSE * log2(e), each [B, Hq, Sq]
   // fp32, each starting on a 256-byte boundary; then the fp32 partial dK/dV
   // of key tiles split over several workgroups (none for most shares); then
-  // the bit table of a boolean user mask (bf16).
+  // a boolean user mask's bit tables (bf16): per key and query tile for
+  // dK/dV, per row and key tile for dQ. Forward: the latter only.
   *bytes = cpattn::bwd_workspace_bytes(d, true);
   return CP_ATTN_OK;
 }
@@ -540,8 +563,6 @@ int32_t cp_attn_plan_stats_fwd(const cp_attn_desc *d, cp_attn_plan_stats *out) {
 int32_t cp_attn_fwd(const cp_attn_desc *d, const void *q, const void *k, const void *v,
                     void *out, float *lse, void *workspace, size_t workspace_bytes,
                     void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int32_t st = validate(d);
   if (st) return st;
   if (d->sq_local == 0) return CP_ATTN_OK;
@@ -550,11 +571,21 @@ int32_t cp_attn_fwd(const cp_attn_desc *d, const void *q, const void *k, const v
   if (!aligned16(q) || !aligned16(out) || (d->skv > 0 && (!aligned16(k) || !aligned16(v))))
     return CP_ATTN_ERR_ALIGNMENT;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return CP_ATTN_ERR_ALIGNMENT;
+  const size_t need = mask_rowbits_bytes(d);
+  if (!mask_rowbits_grid_ok(d)) return CP_ATTN_ERR_UNSUPPORTED;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CP_ATTN_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return CP_ATTN_ERR_ALIGNMENT;
   Share s;
   make_share(d, &s);
   FwdParams p;
   fill_fwd_params(d, s, &p);
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  if (need > 0) {
+    uint64_t *rb = static_cast<uint64_t *>(workspace);
+    p.mask_rowbits = rb;
+    if (launch_mask_rowbits(p.mask, p.m_sb, p.m_sh, p.m_ss, p.mb_batches, p.mb_heads, p.sq, p.skv, rb, stream))
+      return CP_ATTN_ERR_HIP;
+  }
   const int e = (d->dtype == CP_ATTN_BF16) ? launch_fwd_bf16(p, d->head_dim, stream)
                                            : launch_fwd_fp32(p, d->head_dim, stream);
   return e == 0 ? CP_ATTN_OK : CP_ATTN_ERR_HIP;
@@ -584,7 +615,8 @@ size_t bwd_workspace_bytes(const cp_attn_desc *d, bool allow_split) {
   make_share(d, &s);
   BwdParams p;
   fill_bwd_params(d, s, &p, allow_split);
-  return 2 * bwd_stat_bytes(d) + bwd_partial_bytes(p, d->head_dim) + bwd_mask_bits_bytes(d, p);
+  return 2 * bwd_stat_bytes(d) + bwd_partial_bytes(p, d->head_dim) + bwd_mask_bits_bytes(d, p) +
+         mask_rowbits_bytes(d);
 }
 
 int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void *v, const void *out,
@@ -605,10 +637,13 @@ int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void 
   fill_bwd_params(d, s, &p, allow_split);
   const size_t partial = bwd_partial_bytes(p, d->head_dim);
   const size_t bits = bwd_mask_bits_bytes(d, p);
-  const size_t need = 2 * bwd_stat_bytes(d) + partial + bits;
-  // The bit table's pass runs one workgroup per 256 keys, query tile and mask head.
-  if (bits > 0 && (int64_t)((d->skv + 255) / 256) * p.n_q_chunks * p.mb_tpc * p.mb_batches * p.mb_heads > INT32_MAX)
+  const size_t rowbits = mask_rowbits_bytes(d);
+  const size_t need = 2 * bwd_stat_bytes(d) + partial + bits + rowbits;
+  // The bit tables' passes run one workgroup per 256 keys, query tile and
+  // mask head, and per 256 row words.
+  if (bits > 0 && !fits_grid((int64_t)((d->skv + 255) / 256) * p.n_q_chunks * p.mb_tpc * p.mb_batches * p.mb_heads, 256))
     return CP_ATTN_ERR_UNSUPPORTED;
+  if (!mask_rowbits_grid_ok(d)) return CP_ATTN_ERR_UNSUPPORTED;
   if (d->sq_local > 0 && (!q || !out || !lse || !dout || !dq)) return CP_ATTN_ERR_NULL_PTR;
   if (d->skv > 0 && (!k || !v || !dk || !dv)) return CP_ATTN_ERR_NULL_PTR;
   if (need > 0 && (!workspace || workspace_bytes < need)) return CP_ATTN_ERR_WORKSPACE;
@@ -624,6 +659,8 @@ int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void 
     p.kv_partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d));
   if (bits > 0)
     p.mask_bits = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d) + partial);
+  if (rowbits > 0)   // written by the backward's first pass
+    p.mask_rowbits = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d) + partial + bits);
   void *const *ev = n_events == 4 ? events : nullptr;
   const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream, ev)
                                            : launch_bwd_fp32(p, d->head_dim, stream, ev);

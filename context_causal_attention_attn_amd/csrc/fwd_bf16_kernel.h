@@ -160,12 +160,18 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   }
   const int64_t kv_pos0 = p.kv.pos[0];
   // User mask: this lane's mask row per row block (rows past the item's last
-  // read its last row, like Q).
+  // read its last row, like Q). A boolean mask is read from its row-bit table
+  // instead: the row's word of key tile 0 (those of tile kt follow kt * sq
+  // words on).
   const uint8_t *mrow[QB];
   if constexpr (UMASK) {
+    static_assert(BN == 64, "row-bit words cover 64-key tiles");
+    const int64_t bh = (int64_t)(p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? head : 0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      mrow[qb] = p.mask + b * p.m_sb + head * p.m_sh + (int64_t)local_row[qb] * p.m_ss;
+      mrow[qb] = p.mask_add ? p.mask + b * p.m_sb + head * p.m_sh + (int64_t)local_row[qb] * p.m_ss
+                            : reinterpret_cast<const uint8_t *>(p.mask_rowbits + bh * p.mb_ktiles * p.sq +
+                                                                local_row[qb]);
   }
   // Packed sequences: each of this lane's rows sees keys from its sequence's
   // start (the last bound <= its position) on, as a key row index (lo_key);
@@ -428,6 +434,17 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // The S^T product above reads K stage 0 as an odd "step -1" would: K of
   // tile 4 refills that stage in step 1.
   __syncthreads();
+  // Boolean user mask: this lane's rows' words of the row-bit table for the
+  // tile the next step masks, read a step ahead (16 bits per row: keys
+  // 16*kb + 4*grp + i at bit 16*grp + 4*kb + i).
+  uint64_t rbits[QB];
+  if constexpr (UMASK) {
+    if (!p.mask_add && ntiles > 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)t0 * p.sq * 8);
+    }
+  }
 
   // One step on tile j (J4 = j % 4): PV(j-1) and S^T(j+1) on the matrix
   // core, softmax of S^T(j) on the VALU, and K of tile j+3 and V of tile j+1
@@ -505,12 +522,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
           }
         }
         if constexpr (UMASK) {
-          // ... and the user mask: the 4 bytes (or 4 floats) of this lane's
+          // ... and the user mask. Additive: the 4 floats of this lane's
           // keys 16*kb + 4*grp .. +3 per block, every read issued before any
-          // is used. In the ragged last tile keys past the end read nothing
-          // (0: hidden, or no bias on a score the range mask hid).
-          const bool full = kt * BN + BN <= p.skv;
+          // is used; in the ragged last tile keys past the end read nothing
+          // (no bias on a score the range mask hid).
           if (p.mask_add) {
+            const bool full = kt * BN + BN <= p.skv;
             // Additive: in the raw score's units (value / softmax_scale); a
             // value at or below kMaskHide hides the key.
             const float inv = 1.0f / p.scale;
@@ -532,24 +549,16 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
               for (int i = 0; i < 4; ++i)
                 sacc[qb][kb][i] = a[kb][i] <= kMaskHide ? -INFINITY : fmaf(a[kb][i], inv, sacc[qb][kb][i]);
           } else {
-            uint32_t w[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              const int k0 = kt * BN + 16 * kb + 4 * grp;
-              if (full) {
-                w[kb] = *reinterpret_cast<const uint32_t *>(mrow[qb] + k0);
-              } else {
-                w[kb] = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (k0 + i < p.skv) w[kb] |= (uint32_t)mrow[qb][k0 + i] << (8 * i);
-              }
-            }
+            // Boolean: this row's 16 bits of the tile (read in the step
+            // before), then the next tile's word.
+            const uint32_t w16 = (uint32_t)(rbits[qb] >> (16 * grp));
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                sacc[qb][kb][i] = ((w[kb] >> (8 * i)) & 0xffu) ? sacc[qb][kb][i] : -INFINITY;
+                sacc[qb][kb][i] = ((w16 >> (4 * kb + i)) & 1u) ? sacc[qb][kb][i] : -INFINITY;
+            if (j + 1 < ntiles)
+              rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)(kt + 1) * p.sq * 8);
           }
         }
       }

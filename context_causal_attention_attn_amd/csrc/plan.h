@@ -86,6 +86,11 @@ struct FwdParams {
   // longest causal rows start first); chunk_idx maps back to local order.
   int64_t chunk_pos[kMaxQChunks];
   int32_t chunk_idx[kMaxQChunks];
+  // A boolean user mask as row bits (bf16; NULL otherwise): word
+  // [(bm * mb_heads + hm) * mb_ktiles + kt][row], bit 16*g + 4*kb + i for key
+  // 64*kt + 16*kb + 4*g + i (see launch_mask_rowbits).
+  const uint64_t *mask_rowbits;
+  int32_t mb_batches, mb_heads, mb_ktiles;
 };
 
 // Geometry derived from a validated descriptor.
@@ -176,6 +181,10 @@ struct BwdParams {
   // chunk end); bm, hm index the mask's batch and head (0 where it broadcasts).
   uint64_t *mask_bits;
   int32_t mb_batches, mb_heads, mb_tpc;
+  // The same mask as row bits for the query-stationary kernel (FwdParams::
+  // mask_rowbits' layout; NULL: none).
+  const uint64_t *mask_rowbits;
+  int32_t mb_ktiles;
 };
 
 void fill_fwd_params(const cp_attn_desc *d, const Share &s, FwdParams *p);
@@ -195,6 +204,11 @@ int64_t fwd_grid_size(const FwdParams &p);
 
 // Launchers (defined with their kernels); return a hipError_t as int.
 int launch_fwd_bf16(const FwdParams &p, int head_dim, void *stream);
+// Writes a boolean mask [batches][heads][sq][skv] (byte strides m_sb, m_sh,
+// m_ss; batches/heads 1 where it broadcasts) as row bits (FwdParams::
+// mask_rowbits): batches * heads * ceil(skv/64) * sq 64-bit words.
+int launch_mask_rowbits(const uint8_t *mask, int64_t m_sb, int64_t m_sh, int64_t m_ss, int32_t batches,
+                        int32_t heads, int32_t sq, int32_t skv, uint64_t *bits, void *stream);
 // Per-mode instantiations (0: natural order, 1: KV chunk table, 2: packed
 // sequences, 3: user mask), each compiled in a file of its own.
 int launch_fwd_bf16_m0(const FwdParams &p, int head_dim, void *stream);

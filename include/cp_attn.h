@@ -238,14 +238,17 @@ int32_t cp_attn_validate(const cp_attn_desc *desc);
  * cp_attn_validate's, NULL_PTR for `pairs`. Host only. */
 int32_t cp_attn_share_pairs(const cp_attn_desc *desc, int64_t *pairs);
 
-/* Bytes of device workspace cp_attn_fwd (backward == 0: none) or cp_attn_bwd
- * (backward != 0) needs for this descriptor; may be 0. The backward's holds
- * the per-row statistics of the recompute-based gradient of [CP-migration]
- * §6.1 (-Delta and LSE*log2(e)), for shares whose key tiles are split over
- * several workgroups their float32 partial dK/dV, and with a boolean user
- * mask (bf16) the mask as bits: one 64-bit word per key, 64-row query tile
- * and mask batch/head, i.e. about an eighth of the mask's bytes. Errors:
- * cp_attn_validate's, NULL_PTR for `bytes`. Host only. */
+/* Bytes of device workspace cp_attn_fwd (backward == 0) or cp_attn_bwd
+ * (backward != 0) needs for this descriptor; may be 0. With a boolean user
+ * mask (bf16) both hold the mask as row bits, one 64-bit word per query row,
+ * 64-key tile and mask batch/head (about an eighth of the mask's bytes);
+ * the forward needs nothing else. The backward's also holds the per-row
+ * statistics of the recompute-based gradient of [CP-migration] §6.1 (-Delta
+ * and LSE*log2(e)), for shares whose key tiles are split over several
+ * workgroups their float32 partial dK/dV, and with a boolean user mask the
+ * mask's column bits too: one 64-bit word per key, 64-row query tile and
+ * mask batch/head. Errors: cp_attn_validate's, NULL_PTR for `bytes`. Host
+ * only. */
 int32_t cp_attn_workspace_bytes(const cp_attn_desc *desc, int32_t backward, size_t *bytes);
 
 /* Work-list statistics of the forward tile scheduler (host only), for tests
@@ -274,10 +277,15 @@ int32_t cp_attn_plan_stats_fwd(const cp_attn_desc *desc, cp_attn_plan_stats *sta
  * q, k, v: device pointers of `dtype`, caller-owned, read only; out: device,
  * `dtype`, o_strides, written; lse: device float32 [batch, hq, sq_local]
  * contiguous, written. Pointers must be 16-byte aligned (lse 4-byte).
- * Needs no workspace (workspace may be NULL when cp_attn_workspace_bytes
- * reports 0). Returns CP_ATTN_OK once the kernel is enqueued on `stream`;
- * validation errors (cp_attn_validate's, NULL_PTR, ALIGNMENT) return before
- * anything is enqueued or written; CP_ATTN_ERR_HIP if the launch fails.
+ * The workspace (cp_attn_workspace_bytes with backward == 0) is caller-owned
+ * device memory, 16-byte aligned, whose contents on entry do not matter; only
+ * a bf16 share with a boolean user mask needs one (it holds the mask as row
+ * bits, packed by a first kernel), else workspace may be NULL. Returns
+ * CP_ATTN_OK once the kernels are enqueued on `stream`; validation errors
+ * (cp_attn_validate's, NULL_PTR, ALIGNMENT, UNSUPPORTED for a bit table of
+ * 2^32 words or more) and CP_ATTN_ERR_WORKSPACE (needed and NULL or too
+ * small) return before anything is enqueued or written; CP_ATTN_ERR_HIP if a
+ * launch fails.
  * Deterministic: the same inputs give bitwise the same outputs.
  */
 int32_t cp_attn_fwd(const cp_attn_desc *desc, const void *q, const void *k, const void *v,
@@ -337,7 +345,7 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *desc, const void *q, const void *k
  * first call on a device looks up that device's array once.
  * batch * hq * sq_local above CP_ATTN_NOALLOC_MAX_ROWS, or a share whose
  * workspace (cp_attn_workspace_bytes without split key tiles, e.g. with the
- * bit table of a large boolean user mask) exceeds the 16 MiB, returns
+ * bit tables of a large boolean user mask) exceeds the 16 MiB, returns
  * CP_ATTN_ERR_SCRATCH_LIMIT before anything is enqueued. `stream`'s device
  * (the current device for NULL) selects the array. Every call on one GPU
  * shares that GPU's array: calls that overlap on one GPU (different streams,

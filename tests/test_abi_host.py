@@ -229,33 +229,58 @@ def test_workspace_bytes():
     assert extra >= 0 and extra % unit == 0 and extra // unit in (0, 8, 24, 56)   # (parts - 1) x 8 tiles
 
 
-def test_workspace_holds_the_bit_table_of_a_boolean_mask():
-    """bf16 backward with a boolean user mask: the workspace also holds one
-    64-bit word per key, 64-row query tile of each chunk and mask batch/head
-    (256-byte aligned); an additive mask or the fp32 path adds none."""
-    def extra(**kw):
+def _aligned(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_holds_the_bit_tables_of_a_boolean_mask():
+    """bf16 with a boolean user mask. The forward's workspace holds the row
+    table: one 64-bit word per query row, 64-key tile and mask batch/head. The
+    backward's also holds the column table, one word per key, 64-row query
+    tile of each chunk and mask batch/head, besides the row table (each
+    256-byte aligned). An additive mask or the fp32 path adds none."""
+    def extra(backward, **kw):
         d0, dm = desc(**kw), desc(**kw)
         dm.desc.attn_mask = 1 << 40
-        return cp_attn_workspace_bytes(dm, True) - cp_attn_workspace_bytes(d0, True), dm
-    # contiguous 500 rows: 8 query tiles; broadcast mask: one batch, one head
-    e, _ = extra()
-    assert e == (8 * 2000 * 8 + 255) // 256 * 256
+        return cp_attn_workspace_bytes(dm, backward) - cp_attn_workspace_bytes(d0, backward)
+    # contiguous 500 rows: 8 query tiles; 2000 keys: 32 key tiles;
+    # broadcast mask: one batch, one head
+    rows = _aligned(32 * 500 * 8)
+    assert extra(False) == rows
+    assert extra(True) == _aligned(8 * 2000 * 8) + rows
     # Head-Tail, two chunks of 250 rows: 4 tiles each; a per-head mask (stride != 0)
     d = desc(layout="head_tail", q_chunk_pos=[250, 1750], sq_local=500)
-    d0 = cp_attn_workspace_bytes(d, True)
+    f0, b0 = cp_attn_workspace_bytes(d, False), cp_attn_workspace_bytes(d, True)
     d.desc.attn_mask = 1 << 40
     d.desc.mask_strides[1] = 500 * 2000
     d.desc.mask_strides[2] = 2000
-    assert cp_attn_workspace_bytes(d, True) - d0 == (8 * 2 * 4 * 2000 * 8 + 255) // 256 * 256
+    rows = _aligned(8 * 32 * 500 * 8)
+    assert cp_attn_workspace_bytes(d, False) - f0 == rows
+    assert cp_attn_workspace_bytes(d, True) - b0 == _aligned(8 * 2 * 4 * 2000 * 8) + rows
     # additive: none
-    d = desc()
-    d0 = cp_attn_workspace_bytes(d, True)
-    d.desc.attn_mask = 1 << 40
-    d.desc.mask_additive = 1
-    assert cp_attn_workspace_bytes(d, True) == d0
+    for backward in (False, True):
+        d = desc()
+        d0 = cp_attn_workspace_bytes(d, backward)
+        d.desc.attn_mask = 1 << 40
+        d.desc.mask_additive = 1
+        assert cp_attn_workspace_bytes(d, backward) == d0
     # fp32: none
-    e, _ = extra(dtype=1, head_dim=64, q_strides=(0, 0, 64), kv_strides=(0, 0, 64), o_strides=(0, 0, 64))
-    assert e == 0
+    kw = dict(dtype=1, head_dim=64, q_strides=(0, 0, 64), kv_strides=(0, 0, 64), o_strides=(0, 0, 64))
+    assert extra(False, **kw) == 0 and extra(True, **kw) == 0
+
+
+def test_fwd_with_a_boolean_mask_needs_its_workspace():
+    """cp_attn_fwd refuses a bf16 boolean-mask share whose workspace is
+    missing, short or misaligned, before any HIP call."""
+    lib = _lib.load()
+    fake = 1 << 40
+    d = desc()
+    d.desc.attn_mask = fake
+    need = cp_attn_workspace_bytes(d, False)
+    args = (d.ref(), fake, fake, fake, fake, fake)
+    assert lib.cp_attn_fwd(*args, None, 0, None) == -6
+    assert lib.cp_attn_fwd(*args, fake, need - 8, None) == -6
+    assert lib.cp_attn_fwd(*args, fake + 8, need, None) == -9
 
 
 def test_noalloc_rejects_a_bit_table_beyond_its_scratch():

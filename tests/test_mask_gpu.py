@@ -50,6 +50,12 @@ def make_mask(kind, osh, B, Hq, S, rng, dtype="bf16"):
         # whose LSE gate is 1e-4 absolute, 100: float32 keeps 1e-5 there).
         m[:, :, :, S // 2:S // 2 + 4] = 1000.0 if dtype == "bf16" else 100.0
         m[:, :, ::37] = -1e9
+    elif kind == "random_b1":       # random per head, shared by the batch
+        m = rng.random((1, Hq, q_pos.size, S)) < 0.75
+        m[:, :, ::37] = False
+    elif kind == "random_11":       # one random mask for every batch and head
+        m = rng.random((1, 1, q_pos.size, S)) < 0.75
+        m[:, :, ::37] = False
     else:                           # random per head, 25 % hidden, some rows fully hidden
         m = rng.random((B, Hq, q_pos.size, S)) < 0.75
         m[:, :, ::37] = False
@@ -62,6 +68,8 @@ CASES = [
     ("window", "head_tail", 2048, 8, 2, 128, 4, "bf16"),
     ("random", "contiguous", 1000, 4, 2, 64, 2, "bf16"),     # ragged key count (1000)
     ("random", "head_tail", 1024, 4, 4, 128, 4, "bf16"),
+    ("random_b1", "head_tail", 1000, 8, 2, 128, 2, "bf16"),   # per-head mask broadcast over the batch
+    ("random_11", "contiguous", 1100, 4, 2, 64, 2, "bf16"),   # one mask for all batches and heads
     ("random", "head_tail", 512, 2, 1, 64, 4, "fp32"),
     ("additive", "head_tail", 2048, 8, 2, 128, 4, "bf16"),
     ("additive", "contiguous", 1000, 4, 2, 64, 2, "bf16"),    # ragged key count
@@ -109,5 +117,5 @@ def test_user_mask_fwd_bwd_all_ranks(case):
         print(f"mask {case} r{r}: out {err_o:.3e} lse {err_l:.3e} dq {errs[0]:.3e} dk {errs[1]:.3e} "
               f"dv {errs[2]:.3e}", flush=True)
         assert err_o <= tol_o and err_l <= tol_l and max(errs) <= tol_g
-        if mask_kind in ("random", "additive", "padding"):
+        if mask_kind in ("random", "random_b1", "random_11", "additive", "padding"):
             assert torch.all(out[:, :, ::37] == 0) and torch.all(dq[:, :, ::37] == 0)
