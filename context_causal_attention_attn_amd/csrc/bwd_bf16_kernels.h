@@ -615,7 +615,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                   for (int i = 0; i < 4; ++i)
-                    sacc[rb][kn][i] = ((w16 >> (4 * rb + i)) & 1u) ? sacc[rb][kn][i] : -INFINITY;
+                    sacc[rb][kn][i] = keep_if_bit(sacc[rb][kn][i], w16, 4 * rb + i);
               }
             }
           }
@@ -1273,7 +1273,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                scur[h][qb][i] = ((w8 >> (4 * h + i)) & 1u) ? scur[h][qb][i] : -INFINITY;
+                scur[h][qb][i] = keep_if_bit(scur[h][qb][i], w8, 4 * h + i);
             if (KB == 1 && (sb >> 1) + 1 < t0 + ntiles)
               rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)((sb >> 1) + 1) * p.sq * 8);
           }

@@ -556,7 +556,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                sacc[qb][kb][i] = ((w16 >> (4 * kb + i)) & 1u) ? sacc[qb][kb][i] : -INFINITY;
+                sacc[qb][kb][i] = keep_if_bit(sacc[qb][kb][i], w16, 4 * kb + i);
             if (j + 1 < ntiles)
               rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)(kt + 1) * p.sq * 8);
           }

@@ -71,6 +71,14 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 // Sum and max over the four lanes that hold the same accumulator column
 // (lanes l, l^16, l^32, l^48).
+// s where bit `bit` of w is set, else -inf: the bit sign-extended into a
+// whole-word mask that then picks between the two bit patterns (two vector
+// instructions, where a compare and a select take three).
+__device__ __forceinline__ float keep_if_bit(float s, uint32_t w, int bit) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)w, bit, 1);
+  return __uint_as_float((__float_as_uint(s) & m) | (0xff800000u & ~m));
+}
+
 __device__ __forceinline__ float quad_sum(float x) {
   x += __shfl_xor(x, 16);
   return x + __shfl_xor(x, 32);
