@@ -170,7 +170,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   constexpr int X_OFF = O_OFF + OSTG * QTILE * 2;                    // [2][4 waves][NXOP][64 lanes] bf16x8
   constexpr int L_OFF = X_OFF + 2 * 4 * 64 * XPER * 2;               // [QSTG][QT] LSE*log2(e)
   constexpr int DL_OFF = L_OFF + QSTG * QT * 4;                      // [QSTG][QT] Delta
-  constexpr int LDS_BYTES = DL_OFF + QSTG * QT * 4;
+  constexpr int MB_OFF = DL_OFF + QSTG * QT * 4;                     // [QSTG][BK] mask bit words
+  constexpr int LDS_BYTES = MB_OFF + (UMASK ? QSTG * BK * 8 : 0);
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(QT == 64 && XPER == 32, "step shape");
   using T = Tile16<D>;
@@ -384,10 +385,24 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   cq.soff = offset(wst, c0.c, c0.t, c0.h);
   Cursor co = c0;   // step whose dO tile the next dO load fetches
   co.off = offset(wo, c0.c, c0.t, c0.h);
+  // A boolean user mask's bit-table words of step u's query tile for this
+  // P wavefront's 32 keys (two lanes per word; keys past the end read the
+  // last key's word), beside the statistics.
+  auto dma_bits = [&](const Cursor &u, int stage) {
+    if constexpr (UMASK) {
+      if (p.mask_add) return;
+      const int bhm = (p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? hk * p.group + u.h : 0);
+      const int64_t tile = (int64_t)bhm * p.n_q_chunks * p.mb_tpc + u.c * p.mb_tpc + u.t;
+      const int k0 = min(wkey0, p.skv - 1);
+      const uint32_t voff = (uint32_t)((min(wkey0 + (lane >> 1), p.skv - 1) - k0) * 8 + 4 * (lane & 1));
+      dma4(lds0 + MB_OFF + stage * BK * 8 + kw * 32 * 8, voff, p.mask_bits + tile * p.skv + k0);
+    }
+  };
   auto load_q = [&](int s) {   // Q tile (and statistics) of step s = cq's
     const int st = s % QSTG;
     dma_tile(cq, true, Q_OFF + st * QTILE * 2);
     dma_stats(cq, st);
+    dma_bits(cq, st);
     advance(cq, wq, true);
   };
   auto load_o = [&](int s) {   // dO tile of step s = co's
@@ -436,6 +451,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   // at lstat, -Delta at dstat).
   uint32_t lstat = lds0 + L_OFF + 16 * grp, dstat = lds0 + DL_OFF + 16 * grp;
   asm volatile("" : "+v"(lstat), "+v"(dstat));
+  // This P wavefront's mask bit words of stage 0 (boolean user mask).
+  const uint32_t mbase = lds0 + MB_OFF + kw * 32 * 8;
 
   // This lane's key rows of K (P role) or V (dS role): the B operands.
   bf16x8 kvf[KN][KSTEPS];
@@ -605,12 +622,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
               } else {
                 // ... and allowed by a boolean user mask: one word of its bit
                 // table per key and query tile, bit 16grp + 4rb + i for row
-                // 16rb + 4grp + i (a key past the end reads the last key's:
-                // hidden above).
-                const int bh = (p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? hk * p.group + cs.h : 0);
-                const int64_t tile = (int64_t)bh * p.n_q_chunks * p.mb_tpc + cs.c * p.mb_tpc + cs.t;
-                const uint64_t word = p.mask_bits[tile * p.skv + min(my_key[kn], p.skv - 1)];
-                const uint32_t w16 = (uint32_t)(word >> (16 * grp));
+                // 16rb + 4grp + i (a key past the end has the last key's:
+                // hidden above), staged in LDS with the step's statistics;
+                // this lane reads its 16 bits.
+                const uint32_t w16 = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t *>(
+                    (uintptr_t)(mbase + st * BK * 8 + (16 * kn + col) * 8 + 2 * grp));
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -891,7 +907,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int STG = 4;                       // ring stages (K and V)
   constexpr int K_OFF = 0;
   constexpr int V_OFF = STG * TILE * 2;
-  constexpr int LDS_BYTES = 2 * STG * TILE * 2;
+  constexpr int MB_OFF = 2 * STG * TILE * 2;   // [STG][waves][32 rows] row-bit words (boolean mask)
+  constexpr int MB_WAVE = kDqWaveRows * 8;
+  constexpr int LDS_BYTES = MB_OFF + (UMASK ? STG * kDqWaves * MB_WAVE : 0);
   static_assert(BN == 64 && QB == 2 && LDS_BYTES <= 160 * 1024, "tile shape");
   using T = Tile16<D>;
 
@@ -958,20 +976,17 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // User mask: this lane's mask row per row block (lanes past the wave's last
   // row read the item's first row, like Q).
   // A boolean mask comes as row bits instead (FwdParams::mask_rowbits'
-  // layout; mrow then points at the row's word of key tile 0, those of tile
-  // kt following kt * sq words on): the lane's 16 bits of a 64-key tile at
-  // bit 16*grp + 4*kb + i for key 16*kb + 4*grp + i, kb = 2 * (32-key block)
-  // + half; each tile's word is read during the tile before.
+  // layout): each tile's words of the wavefront's rows are staged in LDS with
+  // the tile's K and V; the lane's 16 bits of a 64-key tile lie at bit
+  // 16*grp + 4*kb + i for key 16*kb + 4*grp + i, kb = 2 * (32-key block) +
+  // half.
   const uint8_t *mrow[QB];
-  uint64_t rbits[QB];
   if constexpr (UMASK) {
     static_assert(BN == 64, "row-bit words cover 64-key tiles");
-    const int64_t bh = (int64_t)(p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? head : 0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int mr = qvalid[qb] ? local_row[qb] : chunk * p.chunk_len + item_row0;
-      mrow[qb] = p.mask_add ? p.mask + b * p.m_sb + head * p.m_sh + (int64_t)mr * p.m_ss
-                            : reinterpret_cast<const uint8_t *>(p.mask_rowbits + bh * p.mb_ktiles * p.sq + mr);
+      mrow[qb] = p.mask + b * p.m_sb + head * p.m_sh + (int64_t)mr * p.m_ss;
     }
   }
   // Packed sequences, as in the forward kernel: this lane's rows see keys
@@ -1063,9 +1078,28 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
   };
+  auto dma4 = [](uint32_t m0, uint32_t voff, const void *sbase) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
+  };
+  // Boolean user mask: the row-bit words of the item's rows (tile 0), two
+  // lanes per word of the wavefront's rows (rows past its last read the
+  // item's first row).
+  const uint64_t *rb_item = nullptr;
+  uint32_t rb_voff = 0;
+  if constexpr (UMASK) {
+    const int64_t bhm = (int64_t)(p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? head : 0);
+    rb_item = p.mask_rowbits + bhm * p.mb_ktiles * p.sq + chunk * p.chunk_len + item_row0;
+    const int w = lane >> 1;
+    rb_voff = (uint32_t)((w < wrows ? wrow0 + w : 0) * 8 + 4 * (lane & 1));
+  }
   // K and V of storage tile kt (adj: its KV chunk's extra elements) into
-  // ring stage st.
+  // ring stage st (and the tile's mask words).
   auto dma = [&](int kt, int64_t adj, int st) {
+    if constexpr (UMASK) {
+      if (!p.mask_add) dma4(lds0 + MB_OFF + (st * kDqWaves + wave) * MB_WAVE, rb_voff, rb_item + (int64_t)kt * p.sq);
+    }
     const uint32_t kd = dst0 + K_OFF + 2 * st * TILE;
     const uint32_t vd = dst0 + V_OFF + 2 * st * TILE;
     const char *kt_base = reinterpret_cast<const char *>(kbase + (int64_t)kt * tile_stride + adj);
@@ -1098,6 +1132,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // column 16db + col); stage, key block and k-step are immediates.
   // (Separate K and V bases: the V ring starts 64 KiB in, beyond the reach
   // of an immediate.)
+  // This lane's byte of its row's mask word (boolean mask) at stage 0, row
+  // block 0 and 32-key block 0, beyond the reach of an immediate as well.
+  uint32_t mbits = lds0 + MB_OFF + wave * MB_WAVE + col * 8 + 2 * grp;
   uint32_t kaddr[KSTEPS], vaddr[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
@@ -1266,16 +1303,14 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
               for (int i = 0; i < 4; ++i)
                 scur[h][qb][i] = a[h][i] <= kMaskHide ? -INFINITY : fmaf(a[h][i], inv, scur[h][qb][i]);
           } else {
-            // Boolean: the block's 8 bits of the tile's word; the second
-            // block then reads the next tile's word.
-            const uint32_t w8 = (uint32_t)(rbits[qb] >> (16 * grp + 8 * KB));
+            // Boolean: the block's 8 bits of the row's word of the tile.
+            const uint32_t w8 = *reinterpret_cast<const __attribute__((address_space(3))) uint8_t *>(
+                (uintptr_t)(mbits + J4 * kDqWaves * MB_WAVE + 16 * qb * 8 + KB));
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 scur[h][qb][i] = keep_if_bit(scur[h][qb][i], w8, 4 * h + i);
-            if (KB == 1 && (sb >> 1) + 1 < t0 + ntiles)
-              rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)((sb >> 1) + 1) * p.sq * 8);
           }
         }
       }
@@ -1354,6 +1389,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(taddr[db]));
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]), "+v"(vaddr[s]));
+    if constexpr (UMASK) asm volatile("" : "+v"(mbits));
     TileRef t{t0 + J, kv_pos0, 0};
     if constexpr (MKV) {
       t = t_cur;
@@ -1366,12 +1402,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     wait_vmem_all();
     __syncthreads();
   };
-  if constexpr (UMASK) {
-    if (!p.mask_add && ntiles > 0) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)t0 * p.sq * 8);
-    }
-  }
   for (int J = 0; J < ntiles; J += STG) {
     tile_step(IC<0>{}, J);
     if (J + 1 < ntiles) tile_step(IC<1>{}, J + 1);
