@@ -89,8 +89,13 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // that V of tile t-4 left in step t-3: of any two consecutive steps one
   // ends in a barrier, so every load is published before its tile is read
   // and starts after the previous occupant's last reader passed a barrier.
-  __shared__ __attribute__((aligned(16))) __bf16 smem[(KSTAGES + VSTAGES) * TILE];
-  static_assert((KSTAGES + VSTAGES) * TILE * 2 <= 128 * 1024, "LDS budget");
+  // A boolean user mask's row-bit words follow the rings: per K stage, the
+  // words of each wavefront's 32 rows for that stage's tile.
+  constexpr int MB_OFF = (KSTAGES + VSTAGES) * TILE * 2;
+  constexpr int MB_WAVE = kFwdWaveRows * 8;
+  constexpr int LDS_BYTES = MB_OFF + (UMASK ? KSTAGES * NW * MB_WAVE : 0);
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  static_assert((KSTAGES + VSTAGES) * TILE * 2 <= 128 * 1024 && LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(KSTAGES >= K_AHEAD + 1 && VSTAGES >= V_AHEAD + 3 && K_AHEAD >= 3 && V_AHEAD >= 1 &&
                     UNROLL % KSTAGES == 0 && UNROLL % VSTAGES == 0 && UNROLL % 2 == 0,
                 "ring depths for one barrier per two steps");
@@ -161,17 +166,13 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const int64_t kv_pos0 = p.kv.pos[0];
   // User mask: this lane's mask row per row block (rows past the item's last
   // read its last row, like Q). A boolean mask is read from its row-bit table
-  // instead: the row's word of key tile 0 (those of tile kt follow kt * sq
-  // words on).
+  // instead, staged in LDS with the K tiles.
   const uint8_t *mrow[QB];
   if constexpr (UMASK) {
     static_assert(BN == 64, "row-bit words cover 64-key tiles");
-    const int64_t bh = (int64_t)(p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? head : 0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      mrow[qb] = p.mask_add ? p.mask + b * p.m_sb + head * p.m_sh + (int64_t)local_row[qb] * p.m_ss
-                            : reinterpret_cast<const uint8_t *>(p.mask_rowbits + bh * p.mb_ktiles * p.sq +
-                                                                local_row[qb]);
+      mrow[qb] = p.mask + b * p.m_sb + head * p.m_sh + (int64_t)local_row[qb] * p.m_ss;
   }
   // Packed sequences: each of this lane's rows sees keys from its sequence's
   // start (the last bound <= its position) on, as a key row index (lo_key);
@@ -313,7 +314,27 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
       }
     }
   };
-  auto dma_k = [&](int kt, int64_t adj, int stage) { dma(kt, adj, false, dst0 + 2 * stage * TILE); };
+  // Boolean user mask: the row-bit words of the item's rows (tile 0), two
+  // lanes per word of the wavefront's rows (rows past the item's last read
+  // its last row); K stage st also receives tile kt's words.
+  auto dma4 = [](uint32_t m0, uint32_t voff, const void *sbase) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
+  };
+  const uint64_t *rb_item = nullptr;
+  uint32_t rb_voff = 0;
+  if constexpr (UMASK) {
+    const int64_t bhm = (int64_t)(p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? head : 0);
+    rb_item = p.mask_rowbits + bhm * p.mb_ktiles * p.sq + chunk * p.chunk_len + item_row0;
+    rb_voff = (uint32_t)(min(wrow0 + (lane >> 1), item_rows - 1) * 8 + 4 * (lane & 1));
+  }
+  auto dma_k = [&](int kt, int64_t adj, int stage) {
+    if constexpr (UMASK) {
+      if (!p.mask_add) dma4(lds0 + MB_OFF + (stage * NW + wave) * MB_WAVE, rb_voff, rb_item + (int64_t)kt * p.sq);
+    }
+    dma(kt, adj, false, dst0 + 2 * stage * TILE);
+  };
   auto dma_v = [&](int kt, int64_t adj, int stage) { dma(kt, adj, true, dst0 + 2 * (KSTAGES + stage) * TILE); };
 
   f32x4 oacc[QB][DB];
@@ -394,7 +415,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // not hold NaN bit patterns: clear it.
   {
     constexpr int VEC = TILE / 8;
-    u32x4 *vlast = reinterpret_cast<u32x4 *>(smem + (KSTAGES + VSTAGES - 1) * TILE);
+    u32x4 *vlast = reinterpret_cast<u32x4 *>(smem + 2 * (KSTAGES + VSTAGES - 1) * TILE);
     for (int i = tid; i < VEC; i += NT) vlast[i] = u32x4{0u, 0u, 0u, 0u};
   }
   // Scores and probabilities alternate between two register sets by step
@@ -434,17 +455,10 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // The S^T product above reads K stage 0 as an odd "step -1" would: K of
   // tile 4 refills that stage in step 1.
   __syncthreads();
-  // Boolean user mask: this lane's rows' words of the row-bit table for the
-  // tile the next step masks, read a step ahead (16 bits per row: keys
-  // 16*kb + 4*grp + i at bit 16*grp + 4*kb + i).
-  uint64_t rbits[QB];
-  if constexpr (UMASK) {
-    if (!p.mask_add && ntiles > 0) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)t0 * p.sq * 8);
-    }
-  }
+  // Boolean user mask: this lane's 16 bits of its row's word (keys
+  // 16*kb + 4*grp + i at bit 16*grp + 4*kb + i) in K stage 0, row block 0;
+  // beyond the reach of an immediate from LDS 0.
+  uint32_t mbits = lds0 + MB_OFF + wave * MB_WAVE + col * 8 + 2 * grp;
 
   // One step on tile j (J4 = j % 4): PV(j-1) and S^T(j+1) on the matrix
   // core, softmax of S^T(j) on the VALU, and K of tile j+3 and V of tile j+1
@@ -479,6 +493,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]));
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vaddr[db]));
+    if constexpr (UMASK) asm volatile("" : "+v"(mbits));
     int kt = t0 + j;
     int64_t tile_plo = kv_pos0 + (int64_t)kt * BN;
     if constexpr (MKV) {
@@ -549,16 +564,14 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
               for (int i = 0; i < 4; ++i)
                 sacc[qb][kb][i] = a[kb][i] <= kMaskHide ? -INFINITY : fmaf(a[kb][i], inv, sacc[qb][kb][i]);
           } else {
-            // Boolean: this row's 16 bits of the tile (read in the step
-            // before), then the next tile's word.
-            const uint32_t w16 = (uint32_t)(rbits[qb] >> (16 * grp));
+            // Boolean: this row's 16 bits of the tile.
+            const uint32_t w16 = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t *>(
+                (uintptr_t)(mbits + J4 * NW * MB_WAVE + 16 * qb * 8));
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 sacc[qb][kb][i] = keep_if_bit(sacc[qb][kb][i], w16, 4 * kb + i);
-            if (j + 1 < ntiles)
-              rbits[qb] = *reinterpret_cast<const uint64_t *>(mrow[qb] + (int64_t)(kt + 1) * p.sq * 8);
           }
         }
       }
