@@ -21,7 +21,8 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(blocks), dim3(256), 0, s, p);
   }
   if (p.mask_bits && p.skv > 0 && p.sq > 0) {
-    const int64_t blocks = (int64_t)((p.skv + 255) / 256) * p.n_q_chunks * p.mb_tpc * p.mb_batches * p.mb_heads;
+    const int64_t blocks = (int64_t)((p.skv + kMaskBitsBlockKeys - 1) / kMaskBitsBlockKeys) * p.n_q_chunks *
+                           p.mb_tpc * p.mb_batches * p.mb_heads;
     hipLaunchKernelGGL(bwd_mask_bits_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p);
   }
   if (p.mask_rowbits) {

@@ -76,14 +76,23 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // 1b. A boolean user mask as bits (see BwdParams::mask_bits): one thread per
-//     key and 64-row query tile, consecutive threads on consecutive keys (the
-//     mask's bytes of one row, and the table's words, are contiguous in keys).
+//     4 consecutive keys and 64-row query tile, consecutive threads on
+//     consecutive keys (the mask's bytes of one row, and the table's words,
+//     are contiguous in keys). A thread reads each row's 4 bytes as one
+//     32-bit word (rows start on 4-byte boundaries); a group that runs past
+//     the last key reads bytes.
 // ---------------------------------------------------------------------------
+constexpr int kMaskBitsKeys = kMaskBitsBlockKeys / 256;   // keys per thread of the column-bit pass
+
+__device__ __forceinline__ int col_bit(int r) { return 16 * ((r >> 2) & 3) + 4 * (r >> 4) + (r & 3); }
+
 __global__ void __launch_bounds__(256) bwd_mask_bits_kernel(const BwdParams p) {
-  const int nkb = (p.skv + 255) / 256;
+  constexpr int KPB = kMaskBitsBlockKeys;
+  static_assert(kMaskBitsKeys == 4, "one 32-bit word of bytes per row");
+  const int nkb = (p.skv + KPB - 1) / KPB;
   const int ntiles = p.n_q_chunks * p.mb_tpc;
   const int64_t blk = blockIdx.x;
-  const int key = (int)(blk % nkb) * 256 + threadIdx.x;
+  const int key = (int)(blk % nkb) * KPB + kMaskBitsKeys * (int)threadIdx.x;
   const int n = (int)((blk / nkb) % ntiles);
   const int bh = (int)(blk / ((int64_t)nkb * ntiles));
   if (key >= p.skv) return;
@@ -92,10 +101,46 @@ __global__ void __launch_bounds__(256) bwd_mask_bits_kernel(const BwdParams p) {
   const int bm = bh / p.mb_heads, hm = bh % p.mb_heads;
   const uint8_t *col = p.mask + bm * p.m_sb + hm * p.m_sh +
                        ((int64_t)c * p.chunk_len + (int64_t)t * kBwdBlockQ) * p.m_ss + key;
-  uint64_t w = 0;
-  for (int r = 0; r < rows; ++r)
-    if (col[(int64_t)r * p.m_ss]) w |= (uint64_t)1 << (16 * ((r >> 2) & 3) + 4 * (r >> 4) + (r & 3));
-  p.mask_bits[((int64_t)bh * ntiles + n) * p.skv + key] = w;
+  const int nk = min(kMaskBitsKeys, p.skv - key);
+  uint32_t lo[kMaskBitsKeys] = {}, hi[kMaskBitsKeys] = {};
+  // Bit of row r in the word of key i: from the top bit of byte i of v
+  // (set iff the byte is nonzero).
+  auto add_row = [&](uint32_t v, int r) {
+    const uint32_t nz = (((v & 0x7f7f7f7fu) + 0x7f7f7f7fu) | v) & 0x80808080u;
+    const int b = col_bit(r);
+#pragma unroll
+    for (int i = 0; i < kMaskBitsKeys; ++i) {
+      const uint32_t x = (nz >> (8 * i + 7)) & 1u;
+      if (b < 32) lo[i] |= x << b;
+      else hi[i] |= x << (b - 32);
+    }
+  };
+  if (nk == kMaskBitsKeys && rows == kBwdBlockQ) {
+#pragma unroll
+    for (int r0 = 0; r0 < kBwdBlockQ; r0 += 16) {
+      uint32_t v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = *reinterpret_cast<const uint32_t *>(col + (int64_t)(r0 + r) * p.m_ss);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) add_row(v[r], r0 + r);
+    }
+  } else {
+    for (int r = 0; r < rows; ++r) {
+      uint32_t v = 0;
+      for (int i = 0; i < nk; ++i) v |= (uint32_t)col[(int64_t)r * p.m_ss + i] << (8 * i);
+      const uint32_t nz = (((v & 0x7f7f7f7fu) + 0x7f7f7f7fu) | v) & 0x80808080u;
+      const int b = col_bit(r);
+      for (int i = 0; i < kMaskBitsKeys; ++i) {
+        const uint64_t x = (nz >> (8 * i + 7)) & 1u;
+        if (b < 32) lo[i] |= (uint32_t)(x << b);
+        else hi[i] |= (uint32_t)(x << (b - 32));
+      }
+    }
+  }
+  uint64_t *dst = p.mask_bits + ((int64_t)bh * ntiles + n) * p.skv + key;
+#pragma unroll
+  for (int i = 0; i < kMaskBitsKeys; ++i)
+    if (i < nk) dst[i] = ((uint64_t)hi[i] << 32) | lo[i];
 }
 
 // ---------------------------------------------------------------------------

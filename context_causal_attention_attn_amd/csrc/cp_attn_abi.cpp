@@ -639,9 +639,10 @@ int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void 
   const size_t bits = bwd_mask_bits_bytes(d, p);
   const size_t rowbits = mask_rowbits_bytes(d);
   const size_t need = 2 * bwd_stat_bytes(d) + partial + bits + rowbits;
-  // The bit tables' passes run one workgroup per 256 keys, query tile and
-  // mask head, and per 256 row words.
-  if (bits > 0 && !fits_grid((int64_t)((d->skv + 255) / 256) * p.n_q_chunks * p.mb_tpc * p.mb_batches * p.mb_heads, 256))
+  // The bit tables' passes run one workgroup per kMaskBitsBlockKeys keys,
+  // query tile and mask head, and per 256 row words.
+  if (bits > 0 && !fits_grid((int64_t)((d->skv + kMaskBitsBlockKeys - 1) / kMaskBitsBlockKeys) * p.n_q_chunks *
+                                 p.mb_tpc * p.mb_batches * p.mb_heads, 256))
     return CP_ATTN_ERR_UNSUPPORTED;
   if (!mask_rowbits_grid_ok(d)) return CP_ATTN_ERR_UNSUPPORTED;
   if (d->sq_local > 0 && (!q || !out || !lse || !dout || !dq)) return CP_ATTN_ERR_NULL_PTR;

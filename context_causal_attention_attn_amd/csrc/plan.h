@@ -121,6 +121,8 @@ inline int fwd_block_rows(int g) { return kFwdWaveRows * (kFwdWaves / item_heads
 // it can see.
 constexpr int kBwdBlockKV = 128;
 constexpr int kBwdBlockQ = 64;
+// Keys per 256-thread workgroup of the backward's column-bit pass.
+constexpr int kMaskBitsBlockKeys = 1024;
 constexpr int kDqBlockKV = 64;    // keys per tile of the query-stationary dQ kernel
 constexpr int kDqWaveRows = 32;   // query rows per wavefront of the dQ kernel
 constexpr int kDqWaves = 8;       // wavefronts per dQ workgroup
