@@ -199,8 +199,9 @@ def cp_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_chunk_pos: 
     a Ulysses all-to-all delivers, read in place; out then defaults to q's
     shape, the layout the reverse exchange sends. lse is always [B, Hq, Sq].
 
-    A boolean attn_mask is first packed into a bit table in device memory:
-    workspace, if given and large enough, holds it, else one is allocated.
+    A bf16 share's attn_mask is first packed into a bit table in device
+    memory: workspace, if given and large enough, holds it, else one is
+    allocated.
     """
     lib = _lib.load()
     _check_inputs(q, k, v)

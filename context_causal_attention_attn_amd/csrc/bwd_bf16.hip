@@ -20,15 +20,18 @@ int launch_d(const BwdParams &p, void *stream, void *const *events) {
     const int64_t blocks = (rows * 16 + 255) / 256;
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(blocks), dim3(256), 0, s, p);
   }
+  // The row bits first: for an additive mask that pass also decides whether
+  // the tables are used at all.
+  if (p.mask_rowbits) {
+    if (int e = launch_mask_rowbits(p.mask, p.m_sb, p.m_sh, p.m_ss, p.mb_batches, p.mb_heads, p.sq, p.skv,
+                                    p.mask_add != 0, const_cast<uint64_t *>(p.mask_rowbits),
+                                    const_cast<uint32_t *>(p.mask_flag), stream))
+      return e;
+  }
   if (p.mask_bits && p.skv > 0 && p.sq > 0) {
     const int64_t blocks = (int64_t)((p.skv + kMaskBitsBlockKeys - 1) / kMaskBitsBlockKeys) * p.n_q_chunks *
                            p.mb_tpc * p.mb_batches * p.mb_heads;
     hipLaunchKernelGGL(bwd_mask_bits_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p);
-  }
-  if (p.mask_rowbits) {
-    if (int e = launch_mask_rowbits(p.mask, p.m_sb, p.m_sh, p.m_ss, p.mb_batches, p.mb_heads, p.sq, p.skv,
-                                    const_cast<uint64_t *>(p.mask_rowbits), stream))
-      return e;
   }
   if (int e = mark(1)) return e;
   int e = p.mask ? launch_bwd_dkdv_m2(p, D, stream)

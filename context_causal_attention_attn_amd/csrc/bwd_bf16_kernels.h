@@ -75,12 +75,12 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 1b. A boolean user mask as bits (see BwdParams::mask_bits): one thread per
-//     4 consecutive keys and 64-row query tile, consecutive threads on
-//     consecutive keys (the mask's bytes of one row, and the table's words,
-//     are contiguous in keys). A thread reads each row's 4 bytes as one
-//     32-bit word (rows start on 4-byte boundaries); a group that runs past
-//     the last key reads bytes.
+// 1b. A user mask as bits (see BwdParams::mask_bits): one thread per 4
+//     consecutive keys and 64-row query tile, consecutive threads on
+//     consecutive keys (the mask's values of one row, and the table's words,
+//     are contiguous in keys). A thread reads each row's 4 bytes (an
+//     additive mask: 4 floats) as one 32-bit (16-byte) word; a group that
+//     runs past the last key reads them one by one.
 // ---------------------------------------------------------------------------
 constexpr int kMaskBitsKeys = kMaskBitsBlockKeys / 256;   // keys per thread of the column-bit pass
 
@@ -99,10 +99,42 @@ __global__ void __launch_bounds__(256) bwd_mask_bits_kernel(const BwdParams p) {
   const int c = n / p.mb_tpc, t = n % p.mb_tpc;
   const int rows = min(kBwdBlockQ, p.chunk_len - t * kBwdBlockQ);
   const int bm = bh / p.mb_heads, hm = bh % p.mb_heads;
-  const uint8_t *col = p.mask + bm * p.m_sb + hm * p.m_sh +
-                       ((int64_t)c * p.chunk_len + (int64_t)t * kBwdBlockQ) * p.m_ss + key;
   const int nk = min(kMaskBitsKeys, p.skv - key);
   uint32_t lo[kMaskBitsKeys] = {}, hi[kMaskBitsKeys] = {};
+  if (p.mask_add) {
+    // Additive: a key is kept unless its value is at most kMaskHide; a row's
+    // 4 values are one 16-byte read (rows start on 16-byte boundaries). The
+    // row-bit pass runs first: once it has marked the mask as holding other
+    // values than 0 and hiding ones, the table is not used.
+    if (__atomic_load_n(p.mask_flag, __ATOMIC_RELAXED) != 0) return;
+    const float *colf = reinterpret_cast<const float *>(
+        p.mask + bm * p.m_sb + hm * p.m_sh + ((int64_t)c * p.chunk_len + (int64_t)t * kBwdBlockQ) * p.m_ss) + key;
+    for (int r = 0; r < rows; ++r) {
+      const float *rowp = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(colf) + (int64_t)r * p.m_ss);
+      float v[kMaskBitsKeys];
+      if (nk == kMaskBitsKeys) {
+        const float4 q = *reinterpret_cast<const float4 *>(rowp);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < kMaskBitsKeys; ++i) v[i] = i < nk ? rowp[i] : kMaskHide;
+      }
+      const int b = col_bit(r);
+#pragma unroll
+      for (int i = 0; i < kMaskBitsKeys; ++i) {
+        const uint32_t x = !(v[i] <= kMaskHide) ? 1u : 0u;
+        if (b < 32) lo[i] |= x << b;
+        else hi[i] |= x << (b - 32);
+      }
+    }
+    uint64_t *dst = p.mask_bits + ((int64_t)bh * ntiles + n) * p.skv + key;
+#pragma unroll
+    for (int i = 0; i < kMaskBitsKeys; ++i)
+      if (i < nk) dst[i] = ((uint64_t)hi[i] << 32) | lo[i];
+    return;
+  }
+  const uint8_t *col = p.mask + bm * p.m_sb + hm * p.m_sh +
+                       ((int64_t)c * p.chunk_len + (int64_t)t * kBwdBlockQ) * p.m_ss + key;
   // Bit of row r in the word of key i: from the top bit of byte i of v
   // (set iff the byte is nonzero).
   auto add_row = [&](uint32_t v, int r) {
@@ -220,6 +252,10 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(QT == 64 && XPER == 32, "step shape");
   using T = Tile16<D>;
+  // A user mask's bit table stands for it when it is boolean, or additive
+  // with only 0 and hiding values (the row-bit pass says which).
+  bool use_bits = false;
+  if constexpr (UMASK) use_bits = !p.mask_add || *p.mask_flag == 0;
 
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
@@ -435,7 +471,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   // last key's word), beside the statistics.
   auto dma_bits = [&](const Cursor &u, int stage) {
     if constexpr (UMASK) {
-      if (p.mask_add) return;
+      if (!use_bits) return;
       const int bhm = (p.mb_batches > 1 ? b : 0) * p.mb_heads + (p.mb_heads > 1 ? hk * p.group + u.h : 0);
       const int64_t tile = (int64_t)bhm * p.n_q_chunks * p.mb_tpc + u.c * p.mb_tpc + u.t;
       const int k0 = min(wkey0, p.skv - 1);
@@ -619,7 +655,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
                 }
             }
             if constexpr (UMASK) {
-              if (p.mask_add) {
+              if (!use_bits) {
                 // ... plus an additive user mask: rows 16rb + 4grp + i of the
                 // query tile (of head cs.h of the group), this lane's key, in
                 // the raw score's units (at or below kMaskHide: hidden; a
@@ -957,6 +993,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int LDS_BYTES = MB_OFF + (UMASK ? STG * kDqWaves * MB_WAVE : 0);
   static_assert(BN == 64 && QB == 2 && LDS_BYTES <= 160 * 1024, "tile shape");
   using T = Tile16<D>;
+  // A user mask's bit table stands for it when it is boolean, or additive
+  // with only 0 and hiding values (the row-bit pass says which).
+  bool use_bits = false;
+  if constexpr (UMASK) use_bits = !p.mask_add || *p.mask_flag == 0;
 
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
@@ -1143,7 +1183,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // ring stage st (and the tile's mask words).
   auto dma = [&](int kt, int64_t adj, int st) {
     if constexpr (UMASK) {
-      if (!p.mask_add) dma4(lds0 + MB_OFF + (st * kDqWaves + wave) * MB_WAVE, rb_voff, rb_item + (int64_t)kt * p.sq);
+      if (use_bits) dma4(lds0 + MB_OFF + (st * kDqWaves + wave) * MB_WAVE, rb_voff, rb_item + (int64_t)kt * p.sq);
     }
     const uint32_t kd = dst0 + K_OFF + 2 * st * TILE;
     const uint32_t vd = dst0 + V_OFF + 2 * st * TILE;
@@ -1326,7 +1366,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
           // 16*h + 4*grp .. +3 of the block, every read issued before any is
           // used; in a ragged block keys past the end read nothing (no bias on
           // a score the range mask hid).
-          if (p.mask_add) {
+          if (!use_bits) {
             const bool full = sb * 32 + 32 <= p.skv;
             // Additive: value / softmax_scale; at or below kMaskHide: hidden.
             const float inv = 1.0f / p.scale;

@@ -181,13 +181,24 @@ static void fill_kv_chunks(const cp_attn_desc *d, KvChunks *kv) {
   }
 }
 
-// A boolean user mask's row bits (FwdParams::mask_rowbits; bf16), 256-byte
-// aligned: one 64-bit word per mask batch/head, 64-key tile and local row.
-static size_t mask_rowbits_bytes(const cp_attn_desc *d) {
-  if (!d->attn_mask || d->mask_additive || d->dtype != CP_ATTN_BF16) return 0;
+// A user mask's row bits (FwdParams::mask_rowbits; bf16), 256-byte aligned:
+// one 64-bit word per mask batch/head, 64-key tile and local row.
+static size_t mask_rowbits_table_bytes(const cp_attn_desc *d) {
+  if (!d->attn_mask || d->dtype != CP_ATTN_BF16) return 0;
   const size_t words = (size_t)(d->mask_strides[0] ? d->batch : 1) * (d->mask_strides[1] ? d->hq : 1) *
                        (size_t)((d->skv + 63) / 64) * (size_t)d->sq_local;
   return (words * 8 + 255) & ~(size_t)255;
+}
+
+// The row bits and, for an additive mask, FwdParams::mask_flag in 256 more
+// bytes after them.
+static size_t mask_rowbits_bytes(const cp_attn_desc *d) {
+  const size_t t = mask_rowbits_table_bytes(d);
+  return t > 0 && d->mask_additive ? t + 256 : t;
+}
+static const uint32_t *mask_flag_at(const uint64_t *rowbits, const cp_attn_desc *d) {
+  if (!d->mask_additive) return nullptr;
+  return reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(rowbits) + mask_rowbits_table_bytes(d));
 }
 
 // A launch's grid counts its work-items in 32 bits.
@@ -378,10 +389,10 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool a
   p->mb_ktiles = (int32_t)((d->skv + 63) / 64);
 }
 
-// The bit table of a boolean user mask for the bf16 key-stationary kernel
-// (see BwdParams::mask_bits), 256-byte aligned.
+// The bit table of a user mask for the bf16 key-stationary kernel (see
+// BwdParams::mask_bits), 256-byte aligned.
 static size_t bwd_mask_bits_bytes(const cp_attn_desc *d, const BwdParams &p) {
-  if (!d->attn_mask || d->mask_additive || d->dtype != CP_ATTN_BF16) return 0;
+  if (!d->attn_mask || d->dtype != CP_ATTN_BF16) return 0;
   const size_t words = (size_t)p.mb_batches * p.mb_heads * (size_t)p.n_q_chunks * p.mb_tpc * (size_t)d->skv;
   return (words * 8 + 255) & ~(size_t)255;
 }
@@ -583,7 +594,9 @@ int32_t cp_attn_fwd(const cp_attn_desc *d, const void *q, const void *k, const v
   if (need > 0) {
     uint64_t *rb = static_cast<uint64_t *>(workspace);
     p.mask_rowbits = rb;
-    if (launch_mask_rowbits(p.mask, p.m_sb, p.m_sh, p.m_ss, p.mb_batches, p.mb_heads, p.sq, p.skv, rb, stream))
+    p.mask_flag = mask_flag_at(rb, d);
+    if (launch_mask_rowbits(p.mask, p.m_sb, p.m_sh, p.m_ss, p.mb_batches, p.mb_heads, p.sq, p.skv, p.mask_add != 0,
+                            rb, const_cast<uint32_t *>(p.mask_flag), stream))
       return CP_ATTN_ERR_HIP;
   }
   const int e = (d->dtype == CP_ATTN_BF16) ? launch_fwd_bf16(p, d->head_dim, stream)
@@ -660,8 +673,10 @@ int32_t bwd_run(const cp_attn_desc *d, const void *q, const void *k, const void 
     p.kv_partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d));
   if (bits > 0)
     p.mask_bits = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d) + partial);
-  if (rowbits > 0)   // written by the backward's first pass
+  if (rowbits > 0) {   // written by the backward's first passes
     p.mask_rowbits = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + 2 * bwd_stat_bytes(d) + partial + bits);
+    p.mask_flag = mask_flag_at(p.mask_rowbits, d);
+  }
   void *const *ev = n_events == 4 ? events : nullptr;
   const int e = (d->dtype == CP_ATTN_BF16) ? launch_bwd_bf16(p, d->head_dim, stream, ev)
                                            : launch_bwd_fp32(p, d->head_dim, stream, ev);

@@ -81,6 +81,10 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr int TILE = BN * D;
   static_assert(BN == 64 && QB == 2, "tile shape");
   using T = Tile16<D>;   // K tiles (row reads) and V tiles (transpose reads)
+  // A user mask's bit table stands for it when it is boolean, or additive
+  // with only 0 and hiding values (the row-bit pass says which).
+  bool use_bits = false;
+  if constexpr (UMASK) use_bits = !p.mask_add || *p.mask_flag == 0;
 
   // K ring followed by the V ring, in one LDS array: 128 KiB at D = 128.
   // Barriers close the odd steps only. Step j reads K of tile j+1 and V of
@@ -331,7 +335,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   }
   auto dma_k = [&](int kt, int64_t adj, int stage) {
     if constexpr (UMASK) {
-      if (!p.mask_add) dma4(lds0 + MB_OFF + (stage * NW + wave) * MB_WAVE, rb_voff, rb_item + (int64_t)kt * p.sq);
+      if (use_bits) dma4(lds0 + MB_OFF + (stage * NW + wave) * MB_WAVE, rb_voff, rb_item + (int64_t)kt * p.sq);
     }
     dma(kt, adj, false, dst0 + 2 * stage * TILE);
   };
@@ -541,7 +545,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
           // keys 16*kb + 4*grp .. +3 per block, every read issued before any
           // is used; in the ragged last tile keys past the end read nothing
           // (no bias on a score the range mask hid).
-          if (p.mask_add) {
+          if (!use_bits) {
             const bool full = kt * BN + BN <= p.skv;
             // Additive: in the raw score's units (value / softmax_scale); a
             // value at or below kMaskHide hides the key.

@@ -86,10 +86,13 @@ struct FwdParams {
   // longest causal rows start first); chunk_idx maps back to local order.
   int64_t chunk_pos[kMaxQChunks];
   int32_t chunk_idx[kMaxQChunks];
-  // A boolean user mask as row bits (bf16; NULL otherwise): word
+  // A user mask as row bits (bf16; NULL otherwise): word
   // [(bm * mb_heads + hm) * mb_ktiles + kt][row], bit 16*g + 4*kb + i for key
-  // 64*kt + 16*kb + 4*g + i (see launch_mask_rowbits).
+  // 64*kt + 16*kb + 4*g + i (see launch_mask_rowbits), 1 where the key may
+  // be attended. An additive mask's table is used only while *mask_flag is 0:
+  // every value then is 0 or hides its key, and the bits say everything.
   const uint64_t *mask_rowbits;
+  const uint32_t *mask_flag;
   int32_t mb_batches, mb_heads, mb_ktiles;
 };
 
@@ -175,8 +178,8 @@ struct BwdParams {
   // reduction kernel adds into dK/dV.
   int32_t kv_parts;
   float *kv_partial;
-  // A boolean user mask as bits, for the key-stationary bf16 kernel (NULL:
-  // none, or the mask is additive, or the fp32 kernels): word
+  // A user mask as bits, for the key-stationary bf16 kernel (NULL: none, or
+  // the fp32 kernels; an additive mask's only while *mask_flag is 0): word
   // [(bm * mb_heads + hm) * n_q_chunks * mb_tpc + c * mb_tpc + t][key] holds
   // the 64 rows of query tile t of chunk c, bit 16*g + 4*rb + i for row
   // 16*rb + 4*g + i of the tile (1: the key may be attended; 0 also past the
@@ -184,8 +187,9 @@ struct BwdParams {
   uint64_t *mask_bits;
   int32_t mb_batches, mb_heads, mb_tpc;
   // The same mask as row bits for the query-stationary kernel (FwdParams::
-  // mask_rowbits' layout; NULL: none).
+  // mask_rowbits' layout; NULL: none), and FwdParams::mask_flag.
   const uint64_t *mask_rowbits;
+  const uint32_t *mask_flag;
   int32_t mb_ktiles;
 };
 
@@ -206,11 +210,14 @@ int64_t fwd_grid_size(const FwdParams &p);
 
 // Launchers (defined with their kernels); return a hipError_t as int.
 int launch_fwd_bf16(const FwdParams &p, int head_dim, void *stream);
-// Writes a boolean mask [batches][heads][sq][skv] (byte strides m_sb, m_sh,
-// m_ss; batches/heads 1 where it broadcasts) as row bits (FwdParams::
-// mask_rowbits): batches * heads * ceil(skv/64) * sq 64-bit words.
+// Writes a mask [batches][heads][sq][skv] (byte strides m_sb, m_sh, m_ss;
+// batches/heads 1 where it broadcasts; bytes, or float32 values when
+// additive) as row bits (FwdParams::mask_rowbits): batches * heads *
+// ceil(skv/64) * sq 64-bit words. For an additive mask it also sets *flag
+// to 0 when every value is 0 or at most kMaskHide, else to nonzero.
 int launch_mask_rowbits(const uint8_t *mask, int64_t m_sb, int64_t m_sh, int64_t m_ss, int32_t batches,
-                        int32_t heads, int32_t sq, int32_t skv, uint64_t *bits, void *stream);
+                        int32_t heads, int32_t sq, int32_t skv, bool additive, uint64_t *bits, uint32_t *flag,
+                        void *stream);
 // Per-mode instantiations (0: natural order, 1: KV chunk table, 2: packed
 // sequences, 3: user mask), each compiled in a file of its own.
 int launch_fwd_bf16_m0(const FwdParams &p, int head_dim, void *stream);

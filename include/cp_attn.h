@@ -159,7 +159,10 @@ typedef enum {
  * Requires one KV chunk and no packed sequences; the pointer and strides must
  * be multiples of 4 bytes (16 for an additive mask). The mask is read by
  * the kernels during the call's work on the stream; the caller keeps it alive
- * like the other device buffers.
+ * like the other device buffers. With bf16 a first kernel packs the mask
+ * into bit tables in the workspace; an additive mask whose values are all 0
+ * or hiding (a padding mask) is then applied through them, bitwise as the
+ * boolean mask it encodes, the kernel finding so on the device.
  *
  * The LSE of query i is the natural log of the sum, over its visible keys j,
  * of exp(softmax_scale * q_i.k_j + a_ij), with a_ij the additive mask value
@@ -239,16 +242,17 @@ int32_t cp_attn_validate(const cp_attn_desc *desc);
 int32_t cp_attn_share_pairs(const cp_attn_desc *desc, int64_t *pairs);
 
 /* Bytes of device workspace cp_attn_fwd (backward == 0) or cp_attn_bwd
- * (backward != 0) needs for this descriptor; may be 0. With a boolean user
- * mask (bf16) both hold the mask as row bits, one 64-bit word per query row,
- * 64-key tile and mask batch/head (about an eighth of the mask's bytes);
- * the forward needs nothing else. The backward's also holds the per-row
- * statistics of the recompute-based gradient of [CP-migration] §6.1 (-Delta
- * and LSE*log2(e)), for shares whose key tiles are split over several
- * workgroups their float32 partial dK/dV, and with a boolean user mask the
- * mask's column bits too: one 64-bit word per key, 64-row query tile and
- * mask batch/head. Errors: cp_attn_validate's, NULL_PTR for `bytes`. Host
- * only. */
+ * (backward != 0) needs for this descriptor; may be 0. With a user mask
+ * (bf16) both hold the mask as row bits, one 64-bit word per query row,
+ * 64-key tile and mask batch/head (an eighth of a boolean mask's bytes),
+ * and for an additive mask 256 bytes more for the flag that says whether its
+ * values are only 0 and hiding ones; the forward needs nothing else. The
+ * backward's also holds the per-row statistics of the recompute-based
+ * gradient of [CP-migration] §6.1 (-Delta and LSE*log2(e)), for shares whose
+ * key tiles are split over several workgroups their float32 partial dK/dV,
+ * and with a user mask its column bits too: one 64-bit word per key, 64-row
+ * query tile and mask batch/head. Errors: cp_attn_validate's, NULL_PTR for
+ * `bytes`. Host only. */
 int32_t cp_attn_workspace_bytes(const cp_attn_desc *desc, int32_t backward, size_t *bytes);
 
 /* Work-list statistics of the forward tile scheduler (host only), for tests
@@ -279,8 +283,8 @@ int32_t cp_attn_plan_stats_fwd(const cp_attn_desc *desc, cp_attn_plan_stats *sta
  * contiguous, written. Pointers must be 16-byte aligned (lse 4-byte).
  * The workspace (cp_attn_workspace_bytes with backward == 0) is caller-owned
  * device memory, 16-byte aligned, whose contents on entry do not matter; only
- * a bf16 share with a boolean user mask needs one (it holds the mask as row
- * bits, packed by a first kernel), else workspace may be NULL. Returns
+ * a bf16 share with a user mask needs one (it holds the mask as row bits,
+ * packed by a first kernel), else workspace may be NULL. Returns
  * CP_ATTN_OK once the kernels are enqueued on `stream`; validation errors
  * (cp_attn_validate's, NULL_PTR, ALIGNMENT, UNSUPPORTED for a bit table of
  * 2^32 words or more) and CP_ATTN_ERR_WORKSPACE (needed and NULL or too
@@ -345,7 +349,7 @@ int32_t cp_attn_bwd_timed(const cp_attn_desc *desc, const void *q, const void *k
  * first call on a device looks up that device's array once.
  * batch * hq * sq_local above CP_ATTN_NOALLOC_MAX_ROWS, or a share whose
  * workspace (cp_attn_workspace_bytes without split key tiles, e.g. with the
- * bit tables of a large boolean user mask) exceeds the 16 MiB, returns
+ * bit tables of a large user mask) exceeds the 16 MiB, returns
  * CP_ATTN_ERR_SCRATCH_LIMIT before anything is enqueued. `stream`'s device
  * (the current device for NULL) selects the array. Every call on one GPU
  * shares that GPU's array: calls that overlap on one GPU (different streams,

@@ -233,12 +233,14 @@ def _aligned(n):
     return (n + 255) // 256 * 256
 
 
-def test_workspace_holds_the_bit_tables_of_a_boolean_mask():
-    """bf16 with a boolean user mask. The forward's workspace holds the row
-    table: one 64-bit word per query row, 64-key tile and mask batch/head. The
+def test_workspace_holds_the_bit_tables_of_a_user_mask():
+    """bf16 with a user mask. The forward's workspace holds the row table:
+    one 64-bit word per query row, 64-key tile and mask batch/head. The
     backward's also holds the column table, one word per key, 64-row query
     tile of each chunk and mask batch/head, besides the row table (each
-    256-byte aligned). An additive mask or the fp32 path adds none."""
+    256-byte aligned). An additive mask's tables come with 256 bytes more
+    (the flag that says whether its values are only 0 and hiding ones). The
+    fp32 path adds none."""
     def extra(backward, **kw):
         d0, dm = desc(**kw), desc(**kw)
         dm.desc.attn_mask = 1 << 40
@@ -257,13 +259,15 @@ def test_workspace_holds_the_bit_tables_of_a_boolean_mask():
     rows = _aligned(8 * 32 * 500 * 8)
     assert cp_attn_workspace_bytes(d, False) - f0 == rows
     assert cp_attn_workspace_bytes(d, True) - b0 == _aligned(8 * 2 * 4 * 2000 * 8) + rows
-    # additive: none
-    for backward in (False, True):
+    # additive: the same tables and the flag
+    rows = _aligned(32 * 500 * 8)
+    for backward, tables in ((False, rows), (True, _aligned(8 * 2000 * 8) + rows)):
         d = desc()
         d0 = cp_attn_workspace_bytes(d, backward)
         d.desc.attn_mask = 1 << 40
         d.desc.mask_additive = 1
-        assert cp_attn_workspace_bytes(d, backward) == d0
+        d.desc.mask_strides[2] = 2000 * 4
+        assert cp_attn_workspace_bytes(d, backward) - d0 == tables + 256
     # fp32: none
     kw = dict(dtype=1, head_dim=64, q_strides=(0, 0, 64), kv_strides=(0, 0, 64), o_strides=(0, 0, 64))
     assert extra(False, **kw) == 0 and extra(True, **kw) == 0

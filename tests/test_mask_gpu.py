@@ -119,3 +119,60 @@ def test_user_mask_fwd_bwd_all_ranks(case):
         assert err_o <= tol_o and err_l <= tol_l and max(errs) <= tol_g
         if mask_kind in ("random", "random_b1", "random_11", "additive", "padding"):
             assert torch.all(out[:, :, ::37] == 0) and torch.all(dq[:, :, ::37] == 0)
+
+
+PURE_CASES = [
+    # kind, S, Hq, Hkv, D, cp, rank, mask heads (1: broadcast over heads)
+    ("contiguous", 1000, 4, 2, 64, 2, 1, 4),      # ragged key count, per-head mask
+    ("head_tail", 2048, 8, 2, 128, 4, 2, 1),      # broadcast over heads
+]
+
+
+@pytest.mark.parametrize("case", PURE_CASES, ids=["-".join(map(str, c)) for c in PURE_CASES])
+def test_additive_mask_of_zeros_and_hides_matches_the_boolean_mask(case):
+    """An additive mask whose values are only 0 (either sign) and hiding
+    values (-inf, -1e9, the float32 minimum, -1e4) takes the boolean mask's
+    bit-table path: bitwise the results of the boolean mask it encodes, in
+    both directions. A mask with one small nonzero bias does not, and the
+    call after it (same workspace) is pure again."""
+    kind, S, Hq, Hkv, D, cp, r, mh = case
+    B = 2
+    dev = torch.device("cuda")
+    prob = global_problem(B, Hq, Hkv, S, D, dtype="bf16", seed=23, with_dout=True)
+    sh = cut_share(kind, prob.q.to(dev), prob.k.to(dev), prob.v.to(dev), cp, r)
+    Sq = sh.q.shape[2]
+    g = torch.Generator(device="cpu").manual_seed(29)
+    keep = torch.rand((B, mh, Sq, S), generator=g) < 0.8
+    keep[:, :, ::37] = False
+    hides = torch.tensor([float("-inf"), -1e9, torch.finfo(torch.float32).min, -1e4])
+    hide = hides[torch.randint(0, 4, keep.shape, generator=g)]
+    zero = torch.where(torch.rand(keep.shape, generator=g) < 0.5, torch.tensor(0.0), torch.tensor(-0.0))
+    add = torch.where(keep, zero, hide).to(dev)
+    keep = keep.to(dev)
+    scale = 1.0 / math.sqrt(D)
+    dout = sh.take_rows(prob.dout.to(dev))
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def run(m):
+        out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,
+                               attn_mask=m, workspace=ws)
+        grads = cp_attn_bwd(sh.q, sh.k, sh.v, out, lse, dout, sh.q_chunk_pos, layout=sh.layout,
+                            softmax_scale=scale, attn_mask=m, workspace=ws)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (out, lse, *grads)]
+
+    names = ("out", "lse", "dq", "dk", "dv")
+    ref = run(keep)
+    got = run(add)
+    for n, a, b in zip(names, got, ref):
+        assert torch.equal(a, b), f"{case}: {n} of the 0/hide additive mask differs from the boolean mask's"
+    impure = add.clone()
+    ramp = (torch.arange(S, device=dev) % 7).float() * 0.3      # not a constant shift of the row
+    impure[0, 0, 2, :] = torch.where(keep[0, 0, 2, :], ramp, impure[0, 0, 2, :])
+    bias = run(impure)
+    assert not torch.equal(bias[1][0, 0, 2], ref[1][0, 0, 2]), f"{case}: a biased mask gave the boolean mask's LSE"
+    assert not torch.equal(bias[0][0, 0, 2], ref[0][0, 0, 2]), f"{case}: a biased mask gave the boolean mask's output"
+    again = run(add)
+    for n, a, b in zip(names, again, ref):
+        assert torch.equal(a, b), f"{case}: {n} after a biased mask differs from the boolean mask's"
+    print(f"pure additive {case}: bitwise equal to the boolean mask", flush=True)
