@@ -175,4 +175,14 @@ def test_additive_mask_of_zeros_and_hides_matches_the_boolean_mask(case):
     again = run(add)
     for n, a, b in zip(names, again, ref):
         assert torch.equal(a, b), f"{case}: {n} after a biased mask differs from the boolean mask's"
+    # Which path ran: the forward's workspace holds the row table (256-byte
+    # aligned), then the flag (0: only 0 and hiding values).
+    words = B * mh * ((S + 63) // 64) * Sq
+    at = (words * 8 + 255) // 256 * 256
+    for m, want in ((impure, False), (add, True)):
+        cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale, attn_mask=m,
+                    workspace=ws)
+        torch.cuda.synchronize()
+        flag = int(ws[at:at + 4].view(torch.int32).item())
+        assert (flag == 0) == want, f"{case}: flag {flag} after a {'pure' if want else 'biased'} mask"
     print(f"pure additive {case}: bitwise equal to the boolean mask", flush=True)
