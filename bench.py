@@ -27,8 +27,9 @@ cp=8 rank-0 share, the Hybrid U=2 x C=4 rank-4 share and the Head-Tail B = 2
 backward shares of ranks 0 and 7, and the Colossal rank-7 share over eight
 packed sequences; the Ulysses share also runs straight from the all-to-all's
 received blocks (".../in_place": no unpack or pack pass); the headline share
-also runs under a boolean and an additive user mask (".../user_mask_*": 10 %
-of the pairs hidden at random, FLOPs still over the causal pairs). While the headline step keeps running for
+also runs under a boolean, an additive and an additive padding user mask
+(".../user_mask_*": 10 % of the pairs hidden at random, FLOPs still over
+the causal pairs). While the headline step keeps running for
 about 2.5 s, amd-smi reads the GFX clocks and socket power ("clock"; the chip
 runs at its power cap, below the 2.4 GHz the peak assumes). The oracle's CPU
 baseline runs last, in a child process. Prints ONE JSON line. `--detail` adds
@@ -162,13 +163,13 @@ class BlockShare:
 def share_user_mask(kind, B, Sq, Skv, dev):
     """A seeded user mask for a share, broadcast over heads: "bool", 10 % of
     the (row, key) pairs hidden at random; "additive", N(0, 1) biases with the
-    same 10 % at -inf."""
+    same 10 % at -inf; "padding", 0 with the same 10 % at -inf."""
     import torch
     g = torch.Generator(device="cpu").manual_seed(11)
     keep = torch.rand((1, 1, Sq, Skv), generator=g) >= 0.1
     if kind == "bool":
         return keep.to(dev)
-    bias = torch.randn((1, 1, Sq, Skv), generator=g)
+    bias = torch.randn((1, 1, Sq, Skv), generator=g) if kind == "additive" else torch.zeros((1, 1, Sq, Skv))
     return torch.where(keep, bias, torch.full((), float("-inf"))).to(dev)
 
 
@@ -541,7 +542,7 @@ def time_configs(steps, warmup, probs):
                 del rr
     # The headline share under a user mask (FLOPs still counted over the causal
     # pairs: the kernels visit every causal tile whatever the mask hides).
-    for kind in ("bool", "additive"):
+    for kind in ("bool", "additive", "padding"):
         sp = dict(WORKLOADS[WORKLOAD])
         rr = time_share(sp, probs[problem_key(sp)], 7, steps, warmup, True, warm_s=0.3, user_mask=kind)
         out[f"{WORKLOAD}/r7/user_mask_{kind}"] = share_entry(rr)
