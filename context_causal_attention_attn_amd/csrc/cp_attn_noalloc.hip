@@ -3,8 +3,8 @@
 // tight serving loops, harnesses that forbid allocation).
 //
 // The backward's scratch is its per-row statistics: -Delta and LSE *
-// log2(e), each [batch, hq, sq_local] float32, and with a boolean user mask
-// the mask's bit table (the workspace of cp_attn_bwd, less the partial dK/dV
+// log2(e), each [batch, hq, sq_local] float32, and with a user mask the
+// mask's bit tables (the workspace of cp_attn_bwd, less the partial dK/dV
 // of split key tiles, which this entry point never splits). Here it lives in
 // a file-scope device array, `scratch`, of a fixed size; each GPU the library runs on holds its own copy of it until the
 // process ends. Host code never passes the array's name to a kernel (in host
@@ -21,7 +21,7 @@ namespace {
 
 // -Delta and LSE * log2(e) for up to CP_ATTN_NOALLOC_MAX_ROWS rows each, every
 // array starting on a 256-byte boundary (the layout cp_attn_bwd gives its
-// workspace); a share's bit table follows its statistics when both fit.
+// workspace); a share's bit tables follow its statistics when all fit.
 constexpr size_t kStatBytes = ((size_t)CP_ATTN_NOALLOC_MAX_ROWS * 4 + 255) & ~(size_t)255;
 constexpr size_t kScratchBytes = 2 * kStatBytes;
 

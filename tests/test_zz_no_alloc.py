@@ -7,7 +7,7 @@ too wherever cp_attn_bwd keeps each key tile in one workgroup. Where it splits
 key tiles over several workgroups (few KV heads; partials summed afterwards),
 the no-alloc call, whose scratch holds no partials, does not: only the fp32
 summation order differs, so dK/dV agree to 1e-5 relative. A boolean user
-mask's bit table shares the scratch too."""
+mask's bit tables share the scratch too."""
 import ctypes
 import math
 
@@ -64,18 +64,27 @@ def test_noalloc_backward_matches_workspace_backward_twice(dtype):
         print(f"noalloc {dtype} {kind} B={B} S={S} r{r}: dq bitwise, dk/dv within 1e-5 of cp_attn_bwd", flush=True)
 
 
-def test_noalloc_backward_with_a_boolean_mask():
-    """A boolean user mask: the backward's bit table of it lives in the same
-    scratch; a masked call, then an unmasked smaller one, each against
-    cp_attn_bwd."""
+def test_noalloc_backward_with_user_masks():
+    """User masks: the backward's bit tables of them (and an additive mask's
+    flag) live in the same scratch. A boolean mask, an additive padding mask
+    (0 or -inf: the bit path), an additive mask with biases (the value path)
+    and an unmasked smaller share in a row, each against cp_attn_bwd."""
     dev = torch.device("cuda")
     g = torch.Generator(device="cpu").manual_seed(62)
-    cases = [(2, 8, 2, 2048, 128, "head_tail", 4, 1, True), (1, 4, 2, 640, 64, "contiguous", 2, 1, False)]
+    cases = [(2, 8, 2, 2048, 128, "head_tail", 4, 1, "bool"), (2, 8, 2, 2048, 128, "head_tail", 4, 1, "padding"),
+             (2, 8, 2, 2048, 128, "head_tail", 4, 1, "bias"), (1, 4, 2, 640, 64, "contiguous", 2, 1, None)]
     for B, Hq, Hkv, S, D, kind, cp, r, masked in cases:
         prob = global_problem(B, Hq, Hkv, S, D, dtype="bf16", seed=63, with_dout=True)
         sh = cut_share(kind, prob.q.to(dev), prob.k.to(dev), prob.v.to(dev), cp, r)
         scale = 1.0 / math.sqrt(D)
-        m = (torch.rand((B, Hq, sh.q.shape[2], S), generator=g) < 0.75).to(dev) if masked else None
+        m = None
+        if masked:
+            keep = torch.rand((B, Hq, sh.q.shape[2], S), generator=g) < 0.75
+            if masked == "bool":
+                m = keep.to(dev)
+            else:
+                val = torch.randn(keep.shape, generator=g) if masked == "bias" else torch.zeros(keep.shape)
+                m = torch.where(keep, val, torch.tensor(float("-inf"))).to(dev)
         out, lse = cp_attn_fwd(sh.q, sh.k, sh.v, sh.q_chunk_pos, layout=sh.layout, softmax_scale=scale,
                                attn_mask=m)
         dout = sh.take_rows(prob.dout.to(dev)).contiguous()
