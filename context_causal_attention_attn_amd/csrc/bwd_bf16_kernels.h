@@ -656,7 +656,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
             }
             if constexpr (UMASK) {
               if (!use_bits) {
-                // ... plus an additive user mask: rows 16rb + 4grp + i of the
+                // ... plus an additive user mask with biases (else the
+                // column bits below): rows 16rb + 4grp + i of the
                 // query tile (of head cs.h of the group), this lane's key, in
                 // the raw score's units (at or below kMaskHide: hidden; a
                 // hidden score stays -inf). The sixteen reads are issued
@@ -1362,7 +1363,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
           }
         }
         if constexpr (UMASK) {
-          // ... and the user mask. Additive: the 4 floats of this lane's keys
+          // ... and the user mask (the row bits unless additive with biases).
+          // Additive: the 4 floats of this lane's keys
           // 16*h + 4*grp .. +3 of the block, every read issued before any is
           // used; in a ragged block keys past the end read nothing (no bias on
           // a score the range mask hid).

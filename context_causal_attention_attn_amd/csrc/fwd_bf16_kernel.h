@@ -541,10 +541,11 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
           }
         }
         if constexpr (UMASK) {
-          // ... and the user mask. Additive: the 4 floats of this lane's
-          // keys 16*kb + 4*grp .. +3 per block, every read issued before any
-          // is used; in the ragged last tile keys past the end read nothing
-          // (no bias on a score the range mask hid).
+          // ... and the user mask. Additive with biases: the 4 floats of
+          // this lane's keys 16*kb + 4*grp .. +3 per block, every read issued
+          // before any is used; in the ragged last tile keys past the end
+          // read nothing (no bias on a score the range mask hid). Boolean, or
+          // additive of 0 and hiding values only: the row bits.
           if (!use_bits) {
             const bool full = kt * BN + BN <= p.skv;
             // Additive: in the raw score's units (value / softmax_scale); a
