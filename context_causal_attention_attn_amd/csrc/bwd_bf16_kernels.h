@@ -253,9 +253,10 @@ __global__ void __launch_bounds__(kDkdvThreads, 2) bwd_dkdv_kernel(const BwdPara
   static_assert(QT == 64 && XPER == 32, "step shape");
   using T = Tile16<D>;
   // A user mask's bit table stands for it when it is boolean, or additive
-  // with only 0 and hiding values (the row-bit pass says which).
+  // with only 0 and hiding values (the row-bit pass says which; a share
+  // without keys has no table, and no flag, and reads no mask).
   bool use_bits = false;
-  if constexpr (UMASK) use_bits = !p.mask_add || *p.mask_flag == 0;
+  if constexpr (UMASK) use_bits = !p.mask_add || (p.mask_flag != nullptr && *p.mask_flag == 0);
 
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
@@ -995,9 +996,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   static_assert(BN == 64 && QB == 2 && LDS_BYTES <= 160 * 1024, "tile shape");
   using T = Tile16<D>;
   // A user mask's bit table stands for it when it is boolean, or additive
-  // with only 0 and hiding values (the row-bit pass says which).
+  // with only 0 and hiding values (the row-bit pass says which; a share
+  // without keys has no table, and no flag, and reads no mask).
   bool use_bits = false;
-  if constexpr (UMASK) use_bits = !p.mask_add || *p.mask_flag == 0;
+  if constexpr (UMASK) use_bits = !p.mask_add || (p.mask_flag != nullptr && *p.mask_flag == 0);
 
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;

@@ -82,9 +82,10 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   static_assert(BN == 64 && QB == 2, "tile shape");
   using T = Tile16<D>;   // K tiles (row reads) and V tiles (transpose reads)
   // A user mask's bit table stands for it when it is boolean, or additive
-  // with only 0 and hiding values (the row-bit pass says which).
+  // with only 0 and hiding values (the row-bit pass says which; a share
+  // without keys has no table, and no flag, and reads no mask).
   bool use_bits = false;
-  if constexpr (UMASK) use_bits = !p.mask_add || *p.mask_flag == 0;
+  if constexpr (UMASK) use_bits = !p.mask_add || (p.mask_flag != nullptr && *p.mask_flag == 0);
 
   // K ring followed by the V ring, in one LDS array: 128 KiB at D = 128.
   // Barriers close the odd steps only. Step j reads K of tile j+1 and V of

@@ -186,3 +186,40 @@ def test_additive_mask_of_zeros_and_hides_matches_the_boolean_mask(case):
         flag = int(ws[at:at + 4].view(torch.int32).item())
         assert (flag == 0) == want, f"{case}: flag {flag} after a {'pure' if want else 'biased'} mask"
     print(f"pure additive {case}: bitwise equal to the boolean mask", flush=True)
+
+
+@pytest.mark.parametrize("additive", [0, 1])
+def test_masked_share_without_keys(additive):
+    """A share with no keys under a user mask, through the C ABI with a real
+    mask pointer (torch gives a zero-width view no pointer): no bit table is
+    built, every row comes out empty (out 0, LSE -inf) and dQ is 0, for a
+    boolean and an additive mask."""
+    from context_causal_attention_attn_amd import _lib
+    from context_causal_attention_attn_amd.api import cp_attn_workspace_bytes, make_desc
+    dev = torch.device("cuda")
+    lib = _lib.load()
+    q = torch.randn(1, 4, 64, 64, device=dev).to(torch.bfloat16)
+    kv = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, device=dev)[:, :, :0]
+    base = torch.zeros(1, 4, 64, 16, dtype=torch.float32 if additive else torch.bool, device=dev)
+    d = make_desc(q, kv, kv, q.stride(), [0], [0], "contiguous", True, 0.125)
+    d.desc.attn_mask = base.data_ptr()
+    d.desc.mask_additive = additive
+    d.desc.mask_strides[0] = 0
+    d.desc.mask_strides[1] = base.stride(1) * base.element_size()
+    d.desc.mask_strides[2] = base.stride(2) * base.element_size()
+    assert cp_attn_workspace_bytes(d, False) == 0
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 4, 64), float("nan"), device=dev)
+    fake = base.data_ptr()   # K/V pointers are not read without keys
+    stream = torch.cuda.current_stream().cuda_stream
+    _lib.check(lib.cp_attn_fwd(d.ref(), q.data_ptr(), fake, fake, out.data_ptr(), lse.data_ptr(), None, 0,
+                               stream), "cp_attn_fwd")
+    dout = torch.randn_like(q)
+    dq = torch.full_like(q, float("nan"))
+    need = cp_attn_workspace_bytes(d, True)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _lib.check(lib.cp_attn_bwd(d.ref(), q.data_ptr(), fake, fake, out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                               dq.data_ptr(), fake, fake, ws.data_ptr(), ws.numel(), stream), "cp_attn_bwd")
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(dq == 0)
