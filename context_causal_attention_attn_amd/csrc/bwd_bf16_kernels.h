@@ -990,9 +990,17 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int STG = 4;                       // ring stages (K and V)
   constexpr int K_OFF = 0;
   constexpr int V_OFF = STG * TILE * 2;
-  constexpr int MB_OFF = 2 * STG * TILE * 2;   // [STG][waves][32 rows] row-bit words (boolean mask)
+  // After the K/V rings, a user mask's region: [STG][waves][32 rows] row-bit
+  // words, or (an additive mask with biases, shared by the item's heads)
+  // [2][64 rows][64 keys] float values of a tile, each row's 16-byte chunks
+  // swizzled (chunk c of row r at slot c ^ (r % 16)).
+  constexpr int MB_OFF = 2 * STG * TILE * 2;
   constexpr int MB_WAVE = kDqWaveRows * 8;
-  constexpr int LDS_BYTES = MB_OFF + (UMASK ? STG * kDqWaves * MB_WAVE : 0);
+  constexpr bool ADDS_LDS = UMASK && RB == 2;   // (items of more rows: their tiles do not fit)
+  constexpr int MA_TILE = kDqWaveRows * RB * BN * 4;
+  constexpr int MB_BYTES =
+      !ADDS_LDS || STG * kDqWaves * MB_WAVE > 2 * MA_TILE ? STG * kDqWaves * MB_WAVE : 2 * MA_TILE;
+  constexpr int LDS_BYTES = MB_OFF + (UMASK ? MB_BYTES : 0);
   static_assert(BN == 64 && QB == 2 && LDS_BYTES <= 160 * 1024, "tile shape");
   using T = Tile16<D>;
   // A user mask's bit table stands for it when it is boolean, or additive
@@ -1182,6 +1190,26 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
     const int w = lane >> 1;
     rb_voff = (uint32_t)((w < wrows ? wrow0 + w : 0) * 8 + 4 * (lane & 1));
   }
+  // An additive mask with biases that all the item's heads share: its values
+  // of tile kt for the item's rows into LDS stage st (two 1 KiB loads per
+  // wavefront, four rows each, with the swizzle above; rows past the item's
+  // last read its last row). A ragged tile is not staged (its reads stay
+  // per lane, with the end test).
+  const bool stage_adds = ADDS_LDS && !use_bits && p.mb_heads == 1 && p.mask_add;
+  auto dma_adds = [&](int kt, int st) {
+    if constexpr (ADDS_LDS) {
+      if (!stage_adds || kt * BN + BN > p.skv) return;
+      const uint8_t *rows0 = p.mask + b * p.m_sb + (int64_t)(chunk * p.chunk_len + item_row0) * p.m_ss +
+                             (int64_t)kt * BN * 4;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 4 * (2 * wave + i) + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        const uint32_t vo = (uint32_t)min(r, item_rows - 1) * (uint32_t)p.m_ss + 16u * (uint32_t)c;
+        dma1(lds0 + MB_OFF + st * MA_TILE + (2 * wave + i) * 1024, vo, rows0);
+      }
+    }
+  };
   // K and V of storage tile kt (adj: its KV chunk's extra elements) into
   // ring stage st (and the tile's mask words).
   auto dma = [&](int kt, int64_t adj, int st) {
@@ -1223,6 +1251,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // This lane's byte of its row's mask word (boolean mask) at stage 0, row
   // block 0 and 32-key block 0, beyond the reach of an immediate as well.
   uint32_t mbits = lds0 + MB_OFF + wave * MB_WAVE + col * 8 + 2 * grp;
+  // This lane's row of a staged additive tile (stage 0, row block 0).
+  uint32_t madds = lds0 + MB_OFF + (wrow0 + col) * BN * 4;
   uint32_t kaddr[KSTEPS], vaddr[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
@@ -1283,6 +1313,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   // Storage offset of a natural-order tile (merged chunks; 0 for one chunk).
   auto nat_adj = [&](int kt) { return ((int64_t)kt * BN >> p.kv.store_lg) * p.kv.cadj; };
   if (ntiles > 0) dma(t_cur.kt, MKV ? t_cur.adj : nat_adj(t_cur.kt), 0);
+  if constexpr (UMASK) {
+    if (ntiles > 0) dma_adds(t0, 0);
+  }
   if (ntiles > 1) dma(t_nx1.kt, MKV ? t_nx1.adj : nat_adj(t_nx1.kt), 1);
   wait_vmem_all();
   __syncthreads();
@@ -1376,14 +1409,23 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
             const float inv = 1.0f / p.scale;
             const float *mf = reinterpret_cast<const float *>(mrow[qb]);
             f32x4 a[2];
+            if (ADDS_LDS && stage_adds && (sb >> 1) * BN + BN <= p.skv) {
+              // The tile's values staged in LDS: row wrow0 + 16qb + col,
+              // chunk 8KB + 4h + grp at its swizzled slot.
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int k0 = sb * 32 + 16 * h + 4 * grp;
-              if (full) {
-                a[h] = *reinterpret_cast<const f32x4 *>(mf + k0);
-              } else {
+              for (int h = 0; h < 2; ++h)
+                a[h] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>(
+                    (uintptr_t)(madds + (J4 & 1) * MA_TILE + 16 * qb * BN * 4 + (((grp ^ col) ^ (8 * KB + 4 * h)) << 4)));
+            } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[h][i] = k0 + i < p.skv ? mf[k0 + i] : 0.0f;
+              for (int h = 0; h < 2; ++h) {
+                const int k0 = sb * 32 + 16 * h + 4 * grp;
+                if (full) {
+                  a[h] = *reinterpret_cast<const f32x4 *>(mf + k0);
+                } else {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) a[h][i] = k0 + i < p.skv ? mf[k0 + i] : 0.0f;
+                }
               }
             }
 #pragma unroll
@@ -1472,13 +1514,16 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(const BwdParams p) {
   auto tile_step = [&](auto j4_tag, int J) {
     constexpr int J4 = decltype(j4_tag)::value;
     if (J + 2 < ntiles) dma(MKV ? t_nx2.kt : t0 + J + 2, MKV ? t_nx2.adj : nat_adj(t0 + J + 2), (J4 + 2) % STG);
+    if constexpr (UMASK) {
+      if (J + 1 < ntiles) dma_adds(t0 + J + 1, (J4 + 1) & 1);
+    }
     // Opaque bases: the V ring's start (64 KiB) and the stage offsets then
     // stay instruction offsets instead of per-read address arithmetic.
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(taddr[db]));
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]), "+v"(vaddr[s]));
-    if constexpr (UMASK) asm volatile("" : "+v"(mbits));
+    if constexpr (UMASK) asm volatile("" : "+v"(mbits), "+v"(madds));
     TileRef t{t0 + J, kv_pos0, 0};
     if constexpr (MKV) {
       t = t_cur;

@@ -50,6 +50,10 @@ def make_mask(kind, osh, B, Hq, S, rng, dtype="bf16"):
         # whose LSE gate is 1e-4 absolute, 100: float32 keeps 1e-5 there).
         m[:, :, :, S // 2:S // 2 + 4] = 1000.0 if dtype == "bf16" else 100.0
         m[:, :, ::37] = -1e9
+    elif kind == "additive_h1":     # float biases shared by every head, 15 % -inf, some rows hidden
+        m = rng.normal(0.0, 1.5, (B, 1, q_pos.size, S)).astype(np.float32)
+        m[rng.random(m.shape) < 0.15] = -np.inf
+        m[:, :, ::37] = -np.inf
     elif kind == "random_b1":       # random per head, shared by the batch
         m = rng.random((1, Hq, q_pos.size, S)) < 0.75
         m[:, :, ::37] = False
@@ -73,6 +77,8 @@ CASES = [
     ("random", "head_tail", 512, 2, 1, 64, 4, "fp32"),
     ("additive", "head_tail", 2048, 8, 2, 128, 4, "bf16"),
     ("additive", "contiguous", 1000, 4, 2, 64, 2, "bf16"),    # ragged key count
+    ("additive_h1", "head_tail", 2048, 8, 2, 128, 4, "bf16"),  # biases shared by the heads
+    ("additive_h1", "contiguous", 1000, 8, 2, 64, 2, "bf16"),  # ... with a ragged key count
     ("additive", "contiguous", 512, 2, 1, 64, 4, "fp32"),
     ("padding", "head_tail", 2048, 8, 2, 128, 4, "bf16"),
     ("padding", "contiguous", 1000, 4, 2, 64, 2, "bf16"),     # ragged key count
@@ -117,7 +123,7 @@ def test_user_mask_fwd_bwd_all_ranks(case):
         print(f"mask {case} r{r}: out {err_o:.3e} lse {err_l:.3e} dq {errs[0]:.3e} dk {errs[1]:.3e} "
               f"dv {errs[2]:.3e}", flush=True)
         assert err_o <= tol_o and err_l <= tol_l and max(errs) <= tol_g
-        if mask_kind in ("random", "random_b1", "random_11", "additive", "padding"):
+        if mask_kind in ("random", "random_b1", "random_11", "additive", "additive_h1", "padding"):
             assert torch.all(out[:, :, ::37] == 0) and torch.all(dq[:, :, ::37] == 0)
 
 
