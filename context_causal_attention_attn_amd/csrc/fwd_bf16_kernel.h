@@ -96,9 +96,16 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // and starts after the previous occupant's last reader passed a barrier.
   // A boolean user mask's row-bit words follow the rings: per K stage, the
   // words of each wavefront's 32 rows for that stage's tile.
+  // Or, for an additive mask with biases that all the item's heads share
+  // (items of 64 rows), [2][64 rows][64 keys] float values of a tile, each
+  // row's 16-byte chunks swizzled (chunk c of row r at slot c ^ (r % 16)).
   constexpr int MB_OFF = (KSTAGES + VSTAGES) * TILE * 2;
   constexpr int MB_WAVE = kFwdWaveRows * 8;
-  constexpr int LDS_BYTES = MB_OFF + (UMASK ? KSTAGES * NW * MB_WAVE : 0);
+  constexpr bool ADDS_LDS = UMASK && RB == 2;
+  constexpr int MA_TILE = BM * BN * 4;
+  constexpr int MB_BYTES =
+      !ADDS_LDS || KSTAGES * NW * MB_WAVE > 2 * MA_TILE ? KSTAGES * NW * MB_WAVE : 2 * MA_TILE;
+  constexpr int LDS_BYTES = MB_OFF + (UMASK ? MB_BYTES : 0);
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   static_assert((KSTAGES + VSTAGES) * TILE * 2 <= 128 * 1024 && LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(KSTAGES >= K_AHEAD + 1 && VSTAGES >= V_AHEAD + 3 && K_AHEAD >= 3 && V_AHEAD >= 1 &&
@@ -341,6 +348,27 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     dma(kt, adj, false, dst0 + 2 * stage * TILE);
   };
   auto dma_v = [&](int kt, int64_t adj, int stage) { dma(kt, adj, true, dst0 + 2 * (KSTAGES + stage) * TILE); };
+  // An additive mask with biases that all the item's heads share: its values
+  // of tile kt for the item's rows into LDS stage st (two 1 KiB loads per
+  // wavefront, four rows each, with the swizzle above; rows past the item's
+  // last read its last row). A ragged tile is not staged (its reads stay per
+  // lane, with the end test). In this mode every step ends with a barrier:
+  // a step loads the next tile's values, which the next step reads.
+  const bool stage_adds = ADDS_LDS && !use_bits && p.mb_heads == 1 && p.mask_add;
+  auto dma_adds = [&](int kt, int st) {
+    if constexpr (ADDS_LDS) {
+      if (!stage_adds || kt * BN + BN > p.skv) return;
+      const uint8_t *rows0 = p.mask + b * p.m_sb + (int64_t)(chunk * p.chunk_len + item_row0) * p.m_ss +
+                             (int64_t)kt * BN * 4;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 4 * (2 * wave + i) + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        const uint32_t vo = (uint32_t)min(r, item_rows - 1) * (uint32_t)p.m_ss + 16u * (uint32_t)c;
+        dma1(lds0 + MB_OFF + st * MA_TILE + (2 * wave + i) * 1024, vo, rows0);
+      }
+    }
+  };
 
   f32x4 oacc[QB][DB];
 #pragma unroll
@@ -451,6 +479,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   if (ntiles > 0) {
     dma_k(t_cur.kt, MKV ? t_cur.adj : nat_adj(t_cur.kt), 0);
     dma_v(t_cur.kt, MKV ? t_cur.adj : nat_adj(t_cur.kt), 0);
+    if constexpr (ADDS_LDS) dma_adds(t_cur.kt, 0);
   }
   if (ntiles > 1) dma_k(t_nx1.kt, MKV ? t_nx1.adj : nat_adj(t_nx1.kt), 1);
   if (ntiles > 2) dma_k(t_nx2.kt, MKV ? t_nx2.adj : nat_adj(t_nx2.kt), 2);
@@ -464,6 +493,8 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   // 16*kb + 4*grp + i at bit 16*grp + 4*kb + i) in K stage 0, row block 0;
   // beyond the reach of an immediate from LDS 0.
   uint32_t mbits = lds0 + MB_OFF + wave * MB_WAVE + col * 8 + 2 * grp;
+  // This lane's row of a staged additive tile (stage 0, row block 0).
+  uint32_t madds = lds0 + MB_OFF + (wrow0 + col) * BN * 4;
 
   // One step on tile j (J4 = j % 4): PV(j-1) and S^T(j+1) on the matrix
   // core, softmax of S^T(j) on the VALU, and K of tile j+3 and V of tile j+1
@@ -478,6 +509,12 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     bf16x8 (&pcur)[QB][PSTEPS] = pbuf[SET];
     using KS = IC<(J4 + 1) % KSTAGES>;             // K of tile j+1
     using VS = IC<(J4 + VSTAGES - 1) % VSTAGES>;   // V of tile j-1
+    // The next tile's staged mask values go out before the tiles' loads, so
+    // that the wait after an even step counts only those (2 * INSTS) as
+    // still in flight.
+    if constexpr (ADDS_LDS) {
+      if (j + 1 < ntiles) dma_adds(t0 + j + 1, (J4 + 1) & 1);
+    }
     // K of tile j+3 replaces K of tile j-1 (read in step j-2); V of tile j+1
     // replaces V of tile j-3 (read in step j-2). In natural order the last
     // steps load the item's last tile again instead of branching around the
@@ -498,7 +535,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(kaddr[s]));
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vaddr[db]));
-    if constexpr (UMASK) asm volatile("" : "+v"(mbits));
+    if constexpr (UMASK) asm volatile("" : "+v"(mbits), "+v"(madds));
     int kt = t0 + j;
     int64_t tile_plo = kv_pos0 + (int64_t)kt * BN;
     if constexpr (MKV) {
@@ -554,14 +591,23 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
             const float inv = 1.0f / p.scale;
             const float *mf = reinterpret_cast<const float *>(mrow[qb]);
             f32x4 a[KB];
+            if (ADDS_LDS && stage_adds && full) {
+              // The tile's values staged in LDS: row wrow0 + 16qb + col,
+              // chunk 4kb + grp at its swizzled slot.
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              const int k0 = kt * BN + 16 * kb + 4 * grp;
-              if (full) {
-                a[kb] = *reinterpret_cast<const f32x4 *>(mf + k0);
-              } else {
+              for (int kb = 0; kb < KB; ++kb)
+                a[kb] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>(
+                    (uintptr_t)(madds + (J4 & 1) * MA_TILE + 16 * qb * BN * 4 + (((grp ^ col) ^ (4 * kb)) << 4)));
+            } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[kb][i] = k0 + i < p.skv ? mf[k0 + i] : 0.0f;
+              for (int kb = 0; kb < KB; ++kb) {
+                const int k0 = kt * BN + 16 * kb + 4 * grp;
+                if (full) {
+                  a[kb] = *reinterpret_cast<const f32x4 *>(mf + k0);
+                } else {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) a[kb][i] = k0 + i < p.skv ? mf[k0 + i] : 0.0f;
+                }
               }
             }
 #pragma unroll
@@ -709,6 +755,13 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if constexpr (J4 & 1) {
       wait_vmem_all();   // this wave's rows of every tile loaded so far are in LDS
       __syncthreads();
+    } else if constexpr (ADDS_LDS) {
+      if (stage_adds) {
+        // The next tile's mask values (older than this step's 2 * INSTS
+        // tile loads, which may stay in flight) are in LDS.
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * INSTS));
+        __syncthreads();
+      }
     }
   };
 
