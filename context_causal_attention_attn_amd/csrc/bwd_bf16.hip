@@ -1,5 +1,5 @@
-// Backward dispatch: the Delta pre-pass (and the bit table of a boolean user
-// mask), then the dK/dV and dQ instantiations
+// Backward dispatch: the Delta pre-pass (and a user mask's bit tables), then
+// the dK/dV and dQ instantiations
 // of the share's mode (keys in natural order, a KV chunk table, packed
 // sequences, a user mask). The kernels live in bwd_bf16_kernels.h; each mode
 // is compiled in a file of its own.

@@ -517,8 +517,9 @@ int32_t cp_attn_workspace_bytes(const cp_attn_desc *d, int32_t backward, size_t 
   // Backward: Delta = rowsum(dO o O) and LSE * log2(e), each [B, Hq, Sq]
   // fp32, each starting on a 256-byte boundary; then the fp32 partial dK/dV
   // of key tiles split over several workgroups (none for most shares); then
-  // a boolean user mask's bit tables (bf16): per key and query tile for
-  // dK/dV, per row and key tile for dQ. Forward: the latter only.
+  // a user mask's bit tables (bf16): per key and query tile for dK/dV, per
+  // row and key tile for dQ, and an additive mask's flag. Forward: the row
+  // table (and flag) only.
   *bytes = cpattn::bwd_workspace_bytes(d, true);
   return CP_ATTN_OK;
 }

@@ -199,7 +199,7 @@ void fill_bwd_params(const cp_attn_desc *d, const Share &s, BwdParams *p, bool a
 // Bytes of the backward's per-row statistics (-Delta and LSE*log2e, each on a
 // 256-byte boundary), the part of the workspace every backward needs.
 // Workspace bytes of the backward: the per-row statistics, the partial dK/dV
-// of split key tiles (allow_split) and the bit table of a boolean user mask.
+// of split key tiles (allow_split) and a user mask's bit tables and flag.
 size_t bwd_workspace_bytes(const cp_attn_desc *d, bool allow_split);
 // cp_attn_bwd_timed with the choice of splitting key tiles (the no-alloc
 // entry point passes allow_split = false: its scratch holds no partials).
